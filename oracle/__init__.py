@@ -1,0 +1,8 @@
+"""fp64 CPU oracle (test infrastructure only).
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  It shares no code with the HIP path
+and imports nothing from the product package.
+"""
+from .slikl_ref import slikl_grad_ref, kl_loss_ref, unit_backward  # noqa: F401
+from .metadata_ref import metadata_ref  # noqa: F401

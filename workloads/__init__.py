@@ -1,0 +1,16 @@
+"""Seeded synthetic inputs for the sparse lightning-indexer KL-loss backward.
+
+This package only draws random inputs (queries, keys, head weights, top-k index
+lists, target distributions).  It holds none of the operator's arithmetic, so
+both the fp64 CPU oracle and the GPU path can be fed from it without sharing
+any computation.
+"""
+from .gen import (  # noqa: F401
+    Inputs,
+    Workload,
+    WORKLOADS,
+    make_inputs,
+    round_to_bf16,
+    round_to_f16,
+    workload,
+)
