@@ -1,0 +1,148 @@
+/*
+ * slikl.h -- C ABI of the sparse lightning-indexer KL-loss backward for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The operation is the one defined on the operator page
+ * "aclnnSparseLightningIndexerKLLossGrad" (CANN API reference,
+ * ops-transformer), 计算公式 / formula section: for every query token t and
+ * key head g, gather the top-k key rows named by sparseIndices, form
+ * S = q_t K_topk^T per indexer head, I = sum_h w_h ReLU(S_h), write
+ * y = Softmax(I) to softmaxOut, form dI = y - p (p = attnSoftmaxL1Norm),
+ * dW = dI ReLU(S)^T, dS = w (x) dI masked by S > 0, dq = dS K_topk and
+ * scatter-add dK_topk = dS^T q into the key rows; -1 slots take no part.
+ * The page's two-phase call (workspace query, then execute) and its
+ * constraints section (dtypes, BSND/TND layouts, cuSeqLens for TND, -1
+ * padding, batch-relative indices) fix the interface below.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers, contiguous, non-aliasing, owned
+ *    by the caller.  The library never allocates, frees or synchronises.
+ *    q, k, dq and dk must be 16-byte aligned and the workspace 256-byte
+ *    aligned (PARAM_INVALID / WORKSPACE otherwise); every tensor must hold
+ *    fewer than 2^31 elements (PARAM_INVALID otherwise).
+ *  - Work is only enqueued on `stream` (a hipStream_t passed as void*, NULL =
+ *    the default stream); the caller keeps buffers alive until it completes.
+ *  - A non-OK status is returned from host-side validation only, and then
+ *    nothing has been enqueued.  Device-side contract violations (an index
+ *    outside [0, key length of its batch) other than -1, cuSeqLens that do not
+ *    start at 0, decrease or miss the total) are not reported through the
+ *    status: such slots are treated as -1 and the metadata error word is set.
+ *  - The library is stateless and thread-safe.
+ *
+ * Tensor shapes (BSND | TND):
+ *    q            [B,S1,N1,D] | [T1,N1,D]      fp16 or bf16
+ *    k            [B,S2,N2,D] | [T2,N2,D]      same dtype as q
+ *    w            [B,S1,N1]   | [T1,N1]        fp32
+ *    sparse_indices, attn_softmax_l1norm, softmax_out
+ *                 [B,S1,N2,topk] | [T1,N2,topk]  int32 / fp32 / fp32
+ *    dq, dk, dw   like q, k, w.
+ * Query head h belongs to key head h / (N1/N2).  Indices are relative to
+ * their batch's key sequence.  Outputs are fully overwritten: softmax_out is
+ * 0 at -1 slots, dk is 0 for keys no slot names.
+ */
+#ifndef SLIKL_H
+#define SLIKL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  NULLPTR mirrors the page family's null-pointer errors,
+ * PARAM_INVALID its parameter errors (dtype, layout, shape, range, missing
+ * cuSeqLens for TND). */
+typedef enum slikl_status {
+    SLIKL_OK = 0,
+    SLIKL_ERR_NULLPTR = 1,        /* a required pointer is NULL                 */
+    SLIKL_ERR_PARAM_INVALID = 2,  /* a descriptor field is out of its range     */
+    SLIKL_ERR_UNSUPPORTED = 3,    /* valid per the page, not built here          */
+    SLIKL_ERR_WORKSPACE = 4,      /* workspace missing or smaller than required */
+    SLIKL_ERR_LAUNCH = 5,         /* a HIP launch or device query failed        */
+} slikl_status;
+
+enum { SLIKL_LAYOUT_BSND = 0, SLIKL_LAYOUT_TND = 1 };
+enum { SLIKL_DTYPE_F16 = 0, SLIKL_DTYPE_BF16 = 1 };
+/* Metadata split modes: WEIGHTED balances (valid slots + overhead) per unit;
+ * ROWS is the even row split of the metadata pre-pass prior art. */
+enum { SLIKL_SPLIT_WEIGHTED = 0, SLIKL_SPLIT_ROWS = 1 };
+
+/* Metadata array (int32, SLIKL_METADATA_INTS entries).  A "unit" is one
+ * (query row, key head) pair, u = row * N2 + g.
+ *   [0] total units          [1] former size (ROWS)   [2] remain size (ROWS)
+ *   [3] remain count (ROWS)  [4] used parts           [5] max key length
+ *   [6] parts P              [7] split mode           [8] error word
+ *   [9] per-unit overhead    [10..15] 0
+ *   [16 + i], i = 0..P: first unit of part i (part i = [b_i, b_{i+1})).
+ * Error word bits: 1 = bad cuSeqLensQ, 2 = bad cuSeqLensK, 4 = an index out
+ * of its batch's key range (WEIGHTED mode only; ROWS reads no indices). */
+#define SLIKL_METADATA_HEADER 16
+#define SLIKL_MAX_PARTS 2048
+#define SLIKL_METADATA_INTS 2080
+#define SLIKL_UNIT_OVERHEAD 64
+
+typedef struct slikl_desc {
+    int32_t layout_q;        /* SLIKL_LAYOUT_*                                        */
+    int32_t layout_k;        /* SLIKL_LAYOUT_*                                        */
+    int32_t dtype;           /* SLIKL_DTYPE_* of q, k, dq, dk                         */
+    int32_t deterministic;   /* 0: fp32 atomic dK (run-to-run order may vary);
+                                1: bitwise reproducible dK (fixed-point integer sum)  */
+    int64_t batch;           /* B (> 0).  TND: number of sequences, cuSeqLens hold B+1 */
+    int64_t s1;              /* BSND q: S1 (> 0); TND q: T1 (>= 0, total rows)         */
+    int64_t s2;              /* BSND k: S2 (> 0); TND k: T2 (>= 0, total rows)         */
+    int64_t n1;              /* query (indexer) heads, 1..128                          */
+    int64_t n2;              /* key heads, >= 1, divides n1                            */
+    int64_t d;               /* head dim: 32, 64 or 128                                */
+    int64_t topk;            /* 1..2048                                                */
+    const int32_t *cu_seqlens_q; /* device, B+1 entries starting at 0; required iff TND q */
+    const int32_t *cu_seqlens_k; /* device, B+1 entries starting at 0; required iff TND k */
+    int32_t num_parts;       /* metadata parts; 0 = library default (CUs x blocks/CU)  */
+    int32_t split_mode;      /* SLIKL_SPLIT_*                                         */
+} slikl_desc;
+
+/* First phase (the page's "GetWorkspaceSize" step): validate `desc` and return
+ * the workspace bytes slikl_grad and slikl_grad_metadata need.  Host only: no
+ * device access.  Errors: NULLPTR (desc or bytes NULL, or a TND side without
+ * its cuSeqLens pointer), PARAM_INVALID (any field out of range). */
+slikl_status slikl_grad_workspace_size(const slikl_desc *desc, size_t *bytes);
+
+/* Number of metadata parts the library uses for `desc` (num_parts, or the
+ * default derived from the current device).  Queries the current HIP device
+ * when num_parts == 0 (LAUNCH if that fails). */
+slikl_status slikl_grad_parts(const slikl_desc *desc, int32_t *parts);
+
+/* Load-balancing metadata pre-pass (prior art: the metadata article's
+ * 功能定位 and Metadata 输出布局 sections describe an AICPU pre-operator
+ * that splits the merged B*S1 rows over cores into a fixed int32 array).
+ * Enqueues device kernels that write SLIKL_METADATA_INTS int32 values to
+ * `metadata` (device).  WEIGHTED mode reads `sparse_indices` (device, required
+ * then); ROWS mode ignores it (may be NULL).  `workspace` is the same buffer
+ * slikl_grad takes (at least slikl_grad_workspace_size bytes).  The result
+ * depends only on desc, the indices and the parts count. */
+slikl_status slikl_grad_metadata(const slikl_desc *desc, const int32_t *sparse_indices,
+                                 int32_t *metadata, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/* Second phase (the page's execute step): enqueue the backward pass.
+ * `metadata` may be NULL (the library then runs the metadata pre-pass into
+ * the workspace first) or an array written by slikl_grad_metadata for the
+ * same desc and indices.  Results do not depend on the metadata: dq, dw and
+ * softmax_out are bitwise identical for any split; dk is bitwise identical
+ * too in deterministic mode, and equal up to fp32 summation order otherwise.
+ * Errors: NULLPTR (a required pointer NULL), PARAM_INVALID, WORKSPACE
+ * (workspace NULL or workspace_bytes too small), LAUNCH. */
+slikl_status slikl_grad(const slikl_desc *desc, const void *q, const void *k,
+                        const float *w, const int32_t *sparse_indices,
+                        const float *attn_softmax_l1norm, const int32_t *metadata,
+                        void *dq, void *dk, float *dw, float *softmax_out,
+                        void *workspace, size_t workspace_bytes, void *stream);
+
+/* Static description of a status code. */
+const char *slikl_status_string(slikl_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SLIKL_H */

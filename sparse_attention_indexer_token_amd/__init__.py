@@ -1,0 +1,190 @@
+"""Sparse lightning-indexer KL-loss backward on AMD MI355X (gfx950).
+
+Thin PyTorch binding over the C ABI of ``libslikl.so`` (include/slikl.h).
+The functions below carry the C names and only marshal arguments: they read
+shapes from the tensors, allocate outputs / workspace with torch on the
+tensors' device and pass raw device pointers and the current HIP stream.
+
+    dq, dk, dw, softmax_out = slikl_grad(q, k, w, sparse_indices, p)
+
+Shapes (BSND | TND):
+    q [B,S1,N1,D] | [T1,N1,D] (bf16 or fp16), k [B,S2,N2,D] | [T2,N2,D] (same dtype),
+    w [B,S1,N1] | [T1,N1] fp32, sparse_indices / p [B,S1,N2,topk] | [T1,N2,topk]
+    (int32 / fp32).  TND sides need int32 cumulative lengths (B+1 entries).
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+from . import _native
+from ._native import (  # noqa: F401
+    EXPORTS, LAYOUT, METADATA_HEADER, METADATA_INTS, MAX_PARTS, SliklDesc, SliklError,
+    UNIT_OVERHEAD, load,
+)
+
+__all__ = ["slikl_grad", "slikl_grad_metadata", "slikl_grad_workspace_size",
+           "slikl_grad_parts", "slikl_status_string", "make_desc", "SliklDesc", "SliklError"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return _native.DTYPE["bf16"]
+    if t.dtype == torch.float16:
+        return _native.DTYPE["f16"]
+    raise TypeError(f"q/k must be bfloat16 or float16, got {t.dtype}")
+
+
+def make_desc(q, k, sparse_indices, *, layout_q: str = "BSND", layout_k: str = "BSND",
+              cu_seqlens_q=None, cu_seqlens_k=None, deterministic: bool = False,
+              num_parts: int = 0, split_mode: str = "weighted") -> SliklDesc:
+    """Build the C descriptor from tensor shapes (no device access)."""
+    if layout_q not in LAYOUT or layout_k not in LAYOUT:
+        raise ValueError("layouts must be 'BSND' or 'TND'")
+    if layout_q == "BSND":
+        if q.dim() != 4:
+            raise ValueError("BSND q must be [B,S1,N1,D]")
+        batch, s1, n1, d = q.shape
+    else:
+        if q.dim() != 3 or cu_seqlens_q is None:
+            raise ValueError("TND q must be [T1,N1,D] with cu_seqlens_q")
+        s1, n1, d = q.shape
+        batch = cu_seqlens_q.numel() - 1
+    if layout_k == "BSND":
+        if k.dim() != 4:
+            raise ValueError("BSND k must be [B,S2,N2,D]")
+        kb, s2, n2, dk_ = k.shape
+        if layout_q == "TND" and kb != batch:
+            raise ValueError("batch of k does not match cu_seqlens_q")
+        batch = kb if layout_q == "BSND" else batch
+        if layout_q == "BSND" and kb != q.shape[0]:
+            raise ValueError("q and k disagree on B")
+    else:
+        if k.dim() != 3 or cu_seqlens_k is None:
+            raise ValueError("TND k must be [T2,N2,D] with cu_seqlens_k")
+        s2, n2, dk_ = k.shape
+        if cu_seqlens_k.numel() - 1 != batch:
+            raise ValueError("cu_seqlens_k does not match the batch")
+    if dk_ != d:
+        raise ValueError("q and k disagree on D")
+    desc = SliklDesc()
+    desc.layout_q = LAYOUT[layout_q]
+    desc.layout_k = LAYOUT[layout_k]
+    desc.dtype = _dtype_code(q)
+    desc.deterministic = 1 if deterministic else 0
+    desc.batch, desc.s1, desc.s2 = int(batch), int(s1), int(s2)
+    desc.n1, desc.n2, desc.d = int(n1), int(n2), int(d)
+    desc.topk = int(sparse_indices.shape[-1])
+    desc.cu_seqlens_q = cu_seqlens_q.data_ptr() if layout_q == "TND" else None
+    desc.cu_seqlens_k = cu_seqlens_k.data_ptr() if layout_k == "TND" else None
+    desc.num_parts = int(num_parts)
+    desc.split_mode = _native.SPLIT[split_mode]
+    return desc
+
+
+def _check_tensor(name, t, dtype, device, shape=None):
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} must live on {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream_handle(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def slikl_status_string(status: int) -> str:
+    return _native.status_string(status)
+
+
+def slikl_grad_workspace_size(desc: SliklDesc) -> int:
+    return _native.workspace_size(desc)
+
+
+def slikl_grad_parts(desc: SliklDesc) -> int:
+    return _native.grad_parts(desc)
+
+
+def slikl_grad_metadata(q, k, sparse_indices, *, layout_q="BSND", layout_k="BSND",
+                        cu_seqlens_q=None, cu_seqlens_k=None, deterministic=False,
+                        num_parts: int = 0, split_mode: str = "weighted",
+                        metadata=None, workspace=None):
+    """Run the load-balancing metadata pre-pass; returns the int32 metadata tensor."""
+    torch = _torch()
+    desc = make_desc(q, k, sparse_indices, layout_q=layout_q, layout_k=layout_k,
+                     cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
+                     deterministic=deterministic, num_parts=num_parts, split_mode=split_mode)
+    dev = q.device
+    _check_tensor("sparse_indices", sparse_indices, torch.int32, dev)
+    nbytes = _native.workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if metadata is None:
+        metadata = torch.empty(METADATA_INTS, dtype=torch.int32, device=dev)
+    _check_tensor("metadata", metadata, torch.int32, dev, (METADATA_INTS,))
+    _native.grad_metadata_raw(desc, sparse_indices.data_ptr(), metadata.data_ptr(),
+                              workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                              _stream_handle(dev))
+    return metadata
+
+
+def slikl_grad(q, k, w, sparse_indices, attn_softmax_l1norm, *, layout_q="BSND", layout_k="BSND",
+               cu_seqlens_q=None, cu_seqlens_k=None, deterministic: bool = False,
+               metadata=None, num_parts: int = 0, split_mode: str = "weighted",
+               workspace=None, out: Optional[tuple] = None):
+    """Backward pass; returns (dq, dk, dw, softmax_out).
+
+    ``out`` may hold preallocated (dq, dk, dw, softmax_out); ``workspace`` a
+    uint8 device tensor of at least ``slikl_grad_workspace_size`` bytes.
+    """
+    torch = _torch()
+    desc = make_desc(q, k, sparse_indices, layout_q=layout_q, layout_k=layout_k,
+                     cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
+                     deterministic=deterministic, num_parts=num_parts, split_mode=split_mode)
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    qs = tuple(q.shape)
+    rows = qs[:-2]
+    _check_tensor("q", q, q.dtype, dev)
+    _check_tensor("k", k, q.dtype, dev)
+    _check_tensor("w", w, torch.float32, dev, rows + (desc.n1,))
+    _check_tensor("sparse_indices", sparse_indices, torch.int32, dev, rows + (desc.n2, desc.topk))
+    _check_tensor("attn_softmax_l1norm", attn_softmax_l1norm, torch.float32, dev,
+                  rows + (desc.n2, desc.topk))
+    for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if cu is not None:
+            _check_tensor(name, cu, torch.int32, dev, (desc.batch + 1,))
+    if metadata is not None:
+        _check_tensor("metadata", metadata, torch.int32, dev, (METADATA_INTS,))
+    if out is None:
+        dq = torch.empty_like(q)
+        dk = torch.empty_like(k)
+        dw = torch.empty_like(w)
+        y = torch.empty_like(attn_softmax_l1norm)
+    else:
+        dq, dk, dw, y = out
+        _check_tensor("dq", dq, q.dtype, dev, q.shape)
+        _check_tensor("dk", dk, q.dtype, dev, k.shape)
+        _check_tensor("dw", dw, torch.float32, dev, w.shape)
+        _check_tensor("softmax_out", y, torch.float32, dev, attn_softmax_l1norm.shape)
+    nbytes = _native.workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    _native.grad_raw(desc, q.data_ptr(), k.data_ptr(), w.data_ptr(), sparse_indices.data_ptr(),
+                     attn_softmax_l1norm.data_ptr(),
+                     metadata.data_ptr() if metadata is not None else 0,
+                     dq.data_ptr(), dk.data_ptr(), dw.data_ptr(), y.data_ptr(),
+                     workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                     _stream_handle(dev))
+    return dq, dk, dw, y

@@ -1,0 +1,371 @@
+// Auxiliary kernels: accumulator fill, dK finalisation, the deterministic
+// fixed-point scale, and the load-balancing metadata pre-pass.
+#include "device_common.h"
+#include "slikl_internal.h"
+
+namespace slikl {
+
+// ---------------------------------------------------------------------------
+// Fill with zeros (a plain kernel rather than a memset node, so the sequence
+// stays valid under stream capture).
+// ---------------------------------------------------------------------------
+__global__ void zero_kernel(u32x4 *p, size_t n16, uint32_t *tail, size_t ntail) {
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (; i < n16; i += stride) p[i] = u32x4{0u, 0u, 0u, 0u};
+    if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0u;
+}
+
+hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t stream) {
+    if (bytes == 0) return hipSuccess;
+    size_t n16 = bytes / 16;
+    size_t ntail = (bytes - n16 * 16) / 4;
+    size_t blocks = (n16 + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
+    if (blocks == 0) blocks = 1;
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (u32x4 *)ptr, n16,
+                       (uint32_t *)((char *)ptr + n16 * 16), ntail);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// dK = round16(accumulator).  Deterministic mode: accumulator is int64 fixed
+// point with scale 2^F, read back as acc * 2^-F.
+// ---------------------------------------------------------------------------
+template <bool F16, bool DET>
+__global__ void finalize_kernel(const void *acc, uint16_t *dk, size_t n, const float *scale) {
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    size_t stride = (size_t)gridDim.x * blockDim.x;
+    float inv = 1.f;
+    if constexpr (DET) inv = scale[1];
+    for (; i < n; i += stride) {
+        float v;
+        if constexpr (DET) v = (float)((double)((const long long *)acc)[i] * (double)inv);
+        else v = ((const float *)acc)[i];
+        dk[i] = to16<F16>(v);
+    }
+}
+
+hipError_t launch_finalize_dk(const Problem &pb, bool f16, bool det, hipStream_t stream) {
+    size_t n = (size_t)pb.t2 * pb.n2 * pb.d;
+    if (n == 0) return hipSuccess;
+    size_t blocks = (n + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    dim3 gr((unsigned)blocks), bl(256);
+    if (f16) {
+        if (det) hipLaunchKernelGGL((finalize_kernel<true, true>), gr, bl, 0, stream, pb.dk_acc, pb.dk, n, pb.det_scale);
+        else hipLaunchKernelGGL((finalize_kernel<true, false>), gr, bl, 0, stream, pb.dk_acc, pb.dk, n, pb.det_scale);
+    } else {
+        if (det) hipLaunchKernelGGL((finalize_kernel<false, true>), gr, bl, 0, stream, pb.dk_acc, pb.dk, n, pb.det_scale);
+        else hipLaunchKernelGGL((finalize_kernel<false, false>), gr, bl, 0, stream, pb.dk_acc, pb.dk, n, pb.det_scale);
+    }
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Deterministic mode scale.  Integer addition is associative, so summing the
+// dK parts as int64 fixed point gives the same bits in any order.  The scale
+// 2^F is chosen per call from order-independent maxima so that no sum can
+// overflow:  |part| <= max|q| * max_row sum_h |w| * (1 + max|p|)  (since
+// |dI| = |y - p| <= 1 + |p|), and one key row receives at most T1 * topk
+// parts.  F = floor(61 - log2(T1 * topk * bound)).
+// scale block (as uint32 / float): [0] 2^F  [1] 2^-F  [2] max|q|  [3] max row
+// sum|w|  [4] max|p|.
+// ---------------------------------------------------------------------------
+template <bool F16>
+__global__ void det_bound_kernel(Problem pb, uint32_t *blk) {
+    const size_t tid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    float mq = 0.f, mw = 0.f, mp = 0.f;
+    const size_t nq = (size_t)pb.t1 * pb.n1 * pb.d;
+    for (size_t i = tid; i < nq; i += stride) mq = fmaxf(mq, fabsf(from16<F16>(pb.q[i])));
+    for (size_t r = tid; r < (size_t)pb.t1; r += stride) {
+        float s = 0.f;
+        for (int h = 0; h < pb.n1; ++h) s += fabsf(pb.w[r * pb.n1 + h]);
+        mw = fmaxf(mw, s);
+    }
+    const size_t np = (size_t)pb.t1 * pb.n2 * pb.topk;
+    for (size_t i = tid; i < np; i += stride) mp = fmaxf(mp, fabsf(pb.p[i]));
+    mq = wave_max(mq);
+    mw = wave_max(mw);
+    mp = wave_max(mp);
+    if ((threadIdx.x & 63) == 0) {
+        // non-negative floats order like their bit patterns; NaN maps high
+        atomicMax(blk + 2, __float_as_uint(mq));
+        atomicMax(blk + 3, __float_as_uint(mw));
+        atomicMax(blk + 4, __float_as_uint(mp));
+    }
+}
+
+__global__ void det_finish_kernel(uint32_t *blk, double refs) {
+    if (threadIdx.x != 0 || blockIdx.x != 0) return;
+    float mq = __uint_as_float(blk[2]), mw = __uint_as_float(blk[3]), mp = __uint_as_float(blk[4]);
+    double bound = (double)mq * (double)mw * (1.0 + (double)mp);
+    int F = 60;
+    if (bound > 0.0 && bound < 1e300) {
+        double f = floor(61.0 - log2(refs) - log2(bound));
+        F = f > 120.0 ? 120 : (f < -120.0 ? -120 : (int)f);
+    } else if (!(bound == 0.0)) {
+        F = -120;    // non-finite inputs: results are meaningless but bounded
+    }
+    float *fb = (float *)blk;
+    fb[0] = ldexpf(1.f, F);
+    fb[1] = ldexpf(1.f, -F);
+}
+
+hipError_t launch_det_scale(const Problem &pb, bool f16, float *scale_block, hipStream_t stream) {
+    hipError_t e = hipSuccess;
+    size_t work = (size_t)pb.t1 * pb.n1 * pb.d;
+    size_t blocks = (work + 255) / 256;
+    if (blocks > 1024) blocks = 1024;
+    if (blocks == 0) blocks = 1;
+    if (f16)
+        hipLaunchKernelGGL(det_bound_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, pb,
+                           (uint32_t *)scale_block);
+    else
+        hipLaunchKernelGGL(det_bound_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, pb,
+                           (uint32_t *)scale_block);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    double refs = (double)(pb.t1 > 0 ? pb.t1 : 1) * (double)pb.topk;
+    hipLaunchKernelGGL(det_finish_kernel, dim3(1), dim3(64), 0, stream, (uint32_t *)scale_block, refs);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// fp16 copy of bf16 keys for the second-pass contractions.  A global power of
+// two 2^eK (from max|k|) maps the keys into fp16's range:  max|k| 2^eK < 2^15.
+// bf16 values carry 8 significant bits, fp16 11, so every key whose scaled
+// magnitude is >= 2^-14 converts exactly; smaller ones keep an absolute error
+// below 2^-25 * 2^-eK.  scale block: [5] max|k| bits, [6] 2^-eK, [7] 2^eK.
+// ---------------------------------------------------------------------------
+__global__ void kmax_kernel(const uint16_t *k, size_t n, uint32_t *blk) {
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    float m = 0.f;
+    for (; i < n; i += stride) m = fmaxf(m, fabsf(from16<false>(k[i])));
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) atomicMax(blk + 5, __float_as_uint(m));
+}
+
+__device__ __forceinline__ int k_exponent(const uint32_t *blk) {
+    float m = __uint_as_float(blk[5]);
+    if (!(m > 0.f) || !(m < INFINITY)) return 0;
+    int ex;
+    frexpf(m, &ex);
+    return 15 - ex;
+}
+
+__global__ void k_to_f16_kernel(const uint16_t *k, uint16_t *k16, size_t n8, uint32_t *blk) {
+    const int e = k_exponent(blk);
+    const float sc = ldexpf(1.f, e);
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (; i < n8; i += stride) {
+        u32x4 v = ((const u32x4 *)k)[i];
+        u32x4 o;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            float lo = __uint_as_float(v[c] << 16) * sc;
+            float hi = __uint_as_float(v[c] & 0xffff0000u) * sc;
+            o[c] = pack2<true>(lo, hi);
+        }
+        ((u32x4 *)k16)[i] = o;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        float *fb = (float *)blk;
+        fb[6] = ldexpf(1.f, -e);
+        fb[7] = sc;
+    }
+}
+
+hipError_t launch_k_to_f16(const Problem &pb, uint16_t *k16, float *scale_block, hipStream_t stream) {
+    const size_t n = (size_t)pb.t2 * pb.n2 * pb.d;     // multiple of 32 (d in {32, 64, 128})
+    size_t blocks = (n / 8 + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
+    if (blocks == 0) blocks = 1;
+    hipLaunchKernelGGL(kmax_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pb.k, n,
+                       (uint32_t *)scale_block);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_to_f16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pb.k, k16, n / 8,
+                       (uint32_t *)scale_block);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Metadata pre-pass.
+//  count kernel (weighted mode): one wavefront per unit counts the slots whose
+//    index lies in [0, key length of the batch); prefix[u + 1] = count +
+//    overhead; out-of-range indices other than -1 set error bit 4.
+//  split kernel (one 1024-thread block): checks cuSeqLens, scans the unit
+//    costs, finds the part boundaries and writes the header.
+// Weighted boundary i is the first unit u with E(u) * P >= i * W, E the
+// exclusive cost prefix and W the total; rows mode gives the first
+// former_num parts ceil(U / P) units and the rest one fewer.
+// ---------------------------------------------------------------------------
+__global__ void meta_count_kernel(Problem pb, int64_t *prefix, int overhead, int32_t *flags) {
+    const int lane = threadIdx.x & 63;
+    const int64_t U = pb.t1 * pb.n2;
+    int64_t wv = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+    const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
+    int bad = 0;
+    for (int64_t u = wv; u < U; u += nw) {
+        int64_t r = u / pb.n2;
+        int b = pb.layout_q == 0 ? (int)(r / pb.s1) : batch_of_row(pb.cu_q, pb.batch, r);
+        int64_t klen;
+        if (pb.layout_k == 0) {
+            klen = pb.s2;
+        } else {
+            int64_t k0 = pb.cu_k[b], k1 = pb.cu_k[b + 1];
+            k0 = k0 < 0 ? 0 : (k0 > pb.t2 ? pb.t2 : k0);
+            k1 = k1 < k0 ? k0 : (k1 > pb.t2 ? pb.t2 : k1);
+            klen = k1 - k0;
+        }
+        const int32_t *row = pb.idx + u * pb.topk;
+        int cnt = 0;
+        for (int s = lane; s < pb.topk; s += 64) {
+            int v = row[s];
+            if (v >= 0 && v < klen) ++cnt;
+            else if (v != -1) bad = 1;
+        }
+        for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
+        if (lane == 0) prefix[u + 1] = cnt + overhead;
+    }
+    if (__any(bad) && lane == 0) atomicOr(flags, 4);
+}
+
+__device__ __forceinline__ int check_cu(const int32_t *cu, int batch, int64_t total) {
+    // returns 1 if cu does not start at 0, decreases, or misses the total
+    int bad = 0;
+    for (int b = threadIdx.x; b < batch; b += blockDim.x)
+        if (cu[b + 1] < cu[b]) bad = 1;
+    if (threadIdx.x == 0 && (cu[0] != 0 || (int64_t)cu[batch] != total)) bad = 1;
+    return __syncthreads_or(bad);
+}
+
+__global__ __launch_bounds__(1024) void meta_split_kernel(Problem pb, int parts, int mode, int overhead,
+                                                          int64_t *prefix, const int32_t *cflags,
+                                                          int32_t *md) {
+    __shared__ int64_t s_part[1024];
+    __shared__ int s_used[32];
+    const int tid = threadIdx.x, nt = blockDim.x;
+    const int64_t U = pb.t1 * pb.n2;
+
+    int flags = 0;
+    if (pb.layout_q == 1 && check_cu(pb.cu_q, pb.batch, pb.t1)) flags |= 1;
+    if (pb.layout_k == 1 && check_cu(pb.cu_k, pb.batch, pb.t2)) flags |= 2;
+
+    // max key length over batches
+    int64_t mk = 0;
+    if (pb.layout_k == 0) {
+        mk = pb.s2;
+    } else {
+        int64_t loc = 0;
+        for (int b = tid; b < pb.batch; b += nt) {
+            int64_t l = (int64_t)pb.cu_k[b + 1] - pb.cu_k[b];
+            loc = l > loc ? l : loc;
+        }
+        s_part[tid] = loc;
+        __syncthreads();
+        for (int o = nt / 2; o > 0; o >>= 1) {
+            if (tid < o) s_part[tid] = s_part[tid] > s_part[tid + o] ? s_part[tid] : s_part[tid + o];
+            __syncthreads();
+        }
+        mk = s_part[0];
+        __syncthreads();
+    }
+
+    int32_t *bnd = md + 16;
+    if (mode == 0) {
+        // inclusive scan of prefix[1..U] (prefix[0] = 0): contiguous segments per thread
+        const int64_t seg = (U + nt - 1) / nt;
+        const int64_t a = (int64_t)tid * seg, e = a + seg < U ? a + seg : U;
+        int64_t loc = 0;
+        for (int64_t i = a; i < e; ++i) loc += prefix[i + 1];
+        s_part[tid] = loc;
+        __syncthreads();
+        for (int o = 1; o < nt; o <<= 1) {   // Hillis-Steele inclusive scan
+            int64_t v = tid >= o ? s_part[tid - o] : 0;
+            __syncthreads();
+            s_part[tid] += v;
+            __syncthreads();
+        }
+        int64_t run = tid > 0 ? s_part[tid - 1] : 0;
+        for (int64_t i = a; i < e; ++i) {
+            run += prefix[i + 1];
+            prefix[i + 1] = run;
+        }
+        if (tid == 0) prefix[0] = 0;
+        __syncthreads();
+        const int64_t W = s_part[nt - 1];
+        for (int i = tid; i <= parts; i += nt) {
+            // first u in [0, U] with prefix[u] * parts >= i * W
+            int64_t lo = 0, hi = U;
+            const int64_t target = (int64_t)i * W;
+            while (lo < hi) {
+                int64_t mid = (lo + hi) >> 1;
+                if (prefix[mid] * parts >= target) hi = mid; else lo = mid + 1;
+            }
+            bnd[i] = (int32_t)lo;
+        }
+    } else {
+        int64_t former = 0, remain = 0, remain_num = 0, former_num = 0;
+        if (U > 0) {
+            former = (U + parts - 1) / parts;
+            remain = former - 1;
+            remain_num = (int64_t)parts * former - U;
+            former_num = parts - remain_num;
+        }
+        for (int i = tid; i <= parts; i += nt) {
+            int64_t v = 0;
+            if (U > 0) v = i <= former_num ? i * former : former_num * former + (i - former_num) * remain;
+            bnd[i] = (int32_t)v;
+        }
+        if (tid == 0) {
+            md[1] = (int32_t)former;
+            md[2] = (int32_t)remain;
+            md[3] = (int32_t)remain_num;
+        }
+    }
+    __syncthreads();
+    int used = 0;
+    for (int i = tid; i < parts; i += nt) used += bnd[i + 1] > bnd[i];
+    for (int o = 32; o > 0; o >>= 1) used += __shfl_xor(used, o);
+    if ((tid & 63) == 0) s_used[tid >> 6] = used;
+    __syncthreads();
+    if (tid == 0) {
+        int tot = 0;
+        for (int w = 0; w < nt / 64; ++w) tot += s_used[w];
+        md[0] = (int32_t)U;
+        if (mode == 0) { md[1] = 0; md[2] = 0; md[3] = 0; }
+        md[4] = tot;
+        md[5] = (int32_t)mk;
+        md[6] = parts;
+        md[7] = mode;
+        md[8] = flags | (mode == 0 ? cflags[0] : 0);
+        md[9] = mode == 0 ? overhead : 0;
+        for (int i = 10; i < 16; ++i) md[i] = 0;
+    }
+    for (int i = 16 + parts + 1 + tid; i < 2080; i += nt) md[i] = 0;
+}
+
+hipError_t launch_metadata(const Problem &pb, int parts, int mode, int overhead, int32_t *metadata,
+                           int64_t *prefix, int32_t *flags, hipStream_t stream) {
+    const int64_t U = pb.t1 * pb.n2;
+    hipError_t e = launch_zero(flags, 16, stream);
+    if (e != hipSuccess) return e;
+    if (mode == 0 && U > 0) {
+        int64_t waves = U < 65536 ? U : 65536;
+        int64_t blocks = (waves * 64 + 255) / 256;
+        hipLaunchKernelGGL(meta_count_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pb, prefix,
+                           overhead, flags);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(meta_split_kernel, dim3(1), dim3(1024), 0, stream, pb, parts, mode, overhead, prefix,
+                       flags, metadata);
+    return hipGetLastError();
+}
+
+}  // namespace slikl

@@ -1,0 +1,156 @@
+// Device helpers for gfx950: MFMA wrappers, swizzled LDS tiles, conversions,
+// wave/block reductions.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace slikl {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef s16x4 __attribute__((address_space(3))) lds_s16x4;
+
+constexpr int kBlock = 256;   // 4 wavefronts of 64 lanes
+
+// D(32x32 fp32) += A(32x16) * B(16x32), 16-bit inputs held as 4 dwords/lane.
+// Lane l holds A row l%32 and B column l%32, k elements 8*(l/32)+[0,8);
+// result element j of lane l is row 8*(j/4) + 4*(l/32) + j%4, column l%32.
+template <bool F16>
+__device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+    if constexpr (F16) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                      __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+}
+
+// Byte offset of element (row, col) of a 16-bit LDS tile whose rows hold
+// `CH` 16-byte chunks.  Chunks are XOR-swizzled by the row so that both the
+// 16-byte row reads of 8 consecutive rows and the transposing 8-byte reads of
+// 4 consecutive rows hit distinct banks.
+template <int CH>
+__device__ __forceinline__ int tile_off(int row, int col) {
+    constexpr int mask = CH >= 8 ? 7 : CH - 1;
+    int swz = (((row & 3) << 1) ^ ((row >> 2) & 1)) & mask;
+    return row * (CH * 16) + (((col >> 3) ^ swz) << 4) + ((col & 7) << 1);
+}
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each 16-lane group, lane
+// i supplies the address of 4 consecutive 16-bit elements (row r0 + i/4,
+// columns c0 + 4*(i%4) .. +3); lane j of the group then receives column
+// c0 + j of rows r0 .. r0+3.
+__device__ __forceinline__ u32x2 lds_read_tr(const char *base, int byte_off) {
+    s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(base + byte_off));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// Round two floats to a packed pair of 16-bit values (round to nearest even).
+template <bool F16>
+__device__ __forceinline__ uint32_t pack2(float lo, float hi) {
+    if constexpr (F16) {
+        f16x2 v = {(_Float16)lo, (_Float16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    } else {
+        bf16x2 v = {(__bf16)lo, (__bf16)hi};
+        return __builtin_bit_cast(uint32_t, v);
+    }
+}
+
+template <bool F16>
+__device__ __forceinline__ uint16_t to16(float x) {
+    if constexpr (F16) {
+        return __builtin_bit_cast(uint16_t, (_Float16)x);
+    } else {
+        return __builtin_bit_cast(uint16_t, (__bf16)x);
+    }
+}
+
+template <bool F16>
+__device__ __forceinline__ float from16(uint16_t x) {
+    if constexpr (F16) {
+        return (float)__builtin_bit_cast(_Float16, x);
+    } else {
+        return __builtin_bit_cast(float, (uint32_t)x << 16);
+    }
+}
+
+// v if bit `lane` of the wave-uniform 64-bit mask is set, else 0.
+__device__ __forceinline__ float select_by_mask(float v, uint64_t mask) {
+    float r;
+    asm("v_cndmask_b32_e64 %0, 0, %1, %2" : "=v"(r) : "v"(v), "s"(mask));
+    return r;
+}
+
+__device__ __forceinline__ uint64_t uniform64(uint64_t x) {
+    uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)x);
+    uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(x >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+    return v;
+}
+
+// Block-wide reductions for a 256-thread block; `red` holds >= 4 floats.
+__device__ __forceinline__ float block_max(float v, float *red) {
+    v = wave_max(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+__device__ __forceinline__ float block_sum(float v, float *red) {
+    v = wave_sum(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    return (red[0] + red[1]) + (red[2] + red[3]);
+}
+
+// Exclusive prefix sum over the block; `tmp` holds >= 4 ints.
+__device__ __forceinline__ int block_excl_scan(int v, int *tmp, int *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    __syncthreads();
+    if (lane == 63) tmp[wave] = x;
+    __syncthreads();
+    int off = 0;
+    for (int i = 0; i < wave; ++i) off += tmp[i];
+    *total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+    return off + x - v;
+}
+
+// Batch of flattened row `r` given cumulative lengths cu[0..batch].
+__device__ __forceinline__ int batch_of_row(const int32_t *cu, int batch, int64_t r) {
+    int lo = 0, hi = batch - 1;      // largest b with cu[b] <= r
+    while (lo < hi) {
+        int mid = (lo + hi + 1) >> 1;
+        if ((int64_t)cu[mid] <= r) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+}  // namespace slikl

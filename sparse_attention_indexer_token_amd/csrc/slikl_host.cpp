@@ -1,0 +1,238 @@
+// Host side of the C ABI: descriptor validation, workspace planning and the
+// launch sequence.  Validation and planning touch no device, so they can be
+// exercised on a machine without a GPU.
+#include <hip/hip_runtime.h>
+
+#include <limits.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/slikl.h"
+#include "slikl_internal.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int head_tile(int64_t group) { return group <= 32 ? 32 : (group <= 64 ? 64 : 128); }
+
+int64_t rows_q(const slikl_desc *d) { return d->layout_q == SLIKL_LAYOUT_BSND ? d->batch * d->s1 : d->s1; }
+int64_t rows_k(const slikl_desc *d) { return d->layout_k == SLIKL_LAYOUT_BSND ? d->batch * d->s2 : d->s2; }
+
+// Field checks of the operator page's constraints section (dtypes, layouts,
+// cuSeqLens required for TND) and of this library's limits (N1 <= 128,
+// topk <= 2048 as for the 950-class products; D in {32, 64, 128}).
+slikl_status validate(const slikl_desc *d) {
+    if (!d) return SLIKL_ERR_NULLPTR;
+    if (d->layout_q != SLIKL_LAYOUT_BSND && d->layout_q != SLIKL_LAYOUT_TND) return SLIKL_ERR_PARAM_INVALID;
+    if (d->layout_k != SLIKL_LAYOUT_BSND && d->layout_k != SLIKL_LAYOUT_TND) return SLIKL_ERR_PARAM_INVALID;
+    if (d->dtype != SLIKL_DTYPE_F16 && d->dtype != SLIKL_DTYPE_BF16) return SLIKL_ERR_PARAM_INVALID;
+    if (d->deterministic != 0 && d->deterministic != 1) return SLIKL_ERR_PARAM_INVALID;
+    if (d->split_mode != SLIKL_SPLIT_WEIGHTED && d->split_mode != SLIKL_SPLIT_ROWS) return SLIKL_ERR_PARAM_INVALID;
+    if (d->num_parts < 0 || d->num_parts > SLIKL_MAX_PARTS) return SLIKL_ERR_PARAM_INVALID;
+    if (d->batch <= 0 || d->batch > INT32_MAX - 1) return SLIKL_ERR_PARAM_INVALID;
+    if (d->n1 < 1 || d->n1 > 128) return SLIKL_ERR_PARAM_INVALID;
+    if (d->n2 < 1 || d->n1 % d->n2 != 0) return SLIKL_ERR_PARAM_INVALID;
+    if (d->d != 32 && d->d != 64 && d->d != 128) return SLIKL_ERR_PARAM_INVALID;
+    if (d->topk < 1 || d->topk > 2048) return SLIKL_ERR_PARAM_INVALID;
+    if (d->layout_q == SLIKL_LAYOUT_TND && !d->cu_seqlens_q) return SLIKL_ERR_NULLPTR;
+    if (d->layout_k == SLIKL_LAYOUT_TND && !d->cu_seqlens_k) return SLIKL_ERR_NULLPTR;
+    if (d->layout_q == SLIKL_LAYOUT_BSND ? d->s1 <= 0 : d->s1 < 0) return SLIKL_ERR_PARAM_INVALID;
+    if (d->layout_k == SLIKL_LAYOUT_BSND ? d->s2 <= 0 : d->s2 < 0) return SLIKL_ERR_PARAM_INVALID;
+    // sizes that the kernels index with 32-bit values
+    const int64_t lim = (int64_t)INT32_MAX;
+    if (d->layout_q == SLIKL_LAYOUT_BSND && d->s1 > lim / d->batch) return SLIKL_ERR_PARAM_INVALID;
+    if (d->layout_k == SLIKL_LAYOUT_BSND && d->s2 > lim / d->batch) return SLIKL_ERR_PARAM_INVALID;
+    // every tensor must have fewer than 2^31 elements (32-bit offsets in the kernels)
+    const int64_t t1 = rows_q(d), t2 = rows_k(d);
+    if (t1 > lim / (d->n1 * d->d) || t1 > lim / (d->n2 * d->topk)) return SLIKL_ERR_PARAM_INVALID;
+    if (t2 > lim / (d->n2 * d->d)) return SLIKL_ERR_PARAM_INVALID;
+    return SLIKL_OK;
+}
+
+slikl::WorkspacePlan plan(const slikl_desc *d) {
+    slikl::WorkspacePlan p{};
+    const int64_t t1 = rows_q(d), t2 = rows_k(d);
+    const size_t acc_elem = d->deterministic ? 8 : 4;
+    size_t off = 0;
+    p.acc_off = off;
+    p.acc_bytes = (size_t)t2 * (size_t)d->n2 * (size_t)d->d * acc_elem;
+    off = align_up(off + p.acc_bytes);
+    p.meta_off = off;
+    off = align_up(off + SLIKL_METADATA_INTS * sizeof(int32_t));
+    p.prefix_off = off;
+    p.prefix_bytes = ((size_t)t1 * (size_t)d->n2 + 1) * sizeof(int64_t);
+    off = align_up(off + p.prefix_bytes);
+    p.flags_off = off;
+    off = align_up(off + 16);
+    p.scale_off = off;
+    off = align_up(off + 64);
+    p.k16_off = off;
+    p.k16_bytes = d->dtype == SLIKL_DTYPE_BF16 ? (size_t)t2 * (size_t)d->n2 * (size_t)d->d * 2 : 0;
+    off = align_up(off + p.k16_bytes);
+    p.total = off;
+    return p;
+}
+
+slikl::Problem problem(const slikl_desc *d) {
+    slikl::Problem pb{};
+    pb.t1 = rows_q(d);
+    pb.t2 = rows_k(d);
+    pb.s1 = d->s1;
+    pb.s2 = d->s2;
+    pb.batch = (int32_t)d->batch;
+    pb.n1 = (int32_t)d->n1;
+    pb.n2 = (int32_t)d->n2;
+    pb.group = (int32_t)(d->n1 / d->n2);
+    pb.d = (int32_t)d->d;
+    pb.topk = (int32_t)d->topk;
+    pb.layout_q = d->layout_q;
+    pb.layout_k = d->layout_k;
+    pb.cu_q = d->layout_q == SLIKL_LAYOUT_TND ? d->cu_seqlens_q : nullptr;
+    pb.cu_k = d->layout_k == SLIKL_LAYOUT_TND ? d->cu_seqlens_k : nullptr;
+    return pb;
+}
+
+slikl_status resolve_parts(const slikl_desc *d, int32_t *parts) {
+    if (d->num_parts > 0) {
+        *parts = d->num_parts;
+        return SLIKL_OK;
+    }
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SLIKL_ERR_LAUNCH;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return SLIKL_ERR_LAUNCH;
+    int per_cu = slikl::grad_fused_blocks_per_cu(head_tile(d->n1 / d->n2), (int)d->d,
+                                                 d->dtype == SLIKL_DTYPE_F16, d->deterministic != 0);
+    int64_t p = (int64_t)cus * per_cu;
+    if (p > SLIKL_MAX_PARTS) p = SLIKL_MAX_PARTS;
+    if (p < 1) p = 1;
+    *parts = (int32_t)p;
+    return SLIKL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *slikl_status_string(slikl_status s) {
+    switch (s) {
+        case SLIKL_OK: return "ok";
+        case SLIKL_ERR_NULLPTR: return "a required pointer is NULL";
+        case SLIKL_ERR_PARAM_INVALID: return "a descriptor field is out of range";
+        case SLIKL_ERR_UNSUPPORTED: return "configuration not supported";
+        case SLIKL_ERR_WORKSPACE: return "workspace missing or too small";
+        case SLIKL_ERR_LAUNCH: return "HIP launch or device query failed";
+    }
+    return "unknown status";
+}
+
+slikl_status slikl_grad_workspace_size(const slikl_desc *desc, size_t *bytes) {
+    if (!desc || !bytes) return SLIKL_ERR_NULLPTR;
+    slikl_status st = validate(desc);
+    if (st != SLIKL_OK) return st;
+    *bytes = plan(desc).total;
+    return SLIKL_OK;
+}
+
+slikl_status slikl_grad_parts(const slikl_desc *desc, int32_t *parts) {
+    if (!desc || !parts) return SLIKL_ERR_NULLPTR;
+    slikl_status st = validate(desc);
+    if (st != SLIKL_OK) return st;
+    return resolve_parts(desc, parts);
+}
+
+slikl_status slikl_grad_metadata(const slikl_desc *desc, const int32_t *sparse_indices, int32_t *metadata,
+                                 void *workspace, size_t workspace_bytes, void *stream) {
+    if (!desc || !metadata) return SLIKL_ERR_NULLPTR;
+    slikl_status st = validate(desc);
+    if (st != SLIKL_OK) return st;
+    if (desc->split_mode == SLIKL_SPLIT_WEIGHTED && !sparse_indices && rows_q(desc) > 0)
+        return SLIKL_ERR_NULLPTR;
+    slikl::WorkspacePlan wp = plan(desc);
+    if (!workspace || workspace_bytes < wp.total) return SLIKL_ERR_WORKSPACE;
+    int32_t parts = 0;
+    st = resolve_parts(desc, &parts);
+    if (st != SLIKL_OK) return st;
+    slikl::Problem pb = problem(desc);
+    pb.idx = sparse_indices;
+    if ((uintptr_t)workspace % 256 != 0) return SLIKL_ERR_WORKSPACE;
+    hipError_t e = slikl::launch_metadata(pb, parts, desc->split_mode, SLIKL_UNIT_OVERHEAD, metadata,
+                                          (int64_t *)((char *)workspace + wp.prefix_off),
+                                          (int32_t *)((char *)workspace + wp.flags_off), (hipStream_t)stream);
+    return e == hipSuccess ? SLIKL_OK : SLIKL_ERR_LAUNCH;
+}
+
+slikl_status slikl_grad(const slikl_desc *desc, const void *q, const void *k, const float *w,
+                        const int32_t *sparse_indices, const float *attn_softmax_l1norm,
+                        const int32_t *metadata, void *dq, void *dk, float *dw, float *softmax_out,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    if (!desc) return SLIKL_ERR_NULLPTR;
+    slikl_status st = validate(desc);
+    if (st != SLIKL_OK) return st;
+    const int64_t t1 = rows_q(desc), t2 = rows_k(desc);
+    if (t1 > 0 && (!q || !w || !sparse_indices || !attn_softmax_l1norm || !dq || !dw || !softmax_out))
+        return SLIKL_ERR_NULLPTR;
+    if (t2 > 0 && (!k || !dk)) return SLIKL_ERR_NULLPTR;
+    slikl::WorkspacePlan wp = plan(desc);
+    if (!workspace || workspace_bytes < wp.total || (uintptr_t)workspace % 256 != 0)
+        return SLIKL_ERR_WORKSPACE;
+    // 16-byte vector loads / stores of the 16-bit tensors
+    if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)dq | (uintptr_t)dk) % 16 != 0)
+        return SLIKL_ERR_PARAM_INVALID;
+    int32_t parts = 0;
+    st = resolve_parts(desc, &parts);
+    if (st != SLIKL_OK) return st;
+
+    hipStream_t s = (hipStream_t)stream;
+    char *ws = (char *)workspace;
+    const bool f16 = desc->dtype == SLIKL_DTYPE_F16;
+    const bool det = desc->deterministic != 0;
+
+    slikl::Problem pb = problem(desc);
+    pb.q = (const uint16_t *)q;
+    pb.k = (const uint16_t *)k;
+    pb.w = w;
+    pb.idx = sparse_indices;
+    pb.p = attn_softmax_l1norm;
+    pb.dq = (uint16_t *)dq;
+    pb.dk = (uint16_t *)dk;
+    pb.dw = dw;
+    pb.y = softmax_out;
+    pb.dk_acc = ws + wp.acc_off;
+    pb.det_scale = (const float *)(ws + wp.scale_off);
+    pb.k16 = f16 ? pb.k : (const uint16_t *)(ws + wp.k16_off);
+
+    hipError_t e = hipSuccess;
+    if (!metadata) {
+        int32_t *md = (int32_t *)(ws + wp.meta_off);
+        e = slikl::launch_metadata(pb, parts, desc->split_mode, SLIKL_UNIT_OVERHEAD, md,
+                                   (int64_t *)(ws + wp.prefix_off), (int32_t *)(ws + wp.flags_off), s);
+        if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
+        metadata = md;
+    }
+    pb.metadata = metadata;
+    e = slikl::launch_zero(pb.dk_acc, wp.acc_bytes, s);
+    if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
+    e = slikl::launch_zero(ws + wp.scale_off, 64, s);
+    if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
+    if (!f16 && t2 > 0) {
+        e = slikl::launch_k_to_f16(pb, (uint16_t *)(ws + wp.k16_off), (float *)(ws + wp.scale_off), s);
+        if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
+    }
+    if (det) {
+        e = slikl::launch_det_scale(pb, f16, (float *)(ws + wp.scale_off), s);
+        if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
+    }
+    if (t1 > 0) {
+        e = slikl::launch_grad_fused(pb, head_tile(pb.group), f16, det, parts, s);
+        if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
+    }
+    e = slikl::launch_finalize_dk(pb, f16, det, s);
+    if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
+    return SLIKL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,55 @@
+// Internal declarations shared by the host dispatcher and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace slikl {
+
+// Everything a kernel needs about one call, passed by value.
+struct Problem {
+    const uint16_t *q;       // [T1, N1, D] 16-bit
+    const uint16_t *k;       // [T2, N2, D] 16-bit
+    const float *w;          // [T1, N1]
+    const int32_t *idx;      // [T1, N2, topk]
+    const float *p;          // [T1, N2, topk]
+    const int32_t *metadata; // SLIKL_METADATA_INTS
+    uint16_t *dq;            // [T1, N1, D]
+    uint16_t *dk;            // [T2, N2, D]
+    float *dw;               // [T1, N1]
+    float *y;                // softmax_out [T1, N2, topk]
+    void *dk_acc;            // fp32 or int64 accumulator [T2, N2, D]
+    const float *det_scale;  // scale block: [0] 2^F, [1] 2^-F (deterministic), [6] 2^-eK
+    const uint16_t *k16;     // fp16 keys for the dq / dK-part contractions ([T2, N2, D])
+    const int32_t *cu_q;     // [batch + 1] or null (BSND)
+    const int32_t *cu_k;     // [batch + 1] or null (BSND)
+    int64_t s1, s2;          // BSND per-batch lengths (unused for TND sides)
+    int64_t t1, t2;          // total query / key rows
+    int32_t batch, n1, n2, group, d, topk;
+    int32_t layout_q, layout_k;
+};
+
+// Workspace carve-up (byte offsets), identical for every call with one desc.
+struct WorkspacePlan {
+    size_t acc_off, acc_bytes;      // dK accumulator
+    size_t meta_off;                // internal metadata (SLIKL_METADATA_INTS int32)
+    size_t prefix_off, prefix_bytes;// int64 unit-cost prefix, U + 1 entries
+    size_t flags_off;               // metadata error flags found while counting (16 bytes)
+    size_t scale_off;               // scale block (16 x 32-bit)
+    size_t k16_off, k16_bytes;      // fp16 copy of k (bf16 inputs only)
+    size_t total;
+};
+
+// Kernel launchers (defined in the .hip files).  Return hipSuccess or the error.
+hipError_t launch_grad_fused(const Problem &pb, int hp, bool f16, bool det, int grid,
+                             hipStream_t stream);
+int grad_fused_blocks_per_cu(int hp, int d, bool f16, bool det);
+hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t stream);
+hipError_t launch_finalize_dk(const Problem &pb, bool f16, bool det, hipStream_t stream);
+hipError_t launch_det_scale(const Problem &pb, bool f16, float *scale_block, hipStream_t stream);
+hipError_t launch_k_to_f16(const Problem &pb, uint16_t *k16, float *scale_block, hipStream_t stream);
+hipError_t launch_metadata(const Problem &pb, int parts, int mode, int overhead,
+                           int32_t *metadata, int64_t *prefix, int32_t *flags, hipStream_t stream);
+
+}  // namespace slikl

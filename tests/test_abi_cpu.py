@@ -1,0 +1,129 @@
+"""C ABI checks that need no GPU: exported symbols and host-side validation.
+
+slikl_grad_workspace_size touches no device, so every status path of the
+descriptor validation is exercised here.  Compute entry points are only
+called with descriptors that fail validation (they return before any HIP
+call).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_attention_indexer_token_amd import _native
+from sparse_attention_indexer_token_amd._native import SliklDesc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "slikl.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_native.LIB_PATH):
+        pytest.skip("libslikl.so not built")
+    return _native.load()
+
+
+def header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\S.*?\b(slikl_\w+)\(", text, flags=re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert header_functions() == sorted(_native.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", _native.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    names = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for fn in header_functions():
+        assert fn in names, fn
+        assert getattr(lib, fn) is not None
+
+
+def test_struct_layout_matches_header():
+    # 4 x int32, 7 x int64, 2 pointers, 2 x int32
+    assert ctypes.sizeof(SliklDesc) == 96
+    assert SliklDesc.cu_seqlens_q.offset == 72
+    assert SliklDesc.num_parts.offset == 88
+
+
+def good_desc(**kw):
+    d = SliklDesc()
+    d.layout_q = d.layout_k = 0
+    d.dtype = 1
+    d.deterministic = 0
+    d.batch, d.s1, d.s2 = 1, 4096, 4096
+    d.n1, d.n2, d.d, d.topk = 64, 1, 128, 2048
+    d.cu_seqlens_q = d.cu_seqlens_k = None
+    d.num_parts = 0
+    d.split_mode = 0
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def ws(lib, d):
+    n = ctypes.c_size_t(0)
+    st = lib.slikl_grad_workspace_size(ctypes.byref(d), ctypes.byref(n))
+    return st, n.value
+
+
+def test_workspace_size_of_the_dsv32_shape(lib):
+    st, n = ws(lib, good_desc())
+    assert st == 0
+    acc = 4096 * 1 * 128 * 4
+    assert n >= acc + 2080 * 4 + (4096 + 1) * 8
+    st, n_det = ws(lib, good_desc(deterministic=1))
+    assert st == 0 and n_det >= n + 4096 * 128 * 4
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("layout_q", 2, 2), ("layout_k", -1, 2), ("dtype", 5, 2), ("deterministic", 2, 2),
+    ("batch", 0, 2), ("s1", 0, 2), ("s2", 0, 2), ("n1", 0, 2), ("n1", 129, 2),
+    ("n2", 3, 2), ("n2", 0, 2), ("d", 96, 2), ("d", 256, 2), ("topk", 0, 2), ("topk", 2049, 2),
+    ("num_parts", 2049, 2), ("num_parts", -1, 2), ("split_mode", 2, 2),
+    ("layout_q", 1, 1),                      # TND q without cu_seqlens_q
+    ("layout_k", 1, 1),                      # TND k without cu_seqlens_k
+    ("s1", 1 << 40, 2),                      # more than 2^31 elements
+])
+def test_validation_status(lib, field, value, status):
+    st, _ = ws(lib, good_desc(**{field: value}))
+    assert st == status
+
+
+def test_tnd_total_may_be_zero(lib):
+    cu = (ctypes.c_int32 * 2)(0, 0)
+    d = good_desc(layout_q=1, layout_k=1, s1=0, s2=0)
+    d.cu_seqlens_q = ctypes.cast(cu, ctypes.c_void_p)
+    d.cu_seqlens_k = ctypes.cast(cu, ctypes.c_void_p)
+    st, n = ws(lib, d)
+    assert st == 0 and n > 0
+
+
+def test_null_pointers(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.slikl_grad_workspace_size(None, ctypes.byref(n)) == 1
+    d = good_desc()
+    assert lib.slikl_grad_workspace_size(ctypes.byref(d), None) == 1
+    # execute entry points: null tensors fail before any device work
+    assert lib.slikl_grad(ctypes.byref(d), *([None] * 10), None, 0, None) == 1
+    assert lib.slikl_grad_metadata(ctypes.byref(d), None, None, None, 0, None) == 1
+
+
+def test_small_workspace_is_rejected_before_launch(lib):
+    d = good_desc(num_parts=4)
+    fake = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
+    st = lib.slikl_grad(ctypes.byref(d), *([fake] * 10), fake, 16, None)
+    assert st == 4
+    st = lib.slikl_grad_metadata(ctypes.byref(d), fake, fake, fake, 16, None)
+    assert st == 4
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.slikl_status_string(s)
+    assert b"unknown" in lib.slikl_status_string(99)

@@ -1,0 +1,192 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Small cases are compared element by element on every output; they span
+several chunks, ragged tails, every head-tile width (32/64/128 padded heads),
+D in {32, 64, 128}, fp16 and bf16, N2 = 2, TND with an empty sequence,
+duplicates, interleaved -1, rows without any valid slot and topk = 1.
+The five headline workloads run at full size in the benchmark's launch
+configuration; there the oracle checks sampled rows (dq, dw, softmax_out) and
+sampled keys whose referencing rows are few (dk exactly, from those rows).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from workloads import WORKLOADS, Workload, make_inputs
+from tests.gpu_helpers import (check_close, keys_with_few_refs, oracle, run_gpu, to_device)
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import sparse_attention_indexer_token_amd as slikl
+    slikl.load()          # fail loudly when the library is missing
+
+
+def W(**kw):
+    base = dict(name="case", layout="BSND", batch=1, s1=64, s2=64, n1=8, n2=1, d=32, topk=16,
+                dtype="bf16", w_var=0.5, index_mode="causal", p_var=1.0, seed=7)
+    base.update(kw)
+    return Workload(**base)
+
+
+SMALL = {
+    "tiny_causal": WORKLOADS["tiny_causal"],
+    "hp64_d128_ragged": W(batch=2, s1=150, s2=170, n1=64, d=128, topk=200, w_var=1 / 8, p_var=2.0),
+    "hp32_d128_f16_dups": W(s1=120, s2=130, n1=32, d=128, topk=300, dtype="f16", w_var=1 / 8,
+                            index_mode="random", invalid_frac=0.3, duplicates=True),
+    "hp128_d64": W(s1=70, s2=90, n1=128, d=64, topk=100, w_var=1 / 16, index_mode="random",
+                   invalid_frac=0.1),
+    "hp64_d64_n2": W(batch=2, s1=40, s2=60, n1=128, n2=2, d=64, topk=96, w_var=1 / 8),
+    "g8_d32_tnd": W(layout="TND", seqlens=(50, 1, 0, 90), n1=8, d=32, topk=40),
+    "f16_dirichlet_tnd": W(layout="TND", seqlens=(130, 70), n1=64, d=128, topk=128, dtype="f16",
+                           w_var=1 / 8, p_mode="dirichlet", p_alpha=0.1),
+    "topk1": W(s1=50, s2=50, n1=16, d=64, topk=1),
+    "no_valid_rows": W(s1=30, s2=30, n1=32, d=32, topk=24, index_mode="random", invalid_frac=1.0),
+    "sink_zipf_small": W(batch=2, s1=200, s2=200, n1=16, d=128, topk=64, index_mode="sink_zipf",
+                         invalid_frac=0.1, sink_keys=8, w_var=0.25),
+    "g1_d128": W(s1=40, s2=40, n1=1, d=128, topk=33),
+    "g100_d32": W(s1=20, s2=50, n1=100, d=32, topk=70, w_var=1 / 16),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("det", [False, True])
+def test_small_parity(name, det):
+    _say(f"[parity] {name} det={det}")
+    x = make_inputs(SMALL[name])
+    got = run_gpu(x, deterministic=det)
+    ref = oracle(x)
+    check_close(got, ref, label=name)
+    if name == "no_valid_rows":
+        assert np.all(got["dq"] == 0) and np.all(got["dk"] == 0) and np.all(got["softmax_out"] == 0)
+
+
+def test_metadata_matches_reference():
+    """Integer metadata: bit-exact against the reference split, both modes."""
+    import torch
+    import sparse_attention_indexer_token_amd as slikl
+    from oracle.metadata_ref import metadata_ref
+    for name in ("hp64_d128_ragged", "g8_d32_tnd", "sink_zipf_small"):
+        x = make_inputs(SMALL[name])
+        t = to_device(x)
+        for mode, parts in (("weighted", 37), ("rows", 37), ("weighted", 1), ("rows", 2048)):
+            _say(f"[metadata] {name} {mode} {parts}")
+            md = slikl.slikl_grad_metadata(t["q"], t["k"], t["idx"], layout_q=x.layout_q,
+                                           layout_k=x.layout_k, cu_seqlens_q=t["cu_q"],
+                                           cu_seqlens_k=t["cu_k"], num_parts=parts, split_mode=mode)
+            torch.cuda.synchronize()
+            want = metadata_ref(layout_q=x.layout_q, layout_k=x.layout_k, batch=x.batch,
+                                s1=x.s1, s2=x.s2, n2=x.wl.n2, topk=x.wl.topk, parts=parts,
+                                mode=0 if mode == "weighted" else 1, overhead=slikl.UNIT_OVERHEAD,
+                                cu_seqlens_q=x.cu_q, cu_seqlens_k=x.cu_k,
+                                sparse_indices=x.idx.reshape(-1, x.wl.n2, x.wl.topk))
+            assert np.array_equal(md.cpu().numpy(), want)
+
+
+def test_results_do_not_depend_on_metadata():
+    import torch
+    import sparse_attention_indexer_token_amd as slikl
+    x = make_inputs(SMALL["hp64_d128_ragged"])
+    t = to_device(x)
+    base = run_gpu(x, t)
+    base_det = run_gpu(x, t, deterministic=True)
+    for mode, parts in (("rows", 3), ("weighted", 5), ("rows", 2048), ("weighted", 1)):
+        _say(f"[metadata-independence] {mode} {parts}")
+        md = slikl.slikl_grad_metadata(t["q"], t["k"], t["idx"], num_parts=parts, split_mode=mode)
+        got = run_gpu(x, t, metadata=md, num_parts=parts)
+        for name in ("dq", "dw", "softmax_out"):
+            assert np.array_equal(got[name], base[name]), name
+        check_close(got, oracle(x), what=("dk",))
+        got_det = run_gpu(x, t, deterministic=True, metadata=md, num_parts=parts)
+        for name in ("dq", "dk", "dw", "softmax_out"):
+            assert np.array_equal(got_det[name], base_det[name]), name
+    torch.cuda.synchronize()
+
+
+def test_deterministic_mode_is_bitwise_reproducible():
+    import torch
+    x = make_inputs(SMALL["sink_zipf_small"])
+    t = to_device(x)
+    first = run_gpu(x, t, deterministic=True)
+    s = torch.cuda.Stream()
+    for i in range(6):
+        if i % 2:
+            with torch.cuda.stream(s):
+                again = run_gpu(x, t, deterministic=True)
+        else:
+            again = run_gpu(x, t, deterministic=True)
+        for name in first:
+            assert np.array_equal(first[name], again[name]), (i, name)
+    check_close(first, run_gpu(x, t, deterministic=False), what=("dk",))
+
+
+def test_slot_order_and_padding_invariance():
+    x = make_inputs(SMALL["hp64_d128_ragged"])
+    a = run_gpu(x)
+    perm = np.random.default_rng(5).permutation(x.idx.shape[-1])
+    x2 = make_inputs(SMALL["hp64_d128_ragged"])
+    x2.idx = np.ascontiguousarray(x2.idx[..., perm])
+    x2.p = np.ascontiguousarray(x2.p[..., perm])
+    b = run_gpu(x2)
+    check_close(b, dict(a, softmax_out=a["softmax_out"][..., perm]), what=("softmax_out",))
+    for name in ("dq", "dw"):
+        assert np.allclose(a[name], b[name], rtol=1e-2, atol=1e-3)
+
+
+def test_out_of_range_index_is_skipped_and_flagged():
+    import torch
+    import sparse_attention_indexer_token_amd as slikl
+    x = make_inputs(SMALL["hp64_d128_ragged"])
+    x.idx[0, 5, 0, 0] = 10_000           # outside [0, S2)
+    x.idx[1, 7, 0, 1] = -7               # negative, not -1
+    t = to_device(x)
+    got = run_gpu(x, t)
+    md = slikl.slikl_grad_metadata(t["q"], t["k"], t["idx"], num_parts=8)
+    torch.cuda.synchronize()
+    assert md[8].item() & 4
+    x.idx[0, 5, 0, 0] = -1
+    x.idx[1, 7, 0, 1] = -1
+    check_close(got, oracle(x), label="out-of-range skipped")
+
+
+FULL = ["tiny_causal", "dsv32_indexer", "long_context", "contention_det", "varlen_tnd"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled(name):
+    """Headline workloads at full size, default launch (weighted metadata)."""
+    _say(f"[full] generating {name}")
+    x = make_inputs(WORKLOADS[name])
+    _say(f"[full] running {name} T1={x.t1} valid={x.valid_slots}")
+    got = run_gpu(x)
+    rng = np.random.default_rng(11)
+    rows = np.sort(rng.choice(x.t1, size=min(24, x.t1), replace=False))
+    rows = np.unique(np.concatenate([rows, [0, x.t1 - 1]]))
+    ref = oracle(x, rows=rows)
+    check_close(got, ref, rows=rows, what=("dq", "dw", "softmax_out"), label=name)
+    refs = keys_with_few_refs(x, max_rows=6, want=24)
+    assert refs, "no sparsely referenced keys found"
+    all_rows = np.unique(np.concatenate(list(refs.values())))
+    ref_k = oracle(x, rows=all_rows)
+    n2 = x.k.shape[-2]
+    gk = got["dk"].reshape(-1, n2, x.k.shape[-1])
+    rk = ref_k["dk"].reshape(-1, n2, x.k.shape[-1])
+    keys = np.array(sorted(refs))
+    check_close({"dk": gk[keys]}, {"dk": rk[keys]}, what=("dk",), label=f"{name} dk")
+    # global invariants at full size
+    y = got["softmax_out"]
+    valid = x.idx >= 0
+    assert np.all(y[~valid] == 0)
+    sums = y.sum(-1)[valid.any(-1)]
+    assert np.max(np.abs(sums - 1)) < 1e-4
