@@ -125,6 +125,20 @@ __device__ __forceinline__ float block_sum(float v, float *red) {
     return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
+__device__ __forceinline__ int block_max_int(int v, int *red) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        int x = __shfl_xor(v, o);
+        v = x > v ? x : v;
+    }
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    int a = red[0] > red[1] ? red[0] : red[1];
+    int b = red[2] > red[3] ? red[2] : red[3];
+    return a > b ? a : b;
+}
+
 // Exclusive prefix sum over the block; `tmp` holds >= 4 ints.
 __device__ __forceinline__ int block_excl_scan(int v, int *tmp, int *total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

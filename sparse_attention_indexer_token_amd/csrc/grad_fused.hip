@@ -9,30 +9,31 @@
 //
 // One workgroup (4 wavefronts) processes one (query row, key head) unit at a
 // time, for the units of the metadata parts it owns:
-//   setup   compact the valid slots (index, slot id, p) into LDS; q rows into
-//           registers in two MFMA operand layouts (A of S, B of the dK part).
-//   pass 1  for each chunk of KC compacted slots: gather the K rows into LDS,
-//           S tile (32 heads x 32 keys) per wave on MFMA, ReLU, the partial
-//           head sum of I, S > 0 bit masks (ballots) into LDS, and the
-//           per-lane online sums A_h = sum e^{I-m} R_h, B_h = sum p R_h.
-//   softmax m, Z over the row; y -> softmax_out; dI = y - p into LDS;
-//           dW_h = A_h / Z - B_h.
-//   pass 2  for each chunk: gather K again, dS tile from masks, w and dI into
-//           LDS as [key][head]; dq += dS K (transposing LDS reads feed both
-//           operands); P = dS^T q per key on MFMA, scatter-added into the
-//           dK accumulator (fp32 atomics, or int64 fixed-point atomics in the
-//           deterministic mode).
-// Pass 2 runs its two contractions on fp16 MFMA for both input dtypes: dS is
-// rounded to fp16 (11 significant bits; one bf16 rounding, 8 bits, is too
-// coarse for the elementwise dq tolerance where terms cancel) after a per-unit
-// power-of-two prescale that puts max |dS| just below 2^15.  The dK part sums
-// parts of many query rows whose sum can cancel far below their magnitudes,
-// so it also multiplies the fp16 remainder dS - fp16(dS): two MFMAs per step,
-// about 22 significant bits for dS.  bf16
-// keys come from an fp16 copy made once per call with a global power-of-two
-// scale, bf16 queries are converted per unit with their own power of two; all
-// scales are undone exactly on the fp32 results.  Pass 1 (S) runs on the
-// input dtype's MFMA with the inputs as given.
+//   setup   compact the valid slots (key row, slot id) into LDS; the q rows
+//           into registers as the A operand of S.
+//   pass 1  chunks of KC compacted slots; the K rows of chunk c+1 are copied
+//           straight from global memory into an LDS double buffer
+//           (global_load_lds) while chunk c runs: S tile (32 heads x 32 keys)
+//           per wave on MFMA, ReLU, the per-head-tile partial of I, the S > 0
+//           ballots.  One barrier per chunk.
+//   softmax m, Z over the row; y -> softmax_out; dI = y - p.
+//   pass 2  chunks again over fp16 keys: the tile dI[s] 1[S > 0] (fp16, after a
+//           per-unit power-of-two prescale) goes to LDS as [key][head];
+//           U = sum_s dI 1[S>0] K on MFMA with transposing LDS reads feeding
+//           both operands.  dq = w U and, because U q = sum_s dI ReLU(S),
+//           dW = <q, U> per head: one dot product per row instead of per-slot
+//           bookkeeping.
+//   dK      scatter mode: P'[s,:] = sum_h 1[S>0] w_h q_h on MFMA (the 0/1 mask is
+//           exact in fp16; w is split into fp16 high and low parts, two MFMAs),
+//           P = dI_s P' in fp32, added into the dK accumulator with fp32
+//           atomics or, deterministic, int64 fixed-point atomics.
+//           dense mode: the kernel instead writes per (unit, key) records (dI and
+//           the S > 0 head mask) for the key-major dK kernel.
+// fp16 MFMA for pass 2 with both input dtypes: one bf16 rounding (8
+// significant bits) of dS is too coarse for the elementwise dq tolerance where
+// terms cancel; fp16 keeps 11.  bf16 keys come from an fp16 copy made once
+// per call with a global power-of-two scale, bf16 queries are converted per
+// unit with their own power of two; every scale is undone exactly in fp32.
 #include "device_common.h"
 #include "slikl_internal.h"
 
@@ -46,33 +47,56 @@ struct FusedCfg {
     static constexpr int NDT = D / 32;           // 32-wide d tiles
     static constexpr int DCH = D / 8;            // 16-byte chunks per K / q row
     static constexpr int HCH = HP / 8;           // 16-byte chunks per dS row
-    static constexpr int PIECES = KC * DCH;      // 16-byte pieces per K chunk
-    static constexpr int NPF = (PIECES + kBlock - 1) / kBlock;
+    static constexpr int RPB = 1024 / (2 * D);   // K rows per 1 KiB direct-to-LDS block
+    static constexpr int NB = KC * D * 2 / 1024; // 1 KiB blocks per K chunk
+    static constexpr int NBW = (NB + 3) / 4;     // blocks per wave
+    static constexpr int KBUF = KC * D * 2;      // bytes of one K chunk buffer
     static constexpr int NQ_TILES = NH * NDT;    // dq tiles
     static constexpr int NQW = (NQ_TILES + 3) / 4;
     static constexpr int NP_TILES = NKT * NDT;   // dK-part tiles per chunk
     static constexpr int NPW = (NP_TILES + 3) / 4;
     static constexpr int TOPK_MAX = 2048;
-    static constexpr int QROWS = HP > KC ? HP : KC;
+    // shared scratch: two K chunk buffers; also holds the q rows (16-bit) and
+    // one head tile of U (fp32) at the unit's start / end
+    static constexpr int S0 = 2 * KBUF > HP * D * 2 ? 2 * KBUF : HP * D * 2;
+    static constexpr int SCR = S0 > 32 * D * 4 ? S0 : 32 * D * 4;
     static_assert(HP == 32 || HP == 64 || HP == 128, "head tile");
     static_assert(D == 32 || D == 64 || D == 128, "head dim");
 };
 
-template <int HP, int D, bool F16, bool DET>
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// v if bit `lane` of the wave-uniform mask is set, else 0 (bit patterns).
+__device__ __forceinline__ uint32_t select_bits(uint32_t v, uint64_t mask) {
+    uint32_t r;
+    asm("v_cndmask_b32_e64 %0, 0, %1, %2" : "=v"(r) : "v"(v), "s"(mask));
+    return r;
+}
+
+__device__ __forceinline__ int pow2_exponent_below_2p15(float amax) {
+    // e such that amax * 2^e < 2^15 (0 for zero or non-finite amax), clamped
+    if (!(amax > 0.f) || !(amax < INFINITY)) return 0;
+    int ex;
+    frexpf(amax, &ex);
+    int e = 15 - ex;
+    return e > 100 ? 100 : (e < -100 ? -100 : e);
+}
+
+template <int HP, int D, bool F16, int DKM>
 __global__ __launch_bounds__(kBlock, (HP == 128 ? 1 : 2)) void grad_fused_kernel(Problem pb) {
     using C = FusedCfg<HP, D>;
     constexpr int NH = C::NH, NKT = C::NKT, KC = C::KC, DCH = C::DCH, HCH = C::HCH;
+    constexpr bool DENSE = DKM == 2;
+    constexpr bool DET = DKM == 1;
 
-    __shared__ __attribute__((aligned(16))) char s_kq[C::QROWS * D * 2];  // K chunk / q rows
-    __shared__ __attribute__((aligned(16))) char s_ds[KC * HP * 2];       // dS chunk [key][head], fp16
-    __shared__ __attribute__((aligned(16))) char s_dsl[KC * HP * 2];      // dS - fp16(dS), fp16
+    __shared__ __attribute__((aligned(1024))) char s_scr[C::SCR];        // K chunks / q / U
+    __shared__ __attribute__((aligned(16))) char s_ds[KC * HP * 2];       // dI*1[S>0] [key][head]
     __shared__ int32_t s_key[C::TOPK_MAX];                                // compacted key rows
     __shared__ uint16_t s_slot[C::TOPK_MAX];                              // compacted slot ids
-    __shared__ float s_p[C::TOPK_MAX];                                    // compacted p
     __shared__ float s_I[C::TOPK_MAX];                                    // I, then dI
     __shared__ uint64_t s_mask[(C::TOPK_MAX / 32) * NH * 16];             // S > 0 ballots
-    __shared__ float s_ipart[NH * KC];
-    __shared__ float s_dw[NKT * HP];
+    __shared__ float s_ipart[2][NH * KC];
     __shared__ float s_w[HP];
     __shared__ float s_red[8];
     __shared__ int s_itmp[8];
@@ -122,7 +146,6 @@ __global__ __launch_bounds__(kBlock, (HP == 128 ? 1 : 2)) void grad_fused_kernel
             const int32_t *irow = pb.idx + u * topk;
             const float *prow = pb.p + u * topk;
             float *yrow = pb.y + u * topk;
-            const int rq = r;
             const int spt = (topk + kBlock - 1) / kBlock;
             const int s0 = tid * spt;
             int cnt = 0;
@@ -141,9 +164,8 @@ __global__ __launch_bounds__(kBlock, (HP == 128 ? 1 : 2)) void grad_fused_kernel
                 if (s < topk) {
                     int v = irow[s];
                     if (v >= 0 && v < klen) {
-                        s_key[pos] = (int32_t)(kbase + v);
+                        s_key[pos] = kbase + v;
                         s_slot[pos] = (uint16_t)s;
-                        s_p[pos] = prow[s];
                         ++pos;
                     }
                 }
@@ -152,118 +174,120 @@ __global__ __launch_bounds__(kBlock, (HP == 128 ? 1 : 2)) void grad_fused_kernel
             for (int j = nvalid + tid; j < nchunks * KC; j += kBlock) {
                 s_key[j] = -1;
                 s_slot[j] = 0;
-                s_p[j] = 0.f;
             }
 
             // ---- q rows of this key head -> LDS (rows = heads, zero past G) -------
-            const uint16_t *qrow = pb.q + (rq * pb.n1 + g * G) * D;
-            auto load_q = [&]() {
-                for (int pc = tid; pc < HP * DCH; pc += kBlock) {
-                    int h = pc / DCH, cc = pc % DCH;
-                    u32x4 v = {0u, 0u, 0u, 0u};
-                    if (h < G) v = *(const u32x4 *)(qrow + h * D + cc * 8);
-                    *(u32x4 *)(s_kq + tile_off<DCH>(h, cc * 8)) = v;
-                }
-            };
-            load_q();
-            for (int h = tid; h < HP; h += kBlock) s_w[h] = h < G ? pb.w[rq * pb.n1 + g * G + h] : 0.f;
-            __syncthreads();
-            // head weights in the S-tile row order of this lane
-            float wv[16];
-            float wabs = 0.f;
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                wv[j] = s_w[32 * hb1 + 8 * (j >> 2) + 4 * half + (j & 3)];
-                wabs = fmaxf(wabs, fabsf(wv[j]));
+            const uint16_t *qrow = pb.q + (r * pb.n1 + g * G) * D;
+            for (int pc = tid; pc < HP * DCH; pc += kBlock) {
+                int h = pc / DCH, cc = pc % DCH;
+                u32x4 v = {0u, 0u, 0u, 0u};
+                if (h < G) v = *(const u32x4 *)(qrow + h * D + cc * 8);
+                *(u32x4 *)(s_scr + tile_off<DCH>(h, cc * 8)) = v;
             }
+            for (int h = tid; h < HP; h += kBlock) s_w[h] = h < G ? pb.w[r * pb.n1 + g * G + h] : 0.f;
+            __syncthreads();
+            float wv[16];                     // head weights in the S-tile row order
+#pragma unroll
+            for (int j = 0; j < 16; ++j) wv[j] = s_w[32 * hb1 + 8 * (j >> 2) + 4 * half + (j & 3)];
             u32x4 qa[D / 16];                 // A operand of S: rows = heads, k = d
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks)
-                qa[ks] = *(const u32x4 *)(s_kq + tile_off<DCH>(32 * hb1 + l32, 16 * ks + 8 * half));
-            __syncthreads();   // s_kq is reused for K chunks below
+                qa[ks] = *(const u32x4 *)(s_scr + tile_off<DCH>(32 * hb1 + l32, 16 * ks + 8 * half));
+            __syncthreads();   // s_scr is reused for K chunks below
+
+            // ---- direct-to-LDS K gather --------------------------------------------
+            // Block b (1 KiB) of chunk c holds K rows b*RPB .. +RPB; lane l writes
+            // physical 16-byte chunk l % DCH of row b*RPB + l / DCH, i.e. logical chunk
+            // (l % DCH) ^ swizzle(row).  Padding slots read 16 zero bytes.
+            int krow_pre[C::NBW];
+            auto read_keys = [&](int c) {
+#pragma unroll
+                for (int i = 0; i < C::NBW; ++i) {
+                    const int blk = wave + 4 * i;
+                    const int row = blk * C::RPB + lane / DCH;
+                    krow_pre[i] = blk < C::NB ? s_key[c * KC + row] : -1;
+                }
+            };
+            auto issue_chunk = [&](const uint16_t *ksrc, int buf) {
+#pragma unroll
+                for (int i = 0; i < C::NBW; ++i) {
+                    const int blk = wave + 4 * i;
+                    if (blk < C::NB) {
+                        const int row = blk * C::RPB + lane / DCH;
+                        constexpr int smask = DCH >= 8 ? 7 : DCH - 1;
+                        const int swz = (((row & 3) << 1) ^ ((row >> 2) & 1)) & smask;
+                        const int lc = (lane % DCH) ^ swz;
+                        const int kr = krow_pre[i];
+                        const uint16_t *src = kr >= 0 ? ksrc + (kr * pb.n2 + g) * D + lc * 8 : pb.zero16;
+                        __builtin_amdgcn_global_load_lds((glb_void_t *)src,
+                                                         (lds_void_t *)(s_scr + buf * C::KBUF + blk * 1024),
+                                                         16, 0, 0);
+                    }
+                }
+            };
 
             // ---- pass 1 ---------------------------------------------------------------
-            u32x4 pf[C::NPF];
-            auto issue_gather = [&](const uint16_t *ksrc, int c) {
+            auto combine_I = [&](int c) {      // I of chunk c from the per-head-tile partials
+                if (tid < KC) {
+                    float I = 0.f;
 #pragma unroll
-                for (int i = 0; i < C::NPF; ++i) {
-                    int pc = tid + kBlock * i;
-                    u32x4 v = {0u, 0u, 0u, 0u};
-                    if (pc < C::PIECES) {
-                        int kk = pc / DCH, cc = pc % DCH;
-                        int kr = s_key[c * KC + kk];
-                        if (kr >= 0)
-                            v = *(const u32x4 *)(ksrc + (kr * pb.n2 + g) * D + cc * 8);
-                    }
-                    pf[i] = v;
+                    for (int hb = 0; hb < NH; ++hb) I += s_ipart[c & 1][hb * KC + tid];
+                    const int cpos = c * KC + tid;
+                    s_I[cpos] = s_key[cpos] >= 0 ? I : -INFINITY;
                 }
             };
-            auto store_gather = [&]() {
-#pragma unroll
-                for (int i = 0; i < C::NPF; ++i) {
-                    int pc = tid + kBlock * i;
-                    if (pc < C::PIECES) {
-                        int kk = pc / DCH, cc = pc % DCH;
-                        *(u32x4 *)(s_kq + tile_off<DCH>(kk, cc * 8)) = pf[i];
-                    }
-                }
-            };
-
-            float m_run = -INFINITY;
-            float accA[16], accB[16];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) { accA[j] = 0.f; accB[j] = 0.f; }
-
-            if (nchunks > 0) issue_gather(pb.k, 0);
+            int kmin = 0x7fffffff, kmax = -1;   // dense records: batch-relative key range
+            if (nchunks > 0) {
+                read_keys(0);
+                issue_chunk(pb.k, 0);
+                if (nchunks > 1) read_keys(1);
+            }
             for (int c = 0; c < nchunks; ++c) {
-                store_gather();
-                if (c + 1 < nchunks) issue_gather(pb.k, c + 1);
+                __builtin_amdgcn_s_waitcnt(0x0f70);     // vmcnt(0): chunk c landed in LDS
                 __syncthreads();
+                if (c + 1 < nchunks) issue_chunk(pb.k, (c + 1) & 1);
+                if (c + 2 < nchunks) read_keys(c + 2);
+                if (c > 0) combine_I(c - 1);
+                const char *kb = s_scr + (c & 1) * C::KBUF;
                 f32x16 sacc = {};
 #pragma unroll
                 for (int ks = 0; ks < D / 16; ++ks) {
-                    u32x4 bk = *(const u32x4 *)(s_kq + tile_off<DCH>(32 * kb1 + l32, 16 * ks + 8 * half));
+                    u32x4 bk = *(const u32x4 *)(kb + tile_off<DCH>(32 * kb1 + l32, 16 * ks + 8 * half));
                     sacc = mfma32<F16>(qa[ks], bk, sacc);
                 }
-                float R[16];
+                const int cpos = c * KC + 32 * kb1 + l32;
+                const int mykey = s_key[cpos];
+                if (mykey < 0) sacc = f32x16{};       // padding slot: no score, no mask bit
                 float ip = 0.f;
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    R[j] = fmaxf(sacc[j], 0.f);
-                    ip = fmaf(wv[j], R[j], ip);
-                }
+                for (int j = 0; j < 16; ++j) ip = fmaf(wv[j], fmaxf(sacc[j], 0.f), ip);
                 ip += __shfl_xor(ip, 32);
+                if (half == 0) s_ipart[c & 1][hb1 * KC + 32 * kb1 + l32] = ip;
                 uint64_t bal[16];
 #pragma unroll
                 for (int j = 0; j < 16; ++j) bal[j] = __ballot(sacc[j] > 0.f);
-                if (half == 0) s_ipart[hb1 * KC + 32 * kb1 + l32] = ip;
-                if (lane == 0) {
-                    uint64_t *mw = s_mask + ((c * NKT + kb1) * NH + hb1) * 16;
+                if (lane < 16) {
+                    uint64_t bw = bal[0];
 #pragma unroll
-                    for (int j = 0; j < 16; ++j) mw[j] = bal[j];
+                    for (int j = 1; j < 16; ++j) bw = lane == j ? bal[j] : bw;
+                    s_mask[((c * NKT + kb1) * NH + hb1) * 16 + lane] = bw;
                 }
-                __syncthreads();
-                const int cpos = c * KC + 32 * kb1 + l32;
-                const bool valid = s_key[cpos] >= 0;
-                float I = 0.f;
+                if constexpr (DENSE) {
+                    // head mask of this lane's key for its 16 heads, bit (half*16 + j)
+                    uint32_t m16 = 0;
 #pragma unroll
-                for (int hb = 0; hb < NH; ++hb) I += s_ipart[hb * KC + 32 * kb1 + l32];
-                if (!valid) I = -INFINITY;
-                if (hb1 == 0 && half == 0) s_I[cpos] = I;
-                if (I > m_run) {
-                    float alpha = expf(m_run - I);
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) accA[j] *= alpha;
-                    m_run = I;
-                }
-                const float e = valid ? expf(I - m_run) : 0.f;
-                const float pv = s_p[cpos];
-#pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    accA[j] = fmaf(e, R[j], accA[j]);
-                    accB[j] = fmaf(pv, R[j], accB[j]);
+                    for (int j = 0; j < 16; ++j) m16 |= (sacc[j] > 0.f ? 1u : 0u) << j;
+                    const uint32_t other = __shfl_xor(m16, 32);
+                    if (half == 0 && mykey >= 0) {
+                        const int jrel = mykey - kbase;
+                        pb.mask_map[((size_t)u * pb.s2max + jrel) * NH + hb1] = m16 | (other << 16);
+                        kmin = jrel < kmin ? jrel : kmin;
+                        kmax = jrel > kmax ? jrel : kmax;
+                    }
                 }
             }
+            __syncthreads();
+            if (nchunks > 0) combine_I(nchunks - 1);
             __syncthreads();
 
             // ---- softmax over the valid slots, dI, softmax_out ----------------------
@@ -273,77 +297,43 @@ __global__ __launch_bounds__(kBlock, (HP == 128 ? 1 : 2)) void grad_fused_kernel
             float zloc = 0.f;
             for (int j = tid; j < nvalid; j += kBlock) zloc += expf(s_I[j] - m);
             const float Z = block_sum(zloc, s_red + 4);
-            const float invZ = Z > 0.f ? 1.f / Z : 0.f;
             float amax = 0.f;
             for (int j = tid; j < nchunks * KC; j += kBlock) {
                 float dI = 0.f;
                 if (j < nvalid) {
-                    float y = expf(s_I[j] - m) / Z;
-                    yrow[s_slot[j]] = y;
-                    dI = y - s_p[j];
+                    const int sl = s_slot[j];
+                    const float y = expf(s_I[j] - m) / Z;
+                    yrow[sl] = y;
+                    dI = y - prow[sl];
+                    if constexpr (DENSE) atomicAdd(pb.dI_map + (size_t)u * pb.s2max + (s_key[j] - kbase), dI);
                 }
                 s_I[j] = dI;
                 amax = fmaxf(amax, fabsf(dI));
             }
-
-            // ---- dW = A / Z - B, reduced over the lanes and waves holding a head -------
-            {
-                const float sc = (m_run == -INFINITY || Z <= 0.f) ? 0.f : expf(m_run - m) * invZ;
-                float v[16];
-#pragma unroll
-                for (int j = 0; j < 16; ++j) v[j] = accA[j] * sc - accB[j];
-#pragma unroll
-                for (int o = 1; o < 32; o <<= 1) {
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) v[j] += __shfl_xor(v[j], o);
-                }
-                if (l32 == 0) {
-#pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        s_dw[kb1 * HP + 32 * hb1 + 8 * (j >> 2) + 4 * half + (j & 3)] = v[j];
+            amax = block_max(amax, s_red);
+            // power-of-two prescale of dI before its fp16 rounding
+            const int eds = pow2_exponent_below_2p15(amax);
+            const float dsc = ldexpf(1.f, eds), inv_dsc = ldexpf(1.f, -eds);
+            if constexpr (DENSE) {
+                // key range and the scale inputs of the key-major dK kernel
+                const int kmx = block_max_int(kmax, s_itmp);
+                const int kmn = -block_max_int(-kmin, s_itmp);
+                float wabs = 0.f;
+                for (int h = 0; h < G; ++h) wabs = fmaxf(wabs, fabsf(s_w[h]));
+                if (tid == 0) {
+                    pb.row_range[2 * u] = kmn;
+                    pb.row_range[2 * u + 1] = kmx;
+                    atomicMax(pb.dense_max, __float_as_uint(wabs * amax));
                 }
             }
 
-            // per-unit power-of-two prescale of dS before its fp16 rounding
-            float dsc = 1.f, inv_dsc = 1.f;
-            {
-                float amax_all = block_max(amax, s_red);
-                float wmax = wabs;
-                wmax = wave_max(wmax);
-                __syncthreads();
-                if (lane == 0) s_red[wave] = wmax;
-                __syncthreads();
-                wmax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-                float prod = amax_all * wmax;
-                if (prod > 0.f) {
-                    int ex;
-                    frexpf(prod, &ex);
-                    int sh = 15 - ex;
-                    sh = sh > 60 ? 60 : (sh < -60 ? -60 : sh);
-                    dsc = ldexpf(1.f, sh);
-                    inv_dsc = ldexpf(1.f, -sh);
-                }
-            }
-            __syncthreads();
-            for (int h = tid; h < G; h += kBlock) {
-                float acc = 0.f;
-                for (int kb = 0; kb < NKT; ++kb) acc += s_dw[kb * HP + h];
-                pb.dw[rq * pb.n1 + g * G + h] = acc;
-            }
-
-            // ---- pass 2 -------------------------------------------------------------
-            float wsc[16];
-#pragma unroll
-            for (int j = 0; j < 16; ++j) wsc[j] = wv[j] * dsc;
-            f32x16 dq_acc[C::NQW];
-#pragma unroll
-            for (int i = 0; i < C::NQW; ++i) dq_acc[i] = f32x16{};
-            // q again (s_kq held K chunks in pass 1), in fp16, as the B operand of
-            // the dK part: k = heads, columns = d, read with transposing LDS reads
-            float qinv = 1.f;
-            if constexpr (F16) {
-                load_q();
-            } else {
+            // ---- dK-part operands (scatter mode): q in fp16 and w split in fp16 -------
+            constexpr int NKH = HP / 16;
+            u32x4 qt[DENSE ? 1 : C::NPW][DENSE ? 1 : NKH];
+            uint32_t whi[DENSE ? 1 : NKH][4], wlo[DENSE ? 1 : NKH][4];
+            float part_mul = 1.f;
+            if constexpr (!DENSE) {
+                float qinv = 1.f;
                 constexpr int NQV = (HP * DCH + kBlock - 1) / kBlock;
                 u32x4 qv[NQV];
                 float qm = 0.f;
@@ -354,83 +344,104 @@ __global__ __launch_bounds__(kBlock, (HP == 128 ? 1 : 2)) void grad_fused_kernel
                     u32x4 v = {0u, 0u, 0u, 0u};
                     if (pc < HP * DCH && h < G) v = *(const u32x4 *)(qrow + h * D + cc * 8);
                     qv[i] = v;
+                    if constexpr (!F16) {
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        qm = fmaxf(qm, fmaxf(fabsf(__uint_as_float(v[c] << 16)),
-                                             fabsf(__uint_as_float(v[c] & 0xffff0000u))));
+                        for (int c = 0; c < 4; ++c)
+                            qm = fmaxf(qm, fmaxf(fabsf(__uint_as_float(v[c] << 16)),
+                                                 fabsf(__uint_as_float(v[c] & 0xffff0000u))));
+                    }
                 }
-                qm = block_max(qm, s_red);
-                int eq = 0;
-                if (qm > 0.f && qm < INFINITY) {
-                    int ex;
-                    frexpf(qm, &ex);
-                    eq = 15 - ex;
+                if constexpr (!F16) {
+                    qm = block_max(qm, s_red);
+                    const int eq = pow2_exponent_below_2p15(qm);
+                    const float qsc = ldexpf(1.f, eq);
+                    qinv = ldexpf(1.f, -eq);
+#pragma unroll
+                    for (int i = 0; i < NQV; ++i) {
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            qv[i][c] = pack2<true>(__uint_as_float(qv[i][c] << 16) * qsc,
+                                                   __uint_as_float(qv[i][c] & 0xffff0000u) * qsc);
+                    }
                 }
-                const float qsc = ldexpf(1.f, eq);
-                qinv = ldexpf(1.f, -eq);
 #pragma unroll
                 for (int i = 0; i < NQV; ++i) {
                     const int pc = tid + kBlock * i;
                     if (pc < HP * DCH) {
                         const int h = pc / DCH, cc = pc % DCH;
-                        u32x4 o;
+                        *(u32x4 *)(s_scr + tile_off<DCH>(h, cc * 8)) = qv[i];
+                    }
+                }
+                // w split into fp16 high + low parts at a per-unit power of two;
+                // lane half H, k-step kh, element e <-> head 16kh + 8(e/4) + 4H + e%4
+                float wmax = 0.f;
+                for (int h = 0; h < G; ++h) wmax = fmaxf(wmax, fabsf(s_w[h]));
+                const int ew = pow2_exponent_below_2p15(wmax);
+                const float wsc = ldexpf(1.f, ew);
 #pragma unroll
-                        for (int c = 0; c < 4; ++c)
-                            o[c] = pack2<true>(__uint_as_float(qv[i][c] << 16) * qsc,
-                                               __uint_as_float(qv[i][c] & 0xffff0000u) * qsc);
-                        *(u32x4 *)(s_kq + tile_off<DCH>(h, cc * 8)) = o;
+                for (int kh = 0; kh < NKH; ++kh) {
+#pragma unroll
+                    for (int pr = 0; pr < 4; ++pr) {
+                        const int e0 = 2 * pr, e1 = 2 * pr + 1;
+                        const float w0 = s_w[16 * kh + 8 * (e0 >> 2) + 4 * half + (e0 & 3)] * wsc;
+                        const float w1 = s_w[16 * kh + 8 * (e1 >> 2) + 4 * half + (e1 & 3)] * wsc;
+                        const _Float16 h0 = (_Float16)w0, h1 = (_Float16)w1;
+                        whi[kh][pr] = __builtin_bit_cast(uint32_t, f16x2{h0, h1});
+                        wlo[kh][pr] = pack2<true>(w0 - (float)h0, w1 - (float)h1);
+                    }
+                }
+                part_mul = qinv * ldexpf(1.f, -ew) * det_mul;
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < C::NPW; ++i) {
+                    const int t = wave + 4 * i;
+                    const int dbp = (t < C::NP_TILES ? t : 0) / NKT;
+#pragma unroll
+                    for (int kh = 0; kh < NKH; ++kh) {
+                        const int row = 16 * kh + 4 * half + (l16 >> 2);
+                        const int col = 32 * dbp + 16 * (grp & 1) + 4 * (l16 & 3);
+                        u32x2 lo = lds_read_tr(s_scr, tile_off<DCH>(row, col));
+                        u32x2 hi = lds_read_tr(s_scr, tile_off<DCH>(row + 8, col));
+                        qt[i][kh] = u32x4{lo.x, lo.y, hi.x, hi.y};
                     }
                 }
             }
-            const float part_mul = inv_dsc * qinv * det_mul;
-            __syncthreads();
-            u32x4 qt[C::NPW][HP / 16];
-#pragma unroll
-            for (int i = 0; i < C::NPW; ++i) {
-                int t = wave + 4 * i;
-                int dbp = (t < C::NP_TILES ? t : 0) / NKT;
-#pragma unroll
-                for (int kh = 0; kh < HP / 16; ++kh) {
-                    int row = 16 * kh + 8 * half + (l16 >> 2);
-                    int col = 32 * dbp + 16 * (grp & 1) + 4 * (l16 & 3);
-                    u32x2 lo = lds_read_tr(s_kq, tile_off<DCH>(row, col));
-                    u32x2 hi = lds_read_tr(s_kq, tile_off<DCH>(row + 4, col));
-                    qt[i][kh] = u32x4{lo.x, lo.y, hi.x, hi.y};
-                }
-            }
-            __syncthreads();
+            __syncthreads();   // s_scr is reused for K chunks below
 
-            if (nchunks > 0) issue_gather(pb.k16, 0);
+            // ---- pass 2 -------------------------------------------------------------
+            f32x16 dq_acc[C::NQW];
+#pragma unroll
+            for (int i = 0; i < C::NQW; ++i) dq_acc[i] = f32x16{};
+            if (nchunks > 0) {
+                read_keys(0);
+                issue_chunk(pb.k16, 0);
+                if (nchunks > 1) read_keys(1);
+            }
             for (int c = 0; c < nchunks; ++c) {
-                store_gather();
-                if (c + 1 < nchunks) issue_gather(pb.k16, c + 1);
-                // dS tile (32 heads of hb1 x 32 keys of kb1) -> s_ds[key][head]
+                // dI 1[S>0] tile (32 heads of hb1 x 32 keys of kb1) -> s_ds[key][head]
+                const uint64_t *mw = s_mask + ((c * NKT + kb1) * NH + hb1) * 16;
+                const float dIv = s_I[c * KC + 32 * kb1 + l32] * dsc;
+                const _Float16 dih = (_Float16)dIv;
+                const uint32_t dpair = __builtin_bit_cast(uint32_t, f16x2{dih, dih});
+                __builtin_amdgcn_s_waitcnt(0x0f70);     // vmcnt(0): chunk c landed in LDS
+                __syncthreads();                         // (also: previous chunk's readers done)
+                if (c + 1 < nchunks) issue_chunk(pb.k16, (c + 1) & 1);
+                if (c + 2 < nchunks) read_keys(c + 2);
                 {
-                    const uint64_t *mw = s_mask + ((c * NKT + kb1) * NH + hb1) * 16;
-                    const float dIv = s_I[c * KC + 32 * kb1 + l32];
                     const int krow = 32 * kb1 + l32;
 #pragma unroll
                     for (int jg = 0; jg < 4; ++jg) {
-                        float v0 = select_by_mask(wsc[4 * jg + 0] * dIv, uniform64(mw[4 * jg + 0]));
-                        float v1 = select_by_mask(wsc[4 * jg + 1] * dIv, uniform64(mw[4 * jg + 1]));
-                        float v2 = select_by_mask(wsc[4 * jg + 2] * dIv, uniform64(mw[4 * jg + 2]));
-                        float v3 = select_by_mask(wsc[4 * jg + 3] * dIv, uniform64(mw[4 * jg + 3]));
-                        // fp16 value and the remainder its rounding dropped (the
-                        // remainder feeds the dK part only)
-                        const _Float16 h0 = (_Float16)v0, h1 = (_Float16)v1;
-                        const _Float16 h2 = (_Float16)v2, h3 = (_Float16)v3;
-                        const float r0 = v0 - (float)h0, r1 = v1 - (float)h1;
-                        const float r2 = v2 - (float)h2, r3 = v3 - (float)h3;
-                        u32x2 pk = {__builtin_bit_cast(uint32_t, f16x2{h0, h1}),
-                                    __builtin_bit_cast(uint32_t, f16x2{h2, h3})};
-                        u32x2 pl = {pack2<true>(r0, r1), pack2<true>(r2, r3)};
-                        const int off = tile_off<HCH>(krow, 32 * hb1 + 8 * jg + 4 * half);
-                        *(u32x2 *)(s_ds + off) = pk;
-                        *(u32x2 *)(s_dsl + off) = pl;
+                        const uint32_t a0 = select_bits(0x0000ffffu, uniform64(mw[4 * jg + 0])) |
+                                            select_bits(0xffff0000u, uniform64(mw[4 * jg + 1]));
+                        const uint32_t a1 = select_bits(0x0000ffffu, uniform64(mw[4 * jg + 2])) |
+                                            select_bits(0xffff0000u, uniform64(mw[4 * jg + 3]));
+                        *(u32x2 *)(s_ds + tile_off<HCH>(krow, 32 * hb1 + 8 * jg + 4 * half)) =
+                            u32x2{a0 & dpair, a1 & dpair};
                     }
                 }
                 __syncthreads();
-                // dq += dS K  (both operands via transposing reads; k = keys)
+                const char *kb = s_scr + (c & 1) * C::KBUF;
+                // U += (dI 1[S>0]) K  (both operands via transposing reads; k = keys)
                 if (wave < C::NQ_TILES) {
                     const int hbq = wave % NH;
 #pragma unroll
@@ -446,80 +457,111 @@ __global__ __launch_bounds__(kBlock, (HP == 128 ? 1 : 2)) void grad_fused_kernel
                             if (t < C::NQ_TILES) {
                                 const int dbq = t / NH;
                                 const int dcol = 32 * dbq + 16 * (grp & 1) + 4 * (l16 & 3);
-                                u32x2 b0 = lds_read_tr(s_kq, tile_off<DCH>(row, dcol));
-                                u32x2 b1 = lds_read_tr(s_kq, tile_off<DCH>(row + 4, dcol));
+                                u32x2 b0 = lds_read_tr(kb, tile_off<DCH>(row, dcol));
+                                u32x2 b1 = lds_read_tr(kb, tile_off<DCH>(row + 4, dcol));
                                 dq_acc[i] = mfma32<true>(a, u32x4{b0.x, b0.y, b1.x, b1.y}, dq_acc[i]);
                             }
                         }
                     }
                 }
-                // dK part P[key, d] = sum_h dS[h, key] q[h, d]; scatter-add
-                if (wave < C::NP_TILES) {
-                    u32x4 ad[HP / 16], adl[HP / 16];
+                if constexpr (!DENSE) {
+                    // P'[key, d] = sum_h 1[S>0] w_h q[h, d]; P = dI_key P'; scatter-add
+                    if (wave < C::NP_TILES) {
+                        u32x4 ahi[NKH], alo[NKH];
 #pragma unroll
-                    for (int kh = 0; kh < HP / 16; ++kh) {
-                        const int off = tile_off<HCH>(32 * kbp + l32, 16 * kh + 8 * half);
-                        ad[kh] = *(const u32x4 *)(s_ds + off);
-                        adl[kh] = *(const u32x4 *)(s_dsl + off);
-                    }
-                    int krows[16];
+                        for (int kh = 0; kh < NKH; ++kh) {
+                            const uint64_t *pw = s_mask + ((c * NKT + kbp) * NH + kh / 2) * 16 + 8 * (kh & 1);
 #pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        krows[j] = s_key[c * KC + 32 * kbp + 8 * (j >> 2) + 4 * half + (j & 3)];
-#pragma unroll
-                    for (int i = 0; i < C::NPW; ++i) {
-                        const int t = wave + 4 * i;
-                        if (t < C::NP_TILES) {
-                            const int dbp = t / NKT;
-                            f32x16 pacc = {};
-#pragma unroll
-                            for (int kh = 0; kh < HP / 16; ++kh) {
-                                pacc = mfma32<true>(ad[kh], qt[i][kh], pacc);
-                                pacc = mfma32<true>(adl[kh], qt[i][kh], pacc);
+                            for (int pr = 0; pr < 4; ++pr) {
+                                const uint32_t sel = select_bits(0x0000ffffu, uniform64(pw[2 * pr])) |
+                                                     select_bits(0xffff0000u, uniform64(pw[2 * pr + 1]));
+                                ahi[kh][pr] = sel & whi[kh][pr];
+                                alo[kh][pr] = sel & wlo[kh][pr];
                             }
-                            const int dcol = 32 * dbp + l32;
+                        }
+                        int krows[16];
+                        float dik[16];
 #pragma unroll
-                            for (int j = 0; j < 16; ++j) {
-                                if (krows[j] >= 0) {
-                                    const int off = (krows[j] * pb.n2 + g) * D + dcol;
-                                    const float val = pacc[j] * part_mul;
-                                    if constexpr (DET) {
-                                        long long fx = __float2ll_rn(val);
-                                        atomicAdd((unsigned long long *)pb.dk_acc + off, (unsigned long long)fx);
-                                    } else {
-                                        unsafeAtomicAdd((float *)pb.dk_acc + off, val);
+                        for (int j = 0; j < 16; ++j) {
+                            const int kp = c * KC + 32 * kbp + 8 * (j >> 2) + 4 * half + (j & 3);
+                            krows[j] = s_key[kp];
+                            dik[j] = s_I[kp] * part_mul;
+                        }
+#pragma unroll
+                        for (int i = 0; i < C::NPW; ++i) {
+                            const int t = wave + 4 * i;
+                            if (t < C::NP_TILES) {
+                                const int dbp = t / NKT;
+                                f32x16 pacc = {};
+#pragma unroll
+                                for (int kh = 0; kh < NKH; ++kh) {
+                                    pacc = mfma32<true>(ahi[kh], qt[i][kh], pacc);
+                                    pacc = mfma32<true>(alo[kh], qt[i][kh], pacc);
+                                }
+                                const int dcol = 32 * dbp + l32;
+#pragma unroll
+                                for (int j = 0; j < 16; ++j) {
+                                    if (krows[j] >= 0) {
+                                        const int off = (krows[j] * pb.n2 + g) * D + dcol;
+                                        const float val = pacc[j] * dik[j];
+                                        if constexpr (DET) {
+                                            long long fx = __float2ll_rn(val);
+                                            atomicAdd((unsigned long long *)pb.dk_acc + off, (unsigned long long)fx);
+                                        } else {
+                                            unsafeAtomicAdd((float *)pb.dk_acc + off, val);
+                                        }
                                     }
                                 }
                             }
                         }
                     }
                 }
-                __syncthreads();
             }
 
-            // ---- dq out: stage the 16-bit tiles in LDS, then 16-byte row stores --------
-            if (wave < C::NQ_TILES) {
-                const int hbq = wave % NH;
+            // ---- dq = w U and dW = <q, U>, one head tile at a time through LDS --------
+            const float uscale = inv_dsc * kinv;
+            for (int hb = 0; hb < NH; ++hb) {
+                __syncthreads();
+                if (wave < C::NQ_TILES && wave % NH == hb) {
 #pragma unroll
-                for (int i = 0; i < C::NQW; ++i) {
-                    const int t = wave + 4 * i;
-                    if (t < C::NQ_TILES) {
-                        const int dbq = t / NH;
+                    for (int i = 0; i < C::NQW; ++i) {
+                        const int t = wave + 4 * i;
+                        if (t < C::NQ_TILES) {
+                            const int dbq = t / NH;
+                            float *ut = (float *)s_scr;
 #pragma unroll
-                        for (int j = 0; j < 16; ++j) {
-                            const int h = 32 * hbq + 8 * (j >> 2) + 4 * half + (j & 3);
-                            *(uint16_t *)(s_kq + tile_off<DCH>(h, 32 * dbq + l32)) =
-                                to16<F16>(dq_acc[i][j] * (inv_dsc * kinv));
+                            for (int j = 0; j < 16; ++j)
+                                ut[(8 * (j >> 2) + 4 * half + (j & 3)) * D + 32 * dbq + l32] = dq_acc[i][j] * uscale;
                         }
                     }
                 }
-            }
-            __syncthreads();
-            {
-                uint16_t *dqrow = pb.dq + (rq * pb.n1 + g * G) * D;
-                for (int pc = tid; pc < G * DCH; pc += kBlock) {
-                    int h = pc / DCH, cc = pc % DCH;
-                    *(u32x4 *)(dqrow + h * D + cc * 8) = *(const u32x4 *)(s_kq + tile_off<DCH>(h, cc * 8));
+                __syncthreads();
+                // one 16-byte chunk (8 d) per thread; the DCH chunks of a head sit on
+                // consecutive lanes
+                for (int it = 0; it < (32 * DCH + kBlock - 1) / kBlock; ++it) {
+                    const int idx = tid + kBlock * it;
+                    const int hh = idx / DCH, cc = idx % DCH;
+                    const int h = 32 * hb + hh;
+                    const bool act = hh < 32 && h < G;
+                    float dot = 0.f;
+                    if (act) {
+                        const float *ur = (const float *)s_scr + hh * D + cc * 8;
+                        const u32x4 qv = *(const u32x4 *)(qrow + h * D + cc * 8);
+                        const float wh = s_w[h];
+                        u32x4 o;
+#pragma unroll
+                        for (int c2 = 0; c2 < 4; ++c2) {
+                            const float u0 = ur[2 * c2], u1 = ur[2 * c2 + 1];
+                            const float q0 = from16<F16>((uint16_t)(qv[c2] & 0xffffu));
+                            const float q1 = from16<F16>((uint16_t)(qv[c2] >> 16));
+                            dot = fmaf(q0, u0, fmaf(q1, u1, dot));
+                            o[c2] = (uint32_t)to16<F16>(wh * u0) | ((uint32_t)to16<F16>(wh * u1) << 16);
+                        }
+                        *(u32x4 *)(pb.dq + (r * pb.n1 + g * G + h) * D + cc * 8) = o;
+                    }
+#pragma unroll
+                    for (int o2 = 1; o2 < DCH; o2 <<= 1) dot += __shfl_xor(dot, o2);
+                    if (act && cc == 0) pb.dw[r * pb.n1 + g * G + h] = dot;
                 }
             }
             __syncthreads();
@@ -527,16 +569,16 @@ __global__ __launch_bounds__(kBlock, (HP == 128 ? 1 : 2)) void grad_fused_kernel
     }
 }
 
-template <int HP, int D, bool F16, bool DET>
+template <int HP, int D, bool F16, int DKM>
 static hipError_t launch_one(const Problem &pb, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((grad_fused_kernel<HP, D, F16, DET>), dim3(grid), dim3(kBlock), 0, stream, pb);
+    hipLaunchKernelGGL((grad_fused_kernel<HP, D, F16, DKM>), dim3(grid), dim3(kBlock), 0, stream, pb);
     return hipGetLastError();
 }
 
-template <int HP, int D, bool F16, bool DET>
+template <int HP, int D, bool F16, int DKM>
 static int blocks_one() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grad_fused_kernel<HP, D, F16, DET>, kBlock, 0) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grad_fused_kernel<HP, D, F16, DKM>, kBlock, 0) !=
         hipSuccess)
         return 1;
     return n > 0 ? n : 1;
@@ -545,11 +587,13 @@ static int blocks_one() {
 #define SLIKL_DISPATCH(HPV, DV, FN, ...)                                             \
     do {                                                                             \
         if (f16) {                                                                   \
-            if (det) return FN<HPV, DV, true, true>(__VA_ARGS__);                    \
-            return FN<HPV, DV, true, false>(__VA_ARGS__);                            \
+            if (mode == 2) return FN<HPV, DV, true, 2>(__VA_ARGS__);                 \
+            if (mode == 1) return FN<HPV, DV, true, 1>(__VA_ARGS__);                 \
+            return FN<HPV, DV, true, 0>(__VA_ARGS__);                                \
         }                                                                            \
-        if (det) return FN<HPV, DV, false, true>(__VA_ARGS__);                       \
-        return FN<HPV, DV, false, false>(__VA_ARGS__);                               \
+        if (mode == 2) return FN<HPV, DV, false, 2>(__VA_ARGS__);                    \
+        if (mode == 1) return FN<HPV, DV, false, 1>(__VA_ARGS__);                    \
+        return FN<HPV, DV, false, 0>(__VA_ARGS__);                                   \
     } while (0)
 
 #define SLIKL_DISPATCH_D(HPV, FN, ...)                                               \
@@ -559,7 +603,7 @@ static int blocks_one() {
         SLIKL_DISPATCH(HPV, 128, FN, __VA_ARGS__);                                   \
     } while (0)
 
-hipError_t launch_grad_fused(const Problem &pb, int hp, bool f16, bool det, int grid,
+hipError_t launch_grad_fused(const Problem &pb, int hp, bool f16, int mode, int grid,
                              hipStream_t stream) {
     const int d = pb.d;
     if (hp == 32) SLIKL_DISPATCH_D(32, launch_one, pb, grid, stream);
@@ -567,7 +611,7 @@ hipError_t launch_grad_fused(const Problem &pb, int hp, bool f16, bool det, int 
     SLIKL_DISPATCH_D(128, launch_one, pb, grid, stream);
 }
 
-int grad_fused_blocks_per_cu(int hp, int d, bool f16, bool det) {
+int grad_fused_blocks_per_cu(int hp, int d, bool f16, int mode) {
     if (hp == 32) SLIKL_DISPATCH_D(32, blocks_one);
     if (hp == 64) SLIKL_DISPATCH_D(64, blocks_one);
     SLIKL_DISPATCH_D(128, blocks_one);

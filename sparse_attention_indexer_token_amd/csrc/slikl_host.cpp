@@ -7,7 +7,7 @@
 #include <stdint.h>
 #include <string.h>
 
-#include "../../include/slikl.h"
+#include "slikl.h"
 #include "slikl_internal.h"
 
 namespace {
@@ -69,6 +69,8 @@ slikl::WorkspacePlan plan(const slikl_desc *d) {
     off = align_up(off + 16);
     p.scale_off = off;
     off = align_up(off + 64);
+    p.zero_off = off;
+    off = align_up(off + 256);
     p.k16_off = off;
     p.k16_bytes = d->dtype == SLIKL_DTYPE_BF16 ? (size_t)t2 * (size_t)d->n2 * (size_t)d->d * 2 : 0;
     off = align_up(off + p.k16_bytes);
@@ -105,7 +107,7 @@ slikl_status resolve_parts(const slikl_desc *d, int32_t *parts) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return SLIKL_ERR_LAUNCH;
     int per_cu = slikl::grad_fused_blocks_per_cu(head_tile(d->n1 / d->n2), (int)d->d,
-                                                 d->dtype == SLIKL_DTYPE_F16, d->deterministic != 0);
+                                                 d->dtype == SLIKL_DTYPE_F16, d->deterministic != 0 ? 1 : 0);
     int64_t p = (int64_t)cus * per_cu;
     if (p > SLIKL_MAX_PARTS) p = SLIKL_MAX_PARTS;
     if (p < 1) p = 1;
@@ -204,6 +206,8 @@ slikl_status slikl_grad(const slikl_desc *desc, const void *q, const void *k, co
     pb.dk_acc = ws + wp.acc_off;
     pb.det_scale = (const float *)(ws + wp.scale_off);
     pb.k16 = f16 ? pb.k : (const uint16_t *)(ws + wp.k16_off);
+    pb.zero16 = (const uint16_t *)(ws + wp.zero_off);
+    const int mode = det ? 1 : 0;
 
     hipError_t e = hipSuccess;
     if (!metadata) {
@@ -218,6 +222,8 @@ slikl_status slikl_grad(const slikl_desc *desc, const void *q, const void *k, co
     if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
     e = slikl::launch_zero(ws + wp.scale_off, 64, s);
     if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
+    e = slikl::launch_zero(ws + wp.zero_off, 256, s);
+    if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
     if (!f16 && t2 > 0) {
         e = slikl::launch_k_to_f16(pb, (uint16_t *)(ws + wp.k16_off), (float *)(ws + wp.scale_off), s);
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
@@ -227,7 +233,7 @@ slikl_status slikl_grad(const slikl_desc *desc, const void *q, const void *k, co
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
     }
     if (t1 > 0) {
-        e = slikl::launch_grad_fused(pb, head_tile(pb.group), f16, det, parts, s);
+        e = slikl::launch_grad_fused(pb, head_tile(pb.group), f16, mode, parts, s);
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
     }
     e = slikl::launch_finalize_dk(pb, f16, det, s);

@@ -22,6 +22,13 @@ struct Problem {
     void *dk_acc;            // fp32 or int64 accumulator [T2, N2, D]
     const float *det_scale;  // scale block: [0] 2^F, [1] 2^-F (deterministic), [6] 2^-eK
     const uint16_t *k16;     // fp16 keys for the dq / dK-part contractions ([T2, N2, D])
+    const uint16_t *zero16;  // 16 zero bytes (source of padding rows in direct-to-LDS gathers)
+    // dense dK records (key-major dK kernel): per unit u and batch-relative key j
+    float *dI_map;           // [U, s2max] dI summed over the slots naming j (0 elsewhere)
+    uint32_t *mask_map;      // [U, s2max, HP/32] S > 0 head bits of (u, j)
+    int32_t *row_range;      // [U, 2] smallest / largest j named by u (-1 if none)
+    uint32_t *dense_max;     // max over units of max|w| * max|dI| (float bits)
+    int64_t s2max;           // key length of the dense maps
     const int32_t *cu_q;     // [batch + 1] or null (BSND)
     const int32_t *cu_k;     // [batch + 1] or null (BSND)
     int64_t s1, s2;          // BSND per-batch lengths (unused for TND sides)
@@ -38,13 +45,16 @@ struct WorkspacePlan {
     size_t flags_off;               // metadata error flags found while counting (16 bytes)
     size_t scale_off;               // scale block (16 x 32-bit)
     size_t k16_off, k16_bytes;      // fp16 copy of k (bf16 inputs only)
+    size_t zero_off;                // 256 zero bytes
     size_t total;
 };
 
 // Kernel launchers (defined in the .hip files).  Return hipSuccess or the error.
-hipError_t launch_grad_fused(const Problem &pb, int hp, bool f16, bool det, int grid,
+// mode: 0 scatter-add dK with fp32 atomics, 1 int64 fixed-point atomics
+// (deterministic), 2 dense records for the key-major dK kernel
+hipError_t launch_grad_fused(const Problem &pb, int hp, bool f16, int mode, int grid,
                              hipStream_t stream);
-int grad_fused_blocks_per_cu(int hp, int d, bool f16, bool det);
+int grad_fused_blocks_per_cu(int hp, int d, bool f16, int mode);
 hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t stream);
 hipError_t launch_finalize_dk(const Problem &pb, bool f16, bool det, hipStream_t stream);
 hipError_t launch_det_scale(const Problem &pb, bool f16, float *scale_block, hipStream_t stream);
