@@ -67,6 +67,13 @@ enum { SLIKL_DTYPE_F16 = 0, SLIKL_DTYPE_BF16 = 1 };
 /* Metadata split modes: WEIGHTED balances (valid slots + overhead) per unit;
  * ROWS is the even row split of the metadata pre-pass prior art. */
 enum { SLIKL_SPLIT_WEIGHTED = 0, SLIKL_SPLIT_ROWS = 1 };
+/* dK strategies.  SCATTER adds each slot's dK part into the key rows with
+ * atomics (fp32, or int64 fixed point when deterministic).  DENSE (BSND only)
+ * writes per (query row, key) records and runs a key-major kernel that sums
+ * over query rows in registers: no atomics, bitwise reproducible; it pays off
+ * when the top-k lists cover a large share of each batch's keys.  AUTO picks
+ * DENSE for BSND when 2 * topk >= S2 and the records fit in 8 GiB. */
+enum { SLIKL_DK_AUTO = 0, SLIKL_DK_SCATTER = 1, SLIKL_DK_DENSE = 2 };
 
 /* Metadata array (int32, SLIKL_METADATA_INTS entries).  A "unit" is one
  * (query row, key head) pair, u = row * N2 + g.
@@ -99,6 +106,7 @@ typedef struct slikl_desc {
     const int32_t *cu_seqlens_k; /* device, B+1 entries starting at 0; required iff TND k */
     int32_t num_parts;       /* metadata parts; 0 = library default (CUs x blocks/CU)  */
     int32_t split_mode;      /* SLIKL_SPLIT_*                                         */
+    int32_t dk_mode;         /* SLIKL_DK_*; DENSE with a TND side -> UNSUPPORTED      */
 } slikl_desc;
 
 /* First phase (the page's "GetWorkspaceSize" step): validate `desc` and return

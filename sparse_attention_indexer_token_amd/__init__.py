@@ -42,7 +42,8 @@ def _dtype_code(t) -> int:
 
 def make_desc(q, k, sparse_indices, *, layout_q: str = "BSND", layout_k: str = "BSND",
               cu_seqlens_q=None, cu_seqlens_k=None, deterministic: bool = False,
-              num_parts: int = 0, split_mode: str = "weighted") -> SliklDesc:
+              num_parts: int = 0, split_mode: str = "weighted",
+              dk_mode: str = "auto") -> SliklDesc:
     """Build the C descriptor from tensor shapes (no device access)."""
     if layout_q not in LAYOUT or layout_k not in LAYOUT:
         raise ValueError("layouts must be 'BSND' or 'TND'")
@@ -84,6 +85,7 @@ def make_desc(q, k, sparse_indices, *, layout_q: str = "BSND", layout_k: str = "
     desc.cu_seqlens_k = cu_seqlens_k.data_ptr() if layout_k == "TND" else None
     desc.num_parts = int(num_parts)
     desc.split_mode = _native.SPLIT[split_mode]
+    desc.dk_mode = _native.DK_MODE[dk_mode]
     return desc
 
 
@@ -117,13 +119,14 @@ def slikl_grad_parts(desc: SliklDesc) -> int:
 
 def slikl_grad_metadata(q, k, sparse_indices, *, layout_q="BSND", layout_k="BSND",
                         cu_seqlens_q=None, cu_seqlens_k=None, deterministic=False,
-                        num_parts: int = 0, split_mode: str = "weighted",
+                        num_parts: int = 0, split_mode: str = "weighted", dk_mode: str = "auto",
                         metadata=None, workspace=None):
     """Run the load-balancing metadata pre-pass; returns the int32 metadata tensor."""
     torch = _torch()
     desc = make_desc(q, k, sparse_indices, layout_q=layout_q, layout_k=layout_k,
                      cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
-                     deterministic=deterministic, num_parts=num_parts, split_mode=split_mode)
+                     deterministic=deterministic, num_parts=num_parts, split_mode=split_mode,
+                     dk_mode=dk_mode)
     dev = q.device
     _check_tensor("sparse_indices", sparse_indices, torch.int32, dev)
     nbytes = _native.workspace_size(desc)
@@ -141,7 +144,7 @@ def slikl_grad_metadata(q, k, sparse_indices, *, layout_q="BSND", layout_k="BSND
 def slikl_grad(q, k, w, sparse_indices, attn_softmax_l1norm, *, layout_q="BSND", layout_k="BSND",
                cu_seqlens_q=None, cu_seqlens_k=None, deterministic: bool = False,
                metadata=None, num_parts: int = 0, split_mode: str = "weighted",
-               workspace=None, out: Optional[tuple] = None):
+               dk_mode: str = "auto", workspace=None, out: Optional[tuple] = None):
     """Backward pass; returns (dq, dk, dw, softmax_out).
 
     ``out`` may hold preallocated (dq, dk, dw, softmax_out); ``workspace`` a
@@ -150,7 +153,8 @@ def slikl_grad(q, k, w, sparse_indices, attn_softmax_l1norm, *, layout_q="BSND",
     torch = _torch()
     desc = make_desc(q, k, sparse_indices, layout_q=layout_q, layout_k=layout_k,
                      cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
-                     deterministic=deterministic, num_parts=num_parts, split_mode=split_mode)
+                     deterministic=deterministic, num_parts=num_parts, split_mode=split_mode,
+                     dk_mode=dk_mode)
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("tensors must be on the GPU")

@@ -22,6 +22,7 @@ SLIKL_ERR_LAUNCH = 5
 LAYOUT = {"BSND": 0, "TND": 1}
 DTYPE = {"f16": 0, "bf16": 1}
 SPLIT = {"weighted": 0, "rows": 1}
+DK_MODE = {"auto": 0, "scatter": 1, "dense": 2}
 
 METADATA_HEADER = 16
 MAX_PARTS = 2048
@@ -40,7 +41,7 @@ class SliklDesc(ctypes.Structure):
         ("batch", c_int64), ("s1", c_int64), ("s2", c_int64),
         ("n1", c_int64), ("n2", c_int64), ("d", c_int64), ("topk", c_int64),
         ("cu_seqlens_q", c_void_p), ("cu_seqlens_k", c_void_p),
-        ("num_parts", c_int32), ("split_mode", c_int32),
+        ("num_parts", c_int32), ("split_mode", c_int32), ("dk_mode", c_int32),
     ]
 
 

@@ -315,15 +315,52 @@ __global__ __launch_bounds__(kBlock, (HP == 128 ? 1 : 2)) void grad_fused_kernel
             const int eds = pow2_exponent_below_2p15(amax);
             const float dsc = ldexpf(1.f, eds), inv_dsc = ldexpf(1.f, -eds);
             if constexpr (DENSE) {
-                // key range and the scale inputs of the key-major dK kernel
+                // records of the key-major dK kernel: key range; bf16 queries as fp16
+                // scaled by a per-unit power of two 2^eq (exact to undo); the global
+                // bound max|w| max|dI| 2^-eq that fixes its fp16 scale for dS
                 const int kmx = block_max_int(kmax, s_itmp);
                 const int kmn = -block_max_int(-kmin, s_itmp);
                 float wabs = 0.f;
                 for (int h = 0; h < G; ++h) wabs = fmaxf(wabs, fabsf(s_w[h]));
+                int eq = 0;
+                if constexpr (!F16) {
+                    constexpr int NQV = (HP * DCH + kBlock - 1) / kBlock;
+                    u32x4 qv[NQV];
+                    float qm = 0.f;
+#pragma unroll
+                    for (int i = 0; i < NQV; ++i) {
+                        const int pc = tid + kBlock * i;
+                        const int h = pc / DCH, cc = pc % DCH;
+                        u32x4 v = {0u, 0u, 0u, 0u};
+                        if (pc < HP * DCH && h < G) v = *(const u32x4 *)(qrow + h * D + cc * 8);
+                        qv[i] = v;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            qm = fmaxf(qm, fmaxf(fabsf(__uint_as_float(v[c] << 16)),
+                                                 fabsf(__uint_as_float(v[c] & 0xffff0000u))));
+                    }
+                    qm = block_max(qm, s_red);
+                    eq = pow2_exponent_below_2p15(qm);
+                    const float qsc = ldexpf(1.f, eq);
+#pragma unroll
+                    for (int i = 0; i < NQV; ++i) {
+                        const int pc = tid + kBlock * i;
+                        const int h = pc / DCH, cc = pc % DCH;
+                        if (pc < HP * DCH && h < G) {
+                            u32x4 o;
+#pragma unroll
+                            for (int c = 0; c < 4; ++c)
+                                o[c] = pack2<true>(__uint_as_float(qv[i][c] << 16) * qsc,
+                                                   __uint_as_float(qv[i][c] & 0xffff0000u) * qsc);
+                            *(u32x4 *)(pb.q16 + (r * pb.n1 + g * G + h) * D + cc * 8) = o;
+                        }
+                    }
+                }
                 if (tid == 0) {
                     pb.row_range[2 * u] = kmn;
                     pb.row_range[2 * u + 1] = kmx;
-                    atomicMax(pb.dense_max, __float_as_uint(wabs * amax));
+                    pb.q16_exp[u] = eq;
+                    atomicMax(pb.dense_max, __float_as_uint(wabs * amax * ldexpf(1.f, -eq)));
                 }
             }
 

@@ -31,6 +31,7 @@ slikl_status validate(const slikl_desc *d) {
     if (d->dtype != SLIKL_DTYPE_F16 && d->dtype != SLIKL_DTYPE_BF16) return SLIKL_ERR_PARAM_INVALID;
     if (d->deterministic != 0 && d->deterministic != 1) return SLIKL_ERR_PARAM_INVALID;
     if (d->split_mode != SLIKL_SPLIT_WEIGHTED && d->split_mode != SLIKL_SPLIT_ROWS) return SLIKL_ERR_PARAM_INVALID;
+    if (d->dk_mode < SLIKL_DK_AUTO || d->dk_mode > SLIKL_DK_DENSE) return SLIKL_ERR_PARAM_INVALID;
     if (d->num_parts < 0 || d->num_parts > SLIKL_MAX_PARTS) return SLIKL_ERR_PARAM_INVALID;
     if (d->batch <= 0 || d->batch > INT32_MAX - 1) return SLIKL_ERR_PARAM_INVALID;
     if (d->n1 < 1 || d->n1 > 128) return SLIKL_ERR_PARAM_INVALID;
@@ -49,21 +50,48 @@ slikl_status validate(const slikl_desc *d) {
     const int64_t t1 = rows_q(d), t2 = rows_k(d);
     if (t1 > lim / (d->n1 * d->d) || t1 > lim / (d->n2 * d->topk)) return SLIKL_ERR_PARAM_INVALID;
     if (t2 > lim / (d->n2 * d->d)) return SLIKL_ERR_PARAM_INVALID;
+    if (d->dk_mode == SLIKL_DK_DENSE &&
+        (d->layout_q != SLIKL_LAYOUT_BSND || d->layout_k != SLIKL_LAYOUT_BSND))
+        return SLIKL_ERR_UNSUPPORTED;
     return SLIKL_OK;
+}
+
+// Resolved dK strategy: 0 fp32 atomics, 1 int64 fixed-point atomics
+// (deterministic), 2 dense records + key-major kernel (deterministic).
+int dk_strategy(const slikl_desc *d) {
+    const bool bsnd = d->layout_q == SLIKL_LAYOUT_BSND && d->layout_k == SLIKL_LAYOUT_BSND;
+    if (d->dk_mode == SLIKL_DK_DENSE && bsnd) return 2;
+    if (d->dk_mode == SLIKL_DK_AUTO && bsnd && 2 * d->topk >= d->s2) {
+        // the dense records are sized [units, S2]; keep them modest
+        const double bytes = (double)d->batch * d->s1 * d->n2 * d->s2 * 4.0 * (1 + head_tile(d->n1 / d->n2) / 32);
+        if (bytes <= 8.0 * (1ull << 30)) return 2;
+    }
+    return d->deterministic ? 1 : 0;
+}
+
+int dense_row_splits(const slikl_desc *d) {
+    const int64_t nkb = (d->s2 + 127) / 128;
+    int64_t rs = (1024 + nkb * d->n2 * d->batch - 1) / (nkb * d->n2 * d->batch);
+    const int64_t cap = d->s1 / 16 > 1 ? d->s1 / 16 : 1;
+    rs = rs < 1 ? 1 : (rs > cap ? cap : rs);
+    return (int)rs;
 }
 
 slikl::WorkspacePlan plan(const slikl_desc *d) {
     slikl::WorkspacePlan p{};
     const int64_t t1 = rows_q(d), t2 = rows_k(d);
-    const size_t acc_elem = d->deterministic ? 8 : 4;
+    const size_t U = (size_t)t1 * (size_t)d->n2;
+    const int mode = dk_strategy(d);
+    p.mode = mode;
+    const size_t acc_elem = mode == 1 ? 8 : 4;
     size_t off = 0;
     p.acc_off = off;
-    p.acc_bytes = (size_t)t2 * (size_t)d->n2 * (size_t)d->d * acc_elem;
+    p.acc_bytes = mode == 2 ? 0 : (size_t)t2 * (size_t)d->n2 * (size_t)d->d * acc_elem;
     off = align_up(off + p.acc_bytes);
     p.meta_off = off;
     off = align_up(off + SLIKL_METADATA_INTS * sizeof(int32_t));
     p.prefix_off = off;
-    p.prefix_bytes = ((size_t)t1 * (size_t)d->n2 + 1) * sizeof(int64_t);
+    p.prefix_bytes = (U + 1) * sizeof(int64_t);
     off = align_up(off + p.prefix_bytes);
     p.flags_off = off;
     off = align_up(off + 16);
@@ -74,6 +102,23 @@ slikl::WorkspacePlan plan(const slikl_desc *d) {
     p.k16_off = off;
     p.k16_bytes = d->dtype == SLIKL_DTYPE_BF16 ? (size_t)t2 * (size_t)d->n2 * (size_t)d->d * 2 : 0;
     off = align_up(off + p.k16_bytes);
+    if (mode == 2) {
+        const size_t s2 = (size_t)d->s2, nh = (size_t)head_tile(d->n1 / d->n2) / 32;
+        p.rsplits = dense_row_splits(d);
+        p.dimap_off = off;
+        p.dimap_bytes = U * s2 * 4;
+        off = align_up(off + p.dimap_bytes);
+        p.maskmap_off = off;
+        off = align_up(off + U * s2 * nh * 4);
+        p.range_off = off;
+        off = align_up(off + U * 8);
+        p.qexp_off = off;
+        off = align_up(off + U * 4);
+        p.q16_off = off;
+        off = align_up(off + (d->dtype == SLIKL_DTYPE_BF16 ? (size_t)t1 * (size_t)d->n1 * (size_t)d->d * 2 : 0));
+        p.part_off = off;
+        off = align_up(off + (size_t)p.rsplits * (size_t)t2 * (size_t)d->n2 * (size_t)d->d * 4);
+    }
     p.total = off;
     return p;
 }
@@ -107,7 +152,7 @@ slikl_status resolve_parts(const slikl_desc *d, int32_t *parts) {
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return SLIKL_ERR_LAUNCH;
     int per_cu = slikl::grad_fused_blocks_per_cu(head_tile(d->n1 / d->n2), (int)d->d,
-                                                 d->dtype == SLIKL_DTYPE_F16, d->deterministic != 0 ? 1 : 0);
+                                                 d->dtype == SLIKL_DTYPE_F16, dk_strategy(d));
     int64_t p = (int64_t)cus * per_cu;
     if (p > SLIKL_MAX_PARTS) p = SLIKL_MAX_PARTS;
     if (p < 1) p = 1;
@@ -207,7 +252,17 @@ slikl_status slikl_grad(const slikl_desc *desc, const void *q, const void *k, co
     pb.det_scale = (const float *)(ws + wp.scale_off);
     pb.k16 = f16 ? pb.k : (const uint16_t *)(ws + wp.k16_off);
     pb.zero16 = (const uint16_t *)(ws + wp.zero_off);
-    const int mode = det ? 1 : 0;
+    const int mode = wp.mode;
+    if (mode == 2) {
+        pb.dI_map = (float *)(ws + wp.dimap_off);
+        pb.mask_map = (uint32_t *)(ws + wp.maskmap_off);
+        pb.row_range = (int32_t *)(ws + wp.range_off);
+        pb.q16_exp = (int32_t *)(ws + wp.qexp_off);
+        pb.q16 = (uint16_t *)(ws + wp.q16_off);
+        pb.dk_part = (float *)(ws + wp.part_off);
+        pb.dense_max = (uint32_t *)(ws + wp.scale_off) + 8;
+        pb.s2max = desc->s2;
+    }
 
     hipError_t e = hipSuccess;
     if (!metadata) {
@@ -224,11 +279,15 @@ slikl_status slikl_grad(const slikl_desc *desc, const void *q, const void *k, co
     if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
     e = slikl::launch_zero(ws + wp.zero_off, 256, s);
     if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
+    if (mode == 2) {
+        e = slikl::launch_zero(pb.dI_map, wp.dimap_bytes, s);
+        if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
+    }
     if (!f16 && t2 > 0) {
         e = slikl::launch_k_to_f16(pb, (uint16_t *)(ws + wp.k16_off), (float *)(ws + wp.scale_off), s);
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
     }
-    if (det) {
+    if (mode == 1) {
         e = slikl::launch_det_scale(pb, f16, (float *)(ws + wp.scale_off), s);
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
     }
@@ -236,7 +295,12 @@ slikl_status slikl_grad(const slikl_desc *desc, const void *q, const void *k, co
         e = slikl::launch_grad_fused(pb, head_tile(pb.group), f16, mode, parts, s);
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
     }
-    e = slikl::launch_finalize_dk(pb, f16, det, s);
+    if (mode == 2) {
+        e = slikl::launch_dense_dk(pb, head_tile(pb.group), f16, wp.rsplits, s);
+        if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
+        return SLIKL_OK;
+    }
+    e = slikl::launch_finalize_dk(pb, f16, mode == 1, s);
     if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
     return SLIKL_OK;
 }

@@ -27,7 +27,10 @@ struct Problem {
     float *dI_map;           // [U, s2max] dI summed over the slots naming j (0 elsewhere)
     uint32_t *mask_map;      // [U, s2max, HP/32] S > 0 head bits of (u, j)
     int32_t *row_range;      // [U, 2] smallest / largest j named by u (-1 if none)
-    uint32_t *dense_max;     // max over units of max|w| * max|dI| (float bits)
+    uint32_t *dense_max;     // max over units of max|w| max|dI| 2^-eq (float bits)
+    uint16_t *q16;           // [T1, N1, D] fp16 queries scaled by 2^eq per unit (bf16 inputs)
+    int32_t *q16_exp;        // [U] eq per unit
+    float *dk_part;          // [RS, T2, N2, D] per-row-split partial dK sums
     int64_t s2max;           // key length of the dense maps
     const int32_t *cu_q;     // [batch + 1] or null (BSND)
     const int32_t *cu_k;     // [batch + 1] or null (BSND)
@@ -46,6 +49,9 @@ struct WorkspacePlan {
     size_t scale_off;               // scale block (16 x 32-bit)
     size_t k16_off, k16_bytes;      // fp16 copy of k (bf16 inputs only)
     size_t zero_off;                // 256 zero bytes
+    int mode;                       // dK strategy (see launch_grad_fused)
+    int rsplits;                    // dense mode: query-row ranges of the key-major kernel
+    size_t dimap_off, dimap_bytes, maskmap_off, range_off, qexp_off, q16_off, part_off;
     size_t total;
 };
 
@@ -56,6 +62,7 @@ hipError_t launch_grad_fused(const Problem &pb, int hp, bool f16, int mode, int 
                              hipStream_t stream);
 int grad_fused_blocks_per_cu(int hp, int d, bool f16, int mode);
 hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t stream);
+hipError_t launch_dense_dk(const Problem &pb, int hp, bool f16, int rsplits, hipStream_t stream);
 hipError_t launch_finalize_dk(const Problem &pb, bool f16, bool det, hipStream_t stream);
 hipError_t launch_det_scale(const Problem &pb, bool f16, float *scale_block, hipStream_t stream);
 hipError_t launch_k_to_f16(const Problem &pb, uint16_t *k16, float *scale_block, hipStream_t stream);

@@ -45,10 +45,11 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_struct_layout_matches_header():
-    # 4 x int32, 7 x int64, 2 pointers, 2 x int32
-    assert ctypes.sizeof(SliklDesc) == 96
+    # 4 x int32, 7 x int64, 2 pointers, 3 x int32 (+4 bytes of tail padding)
+    assert ctypes.sizeof(SliklDesc) == 104
     assert SliklDesc.cu_seqlens_q.offset == 72
     assert SliklDesc.num_parts.offset == 88
+    assert SliklDesc.dk_mode.offset == 96
 
 
 def good_desc(**kw):
@@ -61,6 +62,7 @@ def good_desc(**kw):
     d.cu_seqlens_q = d.cu_seqlens_k = None
     d.num_parts = 0
     d.split_mode = 0
+    d.dk_mode = 0
     for k, v in kw.items():
         setattr(d, k, v)
     return d
@@ -73,19 +75,30 @@ def ws(lib, d):
 
 
 def test_workspace_size_of_the_dsv32_shape(lib):
-    st, n = ws(lib, good_desc())
+    st, n = ws(lib, good_desc(dk_mode=1))
     assert st == 0
     acc = 4096 * 1 * 128 * 4
     assert n >= acc + 2080 * 4 + (4096 + 1) * 8
-    st, n_det = ws(lib, good_desc(deterministic=1))
+    st, n_det = ws(lib, good_desc(deterministic=1, dk_mode=1))
     assert st == 0 and n_det >= n + 4096 * 128 * 4
+    # dense records: dI and 64 head bits per (row, key) dominate
+    st, n_dense = ws(lib, good_desc())
+    assert st == 0 and n_dense >= 4096 * 4096 * (4 + 8)
+
+
+def test_dense_mode_needs_bsnd(lib):
+    cu = (ctypes.c_int32 * 2)(0, 4096)
+    d = good_desc(layout_q=1, layout_k=1, dk_mode=2)
+    d.cu_seqlens_q = ctypes.cast(cu, ctypes.c_void_p)
+    d.cu_seqlens_k = ctypes.cast(cu, ctypes.c_void_p)
+    assert ws(lib, d)[0] == 3
 
 
 @pytest.mark.parametrize("field,value,status", [
     ("layout_q", 2, 2), ("layout_k", -1, 2), ("dtype", 5, 2), ("deterministic", 2, 2),
     ("batch", 0, 2), ("s1", 0, 2), ("s2", 0, 2), ("n1", 0, 2), ("n1", 129, 2),
     ("n2", 3, 2), ("n2", 0, 2), ("d", 96, 2), ("d", 256, 2), ("topk", 0, 2), ("topk", 2049, 2),
-    ("num_parts", 2049, 2), ("num_parts", -1, 2), ("split_mode", 2, 2),
+    ("num_parts", 2049, 2), ("num_parts", -1, 2), ("split_mode", 2, 2), ("dk_mode", 3, 2),
     ("layout_q", 1, 1),                      # TND q without cu_seqlens_q
     ("layout_k", 1, 1),                      # TND k without cu_seqlens_k
     ("s1", 1 << 40, 2),                      # more than 2^31 elements

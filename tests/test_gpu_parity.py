@@ -60,12 +60,17 @@ SMALL = {
 }
 
 
+DK_MODES = [("scatter", False), ("scatter", True), ("dense", False)]
+
+
 @pytest.mark.parametrize("name", list(SMALL))
-@pytest.mark.parametrize("det", [False, True])
-def test_small_parity(name, det):
-    _say(f"[parity] {name} det={det}")
+@pytest.mark.parametrize("dk_mode,det", DK_MODES)
+def test_small_parity(name, dk_mode, det):
     x = make_inputs(SMALL[name])
-    got = run_gpu(x, deterministic=det)
+    if dk_mode == "dense" and x.layout_q != "BSND":
+        pytest.skip("the dense dK path takes BSND inputs")
+    _say(f"[parity] {name} dk_mode={dk_mode} det={det}")
+    got = run_gpu(x, deterministic=det, dk_mode=dk_mode)
     ref = oracle(x)
     check_close(got, ref, label=name)
     if name == "no_valid_rows":
@@ -114,21 +119,22 @@ def test_results_do_not_depend_on_metadata():
     torch.cuda.synchronize()
 
 
-def test_deterministic_mode_is_bitwise_reproducible():
+@pytest.mark.parametrize("dk_mode", ["scatter", "dense"])
+def test_deterministic_mode_is_bitwise_reproducible(dk_mode):
     import torch
     x = make_inputs(SMALL["sink_zipf_small"])
     t = to_device(x)
-    first = run_gpu(x, t, deterministic=True)
+    first = run_gpu(x, t, deterministic=True, dk_mode=dk_mode)
     s = torch.cuda.Stream()
     for i in range(6):
         if i % 2:
             with torch.cuda.stream(s):
-                again = run_gpu(x, t, deterministic=True)
+                again = run_gpu(x, t, deterministic=True, dk_mode=dk_mode)
         else:
-            again = run_gpu(x, t, deterministic=True)
+            again = run_gpu(x, t, deterministic=True, dk_mode=dk_mode)
         for name in first:
             assert np.array_equal(first[name], again[name]), (i, name)
-    check_close(first, run_gpu(x, t, deterministic=False), what=("dk",))
+    check_close(first, run_gpu(x, t, deterministic=False, dk_mode="scatter"), what=("dk",))
 
 
 def test_slot_order_and_padding_invariance():
