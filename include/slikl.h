@@ -87,7 +87,10 @@ enum { SLIKL_DK_AUTO = 0, SLIKL_DK_SCATTER = 1, SLIKL_DK_DENSE = 2 };
 #define SLIKL_METADATA_HEADER 16
 #define SLIKL_MAX_PARTS 2048
 #define SLIKL_METADATA_INTS 2080
-#define SLIKL_UNIT_OVERHEAD 64
+/* Fixed cost of one unit in valid-slot equivalents for the WEIGHTED split
+ * (loads, compaction, softmax and epilogue latency of a unit vs the per-slot
+ * cost of the two key passes, measured on MI355X). */
+#define SLIKL_UNIT_OVERHEAD 512
 
 typedef struct slikl_desc {
     int32_t layout_q;        /* SLIKL_LAYOUT_*                                        */

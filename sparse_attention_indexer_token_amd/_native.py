@@ -27,7 +27,7 @@ DK_MODE = {"auto": 0, "scatter": 1, "dense": 2}
 METADATA_HEADER = 16
 MAX_PARTS = 2048
 METADATA_INTS = 2080
-UNIT_OVERHEAD = 64
+UNIT_OVERHEAD = 512
 
 EXPORTS = ("slikl_grad_workspace_size", "slikl_grad_parts", "slikl_grad_metadata",
            "slikl_grad", "slikl_status_string")

@@ -11,10 +11,10 @@
 // the partials in a fixed order.  No atomics, and the result is bitwise
 // reproducible.
 //
-// Inputs come from the fused kernel's dense records: dI[u, j], the S > 0 head
-// bits of (u, j), the key range named by each unit u, fp16 queries scaled by a
-// per-unit power of two 2^eq[u], and a global bound B = max_u max|w| max|dI|
-// 2^-eq[u].  With sA = 2^e, B sA < 2^15, the A operand w dI sA 2^-eq[u] fits
+// Inputs come from the fused kernel's dense records: dI[u, j] (int32 fixed
+// point, exponent ed[u]), the S > 0 head bits of (u, j), the key range named by
+// each unit u, fp16 queries scaled by a per-unit power of two 2^eq[u], and a
+// global bound B = max_u max|w| max|dI| 2^-eq[u].  With sA = 2^e, B sA < 2^15, the A operand w dI sA 2^-eq[u] fits
 // fp16 and is split into high and low fp16 parts (two MFMAs, about 22
 // significant bits: the dK sums over many rows can cancel far below their
 // terms); q in fp16 is exact.  acc / sA is dK.
@@ -113,6 +113,8 @@ __global__ __launch_bounds__(kBlock, 2) void dense_dk_kernel(Problem pb, int rsp
                                              0);
         }
     };
+    // record of (row r, this lane's key): dI (fixed point), head words, and the
+    // exponent that turns the fixed-point dI into dI 2^-eq
     auto load_rec = [&](int r, float &dI, uint32_t (&mw)[NH], int &eq) {
         const int u = r * pb.n2 + g;
         dI = 0.f;
@@ -120,11 +122,11 @@ __global__ __launch_bounds__(kBlock, 2) void dense_dk_kernel(Problem pb, int rsp
         for (int hb = 0; hb < NH; ++hb) mw[hb] = 0u;
         if (jok) {
             const size_t base = (size_t)u * pb.s2max + myj;
-            dI = pb.dI_map[base];
+            dI = (float)pb.dI_map[base];
 #pragma unroll
             for (int hb = 0; hb < NH; ++hb) mw[hb] = pb.mask_map[base * NH + hb];
         }
-        eq = F16 ? 0 : pb.q16_exp[u];
+        eq = pb.rec_exp[2 * u] + pb.rec_exp[2 * u + 1];
     };
 
     f32x16 acc[NDT];

@@ -96,6 +96,24 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t x) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// Workgroup barrier for LDS traffic only: waits for this wave's LDS operations
+// but not for its outstanding global loads and stores.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// m = 2 m + (v > 0); returns max(v, 0) (v_cmp, v_cndmask, v_addc on VCC)
+__device__ __forceinline__ float relu_push_bit(float v, uint32_t &m) {
+    float r;
+    asm("v_cmp_lt_f32 vcc, 0, %2\n\t"
+        "v_cndmask_b32 %0, 0, %2, vcc\n\t"
+        "v_addc_co_u32 %1, vcc, %1, %1, vcc"
+        : "=&v"(r), "+v"(m)
+        : "v"(v)
+        : "vcc");
+    return r;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
@@ -111,17 +129,17 @@ __device__ __forceinline__ float wave_sum(float v) {
 // Block-wide reductions for a 256-thread block; `red` holds >= 4 floats.
 __device__ __forceinline__ float block_max(float v, float *red) {
     v = wave_max(v);
-    __syncthreads();
+    lds_barrier();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
+    lds_barrier();
     return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 __device__ __forceinline__ float block_sum(float v, float *red) {
     v = wave_sum(v);
-    __syncthreads();
+    lds_barrier();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
+    lds_barrier();
     return (red[0] + red[1]) + (red[2] + red[3]);
 }
 
@@ -131,12 +149,38 @@ __device__ __forceinline__ int block_max_int(int v, int *red) {
         int x = __shfl_xor(v, o);
         v = x > v ? x : v;
     }
-    __syncthreads();
+    lds_barrier();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-    __syncthreads();
+    lds_barrier();
     int a = red[0] > red[1] ? red[0] : red[1];
     int b = red[2] > red[3] ? red[2] : red[3];
     return a > b ? a : b;
+}
+
+// Several block-wide reductions with one barrier pair: on return mx[i] holds
+// the block maximum of mx[i] and sm[i] the block sum of sm[i].  `red` holds
+// at least 4 * (NM + NS) floats.
+template <int NM, int NS>
+__device__ __forceinline__ void block_reduce_multi(float (&mx)[NM], float (&sm)[NS], float *red) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) mx[i] = wave_max(mx[i]);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) sm[i] = wave_sum(sm[i]);
+    lds_barrier();
+    if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < NM; ++i) red[wave * (NM + NS) + i] = mx[i];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) red[wave * (NM + NS) + NM + i] = sm[i];
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < NM; ++i)
+        mx[i] = fmaxf(fmaxf(red[i], red[(NM + NS) + i]), fmaxf(red[2 * (NM + NS) + i], red[3 * (NM + NS) + i]));
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+        sm[i] = (red[NM + i] + red[(NM + NS) + NM + i]) + (red[2 * (NM + NS) + NM + i] + red[3 * (NM + NS) + NM + i]);
 }
 
 // Exclusive prefix sum over the block; `tmp` holds >= 4 ints.
@@ -148,13 +192,22 @@ __device__ __forceinline__ int block_excl_scan(int v, int *tmp, int *total) {
         int y = __shfl_up(x, o);
         if (lane >= o) x += y;
     }
-    __syncthreads();
+    lds_barrier();
     if (lane == 63) tmp[wave] = x;
-    __syncthreads();
+    lds_barrier();
     int off = 0;
     for (int i = 0; i < wave; ++i) off += tmp[i];
     *total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
     return off + x - v;
+}
+
+// e such that amax * 2^e < 2^15 (0 for zero or non-finite amax), clamped
+__device__ __forceinline__ int pow2_exponent_below_2p15(float amax) {
+    if (!(amax > 0.f) || !(amax < INFINITY)) return 0;
+    int ex;
+    frexpf(amax, &ex);
+    int e = 15 - ex;
+    return e > 100 ? 100 : (e < -100 ? -100 : e);
 }
 
 // Batch of flattened row `r` given cumulative lengths cu[0..batch].

@@ -23,12 +23,11 @@
 //           both operands.  dq = w U and, because U q = sum_s dI ReLU(S),
 //           dW = <q, U> per head: one dot product per row instead of per-slot
 //           bookkeeping.
-//   dK      scatter mode: P'[s,:] = sum_h 1[S>0] w_h q_h on MFMA (the 0/1 mask is
-//           exact in fp16; w is split into fp16 high and low parts, two MFMAs),
+//   dK      P'[s,:] = sum_h 1[S>0] w_h q_h on MFMA (the 0/1 mask is exact in
+//           fp16; w is split into fp16 high and low parts, two MFMAs),
 //           P = dI_s P' in fp32, added into the dK accumulator with fp32
-//           atomics or, deterministic, int64 fixed-point atomics.
-//           dense mode: the kernel instead writes per (unit, key) records (dI and
-//           the S > 0 head mask) for the key-major dK kernel.
+//           atomics or, deterministic, int64 fixed-point atomics.  (Lists that
+//           cover much of the key range take the dense strategy instead.)
 // fp16 MFMA for pass 2 with both input dtypes: one bf16 rounding (8
 // significant bits) of dS is too coarse for the elementwise dq tolerance where
 // terms cancel; fp16 keeps 11.  bf16 keys come from an fp16 copy made once
@@ -74,20 +73,10 @@ __device__ __forceinline__ uint32_t select_bits(uint32_t v, uint64_t mask) {
     return r;
 }
 
-__device__ __forceinline__ int pow2_exponent_below_2p15(float amax) {
-    // e such that amax * 2^e < 2^15 (0 for zero or non-finite amax), clamped
-    if (!(amax > 0.f) || !(amax < INFINITY)) return 0;
-    int ex;
-    frexpf(amax, &ex);
-    int e = 15 - ex;
-    return e > 100 ? 100 : (e < -100 ? -100 : e);
-}
-
 template <int HP, int D, bool F16, int DKM>
 __global__ __launch_bounds__(kBlock, (HP == 128 ? 1 : 2)) void grad_fused_kernel(Problem pb) {
     using C = FusedCfg<HP, D>;
     constexpr int NH = C::NH, NKT = C::NKT, KC = C::KC, DCH = C::DCH, HCH = C::HCH;
-    constexpr bool DENSE = DKM == 2;
     constexpr bool DET = DKM == 1;
 
     __shared__ __attribute__((aligned(1024))) char s_scr[C::SCR];        // K chunks / q / U
@@ -236,7 +225,6 @@ __global__ __launch_bounds__(kBlock, (HP == 128 ? 1 : 2)) void grad_fused_kernel
                     s_I[cpos] = s_key[cpos] >= 0 ? I : -INFINITY;
                 }
             };
-            int kmin = 0x7fffffff, kmax = -1;   // dense records: batch-relative key range
             if (nchunks > 0) {
                 read_keys(0);
                 issue_chunk(pb.k, 0);
@@ -272,19 +260,6 @@ __global__ __launch_bounds__(kBlock, (HP == 128 ? 1 : 2)) void grad_fused_kernel
                     for (int j = 1; j < 16; ++j) bw = lane == j ? bal[j] : bw;
                     s_mask[((c * NKT + kb1) * NH + hb1) * 16 + lane] = bw;
                 }
-                if constexpr (DENSE) {
-                    // head mask of this lane's key for its 16 heads, bit (half*16 + j)
-                    uint32_t m16 = 0;
-#pragma unroll
-                    for (int j = 0; j < 16; ++j) m16 |= (sacc[j] > 0.f ? 1u : 0u) << j;
-                    const uint32_t other = __shfl_xor(m16, 32);
-                    if (half == 0 && mykey >= 0) {
-                        const int jrel = mykey - kbase;
-                        pb.mask_map[((size_t)u * pb.s2max + jrel) * NH + hb1] = m16 | (other << 16);
-                        kmin = jrel < kmin ? jrel : kmin;
-                        kmax = jrel > kmax ? jrel : kmax;
-                    }
-                }
             }
             __syncthreads();
             if (nchunks > 0) combine_I(nchunks - 1);
@@ -305,7 +280,6 @@ __global__ __launch_bounds__(kBlock, (HP == 128 ? 1 : 2)) void grad_fused_kernel
                     const float y = expf(s_I[j] - m) / Z;
                     yrow[sl] = y;
                     dI = y - prow[sl];
-                    if constexpr (DENSE) atomicAdd(pb.dI_map + (size_t)u * pb.s2max + (s_key[j] - kbase), dI);
                 }
                 s_I[j] = dI;
                 amax = fmaxf(amax, fabsf(dI));
@@ -314,62 +288,13 @@ __global__ __launch_bounds__(kBlock, (HP == 128 ? 1 : 2)) void grad_fused_kernel
             // power-of-two prescale of dI before its fp16 rounding
             const int eds = pow2_exponent_below_2p15(amax);
             const float dsc = ldexpf(1.f, eds), inv_dsc = ldexpf(1.f, -eds);
-            if constexpr (DENSE) {
-                // records of the key-major dK kernel: key range; bf16 queries as fp16
-                // scaled by a per-unit power of two 2^eq (exact to undo); the global
-                // bound max|w| max|dI| 2^-eq that fixes its fp16 scale for dS
-                const int kmx = block_max_int(kmax, s_itmp);
-                const int kmn = -block_max_int(-kmin, s_itmp);
-                float wabs = 0.f;
-                for (int h = 0; h < G; ++h) wabs = fmaxf(wabs, fabsf(s_w[h]));
-                int eq = 0;
-                if constexpr (!F16) {
-                    constexpr int NQV = (HP * DCH + kBlock - 1) / kBlock;
-                    u32x4 qv[NQV];
-                    float qm = 0.f;
-#pragma unroll
-                    for (int i = 0; i < NQV; ++i) {
-                        const int pc = tid + kBlock * i;
-                        const int h = pc / DCH, cc = pc % DCH;
-                        u32x4 v = {0u, 0u, 0u, 0u};
-                        if (pc < HP * DCH && h < G) v = *(const u32x4 *)(qrow + h * D + cc * 8);
-                        qv[i] = v;
-#pragma unroll
-                        for (int c = 0; c < 4; ++c)
-                            qm = fmaxf(qm, fmaxf(fabsf(__uint_as_float(v[c] << 16)),
-                                                 fabsf(__uint_as_float(v[c] & 0xffff0000u))));
-                    }
-                    qm = block_max(qm, s_red);
-                    eq = pow2_exponent_below_2p15(qm);
-                    const float qsc = ldexpf(1.f, eq);
-#pragma unroll
-                    for (int i = 0; i < NQV; ++i) {
-                        const int pc = tid + kBlock * i;
-                        const int h = pc / DCH, cc = pc % DCH;
-                        if (pc < HP * DCH && h < G) {
-                            u32x4 o;
-#pragma unroll
-                            for (int c = 0; c < 4; ++c)
-                                o[c] = pack2<true>(__uint_as_float(qv[i][c] << 16) * qsc,
-                                                   __uint_as_float(qv[i][c] & 0xffff0000u) * qsc);
-                            *(u32x4 *)(pb.q16 + (r * pb.n1 + g * G + h) * D + cc * 8) = o;
-                        }
-                    }
-                }
-                if (tid == 0) {
-                    pb.row_range[2 * u] = kmn;
-                    pb.row_range[2 * u + 1] = kmx;
-                    pb.q16_exp[u] = eq;
-                    atomicMax(pb.dense_max, __float_as_uint(wabs * amax * ldexpf(1.f, -eq)));
-                }
-            }
 
             // ---- dK-part operands (scatter mode): q in fp16 and w split in fp16 -------
             constexpr int NKH = HP / 16;
-            u32x4 qt[DENSE ? 1 : C::NPW][DENSE ? 1 : NKH];
-            uint32_t whi[DENSE ? 1 : NKH][4], wlo[DENSE ? 1 : NKH][4];
+            u32x4 qt[C::NPW][NKH];
+            uint32_t whi[NKH][4], wlo[NKH][4];
             float part_mul = 1.f;
-            if constexpr (!DENSE) {
+            {
                 float qinv = 1.f;
                 constexpr int NQV = (HP * DCH + kBlock - 1) / kBlock;
                 u32x4 qv[NQV];
@@ -501,7 +426,7 @@ __global__ __launch_bounds__(kBlock, (HP == 128 ? 1 : 2)) void grad_fused_kernel
                         }
                     }
                 }
-                if constexpr (!DENSE) {
+                {
                     // P'[key, d] = sum_h 1[S>0] w_h q[h, d]; P = dI_key P'; scatter-add
                     if (wave < C::NP_TILES) {
                         u32x4 ahi[NKH], alo[NKH];
@@ -624,11 +549,9 @@ static int blocks_one() {
 #define SLIKL_DISPATCH(HPV, DV, FN, ...)                                             \
     do {                                                                             \
         if (f16) {                                                                   \
-            if (mode == 2) return FN<HPV, DV, true, 2>(__VA_ARGS__);                 \
             if (mode == 1) return FN<HPV, DV, true, 1>(__VA_ARGS__);                 \
             return FN<HPV, DV, true, 0>(__VA_ARGS__);                                \
         }                                                                            \
-        if (mode == 2) return FN<HPV, DV, false, 2>(__VA_ARGS__);                    \
         if (mode == 1) return FN<HPV, DV, false, 1>(__VA_ARGS__);                    \
         return FN<HPV, DV, false, 0>(__VA_ARGS__);                                   \
     } while (0)

@@ -24,6 +24,13 @@ int64_t rows_k(const slikl_desc *d) { return d->layout_k == SLIKL_LAYOUT_BSND ? 
 // Field checks of the operator page's constraints section (dtypes, layouts,
 // cuSeqLens required for TND) and of this library's limits (N1 <= 128,
 // topk <= 2048 as for the 950-class products; D in {32, 64, 128}).
+// Whether the dense dK strategy can take this problem: BSND on both sides, keys
+// addressed with 32-bit byte offsets (< 2^31 bytes) and key indices exact in fp32.
+bool dense_fits(const slikl_desc *d) {
+    return d->layout_q == SLIKL_LAYOUT_BSND && d->layout_k == SLIKL_LAYOUT_BSND &&
+           (double)d->batch * d->s2 * d->n2 * d->d * 2.0 < 2147483648.0 && d->s2 < (1 << 24);
+}
+
 slikl_status validate(const slikl_desc *d) {
     if (!d) return SLIKL_ERR_NULLPTR;
     if (d->layout_q != SLIKL_LAYOUT_BSND && d->layout_q != SLIKL_LAYOUT_TND) return SLIKL_ERR_PARAM_INVALID;
@@ -50,18 +57,16 @@ slikl_status validate(const slikl_desc *d) {
     const int64_t t1 = rows_q(d), t2 = rows_k(d);
     if (t1 > lim / (d->n1 * d->d) || t1 > lim / (d->n2 * d->topk)) return SLIKL_ERR_PARAM_INVALID;
     if (t2 > lim / (d->n2 * d->d)) return SLIKL_ERR_PARAM_INVALID;
-    if (d->dk_mode == SLIKL_DK_DENSE &&
-        (d->layout_q != SLIKL_LAYOUT_BSND || d->layout_k != SLIKL_LAYOUT_BSND))
-        return SLIKL_ERR_UNSUPPORTED;
+    if (d->dk_mode == SLIKL_DK_DENSE && !dense_fits(d)) return SLIKL_ERR_UNSUPPORTED;
     return SLIKL_OK;
 }
 
 // Resolved dK strategy: 0 fp32 atomics, 1 int64 fixed-point atomics
 // (deterministic), 2 dense records + key-major kernel (deterministic).
 int dk_strategy(const slikl_desc *d) {
-    const bool bsnd = d->layout_q == SLIKL_LAYOUT_BSND && d->layout_k == SLIKL_LAYOUT_BSND;
-    if (d->dk_mode == SLIKL_DK_DENSE && bsnd) return 2;
-    if (d->dk_mode == SLIKL_DK_AUTO && bsnd && 2 * d->topk >= d->s2) {
+    const bool fits = dense_fits(d);
+    if (d->dk_mode == SLIKL_DK_DENSE && fits) return 2;
+    if (d->dk_mode == SLIKL_DK_AUTO && fits && 2 * d->topk >= d->s2) {
         // the dense records are sized [units, S2]; keep them modest
         const double bytes = (double)d->batch * d->s1 * d->n2 * d->s2 * 4.0 * (1 + head_tile(d->n1 / d->n2) / 32);
         if (bytes <= 8.0 * (1ull << 30)) return 2;
@@ -113,7 +118,7 @@ slikl::WorkspacePlan plan(const slikl_desc *d) {
         p.range_off = off;
         off = align_up(off + U * 8);
         p.qexp_off = off;
-        off = align_up(off + U * 4);
+        off = align_up(off + U * 8);
         p.q16_off = off;
         off = align_up(off + (d->dtype == SLIKL_DTYPE_BF16 ? (size_t)t1 * (size_t)d->n1 * (size_t)d->d * 2 : 0));
         p.part_off = off;
@@ -151,8 +156,11 @@ slikl_status resolve_parts(const slikl_desc *d, int32_t *parts) {
     if (hipGetDevice(&dev) != hipSuccess) return SLIKL_ERR_LAUNCH;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return SLIKL_ERR_LAUNCH;
-    int per_cu = slikl::grad_fused_blocks_per_cu(head_tile(d->n1 / d->n2), (int)d->d,
-                                                 d->dtype == SLIKL_DTYPE_F16, dk_strategy(d));
+    const int mode = dk_strategy(d);
+    const int hp = head_tile(d->n1 / d->n2);
+    const bool f16 = d->dtype == SLIKL_DTYPE_F16;
+    int per_cu = mode == 2 ? slikl::grad_dense_blocks_per_cu(hp, (int)d->d, f16)
+                           : slikl::grad_fused_blocks_per_cu(hp, (int)d->d, f16, mode);
     int64_t p = (int64_t)cus * per_cu;
     if (p > SLIKL_MAX_PARTS) p = SLIKL_MAX_PARTS;
     if (p < 1) p = 1;
@@ -254,10 +262,10 @@ slikl_status slikl_grad(const slikl_desc *desc, const void *q, const void *k, co
     pb.zero16 = (const uint16_t *)(ws + wp.zero_off);
     const int mode = wp.mode;
     if (mode == 2) {
-        pb.dI_map = (float *)(ws + wp.dimap_off);
+        pb.dI_map = (int32_t *)(ws + wp.dimap_off);
         pb.mask_map = (uint32_t *)(ws + wp.maskmap_off);
         pb.row_range = (int32_t *)(ws + wp.range_off);
-        pb.q16_exp = (int32_t *)(ws + wp.qexp_off);
+        pb.rec_exp = (int32_t *)(ws + wp.qexp_off);
         pb.q16 = (uint16_t *)(ws + wp.q16_off);
         pb.dk_part = (float *)(ws + wp.part_off);
         pb.dense_max = (uint32_t *)(ws + wp.scale_off) + 8;
@@ -292,7 +300,8 @@ slikl_status slikl_grad(const slikl_desc *desc, const void *q, const void *k, co
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
     }
     if (t1 > 0) {
-        e = slikl::launch_grad_fused(pb, head_tile(pb.group), f16, mode, parts, s);
+        e = mode == 2 ? slikl::launch_grad_dense(pb, head_tile(pb.group), f16, parts, s)
+                      : slikl::launch_grad_fused(pb, head_tile(pb.group), f16, mode, parts, s);
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
     }
     if (mode == 2) {

@@ -24,12 +24,13 @@ struct Problem {
     const uint16_t *k16;     // fp16 keys for the dq / dK-part contractions ([T2, N2, D])
     const uint16_t *zero16;  // 16 zero bytes (source of padding rows in direct-to-LDS gathers)
     // dense dK records (key-major dK kernel): per unit u and batch-relative key j
-    float *dI_map;           // [U, s2max] dI summed over the slots naming j (0 elsewhere)
+    int32_t *dI_map;         // [U, s2max] dI summed over the slots naming j, fixed point
+                             // with exponent rec_exp[2u+1] (0 where no slot names j)
     uint32_t *mask_map;      // [U, s2max, HP/32] S > 0 head bits of (u, j)
     int32_t *row_range;      // [U, 2] smallest / largest j named by u (-1 if none)
     uint32_t *dense_max;     // max over units of max|w| max|dI| 2^-eq (float bits)
     uint16_t *q16;           // [T1, N1, D] fp16 queries scaled by 2^eq per unit (bf16 inputs)
-    int32_t *q16_exp;        // [U] eq per unit
+    int32_t *rec_exp;        // [U, 2] eq (query scale) and the dI fixed-point exponent
     float *dk_part;          // [RS, T2, N2, D] per-row-split partial dK sums
     int64_t s2max;           // key length of the dense maps
     const int32_t *cu_q;     // [batch + 1] or null (BSND)
@@ -57,10 +58,13 @@ struct WorkspacePlan {
 
 // Kernel launchers (defined in the .hip files).  Return hipSuccess or the error.
 // mode: 0 scatter-add dK with fp32 atomics, 1 int64 fixed-point atomics
-// (deterministic), 2 dense records for the key-major dK kernel
+// (deterministic); the dense strategy has its own fused kernel
 hipError_t launch_grad_fused(const Problem &pb, int hp, bool f16, int mode, int grid,
                              hipStream_t stream);
 int grad_fused_blocks_per_cu(int hp, int d, bool f16, int mode);
+// fused kernel of the dense dK strategy (BSND): writes the records above
+hipError_t launch_grad_dense(const Problem &pb, int hp, bool f16, int grid, hipStream_t stream);
+int grad_dense_blocks_per_cu(int hp, int d, bool f16);
 hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t stream);
 hipError_t launch_dense_dk(const Problem &pb, int hp, bool f16, int rsplits, hipStream_t stream);
 hipError_t launch_finalize_dk(const Problem &pb, bool f16, bool det, hipStream_t stream);

@@ -140,3 +140,12 @@ def test_status_strings(lib):
     for s in range(6):
         assert lib.slikl_status_string(s)
     assert b"unknown" in lib.slikl_status_string(99)
+
+
+def test_header_constants_match_the_binding():
+    text = open(HEADER).read()
+    defs = dict(re.findall(r"^#define (SLIKL_\w+) (\d+)", text, flags=re.M))
+    assert int(defs["SLIKL_METADATA_HEADER"]) == _native.METADATA_HEADER
+    assert int(defs["SLIKL_MAX_PARTS"]) == _native.MAX_PARTS
+    assert int(defs["SLIKL_METADATA_INTS"]) == _native.METADATA_INTS
+    assert int(defs["SLIKL_UNIT_OVERHEAD"]) == _native.UNIT_OVERHEAD

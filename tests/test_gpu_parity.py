@@ -137,17 +137,20 @@ def test_deterministic_mode_is_bitwise_reproducible(dk_mode):
     check_close(first, run_gpu(x, t, deterministic=False, dk_mode="scatter"), what=("dk",))
 
 
-def test_slot_order_and_padding_invariance():
+@pytest.mark.parametrize("dk_mode", ["scatter", "dense"])
+def test_slot_order_and_padding_invariance(dk_mode):
+    """Permuting the slots (with -1 padding interleaved) permutes softmax_out and
+    leaves dq, dk, dw within tolerance (the fp16 rounding of dS may move by an
+    ulp with the summation order, so equality is not expected)."""
     x = make_inputs(SMALL["hp64_d128_ragged"])
-    a = run_gpu(x)
+    a = run_gpu(x, dk_mode=dk_mode)
     perm = np.random.default_rng(5).permutation(x.idx.shape[-1])
     x2 = make_inputs(SMALL["hp64_d128_ragged"])
     x2.idx = np.ascontiguousarray(x2.idx[..., perm])
     x2.p = np.ascontiguousarray(x2.p[..., perm])
-    b = run_gpu(x2)
+    b = run_gpu(x2, dk_mode=dk_mode)
     check_close(b, dict(a, softmax_out=a["softmax_out"][..., perm]), what=("softmax_out",))
-    for name in ("dq", "dw"):
-        assert np.allclose(a[name], b[name], rtol=1e-2, atol=1e-3)
+    check_close(b, oracle(x2), label="permuted slots")
 
 
 def test_out_of_range_index_is_skipped_and_flagged():
