@@ -43,6 +43,8 @@ namespace slikl {
 typedef __attribute__((address_space(3))) void lds_void_gd;
 typedef __attribute__((address_space(1))) void glb_void_gd;
 
+constexpr int TOPK_PER_THREAD = 2048 / kBlock;   // slots of one row per thread (topk <= 2048)
+
 template <int HP, int D>
 struct DenseFwdCfg {
     static constexpr int NH = HP / 32;          // 32-head tiles
@@ -77,12 +79,23 @@ __device__ __forceinline__ void wait_for_step(int ahead) {
     wait_vmcnt<0>();
 }
 
+// Inputs of one unit, loaded one unit ahead (during the previous epilogue).
+template <int NH, int NKS>
+struct UnitInputs {
+    u32x4 qa[NH][NKS];               // q rows as A operands of S (rows = heads, zero past G)
+    float wt;                        // w of head `tid` (tid < G)
+    int iv[TOPK_PER_THREAD];         // this thread's run of slots: key index, p
+    float pv[TOPK_PER_THREAD];
+};
+
 template <int HP, int D, bool F16>
 __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
     using C = DenseFwdCfg<HP, D>;
     constexpr int NH = C::NH, NDT = C::NDT, NKS = C::NKS, DCH = C::DCH, NL = C::NL, NST = C::NST;
     constexpr int TOPK_MAX = C::TOPK_MAX;
     constexpr int EPT = D / 8;                 // epilogue: U elements per thread (32 heads x D / 256)
+    constexpr int SPT_MAX = TOPK_PER_THREAD;
+    constexpr int SMASK = DCH >= 8 ? 7 : DCH - 1;
 
     __shared__ __attribute__((aligned(1024))) char s_ring[C::RING];
     __shared__ __attribute__((aligned(16))) uint32_t s_mask[NH * TOPK_MAX];   // [tile][position]
@@ -91,12 +104,13 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
     __shared__ __attribute__((aligned(16))) int32_t s_key[TOPK_MAX];
     __shared__ __attribute__((aligned(16))) uint16_t s_slot[TOPK_MAX];
     __shared__ __attribute__((aligned(16))) uint16_t s_d16[TOPK_MAX];          // fp16 dI 2^eds
-    __shared__ float s_w[HP];
+    __shared__ __attribute__((aligned(16))) float s_w[HP];
     __shared__ float s_red[32];
     __shared__ int s_itmp[8];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
     const int l32 = lane & 31, half = lane >> 5, l16 = lane & 15, grp = lane >> 4;
     const int U = (int)(pb.t1 * pb.n2);
     const int G = pb.group;
@@ -107,7 +121,7 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
     const float kinv = F16 ? 1.f : pb.det_scale[6];   // undoes the fp16 key copy's scale
     // bit of head row l32 of a tile inside a per-key head word
     const int hbit = 16 * ((l32 >> 2) & 1) + 4 * (l32 >> 3) + (l32 & 3);
-    char *ring = s_ring + wave * NST * C::STAGE;
+    char *const ring = s_ring + wave * (NST * C::STAGE);
     // range-checked views of the two key arrays: an offset at or past the end
     // reads zeros, which is what padding positions copy
     const uint32_t kbytes = (uint32_t)(pb.t2 * pb.n2 * D * 2);
@@ -115,422 +129,470 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
     const __amdgpu_buffer_rsrc_t rk16 =
         __builtin_amdgcn_make_buffer_rsrc((void *)pb.k16, (short)0, (int)kbytes, 0x00020000);
     constexpr uint32_t kPadOffset = 0x80000000u;      // >= kbytes (checked on the host)
+    const int krow_bytes = pb.n2 * D * 2;
 
-    for (int part = blockIdx.x; part < parts; part += gridDim.x) {
-        int ub = pb.metadata[16 + part], ue = pb.metadata[17 + part];
-        ub = ub < 0 ? 0 : ub;
-        ue = ue > U ? U : ue;
-        for (int u = ub; u < ue; ++u) {
-            const int r = u / pb.n2;
-            const int g = u - r * pb.n2;
-            const int b = r / S1;
-            const int kbase = b * S2;
-            const int32_t *irow = pb.idx + u * topk;
-            const float *prow = pb.p + u * topk;
-            float *yrow = pb.y + u * topk;
-            const uint16_t *qrow = pb.q + (r * pb.n1 + g * G) * D;
+    // ---- per-lane LDS offsets inside a stage (swizzled [32 rows][D] 16-bit tile) ----
+    // pass 1 B operand: row l32, columns 16 ks + 8 half; chunk (2 ks + half) ^ swz(l32)
+    // = ((2 (ks % 4) + half) ^ swz) + 8 (ks / 4)
+    int off1[NKS < 4 ? NKS : 4];
+    {
+        const int swz = (((l32 & 3) << 1) ^ ((l32 >> 2) & 1)) & SMASK;
+#pragma unroll
+        for (int k = 0; k < (NKS < 4 ? NKS : 4); ++k) off1[k] = l32 * DCH * 16 + (((2 * k + half) ^ swz) << 4);
+    }
+    // pass 2 transposing reads: row 16 ks + 8 half + 4 sec + l16/4, column
+    // 32 dt + 16 (grp & 1) + 4 (l16 & 3); the swizzle of such a row is
+    // ((l16/4) << 1 ^ sec) & SMASK
+    int off2[2][NDT];
+#pragma unroll
+    for (int sec = 0; sec < 2; ++sec) {
+        const int swz = (((l16 >> 2) << 1) ^ sec) & SMASK;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+            const int chunk = (4 * dt + 2 * (grp & 1) + ((l16 & 3) >> 1)) ^ swz;
+            off2[sec][dt] = (8 * half + (l16 >> 2)) * DCH * 16 + (chunk << 4) + 8 * (l16 & 1);
+        }
+    }
 
-            // ---- inputs: q rows -> A operands of S (rows = heads, zero past G), w,
-            //      and this thread's run of slots (all loads issued before any use)
-            u32x4 qa[NH][NKS];
+    // copies: lane l writes physical chunk l % DCH of row i*RPB + l/DCH, which holds
+    // logical chunk (l % DCH) ^ swizzle(row)
+    uint32_t cofs[NL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int row = i * C::RPB + lane / DCH;
+        const int swz = (((row & 3) << 1) ^ ((row >> 2) & 1)) & SMASK;
+        cofs[i] = (uint32_t)(((lane % DCH) ^ swz) << 4);
+    }
+
+    // ---- walk the units of this workgroup's parts, inputs one unit ahead ------------
+    int cpart = (int)blockIdx.x - (int)gridDim.x, cu = 0, cue = 0;
+    auto next_unit = [&]() -> bool {
+        ++cu;
+        while (cu >= cue) {
+            cpart += gridDim.x;
+            if (cpart >= parts) return false;
+            int a = pb.metadata[16 + cpart], e = pb.metadata[17 + cpart];
+            cu = a < 0 ? 0 : a;
+            cue = e > U ? U : e;
+        }
+        return true;
+    };
+    UnitInputs<NH, NKS> in;
+    auto load_inputs = [&](int uu) {
+        const int rr = uu / pb.n2, gg = uu - rr * pb.n2;
+        const uint16_t *qr = pb.q + (rr * pb.n1 + gg * G) * D;
+#pragma unroll
+        for (int ht = 0; ht < NH; ++ht) {
+            const int h = 32 * ht + l32;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+                in.qa[ht][ks] = h < G ? *(const u32x4 *)(qr + h * D + 16 * ks + 8 * half) : u32x4{0u, 0u, 0u, 0u};
+        }
+        in.wt = tid < G ? pb.w[rr * pb.n1 + gg * G + tid] : 0.f;
+        const int spt = (topk + kBlock - 1) / kBlock;
+        const int s0 = tid * spt;
+        const int32_t *ir = pb.idx + uu * topk;
+        const float *pr = pb.p + uu * topk;
+#pragma unroll
+        for (int i = 0; i < SPT_MAX; ++i) {
+            const bool ok = i < spt && s0 + i < topk;
+            in.iv[i] = ok ? ir[s0 + i] : -1;
+            in.pv[i] = ok ? pr[s0 + i] : 0.f;
+        }
+    };
+    bool have = next_unit();
+    if (have) load_inputs(cu);
+
+    while (have) {
+        const int u = cu;
+        const int r = u / pb.n2;
+        const int g = u - r * pb.n2;
+        const int b = r / S1;
+        const int kbase = b * S2;
+        float *yrow = pb.y + u * topk;
+        const uint16_t *qrow = pb.q + (r * pb.n1 + g * G) * D;
+        const int spt = (topk + kBlock - 1) / kBlock;
+        const int s0 = tid * spt;
+        if (tid < HP) s_w[tid] = in.wt;
+
+        // ---- compact the valid slots: key row, slot id, p ------------------------------
+        int cnt = 0;
+        uint32_t zslots = 0;              // in-range slots that are -1 / out of range
+#pragma unroll
+        for (int i = 0; i < SPT_MAX; ++i) {
+            const bool inr = i < spt && s0 + i < topk;
+            const bool ok = in.iv[i] >= 0 && in.iv[i] < S2;
+            cnt += ok ? 1 : 0;
+            zslots |= (inr && !ok) ? (1u << i) : 0u;
+        }
+        int nvalid;
+        int pos = block_excl_scan(cnt, s_itmp, &nvalid);
+        float kmx = -1.f, kmn_neg = -3.0e38f, pabs = 0.f, pmx = 0.f;
+#pragma unroll
+        for (int i = 0; i < SPT_MAX; ++i) {
+            const int v = in.iv[i];
+            if (v >= 0 && v < S2) {
+                s_key[pos] = kbase + v;
+                s_slot[pos] = (uint16_t)(s0 + i);
+                s_p[pos] = in.pv[i];
+                pabs += fabsf(in.pv[i]);
+                pmx = fmaxf(pmx, fabsf(in.pv[i]));
+                kmx = fmaxf(kmx, (float)v);
+                kmn_neg = fmaxf(kmn_neg, -(float)v);
+                ++pos;
+            }
+        }
+        const int nsteps = (nvalid + 127) >> 7;
+        for (int j = nvalid + tid; j < nsteps * 128; j += kBlock) s_key[j] = -1;
+
+        // |q| maximum of this thread's A operands (bf16 only: scale of the fp16 copy)
+        float qm = 0.f;
+        if constexpr (!F16) {
+#pragma unroll
+            for (int ht = 0; ht < NH; ++ht)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        qm = fmaxf(qm, fmaxf(fabsf(__uint_as_float(in.qa[ht][ks][c] << 16)),
+                                             fabsf(__uint_as_float(in.qa[ht][ks][c] & 0xffff0000u))));
+        }
+        // one barrier pair: maxima {|q|, |w|, |p|, key, -key} and the sum of |p|
+        // (its barriers also publish the compacted lists and s_w)
+        float mxv[5] = {qm, fabsf(in.wt), pmx, kmx, kmn_neg};
+        float smv[1] = {pabs};
+        block_reduce_multi<5, 1>(mxv, smv, s_red);
+        const float qmax = mxv[0], wabs = mxv[1], pmax = mxv[2], psum = smv[0];
+        const int kmax_i = (int)mxv[3];
+        const int kmin_i = nvalid > 0 ? (int)(-mxv[4]) : 0x7fffffff;
+
+        // ---- key stream: steps [0, nsteps) pass 1 (k), [nsteps, 2 nsteps) pass 2 ------
+        // Copy i of a step holds rows i*RPB .. +RPB of the wave's 32; lane l writes
+        // physical 16-byte chunk l % DCH of row i*RPB + l / DCH, i.e. logical chunk
+        // (l % DCH) ^ swizzle(row).  Padding positions read past the end: zeros.
+        const int T = 2 * nsteps;
+        uint32_t kofs[NL];                // byte offset of this lane's 16 bytes within a key row
+#pragma unroll
+        for (int i = 0; i < NL; ++i) kofs[i] = (uint32_t)(g * D * 2) + cofs[i];
+        auto issue = [&](int sigma) {
+            const bool second = sigma >= nsteps;
+            const int st = second ? sigma - nsteps : sigma;
+            char *dst = ring + (sigma % NST) * C::STAGE;
+            const int32_t *keys = s_key + st * 128 + wave * 32 + lane / DCH;
+            int key[NL];
+#pragma unroll
+            for (int i = 0; i < NL; ++i) key[i] = keys[i * C::RPB];      // all reads before the copies
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                const uint32_t off = key[i] >= 0 ? __umul24((uint32_t)key[i], (uint32_t)krow_bytes) + kofs[i] : kPadOffset;
+                if (second)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk16, (lds_void_gd *)(dst + i * 1024), 16, off, 0, 0, 0);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_gd *)(dst + i * 1024), 16, off, 0, 0, 0);
+            }
+        };
+#pragma unroll
+        for (int s = 0; s < NST - 1; ++s)
+            if (s < T) issue(s);
+
+        // ---- dense records of the unit (stores behind the first copies) ---------------
+        int eq = 0;
+        if constexpr (!F16) {
+            eq = pow2_exponent_below_2p15(qmax);
+            const float qsc = ldexpf(1.f, eq);
 #pragma unroll
             for (int ht = 0; ht < NH; ++ht) {
                 const int h = 32 * ht + l32;
 #pragma unroll
                 for (int ks = 0; ks < NKS; ++ks) {
-                    u32x4 v = {0u, 0u, 0u, 0u};
-                    if (h < G) v = *(const u32x4 *)(qrow + h * D + 16 * ks + 8 * half);
-                    qa[ht][ks] = v;
-                }
-            }
-            const float wt = tid < G ? pb.w[r * pb.n1 + g * G + tid] : 0.f;
-            constexpr int SPT_MAX = TOPK_MAX / kBlock;
-            const int spt = (topk + kBlock - 1) / kBlock;
-            const int s0 = tid * spt;
-            int iv[SPT_MAX];
-            float pv[SPT_MAX];
-#pragma unroll
-            for (int i = 0; i < SPT_MAX; ++i) {
-                const bool in = i < spt && s0 + i < topk;
-                iv[i] = in ? irow[s0 + i] : -1;
-                pv[i] = in ? prow[s0 + i] : 0.f;
-            }
-            if (tid < HP) s_w[tid] = wt;
-
-            // ---- compact the valid slots: key row, slot id, p --------------------------
-            int cnt = 0;
-#pragma unroll
-            for (int i = 0; i < SPT_MAX; ++i) {
-                const bool in = i < spt && s0 + i < topk;
-                const bool ok = iv[i] >= 0 && iv[i] < S2;
-                cnt += ok ? 1 : 0;
-                if (in && !ok) yrow[s0 + i] = 0.f;
-            }
-            int nvalid;
-            int pos = block_excl_scan(cnt, s_itmp, &nvalid);
-            float kmx = -1.f, kmn_neg = -3.0e38f, pabs = 0.f, pmx = 0.f;
-#pragma unroll
-            for (int i = 0; i < SPT_MAX; ++i) {
-                const int v = iv[i];
-                if (v >= 0 && v < S2) {
-                    s_key[pos] = kbase + v;
-                    s_slot[pos] = (uint16_t)(s0 + i);
-                    s_p[pos] = pv[i];
-                    pabs += fabsf(pv[i]);
-                    pmx = fmaxf(pmx, fabsf(pv[i]));
-                    kmx = fmaxf(kmx, (float)v);
-                    kmn_neg = fmaxf(kmn_neg, -(float)v);
-                    ++pos;
-                }
-            }
-            const int nsteps = (nvalid + 127) >> 7;
-            for (int j = nvalid + tid; j < nsteps * 128; j += kBlock) s_key[j] = -1;
-
-            // |q| maximum of this thread's A operands (bf16 only: fp16 copy scale)
-            float qm = 0.f;
-            if constexpr (!F16) {
-#pragma unroll
-                for (int ht = 0; ht < NH; ++ht)
-#pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks)
+                    if (ks % 4 == wave && h < G) {        // each wave writes a quarter
+                        u32x4 o;
 #pragma unroll
                         for (int c = 0; c < 4; ++c)
-                            qm = fmaxf(qm, fmaxf(fabsf(__uint_as_float(qa[ht][ks][c] << 16)),
-                                                 fabsf(__uint_as_float(qa[ht][ks][c] & 0xffff0000u))));
-            }
-            // one barrier pair: maxima {|q|, |w|, |p|, key, -key} and the sum of |p|
-            // (its barriers also publish the compacted lists and s_w)
-            float mxv[5] = {qm, fabsf(wt), pmx, kmx, kmn_neg};
-            float smv[1] = {pabs};
-            block_reduce_multi<5, 1>(mxv, smv, s_red);
-            const float qmax = mxv[0], wabs = mxv[1], pmax = mxv[2], psum = smv[0];
-            const int kmax_i = (int)mxv[3];
-            const int kmin_i = nvalid > 0 ? (int)(-mxv[4]) : 0x7fffffff;
-
-            float wv[NH][16];                 // head weights in the S-tile row order
-#pragma unroll
-            for (int ht = 0; ht < NH; ++ht)
-#pragma unroll
-                for (int j = 0; j < 16; ++j) wv[ht][j] = s_w[32 * ht + 8 * (j >> 2) + 4 * half + (j & 3)];
-
-            // ---- key stream: steps [0, nsteps) pass 1 (k), [nsteps, 2 nsteps) pass 2 --
-            // Copy i of a step holds rows i*RPB .. +RPB of the wave's 32; lane l writes
-            // physical 16-byte chunk l % DCH of row i*RPB + l / DCH, i.e. logical chunk
-            // (l % DCH) ^ swizzle(row).  Padding positions read past the end: zeros.
-            const int T = 2 * nsteps;
-            auto issue = [&](int sigma) {
-                const bool second = sigma >= nsteps;
-                const int st = second ? sigma - nsteps : sigma;
-                char *dst = ring + (sigma % NST) * C::STAGE;
-#pragma unroll
-                for (int i = 0; i < NL; ++i) {
-                    const int row = i * C::RPB + lane / DCH;
-                    const int key = s_key[st * 128 + wave * 32 + row];
-                    constexpr int smask = DCH >= 8 ? 7 : DCH - 1;
-                    const int swz = (((row & 3) << 1) ^ ((row >> 2) & 1)) & smask;
-                    const uint32_t off = key >= 0 ? (uint32_t)((key * pb.n2 + g) * D + ((lane % DCH) ^ swz) * 8) * 2u
-                                                  : kPadOffset;
-                    if (second)
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk16, (lds_void_gd *)(dst + i * 1024), 16, off, 0, 0, 0);
-                    else
-                        __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_gd *)(dst + i * 1024), 16, off, 0, 0, 0);
+                            o[c] = pack2<true>(__uint_as_float(in.qa[ht][ks][c] << 16) * qsc,
+                                               __uint_as_float(in.qa[ht][ks][c] & 0xffff0000u) * qsc);
+                        *(u32x4 *)(pb.q16 + (r * pb.n1 + g * G + h) * D + 16 * ks + 8 * half) = o;
+                    }
                 }
-            };
-#pragma unroll
-            for (int s = 0; s < NST - 1; ++s)
-                if (s < T) issue(s);
+            }
+        }
+        // dI fixed-point exponent: |sum of dI over the slots naming one key| <= 1 + sum|p|
+        int ed;
+        {
+            int ex;
+            frexpf(1.f + psum, &ex);     // 1 + psum < 2^ex
+            ed = 30 - ex;
+            ed = ed < -60 ? -60 : ed;
+        }
+        if (tid == 0) {
+            pb.row_range[2 * u] = kmin_i;
+            pb.row_range[2 * u + 1] = nvalid > 0 ? kmax_i : -1;
+            pb.rec_exp[2 * u] = eq;
+            pb.rec_exp[2 * u + 1] = ed;
+            // bound of |w dI_key| 2^-eq, dI_key summed over duplicate slots: <= 1 + sum|p|
+            atomicMax(pb.dense_max, __float_as_uint(wabs * (1.f + psum) * ldexpf(1.f, -eq)));
+        }
 
-            // ---- dense records of the unit (stores behind the first copies) -----------
-            int eq = 0;
-            if constexpr (!F16) {
-                eq = pow2_exponent_below_2p15(qmax);
-                const float qsc = ldexpf(1.f, eq);
+        // ---- pass 1: S tiles on MFMA; the VALU epilogue of one tile (ReLU, w, head
+        //      bits) runs while the next tile's MFMA chain executes ---------------------
+        float mloc = -INFINITY;           // running max of I over this lane's positions
+        {
+            float ip = 0.f;
+            uint32_t mw[NH];
+            f32x16 acc[NH];
+            auto post = [&](const f32x16 &a, int ht) {
+                uint32_t m = 0;
+#pragma unroll
+                for (int jq = 3; jq >= 0; --jq) {
+                    // head weights of rows 8 jq + 4 half + (0..3) of this tile
+                    const float4 w4 = *(const float4 *)(s_w + 32 * ht + 8 * jq + 4 * half);
+                    ip = fmaf(w4.w, relu_push_bit(a[4 * jq + 3], m), ip);
+                    ip = fmaf(w4.z, relu_push_bit(a[4 * jq + 2], m), ip);
+                    ip = fmaf(w4.y, relu_push_bit(a[4 * jq + 1], m), ip);
+                    ip = fmaf(w4.x, relu_push_bit(a[4 * jq + 0], m), ip);
+                }
+                mw[ht] = m;
+            };
+            auto finish = [&](int s) {        // I and head words of step s -> LDS
+                const int pos1 = s * 128 + wave * 32 + l32;
+                const bool valid = pos1 < nvalid;
+                const float I = ip + __shfl_xor(ip, 32);
+                ip = 0.f;
 #pragma unroll
                 for (int ht = 0; ht < NH; ++ht) {
-                    const int h = 32 * ht + l32;
-                    if (h < G) {
-#pragma unroll
-                        for (int ks = 0; ks < NKS; ++ks) {
-                            u32x4 o;
-#pragma unroll
-                            for (int c = 0; c < 4; ++c)
-                                o[c] = pack2<true>(__uint_as_float(qa[ht][ks][c] << 16) * qsc,
-                                                   __uint_as_float(qa[ht][ks][c] & 0xffff0000u) * qsc);
-                            *(u32x4 *)(pb.q16 + (r * pb.n1 + g * G + h) * D + 16 * ks + 8 * half) = o;
-                        }
-                    }
+                    const uint32_t other = __shfl_xor(mw[ht], 32);
+                    mw[ht] = valid ? (mw[ht] | (other << 16)) : 0u;
                 }
-            }
-            // dI fixed-point exponent: |sum of dI over the slots naming one key| <= 1 + sum|p|
-            int ed;
-            {
-                int ex;
-                frexpf(1.f + psum, &ex);     // 1 + psum < 2^ex
-                ed = 30 - ex;
-                ed = ed < -60 ? -60 : ed;
-            }
-            if (tid == 0) {
-                pb.row_range[2 * u] = kmin_i;
-                pb.row_range[2 * u + 1] = nvalid > 0 ? kmax_i : -1;
-                pb.rec_exp[2 * u] = eq;
-                pb.rec_exp[2 * u + 1] = ed;
-                // bound of |w dI_key| 2^-eq, dI_key summed over duplicate slots: <= 1 + sum|p|
-                atomicMax(pb.dense_max, __float_as_uint(wabs * (1.f + psum) * ldexpf(1.f, -eq)));
-            }
-
-            // ---- pass 1: S tiles on MFMA; the VALU epilogue of one tile (ReLU, w, head
-            //      bits) runs while the next tile's MFMA chain executes -------------------
-            float mloc = -INFINITY;           // running max of I over this lane's positions
-            {
-                float ip = 0.f;
-                uint32_t mw[NH];
-                f32x16 acc[NH];
-                auto post = [&](const f32x16 &a, int ht) {
-                    uint32_t m = 0;
+                if (valid) mloc = fmaxf(mloc, I);
+                if (half == 0) {
+                    s_I[pos1] = valid ? I : -INFINITY;
 #pragma unroll
-                    for (int j = 15; j >= 0; --j) ip = fmaf(wv[ht][j], relu_push_bit(a[j], m), ip);
-                    mw[ht] = m;
-                };
-                auto finish = [&](int s) {        // I and head words of step s -> LDS
-                    const int pos1 = s * 128 + wave * 32 + l32;
-                    const bool valid = pos1 < nvalid;
-                    const float I = ip + __shfl_xor(ip, 32);
-                    ip = 0.f;
-#pragma unroll
-                    for (int ht = 0; ht < NH; ++ht) {
-                        const uint32_t other = __shfl_xor(mw[ht], 32);
-                        mw[ht] = valid ? (mw[ht] | (other << 16)) : 0u;
-                    }
-                    if (valid) mloc = fmaxf(mloc, I);
-                    if (half == 0) {
-                        s_I[pos1] = valid ? I : -INFINITY;
-#pragma unroll
-                        for (int ht = 0; ht < NH; ++ht) s_mask[ht * TOPK_MAX + pos1] = mw[ht];
-                    }
-                };
-                for (int s = 0; s < nsteps; ++s) {
-                    wait_for_step<NST, NL>(T - 1 - s);
-                    if (s + NST - 1 < T) issue(s + NST - 1);
-                    const char *kb = ring + (s % NST) * C::STAGE;
-                    u32x4 bk[NKS];                  // B operands: this lane's key, all of d
-#pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks)
-                        bk[ks] = *(const u32x4 *)(kb + tile_off<DCH>(l32, 16 * ks + 8 * half));
-#pragma unroll
-                    for (int ht = 0; ht < NH; ++ht) {
-                        f32x16 c = {};
-#pragma unroll
-                        for (int ks = 0; ks < NKS; ++ks) c = mfma32<F16>(qa[ht][ks], bk[ks], c);
-                        if (ht == 0) {
-                            if (s > 0) {
-                                post(acc[NH - 1], NH - 1);
-                                finish(s - 1);
-                            }
-                        } else {
-                            post(acc[ht - 1], ht - 1);
-                        }
-                        acc[ht] = c;
-                    }
+                    for (int ht = 0; ht < NH; ++ht) s_mask[ht * TOPK_MAX + pos1] = mw[ht];
                 }
-                if (nsteps > 0) {
-                    post(acc[NH - 1], NH - 1);
-                    finish(nsteps - 1);
-                }
-            }
-
-            // ---- softmax over the valid positions: m, Z, y -> softmax_out, dI ----------
-            const float m = block_max(mloc, s_red);     // (its barriers publish s_I, s_mask)
-            constexpr int PPT = TOPK_MAX / kBlock;      // positions per thread
-            const int p0 = tid * PPT;
-            float e[PPT];
-            float zl = 0.f;
-            {
-                const float4 a0 = *(const float4 *)(s_I + p0), a1 = *(const float4 *)(s_I + p0 + 4);
-                const float iv8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-                for (int i = 0; i < PPT; ++i) {
-                    e[i] = p0 + i < nvalid ? expf(iv8[i] - m) : 0.f;
-                    zl += e[i];
-                }
-            }
-            const float Z = block_sum(zl, s_red + 8);
-            const float invZ = 1.f / Z;
-            // |dI| <= max(max y, max p) <= max(1/Z, max p): power-of-two prescale of dI
-            // before its fp16 rounding
-            const int eds = pow2_exponent_below_2p15(fmaxf(invZ, pmax));
-            const float dsc = ldexpf(1.f, eds);
-            {
-                const float4 b0 = *(const float4 *)(s_p + p0), b1 = *(const float4 *)(s_p + p0 + 4);
-                const float pp8[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-                uint32_t d16w[PPT / 2];
-#pragma unroll
-                for (int i = 0; i < PPT; i += 2) {
-                    float dd[2];
-#pragma unroll
-                    for (int k2 = 0; k2 < 2; ++k2) {
-                        const int pp = p0 + i + k2;
-                        dd[k2] = 0.f;
-                        if (pp < nvalid) {
-                            const float y = e[i + k2] * invZ;
-                            dd[k2] = y - pp8[i + k2];
-                            yrow[s_slot[pp]] = y;
-                            s_I[pp] = dd[k2];
-                        }
-                    }
-                    d16w[i / 2] = pack2<true>(dd[0] * dsc, dd[1] * dsc);
-                }
-                if (p0 < nsteps * 128) *(u32x4 *)(s_d16 + p0) = u32x4{d16w[0], d16w[1], d16w[2], d16w[3]};
-            }
-            lds_barrier();
-
-            // ---- pass 2: U += dS16 K16 over this wave's positions ---------------------
-            const float dfix = ldexpf(1.f, ed);
-            int32_t *dimap = pb.dI_map + (size_t)u * pb.s2max;
-            uint32_t *mmap = pb.mask_map + (size_t)u * pb.s2max * NH;
-            f32x16 uacc[NH][NDT];
-#pragma unroll
-            for (int ht = 0; ht < NH; ++ht)
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt) uacc[ht][dt] = f32x16{};
-            u32x4 qe[NH][EPT / 8 > 0 ? EPT / 8 : 1];   // epilogue q chunks, fetched at the last step
-            u32x2 qe4[NH];                              // (D = 32: 4 elements)
+            };
             for (int s = 0; s < nsteps; ++s) {
-                const int sigma = nsteps + s;
-                wait_for_step<NST, NL>(T - 1 - sigma);
-                // dK records of this wave's positions (issued before the next copies, so
-                // that the copies issued after an awaited one stay the last NL operations)
-                {
-                    const int pr = s * 128 + wave * 32 + l32;
-                    if (half == 0 && pr < nvalid) {
-                        const int jrel = s_key[pr] - kbase;
-                        atomicAdd(dimap + jrel, (int32_t)__float2int_rn(s_I[pr] * dfix));
-                        if constexpr (NH == 1) {
-                            mmap[jrel] = s_mask[pr];
-                        } else if constexpr (NH == 2) {
-                            *(u32x2 *)(mmap + jrel * 2) = u32x2{s_mask[pr], s_mask[TOPK_MAX + pr]};
-                        } else {
-                            *(u32x4 *)(mmap + jrel * 4) = u32x4{s_mask[pr], s_mask[TOPK_MAX + pr],
-                                                                s_mask[2 * TOPK_MAX + pr], s_mask[3 * TOPK_MAX + pr]};
+                wait_for_step<NST, NL>(T - 1 - s);
+                if (s + NST - 1 < T) issue(s + NST - 1);
+                const char *kb = ring + (s % NST) * C::STAGE;
+                u32x4 bk[NKS];                  // B operands: this lane's key, all of d
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) bk[ks] = *(const u32x4 *)(kb + off1[ks & 3] + 128 * (ks >> 2));
+#pragma unroll
+                for (int ht = 0; ht < NH; ++ht) {
+                    f32x16 c = {};
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) c = mfma32<F16>(in.qa[ht][ks], bk[ks], c);
+                    if (ht == 0) {
+                        if (s > 0) {
+                            post(acc[NH - 1], NH - 1);
+                            finish(s - 1);
                         }
+                    } else {
+                        post(acc[ht - 1], ht - 1);
                     }
-                }
-                if (sigma + NST - 1 < T) issue(sigma + NST - 1);
-                if (s == nsteps - 1) {
-                    const int hh = tid >> 3, c0 = (tid & 7) * EPT;
-#pragma unroll
-                    for (int ht = 0; ht < NH; ++ht) {
-                        const int h = 32 * ht + hh;
-                        if constexpr (EPT >= 8) {
-#pragma unroll
-                            for (int e8 = 0; e8 < EPT / 8; ++e8)
-                                qe[ht][e8] = h < G ? *(const u32x4 *)(qrow + h * D + c0 + 8 * e8) : u32x4{0u, 0u, 0u, 0u};
-                        } else {
-                            qe4[ht] = h < G ? *(const u32x2 *)(qrow + h * D + c0) : u32x2{0u, 0u};
-                        }
-                    }
-                }
-                const char *kb = ring + (sigma % NST) * C::STAGE;
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    // lane: head row l32 of each tile, positions pk .. pk+7
-                    const int pk = s * 128 + wave * 32 + 16 * ks + 8 * half;
-                    const u32x4 d16 = *(const u32x4 *)(s_d16 + pk);
-                    u32x4 a[NH];
-#pragma unroll
-                    for (int ht = 0; ht < NH; ++ht) {
-                        const u32x4 w0 = *(const u32x4 *)(s_mask + ht * TOPK_MAX + pk);
-                        const u32x4 w1 = *(const u32x4 *)(s_mask + ht * TOPK_MAX + pk + 4);
-                        const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-                        for (int pr2 = 0; pr2 < 4; ++pr2) {
-                            const uint32_t lo = (uint32_t)__builtin_amdgcn_sbfe((int)wd[2 * pr2], hbit, 1) & 0x0000ffffu;
-                            const uint32_t hi = (uint32_t)__builtin_amdgcn_sbfe((int)wd[2 * pr2 + 1], hbit, 1) & 0xffff0000u;
-                            a[ht][pr2] = (lo | hi) & d16[pr2];
-                        }
-                    }
-                    const int row = 16 * ks + 8 * half + (l16 >> 2);
-#pragma unroll
-                    for (int dt = 0; dt < NDT; ++dt) {
-                        const int col = 32 * dt + 16 * (grp & 1) + 4 * (l16 & 3);
-                        const u32x2 b0 = lds_read_tr(kb, tile_off<DCH>(row, col));
-                        const u32x2 b1 = lds_read_tr(kb, tile_off<DCH>(row + 4, col));
-                        const u32x4 bv = {b0.x, b0.y, b1.x, b1.y};
-#pragma unroll
-                        for (int ht = 0; ht < NH; ++ht) uacc[ht][dt] = mfma32<true>(a[ht], bv, uacc[ht][dt]);
-                    }
+                    acc[ht] = c;
                 }
             }
-
-            // ---- U = sum of the wave partials (fixed order); dq = w U, dW = <q, U> ------
-            const float uscale = ldexpf(1.f, -eds) * kinv;
-            float *red = (float *)s_ring;
-#pragma unroll
-            for (int ht = 0; ht < NH; ++ht) {
-                lds_barrier();          // ring free (pass 2 reads / previous tile's sums done)
-                float *mine = red + wave * 32 * D;
-#pragma unroll
-                for (int dt = 0; dt < NDT; ++dt)
-#pragma unroll
-                    for (int j = 0; j < 16; ++j)
-                        mine[(8 * (j >> 2) + 4 * half + (j & 3)) * D + 32 * dt + l32] = uacc[ht][dt][j];
-                lds_barrier();
-                const int hh = tid >> 3;
-                const int c0 = (tid & 7) * EPT;
-                const int h = 32 * ht + hh;
-                float dot = 0.f;
-                if (h < G && nsteps > 0) {
-                    float uv[EPT];
-#pragma unroll
-                    for (int e4 = 0; e4 < EPT; e4 += 4) {
-                        float4 acc4 = *(const float4 *)(red + hh * D + c0 + e4);
-#pragma unroll
-                        for (int wv2 = 1; wv2 < 4; ++wv2) {
-                            const float4 t4 = *(const float4 *)(red + wv2 * 32 * D + hh * D + c0 + e4);
-                            acc4.x += t4.x; acc4.y += t4.y; acc4.z += t4.z; acc4.w += t4.w;
-                        }
-                        uv[e4] = acc4.x * uscale;
-                        uv[e4 + 1] = acc4.y * uscale;
-                        uv[e4 + 2] = acc4.z * uscale;
-                        uv[e4 + 3] = acc4.w * uscale;
-                    }
-                    const float wh = s_w[h];
-                    uint16_t *dqh = pb.dq + (r * pb.n1 + g * G + h) * D + c0;
-                    // 16-bit q / dq in groups of 8 (4 when D = 32)
-                    constexpr int GRP = EPT >= 8 ? 8 : 4;
-#pragma unroll
-                    for (int e = 0; e < EPT; e += GRP) {
-                        uint32_t qv[GRP / 2], o[GRP / 2];
-                        if constexpr (GRP == 8) {
-                            const u32x4 t = qe[ht][e / 8];
-                            qv[0] = t.x; qv[1] = t.y; qv[2] = t.z; qv[3] = t.w;
-                        } else {
-                            const u32x2 t = qe4[ht];
-                            qv[0] = t.x; qv[1] = t.y;
-                        }
-#pragma unroll
-                        for (int c = 0; c < GRP / 2; ++c) {
-                            const float q0 = from16<F16>((uint16_t)(qv[c] & 0xffffu));
-                            const float q1 = from16<F16>((uint16_t)(qv[c] >> 16));
-                            dot = fmaf(q0, uv[e + 2 * c], fmaf(q1, uv[e + 2 * c + 1], dot));
-                            o[c] = (uint32_t)to16<F16>(wh * uv[e + 2 * c]) |
-                                   ((uint32_t)to16<F16>(wh * uv[e + 2 * c + 1]) << 16);
-                        }
-                        if constexpr (GRP == 8) *(u32x4 *)(dqh + e) = u32x4{o[0], o[1], o[2], o[3]};
-                        else *(u32x2 *)(dqh + e) = u32x2{o[0], o[1]};
-                    }
-                } else if (h < G) {
-                    // no valid slot: dq = 0, dW = 0
-                    uint16_t *dqh = pb.dq + (r * pb.n1 + g * G + h) * D + c0;
-#pragma unroll
-                    for (int e = 0; e < EPT; e += 4) *(u32x2 *)(dqh + e) = u32x2{0u, 0u};
-                }
-                dot += __shfl_xor(dot, 1);
-                dot += __shfl_xor(dot, 2);
-                dot += __shfl_xor(dot, 4);
-                if (h < G && (tid & 7) == 0) pb.dw[r * pb.n1 + g * G + h] = dot;
+            if (nsteps > 0) {
+                post(acc[NH - 1], NH - 1);
+                finish(nsteps - 1);
             }
-            lds_barrier();          // ring, s_w and the position lists are reused by the next unit
         }
+
+        // ---- prefetch the next unit's inputs (q, w and the slots of this one are dead);
+        //      their latency hides behind softmax, pass 2 and the epilogue
+        have = next_unit();
+        if (have) load_inputs(cu);
+
+        // ---- softmax over the valid positions: m, Z, y -> softmax_out, dI ------------
+        const float m = block_max(mloc, s_red);     // (its barriers publish s_I, s_mask)
+        constexpr int PPT = TOPK_MAX / kBlock;      // positions per thread
+        const int p0 = tid * PPT;
+        float e[PPT];
+        float zl = 0.f;
+        {
+            const float4 a0 = *(const float4 *)(s_I + p0), a1 = *(const float4 *)(s_I + p0 + 4);
+            const float iv8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+            for (int i = 0; i < PPT; ++i) {
+                e[i] = p0 + i < nvalid ? expf(iv8[i] - m) : 0.f;
+                zl += e[i];
+            }
+        }
+        const float Z = block_sum(zl, s_red + 8);
+        const float invZ = 1.f / Z;
+        // |dI| <= max(max y, max p) <= max(1/Z, max p): power-of-two prescale of dI
+        // before its fp16 rounding
+        const int eds = pow2_exponent_below_2p15(fmaxf(invZ, pmax));
+        const float dsc = ldexpf(1.f, eds);
+        {
+            const float4 b0 = *(const float4 *)(s_p + p0), b1 = *(const float4 *)(s_p + p0 + 4);
+            const float pp8[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+            uint32_t d16w[PPT / 2];
+#pragma unroll
+            for (int i = 0; i < PPT; i += 2) {
+                float dd[2];
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2) {
+                    const int pp = p0 + i + k2;
+                    dd[k2] = 0.f;
+                    if (pp < nvalid) {
+                        const float y = e[i + k2] * invZ;
+                        dd[k2] = y - pp8[i + k2];
+                        yrow[s_slot[pp]] = y;
+                        s_I[pp] = dd[k2];
+                    }
+                }
+                d16w[i / 2] = pack2<true>(dd[0] * dsc, dd[1] * dsc);
+            }
+            if (p0 < nsteps * 128) *(u32x4 *)(s_d16 + p0) = u32x4{d16w[0], d16w[1], d16w[2], d16w[3]};
+        }
+#pragma unroll
+        for (int i = 0; i < SPT_MAX; ++i)
+            if (zslots & (1u << i)) yrow[s0 + i] = 0.f;
+        lds_barrier();
+
+        // ---- pass 2: U += dS16 K16 over this wave's positions -------------------------
+        const float dfix = ldexpf(1.f, ed);
+        int32_t *dimap = pb.dI_map + (size_t)u * pb.s2max;
+        uint32_t *mmap = pb.mask_map + (size_t)u * pb.s2max * NH;
+        f32x16 uacc[NH][NDT];
+#pragma unroll
+        for (int ht = 0; ht < NH; ++ht)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) uacc[ht][dt] = f32x16{};
+        u32x4 qe[NH][EPT / 8 > 0 ? EPT / 8 : 1];   // epilogue q chunks, fetched at the last step
+        u32x2 qe4[NH];                              // (D = 32: 4 elements)
+        for (int s = 0; s < nsteps; ++s) {
+            const int sigma = nsteps + s;
+            wait_for_step<NST, NL>(T - 1 - sigma);
+            // dK records of this wave's positions (issued before the next copies, so
+            // that the copies issued after an awaited one stay the last NL operations)
+            {
+                const int pr = s * 128 + wave * 32 + l32;
+                if (half == 0 && pr < nvalid) {
+                    const int jrel = s_key[pr] - kbase;
+                    atomicAdd(dimap + jrel, (int32_t)__float2int_rn(s_I[pr] * dfix));
+                    if constexpr (NH == 1) {
+                        mmap[jrel] = s_mask[pr];
+                    } else if constexpr (NH == 2) {
+                        *(u32x2 *)(mmap + jrel * 2) = u32x2{s_mask[pr], s_mask[TOPK_MAX + pr]};
+                    } else {
+                        *(u32x4 *)(mmap + jrel * 4) = u32x4{s_mask[pr], s_mask[TOPK_MAX + pr],
+                                                            s_mask[2 * TOPK_MAX + pr], s_mask[3 * TOPK_MAX + pr]};
+                    }
+                }
+            }
+            if (sigma + NST - 1 < T) issue(sigma + NST - 1);
+            if (s == nsteps - 1) {
+                const int hh = tid >> 3, c0 = (tid & 7) * EPT;
+#pragma unroll
+                for (int ht = 0; ht < NH; ++ht) {
+                    const int h = 32 * ht + hh;
+                    if constexpr (EPT >= 8) {
+#pragma unroll
+                        for (int e8 = 0; e8 < EPT / 8; ++e8)
+                            qe[ht][e8] = h < G ? *(const u32x4 *)(qrow + h * D + c0 + 8 * e8) : u32x4{0u, 0u, 0u, 0u};
+                    } else {
+                        qe4[ht] = h < G ? *(const u32x2 *)(qrow + h * D + c0) : u32x2{0u, 0u};
+                    }
+                }
+            }
+            const char *kb = ring + (sigma % NST) * C::STAGE;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                // lane: head row l32 of each tile, positions pk .. pk+7
+                const int pk = s * 128 + wave * 32 + 16 * ks + 8 * half;
+                const u32x4 d16 = *(const u32x4 *)(s_d16 + pk);
+                u32x4 a[NH];
+#pragma unroll
+                for (int ht = 0; ht < NH; ++ht) {
+                    const u32x4 w0 = *(const u32x4 *)(s_mask + ht * TOPK_MAX + pk);
+                    const u32x4 w1 = *(const u32x4 *)(s_mask + ht * TOPK_MAX + pk + 4);
+                    const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+                    for (int pr2 = 0; pr2 < 4; ++pr2) {
+                        const uint32_t lo = (uint32_t)__builtin_amdgcn_sbfe((int)wd[2 * pr2], hbit, 1);
+                        const uint32_t hi = (uint32_t)__builtin_amdgcn_sbfe((int)wd[2 * pr2 + 1], hbit, 1);
+                        a[ht][pr2] = __builtin_amdgcn_perm(hi, lo, 0x05040100u) & d16[pr2];
+                    }
+                }
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt) {
+                    // rows 16 ks + 8 half + l16/4 (+4 for the second read)
+                    const u32x2 b0 = lds_read_tr(kb, off2[0][dt] + (16 * ks) * DCH * 16);
+                    const u32x2 b1 = lds_read_tr(kb, off2[1][dt] + (16 * ks + 4) * DCH * 16);
+                    const u32x4 bv = {b0.x, b0.y, b1.x, b1.y};
+#pragma unroll
+                    for (int ht = 0; ht < NH; ++ht) uacc[ht][dt] = mfma32<true>(a[ht], bv, uacc[ht][dt]);
+                }
+            }
+        }
+
+        // ---- U = sum of the wave partials (fixed order); dq = w U, dW = <q, U> --------
+        const float uscale = ldexpf(1.f, -eds) * kinv;
+        float *red = (float *)s_ring;
+#pragma unroll
+        for (int ht = 0; ht < NH; ++ht) {
+            lds_barrier();          // ring free (pass 2 reads / previous tile's sums done)
+            float *mine = red + wave * 32 * D;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    mine[(8 * (j >> 2) + 4 * half + (j & 3)) * D + 32 * dt + l32] = uacc[ht][dt][j];
+            lds_barrier();
+            const int hh = tid >> 3;
+            const int c0 = (tid & 7) * EPT;
+            const int h = 32 * ht + hh;
+            float dot = 0.f;
+            if (h < G) {
+                float uv[EPT];
+#pragma unroll
+                for (int e4 = 0; e4 < EPT; e4 += 4) {
+                    float4 acc4 = *(const float4 *)(red + hh * D + c0 + e4);
+#pragma unroll
+                    for (int wv2 = 1; wv2 < 4; ++wv2) {
+                        const float4 t4 = *(const float4 *)(red + wv2 * 32 * D + hh * D + c0 + e4);
+                        acc4.x += t4.x; acc4.y += t4.y; acc4.z += t4.z; acc4.w += t4.w;
+                    }
+                    uv[e4] = acc4.x * uscale;
+                    uv[e4 + 1] = acc4.y * uscale;
+                    uv[e4 + 2] = acc4.z * uscale;
+                    uv[e4 + 3] = acc4.w * uscale;
+                }
+                const float wh = s_w[h];
+                uint16_t *dqh = pb.dq + (r * pb.n1 + g * G + h) * D + c0;
+                // 16-bit q / dq in groups of 8 (4 when D = 32)
+                constexpr int GRP = EPT >= 8 ? 8 : 4;
+#pragma unroll
+                for (int e = 0; e < EPT; e += GRP) {
+                    uint32_t qv[GRP / 2], o[GRP / 2];
+                    if constexpr (GRP == 8) {
+                        const u32x4 t = nsteps > 0 ? qe[ht][e / 8] : u32x4{0u, 0u, 0u, 0u};
+                        qv[0] = t.x; qv[1] = t.y; qv[2] = t.z; qv[3] = t.w;
+                    } else {
+                        const u32x2 t = nsteps > 0 ? qe4[ht] : u32x2{0u, 0u};
+                        qv[0] = t.x; qv[1] = t.y;
+                    }
+#pragma unroll
+                    for (int c = 0; c < GRP / 2; ++c) {
+                        const float q0 = from16<F16>((uint16_t)(qv[c] & 0xffffu));
+                        const float q1 = from16<F16>((uint16_t)(qv[c] >> 16));
+                        dot = fmaf(q0, uv[e + 2 * c], fmaf(q1, uv[e + 2 * c + 1], dot));
+                        o[c] = (uint32_t)to16<F16>(wh * uv[e + 2 * c]) |
+                               ((uint32_t)to16<F16>(wh * uv[e + 2 * c + 1]) << 16);
+                    }
+                    if constexpr (GRP == 8) *(u32x4 *)(dqh + e) = u32x4{o[0], o[1], o[2], o[3]};
+                    else *(u32x2 *)(dqh + e) = u32x2{o[0], o[1]};
+                }
+            }
+            dot += __shfl_xor(dot, 1);
+            dot += __shfl_xor(dot, 2);
+            dot += __shfl_xor(dot, 4);
+            if (h < G && (tid & 7) == 0) pb.dw[r * pb.n1 + g * G + h] = dot;
+        }
+        lds_barrier();          // ring, s_w and the position lists are reused by the next unit
     }
 }
 

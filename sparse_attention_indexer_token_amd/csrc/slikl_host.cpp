@@ -25,10 +25,11 @@ int64_t rows_k(const slikl_desc *d) { return d->layout_k == SLIKL_LAYOUT_BSND ? 
 // cuSeqLens required for TND) and of this library's limits (N1 <= 128,
 // topk <= 2048 as for the 950-class products; D in {32, 64, 128}).
 // Whether the dense dK strategy can take this problem: BSND on both sides, keys
-// addressed with 32-bit byte offsets (< 2^31 bytes) and key indices exact in fp32.
+// addressed with 32-bit byte offsets (< 2^31 bytes) and key rows below 2^24
+// (24-bit multiplies; exact in fp32).
 bool dense_fits(const slikl_desc *d) {
     return d->layout_q == SLIKL_LAYOUT_BSND && d->layout_k == SLIKL_LAYOUT_BSND &&
-           (double)d->batch * d->s2 * d->n2 * d->d * 2.0 < 2147483648.0 && d->s2 < (1 << 24);
+           (double)d->batch * d->s2 * d->n2 * d->d * 2.0 < 2147483648.0 && (double)d->batch * d->s2 < 16777216.0;
 }
 
 slikl_status validate(const slikl_desc *d) {
