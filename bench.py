@@ -1,25 +1,31 @@
-#!/usr/bin/env python3
 """Benchmark of the sparse lightning-indexer KL-loss backward on one MI355X.
 
 One step = the whole hot path over one batch of synthetic input: the
-load-balancing metadata pre-pass, the accumulator fill, the fused backward
-kernel and the dK finalisation (dq, dk, dw and softmax_out all produced).
-Inputs are resident in HBM before the timed region starts.
+load-balancing metadata pre-pass and slikl_grad (accumulator / record fills,
+fp16 key copy, the fused S / softmax / dI / dW / dq kernel, the dK kernel and
+its finalisation): dq, dk, dw and softmax_out are all produced.  Inputs are
+resident in HBM before the timed region starts.
 
 Default workload: the DeepSeek-V3.2-shaped indexer (BSND B=1, S1=S2=4096,
 N1=64, N2=1, D=128, topk=2048, bf16, causal indices).
 
 Prints one JSON line.  Fields beyond the common contract:
-  roofline      the fused kernel against the bf16 dense MFMA peak; `achieved`
-                is the nominal 6*N1*D*topk FLOP per query token times the
-                tokens of one launch, divided by the launch window measured
-                with HIP events on the launch stream (window = accumulator
-                fill + fused kernel + dK finalisation);
+  roofline      the dominant kernel (the fused kernel) against the bf16 dense
+                MFMA peak.  `achieved` = its algorithmic FLOP per launch (the S
+                and dq contractions over the valid slots, 4 * N1 * D per valid
+                slot and key head) / its average launch time, measured with HIP
+                events recorded on the launch stream (slikl_grad_profiled).
+                `traffic` = HBM bytes per launch from rocprofv3 FETCH_SIZE /
+                WRITE_SIZE counters kept under profiles/, scaled by the same
+                counters read for a plain copy of known size; null when the
+                kernel source changed since the counters were taken.
+  phases_ms     average per-phase milliseconds of the profiled calls.
   cpu_baseline  the fp64 oracle on a bounded row sample, on the host cores.
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -31,7 +37,11 @@ if ROOT not in sys.path:
 
 METRIC = "query tokens/sec at N1=64 D=128 topk=2048 bf16; % of MFMA bf16 peak"
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}
-PEAK_HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grad_dense_kernel_dsv32_indexer_traffic.txt")
+KERNEL_SOURCES = {
+    "dense": os.path.join(ROOT, "sparse_attention_indexer_token_amd", "csrc", "grad_dense.hip"),
+    "scatter": os.path.join(ROOT, "sparse_attention_indexer_token_amd", "csrc", "grad_fused.hip"),
+}
 
 
 def parse():
@@ -41,7 +51,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv32_indexer")
     ap.add_argument("--deterministic", type=int, default=None, help="override the workload's mode")
-    ap.add_argument("--cpu-rows", type=int, default=1024, help="oracle sample size (rows)")
+    ap.add_argument("--cpu-rows", type=int, default=4096, help="oracle sample size (rows)")
+    ap.add_argument("--profiled-calls", type=int, default=5, help="calls timed per phase")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     return ap.parse_args()
 
@@ -60,9 +73,9 @@ def cpu_baseline(x, n_rows):
     slikl_grad_ref(x.q, x.k, x.w, x.idx, x.p, layout_q=x.layout_q, layout_k=x.layout_k,
                    cu_seqlens_q=x.cu_q, cu_seqlens_k=x.cu_k, rows=rows)
     dt = time.perf_counter() - t0
+    which = f"all {len(rows)} query rows" if stride == 1 else f"{len(rows)} query rows (every {stride}th row)"
     return {"value": len(rows) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{len(rows)} query rows (every {stride}th row) of the same workload, "
-                      f"fp64 NumPy oracle, {dt:.1f} s wall"}
+            "sample": f"{which} of the same workload, fp64 NumPy oracle, {dt:.1f} s wall"}
 
 
 def main():
@@ -75,6 +88,16 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.copy_bytes > 0:
+        # reference point for the HBM byte counters: one read and one write of a known size
+        src = torch.ones(args.copy_bytes // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes}), flush=True)
+        return 0
 
     import sparse_attention_indexer_token_amd as slikl
     from workloads import WORKLOADS, make_inputs
@@ -108,33 +131,39 @@ def main():
     out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(w), torch.empty_like(p))
     stream = torch.cuda.current_stream(dev)
 
-    def step(ev0=None, ev1=None):
+    def step():
         slikl.slikl_grad_metadata(q, k, idx, metadata=md, workspace=ws, **kw)
-        if ev0 is not None:
-            ev0.record(stream)
         slikl.slikl_grad(q, k, w, idx, p, metadata=md, workspace=ws, out=out, **kw)
-        if ev1 is not None:
-            ev1.record(stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize(dev)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    torch.cuda.synchronize(dev)
     t0 = time.perf_counter()
-    for e0, e1 in evs:
-        step(e0, e1)
+    for _ in range(args.steps):
+        step()
     torch.cuda.synchronize(dev)
     elapsed = time.perf_counter() - t0
-    win_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+
+    # per-phase times of the same call (HIP events on the launch stream), outside the
+    # timed region
+    phases = []
+    for _ in range(max(1, args.profiled_calls)):
+        _, ms = slikl.slikl_grad_profiled(q, k, w, idx, p, metadata=md, workspace=ws, out=out, **kw)
+        phases.append(ms)
+    phase_ms = {name: float(np.mean([ph[name] for ph in phases])) for name in phases[0]}
+    strategy = "dense" if phase_ms.get("dk", 0.0) > 0.0 else "scatter"
+    kernel = "grad_dense_kernel" if strategy == "dense" else "grad_fused_kernel"
 
     T1 = x.t1
+    G = wl.n1 // wl.n2
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = T1 * args.steps / elapsed
     flop_nominal = 6.0 * wl.n1 * wl.d * wl.topk * T1
-    flop_valid = 6.0 * (wl.n1 // wl.n2) * wl.d * x.valid_slots
-    achieved = flop_nominal / (win_ms * 1e-3) / 1e12
+    flop_valid = 6.0 * G * wl.d * x.valid_slots
+    # the fused kernel's own arithmetic: S and dq over the valid slots
+    flop_kernel = 4.0 * G * wl.d * x.valid_slots
+    kernel_ms = phase_ms["fused"]
+    achieved = flop_kernel / (kernel_ms * 1e-3) / 1e12
     peak = PEAK_MFMA_TFLOPS[wl.dtype]
     res = {
         "metric": METRIC,
@@ -148,20 +177,43 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": wl.dtype,
-        "data": "synthetic (seeded generators, shapes of the workload)",
+        "data": "synthetic (seeded generators with the workload's shapes and value recipes)",
         "config": {"workload": wl.name, "layout": wl.layout, "batch": x.batch, "T1": T1,
                    "T2": x.t2, "N1": wl.n1, "N2": wl.n2, "D": wl.d, "topk": wl.topk,
-                   "valid_slots": x.valid_slots, "deterministic": det},
+                   "valid_slots": x.valid_slots, "deterministic": det, "dk_strategy": strategy},
         "tflops_nominal_step": flop_nominal / (ms_per_step * 1e-3) / 1e12,
         "tflops_valid_step": flop_valid / (ms_per_step * 1e-3) / 1e12,
+        "frac_peak_nominal_step": flop_nominal / (ms_per_step * 1e-3) / 1e12 / peak,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": None,
-                     "kernel": "grad_fused_kernel", "window_ms": win_ms},
+                     "frac": achieved / peak, "traffic": traffic_bytes(kernel, wl.name, strategy),
+                     "kernel": kernel, "kernel_ms": kernel_ms, "flop_per_launch": flop_kernel},
+        "phases_ms": phase_ms,
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(x, args.cpu_rows)
     print(json.dumps(res), flush=True)
     return 0
+
+
+def traffic_bytes(kernel, workload, strategy):
+    """HBM bytes per launch from the committed counter summary, if it was taken
+    on this workload and on the current kernel source; else None."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    fields = dict(line.split(":", 1) for line in text.splitlines() if ":" in line and not line.startswith("#"))
+    fields = {k_.strip(): v.strip() for k_, v in fields.items()}
+    if fields.get("kernel") != kernel or fields.get("workload") != workload:
+        return None
+    src = KERNEL_SOURCES[strategy]
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if fields.get("source_sha256") != sha:
+        return None
+    try:
+        return float(fields["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 if __name__ == "__main__":

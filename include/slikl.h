@@ -149,6 +149,32 @@ slikl_status slikl_grad(const slikl_desc *desc, const void *q, const void *k,
                         void *dq, void *dk, float *dw, float *softmax_out,
                         void *workspace, size_t workspace_bytes, void *stream);
 
+/* Phases of one slikl_grad call, for slikl_grad_profiled. */
+enum {
+    SLIKL_PHASE_METADATA = 0,  /* metadata pre-pass (only when metadata == NULL)       */
+    SLIKL_PHASE_FILL = 1,      /* zero fills of accumulators / records               */
+    SLIKL_PHASE_KEY_COPY = 2,  /* fp16 copy of bf16 keys with its power-of-two scale  */
+    SLIKL_PHASE_DET_SCALE = 3, /* fixed-point scale of the deterministic scatter      */
+    SLIKL_PHASE_FUSED = 4,     /* the fused S / softmax / dI / dW / dq kernel          */
+    SLIKL_PHASE_DK = 5,        /* key-major dK kernel (dense strategy)                */
+    SLIKL_PHASE_DK_FINAL = 6,  /* dK finalisation (rounding / fixed-order reduce)     */
+    SLIKL_PHASES = 7
+};
+
+/* Same work and results as slikl_grad, for measurement: records HIP events on
+ * `stream` around each phase, waits for the last one, and writes the elapsed
+ * milliseconds of every phase to phase_ms[0 .. SLIKL_PHASES) (0 for a phase
+ * the call did not run).  Unlike slikl_grad it blocks the host until the
+ * stream reaches the end of the call.  phase_ms is host memory owned by the
+ * caller.  Errors as slikl_grad; NULLPTR also when phase_ms is NULL; LAUNCH
+ * when an event cannot be created or read. */
+slikl_status slikl_grad_profiled(const slikl_desc *desc, const void *q, const void *k,
+                                 const float *w, const int32_t *sparse_indices,
+                                 const float *attn_softmax_l1norm, const int32_t *metadata,
+                                 void *dq, void *dk, float *dw, float *softmax_out,
+                                 void *workspace, size_t workspace_bytes, void *stream,
+                                 float *phase_ms);
+
 /* Static description of a status code. */
 const char *slikl_status_string(slikl_status s);
 

@@ -22,7 +22,7 @@ from ._native import (  # noqa: F401
     UNIT_OVERHEAD, load,
 )
 
-__all__ = ["slikl_grad", "slikl_grad_metadata", "slikl_grad_workspace_size",
+__all__ = ["slikl_grad", "slikl_grad_profiled", "slikl_grad_metadata", "slikl_grad_workspace_size",
            "slikl_grad_parts", "slikl_status_string", "make_desc", "SliklDesc", "SliklError"]
 
 
@@ -150,6 +150,22 @@ def slikl_grad(q, k, w, sparse_indices, attn_softmax_l1norm, *, layout_q="BSND",
     ``out`` may hold preallocated (dq, dk, dw, softmax_out); ``workspace`` a
     uint8 device tensor of at least ``slikl_grad_workspace_size`` bytes.
     """
+    return _grad(q, k, w, sparse_indices, attn_softmax_l1norm, layout_q=layout_q, layout_k=layout_k,
+                 cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, deterministic=deterministic,
+                 metadata=metadata, num_parts=num_parts, split_mode=split_mode, dk_mode=dk_mode,
+                 workspace=workspace, out=out, profiled=False)[0]
+
+
+def slikl_grad_profiled(q, k, w, sparse_indices, attn_softmax_l1norm, **kw):
+    """slikl_grad plus the per-phase milliseconds (HIP events on the current
+    stream; blocks until the call has run).  Returns ((dq, dk, dw, softmax_out), {phase: ms})."""
+    return _grad(q, k, w, sparse_indices, attn_softmax_l1norm, profiled=True, **kw)
+
+
+def _grad(q, k, w, sparse_indices, attn_softmax_l1norm, *, layout_q="BSND", layout_k="BSND",
+          cu_seqlens_q=None, cu_seqlens_k=None, deterministic: bool = False,
+          metadata=None, num_parts: int = 0, split_mode: str = "weighted",
+          dk_mode: str = "auto", workspace=None, out: Optional[tuple] = None, profiled: bool = False):
     torch = _torch()
     desc = make_desc(q, k, sparse_indices, layout_q=layout_q, layout_k=layout_k,
                      cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
@@ -185,10 +201,11 @@ def slikl_grad(q, k, w, sparse_indices, attn_softmax_l1norm, *, layout_q="BSND",
     nbytes = _native.workspace_size(desc)
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-    _native.grad_raw(desc, q.data_ptr(), k.data_ptr(), w.data_ptr(), sparse_indices.data_ptr(),
-                     attn_softmax_l1norm.data_ptr(),
-                     metadata.data_ptr() if metadata is not None else 0,
-                     dq.data_ptr(), dk.data_ptr(), dw.data_ptr(), y.data_ptr(),
-                     workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                     _stream_handle(dev))
-    return dq, dk, dw, y
+    args = (desc, q.data_ptr(), k.data_ptr(), w.data_ptr(), sparse_indices.data_ptr(),
+            attn_softmax_l1norm.data_ptr(), metadata.data_ptr() if metadata is not None else 0,
+            dq.data_ptr(), dk.data_ptr(), dw.data_ptr(), y.data_ptr(),
+            workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_handle(dev))
+    if profiled:
+        return (dq, dk, dw, y), _native.grad_profiled_raw(*args)
+    _native.grad_raw(*args)
+    return (dq, dk, dw, y), None

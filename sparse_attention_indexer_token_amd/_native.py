@@ -30,7 +30,9 @@ METADATA_INTS = 2080
 UNIT_OVERHEAD = 512
 
 EXPORTS = ("slikl_grad_workspace_size", "slikl_grad_parts", "slikl_grad_metadata",
-           "slikl_grad", "slikl_status_string")
+           "slikl_grad", "slikl_grad_profiled", "slikl_status_string")
+
+PHASES = ("metadata", "fill", "key_copy", "det_scale", "fused", "dk", "dk_final")
 
 
 class SliklDesc(ctypes.Structure):
@@ -72,6 +74,9 @@ def load():
     lib.slikl_grad_metadata.restype = c_int32
     lib.slikl_grad.argtypes = [P(SliklDesc)] + [c_void_p] * 10 + [c_void_p, c_size_t, c_void_p]
     lib.slikl_grad.restype = c_int32
+    lib.slikl_grad_profiled.argtypes = [P(SliklDesc)] + [c_void_p] * 10 + [c_void_p, c_size_t, c_void_p,
+                                                                           P(ctypes.c_float)]
+    lib.slikl_grad_profiled.restype = c_int32
     lib.slikl_status_string.argtypes = [c_int32]
     lib.slikl_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -118,3 +123,12 @@ def grad_raw(desc: SliklDesc, q, k, w, idx, p, metadata, dq, dk, dw, y, ws, ws_b
                              p or None, metadata or None, dq or None, dk or None, dw or None,
                              y or None, ws or None, ws_bytes, stream or None),
            "slikl_grad")
+
+
+def grad_profiled_raw(desc: SliklDesc, q, k, w, idx, p, metadata, dq, dk, dw, y, ws, ws_bytes, stream) -> dict:
+    ms = (ctypes.c_float * len(PHASES))()
+    _check(load().slikl_grad_profiled(ctypes.byref(desc), q or None, k or None, w or None, idx or None,
+                                      p or None, metadata or None, dq or None, dk or None, dw or None,
+                                      y or None, ws or None, ws_bytes, stream or None, ms),
+           "slikl_grad_profiled")
+    return {name: float(ms[i]) for i, name in enumerate(PHASES)}

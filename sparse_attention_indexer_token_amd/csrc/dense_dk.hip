@@ -236,7 +236,10 @@ hipError_t launch_dense_dk(const Problem &pb, int hp, bool f16, int rsplits, hip
     else SLIKL_DENSE_CASE(128, 32) else SLIKL_DENSE_CASE(128, 64) else SLIKL_DENSE_CASE(128, 128)
     else return hipErrorInvalidValue;
 #undef SLIKL_DENSE_CASE
-    if (e != hipSuccess) return e;
+    return e;
+}
+
+hipError_t launch_dense_dk_reduce(const Problem &pb, bool f16, int rsplits, hipStream_t stream) {
     const size_t n = (size_t)pb.t2 * pb.n2 * pb.d;
     size_t blocks = (n + 255) / 256;
     if (blocks > 4096) blocks = 4096;

@@ -221,10 +221,53 @@ slikl_status slikl_grad_metadata(const slikl_desc *desc, const int32_t *sparse_i
     return e == hipSuccess ? SLIKL_OK : SLIKL_ERR_LAUNCH;
 }
 
-slikl_status slikl_grad(const slikl_desc *desc, const void *q, const void *k, const float *w,
-                        const int32_t *sparse_indices, const float *attn_softmax_l1norm,
-                        const int32_t *metadata, void *dq, void *dk, float *dw, float *softmax_out,
-                        void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// Optional per-phase timing with HIP events recorded on the launch stream.
+struct PhaseEvents {
+    bool on = false;
+    hipEvent_t ev[2 * SLIKL_PHASES] = {};
+    bool used[SLIKL_PHASES] = {};
+    hipStream_t s = nullptr;
+    bool init(hipStream_t st) {
+        s = st;
+        on = true;
+        for (int i = 0; i < 2 * SLIKL_PHASES; ++i)
+            if (hipEventCreate(&ev[i]) != hipSuccess) return false;
+        return true;
+    }
+    void begin(int p) {
+        if (on) hipEventRecord(ev[2 * p], s);
+    }
+    void end(int p) {
+        if (on) {
+            hipEventRecord(ev[2 * p + 1], s);
+            used[p] = true;
+        }
+    }
+    bool collect(float *ms) {
+        bool ok = true;
+        for (int p = 0; p < SLIKL_PHASES; ++p) {
+            ms[p] = 0.f;
+            if (!used[p]) continue;
+            if (hipEventSynchronize(ev[2 * p + 1]) != hipSuccess ||
+                hipEventElapsedTime(&ms[p], ev[2 * p], ev[2 * p + 1]) != hipSuccess)
+                ok = false;
+        }
+        return ok;
+    }
+    ~PhaseEvents() {
+        for (int i = 0; i < 2 * SLIKL_PHASES; ++i)
+            if (ev[i]) hipEventDestroy(ev[i]);
+    }
+};
+
+slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, const float *w,
+                       const int32_t *sparse_indices, const float *attn_softmax_l1norm,
+                       const int32_t *metadata, void *dq, void *dk, float *dw, float *softmax_out,
+                       void *workspace, size_t workspace_bytes, void *stream, PhaseEvents &pe) {
     if (!desc) return SLIKL_ERR_NULLPTR;
     slikl_status st = validate(desc);
     if (st != SLIKL_OK) return st;
@@ -243,9 +286,9 @@ slikl_status slikl_grad(const slikl_desc *desc, const void *q, const void *k, co
     if (st != SLIKL_OK) return st;
 
     hipStream_t s = (hipStream_t)stream;
+    if (pe.on && !pe.init(s)) return SLIKL_ERR_LAUNCH;
     char *ws = (char *)workspace;
     const bool f16 = desc->dtype == SLIKL_DTYPE_F16;
-    const bool det = desc->deterministic != 0;
 
     slikl::Problem pb = problem(desc);
     pb.q = (const uint16_t *)q;
@@ -276,43 +319,82 @@ slikl_status slikl_grad(const slikl_desc *desc, const void *q, const void *k, co
     hipError_t e = hipSuccess;
     if (!metadata) {
         int32_t *md = (int32_t *)(ws + wp.meta_off);
+        pe.begin(SLIKL_PHASE_METADATA);
         e = slikl::launch_metadata(pb, parts, desc->split_mode, SLIKL_UNIT_OVERHEAD, md,
                                    (int64_t *)(ws + wp.prefix_off), (int32_t *)(ws + wp.flags_off), s);
+        pe.end(SLIKL_PHASE_METADATA);
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
         metadata = md;
     }
     pb.metadata = metadata;
+    pe.begin(SLIKL_PHASE_FILL);
     e = slikl::launch_zero(pb.dk_acc, wp.acc_bytes, s);
+    if (e == hipSuccess) e = slikl::launch_zero(ws + wp.scale_off, 64, s);
+    if (e == hipSuccess) e = slikl::launch_zero(ws + wp.zero_off, 256, s);
+    if (e == hipSuccess && mode == 2) e = slikl::launch_zero(pb.dI_map, wp.dimap_bytes, s);
+    pe.end(SLIKL_PHASE_FILL);
     if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
-    e = slikl::launch_zero(ws + wp.scale_off, 64, s);
-    if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
-    e = slikl::launch_zero(ws + wp.zero_off, 256, s);
-    if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
-    if (mode == 2) {
-        e = slikl::launch_zero(pb.dI_map, wp.dimap_bytes, s);
-        if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
-    }
     if (!f16 && t2 > 0) {
+        pe.begin(SLIKL_PHASE_KEY_COPY);
         e = slikl::launch_k_to_f16(pb, (uint16_t *)(ws + wp.k16_off), (float *)(ws + wp.scale_off), s);
+        pe.end(SLIKL_PHASE_KEY_COPY);
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
     }
     if (mode == 1) {
+        pe.begin(SLIKL_PHASE_DET_SCALE);
         e = slikl::launch_det_scale(pb, f16, (float *)(ws + wp.scale_off), s);
+        pe.end(SLIKL_PHASE_DET_SCALE);
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
     }
     if (t1 > 0) {
+        pe.begin(SLIKL_PHASE_FUSED);
         e = mode == 2 ? slikl::launch_grad_dense(pb, head_tile(pb.group), f16, parts, s)
                       : slikl::launch_grad_fused(pb, head_tile(pb.group), f16, mode, parts, s);
+        pe.end(SLIKL_PHASE_FUSED);
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
     }
     if (mode == 2) {
+        pe.begin(SLIKL_PHASE_DK);
         e = slikl::launch_dense_dk(pb, head_tile(pb.group), f16, wp.rsplits, s);
+        pe.end(SLIKL_PHASE_DK);
+        if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
+        pe.begin(SLIKL_PHASE_DK_FINAL);
+        e = slikl::launch_dense_dk_reduce(pb, f16, wp.rsplits, s);
+        pe.end(SLIKL_PHASE_DK_FINAL);
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
         return SLIKL_OK;
     }
+    pe.begin(SLIKL_PHASE_DK_FINAL);
     e = slikl::launch_finalize_dk(pb, f16, mode == 1, s);
+    pe.end(SLIKL_PHASE_DK_FINAL);
     if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
     return SLIKL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+slikl_status slikl_grad(const slikl_desc *desc, const void *q, const void *k, const float *w,
+                        const int32_t *sparse_indices, const float *attn_softmax_l1norm,
+                        const int32_t *metadata, void *dq, void *dk, float *dw, float *softmax_out,
+                        void *workspace, size_t workspace_bytes, void *stream) {
+    PhaseEvents pe;
+    return grad_impl(desc, q, k, w, sparse_indices, attn_softmax_l1norm, metadata, dq, dk, dw, softmax_out,
+                     workspace, workspace_bytes, stream, pe);
+}
+
+slikl_status slikl_grad_profiled(const slikl_desc *desc, const void *q, const void *k, const float *w,
+                                 const int32_t *sparse_indices, const float *attn_softmax_l1norm,
+                                 const int32_t *metadata, void *dq, void *dk, float *dw, float *softmax_out,
+                                 void *workspace, size_t workspace_bytes, void *stream, float *phase_ms) {
+    if (!phase_ms) return SLIKL_ERR_NULLPTR;
+    PhaseEvents pe;
+    pe.on = true;
+    slikl_status st = grad_impl(desc, q, k, w, sparse_indices, attn_softmax_l1norm, metadata, dq, dk, dw,
+                                softmax_out, workspace, workspace_bytes, stream, pe);
+    if (st != SLIKL_OK) return st;
+    return pe.collect(phase_ms) ? SLIKL_OK : SLIKL_ERR_LAUNCH;
 }
 
 }  // extern "C"

@@ -67,6 +67,7 @@ hipError_t launch_grad_dense(const Problem &pb, int hp, bool f16, int grid, hipS
 int grad_dense_blocks_per_cu(int hp, int d, bool f16);
 hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t stream);
 hipError_t launch_dense_dk(const Problem &pb, int hp, bool f16, int rsplits, hipStream_t stream);
+hipError_t launch_dense_dk_reduce(const Problem &pb, bool f16, int rsplits, hipStream_t stream);
 hipError_t launch_finalize_dk(const Problem &pb, bool f16, bool det, hipStream_t stream);
 hipError_t launch_det_scale(const Problem &pb, bool f16, float *scale_block, hipStream_t stream);
 hipError_t launch_k_to_f16(const Problem &pb, uint16_t *k16, float *scale_block, hipStream_t stream);

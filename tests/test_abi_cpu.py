@@ -125,6 +125,7 @@ def test_null_pointers(lib):
     # execute entry points: null tensors fail before any device work
     assert lib.slikl_grad(ctypes.byref(d), *([None] * 10), None, 0, None) == 1
     assert lib.slikl_grad_metadata(ctypes.byref(d), None, None, None, 0, None) == 1
+    assert lib.slikl_grad_profiled(ctypes.byref(d), *([None] * 10), None, 0, None, None) == 1
 
 
 def test_small_workspace_is_rejected_before_launch(lib):

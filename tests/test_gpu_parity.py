@@ -169,6 +169,24 @@ def test_out_of_range_index_is_skipped_and_flagged():
     check_close(got, oracle(x), label="out-of-range skipped")
 
 
+@pytest.mark.parametrize("dk_mode", ["scatter", "dense"])
+def test_profiled_call_matches_and_times_phases(dk_mode):
+    import torch
+    import sparse_attention_indexer_token_amd as slikl
+    x = make_inputs(SMALL["hp64_d128_ragged"])
+    t = to_device(x)
+    base = run_gpu(x, t, dk_mode=dk_mode, deterministic=True)
+    (dq, dk, dw, y), ms = slikl.slikl_grad_profiled(t["q"], t["k"], t["w"], t["idx"], t["p"],
+                                                    dk_mode=dk_mode, deterministic=True)
+    torch.cuda.synchronize()
+    got = dict(dq=dq.float().cpu().numpy(), dk=dk.float().cpu().numpy(), dw=dw.cpu().numpy(),
+               softmax_out=y.cpu().numpy())
+    for name in got:
+        assert np.array_equal(got[name], base[name]), name
+    assert ms["fused"] > 0 and ms["dk_final"] > 0 and ms["metadata"] > 0
+    assert (ms["dk"] > 0) == (dk_mode == "dense")
+
+
 FULL = ["tiny_causal", "dsv32_indexer", "long_context", "contention_det", "varlen_tnd"]
 
 
