@@ -60,9 +60,15 @@ __global__ __launch_bounds__(kBlock, 2) void dense_dk_kernel(Problem pb, int rsp
     const int wave = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, half = lane >> 5, l16 = lane & 15, grp = lane >> 4;
 
-    int bid = blockIdx.x;
-    const int kb = bid % nkb;
-    bid /= nkb;
+    // Workgroups are dealt to the 8 XCDs round-robin (block b runs on XCD b % 8).
+    // All key blocks of one row range go to the same XCD, so they share its L2
+    // copy of the range's queries and records; the row ranges (their count is a
+    // multiple of 8) are dealt to the XCDs in snake order 0..7, 7..0, ... so that
+    // work growing along the rows (causal lists) stays balanced across XCDs.
+    const int x = blockIdx.x & 7, li = blockIdx.x >> 3;
+    const int kb = li % nkb;
+    const int m = li / nkb;                       // m-th row range of this XCD
+    int bid = (m & 1) ? 8 * m + 7 - x : 8 * m + x;
     const int sp = bid % rsplits;
     bid /= rsplits;
     const int g = bid % pb.n2;
@@ -80,15 +86,39 @@ __global__ __launch_bounds__(kBlock, 2) void dense_dk_kernel(Problem pb, int rsp
     const float sA = ldexpf(1.f, dense_scale_exponent(pb.dense_max));
     const uint16_t *qsrc = F16 ? pb.q : pb.q16;
 
-    // next row in [from, r1) whose unit names a key of [j0, j1)
-    auto next_row = [&](int from) {
-        int r = from;
-        for (; r < r1; ++r) {
-            const int u = r * pb.n2 + g;
-            const int lo = pb.row_range[2 * u], hi = pb.row_range[2 * u + 1];
-            if (hi >= j0 && lo < j1) break;
+    // The rows of [r0, r1) whose unit names a key of [j0, j1), in order, are
+    // listed in LDS a chunk of kBlock rows at a time (one parallel read of the
+    // key ranges per chunk instead of a dependent read per row).
+    __shared__ int s_rows[kBlock];
+    __shared__ int s_cnt[8];
+    int chunk = r0, nact = 0, ai = 0;
+    auto fill_rows = [&]() {           // next non-empty chunk; nact = 0 at the end
+        nact = 0;
+        ai = 0;
+        while (nact == 0 && chunk < r1) {
+            const int r = chunk + tid;
+            bool act = false;
+            if (r < r1) {
+                const int u = r * pb.n2 + g;
+                const int lo = pb.row_range[2 * u], hi = pb.row_range[2 * u + 1];
+                act = hi >= j0 && lo < j1;
+            }
+            int total;
+            const int pos = block_excl_scan(act ? 1 : 0, s_cnt, &total);
+            if (act) s_rows[pos] = r;
+            lds_barrier();
+            nact = total;
+            chunk += kBlock;
         }
-        return r;
+    };
+    // next active row (r1 at the end); the list of the current chunk is consumed in order
+    auto next_row = [&]() {
+        if (ai >= nact) {
+            __syncthreads();               // readers of the old list are done
+            fill_rows();
+            if (nact == 0) return r1;
+        }
+        return s_rows[ai++];
     };
     auto issue = [&](int r, int buf) {
         const int qbase = (r * pb.n1 + g * G) * D;
@@ -133,7 +163,7 @@ __global__ __launch_bounds__(kBlock, 2) void dense_dk_kernel(Problem pb, int rsp
 #pragma unroll
     for (int i = 0; i < NDT; ++i) acc[i] = f32x16{};
 
-    int cur = next_row(r0);
+    int cur = next_row();
     float dI_c = 0.f, dI_n = 0.f;
     uint32_t mw_c[NH], mw_n[NH];
     int eq_c = 0, eq_n = 0;
@@ -143,7 +173,7 @@ __global__ __launch_bounds__(kBlock, 2) void dense_dk_kernel(Problem pb, int rsp
     }
     int buf = 0;
     while (cur < r1) {
-        const int nxt = next_row(cur + 1);
+        const int nxt = next_row();
         __builtin_amdgcn_s_waitcnt(0x0f70);     // vmcnt(0): this row's q, w, records landed
         __syncthreads();                         // (also: the other buffer's readers are done)
         if (nxt < r1) {

@@ -183,6 +183,49 @@ __device__ __forceinline__ void block_reduce_multi(float (&mx)[NM], float (&sm)[
         sm[i] = (red[NM + i] + red[(NM + NS) + NM + i]) + (red[2 * (NM + NS) + NM + i] + red[3 * (NM + NS) + NM + i]);
 }
 
+// Exclusive prefix sum of v over the block (returned; the total in *total)
+// together with block maxima of mx[] and sums of sm[], with one barrier pair.
+// `red` holds at least 4 * (1 + NM + NS) floats.
+template <int NM, int NS>
+__device__ __forceinline__ int block_scan_reduce(int v, float (&mx)[NM], float (&sm)[NS], float *red, int *total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int W = 1 + NM + NS;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+#pragma unroll
+    for (int i = 0; i < NM; ++i) mx[i] = wave_max(mx[i]);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) sm[i] = wave_sum(sm[i]);
+    lds_barrier();
+    if (lane == 63) red[wave * W] = __int_as_float(x);
+    if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < NM; ++i) red[wave * W + 1 + i] = mx[i];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) red[wave * W + 1 + NM + i] = sm[i];
+    }
+    lds_barrier();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        const int c = __float_as_int(red[w * W]);
+        off += w < wave ? c : 0;
+        tot += c;
+    }
+    *total = tot;
+#pragma unroll
+    for (int i = 0; i < NM; ++i)
+        mx[i] = fmaxf(fmaxf(red[1 + i], red[W + 1 + i]), fmaxf(red[2 * W + 1 + i], red[3 * W + 1 + i]));
+#pragma unroll
+    for (int i = 0; i < NS; ++i)
+        sm[i] = (red[1 + NM + i] + red[W + 1 + NM + i]) + (red[2 * W + 1 + NM + i] + red[3 * W + 1 + NM + i]);
+    return off + x - v;
+}
+
 // Exclusive prefix sum over the block; `tmp` holds >= 4 ints.
 __device__ __forceinline__ int block_excl_scan(int v, int *tmp, int *total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

@@ -57,7 +57,10 @@ struct DenseFwdCfg {
     static constexpr int STAGE = 32 * D * 2;    // bytes of one wave stage
     static constexpr int RING = 4 * NST * STAGE;
     static constexpr int TOPK_MAX = 2048;
-    static_assert(RING >= 4 * 32 * D * 4, "U reduction tile fits the ring");
+    // fp32 row stride of the U reduction tiles (padded when the ring has room:
+    // conflict-free 16-byte writes)
+    static constexpr int RS = 4 * 32 * (D + 4) * 4 <= RING ? D + 4 : D;
+    static_assert(RING >= 4 * 32 * RS * 4, "U reduction tile fits the ring");
 };
 
 // vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding)
@@ -218,16 +221,30 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
         // ---- compact the valid slots: key row, slot id, p ------------------------------
         int cnt = 0;
         uint32_t zslots = 0;              // in-range slots that are -1 / out of range
+        float kmx = -1.f, kmn_neg = -3.0e38f, pabs = 0.f, pmx = 0.f;
 #pragma unroll
         for (int i = 0; i < SPT_MAX; ++i) {
+            const int v = in.iv[i];
             const bool inr = i < spt && s0 + i < topk;
-            const bool ok = in.iv[i] >= 0 && in.iv[i] < S2;
+            const bool ok = v >= 0 && v < S2;
             cnt += ok ? 1 : 0;
             zslots |= (inr && !ok) ? (1u << i) : 0u;
+            if (ok) {
+                pabs += fabsf(in.pv[i]);
+                pmx = fmaxf(pmx, fabsf(in.pv[i]));
+                kmx = fmaxf(kmx, (float)v);
+                kmn_neg = fmaxf(kmn_neg, -(float)v);
+            }
         }
+        // one barrier pair: positions of the valid slots, maxima {|p|, key, -key},
+        // sum of |p| (its barriers also publish s_w)
+        float mxv[3] = {pmx, kmx, kmn_neg};
+        float smv[1] = {pabs};
         int nvalid;
-        int pos = block_excl_scan(cnt, s_itmp, &nvalid);
-        float kmx = -1.f, kmn_neg = -3.0e38f, pabs = 0.f, pmx = 0.f;
+        int pos = block_scan_reduce<3, 1>(cnt, mxv, smv, s_red, &nvalid);
+        const float pmax = mxv[0], psum = smv[0];
+        const int kmax_i = (int)mxv[1];
+        const int kmin_i = nvalid > 0 ? (int)(-mxv[2]) : 0x7fffffff;
 #pragma unroll
         for (int i = 0; i < SPT_MAX; ++i) {
             const int v = in.iv[i];
@@ -235,17 +252,13 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
                 s_key[pos] = kbase + v;
                 s_slot[pos] = (uint16_t)(s0 + i);
                 s_p[pos] = in.pv[i];
-                pabs += fabsf(in.pv[i]);
-                pmx = fmaxf(pmx, fabsf(in.pv[i]));
-                kmx = fmaxf(kmx, (float)v);
-                kmn_neg = fmaxf(kmn_neg, -(float)v);
                 ++pos;
             }
         }
         const int nsteps = (nvalid + 127) >> 7;
         for (int j = nvalid + tid; j < nsteps * 128; j += kBlock) s_key[j] = -1;
 
-        // |q| maximum of this thread's A operands (bf16 only: scale of the fp16 copy)
+        // |q| maximum (bf16 only: scale of the fp16 copy): every wave holds all of q
         float qm = 0.f;
         if constexpr (!F16) {
 #pragma unroll
@@ -256,15 +269,14 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
                     for (int c = 0; c < 4; ++c)
                         qm = fmaxf(qm, fmaxf(fabsf(__uint_as_float(in.qa[ht][ks][c] << 16)),
                                              fabsf(__uint_as_float(in.qa[ht][ks][c] & 0xffff0000u))));
+            qm = wave_max(qm);
         }
-        // one barrier pair: maxima {|q|, |w|, |p|, key, -key} and the sum of |p|
-        // (its barriers also publish the compacted lists and s_w)
-        float mxv[5] = {qm, fabsf(in.wt), pmx, kmx, kmn_neg};
-        float smv[1] = {pabs};
-        block_reduce_multi<5, 1>(mxv, smv, s_red);
-        const float qmax = mxv[0], wabs = mxv[1], pmax = mxv[2], psum = smv[0];
-        const int kmax_i = (int)mxv[3];
-        const int kmin_i = nvalid > 0 ? (int)(-mxv[4]) : 0x7fffffff;
+        const float qmax = qm;
+        // max |w| of the unit from s_w (published by the scan's barriers)
+        float wabs = fabsf(s_w[lane < HP ? lane : 0]);
+        if constexpr (HP > 64) wabs = fmaxf(wabs, fabsf(s_w[lane + 64 < HP ? lane + 64 : 0]));
+        wabs = wave_max(wabs);
+        lds_barrier();            // compacted lists visible to every wave
 
         // ---- key stream: steps [0, nsteps) pass 1 (k), [nsteps, 2 nsteps) pass 2 ------
         // Copy i of a step holds rows i*RPB .. +RPB of the wave's 32; lane l writes
@@ -523,8 +535,9 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
                     const u32x2 b0 = lds_read_tr(kb, off2[0][dt] + (16 * ks) * DCH * 16);
                     const u32x2 b1 = lds_read_tr(kb, off2[1][dt] + (16 * ks + 4) * DCH * 16);
                     const u32x4 bv = {b0.x, b0.y, b1.x, b1.y};
+                    // U^T tile: rows = d (keys as k), columns = heads
 #pragma unroll
-                    for (int ht = 0; ht < NH; ++ht) uacc[ht][dt] = mfma32<true>(a[ht], bv, uacc[ht][dt]);
+                    for (int ht = 0; ht < NH; ++ht) uacc[ht][dt] = mfma32<true>(bv, a[ht], uacc[ht][dt]);
                 }
             }
         }
@@ -535,12 +548,16 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
 #pragma unroll
         for (int ht = 0; ht < NH; ++ht) {
             lds_barrier();          // ring free (pass 2 reads / previous tile's sums done)
-            float *mine = red + wave * 32 * D;
+            // tile element j of lane l: head l32, d = 32 dt + 8 (j/4) + 4 half + j%4, so
+            // four consecutive elements are four consecutive d of one head row
+            float *mine = red + wave * 32 * C::RS + l32 * C::RS + 4 * half;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt)
 #pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    mine[(8 * (j >> 2) + 4 * half + (j & 3)) * D + 32 * dt + l32] = uacc[ht][dt][j];
+                for (int jq = 0; jq < 4; ++jq)
+                    *(float4 *)(mine + 32 * dt + 8 * jq) =
+                        float4{uacc[ht][dt][4 * jq], uacc[ht][dt][4 * jq + 1], uacc[ht][dt][4 * jq + 2],
+                               uacc[ht][dt][4 * jq + 3]};
             lds_barrier();
             const int hh = tid >> 3;
             const int c0 = (tid & 7) * EPT;
@@ -550,10 +567,10 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
                 float uv[EPT];
 #pragma unroll
                 for (int e4 = 0; e4 < EPT; e4 += 4) {
-                    float4 acc4 = *(const float4 *)(red + hh * D + c0 + e4);
+                    float4 acc4 = *(const float4 *)(red + hh * C::RS + c0 + e4);
 #pragma unroll
                     for (int wv2 = 1; wv2 < 4; ++wv2) {
-                        const float4 t4 = *(const float4 *)(red + wv2 * 32 * D + hh * D + c0 + e4);
+                        const float4 t4 = *(const float4 *)(red + (wv2 * 32 + hh) * C::RS + c0 + e4);
                         acc4.x += t4.x; acc4.y += t4.y; acc4.z += t4.z; acc4.w += t4.w;
                     }
                     uv[e4] = acc4.x * uscale;

@@ -75,11 +75,15 @@ int dk_strategy(const slikl_desc *d) {
     return d->deterministic ? 1 : 0;
 }
 
+// Query-row ranges of the key-major dK kernel: about 1024 workgroups in all,
+// ranges of at least 16 rows where possible, and a multiple of 8 ranges (the
+// kernel deals whole ranges to the 8 XCDs).
 int dense_row_splits(const slikl_desc *d) {
     const int64_t nkb = (d->s2 + 127) / 128;
     int64_t rs = (1024 + nkb * d->n2 * d->batch - 1) / (nkb * d->n2 * d->batch);
     const int64_t cap = d->s1 / 16 > 1 ? d->s1 / 16 : 1;
     rs = rs < 1 ? 1 : (rs > cap ? cap : rs);
+    rs = (rs + 7) / 8 * 8;
     return (int)rs;
 }
 
