@@ -10,6 +10,8 @@ namespace slikl {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -126,21 +128,29 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// Block-wide reductions for a 256-thread block; `red` holds >= 4 floats.
+// Block-wide reductions for a block of NW wavefronts; `red` holds >= NW floats.
+template <int NW = 4>
 __device__ __forceinline__ float block_max(float v, float *red) {
     v = wave_max(v);
     lds_barrier();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     lds_barrier();
-    return fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float r = red[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) r = fmaxf(r, red[w]);
+    return r;
 }
 
+template <int NW = 4>
 __device__ __forceinline__ float block_sum(float v, float *red) {
     v = wave_sum(v);
     lds_barrier();
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
     lds_barrier();
-    return (red[0] + red[1]) + (red[2] + red[3]);
+    float r = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) r += red[w];       // fixed order
+    return r;
 }
 
 __device__ __forceinline__ int block_max_int(int v, int *red) {
@@ -185,8 +195,8 @@ __device__ __forceinline__ void block_reduce_multi(float (&mx)[NM], float (&sm)[
 
 // Exclusive prefix sum of v over the block (returned; the total in *total)
 // together with block maxima of mx[] and sums of sm[], with one barrier pair.
-// `red` holds at least 4 * (1 + NM + NS) floats.
-template <int NM, int NS>
+// `red` holds at least NW * (1 + NM + NS) floats.
+template <int NM, int NS, int NW = 4>
 __device__ __forceinline__ int block_scan_reduce(int v, float (&mx)[NM], float (&sm)[NS], float *red, int *total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     constexpr int W = 1 + NM + NS;
@@ -211,18 +221,26 @@ __device__ __forceinline__ int block_scan_reduce(int v, float (&mx)[NM], float (
     lds_barrier();
     int off = 0, tot = 0;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < NW; ++w) {
         const int c = __float_as_int(red[w * W]);
         off += w < wave ? c : 0;
         tot += c;
     }
     *total = tot;
 #pragma unroll
-    for (int i = 0; i < NM; ++i)
-        mx[i] = fmaxf(fmaxf(red[1 + i], red[W + 1 + i]), fmaxf(red[2 * W + 1 + i], red[3 * W + 1 + i]));
+    for (int i = 0; i < NM; ++i) {
+        float r = red[1 + i];
 #pragma unroll
-    for (int i = 0; i < NS; ++i)
-        sm[i] = (red[1 + NM + i] + red[W + 1 + NM + i]) + (red[2 * W + 1 + NM + i] + red[3 * W + 1 + NM + i]);
+        for (int w = 1; w < NW; ++w) r = fmaxf(r, red[w * W + 1 + i]);
+        mx[i] = r;
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        float r = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) r += red[w * W + 1 + NM + i];
+        sm[i] = r;
+    }
     return off + x - v;
 }
 

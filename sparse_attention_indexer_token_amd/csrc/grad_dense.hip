@@ -7,6 +7,9 @@
 // y = Softmax(I), dI = y - p, dW = dI ReLU(S)^T, dq = dS K_topk, with dS read
 // as the chain rule through I = W ReLU(S): dS[h,s] = w[h] dI[s] 1[S[h,s] > 0].
 //
+// Serves head groups of more than 64 (head groups of up to 64 go to the
+// eight-wave variant, whose launcher the dispatch below calls).
+//
 // One workgroup (4 wavefronts, one per SIMD) per compute unit walks the
 // (query row, key head) units of its metadata parts.  Per unit the valid slots
 // are compacted into positions; position block `step` (128 positions) is
@@ -642,11 +645,13 @@ static int blocks_gd() {
 
 hipError_t launch_grad_dense(const Problem &pb, int hp, bool f16, int grid, hipStream_t stream) {
     const int d = pb.d;
+    if (hp <= 64) return launch_grad_dense8(pb, hp, f16, grid, stream);
     SLIKL_GD_CASES(launch_gd, pb, grid, stream);
     return hipErrorInvalidValue;
 }
 
 int grad_dense_blocks_per_cu(int hp, int d, bool f16) {
+    if (hp <= 64) return grad_dense8_blocks_per_cu(hp, d, f16);
     SLIKL_GD_CASES(blocks_gd);
     return 1;
 }

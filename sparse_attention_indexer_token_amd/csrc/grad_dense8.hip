@@ -1,0 +1,714 @@
+// Fused backward of the sparse lightning-indexer KL loss for gfx950, variant
+// for top-k lists that cover much of the key range: everything except dK, plus
+// the per-(query row, key) records that the key-major dK kernel consumes.
+//
+// Follows the formula section of the operator page
+// "aclnnSparseLightningIndexerKLLossGrad": S = q K_topk^T, I = W ReLU(S),
+// y = Softmax(I), dI = y - p, dW = dI ReLU(S)^T, dq = dS K_topk, with dS read
+// as the chain rule through I = W ReLU(S): dS[h,s] = w[h] dI[s] 1[S[h,s] > 0].
+//
+// One workgroup of 8 wavefronts (two per SIMD, so that one wave's waits are
+// covered by the other's work) per compute unit walks the (query row, key
+// head) units of its metadata parts.  Per unit the valid slots are compacted
+// into positions; a step covers 128 positions, 16 per wave, and every wave
+// runs its own barrier-free pipeline over its positions:
+//   pass 1  S for all heads of its 16 keys (16x16x32 MFMA, rows = heads), then
+//           per key I = sum_h w_h ReLU(S) and the S > 0 head bits (one 32-bit
+//           word per 32-head tile, bit 16*(h/4 % 2) + 4*(h/8) + h%4 for head h:
+//           the format the dK kernel and the four-wave variant use).
+//   softmax (block-wide) m, Z, y -> softmax_out, dI = y - p; dI as fp16 after
+//           a per-unit power-of-two scale for pass 2.
+//   pass 2  U^T += K16^T dS16^T over its keys (32x32x16 MFMA; A = fp16 keys via
+//           transposing LDS reads, B = fp16 dI on the S > 0 bits built in
+//           registers), a partial U of every head.
+//   end     the eight partial U are added in a fixed order through LDS;
+//           dq = w U, and dW = <q, U> per head (U q = sum_s dI ReLU(S)).
+// The keys of both passes form one stream of 16-row copies per wave into a
+// ring of NST stages in LDS (range-checked buffer loads straight to LDS,
+// issued NST-1 steps ahead); each wave waits for its own copies with vmcnt,
+// which counts vector memory operations in issue order on this target.
+// The next unit's q, w and slot lists are loaded after pass 1.
+//
+// Records for the dK kernel, per unit u and batch-relative key j:
+//   dI_map[u, j]   sum of dI over the slots naming j, int32 fixed point with
+//                  the per-unit exponent rec_exp[2u+1] (integer adds are
+//                  associative: the sum is exact and run-to-run identical)
+//   mask_map[u, j] the S > 0 head words of (u, j)
+//   row_range[u]   smallest and largest j named by u
+//   q16 / rec_exp[2u] bf16 queries as fp16 scaled by 2^eq per unit
+//   dense_max      max over units of max|w| (1 + sum|p|) 2^-eq
+// Two waves per SIMD need the U accumulators within 128 registers, so this
+// variant serves head groups of up to 64; larger groups use the four-wave one.
+#include "device_common.h"
+#include "slikl_internal.h"
+
+namespace slikl {
+namespace dense8 {
+
+typedef __attribute__((address_space(3))) void lds_void_gd;
+typedef __attribute__((address_space(1))) void glb_void_gd;
+
+constexpr int kWaves8 = 8;
+constexpr int kBlock8 = 64 * kWaves8;
+constexpr int TOPK_PER_THREAD = 2048 / kBlock8;  // slots of one row per thread (topk <= 2048)
+
+template <int HP, int D>
+struct DenseFwdCfg {
+    static constexpr int NH = HP / 32;          // 32-head tiles (pass 2, head words)
+    static constexpr int NQT = HP / 16;         // 16-head tiles (pass 1)
+    static constexpr int NDT = D / 32;          // 32-wide d tiles of U
+    static constexpr int NKS = D / 32;          // k-steps of S over d (16x16x32)
+    static constexpr int DCH = D / 8;           // 16-byte chunks per key row
+    static constexpr int NL = D / 32;           // 1 KiB copies per wave step (16 rows)
+    static constexpr int RPB = 1024 / (2 * D);  // key rows per copy
+    static constexpr int NST = D == 128 ? (HP == 128 ? 2 : 3) : 4;
+    static constexpr int STAGE = 16 * D * 2;    // bytes of one wave stage
+    static constexpr int RING = kWaves8 * NST * STAGE;
+    static constexpr int TOPK_MAX = 2048;
+    // U reductions run in NDH rounds of DH columns (so that 8 partial tiles fit
+    // the ring); fp32 row stride of a round's tile
+    static constexpr int NDH = D == 128 ? 2 : 1;
+    static constexpr int DH = D / NDH;
+    static constexpr int RS = kWaves8 * 32 * (DH + 4) * 4 <= RING ? DH + 4 : DH;
+    static_assert(RING >= kWaves8 * 32 * RS * 4, "U reduction tile fits the ring");
+};
+
+// Swizzle of row `row` of a [16 rows][CH 16-byte chunks] stage tile: logical
+// chunk c sits at c ^ swz(row).  Chosen so that (a) the 16 rows read at one
+// logical chunk by a pass-1 operand load hit 16 different bank groups and
+// (b) a transposing read (4 aligned rows x chunks {2m, 2m+1}) hits 8.
+template <int CH>
+__device__ __forceinline__ int stage_swz(int row) {
+    if constexpr (CH >= 16) {
+        return (((row & 3) << 1) ^ ((row >> 2) & 1)) | (((row >> 3) & 1) << 3);
+    } else if constexpr (CH == 8) {
+        const int s = (row >> 1) & 7;              // rows of one parity share a 256-byte line
+        return ((s & 1) << 2) | (s >> 1);
+    } else {
+        return (row >> 2) & 3;                     // 64-byte rows: row % 4 picks the bank group
+    }
+}
+
+template <int CH>
+__device__ __forceinline__ int stage_off(int row, int col) {
+    return row * (CH * 16) + (((col >> 3) ^ stage_swz<CH>(row)) << 4) + ((col & 7) << 1);
+}
+
+// The lane id as a value the compiler cannot see through: per-lane offsets
+// derived from it inside a loop are recomputed there (a few VALU operations)
+// instead of being hoisted to the kernel start and kept live beside U.
+__device__ __forceinline__ int opaque(int x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+template <bool F16>
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+    if constexpr (F16) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b),
+                                                      c, 0, 0, 0);
+    } else {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    }
+}
+
+// vmcnt(n) with the other counters left alone (gfx9 s_waitcnt encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int NST, int NL>
+__device__ __forceinline__ void wait_for_step(int ahead) {
+    // `ahead` later steps have their copies in flight behind this one
+    if constexpr (NST >= 4) {
+        if (ahead >= 2) { wait_vmcnt<2 * NL>(); return; }
+    }
+    if constexpr (NST >= 3) {
+        if (ahead >= 1) { wait_vmcnt<NL>(); return; }
+    }
+    wait_vmcnt<0>();
+}
+
+// Slot lists and w of one unit, loaded one unit ahead (during the previous
+// unit's epilogue; q itself is loaded at the start of its unit, where its
+// latency overlaps the compaction, so that it is not live beside U).
+struct UnitInputs {
+    float wt;                        // w of head `tid` (tid < G)
+    int iv[TOPK_PER_THREAD];         // this thread's run of slots: key index, p
+    float pv[TOPK_PER_THREAD];
+};
+
+template <int HP, int D, bool F16>
+__global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
+    using C = DenseFwdCfg<HP, D>;
+    constexpr int NH = C::NH, NQT = C::NQT, NDT = C::NDT, NKS = C::NKS, DCH = C::DCH, NL = C::NL;
+    constexpr int NST = C::NST;
+    constexpr int TOPK_MAX = C::TOPK_MAX;
+    constexpr int SPT_MAX = TOPK_PER_THREAD;
+    constexpr int NW = kWaves8;
+
+    __shared__ __attribute__((aligned(1024))) char s_ring[C::RING];
+    __shared__ __attribute__((aligned(16))) uint32_t s_mask[NH * TOPK_MAX];   // [word][position]
+    __shared__ __attribute__((aligned(16))) float s_I[TOPK_MAX];              // I, then dI
+    __shared__ __attribute__((aligned(16))) float s_p[TOPK_MAX];
+    __shared__ __attribute__((aligned(16))) int32_t s_key[TOPK_MAX];
+    __shared__ __attribute__((aligned(16))) uint16_t s_slot[TOPK_MAX];
+    __shared__ __attribute__((aligned(16))) uint16_t s_d16[TOPK_MAX];          // fp16 dI 2^eds
+    __shared__ __attribute__((aligned(16))) float s_w[HP];
+    __shared__ float s_red[NW * 6];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int l32 = lane & 31, half = lane >> 5, l16 = lane & 15, grp = lane >> 4;
+    const int U = (int)(pb.t1 * pb.n2);
+    const int G = pb.group;
+    const int topk = pb.topk;
+    const int S1 = (int)pb.s1, S2 = (int)pb.s2;
+    int parts = pb.metadata[6];
+    parts = parts < 0 ? 0 : (parts > 2048 ? 2048 : parts);
+    const float kinv = F16 ? 1.f : pb.det_scale[6];   // undoes the fp16 key copy's scale
+    char *const ring = s_ring + wave * (NST * C::STAGE);
+    // range-checked views of the two key arrays: an offset at or past the end
+    // reads zeros, which is what padding positions copy
+    const uint32_t kbytes = (uint32_t)(pb.t2 * pb.n2 * D * 2);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)pb.k, (short)0, (int)kbytes, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rk16 =
+        __builtin_amdgcn_make_buffer_rsrc((void *)pb.k16, (short)0, (int)kbytes, 0x00020000);
+    constexpr uint32_t kPadOffset = 0x80000000u;      // >= kbytes (checked on the host)
+    const int krow_bytes = pb.n2 * D * 2;
+
+    // ---- walk the units of this workgroup's parts, inputs one unit ahead ------------
+    int cpart = (int)blockIdx.x - (int)gridDim.x, cu = 0, cue = 0;
+    auto next_unit = [&]() -> bool {
+        ++cu;
+        while (cu >= cue) {
+            cpart += gridDim.x;
+            if (cpart >= parts) return false;
+            int a = pb.metadata[16 + cpart], e = pb.metadata[17 + cpart];
+            cu = a < 0 ? 0 : a;
+            cue = e > U ? U : e;
+        }
+        return true;
+    };
+    UnitInputs in;
+    auto load_inputs = [&](int uu) {
+        const int rr = uu / pb.n2, gg = uu - rr * pb.n2;
+        // every load is issued (clamped to an element that exists, then selected
+        // away): branch-free memory operations keep the compiler's count of
+        // outstanding ones exact, so its waits for these do not become vmcnt(0)
+        const int t = opaque(tid);
+        const float wv = pb.w[rr * pb.n1 + gg * G + (t < G ? t : 0)];
+        in.wt = t < G ? wv : 0.f;
+        const int spt = (topk + kBlock8 - 1) / kBlock8;
+        const int s0 = t * spt;
+        const int32_t *ir = pb.idx + uu * topk;
+        const float *pr = pb.p + uu * topk;
+#pragma unroll
+        for (int i = 0; i < SPT_MAX; ++i) {
+            const bool ok = i < spt && s0 + i < topk;
+            const int e = ok ? s0 + i : 0;                 // topk >= 1
+            const int a = ir[e];
+            const float c = pr[e];
+            in.iv[i] = ok ? a : -1;
+            in.pv[i] = ok ? c : 0.f;
+        }
+    };
+    bool have = next_unit();
+    if (have) load_inputs(cu);
+
+    while (have) {
+        const int u = cu;
+        const int r = u / pb.n2;
+        const int g = u - r * pb.n2;
+        const int b = r / S1;
+        const int kbase = b * S2;
+        float *yrow = pb.y + u * topk;
+        const uint16_t *qrow = pb.q + (r * pb.n1 + g * G) * D;
+        const int spt = (topk + kBlock8 - 1) / kBlock8;
+        const int tu = opaque(tid);
+        const int s0 = tu * spt;
+        if (tu < HP) s_w[tu] = in.wt;
+        // ---- q of the unit into LDS once, [HP rows][D] with the key tiles' swizzle, in
+        //      the head-mask array (free until pass 1): 1 KiB direct-to-LDS copies shared
+        //      out over the waves, the same number per wave (copies past the block's
+        //      end fill unused head-mask space); rows past G read past the end of the
+        //      range-checked view and arrive as zeros
+        char *const s_q = (char *)s_mask;
+        {
+            constexpr int NQC = HP * D * 2 / 1024;
+            constexpr int CPW = (NQC + NW - 1) / NW;
+            static_assert(NW * CPW * 1024 <= NH * TOPK_MAX * 4, "q copies fit the head-mask array");
+            const __amdgpu_buffer_rsrc_t rq =
+                __builtin_amdgcn_make_buffer_rsrc((void *)qrow, (short)0, G * D * 2, 0x00020000);
+            const int ln = tu & 63;
+#pragma unroll
+            for (int i = 0; i < CPW; ++i) {
+                const int c = wave + i * NW;
+                const int row = c * C::RPB + ln / DCH;
+                const uint32_t off = (c < NQC && row < G)
+                                         ? (uint32_t)(row * D * 2) + ((uint32_t)((ln % DCH) ^ stage_swz<DCH>(row)) << 4)
+                                         : kPadOffset;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void_gd *)(s_q + c * 1024), 16, off, 0, 0, 0);
+            }
+        }
+
+        // ---- compact the valid slots: key row, slot id, p ------------------------------
+        int cnt = 0;
+        uint32_t zslots = 0;              // in-range slots that are -1 / out of range
+        float kmx = -1.f, kmn_neg = -3.0e38f, pabs = 0.f, pmx = 0.f;
+#pragma unroll
+        for (int i = 0; i < SPT_MAX; ++i) {
+            const int v = in.iv[i];
+            const bool inr = i < spt && s0 + i < topk;
+            const bool ok = v >= 0 && v < S2;
+            cnt += ok ? 1 : 0;
+            zslots |= (inr && !ok) ? (1u << i) : 0u;
+            if (ok) {
+                pabs += fabsf(in.pv[i]);
+                pmx = fmaxf(pmx, fabsf(in.pv[i]));
+                kmx = fmaxf(kmx, (float)v);
+                kmn_neg = fmaxf(kmn_neg, -(float)v);
+            }
+        }
+        // kept as one register (recomputing it from the slot lists at its late use
+        // would keep those live through pass 1)
+        zslots = (uint32_t)opaque((int)zslots);
+        // one barrier pair: positions of the valid slots, maxima {|p|, key, -key},
+        // sum of |p| (its barriers also publish s_w)
+        float mxv[3] = {pmx, kmx, kmn_neg};
+        float smv[1] = {pabs};
+        int nvalid;
+        int pos = block_scan_reduce<3, 1, NW>(cnt, mxv, smv, s_red, &nvalid);
+        const float pmax = mxv[0], psum = smv[0];
+        const int kmax_i = (int)mxv[1];
+        const int kmin_i = nvalid > 0 ? (int)(-mxv[2]) : 0x7fffffff;
+#pragma unroll
+        for (int i = 0; i < SPT_MAX; ++i) {
+            const int v = in.iv[i];
+            if (v >= 0 && v < S2) {
+                s_key[pos] = kbase + v;
+                s_slot[pos] = (uint16_t)(s0 + i);
+                s_p[pos] = in.pv[i];
+                ++pos;
+            }
+        }
+        const int nsteps = (nvalid + 127) >> 7;
+        for (int j = nvalid + tid; j < nsteps * 128; j += kBlock8) s_key[j] = -1;
+
+        // max |w| of the unit from s_w (published by the scan's barriers)
+        float wabs = fabsf(s_w[lane < HP ? lane : 0]);
+        if constexpr (HP > 64) wabs = fmaxf(wabs, fabsf(s_w[lane + 64 < HP ? lane + 64 : 0]));
+        wabs = wave_max(wabs);
+        wait_vmcnt<0>();          // this wave's q copies have landed
+        lds_barrier();            // compacted lists and q visible to every wave
+
+        // q rows as A operands of S (rows = heads, zero past G)
+        u32x4 qa[NQT][NKS];
+        {
+            const int ql = opaque(tid) & 63;
+#pragma unroll
+            for (int hq = 0; hq < NQT; ++hq)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    qa[hq][ks] = *(const u32x4 *)(s_q + stage_off<DCH>(16 * hq + (ql & 15), 32 * ks + 8 * (ql >> 4)));
+        }
+        // |q| maximum (bf16 only: scale of the fp16 copy): every wave holds all of q.
+        // For bf16 bits b, |x| orders as the integer b & 0x7fff, so the maximum is
+        // taken on the packed bit patterns (no unpacked copies of q stay live).
+        float qm = 0.f;
+        if constexpr (!F16) {
+            u16x2 mb = {0, 0};
+#pragma unroll
+            for (int hq = 0; hq < NQT; ++hq)
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        mb = __builtin_elementwise_max(mb, __builtin_bit_cast(u16x2, qa[hq][ks][c] & 0x7fff7fffu));
+            const uint32_t m1 = mb.x > mb.y ? mb.x : mb.y;
+            qm = wave_max(__uint_as_float(m1 << 16));
+        }
+        const float qmax = qm;
+
+        // ---- key stream: steps [0, nsteps) pass 1 (k), [nsteps, 2 nsteps) pass 2 ------
+        const uint32_t gofs = (uint32_t)(g * D * 2);      // key head g within a key row
+        const int T = 2 * nsteps;
+        auto issue = [&](int sigma) {
+            const bool second = sigma >= nsteps;
+            const int st = second ? sigma - nsteps : sigma;
+            char *dst = ring + (sigma % NST) * C::STAGE;
+            // copy i: lane l writes physical chunk l % DCH of stage row i RPB + l / DCH,
+            // which holds logical chunk (l % DCH) ^ swz(row)
+            const int ln = opaque(lane);
+            const int32_t *keys = s_key + st * 128 + wave * 16 + ln / DCH;
+            int key[NL];
+#pragma unroll
+            for (int i = 0; i < NL; ++i) key[i] = keys[i * C::RPB];      // all reads before the copies
+#pragma unroll
+            for (int i = 0; i < NL; ++i) {
+                const int row = i * C::RPB + ln / DCH;
+                const uint32_t cofs = gofs + ((uint32_t)((ln % DCH) ^ stage_swz<DCH>(row)) << 4);
+                const uint32_t off = key[i] >= 0 ? __umul24((uint32_t)key[i], (uint32_t)krow_bytes) + cofs : kPadOffset;
+                if (second)
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk16, (lds_void_gd *)(dst + i * 1024), 16, off, 0, 0, 0);
+                else
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_gd *)(dst + i * 1024), 16, off, 0, 0, 0);
+            }
+        };
+#pragma unroll
+        for (int s = 0; s < NST - 1; ++s)
+            if (s < T) issue(s);
+
+        // ---- dense records of the unit (stores behind the first copies) ---------------
+        int eq = 0;
+        if constexpr (!F16) {
+            eq = pow2_exponent_below_2p15(qmax);
+            const float qsc = ldexpf(1.f, eq);
+#pragma unroll
+            for (int hq = 0; hq < NQT; ++hq) {
+                const int h = 16 * hq + l16;
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) {
+                    if ((hq * NKS + ks) % NW == wave && h < G) {     // the waves share the writes
+                        u32x4 o;
+#pragma unroll
+                        for (int c = 0; c < 4; ++c)
+                            o[c] = pack2<true>(__uint_as_float(qa[hq][ks][c] << 16) * qsc,
+                                               __uint_as_float(qa[hq][ks][c] & 0xffff0000u) * qsc);
+                        *(u32x4 *)(pb.q16 + (r * pb.n1 + g * G + h) * D + 32 * ks + 8 * grp) = o;
+                    }
+                }
+            }
+        }
+        // dI fixed-point exponent: |sum of dI over the slots naming one key| <= 1 + sum|p|
+        int ed;
+        {
+            int ex;
+            frexpf(1.f + psum, &ex);     // 1 + psum < 2^ex
+            ed = 30 - ex;
+            ed = ed < -60 ? -60 : ed;
+        }
+        if (tid == 0) {
+            pb.row_range[2 * u] = kmin_i;
+            pb.row_range[2 * u + 1] = nvalid > 0 ? kmax_i : -1;
+            pb.rec_exp[2 * u] = eq;
+            pb.rec_exp[2 * u + 1] = ed;
+            // bound of |w dI_key| 2^-eq, dI_key summed over duplicate slots: <= 1 + sum|p|
+            atomicMax(pb.dense_max, __float_as_uint(wabs * (1.f + psum) * ldexpf(1.f, -eq)));
+        }
+
+        lds_barrier();            // every wave has q in registers: pass 1 may overwrite s_mask
+        // ---- pass 1: S tiles (16 heads x 16 keys) on MFMA; ReLU, w, head bits ----------
+        // tile element i of lane l: head 16 hq + 4 grp + i, key l16 of the wave's 16
+        float mloc = -INFINITY;           // running max of I over this lane's positions
+        for (int s = 0; s < nsteps; ++s) {
+            wait_for_step<NST, NL>(T - 1 - s);
+            if (s + NST - 1 < T) issue(s + NST - 1);
+            const char *kb = ring + (s % NST) * C::STAGE;
+            const int ln = opaque(lane);
+            const int p16 = ln & 15, pgrp = ln >> 4;
+            u32x4 bk[NKS];                  // B operands: key p16, d 32 ks + 8 pgrp
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) bk[ks] = *(const u32x4 *)(kb + stage_off<DCH>(p16, 32 * ks + 8 * pgrp));
+            // bit of head 16 hq + 4 pgrp + i in its head word: pbase + 8 (hq % 2) + i
+            const int pbase = 16 * (pgrp & 1) + 4 * (pgrp >> 1);
+            float ipp[4] = {0.f, 0.f, 0.f, 0.f};
+            uint32_t part[NH];
+#pragma unroll
+            for (int t = 0; t < NH; ++t) part[t] = 0u;
+#pragma unroll
+            for (int hq = 0; hq < NQT; ++hq) {
+                f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks) c = mfma16<F16>(qa[hq][ks], bk[ks], c);
+                const float4 w4 = *(const float4 *)(s_w + 16 * hq + 4 * pgrp);
+                const float wq[4] = {w4.x, w4.y, w4.z, w4.w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const bool ps = c[i] > 0.f;
+                    ipp[i] = fmaf(ps ? wq[i] : 0.f, c[i], ipp[i]);
+                    // head 16 hq + 4 grp + i: word hq / 2
+                    part[hq / 2] |= ps ? (1u << (pbase + 8 * (hq & 1) + i)) : 0u;
+                }
+            }
+            float ip = (ipp[0] + ipp[1]) + (ipp[2] + ipp[3]);
+            ip += __shfl_xor(ip, 16);
+            ip += __shfl_xor(ip, 32);
+#pragma unroll
+            for (int t = 0; t < NH; ++t) {
+                part[t] |= __shfl_xor(part[t], 16);
+                part[t] |= __shfl_xor(part[t], 32);
+            }
+            const int pos1 = s * 128 + wave * 16 + p16;
+            const bool valid = pos1 < nvalid;
+            if (valid) mloc = fmaxf(mloc, ip);
+            if (pgrp == 0) {
+                s_I[pos1] = valid ? ip : -INFINITY;
+#pragma unroll
+                for (int t = 0; t < NH; ++t) s_mask[t * TOPK_MAX + pos1] = valid ? part[t] : 0u;
+            }
+        }
+
+        // ---- softmax over the valid positions: m, Z, y -> softmax_out, dI ------------
+        const float m = block_max<NW>(mloc, s_red);     // (its barriers publish s_I, s_mask)
+        constexpr int PPT = TOPK_MAX / kBlock8;        // positions per thread
+        const int p0 = tid * PPT;
+        float e[PPT];
+        float zl = 0.f;
+        {
+            const float4 a0 = *(const float4 *)(s_I + p0);
+            const float iv4[4] = {a0.x, a0.y, a0.z, a0.w};
+#pragma unroll
+            for (int i = 0; i < PPT; ++i) {
+                e[i] = p0 + i < nvalid ? expf(iv4[i] - m) : 0.f;
+                zl += e[i];
+            }
+        }
+        const float Z = block_sum<NW>(zl, s_red + 2 * NW);
+        const float invZ = 1.f / Z;
+        // |dI| <= max(max y, max p) <= max(1/Z, max p): power-of-two prescale of dI
+        // before its fp16 rounding
+        const int eds = pow2_exponent_below_2p15(fmaxf(invZ, pmax));
+        const float dsc = ldexpf(1.f, eds);
+        {
+            const float4 b0 = *(const float4 *)(s_p + p0);
+            const float pp4[4] = {b0.x, b0.y, b0.z, b0.w};
+            uint32_t d16w[PPT / 2];
+#pragma unroll
+            for (int i = 0; i < PPT; i += 2) {
+                float dd[2];
+#pragma unroll
+                for (int k2 = 0; k2 < 2; ++k2) {
+                    const int pp = p0 + i + k2;
+                    dd[k2] = 0.f;
+                    if (pp < nvalid) {
+                        const float y = e[i + k2] * invZ;
+                        dd[k2] = y - pp4[i + k2];
+                        yrow[s_slot[pp]] = y;
+                        s_I[pp] = dd[k2];
+                    }
+                }
+                d16w[i / 2] = pack2<true>(dd[0] * dsc, dd[1] * dsc);
+            }
+            if (p0 < nsteps * 128) *(u32x2 *)(s_d16 + p0) = u32x2{d16w[0], d16w[1]};
+        }
+#pragma unroll
+        for (int i = 0; i < SPT_MAX; ++i)
+            if (zslots & (1u << i)) yrow[s0 + i] = 0.f;
+        lds_barrier();
+
+        // ---- pass 2: U^T += K16^T dS16^T over this wave's positions ----------------------
+        const float dfix = ldexpf(1.f, ed);
+        int32_t *dimap = pb.dI_map + (size_t)u * pb.s2max;
+        uint32_t *mmap = pb.mask_map + (size_t)u * pb.s2max * NH;
+        f32x16 uacc[NH][NDT];
+#pragma unroll
+        for (int ht = 0; ht < NH; ++ht)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) uacc[ht][dt] = f32x16{};
+        for (int s = 0; s < nsteps; ++s) {
+            const int sigma = nsteps + s;
+            wait_for_step<NST, NL>(T - 1 - sigma);
+            const int ln = opaque(lane);
+            const int q32 = ln & 31, qhalf = ln >> 5, q16 = ln & 15, qgrp = ln >> 4;
+            // dK records of this wave's positions (issued before the next copies, so
+            // that the copies issued after an awaited one stay the last NL operations)
+            {
+                const int pr = s * 128 + wave * 16 + q16;
+                if (qgrp == 0 && pr < nvalid) {
+                    const int jrel = s_key[pr] - kbase;
+                    atomicAdd(dimap + jrel, (int32_t)__float2int_rn(s_I[pr] * dfix));
+                    if constexpr (NH == 1) {
+                        mmap[jrel] = s_mask[pr];
+                    } else if constexpr (NH == 2) {
+                        *(u32x2 *)(mmap + jrel * 2) = u32x2{s_mask[pr], s_mask[TOPK_MAX + pr]};
+                    } else {
+                        *(u32x4 *)(mmap + jrel * 4) = u32x4{s_mask[pr], s_mask[TOPK_MAX + pr],
+                                                            s_mask[2 * TOPK_MAX + pr], s_mask[3 * TOPK_MAX + pr]};
+                    }
+                }
+            }
+            if (sigma + NST - 1 < T) issue(sigma + NST - 1);
+            const char *kb = ring + (sigma % NST) * C::STAGE;
+            // bit of head row q32 of a 32-head tile inside a per-key head word
+            const int hbit = 16 * ((q32 >> 2) & 1) + 4 * (q32 >> 3) + (q32 & 3);
+            // B operand: head q32 of each 32-head tile, positions pk .. pk+7 as k
+            const int pk = s * 128 + wave * 16 + 8 * qhalf;
+            const u32x4 d16 = *(const u32x4 *)(s_d16 + pk);
+            u32x4 bb[NH];
+#pragma unroll
+            for (int ht = 0; ht < NH; ++ht) {
+                const u32x4 w0 = *(const u32x4 *)(s_mask + ht * TOPK_MAX + pk);
+                const u32x4 w1 = *(const u32x4 *)(s_mask + ht * TOPK_MAX + pk + 4);
+                const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+                for (int pr2 = 0; pr2 < 4; ++pr2) {
+                    const uint32_t lo = (uint32_t)__builtin_amdgcn_sbfe((int)wd[2 * pr2], hbit, 1);
+                    const uint32_t hi = (uint32_t)__builtin_amdgcn_sbfe((int)wd[2 * pr2 + 1], hbit, 1);
+                    bb[ht][pr2] = __builtin_amdgcn_perm(hi, lo, 0x05040100u) & d16[pr2];
+                }
+            }
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                // A operand: d = 32 dt + q32, keys 8 qhalf + (0..7) of the wave's 16, read
+                // transposed: rows 8 qhalf + 4 sec + q16/4, columns 32 dt + 16 (qgrp % 2) + 4 (q16 % 4)
+                const int col = 32 * dt + 16 * (qgrp & 1) + 4 * (q16 & 3);
+                const u32x2 a0 = lds_read_tr(kb, stage_off<DCH>(8 * qhalf + (q16 >> 2), col));
+                const u32x2 a1 = lds_read_tr(kb, stage_off<DCH>(8 * qhalf + 4 + (q16 >> 2), col));
+                const u32x4 av = {a0.x, a0.y, a1.x, a1.y};
+#pragma unroll
+                for (int ht = 0; ht < NH; ++ht) uacc[ht][dt] = mfma32<true>(av, bb[ht], uacc[ht][dt]);
+            }
+        }
+
+        // ---- U = sum of the eight wave partials (fixed order), NDH rounds over d;
+        //      dq = w U and dW = <q, U> ---------------------------------------------------
+        const float uscale = ldexpf(1.f, -eds) * kinv;
+        float *red = (float *)s_ring;
+        constexpr int EPT = C::DH / 16;          // elements per thread: 32 heads x DH / 512
+        static_assert(EPT == 2 || EPT == 4, "epilogue store width");
+        // range-checked views of this unit's dq rows and dW entries: heads past G
+        // (and lanes that do not write) store at an offset past the end, which the
+        // hardware drops, so that the stores need no branch
+        const __amdgpu_buffer_rsrc_t rdq = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(pb.dq + (r * pb.n1 + g * G) * D), (short)0, G * D * 2, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rdw = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(pb.dw + r * pb.n1 + g * G), (short)0, G * 4, 0x00020000);
+        const int et = opaque(tid);
+        const int hh = et >> 4;                  // head of this thread within the tile
+        const int c0 = (et & 15) * EPT;          // its columns within a round
+        // q elements of the dW dot products, loaded ahead of the next unit's inputs
+        // (rows past G read head 0: their dq and dW stores are dropped)
+        uint32_t qe[NH][C::NDH][EPT / 2];
+#pragma unroll
+        for (int ht = 0; ht < NH; ++ht)
+#pragma unroll
+            for (int dh = 0; dh < C::NDH; ++dh) {
+                const int h = 32 * ht + hh;
+                const uint16_t *src = qrow + (h < G ? h : 0) * D + dh * C::DH + c0;   // branch-free
+                if constexpr (EPT == 4) {
+                    const u32x2 v = *(const u32x2 *)src;
+                    qe[ht][dh][0] = v.x;
+                    qe[ht][dh][1] = v.y;
+                } else {
+#pragma unroll
+                    for (int e2 = 0; e2 < EPT / 2; ++e2) qe[ht][dh][e2] = ((const uint32_t *)src)[e2];
+                }
+            }
+#pragma unroll
+        for (int ht = 0; ht < NH; ++ht) {
+            const int h = 32 * ht + hh;
+            float dot = 0.f;
+            if (ht == NH - 1) {
+                // prefetch the next unit's slots and w (this unit's are dead) once the
+                // other head tiles' accumulators are; the latency hides behind this tile.
+                // Issued unconditionally (past the last unit it rereads this one).
+                have = next_unit();
+                load_inputs(have ? cu : u);
+            }
+#pragma unroll
+            for (int dh = 0; dh < C::NDH; ++dh) {
+                lds_barrier();          // ring free (pass 2 reads / previous sums done)
+                // tile element j of lane l: head l32, d = 32 dt + 8 (j/4) + 4 half + j%4
+                float *mine = red + (wave * 32 + l32) * C::RS;
+#pragma unroll
+                for (int dt = 0; dt < NDT; ++dt)
+#pragma unroll
+                    for (int jq = 0; jq < 4; ++jq) {
+                        const int dd0 = 32 * dt + 8 * jq;       // d = dd0 + 4 half
+                        if (dd0 >= dh * C::DH && dd0 < (dh + 1) * C::DH)
+                            *(float4 *)(mine + dd0 + 4 * half - dh * C::DH) =
+                                float4{uacc[ht][dt][4 * jq], uacc[ht][dt][4 * jq + 1], uacc[ht][dt][4 * jq + 2],
+                                       uacc[ht][dt][4 * jq + 3]};
+                    }
+                lds_barrier();
+                {
+                    float uv[EPT];
+#pragma unroll
+                    for (int e2 = 0; e2 < EPT; ++e2) uv[e2] = 0.f;
+#pragma unroll
+                    for (int wv2 = 0; wv2 < NW; ++wv2) {
+                        const float *src = red + (wv2 * 32 + hh) * C::RS + c0;
+                        if constexpr (EPT % 4 == 0) {
+#pragma unroll
+                            for (int e4 = 0; e4 < EPT; e4 += 4) {
+                                const float4 v4 = *(const float4 *)(src + e4);
+                                uv[e4] += v4.x;
+                                uv[e4 + 1] += v4.y;
+                                uv[e4 + 2] += v4.z;
+                                uv[e4 + 3] += v4.w;
+                            }
+                        } else {
+#pragma unroll
+                            for (int e2 = 0; e2 < EPT; ++e2) uv[e2] += src[e2];
+                        }
+                    }
+                    const float wh = s_w[h];
+                    const int dbase = dh * C::DH + c0;
+                    uint32_t o[EPT / 2];
+#pragma unroll
+                    for (int e2 = 0; e2 < EPT; e2 += 2) {
+                        const uint32_t qv = qe[ht][dh][e2 / 2];
+                        const float u0 = uv[e2] * uscale, u1 = uv[e2 + 1] * uscale;
+                        dot = fmaf(from16<F16>((uint16_t)(qv & 0xffffu)), u0,
+                                   fmaf(from16<F16>((uint16_t)(qv >> 16)), u1, dot));
+                        o[e2 / 2] = (uint32_t)to16<F16>(wh * u0) | ((uint32_t)to16<F16>(wh * u1) << 16);
+                    }
+                    const uint32_t dqo = h < G ? (uint32_t)((h * D + dbase) * 2) : kPadOffset;
+                    if constexpr (EPT == 4) __builtin_amdgcn_raw_buffer_store_b64(u32x2{o[0], o[1]}, rdq, dqo, 0, 0);
+                    else __builtin_amdgcn_raw_buffer_store_b32(o[0], rdq, dqo, 0, 0);
+                }
+            }
+            dot += __shfl_xor(dot, 1);
+            dot += __shfl_xor(dot, 2);
+            dot += __shfl_xor(dot, 4);
+            dot += __shfl_xor(dot, 8);
+            const uint32_t dwo = (h < G && (et & 15) == 0) ? (uint32_t)(h * 4) : kPadOffset;
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dot), rdw, dwo, 0, 0);
+        }
+        lds_barrier();          // ring, s_w and the position lists are reused by the next unit
+    }
+}
+
+template <int HP, int D, bool F16>
+static hipError_t launch_gd8(const Problem &pb, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL((grad_dense8_kernel<HP, D, F16>), dim3(grid), dim3(kBlock8), 0, stream, pb);
+    return hipGetLastError();
+}
+
+template <int HP, int D, bool F16>
+static int blocks_gd8() {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grad_dense8_kernel<HP, D, F16>, kBlock8, 0) != hipSuccess)
+        return 0;
+    return n;
+}
+
+}  // namespace dense8
+
+#define SLIKL_GD8_CASES(FN, ...)                                                                                  \
+    do {                                                                                                          \
+        if (hp == 32 && d == 32) return f16 ? FN<32, 32, true>(__VA_ARGS__) : FN<32, 32, false>(__VA_ARGS__);     \
+        if (hp == 32 && d == 64) return f16 ? FN<32, 64, true>(__VA_ARGS__) : FN<32, 64, false>(__VA_ARGS__);     \
+        if (hp == 32 && d == 128) return f16 ? FN<32, 128, true>(__VA_ARGS__) : FN<32, 128, false>(__VA_ARGS__);  \
+        if (hp == 64 && d == 32) return f16 ? FN<64, 32, true>(__VA_ARGS__) : FN<64, 32, false>(__VA_ARGS__);     \
+        if (hp == 64 && d == 64) return f16 ? FN<64, 64, true>(__VA_ARGS__) : FN<64, 64, false>(__VA_ARGS__);     \
+        if (hp == 64 && d == 128) return f16 ? FN<64, 128, true>(__VA_ARGS__) : FN<64, 128, false>(__VA_ARGS__);  \
+    } while (0)
+
+hipError_t launch_grad_dense8(const Problem &pb, int hp, bool f16, int grid, hipStream_t stream) {
+    const int d = pb.d;
+    SLIKL_GD8_CASES(dense8::launch_gd8, pb, grid, stream);
+    return hipErrorInvalidValue;
+}
+
+int grad_dense8_blocks_per_cu(int hp, int d, bool f16) {
+    SLIKL_GD8_CASES(dense8::blocks_gd8);
+    return 0;
+}
+
+}  // namespace slikl

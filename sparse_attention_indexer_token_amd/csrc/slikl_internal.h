@@ -65,6 +65,9 @@ int grad_fused_blocks_per_cu(int hp, int d, bool f16, int mode);
 // fused kernel of the dense dK strategy (BSND): writes the records above
 hipError_t launch_grad_dense(const Problem &pb, int hp, bool f16, int grid, hipStream_t stream);
 int grad_dense_blocks_per_cu(int hp, int d, bool f16);
+// eight-wave variant for head groups of up to 64 (called by the two above)
+hipError_t launch_grad_dense8(const Problem &pb, int hp, bool f16, int grid, hipStream_t stream);
+int grad_dense8_blocks_per_cu(int hp, int d, bool f16);
 hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t stream);
 hipError_t launch_dense_dk(const Problem &pb, int hp, bool f16, int rsplits, hipStream_t stream);
 hipError_t launch_dense_dk_reduce(const Problem &pb, bool f16, int rsplits, hipStream_t stream);
