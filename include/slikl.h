@@ -89,8 +89,11 @@ enum { SLIKL_DK_AUTO = 0, SLIKL_DK_SCATTER = 1, SLIKL_DK_DENSE = 2 };
 #define SLIKL_METADATA_INTS 2080
 /* Fixed cost of one unit in valid-slot equivalents for the WEIGHTED split
  * (loads, compaction, softmax and epilogue latency of a unit vs the per-slot
- * cost of the two key passes, measured on MI355X). */
+ * cost of the two key passes, measured on MI355X): SLIKL_UNIT_OVERHEAD for the
+ * SCATTER dK strategy, SLIKL_UNIT_OVERHEAD_DENSE for DENSE, whose per-slot key
+ * passes are cheaper relative to its per-unit work. */
 #define SLIKL_UNIT_OVERHEAD 512
+#define SLIKL_UNIT_OVERHEAD_DENSE 1024
 
 typedef struct slikl_desc {
     int32_t layout_q;        /* SLIKL_LAYOUT_*                                        */
@@ -122,6 +125,12 @@ slikl_status slikl_grad_workspace_size(const slikl_desc *desc, size_t *bytes);
  * default derived from the current device).  Queries the current HIP device
  * when num_parts == 0 (LAUNCH if that fails). */
 slikl_status slikl_grad_parts(const slikl_desc *desc, int32_t *parts);
+
+/* Per-unit overhead (valid-slot equivalents) the WEIGHTED split uses for
+ * `desc`: SLIKL_UNIT_OVERHEAD_DENSE when the resolved dK strategy is DENSE,
+ * else SLIKL_UNIT_OVERHEAD.  Host only.  PARAM_INVALID / UNSUPPORTED as
+ * slikl_grad_workspace_size; NULLPTR for a null argument. */
+slikl_status slikl_grad_unit_overhead(const slikl_desc *desc, int32_t *overhead);
 
 /* Load-balancing metadata pre-pass (prior art: the metadata article's
  * 功能定位 and Metadata 输出布局 sections describe an AICPU pre-operator

@@ -19,11 +19,11 @@ from typing import Optional
 from . import _native
 from ._native import (  # noqa: F401
     EXPORTS, LAYOUT, METADATA_HEADER, METADATA_INTS, MAX_PARTS, SliklDesc, SliklError,
-    UNIT_OVERHEAD, load,
+    UNIT_OVERHEAD, UNIT_OVERHEAD_DENSE, load,
 )
 
 __all__ = ["slikl_grad", "slikl_grad_profiled", "slikl_grad_metadata", "slikl_grad_workspace_size",
-           "slikl_grad_parts", "slikl_status_string", "make_desc", "SliklDesc", "SliklError"]
+           "slikl_grad_parts", "slikl_grad_unit_overhead", "slikl_status_string", "make_desc", "SliklDesc", "SliklError"]
 
 
 def _torch():
@@ -115,6 +115,11 @@ def slikl_grad_workspace_size(desc: SliklDesc) -> int:
 
 def slikl_grad_parts(desc: SliklDesc) -> int:
     return _native.grad_parts(desc)
+
+
+def slikl_grad_unit_overhead(desc: SliklDesc) -> int:
+    """Per-unit overhead (valid-slot equivalents) of the weighted split for `desc`."""
+    return _native.unit_overhead(desc)
 
 
 def slikl_grad_metadata(q, k, sparse_indices, *, layout_q="BSND", layout_k="BSND",

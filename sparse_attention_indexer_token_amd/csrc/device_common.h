@@ -104,16 +104,38 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// m = 2 m + (v > 0); returns max(v, 0) (v_cmp, v_cndmask, v_addc on VCC)
+// m = 2 m + (v > 0); returns ReLU(v).  The compare is plain code (a v_cmp into
+// an SGPR lane mask, which the hazard recognizer sees, so a v that an MFMA is
+// still writing gets its wait states); select and add-with-carry reuse the
+// mask in asm (the compiler would otherwise rebuild the shift-in from ORs).
 __device__ __forceinline__ float relu_push_bit(float v, uint32_t &m) {
+    const uint64_t ps = __builtin_amdgcn_ballot_w64(v > 0.f);
     float r;
-    asm("v_cmp_lt_f32 vcc, 0, %2\n\t"
-        "v_cndmask_b32 %0, 0, %2, vcc\n\t"
-        "v_addc_co_u32 %1, vcc, %1, %1, vcc"
-        : "=&v"(r), "+v"(m)
-        : "v"(v)
-        : "vcc");
+    uint64_t carry;
+    asm("v_cndmask_b32_e64 %0, 0, %3, %4\n\t"
+        "v_addc_co_u32_e64 %1, %2, %1, %1, %4"
+        : "=&v"(r), "+v"(m), "=&s"(carry)
+        : "v"(v), "s"(ps));
     return r;
+}
+
+// Sum / OR over the four 16-lane rows of a wavefront (lanes l % 16 + 16 r), every
+// lane receiving the result: v_permlane16_swap then v_permlane32_swap exchange
+// rows in registers.  Each lane adds (row 0 + row 1) + (row 2 + row 3) in that
+// order, so all lanes hold the same bits.
+__device__ __forceinline__ float group_sum(float v) {
+    const uint32_t x = __float_as_uint(v);
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    const uint32_t y = __float_as_uint(__uint_as_float(a[0]) + __uint_as_float(a[1]));
+    const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+__device__ __forceinline__ uint32_t group_or(uint32_t x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    const uint32_t y = a[0] | a[1];
+    const auto b = __builtin_amdgcn_permlane32_swap(y, y, false, false);
+    return b[0] | b[1];
 }
 
 __device__ __forceinline__ float wave_max(float v) {

@@ -172,14 +172,16 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
     parts = parts < 0 ? 0 : (parts > 2048 ? 2048 : parts);
     const float kinv = F16 ? 1.f : pb.det_scale[6];   // undoes the fp16 key copy's scale
     char *const ring = s_ring + wave * (NST * C::STAGE);
-    // range-checked views of the two key arrays: an offset at or past the end
-    // reads zeros, which is what padding positions copy
-    const uint32_t kbytes = (uint32_t)(pb.t2 * pb.n2 * D * 2);
-    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc((void *)pb.k, (short)0, (int)kbytes, 0x00020000);
+    // structured views of the two key arrays, one record per key row: a copy
+    // names its key by record index, and an index at or past the row count
+    // (the padding index stored for positions past the valid ones) reads zeros
+    const int krow_bytes = pb.n2 * D * 2;             // record stride, < 2^14 (checked on the host)
+    const int nkrows = (int)pb.t2;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void *)pb.k, (short)krow_bytes, nkrows, 0x00020000);
     const __amdgpu_buffer_rsrc_t rk16 =
-        __builtin_amdgcn_make_buffer_rsrc((void *)pb.k16, (short)0, (int)kbytes, 0x00020000);
-    constexpr uint32_t kPadOffset = 0x80000000u;      // >= kbytes (checked on the host)
-    const int krow_bytes = pb.n2 * D * 2;
+        __builtin_amdgcn_make_buffer_rsrc((void *)pb.k16, (short)krow_bytes, nkrows, 0x00020000);
+    constexpr uint32_t kPadOffset = 0x80000000u;      // past the end of every raw view below
 
     // ---- walk the units of this workgroup's parts, inputs one unit ahead ------------
     int cpart = (int)blockIdx.x - (int)gridDim.x, cu = 0, cue = 0;
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
             }
         }
         const int nsteps = (nvalid + 127) >> 7;
-        for (int j = nvalid + tid; j < nsteps * 128; j += kBlock8) s_key[j] = -1;
+        for (int j = nvalid + tid; j < nsteps * 128; j += kBlock8) s_key[j] = nkrows;   // reads zeros
 
         // max |w| of the unit from s_w (published by the scan's barriers)
         float wabs = fabsf(s_w[lane < HP ? lane : 0]);
@@ -335,29 +337,26 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
         const float qmax = qm;
 
         // ---- key stream: steps [0, nsteps) pass 1 (k), [nsteps, 2 nsteps) pass 2 ------
+        // copy i of a wave step: lane l writes physical chunk l % DCH of stage row
+        // i RPB + l / DCH, which holds logical chunk (l % DCH) ^ swz(row) of its key
         const uint32_t gofs = (uint32_t)(g * D * 2);      // key head g within a key row
+        uint32_t cofs[NL];
+#pragma unroll
+        for (int i = 0; i < NL; ++i)
+            cofs[i] = gofs + ((uint32_t)((lane % DCH) ^ stage_swz<DCH>(i * C::RPB + lane / DCH)) << 4);
+        const int32_t *const keys_l = s_key + wave * 16 + lane / DCH;
         const int T = 2 * nsteps;
         auto issue = [&](int sigma) {
             const bool second = sigma >= nsteps;
             const int st = second ? sigma - nsteps : sigma;
             char *dst = ring + (sigma % NST) * C::STAGE;
-            // copy i: lane l writes physical chunk l % DCH of stage row i RPB + l / DCH,
-            // which holds logical chunk (l % DCH) ^ swz(row)
-            const int ln = opaque(lane);
-            const int32_t *keys = s_key + st * 128 + wave * 16 + ln / DCH;
-            int key[NL];
+            int32_t key[NL];
 #pragma unroll
-            for (int i = 0; i < NL; ++i) key[i] = keys[i * C::RPB];      // all reads before the copies
+            for (int i = 0; i < NL; ++i) key[i] = keys_l[st * 128 + i * C::RPB];   // all reads first
 #pragma unroll
-            for (int i = 0; i < NL; ++i) {
-                const int row = i * C::RPB + ln / DCH;
-                const uint32_t cofs = gofs + ((uint32_t)((ln % DCH) ^ stage_swz<DCH>(row)) << 4);
-                const uint32_t off = key[i] >= 0 ? __umul24((uint32_t)key[i], (uint32_t)krow_bytes) + cofs : kPadOffset;
-                if (second)
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk16, (lds_void_gd *)(dst + i * 1024), 16, off, 0, 0, 0);
-                else
-                    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_gd *)(dst + i * 1024), 16, off, 0, 0, 0);
-            }
+            for (int i = 0; i < NL; ++i)
+                __builtin_amdgcn_struct_ptr_buffer_load_lds(second ? rk16 : rk, (lds_void_gd *)(dst + i * 1024), 16,
+                                                            (int)key[i], (int)cofs[i], 0, 0, 0);
         };
 #pragma unroll
         for (int s = 0; s < NST - 1; ++s)
@@ -401,55 +400,64 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
             atomicMax(pb.dense_max, __float_as_uint(wabs * (1.f + psum) * ldexpf(1.f, -eq)));
         }
 
+        // w of the heads this lane's pass-1 tile elements belong to: 16 hq + 4 grp + i
+        float wr[NQT][4];
+#pragma unroll
+        for (int hq = 0; hq < NQT; ++hq) {
+            const float4 w4 = *(const float4 *)(s_w + 16 * hq + 4 * grp);
+            wr[hq][0] = w4.x; wr[hq][1] = w4.y; wr[hq][2] = w4.z; wr[hq][3] = w4.w;
+        }
         lds_barrier();            // every wave has q in registers: pass 1 may overwrite s_mask
+
         // ---- pass 1: S tiles (16 heads x 16 keys) on MFMA; ReLU, w, head bits ----------
-        // tile element i of lane l: head 16 hq + 4 grp + i, key l16 of the wave's 16
+        // tile element i of lane l: head 16 hq + 4 grp + i, key l16 of the wave's 16.
+        // The head bits of tile pair (2t, 2t+1) are shifted in (v_addc on the compare
+        // result) odd tile first, i = 3..0, giving odd nibble << 8 | even nibble; the
+        // word format puts head 16 a + 4 grp + i at 16 (grp & 1) + 8 a + 4 (grp >> 1) + i,
+        // i.e. that byte pair shifted by pbase.
+        const int pbase = 16 * (grp & 1) + 4 * (grp >> 1);
+        int boff1[NKS];                   // B operand: key l16, d 32 ks + 8 grp
+#pragma unroll
+        for (int ks = 0; ks < NKS; ++ks) boff1[ks] = stage_off<DCH>(l16, 32 * ks + 8 * grp);
         float mloc = -INFINITY;           // running max of I over this lane's positions
         for (int s = 0; s < nsteps; ++s) {
             wait_for_step<NST, NL>(T - 1 - s);
             if (s + NST - 1 < T) issue(s + NST - 1);
             const char *kb = ring + (s % NST) * C::STAGE;
-            const int ln = opaque(lane);
-            const int p16 = ln & 15, pgrp = ln >> 4;
-            u32x4 bk[NKS];                  // B operands: key p16, d 32 ks + 8 pgrp
+            u32x4 bk[NKS];
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) bk[ks] = *(const u32x4 *)(kb + stage_off<DCH>(p16, 32 * ks + 8 * pgrp));
-            // bit of head 16 hq + 4 pgrp + i in its head word: pbase + 8 (hq % 2) + i
-            const int pbase = 16 * (pgrp & 1) + 4 * (pgrp >> 1);
+            for (int ks = 0; ks < NKS; ++ks) bk[ks] = *(const u32x4 *)(kb + boff1[ks]);
             float ipp[4] = {0.f, 0.f, 0.f, 0.f};
-            uint32_t part[NH];
-#pragma unroll
-            for (int t = 0; t < NH; ++t) part[t] = 0u;
-#pragma unroll
-            for (int hq = 0; hq < NQT; ++hq) {
-                f32x4 c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) c = mfma16<F16>(qa[hq][ks], bk[ks], c);
-                const float4 w4 = *(const float4 *)(s_w + 16 * hq + 4 * pgrp);
-                const float wq[4] = {w4.x, w4.y, w4.z, w4.w};
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const bool ps = c[i] > 0.f;
-                    ipp[i] = fmaf(ps ? wq[i] : 0.f, c[i], ipp[i]);
-                    // head 16 hq + 4 grp + i: word hq / 2
-                    part[hq / 2] |= ps ? (1u << (pbase + 8 * (hq & 1) + i)) : 0u;
-                }
-            }
-            float ip = (ipp[0] + ipp[1]) + (ipp[2] + ipp[3]);
-            ip += __shfl_xor(ip, 16);
-            ip += __shfl_xor(ip, 32);
+            uint32_t word[NH];
 #pragma unroll
             for (int t = 0; t < NH; ++t) {
-                part[t] |= __shfl_xor(part[t], 16);
-                part[t] |= __shfl_xor(part[t], 32);
+                uint32_t mbits = 0u;
+#pragma unroll
+                for (int a = 1; a >= 0; --a) {
+                    const int hq = 2 * t + a;
+                    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) c = mfma16<F16>(qa[hq][ks], bk[ks], c);
+#pragma unroll
+                    for (int i = 3; i >= 0; --i) ipp[i] = fmaf(relu_push_bit(c[i], mbits), wr[hq][i], ipp[i]);
+                    if (a == 1) mbits <<= 4;
+                }
+                word[t] = mbits << pbase;
             }
-            const int pos1 = s * 128 + wave * 16 + p16;
+            const float ip = group_sum((ipp[0] + ipp[1]) + (ipp[2] + ipp[3]));
+#pragma unroll
+            for (int t = 0; t < NH; ++t) word[t] = group_or(word[t]);
+            const int pos1 = s * 128 + wave * 16 + l16;
             const bool valid = pos1 < nvalid;
             if (valid) mloc = fmaxf(mloc, ip);
-            if (pgrp == 0) {
-                s_I[pos1] = valid ? ip : -INFINITY;
+            // lane group 0 writes I, group 1 + t head word t (all groups hold both)
+            if (grp <= NH) {
+                uint32_t v = valid ? __float_as_uint(ip) : 0xff800000u;    // -inf past the valid ones
 #pragma unroll
-                for (int t = 0; t < NH; ++t) s_mask[t * TOPK_MAX + pos1] = valid ? part[t] : 0u;
+                for (int t = 0; t < NH; ++t)
+                    if (grp == t + 1) v = valid ? word[t] : 0u;
+                uint32_t *dst = grp == 0 ? (uint32_t *)s_I + pos1 : s_mask + (grp - 1) * TOPK_MAX + pos1;
+                *dst = v;
             }
         }
 
@@ -502,6 +510,16 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
         lds_barrier();
 
         // ---- pass 2: U^T += K16^T dS16^T over this wave's positions ----------------------
+        // bit of head row l32 of a 32-head tile inside a per-key head word
+        const int hbit = 16 * ((l32 >> 2) & 1) + 4 * (l32 >> 3) + (l32 & 3);
+        // A operand (transposing reads): d = 32 dt + l32, keys 8 half + (0..7) of the
+        // wave's 16: rows 8 half + 4 sec + l16/4, columns 32 dt + 16 (grp % 2) + 4 (l16 % 4)
+        int toff[2][NDT];
+#pragma unroll
+        for (int sec = 0; sec < 2; ++sec)
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt)
+                toff[sec][dt] = stage_off<DCH>(8 * half + 4 * sec + (l16 >> 2), 32 * dt + 16 * (grp & 1) + 4 * (l16 & 3));
         const float dfix = ldexpf(1.f, ed);
         int32_t *dimap = pb.dI_map + (size_t)u * pb.s2max;
         uint32_t *mmap = pb.mask_map + (size_t)u * pb.s2max * NH;
@@ -513,13 +531,14 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
         for (int s = 0; s < nsteps; ++s) {
             const int sigma = nsteps + s;
             wait_for_step<NST, NL>(T - 1 - sigma);
-            const int ln = opaque(lane);
-            const int q32 = ln & 31, qhalf = ln >> 5, q16 = ln & 15, qgrp = ln >> 4;
-            // dK records of this wave's positions (issued before the next copies, so
-            // that the copies issued after an awaited one stay the last NL operations)
-            {
-                const int pr = s * 128 + wave * 16 + q16;
-                if (qgrp == 0 && pr < nvalid) {
+            if ((s & 3) == 0) {
+                // dK records of this wave's positions of steps s .. s+3, one per lane:
+                // dI summed per key (fixed point, integer adds) and the head words.
+                // Scattered writes; spread over pass 2 they hide behind the other
+                // wave's MFMA work.  Issued before the next copies, so that the copies
+                // after an awaited one stay the last NL memory operations.
+                const int pr = (s + (lane >> 4)) * 128 + wave * 16 + (lane & 15);
+                if (pr < nvalid) {
                     const int jrel = s_key[pr] - kbase;
                     atomicAdd(dimap + jrel, (int32_t)__float2int_rn(s_I[pr] * dfix));
                     if constexpr (NH == 1) {
@@ -534,10 +553,8 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
             }
             if (sigma + NST - 1 < T) issue(sigma + NST - 1);
             const char *kb = ring + (sigma % NST) * C::STAGE;
-            // bit of head row q32 of a 32-head tile inside a per-key head word
-            const int hbit = 16 * ((q32 >> 2) & 1) + 4 * (q32 >> 3) + (q32 & 3);
-            // B operand: head q32 of each 32-head tile, positions pk .. pk+7 as k
-            const int pk = s * 128 + wave * 16 + 8 * qhalf;
+            // B operand: head l32 of each 32-head tile, positions pk .. pk+7 as k
+            const int pk = s * 128 + wave * 16 + 8 * half;
             const u32x4 d16 = *(const u32x4 *)(s_d16 + pk);
             u32x4 bb[NH];
 #pragma unroll
@@ -554,11 +571,8 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
             }
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
-                // A operand: d = 32 dt + q32, keys 8 qhalf + (0..7) of the wave's 16, read
-                // transposed: rows 8 qhalf + 4 sec + q16/4, columns 32 dt + 16 (qgrp % 2) + 4 (q16 % 4)
-                const int col = 32 * dt + 16 * (qgrp & 1) + 4 * (q16 & 3);
-                const u32x2 a0 = lds_read_tr(kb, stage_off<DCH>(8 * qhalf + (q16 >> 2), col));
-                const u32x2 a1 = lds_read_tr(kb, stage_off<DCH>(8 * qhalf + 4 + (q16 >> 2), col));
+                const u32x2 a0 = lds_read_tr(kb, toff[0][dt]);
+                const u32x2 a1 = lds_read_tr(kb, toff[1][dt]);
                 const u32x4 av = {a0.x, a0.y, a1.x, a1.y};
 #pragma unroll
                 for (int ht = 0; ht < NH; ++ht) uacc[ht][dt] = mfma32<true>(av, bb[ht], uacc[ht][dt]);

@@ -28,7 +28,10 @@ int64_t rows_k(const slikl_desc *d) { return d->layout_k == SLIKL_LAYOUT_BSND ? 
 // addressed with 32-bit byte offsets (< 2^31 bytes) and key rows below 2^24
 // (24-bit multiplies; exact in fp32).
 bool dense_fits(const slikl_desc *d) {
-    return d->layout_q == SLIKL_LAYOUT_BSND && d->layout_k == SLIKL_LAYOUT_BSND &&
+    // the eight-wave fused kernel (head groups up to 64) addresses key rows as
+    // buffer records, whose stride field holds 14 bits
+    const bool rows_ok = head_tile(d->n2 > 0 ? d->n1 / d->n2 : 1) > 64 || (int64_t)d->n2 * d->d * 2 < 16384;
+    return d->layout_q == SLIKL_LAYOUT_BSND && d->layout_k == SLIKL_LAYOUT_BSND && rows_ok &&
            (double)d->batch * d->s2 * d->n2 * d->d * 2.0 < 2147483648.0 && (double)d->batch * d->s2 < 16777216.0;
 }
 
@@ -73,6 +76,11 @@ int dk_strategy(const slikl_desc *d) {
         if (bytes <= 8.0 * (1ull << 30)) return 2;
     }
     return d->deterministic ? 1 : 0;
+}
+
+// Per-unit overhead of the WEIGHTED split for the resolved dK strategy.
+int unit_overhead(const slikl_desc *d) {
+    return dk_strategy(d) == 2 ? SLIKL_UNIT_OVERHEAD_DENSE : SLIKL_UNIT_OVERHEAD;
 }
 
 // Query-row ranges of the key-major dK kernel: about 1024 workgroups in all,
@@ -204,6 +212,14 @@ slikl_status slikl_grad_parts(const slikl_desc *desc, int32_t *parts) {
     return resolve_parts(desc, parts);
 }
 
+slikl_status slikl_grad_unit_overhead(const slikl_desc *desc, int32_t *overhead) {
+    if (!desc || !overhead) return SLIKL_ERR_NULLPTR;
+    slikl_status st = validate(desc);
+    if (st != SLIKL_OK) return st;
+    *overhead = unit_overhead(desc);
+    return SLIKL_OK;
+}
+
 slikl_status slikl_grad_metadata(const slikl_desc *desc, const int32_t *sparse_indices, int32_t *metadata,
                                  void *workspace, size_t workspace_bytes, void *stream) {
     if (!desc || !metadata) return SLIKL_ERR_NULLPTR;
@@ -219,7 +235,7 @@ slikl_status slikl_grad_metadata(const slikl_desc *desc, const int32_t *sparse_i
     slikl::Problem pb = problem(desc);
     pb.idx = sparse_indices;
     if ((uintptr_t)workspace % 256 != 0) return SLIKL_ERR_WORKSPACE;
-    hipError_t e = slikl::launch_metadata(pb, parts, desc->split_mode, SLIKL_UNIT_OVERHEAD, metadata,
+    hipError_t e = slikl::launch_metadata(pb, parts, desc->split_mode, unit_overhead(desc), metadata,
                                           (int64_t *)((char *)workspace + wp.prefix_off),
                                           (int32_t *)((char *)workspace + wp.flags_off), (hipStream_t)stream);
     return e == hipSuccess ? SLIKL_OK : SLIKL_ERR_LAUNCH;
@@ -324,7 +340,7 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
     if (!metadata) {
         int32_t *md = (int32_t *)(ws + wp.meta_off);
         pe.begin(SLIKL_PHASE_METADATA);
-        e = slikl::launch_metadata(pb, parts, desc->split_mode, SLIKL_UNIT_OVERHEAD, md,
+        e = slikl::launch_metadata(pb, parts, desc->split_mode, unit_overhead(desc), md,
                                    (int64_t *)(ws + wp.prefix_off), (int32_t *)(ws + wp.flags_off), s);
         pe.end(SLIKL_PHASE_METADATA);
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;

@@ -128,6 +128,27 @@ def test_null_pointers(lib):
     assert lib.slikl_grad_profiled(ctypes.byref(d), *([None] * 10), None, 0, None, None) == 1
 
 
+def test_unit_overhead_follows_the_dk_strategy(lib):
+    def oh(d):
+        out = ctypes.c_int32(-1)
+        st = lib.slikl_grad_unit_overhead(ctypes.byref(d), ctypes.byref(out))
+        return st, out.value
+    # dsv32 shape: 2 topk >= S2 picks the dense strategy in auto mode
+    assert oh(good_desc()) == (0, _native.UNIT_OVERHEAD_DENSE)
+    assert oh(good_desc(dk_mode=2)) == (0, _native.UNIT_OVERHEAD_DENSE)
+    assert oh(good_desc(dk_mode=1)) == (0, _native.UNIT_OVERHEAD)
+    assert oh(good_desc(topk=512)) == (0, _native.UNIT_OVERHEAD)          # sparse lists: scatter
+    cu = (ctypes.c_int32 * 2)(0, 4096)
+    d = good_desc(layout_q=1, layout_k=1)                                  # TND: scatter only
+    d.cu_seqlens_q = ctypes.cast(cu, ctypes.c_void_p)
+    d.cu_seqlens_k = ctypes.cast(cu, ctypes.c_void_p)
+    assert oh(d) == (0, _native.UNIT_OVERHEAD)
+    assert oh(good_desc(d=96))[0] == 2
+    out = ctypes.c_int32(0)
+    assert lib.slikl_grad_unit_overhead(None, ctypes.byref(out)) == 1
+    assert lib.slikl_grad_unit_overhead(ctypes.byref(good_desc()), None) == 1
+
+
 def test_small_workspace_is_rejected_before_launch(lib):
     d = good_desc(num_parts=4)
     fake = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
@@ -150,3 +171,4 @@ def test_header_constants_match_the_binding():
     assert int(defs["SLIKL_MAX_PARTS"]) == _native.MAX_PARTS
     assert int(defs["SLIKL_METADATA_INTS"]) == _native.METADATA_INTS
     assert int(defs["SLIKL_UNIT_OVERHEAD"]) == _native.UNIT_OVERHEAD
+    assert int(defs["SLIKL_UNIT_OVERHEAD_DENSE"]) == _native.UNIT_OVERHEAD_DENSE

@@ -91,9 +91,13 @@ def test_metadata_matches_reference():
                                            layout_k=x.layout_k, cu_seqlens_q=t["cu_q"],
                                            cu_seqlens_k=t["cu_k"], num_parts=parts, split_mode=mode)
             torch.cuda.synchronize()
+            desc = slikl.make_desc(t["q"], t["k"], t["idx"], layout_q=x.layout_q, layout_k=x.layout_k,
+                                   cu_seqlens_q=t["cu_q"], cu_seqlens_k=t["cu_k"], num_parts=parts,
+                                   split_mode=mode)
             want = metadata_ref(layout_q=x.layout_q, layout_k=x.layout_k, batch=x.batch,
                                 s1=x.s1, s2=x.s2, n2=x.wl.n2, topk=x.wl.topk, parts=parts,
-                                mode=0 if mode == "weighted" else 1, overhead=slikl.UNIT_OVERHEAD,
+                                mode=0 if mode == "weighted" else 1,
+                                overhead=slikl.slikl_grad_unit_overhead(desc),
                                 cu_seqlens_q=x.cu_q, cu_seqlens_k=x.cu_k,
                                 sparse_indices=x.idx.reshape(-1, x.wl.n2, x.wl.topk))
             assert np.array_equal(md.cpu().numpy(), want)
