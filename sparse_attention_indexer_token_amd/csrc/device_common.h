@@ -266,7 +266,8 @@ __device__ __forceinline__ int block_scan_reduce(int v, float (&mx)[NM], float (
     return off + x - v;
 }
 
-// Exclusive prefix sum over the block; `tmp` holds >= 4 ints.
+// Exclusive prefix sum over a block of NW wavefronts; `tmp` holds >= NW ints.
+template <int NW = 4>
 __device__ __forceinline__ int block_excl_scan(int v, int *tmp, int *total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     int x = v;
@@ -278,9 +279,13 @@ __device__ __forceinline__ int block_excl_scan(int v, int *tmp, int *total) {
     lds_barrier();
     if (lane == 63) tmp[wave] = x;
     lds_barrier();
-    int off = 0;
-    for (int i = 0; i < wave; ++i) off += tmp[i];
-    *total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        off += i < wave ? tmp[i] : 0;
+        tot += tmp[i];
+    }
+    *total = tot;
     return off + x - v;
 }
 

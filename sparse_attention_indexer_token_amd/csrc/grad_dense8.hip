@@ -31,12 +31,13 @@
 //
 // Records for the dK kernel, per unit u and batch-relative key j:
 //   dI_map[u, j]   sum of dI over the slots naming j, int32 fixed point with
-//                  the per-unit exponent rec_exp[2u+1] (integer adds are
+//                  the per-unit exponent ed (integer adds are
 //                  associative: the sum is exact and run-to-run identical)
 //   mask_map[u, j] the S > 0 head words of (u, j)
 //   row_range[u]   smallest and largest j named by u
-//   q16 / rec_exp[2u] bf16 queries as fp16 scaled by 2^eq per unit
-//   dense_max      max over units of max|w| (1 + sum|p|) 2^-eq
+//   q16            bf16 queries as fp16 scaled by 2^eq per unit
+//   wrec[u]        fp16 hi and lo parts of w 2^ew (w carried to about 22 bits),
+//                  then eq + ew and ed
 // Two waves per SIMD need the U accumulators within 128 registers, so this
 // variant serves head groups of up to 64; larger groups use the four-wave one.
 #include "device_common.h"
@@ -391,13 +392,20 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
             ed = 30 - ex;
             ed = ed < -60 ? -60 : ed;
         }
+        // w of the unit as fp16 hi and lo parts of w 2^ew (|w 2^ew| < 2^15; zero past G)
+        const int ew = pow2_exponent_below_2p15(wabs);
+        uint8_t *const wrec = pb.wrec + (size_t)u * wrec_bytes(HP);
+        if (tid < HP) {
+            const float ws = s_w[tid] * ldexpf(1.f, ew);
+            const _Float16 wh = (_Float16)ws;
+            const _Float16 wl = (_Float16)(ws - (float)wh);
+            ((uint16_t *)wrec)[tid] = __builtin_bit_cast(uint16_t, wh);
+            ((uint16_t *)wrec)[HP + tid] = __builtin_bit_cast(uint16_t, wl);
+        }
         if (tid == 0) {
             pb.row_range[2 * u] = kmin_i;
             pb.row_range[2 * u + 1] = nvalid > 0 ? kmax_i : -1;
-            pb.rec_exp[2 * u] = eq;
-            pb.rec_exp[2 * u + 1] = ed;
-            // bound of |w dI_key| 2^-eq, dI_key summed over duplicate slots: <= 1 + sum|p|
-            atomicMax(pb.dense_max, __float_as_uint(wabs * (1.f + psum) * ldexpf(1.f, -eq)));
+            *(u32x4 *)(wrec + HP * 4) = u32x4{(uint32_t)(eq + ew), (uint32_t)ed, 0u, 0u};
         }
 
         // w of the heads this lane's pass-1 tile elements belong to: 16 hq + 4 grp + i

@@ -87,7 +87,8 @@ int unit_overhead(const slikl_desc *d) {
 // ranges of at least 16 rows where possible, and a multiple of 8 ranges (the
 // kernel deals whole ranges to the 8 XCDs).
 int dense_row_splits(const slikl_desc *d) {
-    const int64_t nkb = (d->s2 + 127) / 128;
+    const int64_t kb = slikl::dense_dk_keys_per_block();
+    const int64_t nkb = (d->s2 + kb - 1) / kb;
     int64_t rs = (1024 + nkb * d->n2 * d->batch - 1) / (nkb * d->n2 * d->batch);
     const int64_t cap = d->s1 / 16 > 1 ? d->s1 / 16 : 1;
     rs = rs < 1 ? 1 : (rs > cap ? cap : rs);
@@ -130,10 +131,10 @@ slikl::WorkspacePlan plan(const slikl_desc *d) {
         off = align_up(off + U * s2 * nh * 4);
         p.range_off = off;
         off = align_up(off + U * 8);
-        p.qexp_off = off;
-        off = align_up(off + U * 8);
         p.q16_off = off;
         off = align_up(off + (d->dtype == SLIKL_DTYPE_BF16 ? (size_t)t1 * (size_t)d->n1 * (size_t)d->d * 2 : 0));
+        p.wrec_off = off;
+        off = align_up(off + U * (size_t)slikl::wrec_bytes(head_tile(d->n1 / d->n2)));
         p.part_off = off;
         off = align_up(off + (size_t)p.rsplits * (size_t)t2 * (size_t)d->n2 * (size_t)d->d * 4);
     }
@@ -329,10 +330,9 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
         pb.dI_map = (int32_t *)(ws + wp.dimap_off);
         pb.mask_map = (uint32_t *)(ws + wp.maskmap_off);
         pb.row_range = (int32_t *)(ws + wp.range_off);
-        pb.rec_exp = (int32_t *)(ws + wp.qexp_off);
         pb.q16 = (uint16_t *)(ws + wp.q16_off);
+        pb.wrec = (uint8_t *)(ws + wp.wrec_off);
         pb.dk_part = (float *)(ws + wp.part_off);
-        pb.dense_max = (uint32_t *)(ws + wp.scale_off) + 8;
         pb.s2max = desc->s2;
     }
 

@@ -7,6 +7,9 @@
 
 namespace slikl {
 
+// Bytes of one unit's w / exponent record of the dense dK strategy.
+constexpr int wrec_bytes(int hp) { return hp * 4 + 16; }
+
 // Everything a kernel needs about one call, passed by value.
 struct Problem {
     const uint16_t *q;       // [T1, N1, D] 16-bit
@@ -25,12 +28,13 @@ struct Problem {
     const uint16_t *zero16;  // 16 zero bytes (source of padding rows in direct-to-LDS gathers)
     // dense dK records (key-major dK kernel): per unit u and batch-relative key j
     int32_t *dI_map;         // [U, s2max] dI summed over the slots naming j, fixed point
-                             // with exponent rec_exp[2u+1] (0 where no slot names j)
+                             // with exponent ed of unit u (0 where no slot names j)
     uint32_t *mask_map;      // [U, s2max, HP/32] S > 0 head bits of (u, j)
     int32_t *row_range;      // [U, 2] smallest / largest j named by u (-1 if none)
-    uint32_t *dense_max;     // max over units of max|w| max|dI| 2^-eq (float bits)
     uint16_t *q16;           // [T1, N1, D] fp16 queries scaled by 2^eq per unit (bf16 inputs)
-    int32_t *rec_exp;        // [U, 2] eq (query scale) and the dI fixed-point exponent
+    uint8_t *wrec;           // per unit u, wrec_bytes(HP) bytes at u * wrec_bytes(HP): fp16 hi
+                             // parts of w 2^ew [HP], fp16 lo parts [HP] (zero past G), then
+                             // int32 eq + ew (query and w scales), int32 ed (dI exponent), 0, 0
     float *dk_part;          // [RS, T2, N2, D] per-row-split partial dK sums
     int64_t s2max;           // key length of the dense maps
     const int32_t *cu_q;     // [batch + 1] or null (BSND)
@@ -52,7 +56,7 @@ struct WorkspacePlan {
     size_t zero_off;                // 256 zero bytes
     int mode;                       // dK strategy (see launch_grad_fused)
     int rsplits;                    // dense mode: query-row ranges of the key-major kernel
-    size_t dimap_off, dimap_bytes, maskmap_off, range_off, qexp_off, q16_off, part_off;
+    size_t dimap_off, dimap_bytes, maskmap_off, range_off, q16_off, wrec_off, part_off;
     size_t total;
 };
 
@@ -71,6 +75,7 @@ int grad_dense8_blocks_per_cu(int hp, int d, bool f16);
 hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t stream);
 hipError_t launch_dense_dk(const Problem &pb, int hp, bool f16, int rsplits, hipStream_t stream);
 hipError_t launch_dense_dk_reduce(const Problem &pb, bool f16, int rsplits, hipStream_t stream);
+int dense_dk_keys_per_block();
 hipError_t launch_finalize_dk(const Problem &pb, bool f16, bool det, hipStream_t stream);
 hipError_t launch_det_scale(const Problem &pb, bool f16, float *scale_block, hipStream_t stream);
 hipError_t launch_k_to_f16(const Problem &pb, uint16_t *k16, float *scale_block, hipStream_t stream);
