@@ -6,11 +6,19 @@
 // with dS[t,h,j] = w[t,h] dI[t,j] 1[S[t,h,j] > 0] when row t names key j (dI
 // summed over the slots naming j) and 0 otherwise.  Factored per row:
 //   dK[j] = sum_t dI[t,j] P[t,j],   P[t,j] = sum_h w[t,h] 1[S[t,h,j] > 0] q[t,h].
-// A workgroup owns a block of KB keys and a range of query rows.  Per row, P for
-// its keys is a masked product over the heads on MFMA (operands: q and the
-// head-masked w), and each lane adds dI[t, its key] P into fp32 registers; one
-// partial sum per row range is written and a second kernel adds the partials in
-// a fixed order.  No atomics: the result is bitwise reproducible.
+// A task is a block of KB keys and a range of query rows; per row, P for the
+// block's keys is a masked product over the heads on MFMA (operands: q and the
+// head-masked w), and each lane adds dI[t, its key] P into fp32 registers; each
+// task writes one partial sum, and a last kernel adds a key block's partials in
+// task order.  No atomics in the sums: the result is bitwise reproducible.
+//
+// Tasks are cut so that they hold about equally many active rows (rows whose
+// unit names a key of the block): the fused kernel adds, per row chunk, +1 / -1
+// at the first / past the last key block a unit's named key range meets; a
+// one-workgroup kernel turns that into active rows per (key block, row chunk)
+// and splits every key block into tasks at chunk boundaries, with at most one
+// task per resident workgroup when the key blocks are fewer than those, so that
+// no workgroup is left with a second task while the others idle.
 //
 // Inputs are the fused kernel's dense records: dI[u, j] (int32 fixed point),
 // the S > 0 head words of (u, j), the key range named by each unit u, fp16
@@ -91,7 +99,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dk_view(const void *base, uint
 }
 
 template <int HP, int D, bool F16>
-__device__ __forceinline__ void dense_dk_body(const Problem &pb, int rsplits, int nkb) {
+__device__ __forceinline__ void dense_dk_body(const Problem &pb) {
     using C = DenseCfg<HP, D>;
     constexpr int NH = C::NH, NKH = C::NKH, NDT = C::NDT, DCH = C::DCH, KB = C::KB, NS = C::NS;
     constexpr int CPW = C::CPW;
@@ -107,30 +115,29 @@ __device__ __forceinline__ void dense_dk_body(const Problem &pb, int rsplits, in
     const int lane = tid & 63;
     const int l32 = lane & 31, half = lane >> 5, l16 = lane & 15, grp = lane >> 4;
 
-    // Workgroups are dealt to the 8 XCDs round-robin (block b runs on XCD b % 8).
-    // All key blocks of one row range go to the same XCD, so they share its L2
-    // copy of the range's queries; the row ranges (their count is a multiple of
-    // 8) are dealt to the XCDs in snake order 0..7, 7..0, ... so that work growing
-    // along the rows (causal lists) stays balanced across XCDs.
-    const int x = blockIdx.x & 7, li = blockIdx.x >> 3;
-    const int kb = li % nkb;
-    const int m = li / nkb;
-    int bid = (m & 1) ? 8 * m + 7 - x : 8 * m + x;
-    const int sp = bid % rsplits;
-    bid /= rsplits;
-    const int g = bid % pb.n2;
-    const int b = bid / pb.n2;
-
-    const int S1 = (int)pb.s1, S2 = (int)pb.s2;
+    const int S2 = (int)pb.s2;
     const int G = pb.group;
+    const int kw = 32 * wave + l32;            // this lane's key within the block (B column)
+    const uint16_t *qsrc = F16 ? pb.q : pb.q16;
+    const int ntasks = pb.dk_ntasks[0];
+
+    // per-lane offsets of the transposing q reads (A operand: d = 32 db + l32, heads
+    // 16 kh + 8 (e / 4) + 4 half + e % 4 as k): rows 16 kh + 4 half + l16/4 (+ 8), whose
+    // swizzle does not depend on kh; columns 32 db + 16 (grp % 2) + 4 (l16 % 4)
+    int qoff[NDT];
+#pragma unroll
+    for (int db = 0; db < NDT; ++db)
+        qoff[db] = tile_off<DCH>(4 * half + (l16 >> 2), 32 * db + 16 * (grp & 1) + 4 * (l16 & 3));
+
+  for (int task = blockIdx.x; task < ntasks; task += gridDim.x) {
+    const int kbt = pb.dk_tasks[4 * task];
+    const int r0 = pb.dk_tasks[4 * task + 1], r1 = pb.dk_tasks[4 * task + 2];
+    const int kb = kbt % pb.dk_nkb;
+    const int g = (kbt / pb.dk_nkb) % pb.n2;
     const int j0 = kb * KB;
     const int j1 = j0 + KB < S2 ? j0 + KB : S2;
     const int nk = j1 - j0;                    // keys of this block
-    const int r0 = b * S1 + (int)((int64_t)S1 * sp / rsplits);
-    const int r1 = b * S1 + (int)((int64_t)S1 * (sp + 1) / rsplits);
-    const int kw = 32 * wave + l32;            // this lane's key within the block (B column)
     const bool jok = kw < nk;
-    const uint16_t *qsrc = F16 ? pb.q : pb.q16;
 
     // ---- active rows: those of [r0, r1) whose unit names a key of [j0, j1), in
     //      order, listed in LDS a chunk of kDkBlock rows at a time
@@ -206,14 +213,6 @@ __device__ __forceinline__ void dense_dk_body(const Problem &pb, int rsplits, in
             __builtin_amdgcn_raw_ptr_buffer_load_lds(v, (lds_void_t2 *)dst, 16, vos[i], 0, 0, 0);
         }
     };
-
-    // ---- per-lane offsets of the transposing q reads (A operand: d = 32 db + l32,
-    //      heads 16 kh + 8 (e / 4) + 4 half + e % 4 as k): rows 16 kh + 4 half + l16/4
-    //      (+ 8), whose swizzle does not depend on kh; columns 32 db + 16 (grp % 2) + 4 (l16 % 4)
-    int qoff[NDT];
-#pragma unroll
-    for (int db = 0; db < NDT; ++db)
-        qoff[db] = tile_off<DCH>(4 * half + (l16 >> 2), 32 * db + 16 * (grp & 1) + 4 * (l16 & 3));
 
     f32x16 acc[NDT];
 #pragma unroll
@@ -293,9 +292,9 @@ __device__ __forceinline__ void dense_dk_body(const Problem &pb, int rsplits, in
         --inflight;
     }
 
-    // ---- partial sum of this row range: dk_part[sp][key row][g][d]
-    if (jok) {
-        float *part = pb.dk_part + (((size_t)sp * pb.t2 + (size_t)b * S2 + j0 + kw) * pb.n2 + g) * D;
+    // ---- this task's partial sum: dk_part[task][key within the block][d]
+    {
+        float *part = pb.dk_part + ((size_t)task * KB + kw) * D;
 #pragma unroll
         for (int db = 0; db < NDT; ++db)
 #pragma unroll
@@ -303,52 +302,217 @@ __device__ __forceinline__ void dense_dk_body(const Problem &pb, int rsplits, in
                 *(float4 *)(part + 32 * db + 8 * jq + 4 * half) =
                     float4{acc[db][4 * jq], acc[db][4 * jq + 1], acc[db][4 * jq + 2], acc[db][4 * jq + 3]};
     }
+    lds_barrier();          // the ring and the row list are reused by the next task
+  }
 }
 
 // The body under the register budget of two workgroups per compute unit, or of one.
 template <int HP, int D, bool F16>
-__global__ __launch_bounds__(kDkBlock, 2) void dense_dk_kernel2(Problem pb, int rsplits, int nkb) {
-    dense_dk_body<HP, D, F16>(pb, rsplits, nkb);
+__global__ __launch_bounds__(kDkBlock, 2) void dense_dk_kernel2(Problem pb) {
+    dense_dk_body<HP, D, F16>(pb);
 }
 
 template <int HP, int D, bool F16>
-__global__ __launch_bounds__(kDkBlock, 1) void dense_dk_kernel1(Problem pb, int rsplits, int nkb) {
-    dense_dk_body<HP, D, F16>(pb, rsplits, nkb);
+__global__ __launch_bounds__(kDkBlock, 1) void dense_dk_kernel1(Problem pb) {
+    dense_dk_body<HP, D, F16>(pb);
 }
 
-// dk = round16(sum over row splits of the partials, in split order)
+// Task table (one workgroup): active rows per (key block, row chunk) from the
+// difference arrays, n_k = 1 + floor(c_k (S - K) / C) tasks for a key block with
+// c_k > 0 active rows (C their sum, K such blocks, S resident workgroups; one task
+// each when K >= S), task s of a block starting at the chunk that holds its
+// active row floor(s c_k / n_k).  Key blocks go through LDS KT at a time: a
+// thread per chunk runs the prefix over key blocks, a wave per key block the sums
+// and searches over chunks (at most 256 chunks: four per lane).
+constexpr int kTaskKT = 48;
+constexpr int kTaskNchMax = 256;
+
+__global__ __launch_bounds__(1024) void dense_dk_tasks_kernel(Problem pb) {
+    const int nbg = pb.batch * pb.n2, nkb = pb.dk_nkb, nch = pb.dk_nch, chunk = pb.dk_chunk;
+    const int NT = nbg * nkb;
+    const int S1 = (int)pb.s1;
+    __shared__ int s_cnt[kTaskKT * kTaskNchMax];     // [k within the tile][chunk]
+    __shared__ int s_run[kTaskNchMax];
+    __shared__ long long s_tot[16];
+    __shared__ int s_ne[16];
+    __shared__ int s_scan[1024];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    long long tot = 0;
+    int ne = 0;
+    // pass 1: active rows per (key block, chunk), written over the difference arrays,
+    // and per key block
+    for (int bg = 0; bg < nbg; ++bg) {
+        if (tid < nch) s_run[tid] = 0;
+        for (int k0 = 0; k0 < nkb; k0 += kTaskKT) {
+            const int kt = nkb - k0 < kTaskKT ? nkb - k0 : kTaskKT;
+            __syncthreads();
+            for (int i = tid; i < nch * kt; i += 1024) {
+                const int ch = i / kt, k = i - ch * kt;
+                s_cnt[k * kTaskNchMax + ch] = pb.kb_diff[((size_t)bg * nch + ch) * (nkb + 1) + k0 + k];
+            }
+            __syncthreads();
+            if (tid < nch) {                // prefix over key blocks along the chunk's row
+                int run = s_run[tid];
+                for (int k = 0; k < kt; ++k) {
+                    run += s_cnt[k * kTaskNchMax + tid];
+                    s_cnt[k * kTaskNchMax + tid] = run;
+                }
+                s_run[tid] = run;
+            }
+            __syncthreads();
+            for (int i = tid; i < nch * kt; i += 1024) {
+                const int ch = i / kt, k = i - ch * kt;
+                pb.kb_diff[((size_t)bg * nch + ch) * (nkb + 1) + k0 + k] = s_cnt[k * kTaskNchMax + ch];
+            }
+            for (int k = wave; k < kt; k += 16) {
+                int c = 0;
+                for (int ch = lane; ch < nch; ch += 64) c += s_cnt[k * kTaskNchMax + ch];
+                for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+                if (lane == 0) {
+                    pb.kb_tasks[4 * (bg * nkb + k0 + k) + 2] = c;
+                    tot += c;
+                    ne += c > 0 ? 1 : 0;
+                }
+            }
+        }
+    }
+    if (lane == 0) {
+        s_tot[wave] = tot;
+        s_ne[wave] = ne;
+    }
+    __syncthreads();
+    long long C = 0;
+    int K = 0;
+    for (int w = 0; w < 16; ++w) {
+        C += s_tot[w];
+        K += s_ne[w];
+    }
+    const int S = pb.dk_slots;
+    // pass 2: tasks per key block and their first task (exclusive scan in rounds of 1024)
+    int base = 0;
+    for (int t0 = 0; t0 < NT; t0 += 1024) {
+        const int t = t0 + tid;
+        int n = 0;
+        if (t < NT) {
+            const int c = pb.kb_tasks[4 * t + 2];
+            n = c == 0 ? 0 : (K < S ? 1 + (int)((long long)c * (S - K) / C) : 1);
+        }
+        __syncthreads();
+        s_scan[tid] = n;
+        __syncthreads();
+        for (int o = 1; o < 1024; o <<= 1) {        // inclusive scan
+            const int v = tid >= o ? s_scan[tid - o] : 0;
+            __syncthreads();
+            s_scan[tid] += v;
+            __syncthreads();
+        }
+        if (t < NT) {
+            pb.kb_tasks[4 * t] = base + s_scan[tid] - n;
+            pb.kb_tasks[4 * t + 1] = n;
+        }
+        base += s_scan[1023];
+    }
+    if (tid == 0) pb.dk_ntasks[0] = base;
+    __syncthreads();
+    // pass 3: task rows; a wave per key block, lane l holding chunks 4 l .. 4 l + 3
+    for (int t = wave; t < NT; t += 16) {
+        const int n = pb.kb_tasks[4 * t + 1];
+        if (n == 0) continue;
+        const int first = pb.kb_tasks[4 * t], c = pb.kb_tasks[4 * t + 2];
+        const int bg = t / nkb, k = t - bg * nkb;
+        const int b = bg / pb.n2;
+        int cum[4];
+        int run = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ch = 4 * lane + i;
+            run += ch < nch ? pb.kb_diff[((size_t)bg * nch + ch) * (nkb + 1) + k] : 0;
+            cum[i] = run;                   // inclusive within the lane
+        }
+        int excl = run;                     // exclusive prefix of the lane totals
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(excl, o);
+            if (lane >= o) excl += v;
+        }
+        excl -= run;
+        int prev = 0;
+        for (int s = 0; s < n; ++s) {
+            const int target = (int)((long long)s * c / n);   // task s starts at the chunk holding this active row
+            int mine = 1 << 30;
+#pragma unroll
+            for (int i = 3; i >= 0; --i)
+                if (4 * lane + i < nch && excl + cum[i] > target) mine = 4 * lane + i;
+            for (int o = 32; o > 0; o >>= 1) mine = min(mine, __shfl_xor(mine, o));
+            if (s > 0 && lane == 0) {
+                int32_t *tk = pb.dk_tasks + 4 * (first + s - 1);
+                tk[0] = t;
+                tk[1] = b * S1 + prev * chunk;
+                tk[2] = b * S1 + (mine * chunk < S1 ? mine * chunk : S1);
+                tk[3] = 0;
+            }
+            prev = mine;
+        }
+        if (lane == 0) {
+            int32_t *tk = pb.dk_tasks + 4 * (first + n - 1);
+            tk[0] = t;
+            tk[1] = b * S1 + prev * chunk;
+            tk[2] = b * S1 + S1;
+            tk[3] = 0;
+        }
+    }
+}
+
+// dk = round16(sum of the key block's task partials, in task order)
 template <bool F16>
-__global__ void dense_dk_reduce_kernel(Problem pb, int rsplits) {
-    const size_t n = (size_t)pb.t2 * pb.n2 * pb.d;
+__global__ void dense_dk_reduce_kernel(Problem pb) {
+    const int D = pb.d, KB = pb.dk_kb;
+    const size_t n = (size_t)pb.t2 * pb.n2 * D;
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     for (; i < n; i += stride) {
+        const size_t kr = i / ((size_t)pb.n2 * D);        // key row (b S2 + j)
+        const int g = (int)((i / D) % pb.n2), d = (int)(i % D);
+        const int b = (int)(kr / pb.s2), j = (int)(kr % pb.s2);
+        const int kbt = (b * pb.n2 + g) * pb.dk_nkb + j / KB;
+        const int t0 = pb.kb_tasks[4 * kbt], nt = pb.kb_tasks[4 * kbt + 1];
         float s = 0.f;
-        for (int sp = 0; sp < rsplits; ++sp) s += pb.dk_part[(size_t)sp * n + i];
+        for (int t = t0; t < t0 + nt; ++t) s += pb.dk_part[((size_t)t * KB + j % KB) * D + d];
         pb.dk[i] = to16<F16>(s);
     }
 }
 
 template <int HP, int D, bool F16>
-static hipError_t launch_dense(const Problem &pb, int rsplits, int nkb, hipStream_t stream) {
-    const int grid = nkb * rsplits * pb.n2 * pb.batch;
+static hipError_t launch_dense(const Problem &pb, hipStream_t stream) {
     if constexpr (DenseCfg<HP, D>::WGPC == 2)
-        hipLaunchKernelGGL((dense_dk_kernel2<HP, D, F16>), dim3(grid), dim3(kDkBlock), 0, stream, pb, rsplits, nkb);
+        hipLaunchKernelGGL((dense_dk_kernel2<HP, D, F16>), dim3(pb.dk_slots), dim3(kDkBlock), 0, stream, pb);
     else
-        hipLaunchKernelGGL((dense_dk_kernel1<HP, D, F16>), dim3(grid), dim3(kDkBlock), 0, stream, pb, rsplits, nkb);
+        hipLaunchKernelGGL((dense_dk_kernel1<HP, D, F16>), dim3(pb.dk_slots), dim3(kDkBlock), 0, stream, pb);
     return hipGetLastError();
 }
 
 int dense_dk_keys_per_block() { return DenseCfg<32, 32>::KB; }
 
-hipError_t launch_dense_dk(const Problem &pb, int hp, bool f16, int rsplits, hipStream_t stream) {
-    const int nkb = (int)((pb.s2 + DenseCfg<32, 32>::KB - 1) / DenseCfg<32, 32>::KB);
+int dense_dk_wgs_per_cu(int hp, int d) {
+#define SLIKL_DENSE_WG(HPV, DV) \
+    if (hp == HPV && d == DV) return DenseCfg<HPV, DV>::WGPC;
+    SLIKL_DENSE_WG(32, 32) SLIKL_DENSE_WG(32, 64) SLIKL_DENSE_WG(32, 128)
+    SLIKL_DENSE_WG(64, 32) SLIKL_DENSE_WG(64, 64) SLIKL_DENSE_WG(64, 128)
+    SLIKL_DENSE_WG(128, 32) SLIKL_DENSE_WG(128, 64) SLIKL_DENSE_WG(128, 128)
+#undef SLIKL_DENSE_WG
+    return 1;
+}
+
+hipError_t launch_dense_dk_tasks(const Problem &pb, hipStream_t stream) {
+    hipLaunchKernelGGL(dense_dk_tasks_kernel, dim3(1), dim3(1024), 0, stream, pb);
+    return hipGetLastError();
+}
+
+hipError_t launch_dense_dk(const Problem &pb, int hp, bool f16, hipStream_t stream) {
     const int d = pb.d;
     hipError_t e;
 #define SLIKL_DENSE_CASE(HPV, DV)                                                              \
     if (hp == HPV && d == DV)                                                                  \
-        e = f16 ? launch_dense<HPV, DV, true>(pb, rsplits, nkb, stream)                        \
-                : launch_dense<HPV, DV, false>(pb, rsplits, nkb, stream);
+        e = f16 ? launch_dense<HPV, DV, true>(pb, stream) : launch_dense<HPV, DV, false>(pb, stream);
     SLIKL_DENSE_CASE(32, 32) else SLIKL_DENSE_CASE(32, 64) else SLIKL_DENSE_CASE(32, 128)
     else SLIKL_DENSE_CASE(64, 32) else SLIKL_DENSE_CASE(64, 64) else SLIKL_DENSE_CASE(64, 128)
     else SLIKL_DENSE_CASE(128, 32) else SLIKL_DENSE_CASE(128, 64) else SLIKL_DENSE_CASE(128, 128)
@@ -357,15 +521,15 @@ hipError_t launch_dense_dk(const Problem &pb, int hp, bool f16, int rsplits, hip
     return e;
 }
 
-hipError_t launch_dense_dk_reduce(const Problem &pb, bool f16, int rsplits, hipStream_t stream) {
+hipError_t launch_dense_dk_reduce(const Problem &pb, bool f16, hipStream_t stream) {
     const size_t n = (size_t)pb.t2 * pb.n2 * pb.d;
     size_t blocks = (n + 255) / 256;
     if (blocks > 4096) blocks = 4096;
     if (blocks == 0) return hipSuccess;
     if (f16)
-        hipLaunchKernelGGL(dense_dk_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, pb, rsplits);
+        hipLaunchKernelGGL(dense_dk_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, pb);
     else
-        hipLaunchKernelGGL(dense_dk_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, pb, rsplits);
+        hipLaunchKernelGGL(dense_dk_reduce_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, pb);
     return hipGetLastError();
 }
 

@@ -354,6 +354,14 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
             pb.row_range[2 * u] = kmin_i;
             pb.row_range[2 * u + 1] = nvalid > 0 ? kmax_i : -1;
             *(u32x4 *)(wrec + HP * 4) = u32x4{(uint32_t)(eq + ew), (uint32_t)ed, 0u, 0u};
+            if (nvalid > 0) {
+                // dK task sizing: +1 / -1 at the first / past the last key block that
+                // the named key range [kmin, kmax] meets, in this row's chunk
+                int32_t *dif = pb.kb_diff + ((size_t)(b * pb.n2 + g) * pb.dk_nch + (r - b * S1) / pb.dk_chunk) *
+                                                (pb.dk_nkb + 1);
+                atomicAdd(dif + kmin_i / pb.dk_kb, 1);
+                atomicAdd(dif + kmax_i / pb.dk_kb + 1, -1);
+            }
         }
 
         // ---- pass 1: S tiles on MFMA; the VALU epilogue of one tile (ReLU, w, head

@@ -86,14 +86,15 @@ int unit_overhead(const slikl_desc *d) {
 // Query-row ranges of the key-major dK kernel: about 1024 workgroups in all,
 // ranges of at least 16 rows where possible, and a multiple of 8 ranges (the
 // kernel deals whole ranges to the 8 XCDs).
-int dense_row_splits(const slikl_desc *d) {
+// Dense dK task geometry: key blocks per (batch, key head), row chunk length and
+// count (at most 256 chunks per batch), and the most tasks the table can hold.
+void dense_dk_geometry(const slikl_desc *d, int *nkb, int *chunk, int *nch, int *max_tasks) {
     const int64_t kb = slikl::dense_dk_keys_per_block();
-    const int64_t nkb = (d->s2 + kb - 1) / kb;
-    int64_t rs = (1024 + nkb * d->n2 * d->batch - 1) / (nkb * d->n2 * d->batch);
-    const int64_t cap = d->s1 / 16 > 1 ? d->s1 / 16 : 1;
-    rs = rs < 1 ? 1 : (rs > cap ? cap : rs);
-    rs = (rs + 7) / 8 * 8;
-    return (int)rs;
+    *nkb = (int)((d->s2 + kb - 1) / kb);
+    const int64_t c = (d->s1 + 255) / 256;
+    *chunk = (int)(c < 16 ? 16 : c);
+    *nch = (int)((d->s1 + *chunk - 1) / *chunk);
+    *max_tasks = slikl::kDkSlotsMax + (int)(d->batch * d->n2) * *nkb;
 }
 
 slikl::WorkspacePlan plan(const slikl_desc *d) {
@@ -123,7 +124,8 @@ slikl::WorkspacePlan plan(const slikl_desc *d) {
     off = align_up(off + p.k16_bytes);
     if (mode == 2) {
         const size_t s2 = (size_t)d->s2, nh = (size_t)head_tile(d->n1 / d->n2) / 32;
-        p.rsplits = dense_row_splits(d);
+        dense_dk_geometry(d, &p.dk_nkb, &p.dk_chunk, &p.dk_nch, &p.dk_max_tasks);
+        const size_t nbg = (size_t)d->batch * (size_t)d->n2;
         p.dimap_off = off;
         p.dimap_bytes = U * s2 * 4;
         off = align_up(off + p.dimap_bytes);
@@ -136,7 +138,16 @@ slikl::WorkspacePlan plan(const slikl_desc *d) {
         p.wrec_off = off;
         off = align_up(off + U * (size_t)slikl::wrec_bytes(head_tile(d->n1 / d->n2)));
         p.part_off = off;
-        off = align_up(off + (size_t)p.rsplits * (size_t)t2 * (size_t)d->n2 * (size_t)d->d * 4);
+        off = align_up(off + (size_t)p.dk_max_tasks * slikl::dense_dk_keys_per_block() * (size_t)d->d * 4);
+        p.kbdiff_off = off;
+        p.kbdiff_bytes = nbg * (size_t)p.dk_nch * (size_t)(p.dk_nkb + 1) * 4;
+        off = align_up(off + p.kbdiff_bytes);
+        p.tasks_off = off;
+        off = align_up(off + (size_t)p.dk_max_tasks * 16);
+        p.kbtasks_off = off;
+        off = align_up(off + nbg * (size_t)p.dk_nkb * 16);
+        p.ntasks_off = off;
+        off = align_up(off + 16);
     }
     p.total = off;
     return p;
@@ -333,6 +344,23 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
         pb.q16 = (uint16_t *)(ws + wp.q16_off);
         pb.wrec = (uint8_t *)(ws + wp.wrec_off);
         pb.dk_part = (float *)(ws + wp.part_off);
+        pb.kb_diff = (int32_t *)(ws + wp.kbdiff_off);
+        pb.dk_tasks = (int32_t *)(ws + wp.tasks_off);
+        pb.kb_tasks = (int32_t *)(ws + wp.kbtasks_off);
+        pb.dk_ntasks = (int32_t *)(ws + wp.ntasks_off);
+        pb.dk_kb = slikl::dense_dk_keys_per_block();
+        pb.dk_nkb = wp.dk_nkb;
+        pb.dk_chunk = wp.dk_chunk;
+        pb.dk_nch = wp.dk_nch;
+        pb.dk_max_tasks = wp.dk_max_tasks;
+        {
+            int dev = 0, cus = 0;
+            if (hipGetDevice(&dev) != hipSuccess ||
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+                return SLIKL_ERR_LAUNCH;
+            int64_t slots = (int64_t)cus * slikl::dense_dk_wgs_per_cu(head_tile(pb.group), (int)desc->d);
+            pb.dk_slots = (int)(slots > slikl::kDkSlotsMax ? slikl::kDkSlotsMax : slots);
+        }
         pb.s2max = desc->s2;
     }
 
@@ -352,6 +380,7 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
     if (e == hipSuccess) e = slikl::launch_zero(ws + wp.scale_off, 64, s);
     if (e == hipSuccess) e = slikl::launch_zero(ws + wp.zero_off, 256, s);
     if (e == hipSuccess && mode == 2) e = slikl::launch_zero(pb.dI_map, wp.dimap_bytes, s);
+    if (e == hipSuccess && mode == 2) e = slikl::launch_zero(pb.kb_diff, wp.kbdiff_bytes, s);
     pe.end(SLIKL_PHASE_FILL);
     if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
     if (!f16 && t2 > 0) {
@@ -375,11 +404,12 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
     }
     if (mode == 2) {
         pe.begin(SLIKL_PHASE_DK);
-        e = slikl::launch_dense_dk(pb, head_tile(pb.group), f16, wp.rsplits, s);
+        e = slikl::launch_dense_dk_tasks(pb, s);
+        if (e == hipSuccess) e = slikl::launch_dense_dk(pb, head_tile(pb.group), f16, s);
         pe.end(SLIKL_PHASE_DK);
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
         pe.begin(SLIKL_PHASE_DK_FINAL);
-        e = slikl::launch_dense_dk_reduce(pb, f16, wp.rsplits, s);
+        e = slikl::launch_dense_dk_reduce(pb, f16, s);
         pe.end(SLIKL_PHASE_DK_FINAL);
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
         return SLIKL_OK;

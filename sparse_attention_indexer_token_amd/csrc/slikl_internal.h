@@ -35,7 +35,15 @@ struct Problem {
     uint8_t *wrec;           // per unit u, wrec_bytes(HP) bytes at u * wrec_bytes(HP): fp16 hi
                              // parts of w 2^ew [HP], fp16 lo parts [HP] (zero past G), then
                              // int32 eq + ew (query and w scales), int32 ed (dI exponent), 0, 0
-    float *dk_part;          // [RS, T2, N2, D] per-row-split partial dK sums
+    float *dk_part;          // [dk_max_tasks, dk_kb, D] partial dK sums of the dK tasks
+    // dense dK tasks: per (batch, key head) and row chunk of dk_chunk rows, a difference
+    // array over key blocks of dk_kb keys of the units whose named key range meets the
+    // block (+1 at the first block, -1 past the last); the task table built from it
+    int32_t *kb_diff;        // [batch * N2, dk_nch, dk_nkb + 1]
+    int32_t *dk_tasks;       // [dk_max_tasks, 4]: key block id, first row, end row, 0
+    int32_t *kb_tasks;       // [batch * N2 * dk_nkb, 4]: first task, task count, active rows, 0
+    int32_t *dk_ntasks;      // number of tasks
+    int32_t dk_kb, dk_nkb, dk_chunk, dk_nch, dk_slots, dk_max_tasks;
     int64_t s2max;           // key length of the dense maps
     const int32_t *cu_q;     // [batch + 1] or null (BSND)
     const int32_t *cu_k;     // [batch + 1] or null (BSND)
@@ -55,8 +63,9 @@ struct WorkspacePlan {
     size_t k16_off, k16_bytes;      // fp16 copy of k (bf16 inputs only)
     size_t zero_off;                // 256 zero bytes
     int mode;                       // dK strategy (see launch_grad_fused)
-    int rsplits;                    // dense mode: query-row ranges of the key-major kernel
     size_t dimap_off, dimap_bytes, maskmap_off, range_off, q16_off, wrec_off, part_off;
+    size_t kbdiff_off, kbdiff_bytes, tasks_off, kbtasks_off, ntasks_off;
+    int dk_nkb, dk_chunk, dk_nch, dk_max_tasks;
     size_t total;
 };
 
@@ -73,9 +82,12 @@ int grad_dense_blocks_per_cu(int hp, int d, bool f16);
 hipError_t launch_grad_dense8(const Problem &pb, int hp, bool f16, int grid, hipStream_t stream);
 int grad_dense8_blocks_per_cu(int hp, int d, bool f16);
 hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t stream);
-hipError_t launch_dense_dk(const Problem &pb, int hp, bool f16, int rsplits, hipStream_t stream);
-hipError_t launch_dense_dk_reduce(const Problem &pb, bool f16, int rsplits, hipStream_t stream);
+hipError_t launch_dense_dk_tasks(const Problem &pb, hipStream_t stream);
+hipError_t launch_dense_dk(const Problem &pb, int hp, bool f16, hipStream_t stream);
+hipError_t launch_dense_dk_reduce(const Problem &pb, bool f16, hipStream_t stream);
 int dense_dk_keys_per_block();
+int dense_dk_wgs_per_cu(int hp, int d);
+constexpr int kDkSlotsMax = 1024;   // cap on concurrently resident dK workgroups
 hipError_t launch_finalize_dk(const Problem &pb, bool f16, bool det, hipStream_t stream);
 hipError_t launch_det_scale(const Problem &pb, bool f16, float *scale_block, hipStream_t stream);
 hipError_t launch_k_to_f16(const Problem &pb, uint16_t *k16, float *scale_block, hipStream_t stream);
