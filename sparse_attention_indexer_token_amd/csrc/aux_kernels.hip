@@ -28,6 +28,28 @@ hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t stream) {
     return hipGetLastError();
 }
 
+__global__ void zero_ranges_kernel(ZeroRanges zr) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (int r = 0; r < zr.n; ++r) {
+        const size_t n16 = zr.bytes[r] / 16, ntail = (zr.bytes[r] - n16 * 16) / 4;
+        u32x4 *p = (u32x4 *)zr.ptr[r];
+        for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+            p[i] = u32x4{0u, 0u, 0u, 0u};
+        if (blockIdx.x == 0 && threadIdx.x < ntail) ((uint32_t *)(p + n16))[threadIdx.x] = 0u;
+    }
+}
+
+hipError_t launch_zero_ranges(const ZeroRanges &zr, hipStream_t stream) {
+    size_t most = 0;
+    for (int r = 0; r < zr.n; ++r) most = zr.bytes[r] / 16 > most ? zr.bytes[r] / 16 : most;
+    if (zr.n == 0) return hipSuccess;
+    size_t blocks = (most + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
+    if (blocks == 0) blocks = 1;
+    hipLaunchKernelGGL(zero_ranges_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, zr);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // dK = round16(accumulator).  Deterministic mode: accumulator is int64 fixed
 // point with scale 2^F, read back as acc * 2^-F.
@@ -139,13 +161,30 @@ hipError_t launch_det_scale(const Problem &pb, bool f16, float *scale_block, hip
 // magnitude is >= 2^-14 converts exactly; smaller ones keep an absolute error
 // below 2^-25 * 2^-eK.  scale block: [5] max|k| bits, [6] 2^-eK, [7] 2^eK.
 // ---------------------------------------------------------------------------
-__global__ void kmax_kernel(const uint16_t *k, size_t n, uint32_t *blk) {
+// max |k| over bf16 keys, 16 bytes per load; for bf16 bits b, |x| orders as the
+// integer b & 0x7fff, so the maximum is taken on packed bit patterns
+__global__ __launch_bounds__(256) void kmax_kernel(const uint16_t *k, size_t n8, uint32_t *blk) {
+    __shared__ uint32_t s_m[4];
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
-    float m = 0.f;
-    for (; i < n; i += stride) m = fmaxf(m, fabsf(from16<false>(k[i])));
-    m = wave_max(m);
-    if ((threadIdx.x & 63) == 0) atomicMax(blk + 5, __float_as_uint(m));
+    u16x2 mb = {0, 0};
+    for (; i < n8; i += stride) {
+        const u32x4 v = ((const u32x4 *)k)[i];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) mb = __builtin_elementwise_max(mb, __builtin_bit_cast(u16x2, v[c] & 0x7fff7fffu));
+    }
+    uint32_t m = mb.x > mb.y ? mb.x : mb.y;
+    for (int o = 32; o > 0; o >>= 1) {
+        const uint32_t x = (uint32_t)__shfl_xor((int)m, o);
+        m = x > m ? x : m;
+    }
+    if ((threadIdx.x & 63) == 0) s_m[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = s_m[0];
+        for (int w = 1; w < 4; ++w) r = s_m[w] > r ? s_m[w] : r;
+        atomicMax(blk + 5, __float_as_uint(__uint_as_float(r << 16)));
+    }
 }
 
 __device__ __forceinline__ int k_exponent(const uint32_t *blk) {
@@ -184,7 +223,7 @@ hipError_t launch_k_to_f16(const Problem &pb, uint16_t *k16, float *scale_block,
     size_t blocks = (n / 8 + 255) / 256;
     if (blocks > 2048) blocks = 2048;
     if (blocks == 0) blocks = 1;
-    hipLaunchKernelGGL(kmax_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pb.k, n,
+    hipLaunchKernelGGL(kmax_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pb.k, n / 8,
                        (uint32_t *)scale_block);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -224,10 +263,32 @@ __global__ void meta_count_kernel(Problem pb, int64_t *prefix, int overhead, int
         }
         const int32_t *row = pb.idx + u * pb.topk;
         int cnt = 0;
-        for (int s = lane; s < pb.topk; s += 64) {
-            int v = row[s];
+        auto tally = [&](int v) {
             if (v >= 0 && v < klen) ++cnt;
             else if (v != -1) bad = 1;
+        };
+        if ((pb.topk & 3) == 0 && ((uintptr_t)row & 15) == 0) {
+            // 16-byte loads, all of a lane's issued before any is used
+            const int n4 = pb.topk >> 2;
+            const int4 *r4 = (const int4 *)row;
+            constexpr int UNR = 8;
+            for (int s0 = 0; s0 < n4; s0 += 64 * UNR) {
+                int4 v[UNR];
+#pragma unroll
+                for (int j = 0; j < UNR; ++j) {
+                    const int s = s0 + 64 * j + lane;
+                    v[j] = s < n4 ? r4[s] : int4{-1, -1, -1, -1};
+                }
+#pragma unroll
+                for (int j = 0; j < UNR; ++j) {
+                    tally(v[j].x);
+                    tally(v[j].y);
+                    tally(v[j].z);
+                    tally(v[j].w);
+                }
+            }
+        } else {
+            for (int s = lane; s < pb.topk; s += 64) tally(row[s]);
         }
         for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
         if (lane == 0) prefix[u + 1] = cnt + overhead;
@@ -247,7 +308,9 @@ __device__ __forceinline__ int check_cu(const int32_t *cu, int batch, int64_t to
 __global__ __launch_bounds__(1024) void meta_split_kernel(Problem pb, int parts, int mode, int overhead,
                                                           int64_t *prefix, const int32_t *cflags,
                                                           int32_t *md) {
+    constexpr int kSplitLds = 8192;
     __shared__ int64_t s_part[1024];
+    __shared__ int64_t s_cost[kSplitLds];
     __shared__ int s_used[32];
     const int tid = threadIdx.x, nt = blockDim.x;
     const int64_t U = pb.t1 * pb.n2;
@@ -281,8 +344,16 @@ __global__ __launch_bounds__(1024) void meta_split_kernel(Problem pb, int parts,
         // inclusive scan of prefix[1..U] (prefix[0] = 0): contiguous segments per thread
         const int64_t seg = (U + nt - 1) / nt;
         const int64_t a = (int64_t)tid * seg, e = a + seg < U ? a + seg : U;
+        // up to kSplitLds units: the costs go through LDS (one parallel load instead of
+        // dependent global round trips per unit)
+        const bool inlds = U <= kSplitLds;
+        int64_t *cost = inlds ? s_cost : prefix + 1;   // cost[i] = cost of unit i
+        if (inlds) {
+            for (int64_t i = tid; i < U; i += nt) s_cost[i] = prefix[i + 1];
+            __syncthreads();
+        }
         int64_t loc = 0;
-        for (int64_t i = a; i < e; ++i) loc += prefix[i + 1];
+        for (int64_t i = a; i < e; ++i) loc += cost[i];
         s_part[tid] = loc;
         __syncthreads();
         for (int o = 1; o < nt; o <<= 1) {   // Hillis-Steele inclusive scan
@@ -292,22 +363,30 @@ __global__ __launch_bounds__(1024) void meta_split_kernel(Problem pb, int parts,
             __syncthreads();
         }
         int64_t run = tid > 0 ? s_part[tid - 1] : 0;
-        for (int64_t i = a; i < e; ++i) {
-            run += prefix[i + 1];
-            prefix[i + 1] = run;
+        for (int64_t i = a; i < e; ++i) {      // cost[i] becomes E(i + 1)
+            run += cost[i];
+            cost[i] = run;
         }
-        if (tid == 0) prefix[0] = 0;
         __syncthreads();
         const int64_t W = s_part[nt - 1];
-        for (int i = tid; i <= parts; i += nt) {
-            // first u in [0, U] with prefix[u] * parts >= i * W
-            int64_t lo = 0, hi = U;
-            const int64_t target = (int64_t)i * W;
-            while (lo < hi) {
-                int64_t mid = (lo + hi) >> 1;
-                if (prefix[mid] * parts >= target) hi = mid; else lo = mid + 1;
+        // boundary i is the first u in [0, U] with E(u) parts >= i W (E the exclusive
+        // prefix, E(0) = 0, E(U) = W): u = 0 takes i = 0 (every i when W = 0), and
+        // u >= 1 takes the i with E(u-1) parts < i W <= E(u) parts, i <= parts.  Each
+        // thread writes the boundaries of its own units u in [a + 1, e].
+        if (W == 0) {
+            for (int i = tid; i <= parts; i += nt) bnd[i] = 0;
+        } else {
+            if (tid == 0) bnd[0] = 0;
+            int64_t prev = tid > 0 ? s_part[tid - 1] : 0;      // E(a)
+            for (int64_t u = a + 1; u <= e; ++u) {
+                const int64_t cur = cost[u - 1];               // E(u)
+                // i with prev parts < i W <= cur parts: i in [floor(prev parts / W) + 1, floor(cur parts / W)]
+                int64_t i0 = prev * parts / W + 1;
+                int64_t i1 = cur * parts / W;
+                if (i1 > parts) i1 = parts;
+                for (int64_t i = i0; i <= i1; ++i) bnd[i] = (int32_t)u;
+                prev = cur;
             }
-            bnd[i] = (int32_t)lo;
         }
     } else {
         int64_t former = 0, remain = 0, remain_num = 0, former_num = 0;

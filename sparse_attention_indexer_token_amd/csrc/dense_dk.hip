@@ -346,9 +346,21 @@ __global__ __launch_bounds__(1024) void dense_dk_tasks_kernel(Problem pb) {
         for (int k0 = 0; k0 < nkb; k0 += kTaskKT) {
             const int kt = nkb - k0 < kTaskKT ? nkb - k0 : kTaskKT;
             __syncthreads();
-            for (int i = tid; i < nch * kt; i += 1024) {
-                const int ch = i / kt, k = i - ch * kt;
-                s_cnt[k * kTaskNchMax + ch] = pb.kb_diff[((size_t)bg * nch + ch) * (nkb + 1) + k0 + k];
+            {
+                constexpr int PER = (kTaskKT * kTaskNchMax + 1023) / 1024;
+                int v[PER];                 // all loads issued before any LDS store
+#pragma unroll
+                for (int j = 0; j < PER; ++j) {
+                    const int i = tid + 1024 * j;
+                    const int ch = i / kt, k = i - ch * kt;
+                    v[j] = i < nch * kt ? pb.kb_diff[((size_t)bg * nch + ch) * (nkb + 1) + k0 + k] : 0;
+                }
+#pragma unroll
+                for (int j = 0; j < PER; ++j) {
+                    const int i = tid + 1024 * j;
+                    const int ch = i / kt, k = i - ch * kt;
+                    if (i < nch * kt) s_cnt[k * kTaskNchMax + ch] = v[j];
+                }
             }
             __syncthreads();
             if (tid < nch) {                // prefix over key blocks along the chunk's row
@@ -435,30 +447,28 @@ __global__ __launch_bounds__(1024) void dense_dk_tasks_kernel(Problem pb) {
             if (lane >= o) excl += v;
         }
         excl -= run;
-        int prev = 0;
-        for (int s = 0; s < n; ++s) {
-            const int target = (int)((long long)s * c / n);   // task s starts at the chunk holding this active row
-            int mine = 1 << 30;
+        // task s starts at the chunk holding active row floor(s c / n): the chunk with
+        // cumulative counts (lo, hi] starts tasks ceil(lo n / c) .. ceil(hi n / c) - 1,
+        // and the task before each of them ends there
 #pragma unroll
-            for (int i = 3; i >= 0; --i)
-                if (4 * lane + i < nch && excl + cum[i] > target) mine = 4 * lane + i;
-            for (int o = 32; o > 0; o >>= 1) mine = min(mine, __shfl_xor(mine, o));
-            if (s > 0 && lane == 0) {
-                int32_t *tk = pb.dk_tasks + 4 * (first + s - 1);
+        for (int i = 0; i < 4; ++i) {
+            const int ch = 4 * lane + i;
+            if (ch >= nch) break;
+            const long long lo = excl + (i == 0 ? 0 : cum[i - 1]), hi = excl + cum[i];
+            if (hi == lo) continue;
+            const int s0 = (int)((lo * n + c - 1) / c);
+            int s1 = (int)((hi * n + c - 1) / c);
+            s1 = s1 < n ? s1 : n;
+            const int row = b * S1 + ch * chunk;
+            for (int st = s0; st < s1; ++st) {
+                int32_t *tk = pb.dk_tasks + 4 * (first + st);
                 tk[0] = t;
-                tk[1] = b * S1 + prev * chunk;
-                tk[2] = b * S1 + (mine * chunk < S1 ? mine * chunk : S1);
+                tk[1] = row;
                 tk[3] = 0;
+                if (st > 0) tk[-2] = row;           // end of task st - 1
             }
-            prev = mine;
         }
-        if (lane == 0) {
-            int32_t *tk = pb.dk_tasks + 4 * (first + n - 1);
-            tk[0] = t;
-            tk[1] = b * S1 + prev * chunk;
-            tk[2] = b * S1 + S1;
-            tk[3] = 0;
-        }
+        if (lane == 0) pb.dk_tasks[4 * (first + n - 1) + 2] = b * S1 + S1;
     }
 }
 

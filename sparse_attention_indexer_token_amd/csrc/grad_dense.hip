@@ -249,6 +249,16 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
         const float pmax = mxv[0], psum = smv[0];
         const int kmax_i = (int)mxv[1];
         const int kmin_i = nvalid > 0 ? (int)(-mxv[2]) : 0x7fffffff;
+        // zero this unit's dI row over the key blocks its named keys meet (the dK
+        // kernel reads whole blocks for rows whose range meets them); these stores
+        // complete before the integer adds of pass 2 (waited on before the next barrier)
+        if (nvalid > 0) {
+            const int z0 = (kmin_i / pb.dk_kb) * pb.dk_kb;
+            const int z1e = (kmax_i / pb.dk_kb + 1) * pb.dk_kb;
+            const int z1 = z1e < S2 ? z1e : S2;
+            int32_t *drow = pb.dI_map + (size_t)u * pb.s2max;
+            for (int j = z0 + tid; j < z1; j += kBlock) drow[j] = 0;
+        }
 #pragma unroll
         for (int i = 0; i < SPT_MAX; ++i) {
             const int v = in.iv[i];
@@ -280,6 +290,7 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
         float wabs = fabsf(s_w[lane < HP ? lane : 0]);
         if constexpr (HP > 64) wabs = fmaxf(wabs, fabsf(s_w[lane + 64 < HP ? lane + 64 : 0]));
         wabs = wave_max(wabs);
+        wait_vmcnt<0>();          // the dI row's zero stores have completed
         lds_barrier();            // compacted lists visible to every wave
 
         // ---- key stream: steps [0, nsteps) pass 1 (k), [nsteps, 2 nsteps) pass 2 ------

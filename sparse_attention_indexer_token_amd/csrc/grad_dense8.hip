@@ -415,6 +415,15 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
                 atomicAdd(dif + kmax_i / pb.dk_kb + 1, -1);
             }
         }
+        // zero this unit's dI row over the key blocks its named keys meet (the dK
+        // kernel reads whole blocks for rows whose range meets them)
+        if (nvalid > 0) {
+            const int z0 = (kmin_i / pb.dk_kb) * pb.dk_kb;
+            const int z1e = (kmax_i / pb.dk_kb + 1) * pb.dk_kb;
+            const int z1 = z1e < S2 ? z1e : S2;
+            int32_t *drow = pb.dI_map + (size_t)u * pb.s2max;
+            for (int j = z0 + tid; j < z1; j += kBlock8) drow[j] = 0;
+        }
 
         // w of the heads this lane's pass-1 tile elements belong to: 16 hq + 4 grp + i
         float wr[NQT][4];
@@ -423,6 +432,9 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
             const float4 w4 = *(const float4 *)(s_w + 16 * hq + 4 * grp);
             wr[hq][0] = w4.x; wr[hq][1] = w4.y; wr[hq][2] = w4.z; wr[hq][3] = w4.w;
         }
+        // the zero stores (and the first copies, issued just before them) complete
+        // before the integer adds of pass 2 in any wave
+        wait_vmcnt<0>();
         lds_barrier();            // every wave has q in registers: pass 1 may overwrite s_mask
 
         // ---- pass 1: S tiles (16 heads x 16 keys) on MFMA; ReLU, w, head bits ----------

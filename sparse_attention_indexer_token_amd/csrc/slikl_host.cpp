@@ -376,11 +376,16 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
     }
     pb.metadata = metadata;
     pe.begin(SLIKL_PHASE_FILL);
-    e = slikl::launch_zero(pb.dk_acc, wp.acc_bytes, s);
-    if (e == hipSuccess) e = slikl::launch_zero(ws + wp.scale_off, 64, s);
-    if (e == hipSuccess) e = slikl::launch_zero(ws + wp.zero_off, 256, s);
-    if (e == hipSuccess && mode == 2) e = slikl::launch_zero(pb.dI_map, wp.dimap_bytes, s);
-    if (e == hipSuccess && mode == 2) e = slikl::launch_zero(pb.kb_diff, wp.kbdiff_bytes, s);
+    {
+        // the dense dI rows are zeroed by the fused kernel, each over the key blocks
+        // its unit's named keys meet
+        slikl::ZeroRanges zr{};
+        zr.add(pb.dk_acc, wp.acc_bytes);
+        zr.add(ws + wp.scale_off, 64);
+        zr.add(ws + wp.zero_off, 256);
+        if (mode == 2) zr.add(pb.kb_diff, wp.kbdiff_bytes);
+        e = slikl::launch_zero_ranges(zr, s);
+    }
     pe.end(SLIKL_PHASE_FILL);
     if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
     if (!f16 && t2 > 0) {

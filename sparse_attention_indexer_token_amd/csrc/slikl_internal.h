@@ -82,6 +82,20 @@ int grad_dense_blocks_per_cu(int hp, int d, bool f16);
 hipError_t launch_grad_dense8(const Problem &pb, int hp, bool f16, int grid, hipStream_t stream);
 int grad_dense8_blocks_per_cu(int hp, int d, bool f16);
 hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t stream);
+// Up to 8 byte ranges (16-byte aligned starts, sizes multiples of 4) zeroed by one launch.
+struct ZeroRanges {
+    void *ptr[8];
+    size_t bytes[8];
+    int n;
+    void add(void *p, size_t b) {
+        if (b > 0 && n < 8) {
+            ptr[n] = p;
+            bytes[n] = b;
+            ++n;
+        }
+    }
+};
+hipError_t launch_zero_ranges(const ZeroRanges &zr, hipStream_t stream);
 hipError_t launch_dense_dk_tasks(const Problem &pb, hipStream_t stream);
 hipError_t launch_dense_dk(const Problem &pb, int hp, bool f16, hipStream_t stream);
 hipError_t launch_dense_dk_reduce(const Problem &pb, bool f16, hipStream_t stream);
