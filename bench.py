@@ -37,11 +37,32 @@ if ROOT not in sys.path:
 
 METRIC = "query tokens/sec at N1=64 D=128 topk=2048 bf16; % of MFMA bf16 peak"
 PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "grad_dense_kernel_dsv32_indexer_traffic.txt")
+CSRC = os.path.join(ROOT, "sparse_attention_indexer_token_amd", "csrc")
+# sources each fused kernel is compiled from (a change to any voids its traffic figure)
 KERNEL_SOURCES = {
-    "dense": os.path.join(ROOT, "sparse_attention_indexer_token_amd", "csrc", "grad_dense.hip"),
-    "scatter": os.path.join(ROOT, "sparse_attention_indexer_token_amd", "csrc", "grad_fused.hip"),
+    kern: [os.path.join(CSRC, f) for f in (src, "device_common.h", "slikl_internal.h")]
+    for kern, src in (("grad_dense8_kernel", "grad_dense8.hip"), ("grad_dense_kernel", "grad_dense.hip"),
+                      ("grad_fused_kernel", "grad_fused.hip"))
 }
+
+
+def traffic_file(kernel, workload):
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+
+
+def fused_kernel(strategy, group):
+    """The fused kernel a call runs: the scatter strategy's, or the dense strategy's
+    eight-wave kernel for head groups padded to at most 64 heads, four-wave above."""
+    if strategy != "dense":
+        return "grad_fused_kernel"
+    return "grad_dense8_kernel" if group <= 64 else "grad_dense_kernel"
+
+
+def sources_sha256(kernel):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def parse():
@@ -152,10 +173,9 @@ def main():
         phases.append(ms)
     phase_ms = {name: float(np.mean([ph[name] for ph in phases])) for name in phases[0]}
     strategy = "dense" if phase_ms.get("dk", 0.0) > 0.0 else "scatter"
-    kernel = "grad_dense_kernel" if strategy == "dense" else "grad_fused_kernel"
-
     T1 = x.t1
     G = wl.n1 // wl.n2
+    kernel = fused_kernel(strategy, G)
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = T1 * args.steps / elapsed
     flop_nominal = 6.0 * wl.n1 * wl.d * wl.topk * T1
@@ -185,7 +205,7 @@ def main():
         "tflops_valid_step": flop_valid / (ms_per_step * 1e-3) / 1e12,
         "frac_peak_nominal_step": flop_nominal / (ms_per_step * 1e-3) / 1e12 / peak,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": traffic_bytes(kernel, wl.name, strategy),
+                     "frac": achieved / peak, "traffic": traffic_bytes(kernel, wl.name),
                      "kernel": kernel, "kernel_ms": kernel_ms, "flop_per_launch": flop_kernel},
         "phases_ms": phase_ms,
     }
@@ -195,20 +215,18 @@ def main():
     return 0
 
 
-def traffic_bytes(kernel, workload, strategy):
+def traffic_bytes(kernel, workload):
     """HBM bytes per launch from the committed counter summary, if it was taken
-    on this workload and on the current kernel source; else None."""
+    on this workload and on the current kernel sources; else None."""
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(traffic_file(kernel, workload)).read()
     except OSError:
         return None
     fields = dict(line.split(":", 1) for line in text.splitlines() if ":" in line and not line.startswith("#"))
     fields = {k_.strip(): v.strip() for k_, v in fields.items()}
     if fields.get("kernel") != kernel or fields.get("workload") != workload:
         return None
-    src = KERNEL_SOURCES[strategy]
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if fields.get("source_sha256") != sha:
+    if fields.get("sources_sha256") != sources_sha256(kernel):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
