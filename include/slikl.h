@@ -71,8 +71,9 @@ enum { SLIKL_SPLIT_WEIGHTED = 0, SLIKL_SPLIT_ROWS = 1 };
  * atomics (fp32, or int64 fixed point when deterministic).  DENSE (BSND only)
  * writes per (query row, key) records and runs a key-major kernel that sums
  * over query rows in registers: no atomics, bitwise reproducible; it pays off
- * when the top-k lists cover a large share of each batch's keys.  AUTO picks
- * DENSE for BSND when 2 * topk >= S2 and the records fit in 8 GiB. */
+ * when the top-k lists cover a fair share of each batch's keys.  AUTO picks
+ * DENSE for BSND when S2 <= 16 topk (S2 <= 32 topk when deterministic) and the
+ * records fit in 8 GiB, SCATTER otherwise. */
 enum { SLIKL_DK_AUTO = 0, SLIKL_DK_SCATTER = 1, SLIKL_DK_DENSE = 2 };
 
 /* Metadata array (int32, SLIKL_METADATA_INTS entries).  A "unit" is one

@@ -70,7 +70,12 @@ slikl_status validate(const slikl_desc *d) {
 int dk_strategy(const slikl_desc *d) {
     const bool fits = dense_fits(d);
     if (d->dk_mode == SLIKL_DK_DENSE && fits) return 2;
-    if (d->dk_mode == SLIKL_DK_AUTO && fits && 2 * d->topk >= d->s2) {
+    // AUTO: the dense kernels cost about one (row, 128-key block) step per 128 keys of
+    // a row's named range (at most S2), the scatter about one atomic row per valid
+    // slot, dearer in fixed point (deterministic) and under contention on shared keys:
+    // dense when S2 <= 16 topk, or S2 <= 32 topk when deterministic
+    const int64_t ratio = d->deterministic ? 32 : 16;
+    if (d->dk_mode == SLIKL_DK_AUTO && fits && d->s2 <= ratio * d->topk) {
         // the dense records are sized [units, S2]; keep them modest
         const double bytes = (double)d->batch * d->s1 * d->n2 * d->s2 * 4.0 * (1 + head_tile(d->n1 / d->n2) / 32);
         if (bytes <= 8.0 * (1ull << 30)) return 2;
@@ -83,9 +88,6 @@ int unit_overhead(const slikl_desc *d) {
     return dk_strategy(d) == 2 ? SLIKL_UNIT_OVERHEAD_DENSE : SLIKL_UNIT_OVERHEAD;
 }
 
-// Query-row ranges of the key-major dK kernel: about 1024 workgroups in all,
-// ranges of at least 16 rows where possible, and a multiple of 8 ranges (the
-// kernel deals whole ranges to the 8 XCDs).
 // Dense dK task geometry: key blocks per (batch, key head), row chunk length and
 // count (at most 256 chunks per batch), and the most tasks the table can hold.
 void dense_dk_geometry(const slikl_desc *d, int *nkb, int *chunk, int *nch, int *max_tasks) {

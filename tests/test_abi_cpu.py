@@ -133,11 +133,14 @@ def test_unit_overhead_follows_the_dk_strategy(lib):
         out = ctypes.c_int32(-1)
         st = lib.slikl_grad_unit_overhead(ctypes.byref(d), ctypes.byref(out))
         return st, out.value
-    # dsv32 shape: 2 topk >= S2 picks the dense strategy in auto mode
-    assert oh(good_desc()) == (0, _native.UNIT_OVERHEAD_DENSE)
+    # auto mode: dense when S2 <= 16 topk (32 topk when deterministic), BSND, records fit
+    assert oh(good_desc()) == (0, _native.UNIT_OVERHEAD_DENSE)             # dsv32 shape
     assert oh(good_desc(dk_mode=2)) == (0, _native.UNIT_OVERHEAD_DENSE)
     assert oh(good_desc(dk_mode=1)) == (0, _native.UNIT_OVERHEAD)
-    assert oh(good_desc(topk=512)) == (0, _native.UNIT_OVERHEAD)          # sparse lists: scatter
+    assert oh(good_desc(topk=256)) == (0, _native.UNIT_OVERHEAD_DENSE)     # S2 = 16 topk
+    assert oh(good_desc(topk=128)) == (0, _native.UNIT_OVERHEAD)           # sparser lists: scatter
+    assert oh(good_desc(topk=128, deterministic=1)) == (0, _native.UNIT_OVERHEAD_DENSE)
+    assert oh(good_desc(topk=64, deterministic=1)) == (0, _native.UNIT_OVERHEAD)
     cu = (ctypes.c_int32 * 2)(0, 4096)
     d = good_desc(layout_q=1, layout_k=1)                                  # TND: scatter only
     d.cu_seqlens_q = ctypes.cast(cu, ctypes.c_void_p)
