@@ -331,12 +331,122 @@ __global__ __launch_bounds__(1024) void dense_dk_tasks_kernel(Problem pb) {
     const int nbg = pb.batch * pb.n2, nkb = pb.dk_nkb, nch = pb.dk_nch, chunk = pb.dk_chunk;
     const int NT = nbg * nkb;
     const int S1 = (int)pb.s1;
-    __shared__ int s_cnt[kTaskKT * kTaskNchMax];     // [k within the tile][chunk]
+    // [k within the tile][chunk]; the one-block path uses rows of kTaskNchMax + 1
+    // (a lane per key block writes without bank conflicts)
+    __shared__ int s_cnt[kTaskKT * (kTaskNchMax + 1)];
     __shared__ int s_run[kTaskNchMax];
     __shared__ long long s_tot[16];
     __shared__ int s_ne[16];
     __shared__ int s_scan[1024];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    // rows of the n tasks of key block t (batch b, first task `first`, c active rows),
+    // count(ch) = active rows of chunk ch; lane l takes chunks 4 l .. 4 l + 3.  Task s
+    // starts at the chunk holding active row floor(s c / n): the chunk with cumulative
+    // counts (lo, hi] starts tasks ceil(lo n / c) .. ceil(hi n / c) - 1, and the task
+    // before each of them ends there.
+    auto task_rows = [&](int t, int b, int first, int n, int c, auto count) {
+        int cum[4];
+        int run = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ch = 4 * lane + i;
+            run += ch < nch ? count(ch) : 0;
+            cum[i] = run;                   // inclusive within the lane
+        }
+        int excl = run;                     // exclusive prefix of the lane totals
+        for (int o = 1; o < 64; o <<= 1) {
+            const int v = __shfl_up(excl, o);
+            if (lane >= o) excl += v;
+        }
+        excl -= run;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ch = 4 * lane + i;
+            if (ch >= nch) break;
+            const long long lo = excl + (i == 0 ? 0 : cum[i - 1]), hi = excl + cum[i];
+            if (hi == lo) continue;
+            const int s0 = (int)((lo * n + c - 1) / c);
+            int s1 = (int)((hi * n + c - 1) / c);
+            s1 = s1 < n ? s1 : n;
+            const int row = b * S1 + ch * chunk;
+            for (int st = s0; st < s1; ++st) {
+                int32_t *tk = pb.dk_tasks + 4 * (first + st);
+                tk[0] = t;
+                tk[1] = row;
+                tk[3] = 0;
+                if (st > 0) tk[-2] = row;           // end of task st - 1
+            }
+        }
+        if (lane == 0) pb.dk_tasks[4 * (first + n - 1) + 2] = b * S1 + S1;
+    };
+
+    if (nbg == 1 && nkb <= kTaskKT) {
+        // One (batch, key head) with at most KT key blocks: wave w takes chunks w, w + 16,
+        // ... with lane = key block, loads them in one batch, runs the prefix over key
+        // blocks as a wave scan and keeps the counts in LDS as [key block][chunk].
+        constexpr int CPV = kTaskNchMax / 16;
+        const bool kok = lane < nkb;
+        int v[CPV];
+#pragma unroll
+        for (int i = 0; i < CPV; ++i) {
+            const int ch = wave + 16 * i;
+            v[i] = ch < nch && kok ? pb.kb_diff[(size_t)ch * (nkb + 1) + lane] : 0;
+        }
+        int colsum = 0;
+#pragma unroll
+        for (int i = 0; i < CPV; ++i) {
+            int x = v[i];
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(x, o);
+                if (lane >= o) x += y;
+            }
+            const int ch = wave + 16 * i;
+            if (ch < nch && kok) {
+                s_cnt[lane * (kTaskNchMax + 1) + ch] = x;
+                colsum += x;
+            }
+        }
+        s_scan[wave * 64 + lane] = colsum;
+        __syncthreads();
+        if (wave == 0) {
+            int c = 0;
+            for (int w2 = 0; w2 < 16; ++w2) c += s_scan[w2 * 64 + lane];
+            const int K = __popcll(__ballot(c > 0));
+            long long C = c;
+            for (int o = 32; o > 0; o >>= 1) {
+                const int lo32 = __shfl_xor((int)(C & 0xffffffffll), o);
+                const int hi32 = __shfl_xor((int)(C >> 32), o);
+                C += ((long long)hi32 << 32) | (unsigned)lo32;
+            }
+            const int S = pb.dk_slots;
+            const int n = c == 0 ? 0 : (K < S ? 1 + (int)((long long)c * (S - K) / C) : 1);
+            int first = n;                  // exclusive prefix of the task counts
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(first, o);
+                if (lane >= o) first += y;
+            }
+            const int total = __shfl(first, 63);
+            first -= n;
+            if (kok) {
+                pb.kb_tasks[4 * lane] = first;
+                pb.kb_tasks[4 * lane + 1] = n;
+                pb.kb_tasks[4 * lane + 2] = c;
+            }
+            s_run[lane] = first;
+            s_run[64 + lane] = n;
+            s_run[128 + lane] = c;
+            if (lane == 0) pb.dk_ntasks[0] = total;
+        }
+        __syncthreads();
+        for (int t = wave; t < nkb; t += 16) {
+            const int n = s_run[64 + t];
+            if (n == 0) continue;
+            task_rows(t, 0, s_run[t], n, s_run[128 + t],
+                      [&](int ch) { return s_cnt[t * (kTaskNchMax + 1) + ch]; });
+        }
+        return;
+    }
+
     long long tot = 0;
     int ne = 0;
     // pass 1: active rows per (key block, chunk), written over the difference arrays,
@@ -426,49 +536,13 @@ __global__ __launch_bounds__(1024) void dense_dk_tasks_kernel(Problem pb) {
     }
     if (tid == 0) pb.dk_ntasks[0] = base;
     __syncthreads();
-    // pass 3: task rows; a wave per key block, lane l holding chunks 4 l .. 4 l + 3
+    // pass 3: task rows; a wave per key block
     for (int t = wave; t < NT; t += 16) {
         const int n = pb.kb_tasks[4 * t + 1];
         if (n == 0) continue;
-        const int first = pb.kb_tasks[4 * t], c = pb.kb_tasks[4 * t + 2];
         const int bg = t / nkb, k = t - bg * nkb;
-        const int b = bg / pb.n2;
-        int cum[4];
-        int run = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ch = 4 * lane + i;
-            run += ch < nch ? pb.kb_diff[((size_t)bg * nch + ch) * (nkb + 1) + k] : 0;
-            cum[i] = run;                   // inclusive within the lane
-        }
-        int excl = run;                     // exclusive prefix of the lane totals
-        for (int o = 1; o < 64; o <<= 1) {
-            const int v = __shfl_up(excl, o);
-            if (lane >= o) excl += v;
-        }
-        excl -= run;
-        // task s starts at the chunk holding active row floor(s c / n): the chunk with
-        // cumulative counts (lo, hi] starts tasks ceil(lo n / c) .. ceil(hi n / c) - 1,
-        // and the task before each of them ends there
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ch = 4 * lane + i;
-            if (ch >= nch) break;
-            const long long lo = excl + (i == 0 ? 0 : cum[i - 1]), hi = excl + cum[i];
-            if (hi == lo) continue;
-            const int s0 = (int)((lo * n + c - 1) / c);
-            int s1 = (int)((hi * n + c - 1) / c);
-            s1 = s1 < n ? s1 : n;
-            const int row = b * S1 + ch * chunk;
-            for (int st = s0; st < s1; ++st) {
-                int32_t *tk = pb.dk_tasks + 4 * (first + st);
-                tk[0] = t;
-                tk[1] = row;
-                tk[3] = 0;
-                if (st > 0) tk[-2] = row;           // end of task st - 1
-            }
-        }
-        if (lane == 0) pb.dk_tasks[4 * (first + n - 1) + 2] = b * S1 + S1;
+        task_rows(t, bg / pb.n2, pb.kb_tasks[4 * t], n, pb.kb_tasks[4 * t + 2],
+                  [&](int ch) { return pb.kb_diff[((size_t)bg * nch + ch) * (nkb + 1) + k]; });
     }
 }
 
