@@ -144,8 +144,11 @@ def main():
     p = torch.from_numpy(x.p).to(dev)
     cu_q = None if x.cu_q is None else torch.from_numpy(x.cu_q).to(dev)
     cu_k = None if x.cu_k is None else torch.from_numpy(x.cu_k).to(dev)
+    # TND sides: the longest sequence is known on the host (it sizes the dense dK records)
+    mx = lambda cu: int(np.diff(cu).max()) if cu is not None and len(cu) > 1 else 0
     kw = dict(layout_q=x.layout_q, layout_k=x.layout_k, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
-              deterministic=det)
+              deterministic=det, max_seqlen_q=mx(x.cu_q) if x.layout_q == "TND" else 0,
+              max_seqlen_k=mx(x.cu_k) if x.layout_k == "TND" else 0)
     desc = slikl.make_desc(q, k, idx, **kw)
     ws = torch.empty(slikl.slikl_grad_workspace_size(desc), dtype=torch.uint8, device=dev)
     md = torch.empty(slikl.METADATA_INTS, dtype=torch.int32, device=dev)

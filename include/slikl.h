@@ -68,12 +68,13 @@ enum { SLIKL_DTYPE_F16 = 0, SLIKL_DTYPE_BF16 = 1 };
  * ROWS is the even row split of the metadata pre-pass prior art. */
 enum { SLIKL_SPLIT_WEIGHTED = 0, SLIKL_SPLIT_ROWS = 1 };
 /* dK strategies.  SCATTER adds each slot's dK part into the key rows with
- * atomics (fp32, or int64 fixed point when deterministic).  DENSE (BSND only)
- * writes per (query row, key) records and runs a key-major kernel that sums
- * over query rows in registers: no atomics, bitwise reproducible; it pays off
- * when the top-k lists cover a fair share of each batch's keys.  AUTO picks
- * DENSE for BSND when S2 <= 16 topk (S2 <= 32 topk when deterministic) and the
- * records fit in 8 GiB, SCATTER otherwise. */
+ * atomics (fp32, or int64 fixed point when deterministic).  DENSE (BSND, or TND
+ * with the maxima max_seqlen_q / max_seqlen_k given) writes per (query row, key)
+ * records and runs a key-major kernel that sums over query rows in registers: no
+ * atomics, bitwise reproducible; it pays off when the top-k lists cover a fair
+ * share of each batch's keys.  With L the key length per batch (S2, or
+ * max_seqlen_k for TND), AUTO picks DENSE when L <= 16 topk (L <= 32 topk when
+ * deterministic) and the records fit in 8 GiB, SCATTER otherwise. */
 enum { SLIKL_DK_AUTO = 0, SLIKL_DK_SCATTER = 1, SLIKL_DK_DENSE = 2 };
 
 /* Metadata array (int32, SLIKL_METADATA_INTS entries).  A "unit" is one
@@ -84,7 +85,8 @@ enum { SLIKL_DK_AUTO = 0, SLIKL_DK_SCATTER = 1, SLIKL_DK_DENSE = 2 };
  *   [9] per-unit overhead    [10..15] 0
  *   [16 + i], i = 0..P: first unit of part i (part i = [b_i, b_{i+1})).
  * Error word bits: 1 = bad cuSeqLensQ, 2 = bad cuSeqLensK, 4 = an index out
- * of its batch's key range (WEIGHTED mode only; ROWS reads no indices). */
+ * of its batch's key range (WEIGHTED mode only; ROWS reads no indices), 8 = a TND
+ * sequence longer than the max_seqlen_q / max_seqlen_k given for its side. */
 #define SLIKL_METADATA_HEADER 16
 #define SLIKL_MAX_PARTS 2048
 #define SLIKL_METADATA_INTS 2080
@@ -113,7 +115,15 @@ typedef struct slikl_desc {
     const int32_t *cu_seqlens_k; /* device, B+1 entries starting at 0; required iff TND k */
     int32_t num_parts;       /* metadata parts; 0 = library default (CUs x blocks/CU)  */
     int32_t split_mode;      /* SLIKL_SPLIT_*                                         */
-    int32_t dk_mode;         /* SLIKL_DK_*; DENSE with a TND side -> UNSUPPORTED      */
+    int32_t dk_mode;         /* SLIKL_DK_*; DENSE with a TND side needs its maximum   */
+    /* TND sides only (ignored for BSND): the longest sequence of the side, 0 = not
+     * given.  The DENSE dK strategy sizes its per-(query row, key) records by them, so
+     * with a TND side it needs both given (else DENSE -> UNSUPPORTED, AUTO -> SCATTER).
+     * A sequence longer than its given maximum violates the contract: in the DENSE
+     * strategy its keys past the maximum are treated as -1 slots and its rows past the
+     * maximum add nothing to dk, and the metadata pre-pass sets error bit 8. */
+    int64_t max_seqlen_q;
+    int64_t max_seqlen_k;
 } slikl_desc;
 
 /* First phase (the page's "GetWorkspaceSize" step): validate `desc` and return

@@ -43,8 +43,11 @@ def _dtype_code(t) -> int:
 def make_desc(q, k, sparse_indices, *, layout_q: str = "BSND", layout_k: str = "BSND",
               cu_seqlens_q=None, cu_seqlens_k=None, deterministic: bool = False,
               num_parts: int = 0, split_mode: str = "weighted",
-              dk_mode: str = "auto") -> SliklDesc:
-    """Build the C descriptor from tensor shapes (no device access)."""
+              dk_mode: str = "auto", max_seqlen_q: int = 0, max_seqlen_k: int = 0) -> SliklDesc:
+    """Build the C descriptor from tensor shapes (no device access).
+
+    For a TND side, ``max_seqlen_q`` / ``max_seqlen_k`` may give its longest sequence
+    (0 = not given); the dense dK strategy needs them for TND inputs."""
     if layout_q not in LAYOUT or layout_k not in LAYOUT:
         raise ValueError("layouts must be 'BSND' or 'TND'")
     if layout_q == "BSND":
@@ -86,6 +89,8 @@ def make_desc(q, k, sparse_indices, *, layout_q: str = "BSND", layout_k: str = "
     desc.num_parts = int(num_parts)
     desc.split_mode = _native.SPLIT[split_mode]
     desc.dk_mode = _native.DK_MODE[dk_mode]
+    desc.max_seqlen_q = int(max_seqlen_q) if layout_q == "TND" else 0
+    desc.max_seqlen_k = int(max_seqlen_k) if layout_k == "TND" else 0
     return desc
 
 
@@ -125,13 +130,13 @@ def slikl_grad_unit_overhead(desc: SliklDesc) -> int:
 def slikl_grad_metadata(q, k, sparse_indices, *, layout_q="BSND", layout_k="BSND",
                         cu_seqlens_q=None, cu_seqlens_k=None, deterministic=False,
                         num_parts: int = 0, split_mode: str = "weighted", dk_mode: str = "auto",
-                        metadata=None, workspace=None):
+                        max_seqlen_q: int = 0, max_seqlen_k: int = 0, metadata=None, workspace=None):
     """Run the load-balancing metadata pre-pass; returns the int32 metadata tensor."""
     torch = _torch()
     desc = make_desc(q, k, sparse_indices, layout_q=layout_q, layout_k=layout_k,
                      cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
                      deterministic=deterministic, num_parts=num_parts, split_mode=split_mode,
-                     dk_mode=dk_mode)
+                     dk_mode=dk_mode, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k)
     dev = q.device
     _check_tensor("sparse_indices", sparse_indices, torch.int32, dev)
     nbytes = _native.workspace_size(desc)
@@ -149,7 +154,8 @@ def slikl_grad_metadata(q, k, sparse_indices, *, layout_q="BSND", layout_k="BSND
 def slikl_grad(q, k, w, sparse_indices, attn_softmax_l1norm, *, layout_q="BSND", layout_k="BSND",
                cu_seqlens_q=None, cu_seqlens_k=None, deterministic: bool = False,
                metadata=None, num_parts: int = 0, split_mode: str = "weighted",
-               dk_mode: str = "auto", workspace=None, out: Optional[tuple] = None):
+               dk_mode: str = "auto", max_seqlen_q: int = 0, max_seqlen_k: int = 0,
+               workspace=None, out: Optional[tuple] = None):
     """Backward pass; returns (dq, dk, dw, softmax_out).
 
     ``out`` may hold preallocated (dq, dk, dw, softmax_out); ``workspace`` a
@@ -158,6 +164,7 @@ def slikl_grad(q, k, w, sparse_indices, attn_softmax_l1norm, *, layout_q="BSND",
     return _grad(q, k, w, sparse_indices, attn_softmax_l1norm, layout_q=layout_q, layout_k=layout_k,
                  cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, deterministic=deterministic,
                  metadata=metadata, num_parts=num_parts, split_mode=split_mode, dk_mode=dk_mode,
+                 max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
                  workspace=workspace, out=out, profiled=False)[0]
 
 
@@ -170,12 +177,13 @@ def slikl_grad_profiled(q, k, w, sparse_indices, attn_softmax_l1norm, **kw):
 def _grad(q, k, w, sparse_indices, attn_softmax_l1norm, *, layout_q="BSND", layout_k="BSND",
           cu_seqlens_q=None, cu_seqlens_k=None, deterministic: bool = False,
           metadata=None, num_parts: int = 0, split_mode: str = "weighted",
-          dk_mode: str = "auto", workspace=None, out: Optional[tuple] = None, profiled: bool = False):
+          dk_mode: str = "auto", max_seqlen_q: int = 0, max_seqlen_k: int = 0,
+          workspace=None, out: Optional[tuple] = None, profiled: bool = False):
     torch = _torch()
     desc = make_desc(q, k, sparse_indices, layout_q=layout_q, layout_k=layout_k,
                      cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
                      deterministic=deterministic, num_parts=num_parts, split_mode=split_mode,
-                     dk_mode=dk_mode)
+                     dk_mode=dk_mode, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k)
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("tensors must be on the GPU")

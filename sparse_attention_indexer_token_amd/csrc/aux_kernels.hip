@@ -39,6 +39,42 @@ __global__ void zero_ranges_kernel(ZeroRanges zr) {
     }
 }
 
+// Dense strategy with a TND side: per query row r its batch b, the key base and key
+// length of b (at most the dense maps' key length) and r's index within b.  Broken
+// cuSeqLens (flagged by the metadata pre-pass) still give in-range batches, and the
+// key length is clamped to [0, s2max], so no record access leaves its row.
+__global__ void rowinfo_kernel(Problem pb, i32x4 *info) {
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < pb.t1; r += stride) {
+        int b, rb;
+        if (pb.layout_q == 0) {
+            b = (int)(r / pb.s1);
+            rb = (int)(r - (int64_t)b * pb.s1);
+        } else {
+            b = batch_of_row(pb.cu_q, pb.batch, r);
+            rb = (int)(r - pb.cu_q[b]);
+        }
+        int kbase, klen;
+        if (pb.layout_k == 0) {
+            kbase = (int)((int64_t)b * pb.s2);
+            klen = (int)pb.s2;
+        } else {
+            kbase = pb.cu_k[b];
+            klen = pb.cu_k[b + 1] - kbase;
+        }
+        klen = klen < 0 ? 0 : (klen > (int)pb.s2max ? (int)pb.s2max : klen);
+        info[r] = i32x4{b, kbase, klen, rb};
+    }
+}
+
+hipError_t launch_rowinfo(const Problem &pb, i32x4 *info, hipStream_t stream) {
+    if (pb.t1 <= 0) return hipSuccess;
+    int64_t blocks = (pb.t1 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(rowinfo_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pb, info);
+    return hipGetLastError();
+}
+
 hipError_t launch_zero_ranges(const ZeroRanges &zr, hipStream_t stream) {
     size_t most = 0;
     for (int r = 0; r < zr.n; ++r) most = zr.bytes[r] / 16 > most ? zr.bytes[r] / 16 : most;
@@ -296,13 +332,19 @@ __global__ void meta_count_kernel(Problem pb, int64_t *prefix, int overhead, int
     if (__any(bad) && lane == 0) atomicOr(flags, 4);
 }
 
-__device__ __forceinline__ int check_cu(const int32_t *cu, int batch, int64_t total) {
-    // returns 1 if cu does not start at 0, decreases, or misses the total
-    int bad = 0;
-    for (int b = threadIdx.x; b < batch; b += blockDim.x)
-        if (cu[b + 1] < cu[b]) bad = 1;
+__device__ __forceinline__ int check_cu(const int32_t *cu, int batch, int64_t total, int64_t maxlen) {
+    // bit 0: cu does not start at 0, decreases, or misses the total; bit 1: a
+    // sequence is longer than maxlen (when maxlen > 0)
+    int bad = 0, lng = 0;
+    for (int b = threadIdx.x; b < batch; b += blockDim.x) {
+        const int64_t len = (int64_t)cu[b + 1] - cu[b];
+        if (len < 0) bad = 1;
+        if (maxlen > 0 && len > maxlen) lng = 1;
+    }
     if (threadIdx.x == 0 && (cu[0] != 0 || (int64_t)cu[batch] != total)) bad = 1;
-    return __syncthreads_or(bad);
+    bad = __syncthreads_or(bad);
+    lng = __syncthreads_or(lng);
+    return (bad ? 1 : 0) | (lng ? 2 : 0);
 }
 
 __global__ __launch_bounds__(1024) void meta_split_kernel(Problem pb, int parts, int mode, int overhead,
@@ -316,8 +358,14 @@ __global__ __launch_bounds__(1024) void meta_split_kernel(Problem pb, int parts,
     const int64_t U = pb.t1 * pb.n2;
 
     int flags = 0;
-    if (pb.layout_q == 1 && check_cu(pb.cu_q, pb.batch, pb.t1)) flags |= 1;
-    if (pb.layout_k == 1 && check_cu(pb.cu_k, pb.batch, pb.t2)) flags |= 2;
+    if (pb.layout_q == 1) {
+        const int c = check_cu(pb.cu_q, pb.batch, pb.t1, pb.max_q);
+        flags |= (c & 1 ? 1 : 0) | (c & 2 ? 8 : 0);
+    }
+    if (pb.layout_k == 1) {
+        const int c = check_cu(pb.cu_k, pb.batch, pb.t2, pb.max_k);
+        flags |= (c & 1 ? 2 : 0) | (c & 2 ? 8 : 0);
+    }
 
     // max key length over batches
     int64_t mk = 0;

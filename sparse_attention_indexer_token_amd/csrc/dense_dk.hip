@@ -98,6 +98,20 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dk_view(const void *base, uint
     return __builtin_amdgcn_make_buffer_rsrc((void *)base, (short)0, (int)bytes, 0x00020000);
 }
 
+// Key length of batch b in the dense records: S2, or (TND) its sequence clamped to the
+// records' key length.
+__device__ __forceinline__ int dense_klen(const Problem &pb, int b) {
+    if (pb.layout_k == 0) return (int)pb.s2;
+    const int l = pb.cu_k[b + 1] - pb.cu_k[b];
+    return l < 0 ? 0 : (l > (int)pb.s2max ? (int)pb.s2max : l);
+}
+
+// First query row of batch b and the row past its end.
+__device__ __forceinline__ int2 dense_rows(const Problem &pb, int b) {
+    if (pb.layout_q == 0) return int2{(int)(b * pb.s1), (int)(b * pb.s1 + pb.s1)};
+    return int2{pb.cu_q[b], pb.cu_q[b + 1]};
+}
+
 template <int HP, int D, bool F16>
 __device__ __forceinline__ void dense_dk_body(const Problem &pb) {
     using C = DenseCfg<HP, D>;
@@ -115,7 +129,6 @@ __device__ __forceinline__ void dense_dk_body(const Problem &pb) {
     const int lane = tid & 63;
     const int l32 = lane & 31, half = lane >> 5, l16 = lane & 15, grp = lane >> 4;
 
-    const int S2 = (int)pb.s2;
     const int G = pb.group;
     const int kw = 32 * wave + l32;            // this lane's key within the block (B column)
     const uint16_t *qsrc = F16 ? pb.q : pb.q16;
@@ -134,9 +147,10 @@ __device__ __forceinline__ void dense_dk_body(const Problem &pb) {
     const int r0 = pb.dk_tasks[4 * task + 1], r1 = pb.dk_tasks[4 * task + 2];
     const int kb = kbt % pb.dk_nkb;
     const int g = (kbt / pb.dk_nkb) % pb.n2;
+    const int S2 = dense_klen(pb, kbt / pb.dk_nkb / pb.n2);     // this batch's keys
     const int j0 = kb * KB;
     const int j1 = j0 + KB < S2 ? j0 + KB : S2;
-    const int nk = j1 - j0;                    // keys of this block
+    const int nk = j1 > j0 ? j1 - j0 : 0;      // keys of this block
     const bool jok = kw < nk;
 
     // ---- active rows: those of [r0, r1) whose unit names a key of [j0, j1), in
@@ -330,7 +344,6 @@ constexpr int kTaskNchMax = 256;
 __global__ __launch_bounds__(1024) void dense_dk_tasks_kernel(Problem pb) {
     const int nbg = pb.batch * pb.n2, nkb = pb.dk_nkb, nch = pb.dk_nch, chunk = pb.dk_chunk;
     const int NT = nbg * nkb;
-    const int S1 = (int)pb.s1;
     // [k within the tile][chunk]; the one-block path uses rows of kTaskNchMax + 1
     // (a lane per key block writes without bank conflicts)
     __shared__ int s_cnt[kTaskKT * (kTaskNchMax + 1)];
@@ -345,6 +358,7 @@ __global__ __launch_bounds__(1024) void dense_dk_tasks_kernel(Problem pb) {
     // counts (lo, hi] starts tasks ceil(lo n / c) .. ceil(hi n / c) - 1, and the task
     // before each of them ends there.
     auto task_rows = [&](int t, int b, int first, int n, int c, auto count) {
+        const int2 rows = dense_rows(pb, b);
         int cum[4];
         int run = 0;
 #pragma unroll
@@ -368,7 +382,7 @@ __global__ __launch_bounds__(1024) void dense_dk_tasks_kernel(Problem pb) {
             const int s0 = (int)((lo * n + c - 1) / c);
             int s1 = (int)((hi * n + c - 1) / c);
             s1 = s1 < n ? s1 : n;
-            const int row = b * S1 + ch * chunk;
+            const int row = rows.x + ch * chunk;
             for (int st = s0; st < s1; ++st) {
                 int32_t *tk = pb.dk_tasks + 4 * (first + st);
                 tk[0] = t;
@@ -377,7 +391,7 @@ __global__ __launch_bounds__(1024) void dense_dk_tasks_kernel(Problem pb) {
                 if (st > 0) tk[-2] = row;           // end of task st - 1
             }
         }
-        if (lane == 0) pb.dk_tasks[4 * (first + n - 1) + 2] = b * S1 + S1;
+        if (lane == 0) pb.dk_tasks[4 * (first + n - 1) + 2] = rows.y;
     };
 
     if (nbg == 1 && nkb <= kTaskKT) {
@@ -554,9 +568,20 @@ __global__ void dense_dk_reduce_kernel(Problem pb) {
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     for (; i < n; i += stride) {
-        const size_t kr = i / ((size_t)pb.n2 * D);        // key row (b S2 + j)
+        const size_t kr = i / ((size_t)pb.n2 * D);        // key row (key base of b + j)
         const int g = (int)((i / D) % pb.n2), d = (int)(i % D);
-        const int b = (int)(kr / pb.s2), j = (int)(kr % pb.s2);
+        int b, j;
+        if (pb.layout_k == 0) {
+            b = (int)(kr / pb.s2);
+            j = (int)(kr % pb.s2);
+        } else {
+            b = batch_of_row(pb.cu_k, pb.batch, (int64_t)kr);
+            j = (int)(kr - pb.cu_k[b]);
+            if (j < 0 || j >= (int)pb.s2max) {          // past the given maximum: no records
+                pb.dk[i] = 0;
+                continue;
+            }
+        }
         const int kbt = (b * pb.n2 + g) * pb.dk_nkb + j / KB;
         const int t0 = pb.kb_tasks[4 * kbt], nt = pb.kb_tasks[4 * kbt + 1];
         float s = 0.f;

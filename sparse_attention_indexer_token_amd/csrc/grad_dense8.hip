@@ -137,6 +137,7 @@ __device__ __forceinline__ void wait_for_step(int ahead) {
 // unit's epilogue; q itself is loaded at the start of its unit, where its
 // latency overlaps the compaction, so that it is not live beside U).
 struct UnitInputs {
+    i32x4 ri;                        // row info (TND: batch, key base, key length, row in batch)
     float wt;                        // w of head `tid` (tid < G)
     int iv[TOPK_PER_THREAD];         // this thread's run of slots: key index, p
     float pv[TOPK_PER_THREAD];
@@ -206,6 +207,9 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
         const int t = opaque(tid);
         const float wv = pb.w[rr * pb.n1 + gg * G + (t < G ? t : 0)];
         in.wt = t < G ? wv : 0.f;
+        // row info from the table when one exists, else a read of the zero row (one
+        // unconditional 16-byte load either way)
+        in.ri = *(pb.rowinfo ? pb.rowinfo + rr : (const i32x4 *)pb.zero16);
         const int spt = (topk + kBlock8 - 1) / kBlock8;
         const int s0 = t * spt;
         const int32_t *ir = pb.idx + uu * topk;
@@ -227,8 +231,20 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
         const int u = cu;
         const int r = u / pb.n2;
         const int g = u - r * pb.n2;
-        const int b = r / S1;
-        const int kbase = b * S2;
+        // batch, key base, key length (at most the records' key length) and the
+        // row's index within its batch
+        int b, kbase, klen, rb;
+        if (pb.rowinfo) {
+            b = __builtin_amdgcn_readfirstlane(in.ri.x);
+            kbase = __builtin_amdgcn_readfirstlane(in.ri.y);
+            klen = __builtin_amdgcn_readfirstlane(in.ri.z);
+            rb = __builtin_amdgcn_readfirstlane(in.ri.w);
+        } else {
+            b = r / S1;
+            kbase = b * S2;
+            klen = S2;
+            rb = r - b * S1;
+        }
         float *yrow = pb.y + u * topk;
         const uint16_t *qrow = pb.q + (r * pb.n1 + g * G) * D;
         const int spt = (topk + kBlock8 - 1) / kBlock8;
@@ -267,7 +283,7 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
         for (int i = 0; i < SPT_MAX; ++i) {
             const int v = in.iv[i];
             const bool inr = i < spt && s0 + i < topk;
-            const bool ok = v >= 0 && v < S2;
+            const bool ok = v >= 0 && v < klen;
             cnt += ok ? 1 : 0;
             zslots |= (inr && !ok) ? (1u << i) : 0u;
             if (ok) {
@@ -292,7 +308,7 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
 #pragma unroll
         for (int i = 0; i < SPT_MAX; ++i) {
             const int v = in.iv[i];
-            if (v >= 0 && v < S2) {
+            if (v >= 0 && v < klen) {
                 s_key[pos] = kbase + v;
                 s_slot[pos] = (uint16_t)(s0 + i);
                 s_p[pos] = in.pv[i];
@@ -406,10 +422,11 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
             pb.row_range[2 * u] = kmin_i;
             pb.row_range[2 * u + 1] = nvalid > 0 ? kmax_i : -1;
             *(u32x4 *)(wrec + HP * 4) = u32x4{(uint32_t)(eq + ew), (uint32_t)ed, 0u, 0u};
-            if (nvalid > 0) {
+            if (nvalid > 0 && rb >= 0 && rb < pb.dk_nch * pb.dk_chunk) {
                 // dK task sizing: +1 / -1 at the first / past the last key block that
-                // the named key range [kmin, kmax] meets, in this row's chunk
-                int32_t *dif = pb.kb_diff + ((size_t)(b * pb.n2 + g) * pb.dk_nch + (r - b * S1) / pb.dk_chunk) *
+                // the named key range [kmin, kmax] meets, in this row's chunk (rows
+                // past a TND batch's given maximum are left out of the sizing)
+                int32_t *dif = pb.kb_diff + ((size_t)(b * pb.n2 + g) * pb.dk_nch + rb / pb.dk_chunk) *
                                                 (pb.dk_nkb + 1);
                 atomicAdd(dif + kmin_i / pb.dk_kb, 1);
                 atomicAdd(dif + kmax_i / pb.dk_kb + 1, -1);
@@ -420,7 +437,7 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
         if (nvalid > 0) {
             const int z0 = (kmin_i / pb.dk_kb) * pb.dk_kb;
             const int z1e = (kmax_i / pb.dk_kb + 1) * pb.dk_kb;
-            const int z1 = z1e < S2 ? z1e : S2;
+            const int z1 = z1e < klen ? z1e : klen;
             int32_t *drow = pb.dI_map + (size_t)u * pb.s2max;
             for (int j = z0 + tid; j < z1; j += kBlock8) drow[j] = 0;
         }

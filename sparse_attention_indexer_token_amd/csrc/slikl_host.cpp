@@ -20,19 +20,23 @@ int head_tile(int64_t group) { return group <= 32 ? 32 : (group <= 64 ? 64 : 128
 
 int64_t rows_q(const slikl_desc *d) { return d->layout_q == SLIKL_LAYOUT_BSND ? d->batch * d->s1 : d->s1; }
 int64_t rows_k(const slikl_desc *d) { return d->layout_k == SLIKL_LAYOUT_BSND ? d->batch * d->s2 : d->s2; }
+// longest sequence of a side: S1 / S2 for BSND, the given maximum for TND (0 = not given)
+int64_t len_q(const slikl_desc *d) { return d->layout_q == SLIKL_LAYOUT_BSND ? d->s1 : d->max_seqlen_q; }
+int64_t len_k(const slikl_desc *d) { return d->layout_k == SLIKL_LAYOUT_BSND ? d->s2 : d->max_seqlen_k; }
+bool any_tnd(const slikl_desc *d) { return d->layout_q == SLIKL_LAYOUT_TND || d->layout_k == SLIKL_LAYOUT_TND; }
 
 // Field checks of the operator page's constraints section (dtypes, layouts,
 // cuSeqLens required for TND) and of this library's limits (N1 <= 128,
 // topk <= 2048 as for the 950-class products; D in {32, 64, 128}).
-// Whether the dense dK strategy can take this problem: BSND on both sides, keys
-// addressed with 32-bit byte offsets (< 2^31 bytes) and key rows below 2^24
-// (24-bit multiplies; exact in fp32).
+// Whether the dense dK strategy can take this problem: the longest sequence of each
+// side known (BSND, or TND with its maximum given), keys addressed with 32-bit byte
+// offsets (< 2^31 bytes) and key rows below 2^24 (24-bit multiplies; exact in fp32).
 bool dense_fits(const slikl_desc *d) {
     // the eight-wave fused kernel (head groups up to 64) addresses key rows as
     // buffer records, whose stride field holds 14 bits
     const bool rows_ok = head_tile(d->n2 > 0 ? d->n1 / d->n2 : 1) > 64 || (int64_t)d->n2 * d->d * 2 < 16384;
-    return d->layout_q == SLIKL_LAYOUT_BSND && d->layout_k == SLIKL_LAYOUT_BSND && rows_ok &&
-           (double)d->batch * d->s2 * d->n2 * d->d * 2.0 < 2147483648.0 && (double)d->batch * d->s2 < 16777216.0;
+    return len_q(d) > 0 && len_k(d) > 0 && rows_ok &&
+           (double)rows_k(d) * d->n2 * d->d * 2.0 < 2147483648.0 && (double)rows_k(d) < 16777216.0;
 }
 
 slikl_status validate(const slikl_desc *d) {
@@ -53,6 +57,10 @@ slikl_status validate(const slikl_desc *d) {
     if (d->layout_k == SLIKL_LAYOUT_TND && !d->cu_seqlens_k) return SLIKL_ERR_NULLPTR;
     if (d->layout_q == SLIKL_LAYOUT_BSND ? d->s1 <= 0 : d->s1 < 0) return SLIKL_ERR_PARAM_INVALID;
     if (d->layout_k == SLIKL_LAYOUT_BSND ? d->s2 <= 0 : d->s2 < 0) return SLIKL_ERR_PARAM_INVALID;
+    if (d->layout_q == SLIKL_LAYOUT_TND && (d->max_seqlen_q < 0 || d->max_seqlen_q > INT32_MAX))
+        return SLIKL_ERR_PARAM_INVALID;
+    if (d->layout_k == SLIKL_LAYOUT_TND && (d->max_seqlen_k < 0 || d->max_seqlen_k > INT32_MAX))
+        return SLIKL_ERR_PARAM_INVALID;
     // sizes that the kernels index with 32-bit values
     const int64_t lim = (int64_t)INT32_MAX;
     if (d->layout_q == SLIKL_LAYOUT_BSND && d->s1 > lim / d->batch) return SLIKL_ERR_PARAM_INVALID;
@@ -75,9 +83,9 @@ int dk_strategy(const slikl_desc *d) {
     // slot, dearer in fixed point (deterministic) and under contention on shared keys:
     // dense when S2 <= 16 topk, or S2 <= 32 topk when deterministic
     const int64_t ratio = d->deterministic ? 32 : 16;
-    if (d->dk_mode == SLIKL_DK_AUTO && fits && d->s2 <= ratio * d->topk) {
-        // the dense records are sized [units, S2]; keep them modest
-        const double bytes = (double)d->batch * d->s1 * d->n2 * d->s2 * 4.0 * (1 + head_tile(d->n1 / d->n2) / 32);
+    if (d->dk_mode == SLIKL_DK_AUTO && fits && len_k(d) <= ratio * d->topk) {
+        // the dense records are sized [units, longest key sequence]; keep them modest
+        const double bytes = (double)rows_q(d) * d->n2 * len_k(d) * 4.0 * (1 + head_tile(d->n1 / d->n2) / 32);
         if (bytes <= 8.0 * (1ull << 30)) return 2;
     }
     return d->deterministic ? 1 : 0;
@@ -92,10 +100,10 @@ int unit_overhead(const slikl_desc *d) {
 // count (at most 256 chunks per batch), and the most tasks the table can hold.
 void dense_dk_geometry(const slikl_desc *d, int *nkb, int *chunk, int *nch, int *max_tasks) {
     const int64_t kb = slikl::dense_dk_keys_per_block();
-    *nkb = (int)((d->s2 + kb - 1) / kb);
-    const int64_t c = (d->s1 + 255) / 256;
+    *nkb = (int)((len_k(d) + kb - 1) / kb);
+    const int64_t c = (len_q(d) + 255) / 256;
     *chunk = (int)(c < 16 ? 16 : c);
-    *nch = (int)((d->s1 + *chunk - 1) / *chunk);
+    *nch = (int)((len_q(d) + *chunk - 1) / *chunk);
     *max_tasks = slikl::kDkSlotsMax + (int)(d->batch * d->n2) * *nkb;
 }
 
@@ -125,7 +133,7 @@ slikl::WorkspacePlan plan(const slikl_desc *d) {
     p.k16_bytes = d->dtype == SLIKL_DTYPE_BF16 ? (size_t)t2 * (size_t)d->n2 * (size_t)d->d * 2 : 0;
     off = align_up(off + p.k16_bytes);
     if (mode == 2) {
-        const size_t s2 = (size_t)d->s2, nh = (size_t)head_tile(d->n1 / d->n2) / 32;
+        const size_t s2 = (size_t)len_k(d), nh = (size_t)head_tile(d->n1 / d->n2) / 32;
         dense_dk_geometry(d, &p.dk_nkb, &p.dk_chunk, &p.dk_nch, &p.dk_max_tasks);
         const size_t nbg = (size_t)d->batch * (size_t)d->n2;
         p.dimap_off = off;
@@ -150,6 +158,8 @@ slikl::WorkspacePlan plan(const slikl_desc *d) {
         off = align_up(off + nbg * (size_t)p.dk_nkb * 16);
         p.ntasks_off = off;
         off = align_up(off + 16);
+        p.rowinfo_off = off;
+        off = align_up(off + (any_tnd(d) ? (size_t)t1 * 16 : 0));
     }
     p.total = off;
     return p;
@@ -171,6 +181,8 @@ slikl::Problem problem(const slikl_desc *d) {
     pb.layout_k = d->layout_k;
     pb.cu_q = d->layout_q == SLIKL_LAYOUT_TND ? d->cu_seqlens_q : nullptr;
     pb.cu_k = d->layout_k == SLIKL_LAYOUT_TND ? d->cu_seqlens_k : nullptr;
+    pb.max_q = d->layout_q == SLIKL_LAYOUT_TND ? d->max_seqlen_q : 0;
+    pb.max_k = d->layout_k == SLIKL_LAYOUT_TND ? d->max_seqlen_k : 0;
     return pb;
 }
 
@@ -363,7 +375,8 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
             int64_t slots = (int64_t)cus * slikl::dense_dk_wgs_per_cu(head_tile(pb.group), (int)desc->d);
             pb.dk_slots = (int)(slots > slikl::kDkSlotsMax ? slikl::kDkSlotsMax : slots);
         }
-        pb.s2max = desc->s2;
+        pb.s2max = len_k(desc);
+        pb.rowinfo = any_tnd(desc) ? (const slikl::i32x4 *)(ws + wp.rowinfo_off) : nullptr;
     }
 
     hipError_t e = hipSuccess;
@@ -387,6 +400,8 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
         zr.add(ws + wp.zero_off, 256);
         if (mode == 2) zr.add(pb.kb_diff, wp.kbdiff_bytes);
         e = slikl::launch_zero_ranges(zr, s);
+        if (e == hipSuccess && mode == 2 && pb.rowinfo)
+            e = slikl::launch_rowinfo(pb, (slikl::i32x4 *)pb.rowinfo, s);
     }
     pe.end(SLIKL_PHASE_FILL);
     if (e != hipSuccess) return SLIKL_ERR_LAUNCH;

@@ -7,6 +7,8 @@
 
 namespace slikl {
 
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
 // Bytes of one unit's w / exponent record of the dense dK strategy.
 constexpr int wrec_bytes(int hp) { return hp * 4 + 16; }
 
@@ -44,10 +46,14 @@ struct Problem {
     int32_t *kb_tasks;       // [batch * N2 * dk_nkb, 4]: first task, task count, active rows, 0
     int32_t *dk_ntasks;      // number of tasks
     int32_t dk_kb, dk_nkb, dk_chunk, dk_nch, dk_slots, dk_max_tasks;
-    int64_t s2max;           // key length of the dense maps
+    int64_t s2max;           // key length of the dense maps (longest key sequence)
+    // dense strategy with a TND side: per query row {batch, key base, key length
+    // (at most s2max), row within its batch}; null for BSND (computed in place)
+    const i32x4 *rowinfo;
     const int32_t *cu_q;     // [batch + 1] or null (BSND)
     const int32_t *cu_k;     // [batch + 1] or null (BSND)
     int64_t s1, s2;          // BSND per-batch lengths (unused for TND sides)
+    int64_t max_q, max_k;    // TND sides: the given longest sequence (0 = not given)
     int64_t t1, t2;          // total query / key rows
     int32_t batch, n1, n2, group, d, topk;
     int32_t layout_q, layout_k;
@@ -65,6 +71,7 @@ struct WorkspacePlan {
     int mode;                       // dK strategy (see launch_grad_fused)
     size_t dimap_off, dimap_bytes, maskmap_off, range_off, q16_off, wrec_off, part_off;
     size_t kbdiff_off, kbdiff_bytes, tasks_off, kbtasks_off, ntasks_off;
+    size_t rowinfo_off;             // dense with a TND side: i32x4 per query row
     int dk_nkb, dk_chunk, dk_nch, dk_max_tasks;
     size_t total;
 };
@@ -96,6 +103,7 @@ struct ZeroRanges {
     }
 };
 hipError_t launch_zero_ranges(const ZeroRanges &zr, hipStream_t stream);
+hipError_t launch_rowinfo(const Problem &pb, i32x4 *info, hipStream_t stream);
 hipError_t launch_dense_dk_tasks(const Problem &pb, hipStream_t stream);
 hipError_t launch_dense_dk(const Problem &pb, int hp, bool f16, hipStream_t stream);
 hipError_t launch_dense_dk_reduce(const Problem &pb, bool f16, hipStream_t stream);

@@ -34,12 +34,23 @@ def to_device(x, device="cuda"):
     return t
 
 
+def max_seqlens(x):
+    """Longest sequence of each TND side (host-known from the generator), 0 for BSND."""
+    def mx(cu):
+        return int(np.diff(np.asarray(cu)).max()) if cu is not None and len(cu) > 1 else 0
+    return dict(max_seqlen_q=mx(x.cu_q) if x.layout_q == "TND" else 0,
+                max_seqlen_k=mx(x.cu_k) if x.layout_k == "TND" else 0)
+
+
 def run_gpu(x, t=None, **kw):
-    """Call slikl_grad; returns numpy fp32/fp64 arrays (dq, dk, dw, y)."""
+    """Call slikl_grad; returns numpy fp32/fp64 arrays (dq, dk, dw, y).  TND sides
+    pass their longest sequence unless the caller gives max_seqlen_q / _k."""
     import torch
     import sparse_attention_indexer_token_amd as slikl
     if t is None:
         t = to_device(x)
+    for key, val in max_seqlens(x).items():
+        kw.setdefault(key, val)
     dq, dk, dw, y = slikl.slikl_grad(
         t["q"], t["k"], t["w"], t["idx"], t["p"], layout_q=x.layout_q, layout_k=x.layout_k,
         cu_seqlens_q=t["cu_q"], cu_seqlens_k=t["cu_k"],

@@ -45,11 +45,13 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_struct_layout_matches_header():
-    # 4 x int32, 7 x int64, 2 pointers, 3 x int32 (+4 bytes of tail padding)
-    assert ctypes.sizeof(SliklDesc) == 104
+    # 4 x int32, 7 x int64, 2 pointers, 3 x int32 (+4 bytes of padding), 2 x int64
+    assert ctypes.sizeof(SliklDesc) == 120
     assert SliklDesc.cu_seqlens_q.offset == 72
     assert SliklDesc.num_parts.offset == 88
     assert SliklDesc.dk_mode.offset == 96
+    assert SliklDesc.max_seqlen_q.offset == 104
+    assert SliklDesc.max_seqlen_k.offset == 112
 
 
 def good_desc(**kw):
@@ -86,12 +88,25 @@ def test_workspace_size_of_the_dsv32_shape(lib):
     assert st == 0 and n_dense >= 4096 * 4096 * (4 + 8)
 
 
-def test_dense_mode_needs_bsnd(lib):
-    cu = (ctypes.c_int32 * 2)(0, 4096)
-    d = good_desc(layout_q=1, layout_k=1, dk_mode=2)
+def tnd_desc(cu, **kw):
+    d = good_desc(layout_q=1, layout_k=1, **kw)
     d.cu_seqlens_q = ctypes.cast(cu, ctypes.c_void_p)
     d.cu_seqlens_k = ctypes.cast(cu, ctypes.c_void_p)
-    assert ws(lib, d)[0] == 3
+    return d
+
+
+def test_dense_mode_with_tnd_needs_the_maxima(lib):
+    cu = (ctypes.c_int32 * 2)(0, 4096)
+    assert ws(lib, tnd_desc(cu, dk_mode=2))[0] == 3                        # no maxima given
+    assert ws(lib, tnd_desc(cu, dk_mode=2, max_seqlen_q=4096))[0] == 3     # only one side
+    st, n = ws(lib, tnd_desc(cu, dk_mode=2, max_seqlen_q=4096, max_seqlen_k=4096))
+    st_b, n_b = ws(lib, good_desc(dk_mode=2))
+    # the same records as the BSND problem, plus one int4 of row info per query row
+    assert st == 0 and st_b == 0 and n >= n_b and n - n_b <= 4096 * 16 + 1024
+    assert ws(lib, tnd_desc(cu, max_seqlen_q=-1))[0] == 2
+    assert ws(lib, tnd_desc(cu, max_seqlen_k=1 << 31))[0] == 2
+    # BSND sides ignore the fields
+    assert ws(lib, good_desc(max_seqlen_q=-5, max_seqlen_k=-5))[0] == 0
 
 
 @pytest.mark.parametrize("field,value,status", [
@@ -142,10 +157,9 @@ def test_unit_overhead_follows_the_dk_strategy(lib):
     assert oh(good_desc(topk=128, deterministic=1)) == (0, _native.UNIT_OVERHEAD_DENSE)
     assert oh(good_desc(topk=64, deterministic=1)) == (0, _native.UNIT_OVERHEAD)
     cu = (ctypes.c_int32 * 2)(0, 4096)
-    d = good_desc(layout_q=1, layout_k=1)                                  # TND: scatter only
-    d.cu_seqlens_q = ctypes.cast(cu, ctypes.c_void_p)
-    d.cu_seqlens_k = ctypes.cast(cu, ctypes.c_void_p)
-    assert oh(d) == (0, _native.UNIT_OVERHEAD)
+    assert oh(tnd_desc(cu)) == (0, _native.UNIT_OVERHEAD)                 # TND without maxima: scatter
+    assert oh(tnd_desc(cu, max_seqlen_q=4096, max_seqlen_k=4096)) == (0, _native.UNIT_OVERHEAD_DENSE)
+    assert oh(tnd_desc(cu, max_seqlen_q=4096, max_seqlen_k=65536)) == (0, _native.UNIT_OVERHEAD)
     assert oh(good_desc(d=96))[0] == 2
     out = ctypes.c_int32(0)
     assert lib.slikl_grad_unit_overhead(None, ctypes.byref(out)) == 1

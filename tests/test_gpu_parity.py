@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 from workloads import WORKLOADS, Workload, make_inputs
-from tests.gpu_helpers import (check_close, keys_with_few_refs, oracle, run_gpu, to_device)
+from tests.gpu_helpers import (check_close, keys_with_few_refs, max_seqlens, oracle, run_gpu, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -67,8 +67,6 @@ DK_MODES = [("scatter", False), ("scatter", True), ("dense", False)]
 @pytest.mark.parametrize("dk_mode,det", DK_MODES)
 def test_small_parity(name, dk_mode, det):
     x = make_inputs(SMALL[name])
-    if dk_mode == "dense" and x.layout_q != "BSND":
-        pytest.skip("the dense dK path takes BSND inputs")
     _say(f"[parity] {name} dk_mode={dk_mode} det={det}")
     got = run_gpu(x, deterministic=det, dk_mode=dk_mode)
     ref = oracle(x)
@@ -171,6 +169,34 @@ def test_out_of_range_index_is_skipped_and_flagged():
     x.idx[0, 5, 0, 0] = -1
     x.idx[1, 7, 0, 1] = -1
     check_close(got, oracle(x), label="out-of-range skipped")
+
+
+def test_tnd_sequence_longer_than_its_given_maximum_is_flagged():
+    """Dense strategy with TND sides given a maximum below the longest sequence: the
+    call completes, keys past the maximum act as -1 slots (dq, dw and softmax_out then
+    match the oracle on those indices), and the metadata error word has bit 8."""
+    import torch
+    import sparse_attention_indexer_token_amd as slikl
+    x = make_inputs(SMALL["g8_d32_tnd"])          # sequences of 50, 1, 0 and 90 rows
+    t = to_device(x)
+    lim = 60
+    _say("[tnd max] g8_d32_tnd, maxima 60 < 90")
+    kw = dict(layout_q=x.layout_q, layout_k=x.layout_k, cu_seqlens_q=t["cu_q"], cu_seqlens_k=t["cu_k"],
+              dk_mode="dense", max_seqlen_q=lim, max_seqlen_k=lim)
+    md = slikl.slikl_grad_metadata(t["q"], t["k"], t["idx"], **kw)
+    dq, dk, dw, y = slikl.slikl_grad(t["q"], t["k"], t["w"], t["idx"], t["p"], metadata=md, **kw)
+    torch.cuda.synchronize()
+    assert int(md[8].item()) & 8
+    idx2 = np.where(x.idx >= lim, -1, x.idx)
+    from oracle import slikl_grad_ref
+    ref = slikl_grad_ref(x.q, x.k, x.w, idx2, x.p, layout_q=x.layout_q, layout_k=x.layout_k,
+                         cu_seqlens_q=x.cu_q, cu_seqlens_k=x.cu_k)
+    got = dict(dq=dq.float().cpu().numpy(), dw=dw.cpu().numpy(), softmax_out=y.cpu().numpy())
+    check_close(got, ref, what=("dq", "dw", "softmax_out"), label="tnd max")
+    # within the maxima nothing is flagged
+    md_ok = slikl.slikl_grad_metadata(t["q"], t["k"], t["idx"], **dict(kw, **max_seqlens(x)))
+    torch.cuda.synchronize()
+    assert int(md_ok[8].item()) & 8 == 0
 
 
 @pytest.mark.parametrize("dk_mode", ["scatter", "dense"])
