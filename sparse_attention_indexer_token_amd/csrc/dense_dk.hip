@@ -46,13 +46,14 @@ typedef __attribute__((address_space(3))) void lds_void_t2;
 constexpr int kDkWaves = 4;
 constexpr int kDkBlock = 64 * kDkWaves;
 
-template <int HP, int D>
+template <int HP, int D, int KT_ = 1>
 struct DenseCfg {
     static constexpr int NH = HP / 32;          // head words per key
     static constexpr int NKH = HP / 16;         // k-steps over heads
     static constexpr int NDT = D / 32;          // d tiles
     static constexpr int DCH = D / 8;           // 16-byte chunks per q row
-    static constexpr int KB = 32 * kDkWaves;    // keys per workgroup (32 per wave)
+    static constexpr int KT = KT_;              // 32-key tiles per wave
+    static constexpr int KB = 32 * KT * kDkWaves;  // keys per workgroup
     static constexpr int QBYTES = HP * D * 2;   // q tile
     static constexpr int NQC = QBYTES / 1024;   // its 1 KiB copies
     static constexpr int MBYTES = KB * NH * 4;  // head words of the block's keys
@@ -112,9 +113,9 @@ __device__ __forceinline__ int2 dense_rows(const Problem &pb, int b) {
     return int2{pb.cu_q[b], pb.cu_q[b + 1]};
 }
 
-template <int HP, int D, bool F16>
+template <int HP, int D, bool F16, int KT>
 __device__ __forceinline__ void dense_dk_body(const Problem &pb) {
-    using C = DenseCfg<HP, D>;
+    using C = DenseCfg<HP, D, KT>;
     constexpr int NH = C::NH, NKH = C::NKH, NDT = C::NDT, DCH = C::DCH, KB = C::KB, NS = C::NS;
     constexpr int CPW = C::CPW;
     constexpr uint32_t kPad = 0x80000000u;      // past the end of every view
@@ -130,7 +131,8 @@ __device__ __forceinline__ void dense_dk_body(const Problem &pb) {
     const int l32 = lane & 31, half = lane >> 5, l16 = lane & 15, grp = lane >> 4;
 
     const int G = pb.group;
-    const int kw = 32 * wave + l32;            // this lane's key within the block (B column)
+    // this lane's keys within the block (B columns): kw0 + 32 t for key tile t
+    const int kw0 = 32 * KT * wave + l32;
     const uint16_t *qsrc = F16 ? pb.q : pb.q16;
     const int ntasks = pb.dk_ntasks[0];
 
@@ -151,7 +153,9 @@ __device__ __forceinline__ void dense_dk_body(const Problem &pb) {
     const int j0 = kb * KB;
     const int j1 = j0 + KB < S2 ? j0 + KB : S2;
     const int nk = j1 > j0 ? j1 - j0 : 0;      // keys of this block
-    const bool jok = kw < nk;
+    bool jok[KT];
+#pragma unroll
+    for (int t = 0; t < KT; ++t) jok[t] = kw0 + 32 * t < nk;
 
     // ---- active rows: those of [r0, r1) whose unit names a key of [j0, j1), in
     //      order, listed in LDS a chunk of kDkBlock rows at a time
@@ -228,9 +232,11 @@ __device__ __forceinline__ void dense_dk_body(const Problem &pb) {
         }
     };
 
-    f32x16 acc[NDT];
+    f32x16 acc[KT][NDT];
 #pragma unroll
-    for (int db = 0; db < NDT; ++db) acc[db] = f32x16{};
+    for (int t = 0; t < KT; ++t)
+#pragma unroll
+        for (int db = 0; db < NDT; ++db) acc[t][db] = f32x16{};
 
     // ---- pipeline: rows issued NS - 1 ahead
     int inflight = 0, st_issue = 0, st_use = 0;
@@ -259,7 +265,10 @@ __device__ __forceinline__ void dense_dk_body(const Problem &pb) {
         const char *stg = s_stage + st_use * C::STAGE;
         const int *rec = (const int *)(stg + C::OFF_MISC + HP * 4);
         const float rowscale = ldexpf(1.f, -(rec[0] + rec[1]));
-        const float dIs = jok ? (float)((const int32_t *)(stg + C::OFF_DI))[kw] * rowscale : 0.f;
+#pragma unroll
+        for (int kt = 0; kt < KT; ++kt) {
+        const int kw = kw0 + 32 * kt;
+        const float dIs = jok[kt] ? (float)((const int32_t *)(stg + C::OFF_DI))[kw] * rowscale : 0.f;
         if (__builtin_amdgcn_ballot_w64(dIs != 0.f) != 0) {
             uint32_t mw[NH];
 #pragma unroll
@@ -300,7 +309,8 @@ __device__ __forceinline__ void dense_dk_body(const Problem &pb) {
 #pragma unroll
             for (int db = 0; db < NDT; ++db)
 #pragma unroll
-                for (int j = 0; j < 16; ++j) acc[db][j] = fmaf(dIs, tp[db][j], acc[db][j]);
+                for (int j = 0; j < 16; ++j) acc[kt][db][j] = fmaf(dIs, tp[db][j], acc[kt][db][j]);
+        }
         }
         st_use = st_use + 1 == NS ? 0 : st_use + 1;
         --inflight;
@@ -308,27 +318,31 @@ __device__ __forceinline__ void dense_dk_body(const Problem &pb) {
 
     // ---- this task's partial sum: dk_part[task][key within the block][d]
     {
-        float *part = pb.dk_part + ((size_t)task * KB + kw) * D;
 #pragma unroll
-        for (int db = 0; db < NDT; ++db)
+        for (int kt = 0; kt < KT; ++kt) {
+            float *part = pb.dk_part + ((size_t)task * KB + kw0 + 32 * kt) * D;
 #pragma unroll
-            for (int jq = 0; jq < 4; ++jq)
-                *(float4 *)(part + 32 * db + 8 * jq + 4 * half) =
-                    float4{acc[db][4 * jq], acc[db][4 * jq + 1], acc[db][4 * jq + 2], acc[db][4 * jq + 3]};
+            for (int db = 0; db < NDT; ++db)
+#pragma unroll
+                for (int jq = 0; jq < 4; ++jq)
+                    *(float4 *)(part + 32 * db + 8 * jq + 4 * half) =
+                        float4{acc[kt][db][4 * jq], acc[kt][db][4 * jq + 1], acc[kt][db][4 * jq + 2],
+                               acc[kt][db][4 * jq + 3]};
+        }
     }
     lds_barrier();          // the ring and the row list are reused by the next task
   }
 }
 
 // The body under the register budget of two workgroups per compute unit, or of one.
-template <int HP, int D, bool F16>
+template <int HP, int D, bool F16, int KT>
 __global__ __launch_bounds__(kDkBlock, 2) void dense_dk_kernel2(Problem pb) {
-    dense_dk_body<HP, D, F16>(pb);
+    dense_dk_body<HP, D, F16, KT>(pb);
 }
 
-template <int HP, int D, bool F16>
+template <int HP, int D, bool F16, int KT>
 __global__ __launch_bounds__(kDkBlock, 1) void dense_dk_kernel1(Problem pb) {
-    dense_dk_body<HP, D, F16>(pb);
+    dense_dk_body<HP, D, F16, KT>(pb);
 }
 
 // Task table (one workgroup): active rows per (key block, row chunk) from the
@@ -590,20 +604,20 @@ __global__ void dense_dk_reduce_kernel(Problem pb) {
     }
 }
 
-template <int HP, int D, bool F16>
+template <int HP, int D, bool F16, int KT>
 static hipError_t launch_dense(const Problem &pb, hipStream_t stream) {
-    if constexpr (DenseCfg<HP, D>::WGPC == 2)
-        hipLaunchKernelGGL((dense_dk_kernel2<HP, D, F16>), dim3(pb.dk_slots), dim3(kDkBlock), 0, stream, pb);
+    if constexpr (DenseCfg<HP, D, KT>::WGPC == 2)
+        hipLaunchKernelGGL((dense_dk_kernel2<HP, D, F16, KT>), dim3(pb.dk_slots), dim3(kDkBlock), 0, stream, pb);
     else
-        hipLaunchKernelGGL((dense_dk_kernel1<HP, D, F16>), dim3(pb.dk_slots), dim3(kDkBlock), 0, stream, pb);
+        hipLaunchKernelGGL((dense_dk_kernel1<HP, D, F16, KT>), dim3(pb.dk_slots), dim3(kDkBlock), 0, stream, pb);
     return hipGetLastError();
 }
 
-int dense_dk_keys_per_block() { return DenseCfg<32, 32>::KB; }
+int dense_dk_keys_per_block(int kt) { return kt == 2 ? DenseCfg<32, 32, 2>::KB : DenseCfg<32, 32, 1>::KB; }
 
-int dense_dk_wgs_per_cu(int hp, int d) {
+int dense_dk_wgs_per_cu(int hp, int d, int kt) {
 #define SLIKL_DENSE_WG(HPV, DV) \
-    if (hp == HPV && d == DV) return DenseCfg<HPV, DV>::WGPC;
+    if (hp == HPV && d == DV) return kt == 2 ? DenseCfg<HPV, DV, 2>::WGPC : DenseCfg<HPV, DV, 1>::WGPC;
     SLIKL_DENSE_WG(32, 32) SLIKL_DENSE_WG(32, 64) SLIKL_DENSE_WG(32, 128)
     SLIKL_DENSE_WG(64, 32) SLIKL_DENSE_WG(64, 64) SLIKL_DENSE_WG(64, 128)
     SLIKL_DENSE_WG(128, 32) SLIKL_DENSE_WG(128, 64) SLIKL_DENSE_WG(128, 128)
@@ -618,10 +632,12 @@ hipError_t launch_dense_dk_tasks(const Problem &pb, hipStream_t stream) {
 
 hipError_t launch_dense_dk(const Problem &pb, int hp, bool f16, hipStream_t stream) {
     const int d = pb.d;
+    const bool kt2 = pb.dk_kb == DenseCfg<32, 32, 2>::KB;      // two key tiles per wave
     hipError_t e;
 #define SLIKL_DENSE_CASE(HPV, DV)                                                              \
     if (hp == HPV && d == DV)                                                                  \
-        e = f16 ? launch_dense<HPV, DV, true>(pb, stream) : launch_dense<HPV, DV, false>(pb, stream);
+        e = kt2 ? (f16 ? launch_dense<HPV, DV, true, 2>(pb, stream) : launch_dense<HPV, DV, false, 2>(pb, stream)) \
+                : (f16 ? launch_dense<HPV, DV, true, 1>(pb, stream) : launch_dense<HPV, DV, false, 1>(pb, stream));
     SLIKL_DENSE_CASE(32, 32) else SLIKL_DENSE_CASE(32, 64) else SLIKL_DENSE_CASE(32, 128)
     else SLIKL_DENSE_CASE(64, 32) else SLIKL_DENSE_CASE(64, 64) else SLIKL_DENSE_CASE(64, 128)
     else SLIKL_DENSE_CASE(128, 32) else SLIKL_DENSE_CASE(128, 64) else SLIKL_DENSE_CASE(128, 128)

@@ -24,6 +24,12 @@ int64_t rows_k(const slikl_desc *d) { return d->layout_k == SLIKL_LAYOUT_BSND ? 
 int64_t len_q(const slikl_desc *d) { return d->layout_q == SLIKL_LAYOUT_BSND ? d->s1 : d->max_seqlen_q; }
 int64_t len_k(const slikl_desc *d) { return d->layout_k == SLIKL_LAYOUT_BSND ? d->s2 : d->max_seqlen_k; }
 bool any_tnd(const slikl_desc *d) { return d->layout_q == SLIKL_LAYOUT_TND || d->layout_k == SLIKL_LAYOUT_TND; }
+// 32-key tiles per wave of the dense dK kernel: the kernel fetches a query row's q once
+// per key block that its named keys meet; when q is too large to stay in the on-die
+// caches (more than 128 MiB) blocks of twice the keys halve those fetches from HBM
+int dense_kt(const slikl_desc *d) {
+    return (double)rows_q(d) * d->n1 * d->d * 2.0 > 128.0 * (1 << 20) ? 2 : 1;
+}
 
 // Field checks of the operator page's constraints section (dtypes, layouts,
 // cuSeqLens required for TND) and of this library's limits (N1 <= 128,
@@ -99,7 +105,7 @@ int unit_overhead(const slikl_desc *d) {
 // Dense dK task geometry: key blocks per (batch, key head), row chunk length and
 // count (at most 256 chunks per batch), and the most tasks the table can hold.
 void dense_dk_geometry(const slikl_desc *d, int *nkb, int *chunk, int *nch, int *max_tasks) {
-    const int64_t kb = slikl::dense_dk_keys_per_block();
+    const int64_t kb = slikl::dense_dk_keys_per_block(dense_kt(d));
     *nkb = (int)((len_k(d) + kb - 1) / kb);
     const int64_t c = (len_q(d) + 255) / 256;
     *chunk = (int)(c < 16 ? 16 : c);
@@ -148,7 +154,7 @@ slikl::WorkspacePlan plan(const slikl_desc *d) {
         p.wrec_off = off;
         off = align_up(off + U * (size_t)slikl::wrec_bytes(head_tile(d->n1 / d->n2)));
         p.part_off = off;
-        off = align_up(off + (size_t)p.dk_max_tasks * slikl::dense_dk_keys_per_block() * (size_t)d->d * 4);
+        off = align_up(off + (size_t)p.dk_max_tasks * slikl::dense_dk_keys_per_block(dense_kt(d)) * (size_t)d->d * 4);
         p.kbdiff_off = off;
         p.kbdiff_bytes = nbg * (size_t)p.dk_nch * (size_t)(p.dk_nkb + 1) * 4;
         off = align_up(off + p.kbdiff_bytes);
@@ -362,7 +368,7 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
         pb.dk_tasks = (int32_t *)(ws + wp.tasks_off);
         pb.kb_tasks = (int32_t *)(ws + wp.kbtasks_off);
         pb.dk_ntasks = (int32_t *)(ws + wp.ntasks_off);
-        pb.dk_kb = slikl::dense_dk_keys_per_block();
+        pb.dk_kb = slikl::dense_dk_keys_per_block(dense_kt(desc));
         pb.dk_nkb = wp.dk_nkb;
         pb.dk_chunk = wp.dk_chunk;
         pb.dk_nch = wp.dk_nch;
@@ -372,7 +378,7 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
             if (hipGetDevice(&dev) != hipSuccess ||
                 hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
                 return SLIKL_ERR_LAUNCH;
-            int64_t slots = (int64_t)cus * slikl::dense_dk_wgs_per_cu(head_tile(pb.group), (int)desc->d);
+            int64_t slots = (int64_t)cus * slikl::dense_dk_wgs_per_cu(head_tile(pb.group), (int)desc->d, dense_kt(desc));
             pb.dk_slots = (int)(slots > slikl::kDkSlotsMax ? slikl::kDkSlotsMax : slots);
         }
         pb.s2max = len_k(desc);

@@ -107,8 +107,8 @@ hipError_t launch_rowinfo(const Problem &pb, i32x4 *info, hipStream_t stream);
 hipError_t launch_dense_dk_tasks(const Problem &pb, hipStream_t stream);
 hipError_t launch_dense_dk(const Problem &pb, int hp, bool f16, hipStream_t stream);
 hipError_t launch_dense_dk_reduce(const Problem &pb, bool f16, hipStream_t stream);
-int dense_dk_keys_per_block();
-int dense_dk_wgs_per_cu(int hp, int d);
+int dense_dk_keys_per_block(int kt);   // kt: 32-key tiles per wave (1 or 2)
+int dense_dk_wgs_per_cu(int hp, int d, int kt);
 constexpr int kDkSlotsMax = 1024;   // cap on concurrently resident dK workgroups
 hipError_t launch_finalize_dk(const Problem &pb, bool f16, bool det, hipStream_t stream);
 hipError_t launch_det_scale(const Problem &pb, bool f16, float *scale_block, hipStream_t stream);
