@@ -350,11 +350,12 @@ __device__ __forceinline__ int check_cu(const int32_t *cu, int batch, int64_t to
 __global__ __launch_bounds__(1024) void meta_split_kernel(Problem pb, int parts, int mode, int overhead,
                                                           int64_t *prefix, const int32_t *cflags,
                                                           int32_t *md) {
-    constexpr int kSplitLds = 8192;
+    constexpr int kSplitLds = 65536;
     __shared__ int64_t s_part[1024];
-    __shared__ int64_t s_cost[kSplitLds];
+    __shared__ uint16_t s_cost[kSplitLds];
     __shared__ int s_used[32];
-    const int tid = threadIdx.x, nt = blockDim.x;
+    const int tid = threadIdx.x, nt = blockDim.x;      // nt = 1024
+    const int lane = tid & 63, wave = tid >> 6;
     const int64_t U = pb.t1 * pb.n2;
 
     int flags = 0;
@@ -389,34 +390,40 @@ __global__ __launch_bounds__(1024) void meta_split_kernel(Problem pb, int parts,
 
     int32_t *bnd = md + 16;
     if (mode == 0) {
-        // inclusive scan of prefix[1..U] (prefix[0] = 0): contiguous segments per thread
+        // inclusive scan of the unit costs prefix[1..U]: contiguous segments per thread.
+        // Up to kSplitLds units the costs go through LDS as 16-bit values (a cost is at
+        // most topk + overhead < 2^16): one parallel load instead of dependent global
+        // round trips per unit.
         const int64_t seg = (U + nt - 1) / nt;
         const int64_t a = (int64_t)tid * seg, e = a + seg < U ? a + seg : U;
-        // up to kSplitLds units: the costs go through LDS (one parallel load instead of
-        // dependent global round trips per unit)
-        const bool inlds = U <= kSplitLds;
-        int64_t *cost = inlds ? s_cost : prefix + 1;   // cost[i] = cost of unit i
+        const bool inlds = U <= kSplitLds && pb.topk + overhead < 65536;
         if (inlds) {
-            for (int64_t i = tid; i < U; i += nt) s_cost[i] = prefix[i + 1];
+            for (int64_t i = tid; i < U; i += nt) s_cost[i] = (uint16_t)prefix[i + 1];
             __syncthreads();
         }
+        auto cost = [&](int64_t i) -> int64_t { return inlds ? (int64_t)s_cost[i] : prefix[i + 1]; };
         int64_t loc = 0;
-        for (int64_t i = a; i < e; ++i) loc += cost[i];
-        s_part[tid] = loc;
-        __syncthreads();
-        for (int o = 1; o < nt; o <<= 1) {   // Hillis-Steele inclusive scan
-            int64_t v = tid >= o ? s_part[tid - o] : 0;
-            __syncthreads();
-            s_part[tid] += v;
-            __syncthreads();
+        for (int64_t i = a; i < e; ++i) loc += cost(i);
+        // block-wide inclusive scan of the segment sums: wave scans, then the 16 wave
+        // totals
+        int64_t x = loc;
+        for (int o = 1; o < 64; o <<= 1) {
+            const int64_t y = __shfl_up(x, o);
+            if (lane >= o) x += y;
         }
-        int64_t run = tid > 0 ? s_part[tid - 1] : 0;
-        for (int64_t i = a; i < e; ++i) {      // cost[i] becomes E(i + 1)
-            run += cost[i];
-            cost[i] = run;
+        if (lane == 63) s_part[wave] = x;
+        __syncthreads();
+        if (wave == 0) {
+            int64_t v = lane < nt / 64 ? s_part[lane] : 0;
+            for (int o = 1; o < 16; o <<= 1) {
+                const int64_t y = __shfl_up(v, o);
+                if (lane >= o) v += y;
+            }
+            if (lane < 16) s_part[16 + lane] = v;
         }
         __syncthreads();
-        const int64_t W = s_part[nt - 1];
+        const int64_t incl = x + (wave > 0 ? s_part[16 + wave - 1] : 0);   // E(e)
+        const int64_t W = s_part[16 + nt / 64 - 1];
         // boundary i is the first u in [0, U] with E(u) parts >= i W (E the exclusive
         // prefix, E(0) = 0, E(U) = W): u = 0 takes i = 0 (every i when W = 0), and
         // u >= 1 takes the i with E(u-1) parts < i W <= E(u) parts, i <= parts.  Each
@@ -425,9 +432,9 @@ __global__ __launch_bounds__(1024) void meta_split_kernel(Problem pb, int parts,
             for (int i = tid; i <= parts; i += nt) bnd[i] = 0;
         } else {
             if (tid == 0) bnd[0] = 0;
-            int64_t prev = tid > 0 ? s_part[tid - 1] : 0;      // E(a)
+            int64_t prev = incl - loc;                         // E(a)
             for (int64_t u = a + 1; u <= e; ++u) {
-                const int64_t cur = cost[u - 1];               // E(u)
+                const int64_t cur = prev + cost(u - 1);        // E(u)
                 // i with prev parts < i W <= cur parts: i in [floor(prev parts / W) + 1, floor(cur parts / W)]
                 int64_t i0 = prev * parts / W + 1;
                 int64_t i1 = cur * parts / W;

@@ -479,6 +479,53 @@ __global__ __launch_bounds__(1024) void dense_dk_tasks_kernel(Problem pb) {
     int ne = 0;
     // pass 1: active rows per (key block, chunk), written over the difference arrays,
     // and per key block
+    if (nkb <= 64) {
+        // a wave per row chunk (lane = key block): one load per element, the prefix over
+        // key blocks as a wave scan; lanes of wave 0 add up the key blocks' totals
+        constexpr int CPV = kTaskNchMax / 16;
+        const bool kok = lane < nkb;
+        for (int bg = 0; bg < nbg; ++bg) {
+            int32_t *dif = pb.kb_diff + (size_t)bg * nch * (nkb + 1);
+            int v[CPV];
+#pragma unroll
+            for (int i = 0; i < CPV; ++i) {
+                const int ch = wave + 16 * i;
+                v[i] = ch < nch && kok ? dif[(size_t)ch * (nkb + 1) + lane] : 0;
+            }
+            int colsum = 0;
+#pragma unroll
+            for (int i = 0; i < CPV; ++i) {
+                int x = v[i];
+                for (int o = 1; o < 64; o <<= 1) {
+                    const int y = __shfl_up(x, o);
+                    if (lane >= o) x += y;
+                }
+                const int ch = wave + 16 * i;
+                if (ch < nch && kok) {
+                    dif[(size_t)ch * (nkb + 1) + lane] = x;
+                    colsum += x;
+                }
+            }
+            s_scan[wave * 64 + lane] = colsum;
+            __syncthreads();
+            if (wave == 0) {
+                int c = 0;
+                for (int w2 = 0; w2 < 16; ++w2) c += s_scan[w2 * 64 + lane];
+                if (kok) {
+                    pb.kb_tasks[4 * (bg * nkb + lane) + 2] = c;
+                    tot += c;
+                    ne += c > 0 ? 1 : 0;
+                }
+            }
+            __syncthreads();
+        }
+        if (wave == 0) {
+            for (int o = 32; o > 0; o >>= 1) {
+                tot += __shfl_xor(tot, o);
+                ne += __shfl_xor(ne, o);
+            }
+        }
+    } else
     for (int bg = 0; bg < nbg; ++bg) {
         if (tid < nch) s_run[tid] = 0;
         for (int k0 = 0; k0 < nkb; k0 += kTaskKT) {
