@@ -74,7 +74,8 @@ enum { SLIKL_SPLIT_WEIGHTED = 0, SLIKL_SPLIT_ROWS = 1 };
  * atomics, bitwise reproducible; it pays off when the top-k lists cover a fair
  * share of each batch's keys.  With L the key length per batch (S2, or
  * max_seqlen_k for TND), AUTO picks DENSE when L <= 16 topk (L <= 32 topk when
- * deterministic) and the records fit in 8 GiB, SCATTER otherwise. */
+ * deterministic), there are at least 2048 units and the records fit in 8 GiB,
+ * SCATTER otherwise. */
 enum { SLIKL_DK_AUTO = 0, SLIKL_DK_SCATTER = 1, SLIKL_DK_DENSE = 2 };
 
 /* Metadata array (int32, SLIKL_METADATA_INTS entries).  A "unit" is one

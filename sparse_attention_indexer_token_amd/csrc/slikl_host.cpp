@@ -87,9 +87,10 @@ int dk_strategy(const slikl_desc *d) {
     // AUTO: the dense kernels cost about one (row, 128-key block) step per 128 keys of
     // a row's named range (at most S2), the scatter about one atomic row per valid
     // slot, dearer in fixed point (deterministic) and under contention on shared keys:
-    // dense when S2 <= 16 topk, or S2 <= 32 topk when deterministic
+    // dense when S2 <= 16 topk, or S2 <= 32 topk when deterministic.  Below 2048 units
+    // the dense strategy's extra launches outweigh the atomics it saves.
     const int64_t ratio = d->deterministic ? 32 : 16;
-    if (d->dk_mode == SLIKL_DK_AUTO && fits && len_k(d) <= ratio * d->topk) {
+    if (d->dk_mode == SLIKL_DK_AUTO && fits && len_k(d) <= ratio * d->topk && rows_q(d) * d->n2 >= 2048) {
         // the dense records are sized [units, longest key sequence]; keep them modest
         const double bytes = (double)rows_q(d) * d->n2 * len_k(d) * 4.0 * (1 + head_tile(d->n1 / d->n2) / 32);
         if (bytes <= 8.0 * (1ull << 30)) return 2;
