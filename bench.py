@@ -51,11 +51,12 @@ def traffic_file(kernel, workload):
 
 
 def fused_kernel(strategy, group):
-    """The fused kernel a call runs: the scatter strategy's, or the dense strategy's
-    eight-wave kernel for head groups padded to at most 64 heads, four-wave above."""
-    if strategy != "dense":
-        return "grad_fused_kernel"
-    return "grad_dense8_kernel" if group <= 64 else "grad_dense_kernel"
+    """The fused kernel a call runs: the eight-wave kernel for head groups padded to at
+    most 64 heads (every strategy), above that the four-wave kernel of the dense
+    strategy or of the scatter strategy."""
+    if group <= 64:
+        return "grad_dense8_kernel"
+    return "grad_dense_kernel" if strategy == "dense" else "grad_fused_kernel"
 
 
 def sources_sha256(kernel):
@@ -72,6 +73,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="dsv32_indexer")
     ap.add_argument("--deterministic", type=int, default=None, help="override the workload's mode")
+    ap.add_argument("--dk-mode", default="auto", choices=["auto", "scatter", "dense", "sorted"],
+                    help="dK strategy (auto: the library's choice)")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="oracle sample size (rows)")
     ap.add_argument("--profiled-calls", type=int, default=5, help="calls timed per phase")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -148,8 +151,9 @@ def main():
     mx = lambda cu: int(np.diff(cu).max()) if cu is not None and len(cu) > 1 else 0
     kw = dict(layout_q=x.layout_q, layout_k=x.layout_k, cu_seqlens_q=cu_q, cu_seqlens_k=cu_k,
               deterministic=det, max_seqlen_q=mx(x.cu_q) if x.layout_q == "TND" else 0,
-              max_seqlen_k=mx(x.cu_k) if x.layout_k == "TND" else 0)
+              max_seqlen_k=mx(x.cu_k) if x.layout_k == "TND" else 0, dk_mode=args.dk_mode)
     desc = slikl.make_desc(q, k, idx, **kw)
+    strategy = slikl.slikl_grad_dk_strategy(desc)
     ws = torch.empty(slikl.slikl_grad_workspace_size(desc), dtype=torch.uint8, device=dev)
     md = torch.empty(slikl.METADATA_INTS, dtype=torch.int32, device=dev)
     out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(w), torch.empty_like(p))
@@ -175,7 +179,6 @@ def main():
         _, ms = slikl.slikl_grad_profiled(q, k, w, idx, p, metadata=md, workspace=ws, out=out, **kw)
         phases.append(ms)
     phase_ms = {name: float(np.mean([ph[name] for ph in phases])) for name in phases[0]}
-    strategy = "dense" if phase_ms.get("dk", 0.0) > 0.0 else "scatter"
     T1 = x.t1
     G = wl.n1 // wl.n2
     kernel = fused_kernel(strategy, G)

@@ -75,8 +75,12 @@ enum { SLIKL_SPLIT_WEIGHTED = 0, SLIKL_SPLIT_ROWS = 1 };
  * share of each batch's keys.  With L the key length per batch (S2, or
  * max_seqlen_k for TND), AUTO picks DENSE when L <= 16 topk (L <= 32 topk when
  * deterministic), there are at least 2048 units and the records fit in 8 GiB,
- * SCATTER otherwise. */
-enum { SLIKL_DK_AUTO = 0, SLIKL_DK_SCATTER = 1, SLIKL_DK_DENSE = 2 };
+ * SCATTER otherwise.  SORTED (head groups N1/N2 up to 64 and N2*D*2 < 16384 bytes,
+ * else UNSUPPORTED) writes each valid slot's dK part once (fp32) into a buffer
+ * sorted by key (workspace: D*4 + 4 bytes per (unit, slot) more) and sums each
+ * key's run: atomics only where a run is split between two waves; deterministic mode
+ * sums in int64 fixed point, so its result is bitwise reproducible. */
+enum { SLIKL_DK_AUTO = 0, SLIKL_DK_SCATTER = 1, SLIKL_DK_DENSE = 2, SLIKL_DK_SORTED = 3 };
 
 /* Metadata array (int32, SLIKL_METADATA_INTS entries).  A "unit" is one
  * (query row, key head) pair, u = row * N2 + g.
@@ -143,6 +147,12 @@ slikl_status slikl_grad_parts(const slikl_desc *desc, int32_t *parts);
  * else SLIKL_UNIT_OVERHEAD.  Host only.  PARAM_INVALID / UNSUPPORTED as
  * slikl_grad_workspace_size; NULLPTR for a null argument. */
 slikl_status slikl_grad_unit_overhead(const slikl_desc *desc, int32_t *overhead);
+
+/* The dK strategy a call with `desc` runs: SLIKL_DK_SCATTER, SLIKL_DK_DENSE or
+ * SLIKL_DK_SORTED (AUTO resolved as described at SLIKL_DK_*).  Host only.
+ * PARAM_INVALID / UNSUPPORTED as slikl_grad_workspace_size; NULLPTR for a null
+ * argument. */
+slikl_status slikl_grad_dk_strategy(const slikl_desc *desc, int32_t *strategy);
 
 /* Load-balancing metadata pre-pass (prior art: the metadata article's
  * 功能定位 and Metadata 输出布局 sections describe an AICPU pre-operator

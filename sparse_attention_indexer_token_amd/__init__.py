@@ -23,7 +23,7 @@ from ._native import (  # noqa: F401
 )
 
 __all__ = ["slikl_grad", "slikl_grad_profiled", "slikl_grad_metadata", "slikl_grad_workspace_size",
-           "slikl_grad_parts", "slikl_grad_unit_overhead", "slikl_status_string", "make_desc", "SliklDesc", "SliklError"]
+           "slikl_grad_parts", "slikl_grad_unit_overhead", "slikl_grad_dk_strategy", "slikl_status_string", "make_desc", "SliklDesc", "SliklError"]
 
 
 def _torch():
@@ -125,6 +125,11 @@ def slikl_grad_parts(desc: SliklDesc) -> int:
 def slikl_grad_unit_overhead(desc: SliklDesc) -> int:
     """Per-unit overhead (valid-slot equivalents) of the weighted split for `desc`."""
     return _native.unit_overhead(desc)
+
+
+def slikl_grad_dk_strategy(desc: SliklDesc) -> str:
+    """The dK strategy ("scatter", "dense" or "sorted") a call with `desc` runs."""
+    return _native.dk_strategy(desc)
 
 
 def slikl_grad_metadata(q, k, sparse_indices, *, layout_q="BSND", layout_k="BSND",

@@ -22,7 +22,7 @@ SLIKL_ERR_LAUNCH = 5
 LAYOUT = {"BSND": 0, "TND": 1}
 DTYPE = {"f16": 0, "bf16": 1}
 SPLIT = {"weighted": 0, "rows": 1}
-DK_MODE = {"auto": 0, "scatter": 1, "dense": 2}
+DK_MODE = {"auto": 0, "scatter": 1, "dense": 2, "sorted": 3}
 
 METADATA_HEADER = 16
 MAX_PARTS = 2048
@@ -30,7 +30,7 @@ METADATA_INTS = 2080
 UNIT_OVERHEAD = 512
 UNIT_OVERHEAD_DENSE = 1024
 
-EXPORTS = ("slikl_grad_workspace_size", "slikl_grad_parts", "slikl_grad_unit_overhead", "slikl_grad_metadata",
+EXPORTS = ("slikl_grad_workspace_size", "slikl_grad_parts", "slikl_grad_unit_overhead", "slikl_grad_dk_strategy", "slikl_grad_metadata",
            "slikl_grad", "slikl_grad_profiled", "slikl_status_string")
 
 PHASES = ("metadata", "fill", "key_copy", "det_scale", "fused", "dk", "dk_final")
@@ -74,6 +74,8 @@ def load():
     lib.slikl_grad_parts.restype = c_int32
     lib.slikl_grad_unit_overhead.argtypes = [P(SliklDesc), P(c_int32)]
     lib.slikl_grad_unit_overhead.restype = c_int32
+    lib.slikl_grad_dk_strategy.argtypes = [P(SliklDesc), P(c_int32)]
+    lib.slikl_grad_dk_strategy.restype = c_int32
     lib.slikl_grad_metadata.argtypes = [P(SliklDesc), c_void_p, c_void_p, c_void_p, c_size_t, c_void_p]
     lib.slikl_grad_metadata.restype = c_int32
     lib.slikl_grad.argtypes = [P(SliklDesc)] + [c_void_p] * 10 + [c_void_p, c_size_t, c_void_p]
@@ -119,6 +121,12 @@ def unit_overhead(desc: SliklDesc) -> int:
     out = c_int32(0)
     _check(load().slikl_grad_unit_overhead(ctypes.byref(desc), ctypes.byref(out)), "slikl_grad_unit_overhead")
     return int(out.value)
+
+
+def dk_strategy(desc: SliklDesc) -> str:
+    out = c_int32(0)
+    _check(load().slikl_grad_dk_strategy(ctypes.byref(desc), ctypes.byref(out)), "slikl_grad_dk_strategy")
+    return {v: k for k, v in DK_MODE.items()}[int(out.value)]
 
 
 def grad_metadata_raw(desc: SliklDesc, indices_ptr: int, metadata_ptr: int, ws_ptr: int,

@@ -18,7 +18,8 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libslikl.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["grad_fused.hip", "grad_dense.hip", "grad_dense8.hip", "dense_dk.hip", "aux_kernels.hip", "slikl_host.cpp"]
+SOURCES = ["grad_fused.hip", "grad_dense.hip", "grad_dense8.hip", "dense_dk.hip", "scatter_dk.hip", "sorted_dk.hip",
+           "aux_kernels.hip", "slikl_host.cpp"]
 ARCH = "gfx950"
 
 

@@ -42,7 +42,8 @@ __global__ void zero_ranges_kernel(ZeroRanges zr) {
 // Dense strategy with a TND side: per query row r its batch b, the key base and key
 // length of b (at most the dense maps' key length) and r's index within b.  Broken
 // cuSeqLens (flagged by the metadata pre-pass) still give in-range batches, and the
-// key length is clamped to [0, s2max], so no record access leaves its row.
+// key base and length are clamped so that every key row stays in [0, T2) and no
+// record access leaves its row.
 __global__ void rowinfo_kernel(Problem pb, i32x4 *info) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; r < pb.t1; r += stride) {
@@ -62,7 +63,11 @@ __global__ void rowinfo_kernel(Problem pb, i32x4 *info) {
             kbase = pb.cu_k[b];
             klen = pb.cu_k[b + 1] - kbase;
         }
-        klen = klen < 0 ? 0 : (klen > (int)pb.s2max ? (int)pb.s2max : klen);
+        // keep every key row of the batch inside [0, T2) whatever cuSeqLensK holds
+        const int t2 = (int)pb.t2;
+        kbase = kbase < 0 ? 0 : (kbase > t2 ? t2 : kbase);
+        const int kcap = (int)pb.s2max < t2 - kbase ? (int)pb.s2max : t2 - kbase;
+        klen = klen < 0 ? 0 : (klen > kcap ? kcap : klen);
         info[r] = i32x4{b, kbase, klen, rb};
     }
 }

@@ -689,7 +689,7 @@ static int blocks_gd() {
 
 hipError_t launch_grad_dense(const Problem &pb, int hp, bool f16, int grid, hipStream_t stream) {
     const int d = pb.d;
-    if (hp <= 64) return launch_grad_dense8(pb, hp, f16, grid, stream);
+    if (hp <= 64) return launch_grad_dense8(pb, hp, f16, grid, false, stream);
     SLIKL_GD_CASES(launch_gd, pb, grid, stream);
     return hipErrorInvalidValue;
 }

@@ -143,7 +143,9 @@ struct UnitInputs {
     float pv[TOPK_PER_THREAD];
 };
 
-template <int HP, int D, bool F16>
+// SREC: instead of the dense records, per-slot records for the key-sorted dK strategy
+// (srec_key / srec_dI / srec_mask at [unit, position], srec_cnt[unit]).
+template <int HP, int D, bool F16, bool SREC>
 __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
     using C = DenseFwdCfg<HP, D>;
     constexpr int NH = C::NH, NQT = C::NQT, NDT = C::NDT, NKS = C::NKS, DCH = C::DCH, NL = C::NL;
@@ -381,7 +383,7 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
 
         // ---- dense records of the unit (stores behind the first copies) ---------------
         int eq = 0;
-        if constexpr (!F16) {
+        if constexpr (!F16 && !SREC) {
             eq = pow2_exponent_below_2p15(qmax);
             const float qsc = ldexpf(1.f, eq);
 #pragma unroll
@@ -401,14 +403,17 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
             }
         }
         // dI fixed-point exponent: |sum of dI over the slots naming one key| <= 1 + sum|p|
-        int ed;
-        {
+        int ed = 0;
+        if constexpr (!SREC) {
             int ex;
             frexpf(1.f + psum, &ex);     // 1 + psum < 2^ex
             ed = 30 - ex;
             ed = ed < -60 ? -60 : ed;
         }
         // w of the unit as fp16 hi and lo parts of w 2^ew (|w 2^ew| < 2^15; zero past G)
+        if constexpr (SREC) {
+            if (tid == 0) pb.srec_cnt[u] = nvalid;
+        } else {
         const int ew = pow2_exponent_below_2p15(wabs);
         uint8_t *const wrec = pb.wrec + (size_t)u * wrec_bytes(HP);
         if (tid < HP) {
@@ -440,6 +445,7 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
             const int z1 = z1e < klen ? z1e : klen;
             int32_t *drow = pb.dI_map + (size_t)u * pb.s2max;
             for (int j = z0 + tid; j < z1; j += kBlock8) drow[j] = 0;
+        }
         }
 
         // w of the heads this lane's pass-1 tile elements belong to: 16 hq + 4 grp + i
@@ -566,8 +572,8 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
             for (int dt = 0; dt < NDT; ++dt)
                 toff[sec][dt] = stage_off<DCH>(8 * half + 4 * sec + (l16 >> 2), 32 * dt + 16 * (grp & 1) + 4 * (l16 & 3));
         const float dfix = ldexpf(1.f, ed);
-        int32_t *dimap = pb.dI_map + (size_t)u * pb.s2max;
-        uint32_t *mmap = pb.mask_map + (size_t)u * pb.s2max * NH;
+        int32_t *dimap = SREC ? nullptr : pb.dI_map + (size_t)u * pb.s2max;
+        uint32_t *mmap = SREC ? nullptr : pb.mask_map + (size_t)u * pb.s2max * NH;
         f32x16 uacc[NH][NDT];
 #pragma unroll
         for (int ht = 0; ht < NH; ++ht)
@@ -583,7 +589,17 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
                 // wave's MFMA work.  Issued before the next copies, so that the copies
                 // after an awaited one stay the last NL memory operations.
                 const int pr = (s + (lane >> 4)) * 128 + wave * 16 + (lane & 15);
-                if (pr < nvalid) {
+                if (SREC && pr < nvalid) {
+                    // per-slot records: key row, dI, head words
+                    const size_t o = (size_t)u * topk + pr;
+                    pb.srec_key[o] = s_key[pr];
+                    pb.srec_dI[o] = s_I[pr];
+                    if constexpr (NH == 1) {
+                        pb.srec_mask[o] = s_mask[pr];
+                    } else {
+                        *(u32x2 *)(pb.srec_mask + o * 2) = u32x2{s_mask[pr], s_mask[TOPK_MAX + pr]};
+                    }
+                } else if (!SREC && pr < nvalid) {
                     const int jrel = s_key[pr] - kbase;
                     atomicAdd(dimap + jrel, (int32_t)__float2int_rn(s_I[pr] * dfix));
                     if constexpr (NH == 1) {
@@ -734,15 +750,18 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
 }
 
 template <int HP, int D, bool F16>
-static hipError_t launch_gd8(const Problem &pb, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((grad_dense8_kernel<HP, D, F16>), dim3(grid), dim3(kBlock8), 0, stream, pb);
+static hipError_t launch_gd8(const Problem &pb, int grid, bool srec, hipStream_t stream) {
+    if (srec)
+        hipLaunchKernelGGL((grad_dense8_kernel<HP, D, F16, true>), dim3(grid), dim3(kBlock8), 0, stream, pb);
+    else
+        hipLaunchKernelGGL((grad_dense8_kernel<HP, D, F16, false>), dim3(grid), dim3(kBlock8), 0, stream, pb);
     return hipGetLastError();
 }
 
 template <int HP, int D, bool F16>
 static int blocks_gd8() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grad_dense8_kernel<HP, D, F16>, kBlock8, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grad_dense8_kernel<HP, D, F16, false>, kBlock8, 0) != hipSuccess)
         return 0;
     return n;
 }
@@ -759,9 +778,9 @@ static int blocks_gd8() {
         if (hp == 64 && d == 128) return f16 ? FN<64, 128, true>(__VA_ARGS__) : FN<64, 128, false>(__VA_ARGS__);  \
     } while (0)
 
-hipError_t launch_grad_dense8(const Problem &pb, int hp, bool f16, int grid, hipStream_t stream) {
+hipError_t launch_grad_dense8(const Problem &pb, int hp, bool f16, int grid, bool srec, hipStream_t stream) {
     const int d = pb.d;
-    SLIKL_GD8_CASES(dense8::launch_gd8, pb, grid, stream);
+    SLIKL_GD8_CASES(dense8::launch_gd8, pb, grid, srec, stream);
     return hipErrorInvalidValue;
 }
 

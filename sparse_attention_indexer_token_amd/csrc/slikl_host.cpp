@@ -45,6 +45,13 @@ bool dense_fits(const slikl_desc *d) {
            (double)rows_k(d) * d->n2 * d->d * 2.0 < 2147483648.0 && (double)rows_k(d) < 16777216.0;
 }
 
+// The key-sorted dK runs through the eight-wave kernel's slot records (head groups up to
+// 64, key rows within its 14-bit record stride); its bin prefix is one two-level scan.
+bool sorted_fits(const slikl_desc *d) {
+    return head_tile(d->n2 > 0 ? d->n1 / d->n2 : 1) <= 64 && (int64_t)d->n2 * d->d * 2 < 16384 &&
+           slikl::sorted_scan_blocks(rows_k(d) * d->n2) <= 8192;
+}
+
 slikl_status validate(const slikl_desc *d) {
     if (!d) return SLIKL_ERR_NULLPTR;
     if (d->layout_q != SLIKL_LAYOUT_BSND && d->layout_q != SLIKL_LAYOUT_TND) return SLIKL_ERR_PARAM_INVALID;
@@ -52,7 +59,7 @@ slikl_status validate(const slikl_desc *d) {
     if (d->dtype != SLIKL_DTYPE_F16 && d->dtype != SLIKL_DTYPE_BF16) return SLIKL_ERR_PARAM_INVALID;
     if (d->deterministic != 0 && d->deterministic != 1) return SLIKL_ERR_PARAM_INVALID;
     if (d->split_mode != SLIKL_SPLIT_WEIGHTED && d->split_mode != SLIKL_SPLIT_ROWS) return SLIKL_ERR_PARAM_INVALID;
-    if (d->dk_mode < SLIKL_DK_AUTO || d->dk_mode > SLIKL_DK_DENSE) return SLIKL_ERR_PARAM_INVALID;
+    if (d->dk_mode < SLIKL_DK_AUTO || d->dk_mode > SLIKL_DK_SORTED) return SLIKL_ERR_PARAM_INVALID;
     if (d->num_parts < 0 || d->num_parts > SLIKL_MAX_PARTS) return SLIKL_ERR_PARAM_INVALID;
     if (d->batch <= 0 || d->batch > INT32_MAX - 1) return SLIKL_ERR_PARAM_INVALID;
     if (d->n1 < 1 || d->n1 > 128) return SLIKL_ERR_PARAM_INVALID;
@@ -76,6 +83,7 @@ slikl_status validate(const slikl_desc *d) {
     if (t1 > lim / (d->n1 * d->d) || t1 > lim / (d->n2 * d->topk)) return SLIKL_ERR_PARAM_INVALID;
     if (t2 > lim / (d->n2 * d->d)) return SLIKL_ERR_PARAM_INVALID;
     if (d->dk_mode == SLIKL_DK_DENSE && !dense_fits(d)) return SLIKL_ERR_UNSUPPORTED;
+    if (d->dk_mode == SLIKL_DK_SORTED && !sorted_fits(d)) return SLIKL_ERR_UNSUPPORTED;
     return SLIKL_OK;
 }
 
@@ -84,6 +92,7 @@ slikl_status validate(const slikl_desc *d) {
 int dk_strategy(const slikl_desc *d) {
     const bool fits = dense_fits(d);
     if (d->dk_mode == SLIKL_DK_DENSE && fits) return 2;
+    if (d->dk_mode == SLIKL_DK_SORTED) return d->deterministic ? 1 : 0;
     // AUTO: the dense kernels cost about one (row, 128-key block) step per 128 keys of
     // a row's named range (at most S2), the scatter about one atomic row per valid
     // slot, dearer in fixed point (deterministic) and under contention on shared keys:
@@ -96,6 +105,14 @@ int dk_strategy(const slikl_desc *d) {
         if (bytes <= 8.0 * (1ull << 30)) return 2;
     }
     return d->deterministic ? 1 : 0;
+}
+
+// The key-sorted variant of the scatter strategy: every valid slot's part written once
+// as an fp32 row of a buffer sorted by key, then summed per key; asked for explicitly
+// (SORTED) or taken by AUTO where the scatter strategy applies and the buffer fits.
+bool sorted_dk(const slikl_desc *d) {
+    if (d->dk_mode == SLIKL_DK_SORTED) return true;      // validate checked sorted_fits
+    return false;
 }
 
 // Per-unit overhead of the WEIGHTED split for the resolved dK strategy.
@@ -168,6 +185,31 @@ slikl::WorkspacePlan plan(const slikl_desc *d) {
         p.rowinfo_off = off;
         off = align_up(off + (any_tnd(d) ? (size_t)t1 * 16 : 0));
     }
+    if (mode != 2 && sorted_dk(d)) {
+        const size_t nslot = U * (size_t)d->topk;
+        const size_t nh = (size_t)head_tile(d->n1 / d->n2) / 32;
+        p.srec_key_off = off;
+        off = align_up(off + nslot * 4);
+        p.srec_dI_off = off;
+        off = align_up(off + nslot * 4);
+        p.srec_mask_off = off;
+        off = align_up(off + nslot * nh * 4);
+        p.srec_cnt_off = off;
+        off = align_up(off + U * 4);
+        const size_t nbins = (size_t)t2 * (size_t)d->n2;
+        p.sorted = true;
+        p.srec_pos_off = off;
+        off = align_up(off + nslot * 4);
+        p.bin_off = off;
+        p.bin_bytes = (nbins + 1) * 4;
+        off = align_up(off + p.bin_bytes);
+        p.binblk_off = off;
+        off = align_up(off + (size_t)slikl::sorted_scan_blocks((int64_t)nbins) * 4);
+        p.sorted_off = off;
+        off = align_up(off + nslot * (size_t)d->d * 4);
+        p.rowinfo_off = off;
+        off = align_up(off + (any_tnd(d) ? (size_t)t1 * 16 : 0));
+    }
     p.total = off;
     return p;
 }
@@ -205,8 +247,8 @@ slikl_status resolve_parts(const slikl_desc *d, int32_t *parts) {
     const int mode = dk_strategy(d);
     const int hp = head_tile(d->n1 / d->n2);
     const bool f16 = d->dtype == SLIKL_DTYPE_F16;
-    int per_cu = mode == 2 ? slikl::grad_dense_blocks_per_cu(hp, (int)d->d, f16)
-                           : slikl::grad_fused_blocks_per_cu(hp, (int)d->d, f16, mode);
+    int per_cu = mode == 2 || sorted_dk(d) ? slikl::grad_dense_blocks_per_cu(hp, (int)d->d, f16)
+                                          : slikl::grad_fused_blocks_per_cu(hp, (int)d->d, f16, mode);
     int64_t p = (int64_t)cus * per_cu;
     if (p > SLIKL_MAX_PARTS) p = SLIKL_MAX_PARTS;
     if (p < 1) p = 1;
@@ -250,6 +292,14 @@ slikl_status slikl_grad_unit_overhead(const slikl_desc *desc, int32_t *overhead)
     slikl_status st = validate(desc);
     if (st != SLIKL_OK) return st;
     *overhead = unit_overhead(desc);
+    return SLIKL_OK;
+}
+
+slikl_status slikl_grad_dk_strategy(const slikl_desc *desc, int32_t *strategy) {
+    if (!desc || !strategy) return SLIKL_ERR_NULLPTR;
+    slikl_status st = validate(desc);
+    if (st != SLIKL_OK) return st;
+    *strategy = dk_strategy(desc) == 2 ? SLIKL_DK_DENSE : sorted_dk(desc) ? SLIKL_DK_SORTED : SLIKL_DK_SCATTER;
     return SLIKL_OK;
 }
 
@@ -358,6 +408,19 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
     pb.k16 = f16 ? pb.k : (const uint16_t *)(ws + wp.k16_off);
     pb.zero16 = (const uint16_t *)(ws + wp.zero_off);
     const int mode = wp.mode;
+    const bool s8 = wp.sorted;          // eight-wave kernel writing slot records
+    if (s8) {
+        pb.srec_key = (int32_t *)(ws + wp.srec_key_off);
+        pb.srec_dI = (float *)(ws + wp.srec_dI_off);
+        pb.srec_mask = (uint32_t *)(ws + wp.srec_mask_off);
+        pb.srec_cnt = (int32_t *)(ws + wp.srec_cnt_off);
+        pb.srec_pos = (int32_t *)(ws + wp.srec_pos_off);
+        pb.bin_start = (int32_t *)(ws + wp.bin_off);
+        pb.bin_blk = (int32_t *)(ws + wp.binblk_off);
+        pb.dk_sorted = (float *)(ws + wp.sorted_off);
+        pb.s2max = t2;                  // no record width: key lengths are not clamped
+        pb.rowinfo = any_tnd(desc) ? (const slikl::i32x4 *)(ws + wp.rowinfo_off) : nullptr;
+    }
     if (mode == 2) {
         pb.dI_map = (int32_t *)(ws + wp.dimap_off);
         pb.mask_map = (uint32_t *)(ws + wp.maskmap_off);
@@ -406,8 +469,9 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
         zr.add(ws + wp.scale_off, 64);
         zr.add(ws + wp.zero_off, 256);
         if (mode == 2) zr.add(pb.kb_diff, wp.kbdiff_bytes);
+        if (wp.sorted) zr.add(pb.bin_start, wp.bin_bytes);
         e = slikl::launch_zero_ranges(zr, s);
-        if (e == hipSuccess && mode == 2 && pb.rowinfo)
+        if (e == hipSuccess && pb.rowinfo)
             e = slikl::launch_rowinfo(pb, (slikl::i32x4 *)pb.rowinfo, s);
     }
     pe.end(SLIKL_PHASE_FILL);
@@ -427,9 +491,18 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
     if (t1 > 0) {
         pe.begin(SLIKL_PHASE_FUSED);
         e = mode == 2 ? slikl::launch_grad_dense(pb, head_tile(pb.group), f16, parts, s)
+            : s8      ? slikl::launch_grad_dense8(pb, head_tile(pb.group), f16, parts, true, s)
                       : slikl::launch_grad_fused(pb, head_tile(pb.group), f16, mode, parts, s);
         pe.end(SLIKL_PHASE_FUSED);
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
+        if (s8) {
+            pe.begin(SLIKL_PHASE_DK);
+            e = slikl::launch_sorted_prepare(pb, s);
+            if (e == hipSuccess) e = slikl::launch_scatter_dk(pb, head_tile(pb.group), f16, s);
+            if (e == hipSuccess) e = slikl::launch_sorted_reduce(pb, mode == 1, s);
+            pe.end(SLIKL_PHASE_DK);
+            if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
+        }
     }
     if (mode == 2) {
         pe.begin(SLIKL_PHASE_DK);

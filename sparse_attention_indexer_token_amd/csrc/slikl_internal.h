@@ -50,6 +50,21 @@ struct Problem {
     // dense strategy with a TND side: per query row {batch, key base, key length
     // (at most s2max), row within its batch}; null for BSND (computed in place)
     const i32x4 *rowinfo;
+    // key-sorted strategy (eight-wave kernel): per (unit, valid position) the key row, dI
+    // and the S > 0 head words ([U, topk], [U, topk], [U, topk, HP/32]) and per unit the
+    // valid count
+    int32_t *srec_key;
+    float *srec_dI;
+    uint32_t *srec_mask;
+    int32_t *srec_cnt;
+    // key-sorted dK (no atomics on the slot parts): per record its
+    // rank inside its bin (key row * N2 + key head), then its row in dk_sorted; per bin
+    // the count, then the exclusive prefix ([T2 * N2 + 1]); scan block sums; the parts
+    // as fp32 rows of D sorted by bin
+    int32_t *srec_pos;
+    int32_t *bin_start;
+    int32_t *bin_blk;
+    float *dk_sorted;
     const int32_t *cu_q;     // [batch + 1] or null (BSND)
     const int32_t *cu_k;     // [batch + 1] or null (BSND)
     int64_t s1, s2;          // BSND per-batch lengths (unused for TND sides)
@@ -71,7 +86,10 @@ struct WorkspacePlan {
     int mode;                       // dK strategy (see launch_grad_fused)
     size_t dimap_off, dimap_bytes, maskmap_off, range_off, q16_off, wrec_off, part_off;
     size_t kbdiff_off, kbdiff_bytes, tasks_off, kbtasks_off, ntasks_off;
-    size_t rowinfo_off;             // dense with a TND side: i32x4 per query row
+    size_t rowinfo_off;             // dense or sorted with a TND side: i32x4 per query row
+    size_t srec_key_off, srec_dI_off, srec_mask_off, srec_cnt_off;   // sorted: slot records
+    bool sorted;                    // key-sorted dK (no atomics on the slot parts)
+    size_t srec_pos_off, bin_off, bin_bytes, binblk_off, sorted_off;
     int dk_nkb, dk_chunk, dk_nch, dk_max_tasks;
     size_t total;
 };
@@ -86,7 +104,16 @@ int grad_fused_blocks_per_cu(int hp, int d, bool f16, int mode);
 hipError_t launch_grad_dense(const Problem &pb, int hp, bool f16, int grid, hipStream_t stream);
 int grad_dense_blocks_per_cu(int hp, int d, bool f16);
 // eight-wave variant for head groups of up to 64 (called by the two above)
-hipError_t launch_grad_dense8(const Problem &pb, int hp, bool f16, int grid, hipStream_t stream);
+hipError_t launch_grad_dense8(const Problem &pb, int hp, bool f16, int grid, bool srec, hipStream_t stream);
+// scatter dK from the eight-wave kernel's per-slot records (head groups up to 64)
+// dK parts of the key-sorted strategy from the eight-wave kernel's slot records
+// (head groups up to 64), stored into dk_sorted
+hipError_t launch_scatter_dk(const Problem &pb, int hp, bool f16, hipStream_t stream);
+// key-sorted dK: bin counts, prefix and record rows (before the scatter dK kernel), and
+// the per-bin sums into dk_acc (after it); scan blocks needed for a number of bins
+int sorted_scan_blocks(int64_t nbins);
+hipError_t launch_sorted_prepare(const Problem &pb, hipStream_t stream);
+hipError_t launch_sorted_reduce(const Problem &pb, bool det, hipStream_t stream);
 int grad_dense8_blocks_per_cu(int hp, int d, bool f16);
 hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t stream);
 // Up to 8 byte ranges (16-byte aligned starts, sizes multiples of 4) zeroed by one launch.

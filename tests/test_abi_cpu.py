@@ -113,7 +113,7 @@ def test_dense_mode_with_tnd_needs_the_maxima(lib):
     ("layout_q", 2, 2), ("layout_k", -1, 2), ("dtype", 5, 2), ("deterministic", 2, 2),
     ("batch", 0, 2), ("s1", 0, 2), ("s2", 0, 2), ("n1", 0, 2), ("n1", 129, 2),
     ("n2", 3, 2), ("n2", 0, 2), ("d", 96, 2), ("d", 256, 2), ("topk", 0, 2), ("topk", 2049, 2),
-    ("num_parts", 2049, 2), ("num_parts", -1, 2), ("split_mode", 2, 2), ("dk_mode", 3, 2),
+    ("num_parts", 2049, 2), ("num_parts", -1, 2), ("split_mode", 2, 2), ("dk_mode", 4, 2),
     ("layout_q", 1, 1),                      # TND q without cu_seqlens_q
     ("layout_k", 1, 1),                      # TND k without cu_seqlens_k
     ("s1", 1 << 40, 2),                      # more than 2^31 elements
@@ -164,6 +164,34 @@ def test_unit_overhead_follows_the_dk_strategy(lib):
     out = ctypes.c_int32(0)
     assert lib.slikl_grad_unit_overhead(None, ctypes.byref(out)) == 1
     assert lib.slikl_grad_unit_overhead(ctypes.byref(good_desc()), None) == 1
+
+
+def test_dk_strategy_query_resolves_auto(lib):
+    def strat(d):
+        out = ctypes.c_int32(-1)
+        st = lib.slikl_grad_dk_strategy(ctypes.byref(d), ctypes.byref(out))
+        return st, out.value
+    assert strat(good_desc()) == (0, 2)                        # dsv32 shape: dense
+    assert strat(good_desc(topk=128)) == (0, 1)                # S2 > 16 topk: scatter
+    assert strat(good_desc(dk_mode=1)) == (0, 1)
+    assert strat(good_desc(dk_mode=3)) == (0, 3)
+    assert strat(good_desc(dk_mode=3, deterministic=1)) == (0, 3)
+    # sorted needs head groups of at most 64 (n1 / n2 = 128 is not)
+    assert strat(good_desc(dk_mode=3, n1=128))[0] == 3
+    assert strat(good_desc(dk_mode=3, n1=128, n2=2)) == (0, 3)
+    cu = (ctypes.c_int32 * 2)(0, 4096)
+    assert strat(tnd_desc(cu, dk_mode=3)) == (0, 3)            # no maxima needed
+    assert strat(tnd_desc(cu)) == (0, 1)
+    assert lib.slikl_grad_dk_strategy(None, ctypes.byref(ctypes.c_int32(0))) == 1
+    assert lib.slikl_grad_dk_strategy(ctypes.byref(good_desc()), None) == 1
+
+
+def test_sorted_mode_workspace_holds_the_parts(lib):
+    st, n_sc = ws(lib, good_desc(dk_mode=1))
+    st2, n_so = ws(lib, good_desc(dk_mode=3))
+    assert st == 0 and st2 == 0
+    slots = 4096 * 2048
+    assert n_so - n_sc >= slots * (128 * 4 + 4)                # fp32 rows of D + positions
 
 
 def test_small_workspace_is_rejected_before_launch(lib):

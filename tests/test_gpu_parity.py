@@ -60,7 +60,12 @@ SMALL = {
 }
 
 
-DK_MODES = [("scatter", False), ("scatter", True), ("dense", False)]
+DK_MODES = [("scatter", False), ("scatter", True), ("dense", False), ("sorted", False), ("sorted", True)]
+
+
+def _head_tile(wl):
+    g = wl.n1 // wl.n2
+    return 32 if g <= 32 else 64 if g <= 64 else 128
 
 
 @pytest.mark.parametrize("name", list(SMALL))
@@ -68,6 +73,11 @@ DK_MODES = [("scatter", False), ("scatter", True), ("dense", False)]
 def test_small_parity(name, dk_mode, det):
     x = make_inputs(SMALL[name])
     _say(f"[parity] {name} dk_mode={dk_mode} det={det}")
+    if dk_mode == "sorted" and _head_tile(SMALL[name]) > 64:
+        from sparse_attention_indexer_token_amd._native import SliklError
+        with pytest.raises(SliklError):       # head groups over 64: UNSUPPORTED
+            run_gpu(x, deterministic=det, dk_mode=dk_mode)
+        return
     got = run_gpu(x, deterministic=det, dk_mode=dk_mode)
     ref = oracle(x)
     check_close(got, ref, label=name)
@@ -121,7 +131,7 @@ def test_results_do_not_depend_on_metadata():
     torch.cuda.synchronize()
 
 
-@pytest.mark.parametrize("dk_mode", ["scatter", "dense"])
+@pytest.mark.parametrize("dk_mode", ["scatter", "dense", "sorted"])
 def test_deterministic_mode_is_bitwise_reproducible(dk_mode):
     import torch
     x = make_inputs(SMALL["sink_zipf_small"])
@@ -139,7 +149,7 @@ def test_deterministic_mode_is_bitwise_reproducible(dk_mode):
     check_close(first, run_gpu(x, t, deterministic=False, dk_mode="scatter"), what=("dk",))
 
 
-@pytest.mark.parametrize("dk_mode", ["scatter", "dense"])
+@pytest.mark.parametrize("dk_mode", ["scatter", "dense", "sorted"])
 def test_slot_order_and_padding_invariance(dk_mode):
     """Permuting the slots (with -1 padding interleaved) permutes softmax_out and
     leaves dq, dk, dw within tolerance (the fp16 rounding of dS may move by an
@@ -199,7 +209,7 @@ def test_tnd_sequence_longer_than_its_given_maximum_is_flagged():
     assert int(md_ok[8].item()) & 8 == 0
 
 
-@pytest.mark.parametrize("dk_mode", ["scatter", "dense"])
+@pytest.mark.parametrize("dk_mode", ["scatter", "dense", "sorted"])
 def test_profiled_call_matches_and_times_phases(dk_mode):
     import torch
     import sparse_attention_indexer_token_amd as slikl
@@ -214,7 +224,9 @@ def test_profiled_call_matches_and_times_phases(dk_mode):
     for name in got:
         assert np.array_equal(got[name], base[name]), name
     assert ms["fused"] > 0 and ms["dk_final"] > 0 and ms["metadata"] > 0
-    assert (ms["dk"] > 0) == (dk_mode == "dense")
+    # a separate dK phase runs in the dense (key-major kernel) and sorted (slot parts
+    # sorted by key, then summed per key) strategies; scatter adds dK inside the fused kernel
+    assert (ms["dk"] > 0) == (dk_mode != "scatter")
 
 
 FULL = ["tiny_causal", "dsv32_indexer", "long_context", "contention_det", "varlen_tnd"]
