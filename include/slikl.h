@@ -72,14 +72,16 @@ enum { SLIKL_SPLIT_WEIGHTED = 0, SLIKL_SPLIT_ROWS = 1 };
  * with the maxima max_seqlen_q / max_seqlen_k given) writes per (query row, key)
  * records and runs a key-major kernel that sums over query rows in registers: no
  * atomics, bitwise reproducible; it pays off when the top-k lists cover a fair
- * share of each batch's keys.  With L the key length per batch (S2, or
- * max_seqlen_k for TND), AUTO picks DENSE when L <= 16 topk (L <= 32 topk when
- * deterministic), there are at least 2048 units and the records fit in 8 GiB,
- * SCATTER otherwise.  SORTED (head groups N1/N2 up to 64 and N2*D*2 < 16384 bytes,
- * else UNSUPPORTED) writes each valid slot's dK part once (fp32) into a buffer
- * sorted by key (workspace: D*4 + 4 bytes per (unit, slot) more) and sums each
- * key's run: atomics only where a run is split between two waves; deterministic mode
- * sums in int64 fixed point, so its result is bitwise reproducible. */
+ * share of each batch's keys.  SORTED (head groups N1/N2 up to 64 and
+ * N2*D*2 < 16384 bytes, else UNSUPPORTED) writes each valid slot's dK part once
+ * (fp32) into a buffer (workspace: about D*4 + 16 bytes per (unit, slot) more) and
+ * sums each key's parts through a key-sorted list of them: no atomics on hot keys
+ * (global atomics only where a key's run is split between two waves); deterministic
+ * mode sums in int64 fixed point, so its result is bitwise reproducible.  With L the
+ * key length per batch (S2, or max_seqlen_k for TND), AUTO picks DENSE when
+ * L <= 16 topk (L <= 32 topk when deterministic), there are at least 2048 units and
+ * the records fit in 8 GiB; else SORTED when it is supported, there are at least 2048
+ * units and its parts fit in 8 GiB; else SCATTER. */
 enum { SLIKL_DK_AUTO = 0, SLIKL_DK_SCATTER = 1, SLIKL_DK_DENSE = 2, SLIKL_DK_SORTED = 3 };
 
 /* Metadata array (int32, SLIKL_METADATA_INTS entries).  A "unit" is one
@@ -98,8 +100,8 @@ enum { SLIKL_DK_AUTO = 0, SLIKL_DK_SCATTER = 1, SLIKL_DK_DENSE = 2, SLIKL_DK_SOR
 /* Fixed cost of one unit in valid-slot equivalents for the WEIGHTED split
  * (loads, compaction, softmax and epilogue latency of a unit vs the per-slot
  * cost of the two key passes, measured on MI355X): SLIKL_UNIT_OVERHEAD for the
- * SCATTER dK strategy, SLIKL_UNIT_OVERHEAD_DENSE for DENSE, whose per-slot key
- * passes are cheaper relative to its per-unit work. */
+ * SCATTER dK strategy, SLIKL_UNIT_OVERHEAD_DENSE for DENSE and SORTED, whose fused
+ * kernels' per-slot key passes are cheaper relative to their per-unit work. */
 #define SLIKL_UNIT_OVERHEAD 512
 #define SLIKL_UNIT_OVERHEAD_DENSE 1024
 
@@ -143,8 +145,9 @@ slikl_status slikl_grad_workspace_size(const slikl_desc *desc, size_t *bytes);
 slikl_status slikl_grad_parts(const slikl_desc *desc, int32_t *parts);
 
 /* Per-unit overhead (valid-slot equivalents) the WEIGHTED split uses for
- * `desc`: SLIKL_UNIT_OVERHEAD_DENSE when the resolved dK strategy is DENSE,
- * else SLIKL_UNIT_OVERHEAD.  Host only.  PARAM_INVALID / UNSUPPORTED as
+ * `desc`: SLIKL_UNIT_OVERHEAD_DENSE when the resolved dK strategy is DENSE or
+ * SORTED (which runs the dense strategy's eight-wave fused kernel), else
+ * SLIKL_UNIT_OVERHEAD.  Host only.  PARAM_INVALID / UNSUPPORTED as
  * slikl_grad_workspace_size; NULLPTR for a null argument. */
 slikl_status slikl_grad_unit_overhead(const slikl_desc *desc, int32_t *overhead);
 

@@ -17,11 +17,13 @@
 //   slots   chunks of 32 per wave (32x32x16 MFMA, k = 16 heads): A = the head-masked
 //           w parts (rows = slots), two MFMAs per head step and d tile give P' (rows =
 //           slots, columns = d), scaled in fp32 by the slot's dI and 2^-(eq + ew) and
-//           stored (fp32) as row pos[s] of the key-sorted buffer (pos from the bin
-//           counting and prefix passes), whose per-key runs a reduction sums.
-//           Neighbouring lanes swap one value so that each store writes a pair of
-//           consecutive d of one row.  The next chunk's records are loaded while the
-//           current one computes.
+//           stored (fp32) as row o = unit * topk + position of the parts buffer (the
+//           slots of a chunk are consecutive rows); a reduction sums the rows of each
+//           key through the key-sorted record list.  Neighbouring lanes swap one value
+//           so that each store writes a pair of consecutive d of one row.
+//   records the unit's head words and dI are staged in LDS at the unit's start, every
+//           load issued before the first wait (one memory latency per unit, not one
+//           per chunk).
 #include "device_common.h"
 #include "slikl_internal.h"
 
@@ -31,6 +33,19 @@ namespace {
 
 constexpr int kSdWaves = 4;
 constexpr int kSdBlock = 64 * kSdWaves;
+constexpr int kSdTopkMax = 2048;
+
+typedef __attribute__((address_space(3))) void lds_void_sd;
+
+// vmcnt(0) with the other counters left alone (gfx9 s_waitcnt encoding)
+__device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
+
+// the value of the neighbouring lane (lane ^ 1), a DPP quad permute [1, 0, 3, 2]
+__device__ __forceinline__ float swap_pair(float x) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
+}
+
+constexpr uint32_t kSdPadOffset = 0x80000000u;      // past the end of every buffer view
 
 }  // namespace
 
@@ -39,8 +54,14 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
     constexpr int NH = HP / 32;      // head words per slot
     constexpr int NKH = HP / 16;     // 16-head k-steps (32x32x16 MFMA)
     constexpr int NDT = D / 32;      // 32-wide d tiles
-    __shared__ __attribute__((aligned(16))) uint16_t s_qt[D * HP];     // fp16 q 2^eq, [d][head]
+    // fp16 q 2^eq as [d][head], rows padded by 4 heads: the B-operand reads (lane = d row)
+    // then fall on distinct LDS banks instead of a bank every 64 or 128 bytes
+    constexpr int QS = HP + 4;
+    __shared__ __attribute__((aligned(16))) uint16_t s_qt[D * QS];
     __shared__ float s_red[2 * kSdWaves];
+    // the unit's slot records (head words, dI), staged once per unit
+    __shared__ uint32_t s_mw[kSdTopkMax * NH];
+    __shared__ float s_dI[kSdTopkMax];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, half = lane >> 5;
@@ -52,18 +73,45 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
         const int r = u / pb.n2, g = u - r * pb.n2;
         const uint16_t *qrow = pb.q + ((size_t)r * pb.n1 + g * G) * D;
         const float *wrow = pb.w + (size_t)r * pb.n1 + g * G;
+        const size_t ubase = (size_t)u * topk;
 
-        // ---- max |q| and max |w| of the unit (order-independent) ------------------------
-        constexpr int QPT = (HP * D + kSdBlock - 1) / kSdBlock;
-        auto qval = [&](int e) {            // q element e of the [HP][D] tile, 0 past G
-            const bool ok = e < HP * D && e / D < G;
-            const uint16_t bits = ok ? qrow[e] : (uint16_t)0;
-            return F16 ? (float)__builtin_bit_cast(_Float16, bits) : __uint_as_float((uint32_t)bits << 16);
-        };
+        // ---- the unit's records straight into LDS (4-byte buffer loads, 256 bytes per wave
+        //      instruction, range-checked: lanes past the valid count read zeros) ------------
+        {
+            const __amdgpu_buffer_rsrc_t rdI =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(pb.srec_dI + ubase), (short)0, cnt * 4, 0x00020000);
+            const __amdgpu_buffer_rsrc_t rmw =
+                __builtin_amdgcn_make_buffer_rsrc((void *)(pb.srec_mask + ubase * NH), (short)0, cnt * NH * 4, 0x00020000);
+            const int nc = (cnt + 63) / 64;
+            for (int c = wave; c < nc; c += kSdWaves)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rdI, (lds_void_sd *)(s_dI + c * 64), 4,
+                                                         (uint32_t)(c * 64 + lane) * 4, 0, 0, 0);
+            for (int c = wave; c < nc * NH; c += kSdWaves)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rmw, (lds_void_sd *)(s_mw + c * 64), 4,
+                                                         (uint32_t)(c * 64 + lane) * 4, 0, 0, 0);
+        }
+
+        // ---- max |q| and max |w| of the unit (order-independent).  Loads are unconditional
+        //      on clamped in-range addresses (a guarded load would become a branch and a
+        //      wait of its own); q as 16-byte vectors kept for the LDS copy ------------------
+        constexpr int QV = HP * D / 8;                       // 8-element vectors of the tile
+        constexpr int QVT = (QV + kSdBlock - 1) / kSdBlock;
+        u32x4 qv[QVT];
         float qm = 0.f;
 #pragma unroll
-        for (int i = 0; i < QPT; ++i) qm = fmaxf(qm, fabsf(qval(tid + kSdBlock * i)));
-        float wm = tid < G ? fabsf(wrow[tid]) : 0.f;
+        for (int i = 0; i < QVT; ++i) {
+            const int v = tid + kSdBlock * i;
+            const bool ok = v < QV && (v * 8) / D < G;
+            const u32x4 x = *(const u32x4 *)(qrow + (ok ? v * 8 : 0));
+            qv[i] = ok ? x : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                qm = fmaxf(qm, fabsf(from16<F16>((uint16_t)(qv[i][c] & 0xffffu))));
+                qm = fmaxf(qm, fabsf(from16<F16>((uint16_t)(qv[i][c] >> 16))));
+            }
+        }
+        const float wt = wrow[tid < G ? tid : 0];
+        float wm = tid < G ? fabsf(wt) : 0.f;
         for (int o = 32; o > 0; o >>= 1) {
             qm = fmaxf(qm, __shfl_xor(qm, o));
             wm = fmaxf(wm, __shfl_xor(wm, o));
@@ -79,13 +127,18 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
         const int ew = pow2_exponent_below_2p15(wm);
         const float qsc = ldexpf(1.f, eq), wsc = ldexpf(1.f, ew);
 
-        // ---- q tile into LDS as [d][head] ----------------------------------------------------
+        // ---- q tile into LDS as [d][head] (vector v: head v*8 / D, d from (v*8) % D) --------
 #pragma unroll
-        for (int i = 0; i < QPT; ++i) {
-            const int e = tid + kSdBlock * i;
-            if (e < HP * D) {
-                const int h = e / D, d = e - h * D;
-                s_qt[d * HP + h] = __builtin_bit_cast(uint16_t, (_Float16)(qval(e) * qsc));
+        for (int i = 0; i < QVT; ++i) {
+            const int v = tid + kSdBlock * i;
+            if (v < QV) {
+                const int h = (v * 8) / D, d0 = (v * 8) % D;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const uint32_t bits = (qv[i][c >> 1] >> (16 * (c & 1))) & 0xffffu;
+                    s_qt[(d0 + c) * QS + h] =
+                        __builtin_bit_cast(uint16_t, (_Float16)(from16<F16>((uint16_t)bits) * qsc));
+                }
             }
         }
         // ---- w parts of this lane's k elements: element e of k-step kh <-> head
@@ -97,47 +150,38 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
 #pragma unroll
             for (int pr = 0; pr < 4; ++pr) {
                 const int h0 = 16 * kh + 8 * (pr >> 1) + 4 * half + 2 * (pr & 1);
-                const float w0 = h0 < G ? wrow[h0] * wsc : 0.f;
-                const float w1 = h0 + 1 < G ? wrow[h0 + 1] * wsc : 0.f;
+                const float x0 = wrow[h0 < G ? h0 : 0], x1 = wrow[h0 + 1 < G ? h0 + 1 : 0];
+                const float w0 = h0 < G ? x0 * wsc : 0.f;
+                const float w1 = h0 + 1 < G ? x1 * wsc : 0.f;
                 const _Float16 a0 = (_Float16)w0, a1 = (_Float16)w1;
                 wh[kh][pr] = (uint32_t)__builtin_bit_cast(uint16_t, a0) |
                              ((uint32_t)__builtin_bit_cast(uint16_t, a1) << 16);
                 wl[kh][pr] = pack2<true>(w0 - (float)a0, w1 - (float)a1);
             }
+        wait_vm_all();            // this wave's record copies have landed in LDS
         __syncthreads();
         // B operands (read from LDS at their use): column d = 32 dt + l32, k elements as
         // above (two runs of 4 heads)
         auto bq = [&](int kh, int dt) {
-            const uint16_t *col = s_qt + (32 * dt + l32) * HP + 16 * kh + 4 * half;
+            const uint16_t *col = s_qt + (32 * dt + l32) * QS + 16 * kh + 4 * half;
             const u32x2 lo = *(const u32x2 *)col, hi = *(const u32x2 *)(col + 8);
             return u32x4{lo.x, lo.y, hi.x, hi.y};
         };
         const float part_mul = ldexpf(1.f, -(eq + ew));
+        // the unit's rows of the parts buffer (slots past the valid count stored nowhere)
+        const __amdgpu_buffer_rsrc_t rparts =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(pb.dk_parts + ubase * D), (short)0, topk * D * 4, 0x00020000);
 
-        // ---- slot chunks: 32 per wave, the next chunk's records loaded ahead --------------
-        const size_t ubase = (size_t)u * topk;
-        uint32_t mw[NH];
-        float dIv;
-        int pv;
-        auto load_chunk = [&](int c0) {
+        // ---- slot chunks: 32 per wave, records from LDS ------------------------------------
+        for (int c0 = wave * 32; c0 < cnt; c0 += 32 * kSdWaves) {
+            uint32_t mw[NH];
             const int p = c0 + l32;
             const bool ok = p < cnt;
-            const size_t o = ubase + (ok ? p : 0);
-            if constexpr (NH == 1) {
-                mw[0] = pb.srec_mask[o];
-            } else {
-                const u32x2 m2 = *(const u32x2 *)(pb.srec_mask + 2 * o);
-                mw[0] = m2.x;
-                mw[1] = m2.y;
-            }
-            const float dl = pb.srec_dI[o];
-            const int pl = pb.srec_pos[o];
-            dIv = ok ? dl : 0.f;
-            pv = ok ? pl : -1;
-        };
-        int c0 = wave * 32;
-        if (c0 < cnt) load_chunk(c0);
-        for (; c0 < cnt; c0 += 32 * kSdWaves) {
+            const int pc = ok ? p : 0;
+#pragma unroll
+            for (int h = 0; h < NH; ++h) mw[h] = ok ? s_mw[pc * NH + h] : 0u;
+            const float dIv = ok ? s_dI[pc] : 0.f;
+            const int pv = ok ? p : -1;
             // A operand: row = slot l32 of the chunk
             u32x4 ah[NKH], al[NKH];
 #pragma unroll
@@ -154,10 +198,9 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
             }
             const float dIs = dIv * part_mul;
             const int pvc = pv;
-            if (c0 + 32 * kSdWaves < cnt) load_chunk(c0 + 32 * kSdWaves);     // next chunk
             // output pair jp = rows 8 (jp/2) + 4 half + 2 (jp%2) + {0, 1} (output element j
             // of 32x32 MFMA sits at row 8 (j/4) + 4 half + j%4); after the swap an even lane
-            // holds the first row, an odd lane the second: its scaled dI and sorted row
+            // holds the first row, an odd lane the second: its scaled dI and parts row
             const int odd = l32 & 1;
             float sdI[8];
             int spos[8];
@@ -178,16 +221,22 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
                 }
 #pragma unroll
                 for (int jp = 0; jp < 8; ++jp) {
-                    const float mine = odd ? pa[2 * jp + 1] : pa[2 * jp];
-                    const float other = __shfl_xor(odd ? pa[2 * jp] : pa[2 * jp + 1], 1);
-                    const float lo = odd ? other : mine, hi = odd ? mine : other;
-                    if (spos[jp] >= 0)
-                        *(float2 *)(pb.dk_sorted + (size_t)spos[jp] * D + 32 * dt + (l32 & ~1)) =
-                            make_float2(lo * sdI[jp], hi * sdI[jp]);
+                    // even lane: own e0 and its neighbour's e0; odd lane: its neighbour's e1
+                    // and own e1.  Selecting between an element and a swapped value (never
+                    // between two neighbouring elements) keeps the select from turning into
+                    // a run-time index into the MFMA result, which compiles to a compare chain
+                    const float e0 = pa[2 * jp], e1 = pa[2 * jp + 1];
+                    const float s0 = swap_pair(e0), s1 = swap_pair(e1);
+                    const float lo = odd ? s1 : e0, hi = odd ? e1 : s0;
+                    const uint32_t off = spos[jp] >= 0
+                                             ? (uint32_t)((spos[jp] * D + 32 * dt + (l32 & ~1)) * 4)
+                                             : kSdPadOffset;
+                    __builtin_amdgcn_raw_buffer_store_b64(
+                        u32x2{__float_as_uint(lo * sdI[jp]), __float_as_uint(hi * sdI[jp])}, rparts, off, 0, 0);
                 }
             }
         }
-        __syncthreads();          // s_qt and s_red are reused by the next unit
+        __syncthreads();          // the LDS arrays are reused by the next unit
     }
 }
 

@@ -57,14 +57,16 @@ struct Problem {
     float *srec_dI;
     uint32_t *srec_mask;
     int32_t *srec_cnt;
-    // key-sorted dK (no atomics on the slot parts): per record its
-    // rank inside its bin (key row * N2 + key head), then its row in dk_sorted; per bin
-    // the count, then the exclusive prefix ([T2 * N2 + 1]); scan block sums; the parts
-    // as fp32 rows of D sorted by bin
-    int32_t *srec_pos;
-    int32_t *bin_start;
-    int32_t *bin_blk;
-    float *dk_sorted;
+    // key-sorted dK (no atomics on the slot parts); record o = unit * topk + position
+    // of a valid slot record, bin = key row * N2 + key head, bucket = bin >> sort_shift:
+    int32_t *sort_hist;      // [nbuckets * nblk + 1] per (bucket, tile) counts, then prefix
+    int32_t *sort_blk;       // scan block sums of sort_hist
+    int32_t *sort_tbin;      // [valid records] bins, grouped by bucket
+    int32_t *sort_trec;      // [valid records] the records, in the same order
+    int32_t *sort_list;      // [valid records] the records sorted by bin
+    int32_t *bin_start;      // [T2 * N2 + 1] first list entry of each bin; [T2 * N2] = total
+    float *dk_parts;         // [U * topk, D] fp32 dK part of record o (valid records only)
+    int32_t sort_shift, sort_nbuckets, sort_tile, sort_nblk;
     const int32_t *cu_q;     // [batch + 1] or null (BSND)
     const int32_t *cu_k;     // [batch + 1] or null (BSND)
     int64_t s1, s2;          // BSND per-batch lengths (unused for TND sides)
@@ -89,7 +91,7 @@ struct WorkspacePlan {
     size_t rowinfo_off;             // dense or sorted with a TND side: i32x4 per query row
     size_t srec_key_off, srec_dI_off, srec_mask_off, srec_cnt_off;   // sorted: slot records
     bool sorted;                    // key-sorted dK (no atomics on the slot parts)
-    size_t srec_pos_off, bin_off, bin_bytes, binblk_off, sorted_off;
+    size_t hist_off, sblk_off, tbin_off, trec_off, list_off, bin_off, parts_off;
     int dk_nkb, dk_chunk, dk_nch, dk_max_tasks;
     size_t total;
 };
@@ -107,11 +109,19 @@ int grad_dense_blocks_per_cu(int hp, int d, bool f16);
 hipError_t launch_grad_dense8(const Problem &pb, int hp, bool f16, int grid, bool srec, hipStream_t stream);
 // scatter dK from the eight-wave kernel's per-slot records (head groups up to 64)
 // dK parts of the key-sorted strategy from the eight-wave kernel's slot records
-// (head groups up to 64), stored into dk_sorted
+// (head groups up to 64), stored into dk_parts
 hipError_t launch_scatter_dk(const Problem &pb, int hp, bool f16, hipStream_t stream);
-// key-sorted dK: bin counts, prefix and record rows (before the scatter dK kernel), and
-// the per-bin sums into dk_acc (after it); scan blocks needed for a number of bins
-int sorted_scan_blocks(int64_t nbins);
+// key-sorted dK: the bucket sort of the records by bin (list and bin starts), and the
+// per-bin sums into dk_acc (after the parts are written)
+constexpr int kSortShiftMax = 14;                       // at most 16384 bins per bucket
+constexpr int kSortBinsPerBucketMax = 1 << kSortShiftMax;
+constexpr int kSortBucketsMax = 4096;
+constexpr int kSortTilesMax = 1024;
+struct SortGeometry {
+    int shift, nbuckets, tile, nblk, scan_nb;
+    int64_t hist_n;          // nbuckets * nblk
+};
+SortGeometry sorted_geometry(int64_t nslot, int64_t nbins);
 hipError_t launch_sorted_prepare(const Problem &pb, hipStream_t stream);
 hipError_t launch_sorted_reduce(const Problem &pb, bool det, hipStream_t stream);
 int grad_dense8_blocks_per_cu(int hp, int d, bool f16);

@@ -1,21 +1,28 @@
 // Key-sorted dK of the scatter strategy for gfx950: the bookkeeping around the scatter
-// dK kernel's SORT variant and the final per-key sums.
+// dK kernel and the final per-key sums.
 //
 // Follows the formula section of the operator page "aclnnSparseLightningIndexerKLLossGrad":
 // dK is the scatter-add of every valid slot's part dS^T q into the key row that
-// sparseIndices names.  Instead of adding the parts with atomics, each part is written
-// once (fp32, D values) into a buffer sorted by bin = key row * N2 + key head, and the
-// bins are then summed run by run:
-//   count   per valid slot record o, rank[o] = its place in its bin (returning atomics
-//           on the bin counters; the order inside a bin is arbitrary);
-//   scan    exclusive prefix of the counters, in place: start[bin], start[bins] = total;
-//   fill    rank[o] += start[bin of o]: the record's row in the sorted buffer;
-//   (scatter dK writes part o to that row)
-//   reduce  the sorted rows split evenly over the waves; each wave sums its rows bin by
-//           bin in fp32 (int64 fixed point when deterministic: exact, so the sum does
-//           not depend on the order of a bin's rows), stores bins it holds whole and
-//           adds the two it may share with its neighbours with atomics.
-// Bins no slot names stay at the accumulator's zero.
+// sparseIndices names.  Instead of adding the parts with atomics, the scatter dK kernel
+// writes part o (o = unit * topk + position of a valid slot record) as fp32 row o of a
+// parts buffer, and the rows are summed per bin = key row * N2 + key head through a list
+// of the records sorted by bin:
+//   bucket count    records cut into tiles; per tile a histogram over key buckets
+//                   (bin >> shift) in LDS, written as column `tile` of [bucket][tile];
+//   scan            exclusive prefix of that matrix in bucket-major order (so each
+//                   bucket's records are contiguous, each tile's inside its bucket);
+//   bucket scatter  per tile, each record takes a place in its bucket's range by an LDS
+//                   atomic (bin, record) -> tmp;
+//   bucket sort     one workgroup per bucket: an LDS histogram over its bins, its prefix
+//                   -> start[bin], then each record placed by an LDS atomic -> list.
+//   reduce          the sorted list split evenly over the waves; each wave gathers its
+//                   rows and sums them bin by bin in fp32 (int64 fixed point when
+//                   deterministic: exact, so the sum does not depend on the order of a
+//                   bin's records), stores bins it holds whole and adds the two it may
+//                   share with its neighbours with atomics.
+// No global atomic sits on a hot address: bins named by many slots cost LDS atomics in
+// one workgroup.  The order of the records inside a bin is arbitrary.  Bins no slot names
+// stay at the accumulator's zero.
 #include "device_common.h"
 #include "slikl_internal.h"
 
@@ -26,34 +33,7 @@ namespace {
 constexpr int kScanThreads = 1024;
 constexpr int kScanPer = 8;
 constexpr int kScanBlock = kScanThreads * kScanPer;    // counters per scan block
-
-// Returning atomics are latency bound: each thread keeps kCountIlp of them in flight.
-constexpr int kCountIlp = 4;
-
-__global__ __launch_bounds__(256) void sort_count_kernel(Problem pb) {
-    const int U = (int)(pb.t1 * pb.n2), n2 = pb.n2;
-    for (int u = blockIdx.x; u < U; u += gridDim.x) {
-        const int cnt = pb.srec_cnt[u];
-        const int g = u % n2;
-        const size_t base = (size_t)u * pb.topk;
-        for (int p0 = threadIdx.x; p0 < cnt; p0 += 256 * kCountIlp) {
-            int key[kCountIlp], rank[kCountIlp];
-#pragma unroll
-            for (int i = 0; i < kCountIlp; ++i) {
-                const int p = p0 + 256 * i;
-                key[i] = p < cnt ? pb.srec_key[base + p] : -1;
-            }
-#pragma unroll
-            for (int i = 0; i < kCountIlp; ++i)
-                rank[i] = key[i] >= 0 ? atomicAdd(pb.bin_start + (size_t)key[i] * n2 + g, 1) : 0;
-#pragma unroll
-            for (int i = 0; i < kCountIlp; ++i) {
-                const int p = p0 + 256 * i;
-                if (p < cnt) pb.srec_pos[base + p] = rank[i];
-            }
-        }
-    }
-}
+constexpr int kSortThreads = 1024;
 
 // Block sums of kScanBlock counters each.
 __global__ __launch_bounds__(kScanThreads) void scan_sums_kernel(const int32_t *cnt, int n, int32_t *blk) {
@@ -107,24 +87,90 @@ __global__ __launch_bounds__(kScanThreads) void scan_apply_kernel(int32_t *cnt, 
     }
 }
 
-__global__ __launch_bounds__(256) void sort_fill_kernel(Problem pb) {
-    const int U = (int)(pb.t1 * pb.n2), n2 = pb.n2;
-    for (int u = blockIdx.x; u < U; u += gridDim.x) {
-        const int cnt = pb.srec_cnt[u];
-        const int g = u % n2;
-        const size_t base = (size_t)u * pb.topk;
-        for (int p = threadIdx.x; p < cnt; p += 256) {
-            const int key = pb.srec_key[base + p];
-            pb.srec_pos[base + p] += pb.bin_start[(size_t)key * n2 + g];
+// The bin of record o, or -1 past its unit's valid count.
+__device__ __forceinline__ int record_bin(const Problem &pb, int64_t o) {
+    const int u = (int)(o / pb.topk), p = (int)(o - (int64_t)u * pb.topk);
+    if (p >= pb.srec_cnt[u]) return -1;
+    return pb.srec_key[o] * pb.n2 + u % pb.n2;
+}
+
+__global__ __launch_bounds__(kSortThreads) void bucket_count_kernel(Problem pb) {
+    __shared__ int h[kSortBucketsMax];
+    const int nbk = pb.sort_nbuckets, tile = pb.sort_tile, nblk = pb.sort_nblk, sh = pb.sort_shift;
+    for (int i = threadIdx.x; i < nbk; i += kSortThreads) h[i] = 0;
+    __syncthreads();
+    const int64_t nslot = pb.t1 * pb.n2 * pb.topk;
+    const int64_t o0 = (int64_t)blockIdx.x * tile;
+    const int64_t o1 = o0 + tile < nslot ? o0 + tile : nslot;
+    for (int64_t o = o0 + threadIdx.x; o < o1; o += kSortThreads) {
+        const int bin = record_bin(pb, o);
+        if (bin >= 0) atomicAdd(&h[bin >> sh], 1);
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < nbk; i += kSortThreads) pb.sort_hist[(size_t)i * nblk + blockIdx.x] = h[i];
+}
+
+__global__ __launch_bounds__(kSortThreads) void bucket_scatter_kernel(Problem pb) {
+    __shared__ int c[kSortBucketsMax];
+    const int nbk = pb.sort_nbuckets, tile = pb.sort_tile, nblk = pb.sort_nblk, sh = pb.sort_shift;
+    for (int i = threadIdx.x; i < nbk; i += kSortThreads) c[i] = pb.sort_hist[(size_t)i * nblk + blockIdx.x];
+    __syncthreads();
+    const int64_t nslot = pb.t1 * pb.n2 * pb.topk;
+    const int64_t o0 = (int64_t)blockIdx.x * tile;
+    const int64_t o1 = o0 + tile < nslot ? o0 + tile : nslot;
+    for (int64_t o = o0 + threadIdx.x; o < o1; o += kSortThreads) {
+        const int bin = record_bin(pb, o);
+        if (bin >= 0) {
+            const int at = atomicAdd(&c[bin >> sh], 1);
+            pb.sort_tbin[at] = bin;
+            pb.sort_trec[at] = (int32_t)o;
         }
+    }
+}
+
+// One workgroup per bucket: bin starts and the sorted record list.
+__global__ __launch_bounds__(kSortThreads) void bucket_sort_kernel(Problem pb, int nbins) {
+    __shared__ int h[kSortBinsPerBucketMax];
+    __shared__ int tmp[kSortThreads / 64];
+    const int bk = blockIdx.x, sh = pb.sort_shift, nblk = pb.sort_nblk;
+    const int per = 1 << sh;
+    const int base = bk << sh;
+    const int nloc = nbins - base < per ? nbins - base : per;
+    const int r0 = pb.sort_hist[(size_t)bk * nblk];
+    const int r1 = pb.sort_hist[(size_t)(bk + 1) * nblk];      // index nbuckets * nblk holds the total
+    for (int i = threadIdx.x; i < per; i += kSortThreads) h[i] = 0;
+    __syncthreads();
+    for (int r = r0 + threadIdx.x; r < r1; r += kSortThreads) atomicAdd(&h[pb.sort_tbin[r] - base], 1);
+    __syncthreads();
+    // exclusive prefix of the bin counts: thread t owns bins [t * run, (t + 1) * run)
+    const int run = (per + kSortThreads - 1) / kSortThreads;
+    const int b0 = threadIdx.x * run;
+    int s = 0;
+    for (int i = 0; i < run; ++i) s += b0 + i < per ? h[b0 + i] : 0;
+    int total = 0;
+    int acc = block_excl_scan<kSortThreads / 64>(s, tmp, &total);
+    __syncthreads();                      // every count read before the prefix overwrites it
+    for (int i = 0; i < run; ++i) {
+        if (b0 + i < per) {
+            const int v = h[b0 + i];
+            h[b0 + i] = acc;
+            if (b0 + i < nloc) pb.bin_start[base + b0 + i] = r0 + acc;
+            acc += v;
+        }
+    }
+    if (bk == (int)gridDim.x - 1 && threadIdx.x == 0) pb.bin_start[nbins] = r1;
+    __syncthreads();
+    for (int r = r0 + threadIdx.x; r < r1; r += kSortThreads) {
+        const int at = atomicAdd(&h[pb.sort_tbin[r] - base], 1);
+        pb.sort_list[r0 + at] = pb.sort_trec[r];
     }
 }
 
 constexpr int kRedWaves = 4;
 constexpr int kRedUnroll = 16;
 
-// One wave per contiguous run of sorted rows; lane l holds d = 2l, 2l + 1 (lanes past
-// D/2 idle).
+// One wave per contiguous run of the sorted list; lane l holds d = 2l, 2l + 1 of the
+// rows it names (lanes past D/2 idle).
 template <int D, bool DET>
 __global__ __launch_bounds__(64 * kRedWaves) void sorted_reduce_kernel(Problem pb, int nbins) {
     const int lane = threadIdx.x & 63;
@@ -185,12 +231,23 @@ __global__ __launch_bounds__(64 * kRedWaves) void sorted_reduce_kernel(Problem p
         }
     };
 
-    const float2 *rows = (const float2 *)pb.dk_sorted;
+    const float2 *rows = (const float2 *)pb.dk_parts;
+    const int32_t *list = pb.sort_list;
+    // list entries (wave-uniform) of the next batch are loaded while this batch's rows
+    // are in flight
+    int on[kRedUnroll];
+#pragma unroll
+    for (int i = 0; i < kRedUnroll; ++i) on[i] = r0 + i < r1 ? list[r0 + i] : 0;
     for (int r = r0; r < r1; r += kRedUnroll) {
         float2 v[kRedUnroll];
 #pragma unroll
         for (int i = 0; i < kRedUnroll; ++i)
-            v[i] = act && r + i < r1 ? rows[(size_t)(r + i) * (D / 2) + lane] : make_float2(0.f, 0.f);
+            v[i] = act && r + i < r1 ? rows[(size_t)on[i] * (D / 2) + lane] : make_float2(0.f, 0.f);
+#pragma unroll
+        for (int i = 0; i < kRedUnroll; ++i) {
+            const int rn = r + kRedUnroll + i;
+            on[i] = rn < r1 ? list[rn] : 0;
+        }
 #pragma unroll
         for (int i = 0; i < kRedUnroll; ++i) {
             const int rr = r + i;
@@ -227,22 +284,38 @@ int device_cus() {
 
 }  // namespace
 
-int sorted_scan_blocks(int64_t nbins) { return (int)((nbins + kScanBlock - 1) / kScanBlock); }
+SortGeometry sorted_geometry(int64_t nslot, int64_t nbins) {
+    SortGeometry g{};
+    int lg = 0;
+    while (((int64_t)1 << lg) < nbins) ++lg;
+    g.shift = lg > 10 ? lg - 10 : 0;                                  // about 1024 buckets
+    if (g.shift > kSortShiftMax) g.shift = kSortShiftMax;
+    g.nbuckets = (int)((nbins + ((int64_t)1 << g.shift) - 1) >> g.shift);
+    int64_t tile = (nslot + kSortTilesMax - 1) / kSortTilesMax;      // at most 1024 tiles
+    if (tile < 16384) tile = 16384;
+    g.tile = (int)tile;
+    g.nblk = (int)((nslot + tile - 1) / tile);
+    const int64_t n = (int64_t)g.nbuckets * g.nblk;
+    g.hist_n = n;
+    g.scan_nb = (int)((n + kScanBlock - 1) / kScanBlock);
+    return g;
+}
 
 hipError_t launch_sorted_prepare(const Problem &pb, hipStream_t stream) {
-    const int cus = device_cus();
-    if (cus <= 0) return hipErrorInvalidDevice;
-    const int64_t U = pb.t1 * pb.n2;
+    const int64_t nslot = pb.t1 * pb.n2 * pb.topk;
     const int64_t nbins = pb.t2 * pb.n2;
-    if (U <= 0 || nbins <= 0) return hipSuccess;
-    const int nb = sorted_scan_blocks(nbins);
-    if (nb > kScanBlock) return hipErrorInvalidValue;
-    const unsigned grid = (unsigned)(U < (int64_t)cus * 16 ? U : (int64_t)cus * 16);
-    hipLaunchKernelGGL(sort_count_kernel, dim3(grid), dim3(256), 0, stream, pb);
-    hipLaunchKernelGGL(scan_sums_kernel, dim3(nb), dim3(kScanThreads), 0, stream, pb.bin_start, (int)nbins, pb.bin_blk);
-    hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(kScanThreads), 0, stream, pb.bin_blk, nb);
-    hipLaunchKernelGGL(scan_apply_kernel, dim3(nb), dim3(kScanThreads), 0, stream, pb.bin_start, (int)nbins, pb.bin_blk);
-    hipLaunchKernelGGL(sort_fill_kernel, dim3(grid), dim3(256), 0, stream, pb);
+    if (nslot <= 0 || nbins <= 0) return hipSuccess;
+    const SortGeometry g = sorted_geometry(nslot, nbins);
+    if (g.nbuckets != pb.sort_nbuckets || g.nblk != pb.sort_nblk || g.nbuckets > kSortBucketsMax ||
+        g.scan_nb > kScanBlock)
+        return hipErrorInvalidValue;
+    const int n = (int)g.hist_n;
+    hipLaunchKernelGGL(bucket_count_kernel, dim3(g.nblk), dim3(kSortThreads), 0, stream, pb);
+    hipLaunchKernelGGL(scan_sums_kernel, dim3(g.scan_nb), dim3(kScanThreads), 0, stream, pb.sort_hist, n, pb.sort_blk);
+    hipLaunchKernelGGL(scan_top_kernel, dim3(1), dim3(kScanThreads), 0, stream, pb.sort_blk, g.scan_nb);
+    hipLaunchKernelGGL(scan_apply_kernel, dim3(g.scan_nb), dim3(kScanThreads), 0, stream, pb.sort_hist, n, pb.sort_blk);
+    hipLaunchKernelGGL(bucket_scatter_kernel, dim3(g.nblk), dim3(kSortThreads), 0, stream, pb);
+    hipLaunchKernelGGL(bucket_sort_kernel, dim3(g.nbuckets), dim3(kSortThreads), 0, stream, pb, (int)nbins);
     return hipGetLastError();
 }
 
@@ -250,7 +323,7 @@ hipError_t launch_sorted_reduce(const Problem &pb, bool det, hipStream_t stream)
     const int cus = device_cus();
     if (cus <= 0) return hipErrorInvalidDevice;
     const int64_t nbins = pb.t2 * pb.n2;
-    if (pb.t1 * pb.n2 <= 0 || nbins <= 0) return hipSuccess;
+    if (pb.t1 * pb.n2 * pb.topk <= 0 || nbins <= 0) return hipSuccess;
     const dim3 grid((unsigned)cus * 8), block(64 * kRedWaves);
 #define SLIKL_SR_CASE(DV)                                                                                 \
     if (pb.d == DV) {                                                                                     \

@@ -153,13 +153,15 @@ def test_unit_overhead_follows_the_dk_strategy(lib):
     assert oh(good_desc(dk_mode=2)) == (0, _native.UNIT_OVERHEAD_DENSE)
     assert oh(good_desc(dk_mode=1)) == (0, _native.UNIT_OVERHEAD)
     assert oh(good_desc(topk=256)) == (0, _native.UNIT_OVERHEAD_DENSE)     # S2 = 16 topk
-    assert oh(good_desc(topk=128)) == (0, _native.UNIT_OVERHEAD)           # sparser lists: scatter
+    assert oh(good_desc(topk=128)) == (0, _native.UNIT_OVERHEAD_DENSE)     # sparser lists: sorted
+    assert oh(good_desc(topk=128, dk_mode=1)) == (0, _native.UNIT_OVERHEAD)
+    assert oh(good_desc(topk=128, n1=128)) == (0, _native.UNIT_OVERHEAD)   # scatter
     assert oh(good_desc(topk=128, deterministic=1)) == (0, _native.UNIT_OVERHEAD_DENSE)
-    assert oh(good_desc(topk=64, deterministic=1)) == (0, _native.UNIT_OVERHEAD)
+    assert oh(good_desc(topk=64, deterministic=1)) == (0, _native.UNIT_OVERHEAD_DENSE)  # sorted
     cu = (ctypes.c_int32 * 2)(0, 4096)
-    assert oh(tnd_desc(cu)) == (0, _native.UNIT_OVERHEAD)                 # TND without maxima: scatter
+    assert oh(tnd_desc(cu)) == (0, _native.UNIT_OVERHEAD_DENSE)           # TND without maxima: sorted
     assert oh(tnd_desc(cu, max_seqlen_q=4096, max_seqlen_k=4096)) == (0, _native.UNIT_OVERHEAD_DENSE)
-    assert oh(tnd_desc(cu, max_seqlen_q=4096, max_seqlen_k=65536)) == (0, _native.UNIT_OVERHEAD)
+    assert oh(tnd_desc(cu, max_seqlen_q=4096, max_seqlen_k=65536)) == (0, _native.UNIT_OVERHEAD_DENSE)
     assert oh(good_desc(d=96))[0] == 2
     out = ctypes.c_int32(0)
     assert lib.slikl_grad_unit_overhead(None, ctypes.byref(out)) == 1
@@ -172,7 +174,10 @@ def test_dk_strategy_query_resolves_auto(lib):
         st = lib.slikl_grad_dk_strategy(ctypes.byref(d), ctypes.byref(out))
         return st, out.value
     assert strat(good_desc()) == (0, 2)                        # dsv32 shape: dense
-    assert strat(good_desc(topk=128)) == (0, 1)                # S2 > 16 topk: scatter
+    assert strat(good_desc(topk=128)) == (0, 3)                # S2 > 16 topk: sorted
+    assert strat(good_desc(topk=128, n1=128)) == (0, 1)        # head groups over 64: scatter
+    assert strat(good_desc(topk=128, s1=1024)) == (0, 1)       # under 2048 units: scatter
+    assert strat(good_desc(topk=128, deterministic=1)) == (0, 2)   # S2 <= 32 topk
     assert strat(good_desc(dk_mode=1)) == (0, 1)
     assert strat(good_desc(dk_mode=3)) == (0, 3)
     assert strat(good_desc(dk_mode=3, deterministic=1)) == (0, 3)
@@ -181,7 +186,8 @@ def test_dk_strategy_query_resolves_auto(lib):
     assert strat(good_desc(dk_mode=3, n1=128, n2=2)) == (0, 3)
     cu = (ctypes.c_int32 * 2)(0, 4096)
     assert strat(tnd_desc(cu, dk_mode=3)) == (0, 3)            # no maxima needed
-    assert strat(tnd_desc(cu)) == (0, 1)
+    assert strat(tnd_desc(cu)) == (0, 3)                       # no maxima: not dense
+    assert strat(tnd_desc(cu, dk_mode=1)) == (0, 1)
     assert lib.slikl_grad_dk_strategy(None, ctypes.byref(ctypes.c_int32(0))) == 1
     assert lib.slikl_grad_dk_strategy(ctypes.byref(good_desc()), None) == 1
 
