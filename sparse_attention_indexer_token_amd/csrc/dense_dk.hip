@@ -165,12 +165,11 @@ __device__ __forceinline__ void dense_dk_body(const Problem &pb) {
         ai = 0;
         while (nact == 0 && chunk < r1) {
             const int r = chunk + tid;
-            bool act = false;
-            if (r < r1) {
-                const int u = r * pb.n2 + g;
-                const int lo = pb.row_range[2 * u], hi = pb.row_range[2 * u + 1];
-                act = hi >= j0 && lo < j1;
-            }
+            // one unconditional 8-byte load at a clamped unit (a guarded or short-circuit
+            // load compiles to a branch and a wait of its own)
+            const int u = (r < r1 ? r : r0) * pb.n2 + g;
+            const u32x2 rr = *(const u32x2 *)(pb.row_range + 2 * u);
+            const bool act = r < r1 && (int)rr.y >= j0 && (int)rr.x < j1;
             int total;
             const int pos = block_excl_scan<kDkWaves>(act ? 1 : 0, s_cnt, &total);
             if (act) s_rows[pos] = r;
