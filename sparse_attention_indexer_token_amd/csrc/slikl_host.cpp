@@ -113,7 +113,7 @@ int dk_strategy(const slikl_desc *d) {
 // Asked for explicitly (SORTED), or taken by AUTO where the dense strategy is not and
 // there are at least 2048 units (below that its extra launches cost more than the
 // atomics they save) and the parts buffer fits in 8 GiB.  Measured on long_context
-// (S2 = 64 topk): 5.2 ms against 6.9 ms with fp32 atomics, 5.7 against 12.1 ms when
+// (S2 = 64 topk): 5.0 ms against 6.9 ms with fp32 atomics, 5.4 against 12.1 ms when
 // deterministic.
 bool sorted_dk(const slikl_desc *d) {
     if (d->dk_mode == SLIKL_DK_SORTED) return true;      // validate checked sorted_fits
@@ -211,10 +211,8 @@ slikl::WorkspacePlan plan(const slikl_desc *d) {
         off = align_up(off + ((size_t)g.hist_n + 1) * 4);
         p.sblk_off = off;
         off = align_up(off + (size_t)g.scan_nb * 4);
-        p.tbin_off = off;
-        off = align_up(off + nslot * 4);
-        p.trec_off = off;
-        off = align_up(off + nslot * 4);
+        p.tmp_off = off;
+        off = align_up(off + nslot * 8);
         p.list_off = off;
         off = align_up(off + nslot * 4);
         p.bin_off = off;
@@ -431,8 +429,7 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
         const slikl::SortGeometry g = slikl::sorted_geometry(t1 * desc->n2 * desc->topk, t2 * desc->n2);
         pb.sort_hist = (int32_t *)(ws + wp.hist_off);
         pb.sort_blk = (int32_t *)(ws + wp.sblk_off);
-        pb.sort_tbin = (int32_t *)(ws + wp.tbin_off);
-        pb.sort_trec = (int32_t *)(ws + wp.trec_off);
+        pb.sort_tmp = (int32_t *)(ws + wp.tmp_off);
         pb.sort_list = (int32_t *)(ws + wp.list_off);
         pb.bin_start = (int32_t *)(ws + wp.bin_off);
         pb.dk_parts = (float *)(ws + wp.parts_off);

@@ -61,8 +61,7 @@ struct Problem {
     // of a valid slot record, bin = key row * N2 + key head, bucket = bin >> sort_shift:
     int32_t *sort_hist;      // [nbuckets * nblk + 1] per (bucket, tile) counts, then prefix
     int32_t *sort_blk;       // scan block sums of sort_hist
-    int32_t *sort_tbin;      // [valid records] bins, grouped by bucket
-    int32_t *sort_trec;      // [valid records] the records, in the same order
+    int32_t *sort_tmp;       // [valid records, 2] (bin, record) pairs grouped by bucket
     int32_t *sort_list;      // [valid records] the records sorted by bin
     int32_t *bin_start;      // [T2 * N2 + 1] first list entry of each bin; [T2 * N2] = total
     float *dk_parts;         // [U * topk, D] fp32 dK part of record o (valid records only)
@@ -91,7 +90,7 @@ struct WorkspacePlan {
     size_t rowinfo_off;             // dense or sorted with a TND side: i32x4 per query row
     size_t srec_key_off, srec_dI_off, srec_mask_off, srec_cnt_off;   // sorted: slot records
     bool sorted;                    // key-sorted dK (no atomics on the slot parts)
-    size_t hist_off, sblk_off, tbin_off, trec_off, list_off, bin_off, parts_off;
+    size_t hist_off, sblk_off, tmp_off, list_off, bin_off, parts_off;
     int dk_nkb, dk_chunk, dk_nch, dk_max_tasks;
     size_t total;
 };

@@ -12,7 +12,7 @@
 //   scan            exclusive prefix of that matrix in bucket-major order (so each
 //                   bucket's records are contiguous, each tile's inside its bucket);
 //   bucket scatter  per tile, each record takes a place in its bucket's range by an LDS
-//                   atomic (bin, record) -> tmp;
+//                   atomic; (bin, record) pairs -> tmp;
 //   bucket sort     one workgroup per bucket: an LDS histogram over its bins, its prefix
 //                   -> start[bin], then each record placed by an LDS atomic -> list.
 //   reduce          the sorted list split evenly over the waves; each wave gathers its
@@ -87,11 +87,28 @@ __global__ __launch_bounds__(kScanThreads) void scan_apply_kernel(int32_t *cnt, 
     }
 }
 
-// The bin of record o, or -1 past its unit's valid count.
-__device__ __forceinline__ int record_bin(const Problem &pb, int64_t o) {
-    const int u = (int)(o / pb.topk), p = (int)(o - (int64_t)u * pb.topk);
-    if (p >= pb.srec_cnt[u]) return -1;
-    return pb.srec_key[o] * pb.n2 + u % pb.n2;
+// Records per thread and step of the two tile passes: every load of a step is issued
+// before its first use.
+constexpr int kSortIlp = 4;
+
+// The bins of records o, o + kSortThreads, ... (kSortIlp of them), -1 past the tile end or
+// past a unit's valid count.  Record indices fit in 32 bits (U * topk < 2^31).
+__device__ __forceinline__ void record_bins(const Problem &pb, int o, int o1, int (&bin)[kSortIlp]) {
+    int key[kSortIlp], cnt[kSortIlp], u[kSortIlp];
+#pragma unroll
+    for (int i = 0; i < kSortIlp; ++i) {
+        const int oi = o + kSortThreads * i;
+        const int oc = oi < o1 ? oi : o;                        // clamped: loads stay in range
+        u[i] = (int)((unsigned)oc / (unsigned)pb.topk);
+        key[i] = pb.srec_key[oc];
+        cnt[i] = pb.srec_cnt[u[i]];
+    }
+#pragma unroll
+    for (int i = 0; i < kSortIlp; ++i) {
+        const int oi = o + kSortThreads * i;
+        const int p = oi - u[i] * pb.topk;
+        bin[i] = oi < o1 && p < cnt[i] ? key[i] * pb.n2 + u[i] % pb.n2 : -1;
+    }
 }
 
 __global__ __launch_bounds__(kSortThreads) void bucket_count_kernel(Problem pb) {
@@ -99,12 +116,15 @@ __global__ __launch_bounds__(kSortThreads) void bucket_count_kernel(Problem pb) 
     const int nbk = pb.sort_nbuckets, tile = pb.sort_tile, nblk = pb.sort_nblk, sh = pb.sort_shift;
     for (int i = threadIdx.x; i < nbk; i += kSortThreads) h[i] = 0;
     __syncthreads();
-    const int64_t nslot = pb.t1 * pb.n2 * pb.topk;
-    const int64_t o0 = (int64_t)blockIdx.x * tile;
-    const int64_t o1 = o0 + tile < nslot ? o0 + tile : nslot;
-    for (int64_t o = o0 + threadIdx.x; o < o1; o += kSortThreads) {
-        const int bin = record_bin(pb, o);
-        if (bin >= 0) atomicAdd(&h[bin >> sh], 1);
+    const int nslot = (int)(pb.t1 * pb.n2 * pb.topk);
+    const int o0 = blockIdx.x * tile;
+    const int o1 = o0 + tile < nslot ? o0 + tile : nslot;
+    for (int o = o0 + threadIdx.x; o < o1; o += kSortThreads * kSortIlp) {
+        int bin[kSortIlp];
+        record_bins(pb, o, o1, bin);
+#pragma unroll
+        for (int i = 0; i < kSortIlp; ++i)
+            if (bin[i] >= 0) atomicAdd(&h[bin[i] >> sh], 1);
     }
     __syncthreads();
     for (int i = threadIdx.x; i < nbk; i += kSortThreads) pb.sort_hist[(size_t)i * nblk + blockIdx.x] = h[i];
@@ -115,16 +135,18 @@ __global__ __launch_bounds__(kSortThreads) void bucket_scatter_kernel(Problem pb
     const int nbk = pb.sort_nbuckets, tile = pb.sort_tile, nblk = pb.sort_nblk, sh = pb.sort_shift;
     for (int i = threadIdx.x; i < nbk; i += kSortThreads) c[i] = pb.sort_hist[(size_t)i * nblk + blockIdx.x];
     __syncthreads();
-    const int64_t nslot = pb.t1 * pb.n2 * pb.topk;
-    const int64_t o0 = (int64_t)blockIdx.x * tile;
-    const int64_t o1 = o0 + tile < nslot ? o0 + tile : nslot;
-    for (int64_t o = o0 + threadIdx.x; o < o1; o += kSortThreads) {
-        const int bin = record_bin(pb, o);
-        if (bin >= 0) {
-            const int at = atomicAdd(&c[bin >> sh], 1);
-            pb.sort_tbin[at] = bin;
-            pb.sort_trec[at] = (int32_t)o;
-        }
+    const int nslot = (int)(pb.t1 * pb.n2 * pb.topk);
+    const int o0 = blockIdx.x * tile;
+    const int o1 = o0 + tile < nslot ? o0 + tile : nslot;
+    u32x2 *tmp = (u32x2 *)pb.sort_tmp;
+    for (int o = o0 + threadIdx.x; o < o1; o += kSortThreads * kSortIlp) {
+        int bin[kSortIlp], at[kSortIlp];
+        record_bins(pb, o, o1, bin);
+#pragma unroll
+        for (int i = 0; i < kSortIlp; ++i) at[i] = bin[i] >= 0 ? atomicAdd(&c[bin[i] >> sh], 1) : 0;
+#pragma unroll
+        for (int i = 0; i < kSortIlp; ++i)
+            if (bin[i] >= 0) tmp[at[i]] = u32x2{(uint32_t)bin[i], (uint32_t)(o + kSortThreads * i)};
     }
 }
 
@@ -140,7 +162,8 @@ __global__ __launch_bounds__(kSortThreads) void bucket_sort_kernel(Problem pb, i
     const int r1 = pb.sort_hist[(size_t)(bk + 1) * nblk];      // index nbuckets * nblk holds the total
     for (int i = threadIdx.x; i < per; i += kSortThreads) h[i] = 0;
     __syncthreads();
-    for (int r = r0 + threadIdx.x; r < r1; r += kSortThreads) atomicAdd(&h[pb.sort_tbin[r] - base], 1);
+    const u32x2 *pairs = (const u32x2 *)pb.sort_tmp;
+    for (int r = r0 + threadIdx.x; r < r1; r += kSortThreads) atomicAdd(&h[(int)pairs[r].x - base], 1);
     __syncthreads();
     // exclusive prefix of the bin counts: thread t owns bins [t * run, (t + 1) * run)
     const int run = (per + kSortThreads - 1) / kSortThreads;
@@ -161,8 +184,9 @@ __global__ __launch_bounds__(kSortThreads) void bucket_sort_kernel(Problem pb, i
     if (bk == (int)gridDim.x - 1 && threadIdx.x == 0) pb.bin_start[nbins] = r1;
     __syncthreads();
     for (int r = r0 + threadIdx.x; r < r1; r += kSortThreads) {
-        const int at = atomicAdd(&h[pb.sort_tbin[r] - base], 1);
-        pb.sort_list[r0 + at] = pb.sort_trec[r];
+        const u32x2 e = pairs[r];
+        const int at = atomicAdd(&h[(int)e.x - base], 1);
+        pb.sort_list[r0 + at] = (int32_t)e.y;
     }
 }
 

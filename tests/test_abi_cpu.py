@@ -197,7 +197,7 @@ def test_sorted_mode_workspace_holds_the_parts(lib):
     st2, n_so = ws(lib, good_desc(dk_mode=3))
     assert st == 0 and st2 == 0
     slots = 4096 * 2048
-    assert n_so - n_sc >= slots * (128 * 4 + 4)                # fp32 rows of D + positions
+    assert n_so - n_sc >= slots * (128 * 4 + 12)               # fp32 rows of D + sort pairs, list
 
 
 def test_small_workspace_is_rejected_before_launch(lib):
