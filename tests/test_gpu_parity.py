@@ -230,15 +230,19 @@ def test_profiled_call_matches_and_times_phases(dk_mode):
 
 
 FULL = ["tiny_causal", "dsv32_indexer", "long_context", "contention_det", "varlen_tnd"]
+# strategies the default launch does not take at these sizes: fp32 atomics on the long
+# context, the key-sorted sums under the sink keys' contention (deterministic)
+FULL_FORCED = [("long_context", "scatter"), ("contention_det", "sorted")]
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled(name):
-    """Headline workloads at full size, default launch (weighted metadata)."""
+@pytest.mark.parametrize("name,dk_mode", [(n, "auto") for n in FULL] + FULL_FORCED)
+def test_full_size_sampled(name, dk_mode):
+    """Headline workloads at full size, weighted metadata; the library's dK strategy
+    unless forced."""
     _say(f"[full] generating {name}")
     x = make_inputs(WORKLOADS[name])
-    _say(f"[full] running {name} T1={x.t1} valid={x.valid_slots}")
-    got = run_gpu(x)
+    _say(f"[full] running {name} T1={x.t1} valid={x.valid_slots} dk_mode={dk_mode}")
+    got = run_gpu(x, dk_mode=dk_mode)
     rng = np.random.default_rng(11)
     rows = np.sort(rng.choice(x.t1, size=min(24, x.t1), replace=False))
     rows = np.unique(np.concatenate([rows, [0, x.t1 - 1]]))
