@@ -75,6 +75,8 @@ def parse():
     ap.add_argument("--deterministic", type=int, default=None, help="override the workload's mode")
     ap.add_argument("--dk-mode", default="auto", choices=["auto", "scatter", "dense", "sorted"],
                     help="dK strategy (auto: the library's choice)")
+    ap.add_argument("--kl-loss", action="store_true",
+                    help="also write each unit's KL(p || softmax_out) (the loss terms)")
     ap.add_argument("--cpu-rows", type=int, default=4096, help="oracle sample size (rows)")
     ap.add_argument("--profiled-calls", type=int, default=5, help="calls timed per phase")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -158,10 +160,11 @@ def main():
     md = torch.empty(slikl.METADATA_INTS, dtype=torch.int32, device=dev)
     out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(w), torch.empty_like(p))
     stream = torch.cuda.current_stream(dev)
+    gkw = dict(kl_loss=torch.empty(p.shape[:-1], dtype=torch.float32, device=dev)) if args.kl_loss else {}
 
     def step():
         slikl.slikl_grad_metadata(q, k, idx, metadata=md, workspace=ws, **kw)
-        slikl.slikl_grad(q, k, w, idx, p, metadata=md, workspace=ws, out=out, **kw)
+        slikl.slikl_grad(q, k, w, idx, p, metadata=md, workspace=ws, out=out, **kw, **gkw)
 
     for _ in range(args.warmup):
         step()
@@ -176,7 +179,7 @@ def main():
     # timed region
     phases = []
     for _ in range(max(1, args.profiled_calls)):
-        _, ms = slikl.slikl_grad_profiled(q, k, w, idx, p, metadata=md, workspace=ws, out=out, **kw)
+        _, ms = slikl.slikl_grad_profiled(q, k, w, idx, p, metadata=md, workspace=ws, out=out, **kw, **gkw)
         phases.append(ms)
     phase_ms = {name: float(np.mean([ph[name] for ph in phases])) for name in phases[0]}
     T1 = x.t1
@@ -206,7 +209,8 @@ def main():
         "data": "synthetic (seeded generators with the workload's shapes and value recipes)",
         "config": {"workload": wl.name, "layout": wl.layout, "batch": x.batch, "T1": T1,
                    "T2": x.t2, "N1": wl.n1, "N2": wl.n2, "D": wl.d, "topk": wl.topk,
-                   "valid_slots": x.valid_slots, "deterministic": det, "dk_strategy": strategy},
+                   "valid_slots": x.valid_slots, "deterministic": det, "dk_strategy": strategy,
+                   "kl_loss": bool(args.kl_loss)},
         "tflops_nominal_step": flop_nominal / (ms_per_step * 1e-3) / 1e12,
         "tflops_valid_step": flop_valid / (ms_per_step * 1e-3) / 1e12,
         "frac_peak_nominal_step": flop_nominal / (ms_per_step * 1e-3) / 1e12 / peak,

@@ -131,6 +131,13 @@ typedef struct slikl_desc {
      * maximum add nothing to dk, and the metadata pre-pass sets error bit 8. */
     int64_t max_seqlen_q;
     int64_t max_seqlen_k;
+    /* Optional output (device, fp32 [T1, N2], NULL = not computed): per (query row,
+     * key head) unit, the term of the formula section's loss L = sum_t KL(p_t ||
+     * Softmax(I_t)), i.e. sum over the unit's valid slots with p > 0 of
+     * p (log p - log softmaxOut) (0 log 0 = 0, duplicate slots count separately,
+     * 0 for a unit without a valid slot).  Computed in the softmax step of the same
+     * call, in fp32.  Sum it for L. */
+    float *kl_loss;
 } slikl_desc;
 
 /* First phase (the page's "GetWorkspaceSize" step): validate `desc` and return

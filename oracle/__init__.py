@@ -4,5 +4,5 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  It shares no code with the HIP path
 and imports nothing from the product package.
 """
-from .slikl_ref import slikl_grad_ref, kl_loss_ref, unit_backward  # noqa: F401
+from .slikl_ref import slikl_grad_ref, kl_loss_ref, kl_per_unit_ref, unit_backward  # noqa: F401
 from .metadata_ref import metadata_ref  # noqa: F401

@@ -230,3 +230,54 @@ def kl_loss_ref(q, k, w, sparse_indices, p, *, layout_q=BSND, layout_k=BSND,
                 nz = pv > 0
                 total += float(np.sum(pv[nz] * (np.log(pv[nz]) - logy[nz])))
     return total
+
+
+def kl_per_unit_ref(q, k, w, sparse_indices, p, *, layout_q=BSND, layout_k=BSND,
+                    cu_seqlens_q=None, cu_seqlens_k=None, rows=None):
+    """KL(p_u || Softmax(I_u)) of every (query row, key head) unit u, fp64, shaped
+    [T1, N2]: the terms of the formula section's loss L before its sum over tokens.
+    ``rows`` (optional flattened query rows) restricts the work to them (0 elsewhere).
+
+    Per unit: over its valid slots, log y_s = I_s - logsumexp(I); the unit's value is
+    sum of p_s (log p_s - log y_s) over the valid slots with p_s > 0 (0 log 0 = 0;
+    duplicate slots count separately).  A unit with no valid slot gives 0.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    w = np.asarray(w, dtype=np.float64)
+    p = np.asarray(p, dtype=np.float64)
+    idx = np.asarray(sparse_indices, dtype=np.int64)
+    n1, d = q.shape[-2:]
+    n2 = k.shape[-2]
+    G = n1 // n2
+    topk = idx.shape[-1]
+    if layout_q == BSND:
+        n_batch, s1 = q.shape[0], q.shape[1]
+    else:
+        n_batch, s1 = len(cu_seqlens_q) - 1, 0
+    s2 = k.shape[1] if layout_k == BSND else 0
+    qf, kf = q.reshape(-1, n1, d), k.reshape(-1, n2, d)
+    wf, idxf, pf = w.reshape(-1, n1), idx.reshape(-1, n2, topk), p.reshape(-1, n2, topk)
+    out = np.zeros((qf.shape[0], n2))
+    q_rows = _row_table(layout_q, n_batch, s1, cu_seqlens_q)
+    k_rows = _row_table(layout_k, n_batch, s2, cu_seqlens_k)
+    wanted = None if rows is None else set(int(r) for r in rows)
+    for b in range(n_batch):
+        q0, qlen = q_rows[b]
+        k0, _ = k_rows[b]
+        for r in range(q0, q0 + qlen):
+            if wanted is not None and r not in wanted:
+                continue
+            for g in range(n2):
+                heads = slice(g * G, (g + 1) * G)
+                v = np.flatnonzero(idxf[r, g] != -1)
+                if v.size == 0:
+                    continue
+                S = qf[r, heads] @ kf[k0 + idxf[r, g, v], g].T          # eq. S
+                I = wf[r, heads] @ np.maximum(S, 0.0)                    # eq. I
+                top = I.max()
+                logy = I - (top + np.log(np.sum(np.exp(I - top))))       # log Softmax(I)
+                pv = pf[r, g, v]
+                pos = pv > 0
+                out[r, g] = np.sum(pv[pos] * (np.log(pv[pos]) - logy[pos]))
+    return out

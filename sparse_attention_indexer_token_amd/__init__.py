@@ -160,17 +160,20 @@ def slikl_grad(q, k, w, sparse_indices, attn_softmax_l1norm, *, layout_q="BSND",
                cu_seqlens_q=None, cu_seqlens_k=None, deterministic: bool = False,
                metadata=None, num_parts: int = 0, split_mode: str = "weighted",
                dk_mode: str = "auto", max_seqlen_q: int = 0, max_seqlen_k: int = 0,
-               workspace=None, out: Optional[tuple] = None):
+               workspace=None, out: Optional[tuple] = None, kl_loss=None):
     """Backward pass; returns (dq, dk, dw, softmax_out).
 
     ``out`` may hold preallocated (dq, dk, dw, softmax_out); ``workspace`` a
     uint8 device tensor of at least ``slikl_grad_workspace_size`` bytes.
+    ``kl_loss`` (optional fp32 tensor shaped like softmax_out without its last
+    axis) receives each (query row, key head) unit's KL(p || softmax_out); its sum
+    is the loss.
     """
     return _grad(q, k, w, sparse_indices, attn_softmax_l1norm, layout_q=layout_q, layout_k=layout_k,
                  cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, deterministic=deterministic,
                  metadata=metadata, num_parts=num_parts, split_mode=split_mode, dk_mode=dk_mode,
                  max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
-                 workspace=workspace, out=out, profiled=False)[0]
+                 workspace=workspace, out=out, kl_loss=kl_loss, profiled=False)[0]
 
 
 def slikl_grad_profiled(q, k, w, sparse_indices, attn_softmax_l1norm, **kw):
@@ -183,7 +186,7 @@ def _grad(q, k, w, sparse_indices, attn_softmax_l1norm, *, layout_q="BSND", layo
           cu_seqlens_q=None, cu_seqlens_k=None, deterministic: bool = False,
           metadata=None, num_parts: int = 0, split_mode: str = "weighted",
           dk_mode: str = "auto", max_seqlen_q: int = 0, max_seqlen_k: int = 0,
-          workspace=None, out: Optional[tuple] = None, profiled: bool = False):
+          workspace=None, out: Optional[tuple] = None, kl_loss=None, profiled: bool = False):
     torch = _torch()
     desc = make_desc(q, k, sparse_indices, layout_q=layout_q, layout_k=layout_k,
                      cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
@@ -205,6 +208,9 @@ def _grad(q, k, w, sparse_indices, attn_softmax_l1norm, *, layout_q="BSND", layo
             _check_tensor(name, cu, torch.int32, dev, (desc.batch + 1,))
     if metadata is not None:
         _check_tensor("metadata", metadata, torch.int32, dev, (METADATA_INTS,))
+    if kl_loss is not None:
+        _check_tensor("kl_loss", kl_loss, torch.float32, dev, rows + (desc.n2,))
+        desc.kl_loss = kl_loss.data_ptr()
     if out is None:
         dq = torch.empty_like(q)
         dk = torch.empty_like(k)

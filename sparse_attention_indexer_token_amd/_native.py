@@ -46,6 +46,7 @@ class SliklDesc(ctypes.Structure):
         ("cu_seqlens_q", c_void_p), ("cu_seqlens_k", c_void_p),
         ("num_parts", c_int32), ("split_mode", c_int32), ("dk_mode", c_int32),
         ("max_seqlen_q", c_int64), ("max_seqlen_k", c_int64),
+        ("kl_loss", c_void_p),
     ]
 
 

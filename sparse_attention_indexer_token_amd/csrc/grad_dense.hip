@@ -469,17 +469,27 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
         const int p0 = tid * PPT;
         float e[PPT];
         float zl = 0.f;
-        {
-            const float4 a0 = *(const float4 *)(s_I + p0), a1 = *(const float4 *)(s_I + p0 + 4);
-            const float iv8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        const float4 a0 = *(const float4 *)(s_I + p0), a1 = *(const float4 *)(s_I + p0 + 4);
+        const float iv8[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
-            for (int i = 0; i < PPT; ++i) {
-                e[i] = p0 + i < nvalid ? expf(iv8[i] - m) : 0.f;
-                zl += e[i];
-            }
+        for (int i = 0; i < PPT; ++i) {
+            e[i] = p0 + i < nvalid ? expf(iv8[i] - m) : 0.f;
+            zl += e[i];
         }
         const float Z = block_sum(zl, s_red + 8);
         const float invZ = 1.f / Z;
+        if (pb.kl) {
+            // the unit's KL(p || y): p (log p - (I - m - log Z)) over positions with p > 0
+            const float lz = logf(Z);
+            const float4 b0 = *(const float4 *)(s_p + p0), b1 = *(const float4 *)(s_p + p0 + 4);
+            const float pp8[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
+            float kl = 0.f;
+#pragma unroll
+            for (int i = 0; i < PPT; ++i)
+                if (p0 + i < nvalid && pp8[i] > 0.f) kl += pp8[i] * (logf(pp8[i]) - (iv8[i] - m) + lz);
+            kl = block_sum(kl, s_red + 8);
+            if (tid == 0) pb.kl[u] = kl;
+        }
         // |dI| <= max(max y, max p) <= max(1/Z, max p): power-of-two prescale of dI
         // before its fp16 rounding
         const int eds = pow2_exponent_below_2p15(fmaxf(invZ, pmax));

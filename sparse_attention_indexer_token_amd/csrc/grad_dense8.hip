@@ -518,17 +518,27 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
         const int p0 = tid * PPT;
         float e[PPT];
         float zl = 0.f;
-        {
-            const float4 a0 = *(const float4 *)(s_I + p0);
-            const float iv4[4] = {a0.x, a0.y, a0.z, a0.w};
+        const float4 a0 = *(const float4 *)(s_I + p0);
+        const float iv4[4] = {a0.x, a0.y, a0.z, a0.w};
 #pragma unroll
-            for (int i = 0; i < PPT; ++i) {
-                e[i] = p0 + i < nvalid ? expf(iv4[i] - m) : 0.f;
-                zl += e[i];
-            }
+        for (int i = 0; i < PPT; ++i) {
+            e[i] = p0 + i < nvalid ? expf(iv4[i] - m) : 0.f;
+            zl += e[i];
         }
         const float Z = block_sum<NW>(zl, s_red + 2 * NW);
         const float invZ = 1.f / Z;
+        if (pb.kl) {
+            // the unit's KL(p || y): p (log p - (I - m - log Z)) over positions with p > 0
+            const float lz = logf(Z);
+            const float4 b0 = *(const float4 *)(s_p + p0);
+            const float pp4[4] = {b0.x, b0.y, b0.z, b0.w};
+            float kl = 0.f;
+#pragma unroll
+            for (int i = 0; i < PPT; ++i)
+                if (p0 + i < nvalid && pp4[i] > 0.f) kl += pp4[i] * (logf(pp4[i]) - (iv4[i] - m) + lz);
+            kl = block_sum<NW>(kl, s_red + 2 * NW);
+            if (tid == 0) pb.kl[u] = kl;
+        }
         // |dI| <= max(max y, max p) <= max(1/Z, max p): power-of-two prescale of dI
         // before its fp16 rounding
         const int eds = pow2_exponent_below_2p15(fmaxf(invZ, pmax));

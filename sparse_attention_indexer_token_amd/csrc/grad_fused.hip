@@ -272,6 +272,17 @@ __global__ __launch_bounds__(kBlock, (HP == 128 ? 1 : 2)) void grad_fused_kernel
             float zloc = 0.f;
             for (int j = tid; j < nvalid; j += kBlock) zloc += expf(s_I[j] - m);
             const float Z = block_sum(zloc, s_red + 4);
+            if (pb.kl) {
+                // the unit's KL(p || y): p (log p - (I - m - log Z)) over slots with p > 0
+                const float lz = logf(Z);
+                float kl = 0.f;
+                for (int j = tid; j < nvalid; j += kBlock) {
+                    const float pv = prow[s_slot[j]];
+                    if (pv > 0.f) kl += pv * (logf(pv) - (s_I[j] - m) + lz);
+                }
+                kl = block_sum(kl, s_red + 4);
+                if (tid == 0) pb.kl[u] = kl;
+            }
             float amax = 0.f;
             for (int j = tid; j < nchunks * KC; j += kBlock) {
                 float dI = 0.f;

@@ -244,6 +244,7 @@ slikl::Problem problem(const slikl_desc *d) {
     pb.cu_k = d->layout_k == SLIKL_LAYOUT_TND ? d->cu_seqlens_k : nullptr;
     pb.max_q = d->layout_q == SLIKL_LAYOUT_TND ? d->max_seqlen_q : 0;
     pb.max_k = d->layout_k == SLIKL_LAYOUT_TND ? d->max_seqlen_k : 0;
+    pb.kl = d->kl_loss;
     return pb;
 }
 

@@ -24,6 +24,7 @@ struct Problem {
     uint16_t *dk;            // [T2, N2, D]
     float *dw;               // [T1, N1]
     float *y;                // softmax_out [T1, N2, topk]
+    float *kl;               // optional per-unit KL(p || softmax_out) [T1, N2] (null: none)
     void *dk_acc;            // fp32 or int64 accumulator [T2, N2, D]
     const float *det_scale;  // scale block: [0] 2^F, [1] 2^-F (deterministic), [6] 2^-eK
     const uint16_t *k16;     // fp16 keys for the dq / dK-part contractions ([T2, N2, D])

@@ -42,22 +42,29 @@ def max_seqlens(x):
                 max_seqlen_k=mx(x.cu_k) if x.layout_k == "TND" else 0)
 
 
-def run_gpu(x, t=None, **kw):
-    """Call slikl_grad; returns numpy fp32/fp64 arrays (dq, dk, dw, y).  TND sides
-    pass their longest sequence unless the caller gives max_seqlen_q / _k."""
+def run_gpu(x, t=None, kl=False, **kw):
+    """Call slikl_grad; returns numpy fp32/fp64 arrays (dq, dk, dw, y, and with
+    kl=True the per-unit KL output).  TND sides pass their longest sequence unless
+    the caller gives max_seqlen_q / _k."""
     import torch
     import sparse_attention_indexer_token_amd as slikl
     if t is None:
         t = to_device(x)
     for key, val in max_seqlens(x).items():
         kw.setdefault(key, val)
+    if kl:
+        # filled with NaN first: every unit must be written
+        kw["kl_loss"] = torch.full(t["p"].shape[:-1], float("nan"), dtype=torch.float32, device=t["p"].device)
     dq, dk, dw, y = slikl.slikl_grad(
         t["q"], t["k"], t["w"], t["idx"], t["p"], layout_q=x.layout_q, layout_k=x.layout_k,
         cu_seqlens_q=t["cu_q"], cu_seqlens_k=t["cu_k"],
         deterministic=kw.pop("deterministic", x.wl.deterministic), **kw)
     torch.cuda.synchronize()
-    return dict(dq=dq.float().cpu().numpy(), dk=dk.float().cpu().numpy(),
-                dw=dw.cpu().numpy(), softmax_out=y.cpu().numpy())
+    out = dict(dq=dq.float().cpu().numpy(), dk=dk.float().cpu().numpy(),
+               dw=dw.cpu().numpy(), softmax_out=y.cpu().numpy())
+    if kl:
+        out["kl_loss"] = kw["kl_loss"].cpu().numpy()
+    return out
 
 
 def oracle(x, rows=None):

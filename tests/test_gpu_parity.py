@@ -85,6 +85,31 @@ def test_small_parity(name, dk_mode, det):
         assert np.all(got["dq"] == 0) and np.all(got["dk"] == 0) and np.all(got["softmax_out"] == 0)
 
 
+# KL output tolerance per unit: |got - ref| <= 1e-4 (1 + |ref|).  The unit's value
+# moves by sum_s (p_s - y_s) dI_s under errors dI in I, i.e. by at most 2 max |dI|;
+# I comes from fp32-accumulated 16-bit products (relative error ~ D 2^-24 per S,
+# ~1e-5 of |I| at D = 128), and the fp32 logs and the 2048-term fp32 sum add ~1e-5 of
+# the value.
+@pytest.mark.parametrize("name", list(SMALL))
+@pytest.mark.parametrize("dk_mode", ["scatter", "dense", "sorted"])
+def test_kl_loss_output(name, dk_mode):
+    from oracle import kl_per_unit_ref
+    wl = SMALL[name]
+    if dk_mode == "sorted" and _head_tile(wl) > 64:
+        pytest.skip("sorted strategy: head groups up to 64 (UNSUPPORTED checked in test_small_parity)")
+    x = make_inputs(wl)
+    _say(f"[kl] {name} dk_mode={dk_mode}")
+    got = run_gpu(x, kl=True, dk_mode=dk_mode)
+    ref = kl_per_unit_ref(x.q, x.k, x.w, x.idx, x.p, layout_q=x.layout_q, layout_k=x.layout_k,
+                          cu_seqlens_q=x.cu_q, cu_seqlens_k=x.cu_k)
+    g = got["kl_loss"].reshape(ref.shape).astype(np.float64)
+    assert np.all(np.isfinite(g))
+    excess = np.abs(g - ref) - 1e-4 * (1 + np.abs(ref))
+    assert np.max(excess) <= 0, (name, float(np.max(excess)))
+    # the other outputs are unchanged by asking for the loss
+    check_close(got, oracle(x), label=f"{name} with kl")
+
+
 def test_metadata_matches_reference():
     """Integer metadata: bit-exact against the reference split, both modes."""
     import torch
@@ -242,12 +267,18 @@ def test_full_size_sampled(name, dk_mode):
     _say(f"[full] generating {name}")
     x = make_inputs(WORKLOADS[name])
     _say(f"[full] running {name} T1={x.t1} valid={x.valid_slots} dk_mode={dk_mode}")
-    got = run_gpu(x, dk_mode=dk_mode)
+    got = run_gpu(x, dk_mode=dk_mode, kl=True)
     rng = np.random.default_rng(11)
     rows = np.sort(rng.choice(x.t1, size=min(24, x.t1), replace=False))
     rows = np.unique(np.concatenate([rows, [0, x.t1 - 1]]))
     ref = oracle(x, rows=rows)
     check_close(got, ref, rows=rows, what=("dq", "dw", "softmax_out"), label=name)
+    from oracle import kl_per_unit_ref
+    kref = kl_per_unit_ref(x.q, x.k, x.w, x.idx, x.p, layout_q=x.layout_q, layout_k=x.layout_k,
+                           cu_seqlens_q=x.cu_q, cu_seqlens_k=x.cu_k, rows=rows)[rows]
+    kgot = got["kl_loss"].reshape(x.t1, -1)[rows].astype(np.float64)
+    assert np.all(np.isfinite(got["kl_loss"]))
+    assert np.max(np.abs(kgot - kref) - 1e-4 * (1 + np.abs(kref))) <= 0, f"{name} kl_loss"
     refs = keys_with_few_refs(x, max_rows=6, want=24)
     assert refs, "no sparsely referenced keys found"
     all_rows = np.unique(np.concatenate(list(refs.values())))

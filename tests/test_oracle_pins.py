@@ -23,7 +23,7 @@ import numpy as np
 import pytest
 
 from oracle import slikl_ref
-from oracle.slikl_ref import kl_loss_ref, slikl_grad_ref
+from oracle.slikl_ref import kl_loss_ref, kl_per_unit_ref, slikl_grad_ref
 from workloads import Workload, make_inputs
 
 
@@ -44,7 +44,8 @@ def _args(x):
 # Independent formulation: one-hot selection matrices + torch autograd (fp64).
 # ---------------------------------------------------------------------------
 def _torch_loss_and_grads(torch, x):
-    """KL loss through dense one-hot selection; returns (L, dq, dk, dw, y)."""
+    """KL loss through dense one-hot selection; returns (L, dq, dk, dw, y).  The
+    per-unit terms of L are left in x.kl_units ([T1, N2])."""
     q = torch.tensor(x.q, dtype=torch.float64, requires_grad=True)
     k = torch.tensor(x.k, dtype=torch.float64, requires_grad=True)
     w = torch.tensor(x.w, dtype=torch.float64, requires_grad=True)
@@ -68,6 +69,7 @@ def _torch_loss_and_grads(torch, x):
         kstart = [int(c) for c in x.cu_k[:-1]]
     loss = torch.zeros((), dtype=torch.float64)
     ys = np.zeros(idx.shape)
+    units = np.zeros(idx.shape[:2])
     for b in range(len(qstart) - 1):
         for r in range(qstart[b], qstart[b + 1]):
             for g in range(n2):
@@ -85,9 +87,12 @@ def _torch_loss_and_grads(torch, x):
                 logy = torch.log_softmax(I, dim=0)
                 pv = torch.tensor(p[r, g, valid])
                 nz = pv > 0
-                loss = loss + torch.sum(pv[nz] * (torch.log(pv[nz]) - logy[nz]))
+                term = torch.sum(pv[nz] * (torch.log(pv[nz]) - logy[nz]))
+                units[r, g] = float(term.detach())
+                loss = loss + term
                 ys[r, g, valid] = torch.exp(logy).detach().numpy()
     loss.backward()
+    x.kl_units = units
     return (float(loss.detach()), q.grad.numpy(), k.grad.numpy(), w.grad.numpy(),
             ys.reshape(x.p.shape))
 
@@ -123,6 +128,31 @@ def test_autograd_matches(torch_cpu, case):
     assert _rel(ref["dw"], dw) < 1e-10
     assert np.max(np.abs(ref["softmax_out"] - y)) < 1e-12
     assert abs(kl_loss_ref(x.q, x.k, x.w, x.idx, x.p, **_args(x)) - L) < 1e-10 * max(1, abs(L))
+    units = kl_per_unit_ref(x.q, x.k, x.w, x.idx, x.p, **_args(x))
+    assert np.max(np.abs(units - x.kl_units)) < 1e-10 * max(1, np.max(np.abs(x.kl_units)))
+
+
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_kl_per_unit_closed_forms(case):
+    """KL(p || Softmax(I)) per unit: 0 when p is the unit's softmax itself, -log y_s
+    when p is one-hot at slot s, 0 for a unit without a valid slot; the units sum to
+    the total loss."""
+    x = _small(seed=30 + case, **CASES[case])
+    args = _args(x)
+    y = slikl_grad_ref(x.q, x.k, x.w, x.idx, x.p, **args)["softmax_out"]
+    valid = x.idx >= 0
+    same = kl_per_unit_ref(x.q, x.k, x.w, x.idx, y, **args)
+    assert np.max(np.abs(same)) < 1e-12
+    first = np.argmax(valid, axis=-1)[..., None]                 # first valid slot per unit
+    onehot = np.zeros_like(y)
+    np.put_along_axis(onehot, first, 1.0, axis=-1)
+    onehot = np.where(valid.any(-1, keepdims=True), onehot, 0.0)
+    got = kl_per_unit_ref(x.q, x.k, x.w, x.idx, onehot, **args)
+    ys = np.take_along_axis(y, first, axis=-1)[..., 0]
+    want = np.where(valid.any(-1), -np.log(np.where(valid.any(-1), ys, 1.0)), 0.0)
+    assert np.max(np.abs(got.reshape(want.shape) - want)) < 1e-12 * max(1, np.max(np.abs(want)))
+    tot = kl_loss_ref(x.q, x.k, x.w, x.idx, x.p, **args)
+    assert abs(kl_per_unit_ref(x.q, x.k, x.w, x.idx, x.p, **args).sum() - tot) < 1e-10 * max(1, abs(tot))
 
 
 def test_finite_differences():
