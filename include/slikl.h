@@ -138,6 +138,15 @@ typedef struct slikl_desc {
      * 0 for a unit without a valid slot).  Computed in the softmax step of the same
      * call, in fp32.  Sum it for L. */
     float *kl_loss;
+    /* TND sides only (ignored for BSND), optional (device int32 [B], NULL = whole
+     * sequences): the seqUsedQ / seqUsedK inputs of the constraints section, read as
+     * each batch's used length (values clamped to [0, the sequence's length]; a batch
+     * given 0 takes no part).  Query rows past seq_used_q[b] take no part: their dq,
+     * dw, softmaxOut (and kl_loss) are 0 and their indices are not read for errors.
+     * The batch's key range is cut to seq_used_k[b]: an index at or past it is out of
+     * range (skipped, error bit 4). */
+    const int32_t *seq_used_q;
+    const int32_t *seq_used_k;
 } slikl_desc;
 
 /* First phase (the page's "GetWorkspaceSize" step): validate `desc` and return

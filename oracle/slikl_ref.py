@@ -38,6 +38,11 @@ notes):
    top-k list, p and softmaxOut carry the N2 axis: [.., N2, topk].
 9. Out-of-range indices (other than -1) violate the contract: the oracle
    raises.
+10. seqUsedQ / seqUsedK (optional INT32 inputs of the constraints section; their
+    meaning follows the sibling page's convention for TND, where a batch given 0
+    takes no part): per batch of a TND side, the used length (clamped to the
+    sequence's length).  Query rows past it take no part (all their outputs 0);
+    the batch's key range is cut to it (indices past it are out of range).
 """
 from __future__ import annotations
 
@@ -47,6 +52,14 @@ import numpy as np
 
 BSND = "BSND"
 TND = "TND"
+
+
+def _used(rows, layout, used):
+    """Cut each batch's length to its used length (TND side with a used array)."""
+    if used is None or layout != TND:
+        return rows
+    used = np.asarray(used, dtype=np.int64)
+    return [(s0, int(min(n, max(0, used[b])))) for b, (s0, n) in enumerate(rows)]
 
 
 def _row_table(layout: str, n_batch: int, s: int, cu: Optional[np.ndarray]):
@@ -103,7 +116,8 @@ def unit_backward(q_t, k_sel, valid, w_t, p_t):
 
 
 def slikl_grad_ref(q, k, w, sparse_indices, p, *, layout_q=BSND, layout_k=BSND,
-                   cu_seqlens_q=None, cu_seqlens_k=None, rows=None):
+                   cu_seqlens_q=None, cu_seqlens_k=None, rows=None, seq_used_q=None,
+                   seq_used_k=None):
     """Whole-operator oracle.  Arrays are converted to fp64 on entry.
 
     Shapes: q [B,S1,N1,D] | [T1,N1,D]; k [B,S2,N2,D] | [T2,N2,D];
@@ -111,7 +125,8 @@ def slikl_grad_ref(q, k, w, sparse_indices, p, *, layout_q=BSND, layout_k=BSND,
 
     ``rows`` (optional iterable of flattened query rows) restricts the work to
     those rows: the other rows of dq / dw / softmax_out stay 0 and dk holds
-    only those rows' scatter-add terms.
+    only those rows' scatter-add terms.  ``seq_used_q`` / ``seq_used_k``: the
+    used length of each batch of a TND side (reading 10).
 
     Returns a dict with fp64 ``dq``, ``dk``, ``dw``, ``softmax_out`` shaped
     like q, k, w and p.
@@ -146,8 +161,8 @@ def slikl_grad_ref(q, k, w, sparse_indices, p, *, layout_q=BSND, layout_k=BSND,
     pf = p.reshape(-1, n2, topk)
     T1, T2 = qf.shape[0], kf.shape[0]
 
-    q_rows = _row_table(layout_q, n_batch, s1, cu_seqlens_q)
-    k_rows = _row_table(layout_k, n_batch, s2, cu_seqlens_k)
+    q_rows = _used(_row_table(layout_q, n_batch, s1, cu_seqlens_q), layout_q, seq_used_q)
+    k_rows = _used(_row_table(layout_k, n_batch, s2, cu_seqlens_k), layout_k, seq_used_k)
 
     dq = np.zeros_like(qf)
     dk = np.zeros_like(kf)
@@ -233,7 +248,8 @@ def kl_loss_ref(q, k, w, sparse_indices, p, *, layout_q=BSND, layout_k=BSND,
 
 
 def kl_per_unit_ref(q, k, w, sparse_indices, p, *, layout_q=BSND, layout_k=BSND,
-                    cu_seqlens_q=None, cu_seqlens_k=None, rows=None):
+                    cu_seqlens_q=None, cu_seqlens_k=None, rows=None, seq_used_q=None,
+                    seq_used_k=None):
     """KL(p_u || Softmax(I_u)) of every (query row, key head) unit u, fp64, shaped
     [T1, N2]: the terms of the formula section's loss L before its sum over tokens.
     ``rows`` (optional flattened query rows) restricts the work to them (0 elsewhere).
@@ -259,8 +275,8 @@ def kl_per_unit_ref(q, k, w, sparse_indices, p, *, layout_q=BSND, layout_k=BSND,
     qf, kf = q.reshape(-1, n1, d), k.reshape(-1, n2, d)
     wf, idxf, pf = w.reshape(-1, n1), idx.reshape(-1, n2, topk), p.reshape(-1, n2, topk)
     out = np.zeros((qf.shape[0], n2))
-    q_rows = _row_table(layout_q, n_batch, s1, cu_seqlens_q)
-    k_rows = _row_table(layout_k, n_batch, s2, cu_seqlens_k)
+    q_rows = _used(_row_table(layout_q, n_batch, s1, cu_seqlens_q), layout_q, seq_used_q)
+    k_rows = _used(_row_table(layout_k, n_batch, s2, cu_seqlens_k), layout_k, seq_used_k)
     wanted = None if rows is None else set(int(r) for r in rows)
     for b in range(n_batch):
         q0, qlen = q_rows[b]

@@ -43,11 +43,15 @@ def _dtype_code(t) -> int:
 def make_desc(q, k, sparse_indices, *, layout_q: str = "BSND", layout_k: str = "BSND",
               cu_seqlens_q=None, cu_seqlens_k=None, deterministic: bool = False,
               num_parts: int = 0, split_mode: str = "weighted",
-              dk_mode: str = "auto", max_seqlen_q: int = 0, max_seqlen_k: int = 0) -> SliklDesc:
+              dk_mode: str = "auto", max_seqlen_q: int = 0, max_seqlen_k: int = 0,
+              seq_used_q=None, seq_used_k=None) -> SliklDesc:
     """Build the C descriptor from tensor shapes (no device access).
 
     For a TND side, ``max_seqlen_q`` / ``max_seqlen_k`` may give its longest sequence
-    (0 = not given); the dense dK strategy needs them for TND inputs."""
+    (0 = not given); the dense dK strategy needs them for TND inputs.
+    ``seq_used_q`` / ``seq_used_k`` (TND sides, optional int32 [B] device tensors):
+    each batch's used length; rows past it take no part, keys past it are out of
+    range."""
     if layout_q not in LAYOUT or layout_k not in LAYOUT:
         raise ValueError("layouts must be 'BSND' or 'TND'")
     if layout_q == "BSND":
@@ -91,6 +95,14 @@ def make_desc(q, k, sparse_indices, *, layout_q: str = "BSND", layout_k: str = "
     desc.dk_mode = _native.DK_MODE[dk_mode]
     desc.max_seqlen_q = int(max_seqlen_q) if layout_q == "TND" else 0
     desc.max_seqlen_k = int(max_seqlen_k) if layout_k == "TND" else 0
+    for name, t, lay in (("seq_used_q", seq_used_q, layout_q), ("seq_used_k", seq_used_k, layout_k)):
+        if t is None:
+            setattr(desc, name, None)
+            continue
+        if lay != "TND":
+            raise ValueError(f"{name} applies to a TND side only")
+        _check_tensor(name, t, _torch().int32, q.device, (desc.batch,))
+        setattr(desc, name, t.data_ptr())
     return desc
 
 
@@ -135,13 +147,15 @@ def slikl_grad_dk_strategy(desc: SliklDesc) -> str:
 def slikl_grad_metadata(q, k, sparse_indices, *, layout_q="BSND", layout_k="BSND",
                         cu_seqlens_q=None, cu_seqlens_k=None, deterministic=False,
                         num_parts: int = 0, split_mode: str = "weighted", dk_mode: str = "auto",
-                        max_seqlen_q: int = 0, max_seqlen_k: int = 0, metadata=None, workspace=None):
+                        max_seqlen_q: int = 0, max_seqlen_k: int = 0, metadata=None, workspace=None,
+                        seq_used_q=None, seq_used_k=None):
     """Run the load-balancing metadata pre-pass; returns the int32 metadata tensor."""
     torch = _torch()
     desc = make_desc(q, k, sparse_indices, layout_q=layout_q, layout_k=layout_k,
                      cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
                      deterministic=deterministic, num_parts=num_parts, split_mode=split_mode,
-                     dk_mode=dk_mode, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k)
+                     dk_mode=dk_mode, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
+                     seq_used_q=seq_used_q, seq_used_k=seq_used_k)
     dev = q.device
     _check_tensor("sparse_indices", sparse_indices, torch.int32, dev)
     nbytes = _native.workspace_size(desc)
@@ -160,7 +174,8 @@ def slikl_grad(q, k, w, sparse_indices, attn_softmax_l1norm, *, layout_q="BSND",
                cu_seqlens_q=None, cu_seqlens_k=None, deterministic: bool = False,
                metadata=None, num_parts: int = 0, split_mode: str = "weighted",
                dk_mode: str = "auto", max_seqlen_q: int = 0, max_seqlen_k: int = 0,
-               workspace=None, out: Optional[tuple] = None, kl_loss=None):
+               workspace=None, out: Optional[tuple] = None, kl_loss=None,
+               seq_used_q=None, seq_used_k=None):
     """Backward pass; returns (dq, dk, dw, softmax_out).
 
     ``out`` may hold preallocated (dq, dk, dw, softmax_out); ``workspace`` a
@@ -173,7 +188,8 @@ def slikl_grad(q, k, w, sparse_indices, attn_softmax_l1norm, *, layout_q="BSND",
                  cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k, deterministic=deterministic,
                  metadata=metadata, num_parts=num_parts, split_mode=split_mode, dk_mode=dk_mode,
                  max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
-                 workspace=workspace, out=out, kl_loss=kl_loss, profiled=False)[0]
+                 workspace=workspace, out=out, kl_loss=kl_loss, seq_used_q=seq_used_q,
+                 seq_used_k=seq_used_k, profiled=False)[0]
 
 
 def slikl_grad_profiled(q, k, w, sparse_indices, attn_softmax_l1norm, **kw):
@@ -186,12 +202,14 @@ def _grad(q, k, w, sparse_indices, attn_softmax_l1norm, *, layout_q="BSND", layo
           cu_seqlens_q=None, cu_seqlens_k=None, deterministic: bool = False,
           metadata=None, num_parts: int = 0, split_mode: str = "weighted",
           dk_mode: str = "auto", max_seqlen_q: int = 0, max_seqlen_k: int = 0,
-          workspace=None, out: Optional[tuple] = None, kl_loss=None, profiled: bool = False):
+          workspace=None, out: Optional[tuple] = None, kl_loss=None, seq_used_q=None,
+          seq_used_k=None, profiled: bool = False):
     torch = _torch()
     desc = make_desc(q, k, sparse_indices, layout_q=layout_q, layout_k=layout_k,
                      cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
                      deterministic=deterministic, num_parts=num_parts, split_mode=split_mode,
-                     dk_mode=dk_mode, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k)
+                     dk_mode=dk_mode, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
+                     seq_used_q=seq_used_q, seq_used_k=seq_used_k)
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("tensors must be on the GPU")

@@ -47,6 +47,7 @@ class SliklDesc(ctypes.Structure):
         ("num_parts", c_int32), ("split_mode", c_int32), ("dk_mode", c_int32),
         ("max_seqlen_q", c_int64), ("max_seqlen_k", c_int64),
         ("kl_loss", c_void_p),
+        ("seq_used_q", c_void_p), ("seq_used_k", c_void_p),
     ]
 
 

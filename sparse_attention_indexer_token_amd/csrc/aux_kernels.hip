@@ -68,6 +68,7 @@ __global__ void rowinfo_kernel(Problem pb, i32x4 *info) {
         kbase = kbase < 0 ? 0 : (kbase > t2 ? t2 : kbase);
         const int kcap = (int)pb.s2max < t2 - kbase ? (int)pb.s2max : t2 - kbase;
         klen = klen < 0 ? 0 : (klen > kcap ? kcap : klen);
+        klen = used_klen(pb, b, rb, klen);          // used lengths (TND), if given
         info[r] = i32x4{b, kbase, klen, rb};
     }
 }
@@ -302,11 +303,16 @@ __global__ void meta_count_kernel(Problem pb, int64_t *prefix, int overhead, int
             k1 = k1 < k0 ? k0 : (k1 > pb.t2 ? pb.t2 : k1);
             klen = k1 - k0;
         }
+        // used lengths (TND): a row past its batch's used rows counts no slot and
+        // flags nothing; the key range is cut to the used keys
+        const int rb = pb.layout_q == 0 ? (int)(r - (int64_t)b * pb.s1) : (int)(r - pb.cu_q[b]);
+        const bool unused = row_unused(pb, b, rb);
+        klen = used_klen(pb, b, rb, (int)klen);
         const int32_t *row = pb.idx + u * pb.topk;
         int cnt = 0;
         auto tally = [&](int v) {
             if (v >= 0 && v < klen) ++cnt;
-            else if (v != -1) bad = 1;
+            else if (v != -1 && !unused) bad = 1;
         };
         if ((pb.topk & 3) == 0 && ((uintptr_t)row & 15) == 0) {
             // 16-byte loads, all of a lane's issued before any is used

@@ -130,6 +130,10 @@ __global__ __launch_bounds__(kBlock, (HP == 128 ? 1 : 2)) void grad_fused_kernel
                 kbase = k0;
                 klen = k1 - k0;
             }
+            if (pb.used_q || pb.used_k) {        // used lengths (TND)
+                const int rb = pb.layout_q == 0 ? r - b * (int)pb.s1 : r - pb.cu_q[b];
+                klen = used_klen(pb, b, rb, klen);
+            }
 
             // ---- compact the valid slots -------------------------------------------
             const int32_t *irow = pb.idx + u * topk;

@@ -245,6 +245,8 @@ slikl::Problem problem(const slikl_desc *d) {
     pb.max_q = d->layout_q == SLIKL_LAYOUT_TND ? d->max_seqlen_q : 0;
     pb.max_k = d->layout_k == SLIKL_LAYOUT_TND ? d->max_seqlen_k : 0;
     pb.kl = d->kl_loss;
+    pb.used_q = d->layout_q == SLIKL_LAYOUT_TND ? d->seq_used_q : nullptr;
+    pb.used_k = d->layout_k == SLIKL_LAYOUT_TND ? d->seq_used_k : nullptr;
     return pb;
 }
 

@@ -25,6 +25,8 @@ struct Problem {
     float *dw;               // [T1, N1]
     float *y;                // softmax_out [T1, N2, topk]
     float *kl;               // optional per-unit KL(p || softmax_out) [T1, N2] (null: none)
+    const int32_t *used_q;   // TND q: used rows per batch [batch] (null: whole sequences)
+    const int32_t *used_k;   // TND k: used keys per batch [batch] (null: whole sequences)
     void *dk_acc;            // fp32 or int64 accumulator [T2, N2, D]
     const float *det_scale;  // scale block: [0] 2^F, [1] 2^-F (deterministic), [6] 2^-eK
     const uint16_t *k16;     // fp16 keys for the dq / dK-part contractions ([T2, N2, D])
@@ -75,6 +77,22 @@ struct Problem {
     int32_t batch, n1, n2, group, d, topk;
     int32_t layout_q, layout_k;
 };
+
+// A query row (batch b, row rb within it) past its batch's used length takes no part.
+__device__ __forceinline__ bool row_unused(const Problem &pb, int b, int rb) {
+    return pb.used_q != nullptr && rb >= pb.used_q[b];
+}
+
+// Key length the kernels use for such a row: 0 for an unused row (no slot is valid),
+// else the batch's key length cut to its used key length.
+__device__ __forceinline__ int used_klen(const Problem &pb, int b, int rb, int klen) {
+    if (row_unused(pb, b, rb)) return 0;
+    if (pb.used_k != nullptr) {
+        const int uk = pb.used_k[b] < 0 ? 0 : pb.used_k[b];
+        klen = uk < klen ? uk : klen;
+    }
+    return klen;
+}
 
 // Workspace carve-up (byte offsets), identical for every call with one desc.
 struct WorkspacePlan {

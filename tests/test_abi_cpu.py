@@ -46,13 +46,15 @@ def test_library_exports_every_declared_symbol(lib):
 
 def test_struct_layout_matches_header():
     # 4 x int32, 7 x int64, 2 pointers, 3 x int32 (+4 bytes of padding), 2 x int64
-    assert ctypes.sizeof(SliklDesc) == 128
+    assert ctypes.sizeof(SliklDesc) == 144
     assert SliklDesc.cu_seqlens_q.offset == 72
     assert SliklDesc.num_parts.offset == 88
     assert SliklDesc.dk_mode.offset == 96
     assert SliklDesc.max_seqlen_q.offset == 104
     assert SliklDesc.max_seqlen_k.offset == 112
     assert SliklDesc.kl_loss.offset == 120
+    assert SliklDesc.seq_used_q.offset == 128
+    assert SliklDesc.seq_used_k.offset == 136
 
 
 def good_desc(**kw):

@@ -294,3 +294,56 @@ def test_full_size_sampled(name, dk_mode):
     assert np.all(y[~valid] == 0)
     sums = y.sum(-1)[valid.any(-1)]
     assert np.max(np.abs(sums - 1)) < 1e-4
+
+
+@pytest.mark.parametrize("dk_mode", ["scatter", "dense", "sorted"])
+@pytest.mark.parametrize("name", ["g8_d32_tnd", "f16_dirichlet_tnd"])
+def test_seq_used_lengths(name, dk_mode):
+    """seqUsedQ / seqUsedK on TND inputs: rows past a batch's used length take no part
+    (their indices are not flagged), indices past the used keys are skipped and flagged."""
+    import torch
+    import sparse_attention_indexer_token_amd as slikl
+    from oracle import kl_per_unit_ref, slikl_grad_ref
+    x = make_inputs(SMALL[name])
+    nb = len(x.cu_q) - 1
+    lens = np.diff(x.cu_q)
+    used_q = np.array([(l * 2) // 3 if b % 2 == 0 else l for b, l in enumerate(lens)], dtype=np.int32)
+    used_k = np.array([l if b % 2 == 0 else l // 2 for b, l in enumerate(lens)], dtype=np.int32)
+    if nb > 1:
+        used_q[-1] = 0                                   # a batch that takes no part
+    t = to_device(x)
+    uq = torch.from_numpy(used_q).cuda()
+    uk = torch.from_numpy(used_k).cuda()
+    kw = dict(layout_q=x.layout_q, layout_k=x.layout_k, cu_seqlens_q=t["cu_q"], cu_seqlens_k=t["cu_k"],
+              seq_used_q=uq, seq_used_k=uk)
+    cleaned = x.idx.copy()
+    row_b = np.searchsorted(x.cu_q, np.arange(x.t1), side="right") - 1
+    row_in = np.arange(x.t1) - x.cu_q[row_b]
+    for r in range(x.t1):
+        cleaned[r] = np.where(cleaned[r] >= used_k[row_b[r]], -1, cleaned[r])
+    ref = slikl_grad_ref(x.q, x.k, x.w, cleaned, x.p, layout_q=x.layout_q, layout_k=x.layout_k,
+                         cu_seqlens_q=x.cu_q, cu_seqlens_k=x.cu_k, seq_used_q=used_q, seq_used_k=used_k)
+    kref = kl_per_unit_ref(x.q, x.k, x.w, cleaned, x.p, layout_q=x.layout_q, layout_k=x.layout_k,
+                           cu_seqlens_q=x.cu_q, cu_seqlens_k=x.cu_k, seq_used_q=used_q, seq_used_k=used_k)
+    for variant in ("past_used_keys", "garbage_in_unused_rows"):
+        _say(f"[seq_used] {name} dk_mode={dk_mode} {variant}")
+        idx = x.idx.copy()
+        if variant == "garbage_in_unused_rows":
+            idx = cleaned.copy()
+            unused = row_in >= used_q[row_b]
+            idx[unused] = 1_000_000
+        ti = torch.from_numpy(idx).cuda()
+        md = slikl.slikl_grad_metadata(t["q"], t["k"], ti, dk_mode=dk_mode, **max_seqlens(x), **kw)
+        kl = torch.full(t["p"].shape[:-1], float("nan"), dtype=torch.float32, device="cuda")
+        dq, dk, dw, y = slikl.slikl_grad(t["q"], t["k"], t["w"], ti, t["p"], metadata=md, dk_mode=dk_mode,
+                                         kl_loss=kl, **max_seqlens(x), **kw)
+        torch.cuda.synchronize()
+        flagged = bool(int(md[8].item()) & 4)
+        used_rows = row_in < used_q[row_b]
+        past = bool(np.any((cleaned != x.idx)[used_rows]))     # a used row names a key past the used ones
+        assert flagged == (variant == "past_used_keys" and past)
+        got = dict(dq=dq.float().cpu().numpy(), dk=dk.float().cpu().numpy(), dw=dw.cpu().numpy(),
+                   softmax_out=y.cpu().numpy())
+        check_close(got, ref, label=f"{name} {dk_mode} {variant}")
+        kg = kl.cpu().numpy().reshape(kref.shape).astype(np.float64)
+        assert np.max(np.abs(kg - kref) - 1e-4 * (1 + np.abs(kref))) <= 0

@@ -392,3 +392,36 @@ def test_planted_mistakes_are_caught(torch_cpu, monkeypatch, kind):
     out = slikl_ref.slikl_grad_ref(x.q, x.k, x.w, x.idx, x.p, **_args(x))
     worst = max(_rel(out["dq"], dq), _rel(out["dk"], dk), _rel(out["dw"], dw))
     assert worst > 1e-3, kind
+
+
+def test_seq_used_equals_the_cut_problem():
+    """seqUsedQ / seqUsedK (TND): the outputs equal those of the problem built from
+    each batch's used rows and keys only; the other query rows give 0, the other keys
+    get no dK."""
+    x = _small(seed=77, layout="TND", batch=3, seqlens=(5, 1, 8), s1=0, s2=0, topk=6)
+    used_q = np.array([3, 1, 0])
+    used_k = np.array([4, 0, 8])
+    cu = x.cu_q.astype(np.int64)
+    idx = x.idx.copy()
+    for b in range(3):
+        rows = slice(cu[b], cu[b + 1])
+        idx[rows] = np.where(idx[rows] >= used_k[b], -1, idx[rows])    # inside the used keys
+    full = slikl_grad_ref(x.q, x.k, x.w, idx, x.p, layout_q="TND", layout_k="TND",
+                          cu_seqlens_q=cu, cu_seqlens_k=cu, seq_used_q=used_q, seq_used_k=used_k)
+    qr = np.concatenate([np.arange(cu[b], cu[b] + used_q[b]) for b in range(3)]).astype(int)
+    kr = np.concatenate([np.arange(cu[b], cu[b] + used_k[b]) for b in range(3)]).astype(int)
+    cuq = np.concatenate([[0], np.cumsum(used_q)])
+    cuk = np.concatenate([[0], np.cumsum(used_k)])
+    cut = slikl_grad_ref(x.q[qr], x.k[kr], x.w[qr], idx[qr], x.p[qr], layout_q="TND",
+                         layout_k="TND", cu_seqlens_q=cuq, cu_seqlens_k=cuk)
+    for name in ("dq", "dw", "softmax_out"):
+        assert np.array_equal(full[name][qr], cut[name])
+        rest = np.setdiff1d(np.arange(full[name].shape[0]), qr)
+        assert not np.any(full[name][rest])
+    assert np.allclose(full["dk"][kr], cut["dk"], rtol=1e-13, atol=1e-15)
+    assert not np.any(np.delete(full["dk"], kr, axis=0))
+    units = kl_per_unit_ref(x.q, x.k, x.w, idx, x.p, layout_q="TND", layout_k="TND",
+                            cu_seqlens_q=cu, cu_seqlens_k=cu, seq_used_q=used_q, seq_used_k=used_k)
+    units_cut = kl_per_unit_ref(x.q[qr], x.k[kr], x.w[qr], idx[qr], x.p[qr], layout_q="TND",
+                                layout_k="TND", cu_seqlens_q=cuq, cu_seqlens_k=cuk)
+    assert np.allclose(units[qr], units_cut, rtol=1e-13, atol=1e-15)
