@@ -226,3 +226,25 @@ def test_header_constants_match_the_binding():
     assert int(defs["SLIKL_METADATA_INTS"]) == _native.METADATA_INTS
     assert int(defs["SLIKL_UNIT_OVERHEAD"]) == _native.UNIT_OVERHEAD
     assert int(defs["SLIKL_UNIT_OVERHEAD_DENSE"]) == _native.UNIT_OVERHEAD_DENSE
+
+
+def test_seq_used_applies_to_tnd_sides_only():
+    import torch
+    import sparse_attention_indexer_token_amd as slikl
+    q = torch.zeros(1, 8, 4, 32, dtype=torch.bfloat16)
+    k = torch.zeros(1, 8, 1, 32, dtype=torch.bfloat16)
+    idx = torch.zeros(1, 8, 1, 4, dtype=torch.int32)
+    used = torch.zeros(1, dtype=torch.int32)
+    with pytest.raises(ValueError):
+        slikl.make_desc(q, k, idx, seq_used_q=used)          # BSND query side
+    with pytest.raises(ValueError):
+        slikl.make_desc(q, k, idx, seq_used_k=used)          # BSND key side
+    d = slikl.make_desc(q, k, idx)
+    assert d.seq_used_q is None and d.seq_used_k is None and d.kl_loss is None
+
+
+def test_optional_outputs_do_not_change_the_workspace(lib):
+    base = ws(lib, good_desc())
+    d = good_desc()
+    d.kl_loss = 0x1000                  # never dereferenced by the size query
+    assert ws(lib, d) == base
