@@ -241,8 +241,8 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
 }
 
 // The body under the register budget of four workgroups per compute unit (32-head
-// groups with D <= 64), three (32-head groups, D = 128) or two (64-head groups): the
-// most that run without spills.
+// groups with D = 32), three (32-head groups, D = 64 or 128) or two (64-head groups):
+// the most that run without spills.
 template <int HP, int D, bool F16>
 __global__ __launch_bounds__(kSdBlock, 4) void scatter_dk_kernel4(Problem pb) {
     scatter_dk_body<HP, D, F16>(pb);
@@ -265,7 +265,7 @@ static hipError_t launch_sd(const Problem &pb, hipStream_t stream) {
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return hipErrorInvalidDevice;
     auto kern = HP > 32 ? scatter_dk_kernel2<HP, D, F16>
-                : D <= 64 ? scatter_dk_kernel4<HP, D, F16> : scatter_dk_kernel3<HP, D, F16>;
+                : D <= 32 ? scatter_dk_kernel4<HP, D, F16> : scatter_dk_kernel3<HP, D, F16>;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, kSdBlock, 0) != hipSuccess || per <= 0) per = 1;
     const int64_t U = pb.t1 * pb.n2;
     int64_t grid = (int64_t)cus * per;
