@@ -49,6 +49,8 @@ bool dense_fits(const slikl_desc *d) {
 // 64, key rows within its 14-bit record stride); its bin prefix is one two-level scan.
 bool sorted_fits(const slikl_desc *d) {
     if (head_tile(d->n2 > 0 ? d->n1 / d->n2 : 1) > 64 || (int64_t)d->n2 * d->d * 2 >= 16384) return false;
+    // record indices are 32-bit; the sort loops step past the last record by up to 4096
+    if ((double)rows_q(d) * d->n2 * d->topk >= 2147483648.0 - 65536.0) return false;
     const slikl::SortGeometry g = slikl::sorted_geometry(rows_q(d) * d->n2 * d->topk, rows_k(d) * d->n2);
     return g.nbuckets <= slikl::kSortBucketsMax && g.scan_nb <= 8192;
 }

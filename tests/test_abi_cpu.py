@@ -187,6 +187,9 @@ def test_dk_strategy_query_resolves_auto(lib):
     # sorted needs head groups of at most 64 (n1 / n2 = 128 is not)
     assert strat(good_desc(dk_mode=3, n1=128))[0] == 3
     assert strat(good_desc(dk_mode=3, n1=128, n2=2)) == (0, 3)
+    # 32-bit record indices: T1 * N2 * topk below 2^31 - 65536
+    assert strat(good_desc(dk_mode=3, s1=1048576 - 33, topk=2048, n1=1, d=32, s2=64))[0] == 0
+    assert strat(good_desc(dk_mode=3, s1=1048576 - 32, topk=2048, n1=1, d=32, s2=64))[0] == 3
     cu = (ctypes.c_int32 * 2)(0, 4096)
     assert strat(tnd_desc(cu, dk_mode=3)) == (0, 3)            # no maxima needed
     assert strat(tnd_desc(cu)) == (0, 3)                       # no maxima: not dense
