@@ -5,29 +5,6 @@
 
 namespace slikl {
 
-// ---------------------------------------------------------------------------
-// Fill with zeros (a plain kernel rather than a memset node, so the sequence
-// stays valid under stream capture).
-// ---------------------------------------------------------------------------
-__global__ void zero_kernel(u32x4 *p, size_t n16, uint32_t *tail, size_t ntail) {
-    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-    size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (; i < n16; i += stride) p[i] = u32x4{0u, 0u, 0u, 0u};
-    if (blockIdx.x == 0 && threadIdx.x < ntail) tail[threadIdx.x] = 0u;
-}
-
-hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t stream) {
-    if (bytes == 0) return hipSuccess;
-    size_t n16 = bytes / 16;
-    size_t ntail = (bytes - n16 * 16) / 4;
-    size_t blocks = (n16 + 255) / 256;
-    if (blocks > 2048) blocks = 2048;
-    if (blocks == 0) blocks = 1;
-    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (u32x4 *)ptr, n16,
-                       (uint32_t *)((char *)ptr + n16 * 16), ntail);
-    return hipGetLastError();
-}
-
 __global__ void zero_ranges_kernel(ZeroRanges zr) {
     const size_t stride = (size_t)gridDim.x * blockDim.x;
     for (int r = 0; r < zr.n; ++r) {
@@ -285,8 +262,13 @@ hipError_t launch_k_to_f16(const Problem &pb, uint16_t *k16, float *scale_block,
 // exclusive cost prefix and W the total; rows mode gives the first
 // former_num parts ceil(U / P) units and the rest one fewer.
 // ---------------------------------------------------------------------------
+// flags[block] receives the block's error bits (every block writes its word, so the
+// array needs no clearing); the split kernel ORs them.
 __global__ void meta_count_kernel(Problem pb, int64_t *prefix, int overhead, int32_t *flags) {
     const int lane = threadIdx.x & 63;
+    __shared__ int s_bad;
+    if (threadIdx.x == 0) s_bad = 0;
+    __syncthreads();
     const int64_t U = pb.t1 * pb.n2;
     int64_t wv = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6;
     const int64_t nw = ((int64_t)gridDim.x * blockDim.x) >> 6;
@@ -323,8 +305,11 @@ __global__ void meta_count_kernel(Problem pb, int64_t *prefix, int overhead, int
                 int4 v[UNR];
 #pragma unroll
                 for (int j = 0; j < UNR; ++j) {
+                    // unconditional load at a clamped index (a guarded load becomes a
+                    // branch with a wait of its own)
                     const int s = s0 + 64 * j + lane;
-                    v[j] = s < n4 ? r4[s] : int4{-1, -1, -1, -1};
+                    const int4 x = r4[s < n4 ? s : 0];
+                    v[j] = s < n4 ? x : int4{-1, -1, -1, -1};
                 }
 #pragma unroll
                 for (int j = 0; j < UNR; ++j) {
@@ -340,7 +325,9 @@ __global__ void meta_count_kernel(Problem pb, int64_t *prefix, int overhead, int
         for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
         if (lane == 0) prefix[u + 1] = cnt + overhead;
     }
-    if (__any(bad) && lane == 0) atomicOr(flags, 4);
+    if (__any(bad) && lane == 0) atomicOr(&s_bad, 4);
+    __syncthreads();
+    if (threadIdx.x == 0) flags[blockIdx.x] = s_bad;
 }
 
 __device__ __forceinline__ int check_cu(const int32_t *cu, int batch, int64_t total, int64_t maxlen) {
@@ -360,7 +347,7 @@ __device__ __forceinline__ int check_cu(const int32_t *cu, int batch, int64_t to
 
 __global__ __launch_bounds__(1024) void meta_split_kernel(Problem pb, int parts, int mode, int overhead,
                                                           int64_t *prefix, const int32_t *cflags,
-                                                          int32_t *md) {
+                                                          int ncflags, int32_t *md) {
     constexpr int kSplitLds = 65536;
     __shared__ int64_t s_part[1024];
     __shared__ uint16_t s_cost[kSplitLds];
@@ -478,7 +465,10 @@ __global__ __launch_bounds__(1024) void meta_split_kernel(Problem pb, int parts,
     for (int i = tid; i < parts; i += nt) used += bnd[i + 1] > bnd[i];
     for (int o = 32; o > 0; o >>= 1) used += __shfl_xor(used, o);
     if ((tid & 63) == 0) s_used[tid >> 6] = used;
-    __syncthreads();
+    // the counting blocks' error words
+    int cf = 0;
+    for (int i = tid; i < ncflags; i += nt) cf |= cflags[i];
+    cf = __syncthreads_or(cf);
     if (tid == 0) {
         int tot = 0;
         for (int w = 0; w < nt / 64; ++w) tot += s_used[w];
@@ -488,7 +478,7 @@ __global__ __launch_bounds__(1024) void meta_split_kernel(Problem pb, int parts,
         md[5] = (int32_t)mk;
         md[6] = parts;
         md[7] = mode;
-        md[8] = flags | (mode == 0 ? cflags[0] : 0);
+        md[8] = flags | (cf ? 4 : 0);
         md[9] = mode == 0 ? overhead : 0;
         for (int i = 10; i < 16; ++i) md[i] = 0;
     }
@@ -498,18 +488,19 @@ __global__ __launch_bounds__(1024) void meta_split_kernel(Problem pb, int parts,
 hipError_t launch_metadata(const Problem &pb, int parts, int mode, int overhead, int32_t *metadata,
                            int64_t *prefix, int32_t *flags, hipStream_t stream) {
     const int64_t U = pb.t1 * pb.n2;
-    hipError_t e = launch_zero(flags, 16, stream);
-    if (e != hipSuccess) return e;
+    int ncflags = 0;
     if (mode == 0 && U > 0) {
         int64_t waves = U < 65536 ? U : 65536;
         int64_t blocks = (waves * 64 + 255) / 256;
+        if (blocks > kMetaCountBlocksMax) return hipErrorInvalidValue;
         hipLaunchKernelGGL(meta_count_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pb, prefix,
                            overhead, flags);
-        e = hipGetLastError();
+        hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
+        ncflags = (int)blocks;
     }
     hipLaunchKernelGGL(meta_split_kernel, dim3(1), dim3(1024), 0, stream, pb, parts, mode, overhead, prefix,
-                       flags, metadata);
+                       flags, ncflags, metadata);
     return hipGetLastError();
 }
 

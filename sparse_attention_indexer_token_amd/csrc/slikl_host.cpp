@@ -158,7 +158,7 @@ slikl::WorkspacePlan plan(const slikl_desc *d) {
     p.prefix_bytes = (U + 1) * sizeof(int64_t);
     off = align_up(off + p.prefix_bytes);
     p.flags_off = off;
-    off = align_up(off + 16);
+    off = align_up(off + (size_t)slikl::kMetaCountBlocksMax * 4);
     p.scale_off = off;
     off = align_up(off + 64);
     p.zero_off = off;

@@ -99,7 +99,7 @@ struct WorkspacePlan {
     size_t acc_off, acc_bytes;      // dK accumulator
     size_t meta_off;                // internal metadata (SLIKL_METADATA_INTS int32)
     size_t prefix_off, prefix_bytes;// int64 unit-cost prefix, U + 1 entries
-    size_t flags_off;               // metadata error flags found while counting (16 bytes)
+    size_t flags_off;               // metadata error words of the counting blocks (int32 each)
     size_t scale_off;               // scale block (16 x 32-bit)
     size_t k16_off, k16_bytes;      // fp16 copy of k (bf16 inputs only)
     size_t zero_off;                // 256 zero bytes
@@ -143,7 +143,6 @@ SortGeometry sorted_geometry(int64_t nslot, int64_t nbins);
 hipError_t launch_sorted_prepare(const Problem &pb, hipStream_t stream);
 hipError_t launch_sorted_reduce(const Problem &pb, bool det, hipStream_t stream);
 int grad_dense8_blocks_per_cu(int hp, int d, bool f16);
-hipError_t launch_zero(void *ptr, size_t bytes, hipStream_t stream);
 // Up to 8 byte ranges (16-byte aligned starts, sizes multiples of 4) zeroed by one launch.
 struct ZeroRanges {
     void *ptr[8];
@@ -168,6 +167,7 @@ constexpr int kDkSlotsMax = 1024;   // cap on concurrently resident dK workgroup
 hipError_t launch_finalize_dk(const Problem &pb, bool f16, bool det, hipStream_t stream);
 hipError_t launch_det_scale(const Problem &pb, bool f16, float *scale_block, hipStream_t stream);
 hipError_t launch_k_to_f16(const Problem &pb, uint16_t *k16, float *scale_block, hipStream_t stream);
+constexpr int kMetaCountBlocksMax = 16384;   // blocks of the metadata count (error words)
 hipError_t launch_metadata(const Problem &pb, int parts, int mode, int overhead,
                            int32_t *metadata, int64_t *prefix, int32_t *flags, hipStream_t stream);
 
