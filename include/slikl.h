@@ -72,8 +72,8 @@ enum { SLIKL_SPLIT_WEIGHTED = 0, SLIKL_SPLIT_ROWS = 1 };
  * with the maxima max_seqlen_q / max_seqlen_k given) writes per (query row, key)
  * records and runs a key-major kernel that sums over query rows in registers: no
  * atomics, bitwise reproducible; it pays off when the top-k lists cover a fair
- * share of each batch's keys.  SORTED (head groups N1/N2 up to 64,
- * N2*D*2 < 16384 bytes and T1*N2*topk < 2^31 - 65536, else UNSUPPORTED) writes each valid slot's dK part once
+ * share of each batch's keys.  SORTED (T1*N2*topk < 2^31 - 65536, and with head
+ * groups N1/N2 up to 64 N2*D*2 < 16384 bytes, else UNSUPPORTED) writes each valid slot's dK part once
  * (fp32) into a buffer (workspace: about D*4 + 16 bytes per (unit, slot) more) and
  * sums each key's parts through a key-sorted list of them: no atomics on hot keys
  * (global atomics only where a key's run is split between two waves); deterministic

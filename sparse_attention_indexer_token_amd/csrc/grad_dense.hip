@@ -96,7 +96,9 @@ struct UnitInputs {
     float pv[TOPK_PER_THREAD];
 };
 
-template <int HP, int D, bool F16>
+// SREC: instead of the dense records, per-slot records for the key-sorted dK strategy
+// (srec_key / srec_dI / srec_mask at [unit, position], srec_cnt[unit]).
+template <int HP, int D, bool F16, bool SREC>
 __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
     using C = DenseFwdCfg<HP, D>;
     constexpr int NH = C::NH, NDT = C::NDT, NKS = C::NKS, DCH = C::DCH, NL = C::NL, NST = C::NST;
@@ -268,7 +270,7 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
         // zero this unit's dI row over the key blocks its named keys meet (the dK
         // kernel reads whole blocks for rows whose range meets them); these stores
         // complete before the integer adds of pass 2 (waited on before the next barrier)
-        if (nvalid > 0) {
+        if (!SREC && nvalid > 0) {
             const int z0 = (kmin_i / pb.dk_kb) * pb.dk_kb;
             const int z1e = (kmax_i / pb.dk_kb + 1) * pb.dk_kb;
             const int z1 = z1e < klen ? z1e : klen;
@@ -340,7 +342,7 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
 
         // ---- dense records of the unit (stores behind the first copies) ---------------
         int eq = 0;
-        if constexpr (!F16) {
+        if constexpr (!F16 && !SREC) {
             eq = pow2_exponent_below_2p15(qmax);
             const float qsc = ldexpf(1.f, eq);
 #pragma unroll
@@ -369,15 +371,17 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
         }
         // w of the unit as fp16 hi and lo parts of w 2^ew (|w 2^ew| < 2^15; zero past G)
         const int ew = pow2_exponent_below_2p15(wabs);
-        uint8_t *const wrec = pb.wrec + (size_t)u * wrec_bytes(HP);
-        if (tid < HP) {
+        uint8_t *const wrec = SREC ? nullptr : pb.wrec + (size_t)u * wrec_bytes(HP);
+        if (SREC) {
+            if (tid == 0) pb.srec_cnt[u] = nvalid;
+        } else if (tid < HP) {
             const float ws = s_w[tid] * ldexpf(1.f, ew);
             const _Float16 wh = (_Float16)ws;
             const _Float16 wl = (_Float16)(ws - (float)wh);
             ((uint16_t *)wrec)[tid] = __builtin_bit_cast(uint16_t, wh);
             ((uint16_t *)wrec)[HP + tid] = __builtin_bit_cast(uint16_t, wl);
         }
-        if (tid == 0) {
+        if (!SREC && tid == 0) {
             pb.row_range[2 * u] = kmin_i;
             pb.row_range[2 * u + 1] = nvalid > 0 ? kmax_i : -1;
             *(u32x4 *)(wrec + HP * 4) = u32x4{(uint32_t)(eq + ew), (uint32_t)ed, 0u, 0u};
@@ -523,8 +527,8 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
 
         // ---- pass 2: U += dS16 K16 over this wave's positions -------------------------
         const float dfix = ldexpf(1.f, ed);
-        int32_t *dimap = pb.dI_map + (size_t)u * pb.s2max;
-        uint32_t *mmap = pb.mask_map + (size_t)u * pb.s2max * NH;
+        int32_t *dimap = SREC ? nullptr : pb.dI_map + (size_t)u * pb.s2max;
+        uint32_t *mmap = SREC ? nullptr : pb.mask_map + (size_t)u * pb.s2max * NH;
         f32x16 uacc[NH][NDT];
 #pragma unroll
         for (int ht = 0; ht < NH; ++ht)
@@ -539,7 +543,19 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
             // that the copies issued after an awaited one stay the last NL operations)
             {
                 const int pr = s * 128 + wave * 32 + l32;
-                if (half == 0 && pr < nvalid) {
+                if (SREC && half == 0 && pr < nvalid) {
+                    const size_t o = (size_t)u * topk + pr;
+                    pb.srec_key[o] = s_key[pr];
+                    pb.srec_dI[o] = s_I[pr];
+                    if constexpr (NH == 1) {
+                        pb.srec_mask[o] = s_mask[pr];
+                    } else if constexpr (NH == 2) {
+                        *(u32x2 *)(pb.srec_mask + o * 2) = u32x2{s_mask[pr], s_mask[TOPK_MAX + pr]};
+                    } else {
+                        *(u32x4 *)(pb.srec_mask + o * 4) = u32x4{s_mask[pr], s_mask[TOPK_MAX + pr],
+                                                                 s_mask[2 * TOPK_MAX + pr], s_mask[3 * TOPK_MAX + pr]};
+                    }
+                } else if (!SREC && half == 0 && pr < nvalid) {
                     const int jrel = s_key[pr] - kbase;
                     atomicAdd(dimap + jrel, (int32_t)__float2int_rn(s_I[pr] * dfix));
                     if constexpr (NH == 1) {
@@ -671,15 +687,18 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
 }
 
 template <int HP, int D, bool F16>
-static hipError_t launch_gd(const Problem &pb, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((grad_dense_kernel<HP, D, F16>), dim3(grid), dim3(kBlock), 0, stream, pb);
+static hipError_t launch_gd(const Problem &pb, int grid, bool srec, hipStream_t stream) {
+    if (srec)
+        hipLaunchKernelGGL((grad_dense_kernel<HP, D, F16, true>), dim3(grid), dim3(kBlock), 0, stream, pb);
+    else
+        hipLaunchKernelGGL((grad_dense_kernel<HP, D, F16, false>), dim3(grid), dim3(kBlock), 0, stream, pb);
     return hipGetLastError();
 }
 
 template <int HP, int D, bool F16>
 static int blocks_gd() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grad_dense_kernel<HP, D, F16>, kBlock, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grad_dense_kernel<HP, D, F16, false>, kBlock, 0) != hipSuccess)
         return 1;
     return n > 0 ? n : 1;
 }
@@ -697,10 +716,10 @@ static int blocks_gd() {
         if (hp == 128 && d == 128) return f16 ? FN<128, 128, true>(__VA_ARGS__) : FN<128, 128, false>(__VA_ARGS__); \
     } while (0)
 
-hipError_t launch_grad_dense(const Problem &pb, int hp, bool f16, int grid, hipStream_t stream) {
+hipError_t launch_grad_dense(const Problem &pb, int hp, bool f16, int grid, bool srec, hipStream_t stream) {
     const int d = pb.d;
-    if (hp <= 64) return launch_grad_dense8(pb, hp, f16, grid, false, stream);
-    SLIKL_GD_CASES(launch_gd, pb, grid, stream);
+    if (hp <= 64) return launch_grad_dense8(pb, hp, f16, grid, srec, stream);
+    SLIKL_GD_CASES(launch_gd, pb, grid, srec, stream);
     return hipErrorInvalidValue;
 }
 

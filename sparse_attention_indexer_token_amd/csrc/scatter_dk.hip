@@ -241,8 +241,9 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
 }
 
 // The body under the register budget of four workgroups per compute unit (32-head
-// groups with D = 32), three (32-head groups, D = 64 or 128) or two (64-head groups):
-// the most that run without spills.
+// groups with D = 32), three (32-head groups, D = 64 or 128), two (64-head groups) or
+// one (128-head groups, which need the whole register file): the most that run without
+// spills.
 template <int HP, int D, bool F16>
 __global__ __launch_bounds__(kSdBlock, 4) void scatter_dk_kernel4(Problem pb) {
     scatter_dk_body<HP, D, F16>(pb);
@@ -259,12 +260,18 @@ __global__ __launch_bounds__(kSdBlock, 2) void scatter_dk_kernel2(Problem pb) {
 }
 
 template <int HP, int D, bool F16>
+__global__ __launch_bounds__(kSdBlock, 1) void scatter_dk_kernel1(Problem pb) {
+    scatter_dk_body<HP, D, F16>(pb);
+}
+
+template <int HP, int D, bool F16>
 static hipError_t launch_sd(const Problem &pb, hipStream_t stream) {
     int dev = 0, cus = 0, per = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return hipErrorInvalidDevice;
-    auto kern = HP > 32 ? scatter_dk_kernel2<HP, D, F16>
+    auto kern = HP > 64   ? scatter_dk_kernel1<HP, D, F16>
+                : HP > 32 ? scatter_dk_kernel2<HP, D, F16>
                 : D <= 32 ? scatter_dk_kernel4<HP, D, F16> : scatter_dk_kernel3<HP, D, F16>;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, kSdBlock, 0) != hipSuccess || per <= 0) per = 1;
     const int64_t U = pb.t1 * pb.n2;
@@ -282,6 +289,7 @@ hipError_t launch_scatter_dk(const Problem &pb, int hp, bool f16, hipStream_t st
         return f16 ? launch_sd<HPV, DV, true>(pb, stream) : launch_sd<HPV, DV, false>(pb, stream);
     SLIKL_SD_CASE(32, 32) SLIKL_SD_CASE(32, 64) SLIKL_SD_CASE(32, 128)
     SLIKL_SD_CASE(64, 32) SLIKL_SD_CASE(64, 64) SLIKL_SD_CASE(64, 128)
+    SLIKL_SD_CASE(128, 32) SLIKL_SD_CASE(128, 64) SLIKL_SD_CASE(128, 128)
 #undef SLIKL_SD_CASE
     return hipErrorInvalidValue;
 }

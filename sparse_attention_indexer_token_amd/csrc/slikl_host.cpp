@@ -48,7 +48,9 @@ bool dense_fits(const slikl_desc *d) {
 // The key-sorted dK runs through the eight-wave kernel's slot records (head groups up to
 // 64, key rows within its 14-bit record stride); its bin prefix is one two-level scan.
 bool sorted_fits(const slikl_desc *d) {
-    if (head_tile(d->n2 > 0 ? d->n1 / d->n2 : 1) > 64 || (int64_t)d->n2 * d->d * 2 >= 16384) return false;
+    // the eight-wave kernel (head groups up to 64) addresses key rows as buffer records,
+    // whose stride field holds 14 bits
+    if (head_tile(d->n2 > 0 ? d->n1 / d->n2 : 1) <= 64 && (int64_t)d->n2 * d->d * 2 >= 16384) return false;
     // record indices are 32-bit; the sort loops step past the last record by up to 4096
     if ((double)rows_q(d) * d->n2 * d->topk >= 2147483648.0 - 65536.0) return false;
     const slikl::SortGeometry g = slikl::sorted_geometry(rows_q(d) * d->n2 * d->topk, rows_k(d) * d->n2);
@@ -513,9 +515,8 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
     }
     if (t1 > 0) {
         pe.begin(SLIKL_PHASE_FUSED);
-        e = mode == 2 ? slikl::launch_grad_dense(pb, head_tile(pb.group), f16, parts, s)
-            : s8      ? slikl::launch_grad_dense8(pb, head_tile(pb.group), f16, parts, true, s)
-                      : slikl::launch_grad_fused(pb, head_tile(pb.group), f16, mode, parts, s);
+        e = mode == 2 || s8 ? slikl::launch_grad_dense(pb, head_tile(pb.group), f16, parts, s8, s)
+                            : slikl::launch_grad_fused(pb, head_tile(pb.group), f16, mode, parts, s);
         pe.end(SLIKL_PHASE_FUSED);
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
         if (s8) {

@@ -120,8 +120,10 @@ struct WorkspacePlan {
 hipError_t launch_grad_fused(const Problem &pb, int hp, bool f16, int mode, int grid,
                              hipStream_t stream);
 int grad_fused_blocks_per_cu(int hp, int d, bool f16, int mode);
-// fused kernel of the dense dK strategy (BSND): writes the records above
-hipError_t launch_grad_dense(const Problem &pb, int hp, bool f16, int grid, hipStream_t stream);
+// fused kernel of the dense dK strategy: writes the dense records above, or with srec
+// the per-slot records of the key-sorted strategy (eight waves up to 64 heads, four
+// above)
+hipError_t launch_grad_dense(const Problem &pb, int hp, bool f16, int grid, bool srec, hipStream_t stream);
 int grad_dense_blocks_per_cu(int hp, int d, bool f16);
 // eight-wave variant for head groups of up to 64 (called by the two above)
 hipError_t launch_grad_dense8(const Problem &pb, int hp, bool f16, int grid, bool srec, hipStream_t stream);

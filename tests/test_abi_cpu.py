@@ -158,7 +158,8 @@ def test_unit_overhead_follows_the_dk_strategy(lib):
     assert oh(good_desc(topk=256)) == (0, _native.UNIT_OVERHEAD_DENSE)     # S2 = 16 topk
     assert oh(good_desc(topk=128)) == (0, _native.UNIT_OVERHEAD_DENSE)     # sparser lists: sorted
     assert oh(good_desc(topk=128, dk_mode=1)) == (0, _native.UNIT_OVERHEAD)
-    assert oh(good_desc(topk=128, n1=128)) == (0, _native.UNIT_OVERHEAD)   # scatter
+    assert oh(good_desc(topk=128, n1=128)) == (0, _native.UNIT_OVERHEAD_DENSE)   # sorted
+    assert oh(good_desc(topk=128, n1=128, dk_mode=1)) == (0, _native.UNIT_OVERHEAD)
     assert oh(good_desc(topk=128, deterministic=1)) == (0, _native.UNIT_OVERHEAD_DENSE)
     assert oh(good_desc(topk=64, deterministic=1)) == (0, _native.UNIT_OVERHEAD_DENSE)  # sorted
     cu = (ctypes.c_int32 * 2)(0, 4096)
@@ -178,15 +179,17 @@ def test_dk_strategy_query_resolves_auto(lib):
         return st, out.value
     assert strat(good_desc()) == (0, 2)                        # dsv32 shape: dense
     assert strat(good_desc(topk=128)) == (0, 3)                # S2 > 16 topk: sorted
-    assert strat(good_desc(topk=128, n1=128)) == (0, 1)        # head groups over 64: scatter
+    assert strat(good_desc(topk=128, n1=128)) == (0, 3)        # 128-head groups: sorted too
     assert strat(good_desc(topk=128, s1=1024)) == (0, 1)       # under 2048 units: scatter
     assert strat(good_desc(topk=128, deterministic=1)) == (0, 2)   # S2 <= 32 topk
     assert strat(good_desc(dk_mode=1)) == (0, 1)
     assert strat(good_desc(dk_mode=3)) == (0, 3)
     assert strat(good_desc(dk_mode=3, deterministic=1)) == (0, 3)
-    # sorted needs head groups of at most 64 (n1 / n2 = 128 is not)
-    assert strat(good_desc(dk_mode=3, n1=128))[0] == 3
+    assert strat(good_desc(dk_mode=3, n1=128)) == (0, 3)
     assert strat(good_desc(dk_mode=3, n1=128, n2=2)) == (0, 3)
+    # head groups up to 64 run the eight-wave kernel: N2 * D * 2 below 16384 bytes
+    assert strat(good_desc(dk_mode=3, n1=64, n2=64, d=128, s2=512))[0] == 3
+    assert strat(good_desc(dk_mode=3, n1=64, n2=32, d=128, s2=512)) == (0, 3)
     # 32-bit record indices: T1 * N2 * topk below 2^31 - 65536
     assert strat(good_desc(dk_mode=3, s1=1048576 - 33, topk=2048, n1=1, d=32, s2=64))[0] == 0
     assert strat(good_desc(dk_mode=3, s1=1048576 - 32, topk=2048, n1=1, d=32, s2=64))[0] == 3
