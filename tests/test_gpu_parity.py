@@ -335,3 +335,51 @@ def test_seq_used_lengths(name, dk_mode):
         check_close(got, ref, label=f"{name} {dk_mode} {variant}")
         kg = kl.cpu().numpy().reshape(kref.shape).astype(np.float64)
         assert np.max(np.abs(kg - kref) - 1e-4 * (1 + np.abs(kref))) <= 0
+
+
+@pytest.mark.parametrize("dk_mode,det", [("dense", False), ("sorted", True), ("scatter", True)])
+def test_graph_capture_replays_match_eager(dk_mode, det):
+    """The metadata pre-pass and slikl_grad captured into one HIP graph: every replay
+    (eager fills of the outputs and synchronisations in between) gives the eager call's
+    results bit for bit (strategies with reproducible dk)."""
+    import torch
+    import sparse_attention_indexer_token_amd as slikl
+    x = make_inputs(SMALL["hp64_d128_ragged"])
+    t = to_device(x)
+    kw = dict(dk_mode=dk_mode, deterministic=det)
+    desc = slikl.make_desc(t["q"], t["k"], t["idx"], **kw)
+    ws = torch.empty(slikl.slikl_grad_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    md = torch.empty(slikl.METADATA_INTS, dtype=torch.int32, device="cuda")
+    out = (torch.empty_like(t["q"]), torch.empty_like(t["k"]), torch.empty_like(t["w"]),
+           torch.empty_like(t["p"]))
+
+    def call():
+        slikl.slikl_grad_metadata(t["q"], t["k"], t["idx"], metadata=md, workspace=ws, **kw)
+        slikl.slikl_grad(t["q"], t["k"], t["w"], t["idx"], t["p"], metadata=md, workspace=ws, out=out, **kw)
+
+    _say(f"[graph] {dk_mode} det={det}")
+    call()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in out]
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for i in range(3):
+        for o in out:
+            o.fill_(7)
+        ws.fill_(3)                     # stale workspace contents must not matter
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, a, b in zip(("dq", "dk", "dw", "softmax_out"), out, eager):
+            assert torch.equal(a, b), (i, name)
+    check_close(dict(dq=eager[0].float().cpu().numpy(), dk=eager[1].float().cpu().numpy(),
+                     dw=eager[2].cpu().numpy(), softmax_out=eager[3].cpu().numpy()), oracle(x),
+                label=f"graph {dk_mode}")
