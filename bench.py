@@ -10,15 +10,21 @@ Default workload: the DeepSeek-V3.2-shaped indexer (BSND B=1, S1=S2=4096,
 N1=64, N2=1, D=128, topk=2048, bf16, causal indices).
 
 Prints one JSON line.  Fields beyond the common contract:
-  roofline      the dominant kernel (the fused kernel) against the bf16 dense
-                MFMA peak.  `achieved` = its algorithmic FLOP per launch (the S
-                and dq contractions over the valid slots, 4 * N1 * D per valid
-                slot and key head) / its average launch time, measured with HIP
-                events recorded on the launch stream (slikl_grad_profiled).
-                `traffic` = HBM bytes per launch from rocprofv3 FETCH_SIZE /
-                WRITE_SIZE counters kept under profiles/, scaled by the same
-                counters read for a plain copy of known size; null when the
-                kernel source changed since the counters were taken.
+  roofline      the dominant kernel (the phase that takes longest) against its own
+                bound: the fused kernel and the dense dK kernel against the bf16 /
+                fp16 dense MFMA peak, the sorted strategy's parts and per-key sum
+                kernels against HBM.  `achieved` = the kernel's algorithmic work per
+                launch (FLOP of the method's contractions over the valid slots, or
+                the bytes each input and output needs once) / its average launch
+                time, measured with HIP events recorded on the launch stream
+                (slikl_grad_profiled).  `traffic` = HBM bytes per launch from
+                rocprofv3 FETCH_SIZE / WRITE_SIZE counters kept under profiles/,
+                scaled by the same counters read for a plain copy of known size;
+                null when the kernel source changed since the counters were taken.
+  rooflines     the same for every timed phase.
+  step_bound    the whole step against the workload's own bound: nominal MFMA
+                FLOP (6 N1 D topk per query token), HBM on the compulsory bytes,
+                the K gather and the dK scatter rates.
   phases_ms     average per-phase milliseconds of the profiled calls.
   cpu_baseline  the fp64 oracle on a bounded row sample, on the host cores.
 """
@@ -36,14 +42,27 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "query tokens/sec at N1=64 D=128 topk=2048 bf16; % of MFMA bf16 peak"
-PEAK_MFMA_TFLOPS = {"bf16": 2500.0, "f16": 2500.0}
+HEADLINE = "dsv32_indexer"          # the workload METRIC is quoted on
+# MI355X published peaks: dense bf16 / fp16 MFMA (256 CU x 4096 FLOP/clk x 2.4 GHz) and
+# HBM3E bandwidth
+PEAK_MFMA_TFLOPS = 2516.6
+PEAK_HBM_GBPS = 8000.0
 CSRC = os.path.join(ROOT, "sparse_attention_indexer_token_amd", "csrc")
-# sources each fused kernel is compiled from (a change to any voids its traffic figure)
+# sources each kernel is compiled from (a change to any voids its traffic figure)
+_COMMON = ("device_common.h", "slikl_internal.h")
 KERNEL_SOURCES = {
-    kern: [os.path.join(CSRC, f) for f in (src, "device_common.h", "slikl_internal.h")]
+    kern: [os.path.join(CSRC, f) for f in (src,) + _COMMON]
     for kern, src in (("grad_dense8_kernel", "grad_dense8.hip"), ("grad_dense_kernel", "grad_dense.hip"),
-                      ("grad_fused_kernel", "grad_fused.hip"))
+                      ("grad_fused_kernel", "grad_fused.hip"), ("dense_dk_kernel", "dense_dk.hip"),
+                      ("scatter_dk_kernel", "scatter_dk.hip"), ("sorted_reduce_kernel", "sorted_dk.hip"))
 }
+
+
+def metric_for(wl):
+    if wl.name == HEADLINE:
+        return METRIC
+    return (f"query tokens/sec at N1={wl.n1} D={wl.d} topk={wl.topk} {wl.dtype} ({wl.name}); "
+            f"% of MFMA {wl.dtype} peak")
 
 
 def traffic_file(kernel, workload):
@@ -51,12 +70,52 @@ def traffic_file(kernel, workload):
 
 
 def fused_kernel(strategy, group):
-    """The fused kernel a call runs: the eight-wave kernel for head groups padded to at
-    most 64 heads (every strategy), above that the four-wave kernel of the dense
-    strategy or of the scatter strategy."""
-    if group <= 64:
-        return "grad_dense8_kernel"
-    return "grad_dense_kernel" if strategy == "dense" else "grad_fused_kernel"
+    """The fused kernel a call runs: with the dense and sorted dK strategies the
+    eight-wave kernel for head groups padded to at most 64 heads, the four-wave one
+    above; with the scatter strategy its own four-wave kernel (which also forms and
+    adds the dK parts)."""
+    if strategy == "scatter":
+        return "grad_fused_kernel"
+    return "grad_dense8_kernel" if group <= 64 else "grad_dense_kernel"
+
+
+def phase_work(strategy, wl, x, det):
+    """Algorithmic work of each timed phase's kernel per launch:
+    {phase: (kernel, bound, amount, unit)} with amount in FLOP ("mfma") or HBM bytes
+    ("hbm").  V = valid (unit, slot) pairs, G = N1 / N2 heads per unit."""
+    G = wl.n1 // wl.n2
+    V = x.valid_slots
+    D = wl.d
+    U = x.t1 * wl.n2
+    nh = max(1, (32 if G <= 32 else 64 if G <= 64 else 128) // 32)
+    acc_elem = 8 if det else 4          # int64 fixed point when deterministic
+    work = {}
+    if strategy == "scatter":
+        # S, dq and the dK parts: three G x D contractions per valid slot
+        work["fused"] = ("grad_fused_kernel", "mfma", 6.0 * G * D * V, "FLOP")
+        work["dk_final"] = ("finalize_kernel", "hbm", x.t2 * wl.n2 * D * (acc_elem + 2.0), "B")
+    else:
+        # S and dq (U = K^T dS^T): two G x D contractions per valid slot
+        work["fused"] = (fused_kernel(strategy, G), "mfma", 4.0 * G * D * V, "FLOP")
+    if strategy == "dense":
+        # the method's dK contraction dS^T q: one G x D contraction per valid slot
+        work["dk"] = ("dense_dk_kernel", "mfma", 2.0 * G * D * V, "FLOP")
+    if strategy == "sorted":
+        # each valid slot's fp32 part written once, with its record (key, dI, head words)
+        # read; q read once
+        work["dk"] = ("scatter_dk_kernel", "hbm", V * (4.0 * D + 8 + 4 * nh) + x.t1 * wl.n1 * D * 2.0, "B")
+        # the parts and the sorted list read once, the fp32 accumulator written once
+        work["dk_reduce"] = ("sorted_reduce_kernel", "hbm", V * (4.0 * D + 4) + x.t2 * wl.n2 * D * 4.0, "B")
+        work["dk_final"] = ("finalize_kernel", "hbm", x.t2 * wl.n2 * D * (acc_elem + 2.0), "B")
+    return work
+
+
+def compulsory_bytes(wl, x):
+    """Bytes every step must move to and from HBM: q in and dq out, w and dw, the
+    indices, p and softmax_out, k in and dk out (each once)."""
+    e16 = 2.0
+    return (x.t1 * wl.n1 * wl.d * e16 * 2 + x.t1 * wl.n1 * 4.0 * 2 + x.t1 * wl.n2 * wl.topk * 4.0 * 3
+            + x.t2 * wl.n2 * wl.d * e16 * 2)
 
 
 def sources_sha256(kernel):
@@ -89,11 +148,12 @@ def parse():
 def cpu_baseline(x, n_rows):
     import numpy as np
     from oracle import slikl_grad_ref
+    cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:       # threadpoolctl missing: report the affinity size
-        threads = len(os.sched_getaffinity(0))
+        blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:       # threadpoolctl missing: the BLAS count is unknown
+        blas = None
     stride = max(1, x.t1 // max(1, n_rows))
     rows = np.arange(0, x.t1, stride)[:n_rows]
     t0 = time.perf_counter()
@@ -101,7 +161,10 @@ def cpu_baseline(x, n_rows):
                    cu_seqlens_q=x.cu_q, cu_seqlens_k=x.cu_k, rows=rows)
     dt = time.perf_counter() - t0
     which = f"all {len(rows)} query rows" if stride == 1 else f"{len(rows)} query rows (every {stride}th row)"
-    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    # the oracle loops over units in Python and calls BLAS per unit: the BLAS threads
+    # are the threads it uses
+    return {"value": len(rows) / dt, "unit": "tokens/s", "cores": int(blas or cores), "kind": "oracle",
+            "affinity_cores": cores, "blas_threads": blas,
             "sample": f"{which} of the same workload, fp64 NumPy oracle, {dt:.1f} s wall"}
 
 
@@ -185,18 +248,56 @@ def main():
     phase_ms = {name: float(np.mean([ph[name] for ph in phases])) for name in phases[0]}
     T1 = x.t1
     G = wl.n1 // wl.n2
-    kernel = fused_kernel(strategy, G)
     ms_per_step = elapsed * 1e3 / args.steps
+    t_step = ms_per_step * 1e-3
     tokens_per_s = T1 * args.steps / elapsed
     flop_nominal = 6.0 * wl.n1 * wl.d * wl.topk * T1
     flop_valid = 6.0 * G * wl.d * x.valid_slots
-    # the fused kernel's own arithmetic: S and dq over the valid slots
-    flop_kernel = 4.0 * G * wl.d * x.valid_slots
-    kernel_ms = phase_ms["fused"]
-    achieved = flop_kernel / (kernel_ms * 1e-3) / 1e12
-    peak = PEAK_MFMA_TFLOPS[wl.dtype]
+
+    # per-phase rooflines (HIP events on the launch stream, the phases' average over the
+    # profiled calls); the dominant kernel is the phase that takes longest
+    rooflines = {}
+    for phase, (kern, bound, amount, unit) in phase_work(strategy, wl, x, det).items():
+        ms = phase_ms.get(phase, 0.0)
+        if ms <= 0:
+            continue
+        if bound == "mfma":
+            ach, peak, u = amount / (ms * 1e-3) / 1e12, PEAK_MFMA_TFLOPS, "TFLOP/s"
+        else:
+            ach, peak, u = amount / (ms * 1e-3) / 1e9, PEAK_HBM_GBPS, "GB/s"
+        rooflines[phase] = {"bound": bound, "achieved": ach, "peak": peak, "unit": u, "frac": ach / peak,
+                            "kernel": kern, "kernel_ms": ms,
+                            ("flop_per_launch" if bound == "mfma" else "bytes_per_launch"): amount}
+    dom = max(rooflines, key=lambda ph: rooflines[ph]["kernel_ms"])
+    roof = dict(rooflines[dom])
+    roof["traffic"] = traffic_bytes(roof["kernel"], wl.name)
+
+    # the workload's own bound: MFMA on the nominal FLOP, HBM on the compulsory bytes,
+    # the K gather (both passes read D 16-bit values per valid slot) and the dK scatter
+    # (D fp32 adds per valid slot); in deterministic mode with the sorted or scatter
+    # strategy also the parts' round trip (written and read once as fp32)
+    comp = compulsory_bytes(wl, x)
+    gather = 2.0 * x.valid_slots * wl.d * 2.0
+    scatter = x.valid_slots * wl.d * 4.0
+    dk_ms = sum(phase_ms.get(ph, 0.0) for ph in ("dk", "dk_prep", "dk_reduce", "dk_final"))
+    step_bound = {
+        "mfma_nominal_tflops": flop_nominal / t_step / 1e12,
+        "mfma_frac_nominal": flop_nominal / t_step / 1e12 / PEAK_MFMA_TFLOPS,
+        "hbm_compulsory_bytes": comp,
+        "hbm_frac_compulsory": comp / t_step / 1e9 / PEAK_HBM_GBPS,
+        "gather_bytes": gather,
+        "gather_gbps_fused": gather / (phase_ms["fused"] * 1e-3) / 1e9 if phase_ms.get("fused") else None,
+        "scatter_bytes": scatter,
+        "scatter_gbps": scatter / ((phase_ms["fused"] if strategy == "scatter" else dk_ms) * 1e-3) / 1e9
+        if (phase_ms.get("fused") if strategy == "scatter" else dk_ms) else None,
+    }
+    if det and strategy in ("sorted", "scatter"):
+        parts = 2.0 * x.valid_slots * wl.d * 4.0
+        step_bound["hbm_bytes_with_parts"] = comp + parts
+        step_bound["hbm_frac_with_parts"] = (comp + parts) / t_step / 1e9 / PEAK_HBM_GBPS
+    step_bound["bound"] = {"long_context": "gather", "contention_det": "hbm"}.get(wl.name, "mfma")
     res = {
-        "metric": METRIC,
+        "metric": metric_for(wl),
         "value": tokens_per_s,
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -212,12 +313,12 @@ def main():
                    "T2": x.t2, "N1": wl.n1, "N2": wl.n2, "D": wl.d, "topk": wl.topk,
                    "valid_slots": x.valid_slots, "deterministic": det, "dk_strategy": strategy,
                    "kl_loss": bool(args.kl_loss)},
-        "tflops_nominal_step": flop_nominal / (ms_per_step * 1e-3) / 1e12,
-        "tflops_valid_step": flop_valid / (ms_per_step * 1e-3) / 1e12,
-        "frac_peak_nominal_step": flop_nominal / (ms_per_step * 1e-3) / 1e12 / peak,
-        "roofline": {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": traffic_bytes(kernel, wl.name),
-                     "kernel": kernel, "kernel_ms": kernel_ms, "flop_per_launch": flop_kernel},
+        "tflops_nominal_step": flop_nominal / t_step / 1e12,
+        "tflops_valid_step": flop_valid / t_step / 1e12,
+        "frac_peak_nominal_step": flop_nominal / t_step / 1e12 / PEAK_MFMA_TFLOPS,
+        "roofline": roof,
+        "rooflines": rooflines,
+        "step_bound": step_bound,
         "phases_ms": phase_ms,
     }
     if not args.no_cpu_baseline:

@@ -206,9 +206,12 @@ enum {
     SLIKL_PHASE_KEY_COPY = 2,  /* fp16 copy of bf16 keys with its power-of-two scale  */
     SLIKL_PHASE_DET_SCALE = 3, /* fixed-point scale of the deterministic scatter      */
     SLIKL_PHASE_FUSED = 4,     /* the fused S / softmax / dI / dW / dq kernel          */
-    SLIKL_PHASE_DK = 5,        /* key-major dK kernel (dense strategy)                */
+    SLIKL_PHASE_DK = 5,        /* the main dK kernel: key-major sums (DENSE) or the
+                                  slot parts (SORTED)                                 */
     SLIKL_PHASE_DK_FINAL = 6,  /* dK finalisation (rounding / fixed-order reduce)     */
-    SLIKL_PHASES = 7
+    SLIKL_PHASE_DK_PREP = 7,   /* dK task table (DENSE) or key bucket sort (SORTED)   */
+    SLIKL_PHASE_DK_REDUCE = 8, /* per-key sums of the sorted parts (SORTED)           */
+    SLIKL_PHASES = 9
 };
 
 /* Same work and results as slikl_grad, for measurement: records HIP events on

@@ -43,6 +43,11 @@ notes):
     takes no part): per batch of a TND side, the used length (clamped to the
     sequence's length).  Query rows past it take no part (all their outputs 0);
     the batch's key range is cut to it (indices past it are out of range).
+11. The mask 1[S > 0] is a decision taken on a floating-point S.  An
+    implementation that forms S in fp32 may take it the other way wherever S lies
+    within fp32's rounding error of 0; both results are then correct.  With
+    ``kink=True`` the oracle reports, per dq and dk element, the largest change
+    such flips can make (see ``unit_backward``), for comparisons to allow.
 """
 from __future__ import annotations
 
@@ -52,6 +57,14 @@ import numpy as np
 
 BSND = "BSND"
 TND = "TND"
+# fp32 unit roundoff
+U32 = 2.0 ** -24
+
+
+def gamma(n: int) -> float:
+    """Worst-case relative error bound of an n-term fp32 sum of products, in any
+    order: gamma_n = n u / (1 - n u) times the sum of the terms' magnitudes."""
+    return n * U32 / (1.0 - n * U32)
 
 
 def _used(rows, layout, used):
@@ -76,7 +89,7 @@ def _row_table(layout: str, n_batch: int, s: int, cu: Optional[np.ndarray]):
     raise ValueError(f"unknown layout {layout!r}")
 
 
-def unit_backward(q_t, k_sel, valid, w_t, p_t):
+def unit_backward(q_t, k_sel, valid, w_t, p_t, kink=False):
     """One (query token, key head) unit of the backward pass, in fp64.
 
     q_t    [G, D]   the token's queries for the G heads of this key head
@@ -89,6 +102,15 @@ def unit_backward(q_t, k_sel, valid, w_t, p_t):
     Returns (y [K], dq_t [G, D], dw_t [G], dk_part [K, D]) where dk_part[s] is
     the row to scatter-add into the key named by slot s (zero for -1 slots).
     Follows the page's formula section equation by equation.
+
+    With kink=True also returns (dq_kink [G, D], dk_kink [K, D], scale): the
+    pairs (h, s) with |S| <= gamma_D sum_d |q_hd k_sd| are those whose mask an
+    fp32 S may decide either way (reading 11); flipping the mask of pair (h, s)
+    moves dq[h] by w_h dI_s K_s and the slot's dK part by w_h dI_s q_h, so
+    dq_kink[h] = sum over its ambiguous pairs of |w_h dI_s| |K_s| and
+    dk_kink[s] = sum over the slot's ambiguous pairs of |w_h dI_s| |q_h|
+    (elementwise).  ``scale`` = max over valid slots of sum_h |w_h S_hs|, the
+    magnitude of the terms that form I.
     """
     G, D = q_t.shape
     K = k_sel.shape[0]
@@ -97,8 +119,10 @@ def unit_backward(q_t, k_sel, valid, w_t, p_t):
     dq_t = np.zeros((G, D))
     dw_t = np.zeros(G)
     dk_part = np.zeros((K, D))
-    if v.size == 0:
-        return y, dq_t, dw_t, dk_part                     # reading 7
+    if v.size == 0:                                       # reading 7
+        if kink:
+            return y, dq_t, dw_t, dk_part, np.zeros((G, D)), np.zeros((K, D)), 0.0
+        return y, dq_t, dw_t, dk_part
     kv = k_sel[v]                                         # K_topk(t), valid slots only
     S = q_t @ kv.T                                        # eq. S: [G, |V|]
     R = np.maximum(S, 0.0)                                # ReLU(S)
@@ -112,12 +136,20 @@ def unit_backward(q_t, k_sel, valid, w_t, p_t):
     dq_t = dS @ kv                                        # dq = dS K_topk
     dk_part[v] = dS.T @ q_t                               # dK_topk = dS^T q
     y[v] = yv
-    return y, dq_t, dw_t, dk_part
+    if not kink:
+        return y, dq_t, dw_t, dk_part
+    amb = np.abs(S) <= gamma(D) * (np.abs(q_t) @ np.abs(kv).T)   # reading 11
+    flip = np.abs(w_t)[:, None] * np.abs(dI)[None, :] * amb      # |w_h dI_s| on those pairs
+    dq_kink = flip @ np.abs(kv)
+    dk_kink = np.zeros((K, D))
+    dk_kink[v] = flip.T @ np.abs(q_t)
+    scale = float((np.abs(w_t) @ np.abs(S)).max())
+    return y, dq_t, dw_t, dk_part, dq_kink, dk_kink, scale
 
 
 def slikl_grad_ref(q, k, w, sparse_indices, p, *, layout_q=BSND, layout_k=BSND,
                    cu_seqlens_q=None, cu_seqlens_k=None, rows=None, seq_used_q=None,
-                   seq_used_k=None):
+                   seq_used_k=None, kink=False):
     """Whole-operator oracle.  Arrays are converted to fp64 on entry.
 
     Shapes: q [B,S1,N1,D] | [T1,N1,D]; k [B,S2,N2,D] | [T2,N2,D];
@@ -129,7 +161,11 @@ def slikl_grad_ref(q, k, w, sparse_indices, p, *, layout_q=BSND, layout_k=BSND,
     used length of each batch of a TND side (reading 10).
 
     Returns a dict with fp64 ``dq``, ``dk``, ``dw``, ``softmax_out`` shaped
-    like q, k, w and p.
+    like q, k, w and p.  With ``kink=True`` also ``dq_kink`` and ``dk_kink``
+    (shaped like dq and dk: the largest change fp32 decisions of the mask at
+    S near 0 can make to each element, reading 11) and ``logit_scale``
+    ([..., N2] like p without its last axis: per unit, max over its valid slots
+    of sum_h |w_h S_hs|).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -168,6 +204,10 @@ def slikl_grad_ref(q, k, w, sparse_indices, p, *, layout_q=BSND, layout_k=BSND,
     dk = np.zeros_like(kf)
     dw = np.zeros_like(wf)
     y_out = np.zeros_like(pf)
+    if kink:
+        dq_k = np.zeros_like(qf)
+        dk_k = np.zeros_like(kf)
+        lscale = np.zeros(pf.shape[:2])
 
     wanted = None if rows is None else set(int(r) for r in rows)
     for b in range(n_batch):
@@ -185,14 +225,18 @@ def slikl_grad_ref(q, k, w, sparse_indices, p, *, layout_q=BSND, layout_k=BSND,
                     raise ValueError(f"row {r}: index outside the batch's key range")
                 krow = np.where(valid, k0 + ids, k0)      # key rows (dummy for -1)
                 k_sel = kf[krow, g] if klen else np.zeros((topk, d))
-                y, dq_t, dw_t, dk_part = unit_backward(
-                    qf[r, heads], k_sel, valid, wf[r, heads], pf[r, g])
+                res = unit_backward(qf[r, heads], k_sel, valid, wf[r, heads], pf[r, g], kink=kink)
+                y, dq_t, dw_t, dk_part = res[:4]
                 y_out[r, g] = y
                 dq[r, heads] = dq_t
                 dw[r, heads] = dw_t
                 vv = np.flatnonzero(valid)
                 np.add.at(dk[:, g], krow[vv], dk_part[vv])   # scatter-add (duplicates add)
-    return {
+                if kink:
+                    dq_k[r, heads] = res[4]
+                    np.add.at(dk_k[:, g], krow[vv], res[5][vv])
+                    lscale[r, g] = res[6]
+    out = {
         "dq": dq.reshape(q.shape),
         "dk": dk.reshape(k.shape),
         "dw": dw.reshape(w.shape),
@@ -200,6 +244,11 @@ def slikl_grad_ref(q, k, w, sparse_indices, p, *, layout_q=BSND, layout_k=BSND,
         "T1": T1,
         "T2": T2,
     }
+    if kink:
+        out["dq_kink"] = dq_k.reshape(q.shape)
+        out["dk_kink"] = dk_k.reshape(k.shape)
+        out["logit_scale"] = lscale.reshape(p.shape[:-1])
+    return out
 
 
 def kl_loss_ref(q, k, w, sparse_indices, p, *, layout_q=BSND, layout_k=BSND,

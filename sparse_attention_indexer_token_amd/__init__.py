@@ -18,12 +18,13 @@ from typing import Optional
 
 from . import _native
 from ._native import (  # noqa: F401
-    EXPORTS, LAYOUT, METADATA_HEADER, METADATA_INTS, MAX_PARTS, SliklDesc, SliklError,
-    UNIT_OVERHEAD, UNIT_OVERHEAD_DENSE, load,
+    EXPORTS, LAYOUT, METADATA_HEADER, METADATA_INTS, MAX_PARTS, SliklDesc,
+    SliklError, UNIT_OVERHEAD, UNIT_OVERHEAD_DENSE, load,
 )
 
 __all__ = ["slikl_grad", "slikl_grad_profiled", "slikl_grad_metadata", "slikl_grad_workspace_size",
-           "slikl_grad_parts", "slikl_grad_unit_overhead", "slikl_grad_dk_strategy", "slikl_status_string", "make_desc", "SliklDesc", "SliklError"]
+           "slikl_grad_parts", "slikl_grad_unit_overhead", "slikl_grad_dk_strategy", "slikl_status_string",
+           "make_desc", "SliklDesc", "SliklError"]
 
 
 def _torch():

@@ -33,7 +33,7 @@ UNIT_OVERHEAD_DENSE = 1024
 EXPORTS = ("slikl_grad_workspace_size", "slikl_grad_parts", "slikl_grad_unit_overhead", "slikl_grad_dk_strategy", "slikl_grad_metadata",
            "slikl_grad", "slikl_grad_profiled", "slikl_status_string")
 
-PHASES = ("metadata", "fill", "key_copy", "det_scale", "fused", "dk", "dk_final")
+PHASES = ("metadata", "fill", "key_copy", "det_scale", "fused", "dk", "dk_final", "dk_prep", "dk_reduce")
 
 
 class SliklDesc(ctypes.Structure):
@@ -152,3 +152,4 @@ def grad_profiled_raw(desc: SliklDesc, q, k, w, idx, p, metadata, dq, dk, dw, y,
                                       y or None, ws or None, ws_bytes, stream or None, ms),
            "slikl_grad_profiled")
     return {name: float(ms[i]) for i, name in enumerate(PHASES)}
+

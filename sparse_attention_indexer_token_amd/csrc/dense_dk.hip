@@ -100,11 +100,18 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t dk_view(const void *base, uint
 }
 
 // Key length of batch b in the dense records: S2, or (TND) its sequence clamped to the
-// records' key length.
+// records' key length and cut to its used key length when one is given.  The fused
+// kernels zero a unit's dI row only below that same length, so no key at or past it
+// is ever read from the records (dk there is 0: no slot may name it).
 __device__ __forceinline__ int dense_klen(const Problem &pb, int b) {
     if (pb.layout_k == 0) return (int)pb.s2;
-    const int l = pb.cu_k[b + 1] - pb.cu_k[b];
-    return l < 0 ? 0 : (l > (int)pb.s2max ? (int)pb.s2max : l);
+    int l = pb.cu_k[b + 1] - pb.cu_k[b];
+    l = l < 0 ? 0 : (l > (int)pb.s2max ? (int)pb.s2max : l);
+    if (pb.used_k != nullptr) {
+        const int uk = pb.used_k[b] < 0 ? 0 : pb.used_k[b];
+        l = uk < l ? uk : l;
+    }
+    return l;
 }
 
 // First query row of batch b and the row past its end.

@@ -270,7 +270,10 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
         // zero this unit's dI row over the key blocks its named keys meet (the dK
         // kernel reads whole blocks for rows whose range meets them); these stores
         // complete before the integer adds of pass 2 (waited on before the next barrier)
-        if (!SREC && nvalid > 0) {
+        // rows past a TND batch's given maximum add nothing to dK: their range is
+        // empty, so the dK kernel skips them and their records are never read
+        const bool dk_row = nvalid > 0 && !(pb.layout_q != 0 && rb >= pb.max_q);
+        if (!SREC && dk_row) {
             const int z0 = (kmin_i / pb.dk_kb) * pb.dk_kb;
             const int z1e = (kmax_i / pb.dk_kb + 1) * pb.dk_kb;
             const int z1 = z1e < klen ? z1e : klen;
@@ -382,13 +385,12 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
             ((uint16_t *)wrec)[HP + tid] = __builtin_bit_cast(uint16_t, wl);
         }
         if (!SREC && tid == 0) {
-            pb.row_range[2 * u] = kmin_i;
-            pb.row_range[2 * u + 1] = nvalid > 0 ? kmax_i : -1;
+            pb.row_range[2 * u] = dk_row ? kmin_i : 0x7fffffff;
+            pb.row_range[2 * u + 1] = dk_row ? kmax_i : -1;
             *(u32x4 *)(wrec + HP * 4) = u32x4{(uint32_t)(eq + ew), (uint32_t)ed, 0u, 0u};
-            if (nvalid > 0 && rb >= 0 && rb < pb.dk_nch * pb.dk_chunk) {
+            if (dk_row && rb >= 0 && rb < pb.dk_nch * pb.dk_chunk) {
                 // dK task sizing: +1 / -1 at the first / past the last key block that
-                // the named key range [kmin, kmax] meets, in this row's chunk (rows
-                // past a TND batch's given maximum are left out of the sizing)
+                // the named key range [kmin, kmax] meets, in this row's chunk
                 int32_t *dif = pb.kb_diff + ((size_t)(b * pb.n2 + g) * pb.dk_nch + rb / pb.dk_chunk) *
                                                 (pb.dk_nkb + 1);
                 atomicAdd(dif + kmin_i / pb.dk_kb, 1);

@@ -520,18 +520,27 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
         pe.end(SLIKL_PHASE_FUSED);
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
         if (s8) {
-            pe.begin(SLIKL_PHASE_DK);
+            pe.begin(SLIKL_PHASE_DK_PREP);
             e = slikl::launch_sorted_prepare(pb, s);
-            if (e == hipSuccess) e = slikl::launch_scatter_dk(pb, head_tile(pb.group), f16, s);
-            if (e == hipSuccess) e = slikl::launch_sorted_reduce(pb, mode == 1, s);
+            pe.end(SLIKL_PHASE_DK_PREP);
+            if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
+            pe.begin(SLIKL_PHASE_DK);
+            e = slikl::launch_scatter_dk(pb, head_tile(pb.group), f16, s);
             pe.end(SLIKL_PHASE_DK);
+            if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
+            pe.begin(SLIKL_PHASE_DK_REDUCE);
+            e = slikl::launch_sorted_reduce(pb, mode == 1, s);
+            pe.end(SLIKL_PHASE_DK_REDUCE);
             if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
         }
     }
     if (mode == 2) {
-        pe.begin(SLIKL_PHASE_DK);
+        pe.begin(SLIKL_PHASE_DK_PREP);
         e = slikl::launch_dense_dk_tasks(pb, s);
-        if (e == hipSuccess) e = slikl::launch_dense_dk(pb, head_tile(pb.group), f16, s);
+        pe.end(SLIKL_PHASE_DK_PREP);
+        if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
+        pe.begin(SLIKL_PHASE_DK);
+        e = slikl::launch_dense_dk(pb, head_tile(pb.group), f16, s);
         pe.end(SLIKL_PHASE_DK);
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
         pe.begin(SLIKL_PHASE_DK_FINAL);

@@ -70,62 +70,64 @@ def run_gpu(x, t=None, kl=False, **kw):
 def oracle(x, rows=None):
     from oracle import slikl_grad_ref
     return slikl_grad_ref(x.q, x.k, x.w, x.idx, x.p, layout_q=x.layout_q, layout_k=x.layout_k,
-                          cu_seqlens_q=x.cu_q, cu_seqlens_k=x.cu_k, rows=rows)
+                          cu_seqlens_q=x.cu_q, cu_seqlens_k=x.cu_k, rows=rows, kink=True)
 
 
-def check_close(got, ref, *, rows=None, what=("dq", "dk", "dw", "softmax_out"), label=""):
-    """Assert the tolerances; `rows` restricts dq / dw / softmax_out to those flat rows."""
+def check_close(got, ref, *, rows=None, what=("dq", "dk", "dw", "softmax_out"), label="",
+                y_logit_scaled=False):
+    """Assert the tolerances; `rows` restricts dq / dw / softmax_out to those flat rows.
+
+    dq and dk elements also allow the oracle's kink allowance (``dq_kink`` /
+    ``dk_kink`` when present): the change that deciding 1[S > 0] the other way at
+    scores within fp32 rounding of 0 makes.  With y_logit_scaled, softmax_out
+    allows 1e-5 + 2 u M y elementwise, u = 2^-24 and M the unit's logit scale
+    (max_s sum_h |w_h S_hs|): the first-order change of a softmax whose logits
+    carry errors up to u M, for inputs whose logits are far larger than the
+    pages' workloads have."""
     msgs = []
+
+    def pick(a, name, trail):
+        # flat query rows of an output whose last `trail` axes are per row
+        a = np.asarray(a, dtype=np.float64)
+        if rows is None or name == "dk":
+            return a
+        return a.reshape((-1,) + a.shape[a.ndim - trail:])[rows]
+
     for name in what:
-        g = np.asarray(got[name], dtype=np.float64)
-        r = np.asarray(ref[name], dtype=np.float64)
-        if rows is not None and name != "dk":
-            lead = g.shape[:-2] if name != "dw" else g.shape[:-1]
-            n_lead = int(np.prod(lead[:2])) if len(lead) >= 2 else int(lead[0])
-            g = g.reshape((n_lead,) + g.shape[len(lead):])[rows]
-            r = r.reshape((n_lead,) + r.shape[len(lead):])[rows]
+        trail = 1 if name == "dw" else 2
+        g = pick(got[name], name, trail)
+        r = pick(ref[name], name, trail).reshape(g.shape)
         if g.size == 0:
             continue
         err = np.abs(g - r)
         if name == "softmax_out":
-            ok = err.max() <= Y_ATOL
-            msgs.append(f"{name}: max abs {err.max():.3e}")
+            if y_logit_scaled:
+                m = pick(ref["logit_scale"], name, 1).reshape(g.shape[:-1])[..., None]
+                bound = Y_ATOL + 2.0 * 2.0 ** -24 * m * np.abs(r)
+                ok = bool(np.all(err <= bound))
+                msgs.append(f"{name}: max abs {err.max():.3e}, worst err/bound {float((err / bound).max()):.3f}")
+            else:
+                ok = err.max() <= Y_ATOL
+                msgs.append(f"{name}: max abs {err.max():.3e}")
         elif name == "dw":
+            # the bound reads max |err| / max |ref| over the tensor; a per-row reading
+            # (|err_row| / |ref_row| in the 2-norm, over rows whose norm exceeds 1e-3 of
+            # the largest) is checked beside it
             scale = max(np.abs(r).max(), 1e-30)
             ok = err.max() / scale <= DW_REL
-            msgs.append(f"{name}: max rel {err.max() / scale:.3e}")
+            en = np.sqrt((err.reshape(-1, err.shape[-1]) ** 2).sum(-1))
+            rn = np.sqrt((r.reshape(-1, r.shape[-1]) ** 2).sum(-1))
+            big = rn > 1e-3 * max(rn.max(), 1e-30)
+            row_rel = float((en[big] / rn[big]).max()) if big.any() else 0.0
+            ok = ok and row_rel <= DW_REL
+            msgs.append(f"{name}: max rel {err.max() / scale:.3e}, worst row rel {row_rel:.3e}")
         else:
             bound = G_ATOL + G_RTOL * np.abs(r)
+            if f"{name}_kink" in ref:
+                bound = bound + pick(ref[f"{name}_kink"], name, trail).reshape(g.shape)
             ok = bool(np.all(err <= bound))
             worst = np.unravel_index(np.argmax(err - bound), err.shape)
             msgs.append(f"{name}: worst excess {float((err - bound)[worst]):.3e} at {worst} "
                         f"(got {g[worst]:.5g} ref {r[worst]:.5g})")
         assert ok, f"{label} {' | '.join(msgs)}"
     return msgs
-
-
-def keys_with_few_refs(x, max_rows=8, want=16, rng=None):
-    """Flat key rows whose referencing query rows are few; returns {key: rows}."""
-    n2 = x.idx.shape[-2]
-    topk = x.idx.shape[-1]
-    idx = x.idx.reshape(-1, n2, topk)
-    T1 = idx.shape[0]
-    if x.layout_q == "BSND":
-        S1 = x.q.shape[1]
-        qbatch = np.arange(T1) // S1
-    else:
-        qbatch = np.searchsorted(x.cu_q, np.arange(T1), side="right") - 1
-    if x.layout_k == "BSND":
-        kbase = qbatch * x.k.shape[1]
-    else:
-        kbase = x.cu_k[qbatch]
-    flat = np.where(idx >= 0, idx + kbase[:, None, None], -1).reshape(T1, -1)
-    rows = np.broadcast_to(np.arange(T1)[:, None], flat.shape)
-    v = flat >= 0
-    pair = np.unique(flat[v].astype(np.int64) * T1 + rows[v])      # unique (key, row)
-    keys, rws = pair // T1, pair % T1
-    uk, start, cnt = np.unique(keys, return_index=True, return_counts=True)
-    ok = np.flatnonzero(cnt <= max_rows)
-    rng = rng or np.random.default_rng(0)
-    pick = rng.permutation(ok)[:want]
-    return {int(uk[i]): rws[start[i]:start[i] + cnt[i]] for i in pick}

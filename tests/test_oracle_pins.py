@@ -23,7 +23,7 @@ import numpy as np
 import pytest
 
 from oracle import slikl_ref
-from oracle.slikl_ref import kl_loss_ref, kl_per_unit_ref, slikl_grad_ref
+from oracle.slikl_ref import kl_loss_ref, kl_per_unit_ref, slikl_grad_ref, unit_backward
 from workloads import Workload, make_inputs
 
 
@@ -356,7 +356,7 @@ def test_out_of_range_index_raises():
 # Planted mistakes: each mutated unit step must fail the autograd pin.
 # ---------------------------------------------------------------------------
 def _mutant(kind):
-    def unit(q_t, k_sel, valid, w_t, p_t):
+    def unit(q_t, k_sel, valid, w_t, p_t, kink=False):
         G, D = q_t.shape
         K = k_sel.shape[0]
         v = np.flatnonzero(valid)
@@ -425,3 +425,83 @@ def test_seq_used_equals_the_cut_problem():
     units_cut = kl_per_unit_ref(x.q[qr], x.k[kr], x.w[qr], idx[qr], x.p[qr], layout_q="TND",
                                 layout_k="TND", cu_seqlens_q=cuq, cu_seqlens_k=cuk)
     assert np.allclose(units[qr], units_cut, rtol=1e-13, atol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# Mask decisions at S = 0 (reading 11): the kink allowance.
+# ---------------------------------------------------------------------------
+def _unit_grads_torch(torch, q_t, k_sel, w_t, p_t, ge):
+    """One unit's gradients by fp64 autograd of its KL term, with ReLU written as
+    where(S > 0, S, 0) (ge=False: derivative 0 at S = 0) or where(S >= 0, S, 0)
+    (ge=True: derivative 1 at S = 0)."""
+    q = torch.tensor(q_t, dtype=torch.float64, requires_grad=True)
+    k = torch.tensor(k_sel, dtype=torch.float64, requires_grad=True)
+    w = torch.tensor(w_t, dtype=torch.float64, requires_grad=True)
+    S = q @ k.T
+    R = torch.where(S >= 0, S, torch.zeros_like(S)) if ge else torch.where(S > 0, S, torch.zeros_like(S))
+    I = w @ R
+    p = torch.tensor(p_t, dtype=torch.float64)
+    loss = torch.sum(p * (torch.log(p) - torch.log_softmax(I, dim=0)))
+    loss.backward()
+    return q.grad.numpy(), k.grad.numpy(), w.grad.numpy()
+
+
+def test_kink_allowance_covers_the_other_decision(torch_cpu):
+    torch = torch_cpu
+    rng = np.random.default_rng(4)
+    G, D, K = 3, 4, 5
+    q_t = rng.normal(size=(G, D))
+    k_sel = rng.normal(size=(K, D))
+    # head 1 and slot 2 meet exactly at S = 0: q = (1, 1, 0, 0), k = (1, -1, 0, 0)
+    q_t[1] = [1.0, 1.0, 0.0, 0.0]
+    k_sel[2] = [1.0, -1.0, 0.0, 0.0]
+    w_t = np.array([0.7, -1.3, 0.4])
+    p_t = rng.dirichlet(np.ones(K))
+    S = q_t @ k_sel.T
+    assert S[1, 2] == 0.0
+    off = np.abs(S) > 1e-2
+    off[1, 2] = True
+    assert off.all(), "only the planted pair may be near 0"
+    valid = np.ones(K, dtype=bool)
+    y, dq, dw, dk, dq_kink, dk_kink, scale = unit_backward(q_t, k_sel, valid, w_t, p_t, kink=True)
+    gq0, gk0, gw0 = _unit_grads_torch(torch, q_t, k_sel, w_t, p_t, ge=False)
+    gq1, gk1, gw1 = _unit_grads_torch(torch, q_t, k_sel, w_t, p_t, ge=True)
+    # the oracle takes ReLU'(0) = 0 (reading 1) ...
+    np.testing.assert_allclose(dq, gq0, atol=1e-13)
+    np.testing.assert_allclose(dk, gk0, atol=1e-13)
+    # ... and its allowance is exactly the change the other decision makes
+    np.testing.assert_allclose(np.abs(gq1 - gq0), dq_kink, atol=1e-13)
+    np.testing.assert_allclose(np.abs(gk1 - gk0), dk_kink, atol=1e-13)
+    assert np.count_nonzero(dq_kink.any(axis=1)) == 1 and np.count_nonzero(dk_kink.any(axis=1)) == 1
+    np.testing.assert_allclose(gw1, gw0, atol=1e-13)       # ReLU(0) = 0 either way
+    # logit scale: max over slots of sum_h |w_h S_hs|
+    assert scale == pytest.approx(float((np.abs(w_t) @ np.abs(S)).max()), rel=1e-15)
+
+
+def test_kink_allowance_band_is_the_fp32_dot_product_bound():
+    """Pairs with |S| just inside gamma_D sum|q k| count, just outside do not."""
+    G, D, K = 1, 8, 2
+    q_t = np.ones((G, D))
+    k_sel = np.ones((K, D))
+    bound = slikl_ref.gamma(D) * D                  # sum |q k| = D
+    k_sel[0, 0] = 1.0 - D + 0.5 * bound              # S = 0.5 bound: inside
+    k_sel[1, 0] = 1.0 - D + 2.0 * bound              # S = 2 bound: outside
+    S = q_t @ k_sel.T
+    mag = np.abs(q_t) @ np.abs(k_sel).T
+    assert S[0, 0] <= slikl_ref.gamma(D) * mag[0, 0] < S[0, 1]
+    out = unit_backward(q_t, k_sel, np.ones(K, dtype=bool), np.array([0.9]), np.array([0.3, 0.7]), kink=True)
+    dq_kink, dk_kink = out[4], out[5]
+    assert dk_kink[0].any() and not dk_kink[1].any()
+    assert dq_kink.any()
+
+
+def test_kink_outputs_leave_the_results_unchanged():
+    x = _small(seed=11, n2=2, n1=6, duplicates=True)
+    a = slikl_grad_ref(x.q, x.k, x.w, x.idx, x.p, **_args(x))
+    b = slikl_grad_ref(x.q, x.k, x.w, x.idx, x.p, kink=True, **_args(x))
+    for name in ("dq", "dk", "dw", "softmax_out"):
+        assert np.array_equal(a[name], b[name])
+    assert b["dq_kink"].shape == a["dq"].shape and b["dk_kink"].shape == a["dk"].shape
+    assert b["logit_scale"].shape == a["softmax_out"].shape[:-1]
+    # random data has no S within fp32 rounding of 0 at these sizes
+    assert not b["dq_kink"].any() and not b["dk_kink"].any()

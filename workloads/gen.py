@@ -83,6 +83,8 @@ class Workload:
     p_alpha: float = 0.1               # dirichlet concentration
     deterministic: bool = False
     seed: int = 0
+    k_outliers: int = 0                # key rows (of the flattened [T2, N2]) scaled up
+    k_outlier_scale: float = 100.0     # their factor, applied before the 16-bit rounding
 
     @property
     def flops_per_token(self) -> int:
@@ -226,7 +228,9 @@ def _target_dist(wl: Workload, rng: np.random.Generator, idx: np.ndarray) -> np.
 def make_inputs(wl: Workload, seed: Optional[int] = None) -> Inputs:
     """Expand a workload into seeded host arrays (see module docstring)."""
     ss = np.random.SeedSequence(wl.seed if seed is None else seed)
-    rq, rk, rw, ri, rp, rl = (np.random.Generator(np.random.PCG64(c)) for c in ss.spawn(6))
+    # spawned children depend only on their index: adding the seventh (outlier rows)
+    # leaves the draws of the first six unchanged
+    rq, rk, rw, ri, rp, rl, ro = (np.random.Generator(np.random.PCG64(c)) for c in ss.spawn(7))
     rnd = round_to_bf16 if wl.dtype == "bf16" else round_to_f16
 
     if wl.layout == BSND:
@@ -252,7 +256,12 @@ def make_inputs(wl: Workload, seed: Optional[int] = None) -> Inputs:
         k_shape = (int(cu[-1]), wl.n2, wl.d)
 
     q, q_bits = rnd(rq.normal(0.0, np.sqrt(wl.q_var), size=q_shape).astype(np.float32))
-    k, k_bits = rnd(rk.normal(0.0, np.sqrt(wl.k_var), size=k_shape).astype(np.float32))
+    kf = rk.normal(0.0, np.sqrt(wl.k_var), size=k_shape).astype(np.float32)
+    if wl.k_outliers > 0:
+        flat = kf.reshape(-1, wl.d)
+        pick = ro.choice(flat.shape[0], size=min(wl.k_outliers, flat.shape[0]), replace=False)
+        flat[pick] *= np.float32(wl.k_outlier_scale)
+    k, k_bits = rnd(kf)
     w = rw.normal(0.0, np.sqrt(wl.w_var), size=q_shape[:-1]).astype(np.float32)
 
     zipf_cdf = _zipf_table(max(klens), wl.zipf_s) if wl.index_mode == "sink_zipf" else None
