@@ -228,6 +228,31 @@ slikl_status slikl_grad_profiled(const slikl_desc *desc, const void *q, const vo
                                  void *workspace, size_t workspace_bytes, void *stream,
                                  float *phase_ms);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation): slikl_grad with the
+ * workspace taken from a fixed array inside this library instead of the caller.
+ * The array holds SLIKL_STATIC_SCRATCH_BYTES bytes per GPU, kept from the first
+ * call on that GPU until the process ends; its device address is looked up once
+ * per device (the call's current device).  The call allocates and frees nothing.
+ * It runs the dK strategy of `desc` when that strategy's workspace fits the array;
+ * with dk_mode AUTO it otherwise runs SCATTER (the least workspace: the dK
+ * accumulator, T2*N2*D*4 bytes, 8 when deterministic, plus the fp16 key copy for
+ * bf16 and the split prefix); slikl_grad_noalloc_strategy names the strategy.
+ * Errors as slikl_grad; WORKSPACE when no strategy allowed by `desc` fits the
+ * array (nothing is launched).  Every call on one GPU uses that GPU's one array,
+ * which keeps the last call's contents (each call clears what must start at zero):
+ * calls that overlap on one GPU (concurrent streams or host threads) race and give
+ * wrong results; serialize them. */
+#define SLIKL_STATIC_SCRATCH_BYTES (64u << 20)
+slikl_status slikl_grad_noalloc(const slikl_desc *desc, const void *q, const void *k,
+                                const float *w, const int32_t *sparse_indices,
+                                const float *attn_softmax_l1norm, const int32_t *metadata,
+                                void *dq, void *dk, float *dw, float *softmax_out, void *stream);
+
+/* The dK strategy slikl_grad_noalloc runs for `desc` (as slikl_grad_dk_strategy);
+ * WORKSPACE when none fits its fixed array.  Host only. */
+slikl_status slikl_grad_noalloc_strategy(const slikl_desc *desc, int32_t *strategy);
+
 /* Static description of a status code. */
 const char *slikl_status_string(slikl_status s);
 

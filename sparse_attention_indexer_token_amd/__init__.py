@@ -18,13 +18,13 @@ from typing import Optional
 
 from . import _native
 from ._native import (  # noqa: F401
-    EXPORTS, LAYOUT, METADATA_HEADER, METADATA_INTS, MAX_PARTS, SliklDesc,
+    EXPORTS, LAYOUT, METADATA_HEADER, METADATA_INTS, MAX_PARTS, STATIC_SCRATCH_BYTES, SliklDesc,
     SliklError, UNIT_OVERHEAD, UNIT_OVERHEAD_DENSE, load,
 )
 
 __all__ = ["slikl_grad", "slikl_grad_profiled", "slikl_grad_metadata", "slikl_grad_workspace_size",
            "slikl_grad_parts", "slikl_grad_unit_overhead", "slikl_grad_dk_strategy", "slikl_status_string",
-           "make_desc", "SliklDesc", "SliklError"]
+           "slikl_grad_noalloc", "slikl_grad_noalloc_strategy", "make_desc", "SliklDesc", "SliklError"]
 
 
 def _torch():
@@ -191,6 +191,49 @@ def slikl_grad(q, k, w, sparse_indices, attn_softmax_l1norm, *, layout_q="BSND",
                  max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
                  workspace=workspace, out=out, kl_loss=kl_loss, seq_used_q=seq_used_q,
                  seq_used_k=seq_used_k, profiled=False)[0]
+
+
+def slikl_grad_noalloc_strategy(desc: SliklDesc) -> str:
+    """The dK strategy slikl_grad_noalloc runs for `desc`."""
+    return _native.noalloc_strategy(desc)
+
+
+def slikl_grad_noalloc(q, k, w, sparse_indices, attn_softmax_l1norm, *, out, layout_q="BSND",
+                       layout_k="BSND", cu_seqlens_q=None, cu_seqlens_k=None,
+                       deterministic: bool = False, metadata=None, num_parts: int = 0,
+                       split_mode: str = "weighted", dk_mode: str = "auto", max_seqlen_q: int = 0,
+                       max_seqlen_k: int = 0, kl_loss=None, seq_used_q=None, seq_used_k=None):
+    """slikl_grad into the caller's preallocated ``out`` = (dq, dk, dw, softmax_out),
+    with the library's fixed per-GPU workspace: neither this call nor the library
+    allocates device memory.  Calls that overlap on one GPU race (one shared array)."""
+    torch = _torch()
+    desc = make_desc(q, k, sparse_indices, layout_q=layout_q, layout_k=layout_k,
+                     cu_seqlens_q=cu_seqlens_q, cu_seqlens_k=cu_seqlens_k,
+                     deterministic=deterministic, num_parts=num_parts, split_mode=split_mode,
+                     dk_mode=dk_mode, max_seqlen_q=max_seqlen_q, max_seqlen_k=max_seqlen_k,
+                     seq_used_q=seq_used_q, seq_used_k=seq_used_k)
+    dev = q.device
+    rows = tuple(q.shape)[:-2]
+    _check_tensor("q", q, q.dtype, dev)
+    _check_tensor("k", k, q.dtype, dev)
+    _check_tensor("w", w, torch.float32, dev, rows + (desc.n1,))
+    _check_tensor("sparse_indices", sparse_indices, torch.int32, dev, rows + (desc.n2, desc.topk))
+    _check_tensor("attn_softmax_l1norm", attn_softmax_l1norm, torch.float32, dev,
+                  rows + (desc.n2, desc.topk))
+    if metadata is not None:
+        _check_tensor("metadata", metadata, torch.int32, dev, (METADATA_INTS,))
+    if kl_loss is not None:
+        _check_tensor("kl_loss", kl_loss, torch.float32, dev, rows + (desc.n2,))
+        desc.kl_loss = kl_loss.data_ptr()
+    dq, dk, dw, y = out
+    _check_tensor("dq", dq, q.dtype, dev, q.shape)
+    _check_tensor("dk", dk, q.dtype, dev, k.shape)
+    _check_tensor("dw", dw, torch.float32, dev, w.shape)
+    _check_tensor("softmax_out", y, torch.float32, dev, attn_softmax_l1norm.shape)
+    _native.grad_noalloc_raw(desc, q.data_ptr(), k.data_ptr(), w.data_ptr(), sparse_indices.data_ptr(),
+                             attn_softmax_l1norm.data_ptr(), metadata.data_ptr() if metadata is not None else 0,
+                             dq.data_ptr(), dk.data_ptr(), dw.data_ptr(), y.data_ptr(), _stream_handle(dev))
+    return out
 
 
 def slikl_grad_profiled(q, k, w, sparse_indices, attn_softmax_l1norm, **kw):

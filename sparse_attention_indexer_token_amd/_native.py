@@ -31,7 +31,9 @@ UNIT_OVERHEAD = 512
 UNIT_OVERHEAD_DENSE = 1024
 
 EXPORTS = ("slikl_grad_workspace_size", "slikl_grad_parts", "slikl_grad_unit_overhead", "slikl_grad_dk_strategy", "slikl_grad_metadata",
-           "slikl_grad", "slikl_grad_profiled", "slikl_status_string")
+           "slikl_grad", "slikl_grad_profiled", "slikl_status_string", "slikl_grad_noalloc",
+           "slikl_grad_noalloc_strategy")
+STATIC_SCRATCH_BYTES = 64 << 20
 
 PHASES = ("metadata", "fill", "key_copy", "det_scale", "fused", "dk", "dk_final", "dk_prep", "dk_reduce")
 
@@ -85,6 +87,10 @@ def load():
     lib.slikl_grad_profiled.argtypes = [P(SliklDesc)] + [c_void_p] * 10 + [c_void_p, c_size_t, c_void_p,
                                                                            P(ctypes.c_float)]
     lib.slikl_grad_profiled.restype = c_int32
+    lib.slikl_grad_noalloc.argtypes = [P(SliklDesc)] + [c_void_p] * 10 + [c_void_p]
+    lib.slikl_grad_noalloc.restype = c_int32
+    lib.slikl_grad_noalloc_strategy.argtypes = [P(SliklDesc), P(c_int32)]
+    lib.slikl_grad_noalloc_strategy.restype = c_int32
     lib.slikl_status_string.argtypes = [c_int32]
     lib.slikl_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -153,3 +159,16 @@ def grad_profiled_raw(desc: SliklDesc, q, k, w, idx, p, metadata, dq, dk, dw, y,
            "slikl_grad_profiled")
     return {name: float(ms[i]) for i, name in enumerate(PHASES)}
 
+
+def noalloc_strategy(desc: SliklDesc) -> str:
+    out = c_int32(0)
+    _check(load().slikl_grad_noalloc_strategy(ctypes.byref(desc), ctypes.byref(out)),
+           "slikl_grad_noalloc_strategy")
+    return {v: k for k, v in DK_MODE.items()}[int(out.value)]
+
+
+def grad_noalloc_raw(desc: SliklDesc, q, k, w, idx, p, metadata, dq, dk, dw, y, stream) -> None:
+    _check(load().slikl_grad_noalloc(ctypes.byref(desc), q or None, k or None, w or None, idx or None,
+                                     p or None, metadata or None, dq or None, dk or None, dw or None,
+                                     y or None, stream or None),
+           "slikl_grad_noalloc")

@@ -7,6 +7,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "slikl.h"
 #include "slikl_internal.h"
 
@@ -580,6 +582,76 @@ slikl_status slikl_grad_profiled(const slikl_desc *desc, const void *q, const vo
                                 softmax_out, workspace, workspace_bytes, stream, pe);
     if (st != SLIKL_OK) return st;
     return pe.collect(phase_ms) ? SLIKL_OK : SLIKL_ERR_LAUNCH;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The entry point that allocates nothing: its workspace is a fixed device array of
+// this library, one copy per GPU, whose device address is looked up once per device.
+// ---------------------------------------------------------------------------
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[SLIKL_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of this device's copy of `scratch` (nullptr on failure).  Called with
+// the caller's device current; the address is kept per device.
+void *scratch_address() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
+// The strategy the no-alloc call runs: the descriptor's own when its workspace fits
+// the fixed array; with AUTO, else the scatter strategy (the least workspace).
+bool noalloc_desc(const slikl_desc *in, slikl_desc *out) {
+    *out = *in;
+    if (plan(out).total <= SLIKL_STATIC_SCRATCH_BYTES) return true;
+    if (in->dk_mode != SLIKL_DK_AUTO) return false;
+    out->dk_mode = SLIKL_DK_SCATTER;
+    return plan(out).total <= SLIKL_STATIC_SCRATCH_BYTES;
+}
+
+}  // namespace
+
+extern "C" {
+
+slikl_status slikl_grad_noalloc_strategy(const slikl_desc *desc, int32_t *strategy) {
+    if (!desc || !strategy) return SLIKL_ERR_NULLPTR;
+    slikl_status st = validate(desc);
+    if (st != SLIKL_OK) return st;
+    slikl_desc d2;
+    if (!noalloc_desc(desc, &d2)) return SLIKL_ERR_WORKSPACE;
+    *strategy = dk_strategy(&d2) == 2 ? SLIKL_DK_DENSE : sorted_dk(&d2) ? SLIKL_DK_SORTED : SLIKL_DK_SCATTER;
+    return SLIKL_OK;
+}
+
+slikl_status slikl_grad_noalloc(const slikl_desc *desc, const void *q, const void *k, const float *w,
+                                const int32_t *sparse_indices, const float *attn_softmax_l1norm,
+                                const int32_t *metadata, void *dq, void *dk, float *dw, float *softmax_out,
+                                void *stream) {
+    if (!desc) return SLIKL_ERR_NULLPTR;
+    slikl_status st = validate(desc);
+    if (st != SLIKL_OK) return st;
+    slikl_desc d2;
+    if (!noalloc_desc(desc, &d2)) return SLIKL_ERR_WORKSPACE;
+    // a caller's metadata may have been cut for another strategy: the fused kernels walk
+    // whatever parts it holds, and results do not depend on the split
+    void *ws = scratch_address();
+    if (!ws) return SLIKL_ERR_LAUNCH;
+    PhaseEvents pe;
+    return grad_impl(&d2, q, k, w, sparse_indices, attn_softmax_l1norm, metadata, dq, dk, dw, softmax_out, ws,
+                     SLIKL_STATIC_SCRATCH_BYTES, stream, pe);
 }
 
 }  // extern "C"
