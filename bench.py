@@ -142,6 +142,8 @@ def parse():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="only run a plain device copy of this many bytes (counter calibration)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--attn-p-lse", action="store_true",
+                    help="p producer workloads: give each head's log-sum-exp (one pass over the keys)")
     return ap.parse_args()
 
 
@@ -168,6 +170,112 @@ def cpu_baseline(x, n_rows):
             "sample": f"{which} of the same workload, fp64 NumPy oracle, {dt:.1f} s wall"}
 
 
+def run_attn_p(args, wl_name):
+    """Bench of the p producer (slikl_attn_softmax_l1norm) on a main-attention workload:
+    one step = one call over all query rows.  Without lse the call makes two passes over
+    the keys (the heads' log-sum-exp over the slots, then p); with --attn-p-lse it is
+    given (computed beforehand with torch in fp32) and one pass runs."""
+    import numpy as np
+    import torch
+    import sparse_attention_indexer_token_amd as slikl
+    from workloads import ATTN_P_WORKLOADS, make_attn_p_inputs
+
+    slikl.load()
+    dev = torch.device("cuda:0")
+    wl = ATTN_P_WORKLOADS[wl_name]
+    x = make_attn_p_inputs(wl)
+    tdt = torch.bfloat16 if wl.index.dtype == "bf16" else torch.float16
+
+    def b16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).to(dev)
+
+    qm, km = b16(x.qm_bits), b16(x.km_bits)
+    idx = torch.from_numpy(np.ascontiguousarray(x.idx)).to(dev)
+    nm, dm = x.qm.shape[-2:]
+    n2, topk = x.idx.shape[-2:]
+    lse = None
+    if args.attn_p_lse:
+        # each head's log-sum-exp over its unit's valid slots, in fp32 with torch
+        qf = qm.reshape(-1, nm, dm)
+        kf = km.reshape(-1, n2, dm)
+        idf = idx.reshape(-1, n2, topk).long()
+        if x.layout_q != "BSND":
+            raise SystemExit("--attn-p-lse is built for BSND workloads")
+        # key base of each query row's batch
+        base = (torch.arange(qf.shape[0], device=dev) // x.idx.shape[1]) * km.shape[1]
+        lse = torch.empty(qf.shape[0], nm, dtype=torch.float32, device=dev)
+        hm = nm // n2
+        for r0 in range(0, qf.shape[0], 128):
+            r1 = min(qf.shape[0], r0 + 128)
+            for g in range(n2):
+                ids = idf[r0:r1, g]
+                valid = ids >= 0
+                rows = (ids.clamp(min=0) + base[r0:r1, None])
+                ksel = kf[rows, g].float().contiguous()                     # [R, topk, dm]
+                qsel = qf[r0:r1, g * hm:(g + 1) * hm].float().contiguous()  # [R, hm, dm]
+                z = torch.bmm(qsel, ksel.transpose(1, 2).contiguous()) * wl.scale
+                z = z.masked_fill(~valid[:, None, :], float("-inf"))
+                lse[r0:r1, g * hm:(g + 1) * hm] = torch.logsumexp(z, dim=-1)
+        lse = lse.reshape(x.qm.shape[:-1]).contiguous()
+    out = torch.empty(idx.shape, dtype=torch.float32, device=dev)
+    kw = dict(lse=lse, out=out, layout_q=x.layout_q, layout_k=x.layout_k)
+
+    def step():
+        slikl.slikl_attn_softmax_l1norm(qm, km, idx, wl.scale, **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    stream = torch.cuda.current_stream(dev)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    kernel_ms = ev0.elapsed_time(ev1) / args.steps
+    ms_per_step = elapsed * 1e3 / args.steps
+    passes = 1 if lse is not None else 2
+    hm = nm // n2
+    flop = passes * 2.0 * hm * dm * x.valid_slots
+    ach = flop / (kernel_ms * 1e-3) / 1e12
+    res = {
+        "metric": f"query tokens/sec of the p producer (attnSoftmaxL1Norm) at Nm={nm} Dm={dm} topk={topk} "
+                  f"{wl.index.dtype}; % of MFMA {wl.index.dtype} peak",
+        "value": x.t1 * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.index.dtype,
+        "data": "synthetic (seeded generators with the workload's shapes and value recipes)",
+        "config": {"workload": wl.name, "layout": x.layout_q, "T1": x.t1, "Nm": nm, "N2": n2, "Dm": dm,
+                   "topk": topk, "valid_slots": x.valid_slots, "lse_given": lse is not None, "passes": passes},
+        # one kernel per step: the events bracket the timed steps on the launch stream
+        "roofline": {"bound": "mfma", "achieved": ach, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": ach / PEAK_MFMA_TFLOPS, "traffic": None, "kernel": "attn_p_kernel",
+                     "kernel_ms": kernel_ms, "flop_per_launch": flop},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import attn_softmax_l1norm_ref
+        rows = np.arange(0, x.t1, max(1, x.t1 // 64))[:64]
+        t0 = time.perf_counter()
+        attn_softmax_l1norm_ref(x.qm, x.km, x.idx, scale=wl.scale, layout_q=x.layout_q, layout_k=x.layout_k,
+                                cu_seqlens_q=x.cu_q, cu_seqlens_k=x.cu_k, rows=rows)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": len(rows) / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
+                               "kind": "oracle", "sample": f"{len(rows)} query rows (evenly spaced), fp64 NumPy "
+                                                           f"oracle of p, {dt:.1f} s wall"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -190,7 +298,7 @@ def main():
         return 0
 
     import sparse_attention_indexer_token_amd as slikl
-    from workloads import WORKLOADS, make_inputs
+    from workloads import ATTN_P_WORKLOADS, WORKLOADS, make_inputs
 
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}), flush=True)
@@ -198,6 +306,8 @@ def main():
     slikl.load()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.workload in ATTN_P_WORKLOADS:
+        return run_attn_p(args, args.workload)
 
     wl = WORKLOADS[args.workload]
     det = wl.deterministic if args.deterministic is None else bool(args.deterministic)

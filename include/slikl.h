@@ -253,6 +253,54 @@ slikl_status slikl_grad_noalloc(const slikl_desc *desc, const void *q, const voi
  * WORKSPACE when none fits its fixed array.  Host only. */
 slikl_status slikl_grad_noalloc_strategy(const slikl_desc *desc, int32_t *strategy);
 
+/* ---------------------------------------------------------------------------
+ * The target distribution p = attnSoftmaxL1Norm from the main attention.
+ * The operator page's function section (接口功能) and the note after its softmax
+ * equation (计算公式) describe p as the main attention's score summed over heads
+ * and L1-normalised, computed by the main attention branch beforehand (the older
+ * fused operator formed it in its kernel).  Per (query row, key head g) unit and
+ * valid slot s of the unit's index list (key rows as for slikl_grad):
+ *    z[h, s] = scale * q_main[h] . k_main[key of s, g]   for the Hm = heads / n2
+ *              main-attention heads h of key head g (h = g*Hm .. g*Hm + Hm - 1),
+ *    P[h, s] = exp(z[h, s] - lse[h]),
+ *    p[s]    = sum_h P[h, s] / sum over the unit's valid slots of sum_h P[h, .],
+ * p = 0 at -1 slots (and at indices outside their batch's key range, which are
+ * skipped as in slikl_grad); a unit without a valid slot gets p = 0.  lse[h] is
+ * the natural log-sum-exp of z[h, .] over the keys the main attention normalised
+ * over: the caller's (its forward keeps it), or when lse is NULL the log-sum-exp
+ * over the unit's valid slots, computed here (one more pass over the keys).
+ *
+ * Shapes (BSND | TND): q_main [B,S1,Nm,Dm] | [T1,Nm,Dm] and k_main [B,S2,N2,Dm] |
+ * [T2,N2,Dm], fp16 or bf16 (one dtype); sparse_indices and p [B,S1,N2,topk] |
+ * [T1,N2,topk] (int32 / fp32); lse [B,S1,Nm] | [T1,Nm] fp32.  Device pointers,
+ * caller-owned, contiguous; q_main and k_main 16-byte aligned.  No workspace; the
+ * call only enqueues on `stream`.  fp32 arithmetic with MFMA dot products; every
+ * sum has a fixed order, so p is bitwise reproducible.
+ * Errors: NULLPTR (desc, or a tensor pointer NULL while T1 > 0 / T2 > 0, or a TND
+ * side without cuSeqLens), PARAM_INVALID (a field out of range, heads / n2 outside
+ * 1..128, d not one of 64, 128, 256, 512, 576, n2 * d * 2 >= 16384, scale not
+ * finite, misaligned q_main / k_main), LAUNCH. */
+typedef struct slikl_attn_p_desc {
+    int32_t layout_q;        /* SLIKL_LAYOUT_* of q_main                              */
+    int32_t layout_k;        /* SLIKL_LAYOUT_* of k_main                              */
+    int32_t dtype;           /* SLIKL_DTYPE_* of q_main and k_main                    */
+    int32_t reserved;        /* 0                                                     */
+    int64_t batch;           /* B (> 0); TND: number of sequences                     */
+    int64_t s1;              /* BSND: S1 (> 0); TND: T1 (>= 0)                        */
+    int64_t s2;              /* BSND: S2 (> 0); TND: T2 (>= 0)                        */
+    int64_t heads;           /* Nm, main-attention query heads; heads / n2 in 1..128  */
+    int64_t n2;              /* key heads (index lists), divides heads                 */
+    int64_t d;               /* Dm: 64, 128, 256, 512 or 576                          */
+    int64_t topk;            /* 1..2048                                               */
+    float scale;             /* softmax scale of the main attention                   */
+    const int32_t *cu_seqlens_q; /* device, B+1 entries starting at 0; required iff TND */
+    const int32_t *cu_seqlens_k;
+} slikl_attn_p_desc;
+
+slikl_status slikl_attn_softmax_l1norm(const slikl_attn_p_desc *desc, const void *q_main,
+                                       const void *k_main, const int32_t *sparse_indices,
+                                       const float *lse, float *p, void *stream);
+
 /* Static description of a status code. */
 const char *slikl_status_string(slikl_status s);
 

@@ -24,7 +24,8 @@ from ._native import (  # noqa: F401
 
 __all__ = ["slikl_grad", "slikl_grad_profiled", "slikl_grad_metadata", "slikl_grad_workspace_size",
            "slikl_grad_parts", "slikl_grad_unit_overhead", "slikl_grad_dk_strategy", "slikl_status_string",
-           "slikl_grad_noalloc", "slikl_grad_noalloc_strategy", "make_desc", "SliklDesc", "SliklError"]
+           "slikl_grad_noalloc", "slikl_grad_noalloc_strategy", "slikl_attn_softmax_l1norm", "make_desc",
+           "SliklDesc", "SliklError"]
 
 
 def _torch():
@@ -295,3 +296,65 @@ def _grad(q, k, w, sparse_indices, attn_softmax_l1norm, *, layout_q="BSND", layo
         return (dq, dk, dw, y), _native.grad_profiled_raw(*args)
     _native.grad_raw(*args)
     return (dq, dk, dw, y), None
+
+
+def slikl_attn_softmax_l1norm(q_main, k_main, sparse_indices, scale: float, *, lse=None, out=None,
+                              layout_q: str = "BSND", layout_k: str = "BSND", cu_seqlens_q=None,
+                              cu_seqlens_k=None):
+    """The target distribution p (attnSoftmaxL1Norm) from the main attention: per
+    (query row, key head) unit, the main-attention softmax probabilities of the
+    unit's heads at its top-k slots, summed over the heads and L1-normalised.
+
+    q_main [B,S1,Nm,Dm] | [T1,Nm,Dm], k_main [B,S2,N2,Dm] | [T2,N2,Dm] (bf16 / fp16),
+    sparse_indices [.., N2, topk] int32; ``lse`` (optional fp32 [.., Nm]): each head's
+    natural log-sum-exp over the keys the main attention normalised over (default:
+    over the unit's valid slots).  Returns p [.., N2, topk] fp32 (or fills ``out``)."""
+    torch = _torch()
+    if layout_q not in LAYOUT or layout_k not in LAYOUT:
+        raise ValueError("layouts must be 'BSND' or 'TND'")
+    dev = q_main.device
+    if layout_q == "BSND":
+        if q_main.dim() != 4:
+            raise ValueError("BSND q_main must be [B,S1,Nm,Dm]")
+        batch, s1, nm, d = q_main.shape
+    else:
+        if q_main.dim() != 3 or cu_seqlens_q is None:
+            raise ValueError("TND q_main must be [T1,Nm,Dm] with cu_seqlens_q")
+        s1, nm, d = q_main.shape
+        batch = cu_seqlens_q.numel() - 1
+    if layout_k == "BSND":
+        if k_main.dim() != 4 or (layout_q == "BSND" and k_main.shape[0] != batch):
+            raise ValueError("BSND k_main must be [B,S2,N2,Dm] with the batch of q_main")
+        kb, s2, n2, dk_ = k_main.shape
+        batch = kb if layout_q == "BSND" else batch
+    else:
+        if k_main.dim() != 3 or cu_seqlens_k is None or cu_seqlens_k.numel() - 1 != batch:
+            raise ValueError("TND k_main must be [T2,N2,Dm] with cu_seqlens_k of the batch")
+        s2, n2, dk_ = k_main.shape
+    if dk_ != d:
+        raise ValueError("q_main and k_main disagree on Dm")
+    rows = tuple(q_main.shape)[:-2]
+    _check_tensor("q_main", q_main, q_main.dtype, dev)
+    _check_tensor("k_main", k_main, q_main.dtype, dev)
+    _check_tensor("sparse_indices", sparse_indices, torch.int32, dev, rows + (n2, sparse_indices.shape[-1]))
+    if lse is not None:
+        _check_tensor("lse", lse, torch.float32, dev, rows + (nm,))
+    for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if cu is not None:
+            _check_tensor(name, cu, torch.int32, dev, (batch + 1,))
+    desc = _native.SliklAttnPDesc()
+    desc.layout_q, desc.layout_k = LAYOUT[layout_q], LAYOUT[layout_k]
+    desc.dtype = _dtype_code(q_main)
+    desc.reserved = 0
+    desc.batch, desc.s1, desc.s2 = int(batch), int(s1), int(s2)
+    desc.heads, desc.n2, desc.d = int(nm), int(n2), int(d)
+    desc.topk = int(sparse_indices.shape[-1])
+    desc.scale = float(scale)
+    desc.cu_seqlens_q = cu_seqlens_q.data_ptr() if layout_q == "TND" else None
+    desc.cu_seqlens_k = cu_seqlens_k.data_ptr() if layout_k == "TND" else None
+    if out is None:
+        out = torch.empty(sparse_indices.shape, dtype=torch.float32, device=dev)
+    _check_tensor("p", out, torch.float32, dev, tuple(sparse_indices.shape))
+    _native.attn_p_raw(desc, q_main.data_ptr(), k_main.data_ptr(), sparse_indices.data_ptr(),
+                       lse.data_ptr() if lse is not None else 0, out.data_ptr(), _stream_handle(dev))
+    return out

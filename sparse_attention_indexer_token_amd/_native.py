@@ -32,7 +32,7 @@ UNIT_OVERHEAD_DENSE = 1024
 
 EXPORTS = ("slikl_grad_workspace_size", "slikl_grad_parts", "slikl_grad_unit_overhead", "slikl_grad_dk_strategy", "slikl_grad_metadata",
            "slikl_grad", "slikl_grad_profiled", "slikl_status_string", "slikl_grad_noalloc",
-           "slikl_grad_noalloc_strategy")
+           "slikl_grad_noalloc_strategy", "slikl_attn_softmax_l1norm")
 STATIC_SCRATCH_BYTES = 64 << 20
 
 PHASES = ("metadata", "fill", "key_copy", "det_scale", "fused", "dk", "dk_final", "dk_prep", "dk_reduce")
@@ -50,6 +50,17 @@ class SliklDesc(ctypes.Structure):
         ("max_seqlen_q", c_int64), ("max_seqlen_k", c_int64),
         ("kl_loss", c_void_p),
         ("seq_used_q", c_void_p), ("seq_used_k", c_void_p),
+    ]
+
+
+class SliklAttnPDesc(ctypes.Structure):
+    """Mirror of ``slikl_attn_p_desc``."""
+    _fields_ = [
+        ("layout_q", c_int32), ("layout_k", c_int32), ("dtype", c_int32), ("reserved", c_int32),
+        ("batch", c_int64), ("s1", c_int64), ("s2", c_int64),
+        ("heads", c_int64), ("n2", c_int64), ("d", c_int64), ("topk", c_int64),
+        ("scale", ctypes.c_float),
+        ("cu_seqlens_q", c_void_p), ("cu_seqlens_k", c_void_p),
     ]
 
 
@@ -91,6 +102,8 @@ def load():
     lib.slikl_grad_noalloc.restype = c_int32
     lib.slikl_grad_noalloc_strategy.argtypes = [P(SliklDesc), P(c_int32)]
     lib.slikl_grad_noalloc_strategy.restype = c_int32
+    lib.slikl_attn_softmax_l1norm.argtypes = [P(SliklAttnPDesc)] + [c_void_p] * 6
+    lib.slikl_attn_softmax_l1norm.restype = c_int32
     lib.slikl_status_string.argtypes = [c_int32]
     lib.slikl_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -163,7 +176,7 @@ def grad_profiled_raw(desc: SliklDesc, q, k, w, idx, p, metadata, dq, dk, dw, y,
 def noalloc_strategy(desc: SliklDesc) -> str:
     out = c_int32(0)
     _check(load().slikl_grad_noalloc_strategy(ctypes.byref(desc), ctypes.byref(out)),
-           "slikl_grad_noalloc_strategy")
+           "slikl_grad_noalloc_strategy", "slikl_attn_softmax_l1norm")
     return {v: k for k, v in DK_MODE.items()}[int(out.value)]
 
 
@@ -172,3 +185,9 @@ def grad_noalloc_raw(desc: SliklDesc, q, k, w, idx, p, metadata, dq, dk, dw, y, 
                                      p or None, metadata or None, dq or None, dk or None, dw or None,
                                      y or None, stream or None),
            "slikl_grad_noalloc")
+
+
+def attn_p_raw(desc: SliklAttnPDesc, q, k, idx, lse, p, stream) -> None:
+    _check(load().slikl_attn_softmax_l1norm(ctypes.byref(desc), q or None, k or None, idx or None,
+                                            lse or None, p or None, stream or None),
+           "slikl_attn_softmax_l1norm")

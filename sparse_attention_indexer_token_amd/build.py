@@ -19,7 +19,7 @@ LIB = os.path.join(PKG, "libslikl.so")
 OBJDIR = os.path.join(PKG, "_build")
 
 SOURCES = ["grad_fused.hip", "grad_dense.hip", "grad_dense8.hip", "dense_dk.hip", "scatter_dk.hip", "sorted_dk.hip",
-           "aux_kernels.hip", "slikl_host.cpp"]
+           "aux_kernels.hip", "attn_p.hip", "slikl_host.cpp"]
 ARCH = "gfx950"
 
 

@@ -587,6 +587,76 @@ slikl_status slikl_grad_profiled(const slikl_desc *desc, const void *q, const vo
 }  // extern "C"
 
 // ---------------------------------------------------------------------------
+// The target distribution p from the main attention.
+// ---------------------------------------------------------------------------
+namespace {
+
+slikl_status validate_attn_p(const slikl_attn_p_desc *d) {
+    if (!d) return SLIKL_ERR_NULLPTR;
+    if (d->layout_q != SLIKL_LAYOUT_BSND && d->layout_q != SLIKL_LAYOUT_TND) return SLIKL_ERR_PARAM_INVALID;
+    if (d->layout_k != SLIKL_LAYOUT_BSND && d->layout_k != SLIKL_LAYOUT_TND) return SLIKL_ERR_PARAM_INVALID;
+    if (d->dtype != SLIKL_DTYPE_F16 && d->dtype != SLIKL_DTYPE_BF16) return SLIKL_ERR_PARAM_INVALID;
+    if (d->reserved != 0) return SLIKL_ERR_PARAM_INVALID;
+    if (d->batch <= 0 || d->batch > INT32_MAX - 1) return SLIKL_ERR_PARAM_INVALID;
+    if (d->n2 < 1 || d->heads < 1 || d->heads % d->n2 != 0 || d->heads / d->n2 > 128) return SLIKL_ERR_PARAM_INVALID;
+    if (d->d != 64 && d->d != 128 && d->d != 256 && d->d != 512 && d->d != 576) return SLIKL_ERR_PARAM_INVALID;
+    if (d->n2 * d->d * 2 >= 16384) return SLIKL_ERR_PARAM_INVALID;     // key record stride: 14 bits
+    if (d->topk < 1 || d->topk > 2048) return SLIKL_ERR_PARAM_INVALID;
+    if (!(d->scale == d->scale) || d->scale > 3.0e38f || d->scale < -3.0e38f) return SLIKL_ERR_PARAM_INVALID;
+    if (d->layout_q == SLIKL_LAYOUT_TND && !d->cu_seqlens_q) return SLIKL_ERR_NULLPTR;
+    if (d->layout_k == SLIKL_LAYOUT_TND && !d->cu_seqlens_k) return SLIKL_ERR_NULLPTR;
+    if (d->layout_q == SLIKL_LAYOUT_BSND ? d->s1 <= 0 : d->s1 < 0) return SLIKL_ERR_PARAM_INVALID;
+    if (d->layout_k == SLIKL_LAYOUT_BSND ? d->s2 <= 0 : d->s2 < 0) return SLIKL_ERR_PARAM_INVALID;
+    const int64_t lim = (int64_t)INT32_MAX;
+    if (d->layout_q == SLIKL_LAYOUT_BSND && d->s1 > lim / d->batch) return SLIKL_ERR_PARAM_INVALID;
+    if (d->layout_k == SLIKL_LAYOUT_BSND && d->s2 > lim / d->batch) return SLIKL_ERR_PARAM_INVALID;
+    const int64_t t1 = d->layout_q == SLIKL_LAYOUT_BSND ? d->batch * d->s1 : d->s1;
+    const int64_t t2 = d->layout_k == SLIKL_LAYOUT_BSND ? d->batch * d->s2 : d->s2;
+    // 32-bit element offsets in the kernel for the index lists, p and lse; 64-bit for q
+    if (t1 > lim / (d->n2 * d->topk) || t1 > lim / d->heads) return SLIKL_ERR_PARAM_INVALID;
+    if (t2 > lim / (d->n2 * d->d)) return SLIKL_ERR_PARAM_INVALID;
+    return SLIKL_OK;
+}
+
+}  // namespace
+
+extern "C" slikl_status slikl_attn_softmax_l1norm(const slikl_attn_p_desc *desc, const void *q_main,
+                                                  const void *k_main, const int32_t *sparse_indices,
+                                                  const float *lse, float *p, void *stream) {
+    slikl_status st = validate_attn_p(desc);
+    if (st != SLIKL_OK) return st;
+    const int64_t t1 = desc->layout_q == SLIKL_LAYOUT_BSND ? desc->batch * desc->s1 : desc->s1;
+    const int64_t t2 = desc->layout_k == SLIKL_LAYOUT_BSND ? desc->batch * desc->s2 : desc->s2;
+    if (t1 > 0 && (!q_main || !sparse_indices || !p)) return SLIKL_ERR_NULLPTR;
+    if (t2 > 0 && !k_main) return SLIKL_ERR_NULLPTR;
+    if (((uintptr_t)q_main | (uintptr_t)k_main) % 16 != 0) return SLIKL_ERR_PARAM_INVALID;
+    if (t1 == 0) return SLIKL_OK;
+    slikl::AttnPProblem pb{};
+    pb.q = (const uint16_t *)q_main;
+    pb.k = (const uint16_t *)k_main;
+    pb.idx = sparse_indices;
+    pb.lse = lse;
+    pb.p = p;
+    pb.cu_q = desc->layout_q == SLIKL_LAYOUT_TND ? desc->cu_seqlens_q : nullptr;
+    pb.cu_k = desc->layout_k == SLIKL_LAYOUT_TND ? desc->cu_seqlens_k : nullptr;
+    pb.s1 = desc->s1;
+    pb.s2 = desc->s2;
+    pb.t1 = t1;
+    pb.t2 = t2;
+    pb.batch = (int32_t)desc->batch;
+    pb.nm = (int32_t)desc->heads;
+    pb.n2 = (int32_t)desc->n2;
+    pb.hm = (int32_t)(desc->heads / desc->n2);
+    pb.dm = (int32_t)desc->d;
+    pb.topk = (int32_t)desc->topk;
+    pb.layout_q = desc->layout_q;
+    pb.layout_k = desc->layout_k;
+    pb.scale_log2 = desc->scale * 1.4426950408889634f;
+    hipError_t e = slikl::launch_attn_p(pb, desc->dtype == SLIKL_DTYPE_F16, (hipStream_t)stream);
+    return e == hipSuccess ? SLIKL_OK : SLIKL_ERR_LAUNCH;
+}
+
+// ---------------------------------------------------------------------------
 // The entry point that allocates nothing: its workspace is a fixed device array of
 // this library, one copy per GPU, whose device address is looked up once per device.
 // ---------------------------------------------------------------------------

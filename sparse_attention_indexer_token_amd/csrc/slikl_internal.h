@@ -94,6 +94,21 @@ __device__ __forceinline__ int used_klen(const Problem &pb, int b, int rb, int k
     return klen;
 }
 
+// The target distribution p from the main attention (attn_p.hip): one call's inputs.
+struct AttnPProblem {
+    const uint16_t *q;       // [T1, Nm, Dm] 16-bit main-attention queries
+    const uint16_t *k;       // [T2, N2, Dm] 16-bit main-attention keys
+    const int32_t *idx;      // [T1, N2, topk]
+    const float *lse;        // [T1, Nm] natural log-sum-exp per head, or null (over the slots)
+    float *p;                // [T1, N2, topk]
+    const int32_t *cu_q;     // [batch + 1] or null (BSND)
+    const int32_t *cu_k;     // [batch + 1] or null (BSND)
+    int64_t s1, s2, t1, t2;
+    int32_t batch, nm, n2, hm, dm, topk, layout_q, layout_k;
+    float scale_log2;        // softmax scale times log2(e)
+};
+hipError_t launch_attn_p(const AttnPProblem &pb, bool f16, hipStream_t stream);
+
 // Workspace carve-up (byte offsets), identical for every call with one desc.
 struct WorkspacePlan {
     size_t acc_off, acc_bytes;      // dK accumulator

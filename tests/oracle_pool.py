@@ -57,13 +57,15 @@ def workers() -> int:
 def batch_tables(x):
     """(first query row, rows, first key row, keys) of every batch, flattened."""
     n_batch = x.batch
+    xq = x.q if hasattr(x, "q") else x.qm
+    xk = x.k if hasattr(x, "k") else x.km
     if x.layout_q == "BSND":
-        S1 = x.q.shape[1]
+        S1 = xq.shape[1]
         qt = [(b * S1, S1) for b in range(n_batch)]
     else:
         qt = [(int(x.cu_q[b]), int(x.cu_q[b + 1] - x.cu_q[b])) for b in range(n_batch)]
     if x.layout_k == "BSND":
-        S2 = x.k.shape[1]
+        S2 = xk.shape[1]
         kt = [(b * S2, S2) for b in range(n_batch)]
     else:
         kt = [(int(x.cu_k[b]), int(x.cu_k[b + 1] - x.cu_k[b])) for b in range(n_batch)]
@@ -130,4 +132,55 @@ def oracle_full(x, *, batches=None, kl=True, n_workers=None, pieces_per_worker=4
             out["dk_kink"][k0:k0 + nk] += res["dk_kink"]
             rows.append(np.arange(a, e))
     out["rows"] = np.concatenate(rows) if rows else np.zeros(0, dtype=np.int64)
+    return out
+
+
+def _attn_piece(args):
+    qm, km, idx, scale, lse = args
+    from oracle import attn_softmax_l1norm_ref
+    cu_q = np.array([0, qm.shape[0]], dtype=np.int64)
+    cu_k = np.array([0, km.shape[0]], dtype=np.int64)
+    return attn_softmax_l1norm_ref(qm, km, idx, scale=scale, lse=lse, layout_q="TND", layout_k="TND",
+                                   cu_seqlens_q=cu_q, cu_seqlens_k=cu_k)
+
+
+def attn_p_full(x, *, lse=None, n_workers=None, pieces_per_worker=4):
+    """fp64 oracle of p for a whole workloads.AttnPInputs problem, flattened
+    [T1, N2, topk], computed over row pieces (one batch each) in worker processes."""
+    nm, dm = x.qm.shape[-2:]
+    n2 = x.km.shape[-2]
+    topk = x.idx.shape[-1]
+    qf = x.qm.reshape(-1, nm, dm)
+    kf = x.km.reshape(-1, n2, dm)
+    idxf = x.idx.reshape(-1, n2, topk)
+    lf = None if lse is None else np.asarray(lse).reshape(-1, nm)
+    T1 = qf.shape[0]
+    qt, kt = batch_tables(x)
+    nw = n_workers or workers()
+    cost = (idxf >= 0).sum(axis=(1, 2)).astype(np.int64) + 64
+    target = max(1, int(cost.sum()) // (nw * pieces_per_worker))
+    pieces = []
+    for b in range(x.batch):
+        q0, nq = qt[b]
+        start, acc = 0, 0
+        for r in range(nq):
+            acc += int(cost[q0 + r])
+            if acc >= target or r == nq - 1:
+                pieces.append((b, start, r + 1))
+                start, acc = r + 1, 0
+    args = []
+    for b, r0, r1 in pieces:
+        q0, _ = qt[b]
+        k0, nk = kt[b]
+        a, e = q0 + r0, q0 + r1
+        args.append((qf[a:e], kf[k0:k0 + nk], idxf[a:e], x.wl.scale, None if lf is None else lf[a:e]))
+    out = np.zeros((T1, n2, topk))
+    ctx = mp.get_context("spawn")
+    step = max(1, len(pieces) // 10)
+    with ctx.Pool(nw, initializer=_limit_threads) as pool:
+        for i, ((b, r0, r1), res) in enumerate(zip(pieces, pool.imap(_attn_piece, args))):
+            if (i + 1) % step == 0 or i + 1 == len(pieces):
+                print(f"[oracle p] {i + 1}/{len(pieces)} pieces", flush=True)
+            q0, _ = qt[b]
+            out[q0 + r0:q0 + r1] = res
     return out

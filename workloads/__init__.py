@@ -6,9 +6,13 @@ both the fp64 CPU oracle and the GPU path can be fed from it without sharing
 any computation.
 """
 from .gen import (  # noqa: F401
+    ATTN_P_WORKLOADS,
+    AttnPInputs,
+    AttnPWorkload,
     Inputs,
     Workload,
     WORKLOADS,
+    make_attn_p_inputs,
     make_inputs,
     round_to_bf16,
     round_to_f16,

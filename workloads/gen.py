@@ -285,3 +285,69 @@ def make_inputs(wl: Workload, seed: Optional[int] = None) -> Inputs:
         max_seqlen_q=max(qlens) if qlens else 0,
         max_seqlen_k=max(klens) if klens else 0,
     )
+
+
+# --------------------------------------------------------------------------
+# Main-attention inputs of the target distribution p (attnSoftmaxL1Norm).
+# --------------------------------------------------------------------------
+@dataclasses.dataclass(frozen=True)
+class AttnPWorkload:
+    """Main-attention queries / keys and the index lists p is taken at.  The
+    index lists follow the recipe of ``index`` (an indexer Workload: layout,
+    lengths, key heads, topk and index mode); nm / dm are the main attention's
+    query heads and head dim."""
+    name: str
+    index: Workload
+    nm: int = 128
+    dm: int = 576
+    scale: float = 1.0 / 192 ** 0.5
+    q_var: float = 1.0
+    k_var: float = 1.0
+    seed: int = 0
+
+
+@dataclasses.dataclass
+class AttnPInputs:
+    wl: AttnPWorkload
+    layout_q: str
+    layout_k: str
+    batch: int
+    qm: np.ndarray              # float32 values of the 16-bit qm
+    km: np.ndarray
+    qm_bits: np.ndarray
+    km_bits: np.ndarray
+    idx: np.ndarray
+    cu_q: Optional[np.ndarray]
+    cu_k: Optional[np.ndarray]
+
+    @property
+    def t1(self) -> int:
+        return int(self.idx.reshape(-1, self.idx.shape[-2], self.idx.shape[-1]).shape[0])
+
+    @property
+    def valid_slots(self) -> int:
+        return int((self.idx >= 0).sum())
+
+
+def make_attn_p_inputs(wl: AttnPWorkload) -> AttnPInputs:
+    """Index lists (and lengths) exactly as make_inputs(wl.index) draws them, plus
+    main-attention queries [.., nm, dm] and keys [.., N2, dm] from their own streams."""
+    base = make_inputs(wl.index)
+    rq, rk = (np.random.Generator(np.random.PCG64(c)) for c in np.random.SeedSequence(wl.seed).spawn(2))
+    rnd = round_to_bf16 if wl.index.dtype == "bf16" else round_to_f16
+    lead_q = base.q.shape[:-2]
+    lead_k = base.k.shape[:-2]
+    n2 = base.k.shape[-2]
+    qm, qm_bits = rnd(rq.normal(0.0, np.sqrt(wl.q_var), size=lead_q + (wl.nm, wl.dm)).astype(np.float32))
+    km, km_bits = rnd(rk.normal(0.0, np.sqrt(wl.k_var), size=lead_k + (n2, wl.dm)).astype(np.float32))
+    return AttnPInputs(wl=wl, layout_q=base.layout_q, layout_k=base.layout_k, batch=base.batch, qm=qm, km=km,
+                       qm_bits=qm_bits, km_bits=km_bits, idx=base.idx, cu_q=base.cu_q, cu_k=base.cu_k)
+
+
+# The main-attention workload of p at the DeepSeek-V3.2 indexer's shape: 128 query heads
+# sharing one key head, head dim 576 (a 512-wide latent plus 64 rotary dims), softmax
+# scale 1/sqrt(192), over the DeepSeek-shaped indexer's causal top-2048 lists.
+ATTN_P_WORKLOADS = {
+    "attn_p_dsv32": AttnPWorkload(name="attn_p_dsv32", index=WORKLOADS["dsv32_indexer"], nm=128, dm=576,
+                                  scale=1.0 / 192 ** 0.5, seed=2001),
+}
