@@ -7,3 +7,4 @@ and imports nothing from the product package.
 from .slikl_ref import slikl_grad_ref, kl_loss_ref, kl_per_unit_ref, unit_backward  # noqa: F401
 from .metadata_ref import metadata_ref  # noqa: F401
 from .attn_p_ref import attn_softmax_l1norm_ref, lse_over_slots_ref  # noqa: F401
+from .dense_ref import dense_grad_ref, visible_keys  # noqa: F401
