@@ -276,6 +276,106 @@ def run_attn_p(args, wl_name):
     return 0
 
 
+def run_dense(args, wl_name):
+    """Bench of the dense sibling operator (slikl_dense_grad): one step = the dense
+    pre-pass (index lists and metadata) and the call, all outputs produced."""
+    import types
+    import numpy as np
+    import torch
+    import sparse_attention_indexer_token_amd as slikl
+    from workloads import DENSE_WORKLOADS, make_dense_inputs
+
+    slikl.load()
+    dev = torch.device("cuda:0")
+    wl, mask = DENSE_WORKLOADS[wl_name]
+    det = wl.deterministic if args.deterministic is None else bool(args.deterministic)
+    x = make_dense_inputs(wl, mask)
+    tdt = torch.bfloat16 if wl.dtype == "bf16" else torch.float16
+
+    def b16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(tdt).to(dev)
+
+    q, k = b16(x.q_bits), b16(x.k_bits)
+    w = torch.from_numpy(np.ascontiguousarray(x.w)).to(dev)
+    p = torch.from_numpy(np.ascontiguousarray(x.p)).to(dev)
+    kw = dict(mask_mode=mask, deterministic=det, dk_mode=args.dk_mode, layout_q=x.layout_q, layout_k=x.layout_k)
+    desc = slikl.make_dense_desc(q, k, p, **kw)
+    ws = torch.empty(slikl.slikl_dense_grad_workspace_size(desc), dtype=torch.uint8, device=dev)
+    md = torch.empty(slikl.METADATA_INTS, dtype=torch.int32, device=dev)
+    out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(w), torch.empty_like(p))
+    sdesc = desc.base
+    sdesc.topk = p.shape[-1]
+    strategy = slikl.slikl_grad_dk_strategy(sdesc)
+
+    def step():
+        slikl.slikl_dense_grad_metadata(q, k, p, metadata=md, workspace=ws, **kw)
+        slikl.slikl_dense_grad(q, k, w, p, metadata=md, workspace=ws, out=out, **kw)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize(dev)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize(dev)
+    elapsed = time.perf_counter() - t0
+    phases = [slikl.slikl_dense_grad_profiled(q, k, w, p, metadata=md, workspace=ws, out=out, **kw)[1]
+              for _ in range(max(1, args.profiled_calls))]
+    phase_ms = {name: float(np.mean([ph[name] for ph in phases])) for name in phases[0]}
+    V = x.visible // 1
+    xs = types.SimpleNamespace(t1=x.t1, t2=int(np.prod(x.k.shape[:-2])), valid_slots=V)
+    rooflines = {}
+    for phase, (kern, bound, amount, unit) in phase_work(strategy, wl, xs, det).items():
+        ms = phase_ms.get(phase, 0.0)
+        if ms <= 0:
+            continue
+        if bound == "mfma":
+            ach, peak, u = amount / (ms * 1e-3) / 1e12, PEAK_MFMA_TFLOPS, "TFLOP/s"
+        else:
+            ach, peak, u = amount / (ms * 1e-3) / 1e9, PEAK_HBM_GBPS, "GB/s"
+        rooflines[phase] = {"bound": bound, "achieved": ach, "peak": peak, "unit": u, "frac": ach / peak,
+                            "kernel": kern, "kernel_ms": ms,
+                            ("flop_per_launch" if bound == "mfma" else "bytes_per_launch"): amount}
+    dom = max(rooflines, key=lambda ph: rooflines[ph]["kernel_ms"])
+    ms_per_step = elapsed * 1e3 / args.steps
+    G = wl.n1 // wl.n2
+    flop_valid = 6.0 * G * wl.d * V
+    res = {
+        "metric": f"query tokens/sec of the dense operator (maskMode {mask}) at N1={wl.n1} D={wl.d} "
+                  f"S2={x.k.shape[1] if x.layout_k == 'BSND' else x.max_seqlen_k} {wl.dtype}; % of MFMA {wl.dtype} peak",
+        "value": x.t1 * args.steps / elapsed,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded generators with the workload's shapes and value recipes)",
+        "config": {"workload": wl_name, "layout": x.layout_q, "batch": x.batch, "T1": x.t1, "N1": wl.n1,
+                   "N2": wl.n2, "D": wl.d, "mask_mode": mask, "visible_pairs": V, "deterministic": det,
+                   "dk_strategy": strategy},
+        "tflops_valid_step": flop_valid / (ms_per_step * 1e-3) / 1e12,
+        "roofline": dict(rooflines[dom], traffic=None),
+        "rooflines": rooflines,
+        "phases_ms": phase_ms,
+    }
+    if not args.no_cpu_baseline:
+        from oracle import dense_grad_ref
+        rows = np.arange(0, x.t1, max(1, x.t1 // 256))[:256]
+        t0 = time.perf_counter()
+        dense_grad_ref(x.q, x.k, x.w, x.p, mask_mode=mask, layout_q=x.layout_q, layout_k=x.layout_k,
+                       cu_seqlens_q=x.cu_q, cu_seqlens_k=x.cu_k, rows=rows)
+        dt = time.perf_counter() - t0
+        res["cpu_baseline"] = {"value": len(rows) / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
+                               "kind": "oracle", "sample": f"{len(rows)} query rows (evenly spaced), fp64 NumPy "
+                                                           f"oracle of the dense operator, {dt:.1f} s wall"}
+    print(json.dumps(res), flush=True)
+    return 0
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -298,7 +398,7 @@ def main():
         return 0
 
     import sparse_attention_indexer_token_amd as slikl
-    from workloads import ATTN_P_WORKLOADS, WORKLOADS, make_inputs
+    from workloads import ATTN_P_WORKLOADS, DENSE_WORKLOADS, WORKLOADS, make_inputs
 
     if not torch.cuda.is_available():
         print(json.dumps({"error": "no GPU visible"}), flush=True)
@@ -308,6 +408,8 @@ def main():
     torch.cuda.set_device(dev)
     if args.workload in ATTN_P_WORKLOADS:
         return run_attn_p(args, args.workload)
+    if args.workload in DENSE_WORKLOADS:
+        return run_dense(args, args.workload)
 
     wl = WORKLOADS[args.workload]
     det = wl.deterministic if args.deterministic is None else bool(args.deterministic)

@@ -301,6 +301,52 @@ slikl_status slikl_attn_softmax_l1norm(const slikl_attn_p_desc *desc, const void
                                        const void *k_main, const int32_t *sparse_indices,
                                        const float *lse, float *p, void *stream);
 
+/* ---------------------------------------------------------------------------
+ * The dense sibling operator (DenseLightningIndexerKLLossGrad).  The metadata
+ * article (DenseLightningIndexerKLLossGradMetadata: 导读, 功能定位, 约束说明 Mask)
+ * names it and fixes its mask modes: 0 = no mask, 3 = rightDownCausal (the lower
+ * triangle cornered at the bottom-right vertex: row t of a batch with S1_b rows and
+ * S2_b keys sees keys j <= t + S2_b - S1_b).  Its formulas are the sparse operator's
+ * with the top-k set replaced by the keys the mask shows; p (attnSoftmaxL1Norm) and
+ * softmax_out are dense over the key positions, [B,S1,N2,L] | [T1,N2,L] with
+ * L = S2 (BSND k) or max_seqlen_k (TND k); positions a row does not see get
+ * softmax_out 0 and their p is ignored.  q, k, w, dq, dk, dw as for slikl_grad.
+ * `base` is a slikl_desc read as for slikl_grad except that base.topk is ignored
+ * (the dense axis is L) and seq_used_q / seq_used_k must be NULL.  Limits: L in
+ * 1..2048 (the fused kernel holds a row's keys in LDS; UNSUPPORTED above), and
+ * cmp_ratio must be 1 (key compression is named on the page but not defined:
+ * cmp_ratio in 2..128 gives UNSUPPORTED, outside 1..128 PARAM_INVALID).  The work
+ * runs through slikl_grad's kernels on index lists of the visible keys that the
+ * call writes into its workspace (T1*N2*L*4 bytes beyond slikl_grad's), so the dK
+ * strategies, determinism, metadata and loss output behave as there.
+ * Errors as slikl_grad, plus the limits above. */
+typedef struct slikl_dense_desc {
+    slikl_desc base;
+    int32_t mask_mode;       /* 0 or 3                                                */
+    int32_t cmp_ratio;       /* 1                                                     */
+} slikl_dense_desc;
+
+slikl_status slikl_dense_grad_workspace_size(const slikl_dense_desc *desc, size_t *bytes);
+
+/* The load-balancing pre-pass of the dense operator (the metadata article's own
+ * subject): writes the index lists into the workspace and splits the rows by their
+ * visible keys (base.split_mode) into `metadata` (SLIKL_METADATA_INTS int32). */
+slikl_status slikl_dense_grad_metadata(const slikl_dense_desc *desc, int32_t *metadata, void *workspace,
+                                       size_t workspace_bytes, void *stream);
+
+slikl_status slikl_dense_grad(const slikl_dense_desc *desc, const void *q, const void *k, const float *w,
+                              const float *attn_softmax_l1norm, const int32_t *metadata, void *dq,
+                              void *dk, float *dw, float *softmax_out, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* slikl_dense_grad with the per-phase times of slikl_grad_profiled (the index-list
+ * fill is counted in SLIKL_PHASE_FILL); blocks until the call has run. */
+slikl_status slikl_dense_grad_profiled(const slikl_dense_desc *desc, const void *q, const void *k,
+                                       const float *w, const float *attn_softmax_l1norm,
+                                       const int32_t *metadata, void *dq, void *dk, float *dw,
+                                       float *softmax_out, void *workspace, size_t workspace_bytes,
+                                       void *stream, float *phase_ms);
+
 /* Static description of a status code. */
 const char *slikl_status_string(slikl_status s);
 

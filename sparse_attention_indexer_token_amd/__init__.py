@@ -24,8 +24,9 @@ from ._native import (  # noqa: F401
 
 __all__ = ["slikl_grad", "slikl_grad_profiled", "slikl_grad_metadata", "slikl_grad_workspace_size",
            "slikl_grad_parts", "slikl_grad_unit_overhead", "slikl_grad_dk_strategy", "slikl_status_string",
-           "slikl_grad_noalloc", "slikl_grad_noalloc_strategy", "slikl_attn_softmax_l1norm", "make_desc",
-           "SliklDesc", "SliklError"]
+           "slikl_grad_noalloc", "slikl_grad_noalloc_strategy", "slikl_attn_softmax_l1norm",
+           "slikl_dense_grad", "slikl_dense_grad_profiled", "slikl_dense_grad_metadata",
+           "slikl_dense_grad_workspace_size", "make_dense_desc", "make_desc", "SliklDesc", "SliklError"]
 
 
 def _torch():
@@ -358,3 +359,86 @@ def slikl_attn_softmax_l1norm(q_main, k_main, sparse_indices, scale: float, *, l
     _native.attn_p_raw(desc, q_main.data_ptr(), k_main.data_ptr(), sparse_indices.data_ptr(),
                        lse.data_ptr() if lse is not None else 0, out.data_ptr(), _stream_handle(dev))
     return out
+
+
+def make_dense_desc(q, k, attn_softmax_l1norm, *, mask_mode: int = 3, cmp_ratio: int = 1,
+                    **kw) -> "_native.SliklDenseDesc":
+    """Descriptor of the dense operator; ``kw`` as for make_desc (layouts, cuSeqLens,
+    determinism, split, dK strategy, maxima).  The dense axis of p / softmax_out is
+    the key length (S2, or max_seqlen_k for a TND k)."""
+    desc = _native.SliklDenseDesc()
+    desc.base = make_desc(q, k, attn_softmax_l1norm, **kw)   # (only the shape of p is read)
+    desc.mask_mode = int(mask_mode)
+    desc.cmp_ratio = int(cmp_ratio)
+    return desc
+
+
+def slikl_dense_grad_workspace_size(desc) -> int:
+    return _native.dense_workspace_size(desc)
+
+
+def slikl_dense_grad_metadata(q, k, attn_softmax_l1norm, *, mask_mode: int = 3, cmp_ratio: int = 1,
+                              metadata=None, workspace=None, **kw):
+    """The dense operator's load-balancing pre-pass; returns the int32 metadata."""
+    torch = _torch()
+    desc = make_dense_desc(q, k, attn_softmax_l1norm, mask_mode=mask_mode, cmp_ratio=cmp_ratio, **kw)
+    dev = q.device
+    nbytes = _native.dense_workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    if metadata is None:
+        metadata = torch.empty(METADATA_INTS, dtype=torch.int32, device=dev)
+    _check_tensor("metadata", metadata, torch.int32, dev, (METADATA_INTS,))
+    _native.dense_metadata_raw(desc, metadata.data_ptr(), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _stream_handle(dev))
+    return metadata
+
+
+def slikl_dense_grad(q, k, w, attn_softmax_l1norm, *, mask_mode: int = 3, cmp_ratio: int = 1, metadata=None,
+                     workspace=None, out=None, kl_loss=None, **kw):
+    """Dense operator backward; returns (dq, dk, dw, softmax_out).  attn_softmax_l1norm
+    and softmax_out are dense over the key positions: [.., N2, L]."""
+    return _dense(q, k, w, attn_softmax_l1norm, mask_mode, cmp_ratio, metadata, workspace, out, kl_loss, kw,
+                  profiled=False)[0]
+
+
+def slikl_dense_grad_profiled(q, k, w, attn_softmax_l1norm, *, mask_mode: int = 3, cmp_ratio: int = 1,
+                              metadata=None, workspace=None, out=None, kl_loss=None, **kw):
+    return _dense(q, k, w, attn_softmax_l1norm, mask_mode, cmp_ratio, metadata, workspace, out, kl_loss, kw,
+                  profiled=True)
+
+
+def _dense(q, k, w, p, mask_mode, cmp_ratio, metadata, workspace, out, kl_loss, kw, profiled):
+    torch = _torch()
+    desc = make_dense_desc(q, k, p, mask_mode=mask_mode, cmp_ratio=cmp_ratio, **kw)
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("tensors must be on the GPU")
+    rows = tuple(q.shape)[:-2]
+    n2 = k.shape[-2]
+    L = desc.base.s2 if kw.get("layout_k", "BSND") == "BSND" else desc.base.max_seqlen_k
+    _check_tensor("q", q, q.dtype, dev)
+    _check_tensor("k", k, q.dtype, dev)
+    _check_tensor("w", w, torch.float32, dev, rows + (q.shape[-2],))
+    _check_tensor("attn_softmax_l1norm", p, torch.float32, dev, rows + (n2, L))
+    if metadata is not None:
+        _check_tensor("metadata", metadata, torch.int32, dev, (METADATA_INTS,))
+    if kl_loss is not None:
+        _check_tensor("kl_loss", kl_loss, torch.float32, dev, rows + (n2,))
+        desc.base.kl_loss = kl_loss.data_ptr()
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(w), torch.empty_like(p))
+    dq, dk, dw, y = out
+    _check_tensor("dq", dq, q.dtype, dev, q.shape)
+    _check_tensor("dk", dk, q.dtype, dev, k.shape)
+    _check_tensor("dw", dw, torch.float32, dev, w.shape)
+    _check_tensor("softmax_out", y, torch.float32, dev, p.shape)
+    nbytes = _native.dense_workspace_size(desc)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    ms = _native.dense_grad_raw(desc, q.data_ptr(), k.data_ptr(), w.data_ptr(), p.data_ptr(),
+                                metadata.data_ptr() if metadata is not None else 0, dq.data_ptr(),
+                                dk.data_ptr(), dw.data_ptr(), y.data_ptr(), workspace.data_ptr(),
+                                workspace.numel() * workspace.element_size(), _stream_handle(dev),
+                                profiled=profiled)
+    return out, ms

@@ -32,7 +32,8 @@ UNIT_OVERHEAD_DENSE = 1024
 
 EXPORTS = ("slikl_grad_workspace_size", "slikl_grad_parts", "slikl_grad_unit_overhead", "slikl_grad_dk_strategy", "slikl_grad_metadata",
            "slikl_grad", "slikl_grad_profiled", "slikl_status_string", "slikl_grad_noalloc",
-           "slikl_grad_noalloc_strategy", "slikl_attn_softmax_l1norm")
+           "slikl_grad_noalloc_strategy", "slikl_attn_softmax_l1norm", "slikl_dense_grad_workspace_size",
+           "slikl_dense_grad_metadata", "slikl_dense_grad", "slikl_dense_grad_profiled")
 STATIC_SCRATCH_BYTES = 64 << 20
 
 PHASES = ("metadata", "fill", "key_copy", "det_scale", "fused", "dk", "dk_final", "dk_prep", "dk_reduce")
@@ -51,6 +52,11 @@ class SliklDesc(ctypes.Structure):
         ("kl_loss", c_void_p),
         ("seq_used_q", c_void_p), ("seq_used_k", c_void_p),
     ]
+
+
+class SliklDenseDesc(ctypes.Structure):
+    """Mirror of ``slikl_dense_desc``."""
+    _fields_ = [("base", SliklDesc), ("mask_mode", c_int32), ("cmp_ratio", c_int32)]
 
 
 class SliklAttnPDesc(ctypes.Structure):
@@ -102,6 +108,15 @@ def load():
     lib.slikl_grad_noalloc.restype = c_int32
     lib.slikl_grad_noalloc_strategy.argtypes = [P(SliklDesc), P(c_int32)]
     lib.slikl_grad_noalloc_strategy.restype = c_int32
+    lib.slikl_dense_grad_workspace_size.argtypes = [P(SliklDenseDesc), P(c_size_t)]
+    lib.slikl_dense_grad_workspace_size.restype = c_int32
+    lib.slikl_dense_grad_metadata.argtypes = [P(SliklDenseDesc), c_void_p, c_void_p, c_size_t, c_void_p]
+    lib.slikl_dense_grad_metadata.restype = c_int32
+    lib.slikl_dense_grad.argtypes = [P(SliklDenseDesc)] + [c_void_p] * 9 + [c_void_p, c_size_t, c_void_p]
+    lib.slikl_dense_grad.restype = c_int32
+    lib.slikl_dense_grad_profiled.argtypes = [P(SliklDenseDesc)] + [c_void_p] * 9 + [c_void_p, c_size_t, c_void_p,
+                                                                                     P(ctypes.c_float)]
+    lib.slikl_dense_grad_profiled.restype = c_int32
     lib.slikl_attn_softmax_l1norm.argtypes = [P(SliklAttnPDesc)] + [c_void_p] * 6
     lib.slikl_attn_softmax_l1norm.restype = c_int32
     lib.slikl_status_string.argtypes = [c_int32]
@@ -176,7 +191,8 @@ def grad_profiled_raw(desc: SliklDesc, q, k, w, idx, p, metadata, dq, dk, dw, y,
 def noalloc_strategy(desc: SliklDesc) -> str:
     out = c_int32(0)
     _check(load().slikl_grad_noalloc_strategy(ctypes.byref(desc), ctypes.byref(out)),
-           "slikl_grad_noalloc_strategy", "slikl_attn_softmax_l1norm")
+           "slikl_grad_noalloc_strategy", "slikl_attn_softmax_l1norm", "slikl_dense_grad_workspace_size",
+           "slikl_dense_grad_metadata", "slikl_dense_grad", "slikl_dense_grad_profiled")
     return {v: k for k, v in DK_MODE.items()}[int(out.value)]
 
 
@@ -191,3 +207,26 @@ def attn_p_raw(desc: SliklAttnPDesc, q, k, idx, lse, p, stream) -> None:
     _check(load().slikl_attn_softmax_l1norm(ctypes.byref(desc), q or None, k or None, idx or None,
                                             lse or None, p or None, stream or None),
            "slikl_attn_softmax_l1norm")
+
+
+def dense_workspace_size(desc: SliklDenseDesc) -> int:
+    out = c_size_t(0)
+    _check(load().slikl_dense_grad_workspace_size(ctypes.byref(desc), ctypes.byref(out)),
+           "slikl_dense_grad_workspace_size")
+    return out.value
+
+
+def dense_metadata_raw(desc: SliklDenseDesc, metadata_ptr: int, ws_ptr: int, ws_bytes: int, stream: int) -> None:
+    _check(load().slikl_dense_grad_metadata(ctypes.byref(desc), metadata_ptr or None, ws_ptr or None, ws_bytes,
+                                            stream or None), "slikl_dense_grad_metadata")
+
+
+def dense_grad_raw(desc: SliklDenseDesc, q, k, w, p, metadata, dq, dk, dw, y, ws, ws_bytes, stream, profiled=False):
+    args = (ctypes.byref(desc), q or None, k or None, w or None, p or None, metadata or None, dq or None,
+            dk or None, dw or None, y or None, ws or None, ws_bytes, stream or None)
+    if not profiled:
+        _check(load().slikl_dense_grad(*args), "slikl_dense_grad")
+        return None
+    ms = (ctypes.c_float * len(PHASES))()
+    _check(load().slikl_dense_grad_profiled(*args, ms), "slikl_dense_grad_profiled")
+    return {name: float(ms[i]) for i, name in enumerate(PHASES)}

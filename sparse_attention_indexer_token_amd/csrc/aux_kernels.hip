@@ -58,6 +58,47 @@ hipError_t launch_rowinfo(const Problem &pb, i32x4 *info, hipStream_t stream) {
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Index lists of the dense operator: for unit u = (row r, key head g) and key
+// position j < L, j when row r sees key j under the mask, else -1.  maskMode 0: a
+// row sees all keys of its batch; maskMode 3 (rightDownCausal): row t of a batch
+// with S1_b rows and S2_b keys sees keys j <= t + S2_b - S1_b.  Key positions at or
+// past L (the dense axis, the longest key sequence given) are not listed.
+// ---------------------------------------------------------------------------
+__global__ void dense_index_kernel(Problem pb, int32_t *idx, int mask_mode, int L) {
+    const int64_t n = pb.t1 * pb.n2 * (int64_t)L;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) {
+        const int j = (int)(e % L);
+        const int64_t r = e / L / pb.n2;
+        int t, s1b, s2b;
+        if (pb.layout_q == 0) {
+            const int b = (int)(r / pb.s1);
+            t = (int)(r - (int64_t)b * pb.s1);
+            s1b = (int)pb.s1;
+            s2b = pb.layout_k == 0 ? (int)pb.s2 : pb.cu_k[b + 1] - pb.cu_k[b];
+        } else {
+            const int b = batch_of_row(pb.cu_q, pb.batch, r);
+            t = (int)(r - pb.cu_q[b]);
+            s1b = pb.cu_q[b + 1] - pb.cu_q[b];
+            s2b = pb.layout_k == 0 ? (int)pb.s2 : pb.cu_k[b + 1] - pb.cu_k[b];
+        }
+        int vis = s2b;
+        if (mask_mode == 3) vis = t + s2b - s1b + 1;
+        vis = vis < 0 ? 0 : (vis > s2b ? s2b : vis);
+        idx[e] = j < vis ? j : -1;
+    }
+}
+
+hipError_t launch_dense_index(const Problem &pb, int32_t *idx, int mask_mode, int L, hipStream_t stream) {
+    const int64_t n = pb.t1 * pb.n2 * (int64_t)L;
+    if (n <= 0) return hipSuccess;
+    int64_t blocks = (n + 255) / 256;
+    if (blocks > 8192) blocks = 8192;
+    hipLaunchKernelGGL(dense_index_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pb, idx, mask_mode, L);
+    return hipGetLastError();
+}
+
 hipError_t launch_zero_ranges(const ZeroRanges &zr, hipStream_t stream) {
     size_t most = 0;
     for (int r = 0; r < zr.n; ++r) most = zr.bytes[r] / 16 > most ? zr.bytes[r] / 16 : most;

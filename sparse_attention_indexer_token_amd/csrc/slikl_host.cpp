@@ -355,6 +355,7 @@ struct PhaseEvents {
     hipEvent_t ev[2 * SLIKL_PHASES] = {};
     bool used[SLIKL_PHASES] = {};
     hipStream_t s = nullptr;
+    float extra_fill_ms = 0.f;      // fills timed outside these events (dense index lists)
     bool init(hipStream_t st) {
         s = st;
         on = true;
@@ -582,6 +583,125 @@ slikl_status slikl_grad_profiled(const slikl_desc *desc, const void *q, const vo
                                 softmax_out, workspace, workspace_bytes, stream, pe);
     if (st != SLIKL_OK) return st;
     return pe.collect(phase_ms) ? SLIKL_OK : SLIKL_ERR_LAUNCH;
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The dense sibling operator: slikl_grad over index lists of the visible keys.
+// ---------------------------------------------------------------------------
+namespace {
+
+// The sparse descriptor the dense call runs (topk = the dense axis L), validated.
+slikl_status dense_sparse_desc(const slikl_dense_desc *d, slikl_desc *sd) {
+    if (!d) return SLIKL_ERR_NULLPTR;
+    if (d->mask_mode != 0 && d->mask_mode != 3) return SLIKL_ERR_PARAM_INVALID;
+    if (d->cmp_ratio < 1 || d->cmp_ratio > 128) return SLIKL_ERR_PARAM_INVALID;
+    if (d->cmp_ratio != 1) return SLIKL_ERR_UNSUPPORTED;
+    if (d->base.seq_used_q || d->base.seq_used_k) return SLIKL_ERR_UNSUPPORTED;
+    *sd = d->base;
+    const int64_t L = sd->layout_k == SLIKL_LAYOUT_BSND ? sd->s2 : sd->max_seqlen_k;
+    if (L < 1) return SLIKL_ERR_PARAM_INVALID;
+    if (L > 2048) return SLIKL_ERR_UNSUPPORTED;
+    sd->topk = L;
+    return validate(sd);
+}
+
+size_t dense_idx_off(const slikl_desc *sd) { return align_up(plan(sd).total); }
+size_t dense_ws_bytes(const slikl_desc *sd) {
+    return dense_idx_off(sd) + align_up((size_t)rows_q(sd) * (size_t)sd->n2 * (size_t)sd->topk * 4);
+}
+
+}  // namespace
+
+extern "C" {
+
+slikl_status slikl_dense_grad_workspace_size(const slikl_dense_desc *desc, size_t *bytes) {
+    if (!desc || !bytes) return SLIKL_ERR_NULLPTR;
+    slikl_desc sd;
+    slikl_status st = dense_sparse_desc(desc, &sd);
+    if (st != SLIKL_OK) return st;
+    *bytes = dense_ws_bytes(&sd);
+    return SLIKL_OK;
+}
+
+slikl_status slikl_dense_grad_metadata(const slikl_dense_desc *desc, int32_t *metadata, void *workspace,
+                                       size_t workspace_bytes, void *stream) {
+    if (!desc || !metadata) return SLIKL_ERR_NULLPTR;
+    slikl_desc sd;
+    slikl_status st = dense_sparse_desc(desc, &sd);
+    if (st != SLIKL_OK) return st;
+    if (!workspace || workspace_bytes < dense_ws_bytes(&sd) || (uintptr_t)workspace % 256 != 0)
+        return SLIKL_ERR_WORKSPACE;
+    int32_t *idx = (int32_t *)((char *)workspace + dense_idx_off(&sd));
+    slikl::Problem pb = problem(&sd);
+    hipError_t e = slikl::launch_dense_index(pb, idx, desc->mask_mode, (int)sd.topk, (hipStream_t)stream);
+    if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
+    return slikl_grad_metadata(&sd, idx, metadata, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+slikl_status dense_grad_impl(const slikl_dense_desc *desc, const void *q, const void *k, const float *w,
+                             const float *p, const int32_t *metadata, void *dq, void *dk, float *dw, float *y,
+                             void *workspace, size_t workspace_bytes, void *stream, PhaseEvents &pe) {
+    slikl_desc sd;
+    slikl_status st = dense_sparse_desc(desc, &sd);
+    if (st != SLIKL_OK) return st;
+    if (!workspace || workspace_bytes < dense_ws_bytes(&sd) || (uintptr_t)workspace % 256 != 0)
+        return SLIKL_ERR_WORKSPACE;
+    int32_t *idx = (int32_t *)((char *)workspace + dense_idx_off(&sd));
+    slikl::Problem pb = problem(&sd);
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (pe.on) {
+        if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) return SLIKL_ERR_LAUNCH;
+        hipEventRecord(e0, (hipStream_t)stream);
+    }
+    hipError_t e = slikl::launch_dense_index(pb, idx, desc->mask_mode, (int)sd.topk, (hipStream_t)stream);
+    if (pe.on) hipEventRecord(e1, (hipStream_t)stream);
+    if (e != hipSuccess) return SLIKL_ERR_LAUNCH;
+    st = grad_impl(&sd, q, k, w, rows_q(&sd) > 0 ? idx : nullptr, p, metadata, dq, dk, dw, y, workspace,
+                   workspace_bytes, stream, pe);
+    if (pe.on) {
+        // the index fill is part of the call's fills
+        float ms = 0.f;
+        if (hipEventSynchronize(e1) == hipSuccess && hipEventElapsedTime(&ms, e0, e1) == hipSuccess)
+            pe.extra_fill_ms = ms;
+        hipEventDestroy(e0);
+        hipEventDestroy(e1);
+    }
+    return st;
+}
+
+}  // namespace
+
+extern "C" {
+
+slikl_status slikl_dense_grad(const slikl_dense_desc *desc, const void *q, const void *k, const float *w,
+                              const float *attn_softmax_l1norm, const int32_t *metadata, void *dq, void *dk,
+                              float *dw, float *softmax_out, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+    PhaseEvents pe;
+    return dense_grad_impl(desc, q, k, w, attn_softmax_l1norm, metadata, dq, dk, dw, softmax_out, workspace,
+                           workspace_bytes, stream, pe);
+}
+
+slikl_status slikl_dense_grad_profiled(const slikl_dense_desc *desc, const void *q, const void *k,
+                                       const float *w, const float *attn_softmax_l1norm,
+                                       const int32_t *metadata, void *dq, void *dk, float *dw,
+                                       float *softmax_out, void *workspace, size_t workspace_bytes,
+                                       void *stream, float *phase_ms) {
+    if (!phase_ms) return SLIKL_ERR_NULLPTR;
+    PhaseEvents pe;
+    pe.on = true;
+    slikl_status st = dense_grad_impl(desc, q, k, w, attn_softmax_l1norm, metadata, dq, dk, dw, softmax_out,
+                                      workspace, workspace_bytes, stream, pe);
+    if (st != SLIKL_OK) return st;
+    if (!pe.collect(phase_ms)) return SLIKL_ERR_LAUNCH;
+    phase_ms[SLIKL_PHASE_FILL] += pe.extra_fill_ms;
+    return SLIKL_OK;
 }
 
 }  // extern "C"

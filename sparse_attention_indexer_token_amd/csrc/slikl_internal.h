@@ -174,6 +174,8 @@ struct ZeroRanges {
     }
 };
 hipError_t launch_zero_ranges(const ZeroRanges &zr, hipStream_t stream);
+// index lists of the dense operator over its L key positions (mask 0 or 3)
+hipError_t launch_dense_index(const Problem &pb, int32_t *idx, int mask_mode, int L, hipStream_t stream);
 hipError_t launch_rowinfo(const Problem &pb, i32x4 *info, hipStream_t stream);
 hipError_t launch_dense_dk_tasks(const Problem &pb, hipStream_t stream);
 hipError_t launch_dense_dk(const Problem &pb, int hp, bool f16, hipStream_t stream);

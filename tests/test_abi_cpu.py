@@ -57,6 +57,16 @@ def test_struct_layout_matches_header():
     assert SliklDesc.seq_used_k.offset == 136
 
 
+def test_other_struct_layouts_match_header():
+    # slikl_dense_desc: slikl_desc then two int32
+    assert ctypes.sizeof(_native.SliklDenseDesc) == 152
+    assert _native.SliklDenseDesc.mask_mode.offset == 144
+    # slikl_attn_p_desc: 4 x int32, 7 x int64, float (+4 bytes of padding), 2 pointers
+    assert ctypes.sizeof(_native.SliklAttnPDesc) == 96
+    assert _native.SliklAttnPDesc.scale.offset == 72
+    assert _native.SliklAttnPDesc.cu_seqlens_q.offset == 80
+
+
 def good_desc(**kw):
     d = SliklDesc()
     d.layout_q = d.layout_k = 0

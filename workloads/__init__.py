@@ -9,10 +9,13 @@ from .gen import (  # noqa: F401
     ATTN_P_WORKLOADS,
     AttnPInputs,
     AttnPWorkload,
+    DENSE_WORKLOADS,
+    DenseInputs,
     Inputs,
     Workload,
     WORKLOADS,
     make_attn_p_inputs,
+    make_dense_inputs,
     make_inputs,
     round_to_bf16,
     round_to_f16,

@@ -351,3 +351,82 @@ ATTN_P_WORKLOADS = {
     "attn_p_dsv32": AttnPWorkload(name="attn_p_dsv32", index=WORKLOADS["dsv32_indexer"], nm=128, dm=576,
                                   scale=1.0 / 192 ** 0.5, seed=2001),
 }
+
+
+# --------------------------------------------------------------------------
+# Inputs of the dense sibling operator: no index lists; p is dense over the key
+# positions and nonzero on the keys the mask shows.
+# --------------------------------------------------------------------------
+@dataclasses.dataclass
+class DenseInputs:
+    wl: Workload
+    mask_mode: int
+    layout_q: str
+    layout_k: str
+    batch: int
+    q: np.ndarray
+    k: np.ndarray
+    q_bits: np.ndarray
+    k_bits: np.ndarray
+    w: np.ndarray
+    p: np.ndarray                # [.., N2, L]
+    cu_q: Optional[np.ndarray]
+    cu_k: Optional[np.ndarray]
+    max_seqlen_q: int
+    max_seqlen_k: int
+
+    @property
+    def t1(self) -> int:
+        return int(self.p.reshape(-1, self.p.shape[-2], self.p.shape[-1]).shape[0])
+
+    @property
+    def visible(self) -> int:
+        return int((self.p > 0).sum())
+
+
+def make_dense_inputs(wl: Workload, mask_mode: int) -> DenseInputs:
+    """q, k, w (and TND lengths) as make_inputs draws them; p from the workload's
+    p recipe over each row's visible keys (maskMode 0: all keys of the batch; 3: keys
+    j <= t + S2_b - S1_b), 0 elsewhere.  The dense axis L is the longest key sequence."""
+    base = make_inputs(dataclasses.replace(wl, topk=1, index_mode="causal"))
+    rp = np.random.Generator(np.random.PCG64(np.random.SeedSequence(wl.seed + 7919)))
+    n2 = base.k.shape[-2]
+    if base.layout_q == BSND:
+        qlens = [base.q.shape[1]] * base.batch
+        klens = [base.k.shape[1]] * base.batch
+    else:
+        qlens = list(np.diff(base.cu_q))
+        klens = list(np.diff(base.cu_k))
+    L = max(klens) if klens else 0
+    rows = []
+    for b in range(base.batch):
+        s1b, s2b = int(qlens[b]), int(klens[b])
+        pb = np.zeros((s1b, n2, L))
+        for t in range(s1b):
+            n = s2b if mask_mode == 0 else max(0, min(s2b, t + s2b - s1b + 1))
+            if n == 0:
+                continue
+            if wl.p_mode == "dirichlet":
+                for g in range(n2):
+                    pb[t, g, :n] = rp.dirichlet(np.full(n, wl.p_alpha))
+            else:
+                lg = rp.normal(0.0, np.sqrt(wl.p_var), size=(n2, n))
+                e = np.exp(lg - lg.max(-1, keepdims=True))
+                pb[t, :, :n] = e / e.sum(-1, keepdims=True)
+        rows.append(pb)
+    if base.layout_q == BSND:
+        p = np.stack(rows, axis=0)
+    else:
+        p = np.concatenate(rows, axis=0) if rows else np.zeros((0, n2, L))
+    return DenseInputs(wl=wl, mask_mode=mask_mode, layout_q=base.layout_q, layout_k=base.layout_k,
+                       batch=base.batch, q=base.q, k=base.k, q_bits=base.q_bits, k_bits=base.k_bits, w=base.w,
+                       p=p.astype(np.float32), cu_q=base.cu_q, cu_k=base.cu_k,
+                       max_seqlen_q=max(qlens) if qlens else 0, max_seqlen_k=L)
+
+
+# The dense operator at the DeepSeek-shaped indexer's width over 2048-key rows (the
+# longest row the fused kernel holds): two sequences of 2048, rightDownCausal mask.
+DENSE_WORKLOADS = {
+    "dense_dsv32_2k": (Workload(name="dense_dsv32_2k", layout=BSND, batch=2, s1=2048, s2=2048, n1=64, n2=1, d=128,
+                                topk=1, dtype="bf16", w_var=1.0 / 8, p_var=2.0, seed=3001), 3),
+}
