@@ -79,6 +79,33 @@ def fused_kernel(strategy, group):
     return "grad_dense8_kernel" if group <= 64 else "grad_dense_kernel"
 
 
+# the library's parts format: 16-bit rows when no key row takes more than this many
+# parts, fp32 rows otherwise (the same threshold as the library's)
+PARTS_I16_MAX_REFS = 1024
+
+
+def max_key_refs(x):
+    """Most valid slots naming one key row (per key head) of the workload."""
+    import numpy as np
+    n2 = x.idx.shape[-2]
+    flat = x.idx.reshape(-1, n2, x.idx.shape[-1])
+    if x.layout_q == "BSND":
+        rows_b = np.repeat(np.arange(x.batch), flat.shape[0] // x.batch)
+    else:
+        rows_b = np.repeat(np.arange(x.batch), np.diff(x.cu_q))
+    if x.layout_k == "BSND":
+        kbase = np.arange(x.batch) * x.k.shape[1]
+    else:
+        kbase = np.asarray(x.cu_k[:-1])
+    best = 0
+    for g in range(n2):
+        ids = flat[:, g, :]
+        keys = (ids + kbase[rows_b][:, None])[ids >= 0]
+        if keys.size:
+            best = max(best, int(np.bincount(keys).max()))
+    return best
+
+
 def phase_work(strategy, wl, x, det):
     """Algorithmic work of each timed phase's kernel per launch:
     {phase: (kernel, bound, amount, unit)} with amount in FLOP ("mfma") or HBM bytes
@@ -101,11 +128,13 @@ def phase_work(strategy, wl, x, det):
         # the method's dK contraction dS^T q: one G x D contraction per valid slot
         work["dk"] = ("dense_dk_kernel", "mfma", 2.0 * G * D * V, "FLOP")
     if strategy == "sorted":
-        # each valid slot's fp32 part written once, with its record (key, dI, head words)
-        # read; q read once
-        work["dk"] = ("scatter_dk_kernel", "hbm", V * (4.0 * D + 8 + 4 * nh) + x.t1 * wl.n1 * D * 2.0, "B")
-        # the parts and the sorted list read once, the fp32 accumulator written once
-        work["dk_reduce"] = ("sorted_reduce_kernel", "hbm", V * (4.0 * D + 4) + x.t2 * wl.n2 * D * 4.0, "B")
+        # each valid slot's part written once (16-bit or fp32 elements, and its
+        # multiplier), with its record (key, dI, head words) read; q read once
+        eb = 2.0 if max_key_refs(x) <= PARTS_I16_MAX_REFS else 4.0
+        work["dk"] = ("scatter_dk_kernel", "hbm", V * (eb * D + 12 + 4 * nh) + x.t1 * wl.n1 * D * 2.0, "B")
+        # the parts, their multipliers and the sorted list read once, the fp32
+        # accumulator written once
+        work["dk_reduce"] = ("sorted_reduce_kernel", "hbm", V * (eb * D + 8) + x.t2 * wl.n2 * D * 4.0, "B")
         work["dk_final"] = ("finalize_kernel", "hbm", x.t2 * wl.n2 * D * (acc_elem + 2.0), "B")
     return work
 
@@ -487,7 +516,7 @@ def main():
     # the workload's own bound: MFMA on the nominal FLOP, HBM on the compulsory bytes,
     # the K gather (both passes read D 16-bit values per valid slot) and the dK scatter
     # (D fp32 adds per valid slot); in deterministic mode with the sorted or scatter
-    # strategy also the parts' round trip (written and read once as fp32)
+    # strategy also the parts' round trip (written and read once)
     comp = compulsory_bytes(wl, x)
     gather = 2.0 * x.valid_slots * wl.d * 2.0
     scatter = x.valid_slots * wl.d * 4.0
@@ -504,7 +533,8 @@ def main():
         if (phase_ms.get("fused") if strategy == "scatter" else dk_ms) else None,
     }
     if det and strategy in ("sorted", "scatter"):
-        parts = 2.0 * x.valid_slots * wl.d * 4.0
+        eb = 2.0 if strategy == "sorted" and max_key_refs(x) <= PARTS_I16_MAX_REFS else 4.0
+        parts = 2.0 * x.valid_slots * wl.d * eb
         step_bound["hbm_bytes_with_parts"] = comp + parts
         step_bound["hbm_frac_with_parts"] = (comp + parts) / t_step / 1e9 / PEAK_HBM_GBPS
     step_bound["bound"] = {"long_context": "gather", "contention_det": "hbm"}.get(wl.name, "mfma")

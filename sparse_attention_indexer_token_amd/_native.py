@@ -191,8 +191,7 @@ def grad_profiled_raw(desc: SliklDesc, q, k, w, idx, p, metadata, dq, dk, dw, y,
 def noalloc_strategy(desc: SliklDesc) -> str:
     out = c_int32(0)
     _check(load().slikl_grad_noalloc_strategy(ctypes.byref(desc), ctypes.byref(out)),
-           "slikl_grad_noalloc_strategy", "slikl_attn_softmax_l1norm", "slikl_dense_grad_workspace_size",
-           "slikl_dense_grad_metadata", "slikl_dense_grad", "slikl_dense_grad_profiled")
+           "slikl_grad_noalloc_strategy")
     return {v: k for k, v in DK_MODE.items()}[int(out.value)]
 
 

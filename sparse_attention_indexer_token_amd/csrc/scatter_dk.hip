@@ -10,17 +10,26 @@
 //
 // A workgroup of four waves walks units.  Per unit:
 //   q       fp16 of q 2^eq (bf16 inputs: a per-unit power of two, exact) into LDS as
-//           [d][head], read from there as the B operands of 32x32x16 MFMA (k = 16
-//           heads, n = 32 d);
+//           [d][head], read from there as the A operands of 32x32x16 MFMA (k = 16
+//           heads, m = 32 d);
 //   w       fp16 high and low parts of w 2^ew for the lane's k elements (w carried to
 //           about 22 bits, as in the dense dK kernel);
-//   slots   chunks of 32 per wave (32x32x16 MFMA, k = 16 heads): A = the head-masked
-//           w parts (rows = slots), two MFMAs per head step and d tile give P' (rows =
-//           slots, columns = d), scaled in fp32 by the slot's dI and 2^-(eq + ew) and
-//           stored (fp32) as row o = unit * topk + position of the parts buffer (the
-//           slots of a chunk are consecutive rows); a reduction sums the rows of each
-//           key through the key-sorted record list.  Neighbouring lanes swap one value
-//           so that each store writes a pair of consecutive d of one row.
+//   slots   chunks of 32 per wave (32x32x16 MFMA, k = 16 heads): A = q (rows = d), B =
+//           the head-masked w parts (columns = slots), two MFMAs per head step and d
+//           tile give R = sum_h 1[S > 0] w[h] q[h, :] 2^(eq + ew) per slot, each lane
+//           holding half of one slot's row.  The row is stored as 16-bit integers
+//           R 2^e with a per-slot exponent e from its largest element m (m 2^e in
+//           [2^14, 2^15), so the rounding error is at most 2^-15 m), as row o = unit *
+//           topk + position of the parts buffer (the slots of a chunk are consecutive
+//           rows), and the record's dI is overwritten by the multiplier
+//           dI 2^-(eq + ew + e) that turns the integers back into the part P[s, :].
+//           Half the bytes of fp32 rows, with 15 to 16 significant bits where the part
+//           is largest: the parts buffer is written once and read once, and its
+//           traffic bounds the strategy.  When the key sort finds a key taking more
+//           than kPartsI16MaxRefs parts (an attention sink), the rounding errors of
+//           its many parts could add up past the dk tolerance, and the rows are stored
+//           in fp32 instead (same multiplier, without 2^-e).  A reduction sums the
+//           rows of each key through the key-sorted record list.
 //   records the unit's head words and dI are staged in LDS at the unit's start, every
 //           load issued before the first wait (one memory latency per unit, not one
 //           per chunk).
@@ -40,11 +49,6 @@ typedef __attribute__((address_space(3))) void lds_void_sd;
 // vmcnt(0) with the other counters left alone (gfx9 s_waitcnt encoding)
 __device__ __forceinline__ void wait_vm_all() { __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); }
 
-// the value of the neighbouring lane (lane ^ 1), a DPP quad permute [1, 0, 3, 2]
-__device__ __forceinline__ float swap_pair(float x) {
-    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false));
-}
-
 constexpr uint32_t kSdPadOffset = 0x80000000u;      // past the end of every buffer view
 
 }  // namespace
@@ -54,7 +58,7 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
     constexpr int NH = HP / 32;      // head words per slot
     constexpr int NKH = HP / 16;     // 16-head k-steps (32x32x16 MFMA)
     constexpr int NDT = D / 32;      // 32-wide d tiles
-    // fp16 q 2^eq as [d][head], rows padded by 4 heads: the B-operand reads (lane = d row)
+    // fp16 q 2^eq as [d][head], rows padded by 4 heads: the A-operand reads (lane = d row)
     // then fall on distinct LDS banks instead of a bank every 64 or 128 bytes
     constexpr int QS = HP + 4;
     __shared__ __attribute__((aligned(16))) uint16_t s_qt[D * QS];
@@ -66,6 +70,10 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, half = lane >> 5;
     const int U = (int)(pb.t1 * pb.n2), G = pb.group, topk = pb.topk;
+    // row format (uniform): 16-bit integers unless some key takes many parts
+    const bool i16 = *pb.sort_maxref <= kPartsI16MaxRefs;
+    int16_t *const parts16 = (int16_t *)pb.dk_parts;
+    float *const parts32 = (float *)pb.dk_parts;
 
     for (int u = blockIdx.x; u < U; u += gridDim.x) {
         const int cnt = pb.srec_cnt[u];
@@ -160,7 +168,7 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
             }
         wait_vm_all();            // this wave's record copies have landed in LDS
         __syncthreads();
-        // B operands (read from LDS at their use): column d = 32 dt + l32, k elements as
+        // A operands (read from LDS at their use): row d = 32 dt + l32, k elements as
         // above (two runs of 4 heads)
         auto bq = [&](int kh, int dt) {
             const uint16_t *col = s_qt + (32 * dt + l32) * QS + 16 * kh + 4 * half;
@@ -170,7 +178,8 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
         const float part_mul = ldexpf(1.f, -(eq + ew));
         // the unit's rows of the parts buffer (slots past the valid count stored nowhere)
         const __amdgpu_buffer_rsrc_t rparts =
-            __builtin_amdgcn_make_buffer_rsrc((void *)(pb.dk_parts + ubase * D), (short)0, topk * D * 4, 0x00020000);
+            i16 ? __builtin_amdgcn_make_buffer_rsrc((void *)(parts16 + ubase * D), (short)0, topk * D * 2, 0x00020000)
+                : __builtin_amdgcn_make_buffer_rsrc((void *)(parts32 + ubase * D), (short)0, topk * D * 4, 0x00020000);
 
         // ---- slot chunks: 32 per wave, records from LDS ------------------------------------
         for (int c0 = wave * 32; c0 < cnt; c0 += 32 * kSdWaves) {
@@ -181,8 +190,7 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
 #pragma unroll
             for (int h = 0; h < NH; ++h) mw[h] = ok ? s_mw[pc * NH + h] : 0u;
             const float dIv = ok ? s_dI[pc] : 0.f;
-            const int pv = ok ? p : -1;
-            // A operand: row = slot l32 of the chunk
+            // B operand: column = slot l32 of the chunk
             u32x4 ah[NKH], al[NKH];
 #pragma unroll
             for (int kh = 0; kh < NKH; ++kh) {
@@ -196,43 +204,97 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
                     al[kh][pr] = wl[kh][pr] & msk;
                 }
             }
-            const float dIs = dIv * part_mul;
-            const int pvc = pv;
-            // output pair jp = rows 8 (jp/2) + 4 half + 2 (jp%2) + {0, 1} (output element j
-            // of 32x32 MFMA sits at row 8 (j/4) + 4 half + j%4); after the swap an even lane
-            // holds the first row, an odd lane the second: its scaled dI and parts row
-            const int odd = l32 & 1;
-            float sdI[8];
-            int spos[8];
-#pragma unroll
-            for (int jp = 0; jp < 8; ++jp) {
-                const int sel = 8 * (jp >> 1) + 4 * half + 2 * (jp & 1) + odd;
-                sdI[jp] = __shfl(dIs, sel);
-                spos[jp] = __shfl(pvc, sel);
-            }
-#pragma unroll
-            for (int dt = 0; dt < NDT; ++dt) {
+            // R^T = q^T (masked w): element j of lane l is d = 32 dt + 8 (j/4) + 4 half + j%4
+            // of slot l32, so each lane holds half of its slot's row.  The tiles are formed
+            // twice, for the row's largest |R| and then for the stores, rather than kept
+            // live together (the MFMA work is small beside the stores)
+            auto tile = [&](int dt) {
                 f32x16 pa = {};
 #pragma unroll
                 for (int kh = 0; kh < NKH; ++kh) {
                     const u32x4 b = bq(kh, dt);
-                    pa = mfma32<true>(ah[kh], b, pa);
-                    pa = mfma32<true>(al[kh], b, pa);
+                    pa = mfma32<true>(b, ah[kh], pa);
+                    pa = mfma32<true>(b, al[kh], pa);
                 }
+                return pa;
+            };
+            if (!i16) {
+                // fp32 rows: R as formed, the multiplier dI 2^-(eq + ew).  Element group
+                // g of a lane is d = 32 dt + 8 g + 4 half + 0..3 of its slot
+                if (ok && half == 0) pb.srec_dI[ubase + p] = dIv * part_mul;
 #pragma unroll
-                for (int jp = 0; jp < 8; ++jp) {
-                    // even lane: own e0 and its neighbour's e0; odd lane: its neighbour's e1
-                    // and own e1.  Selecting between an element and a swapped value (never
-                    // between two neighbouring elements) keeps the select from turning into
-                    // a run-time index into the MFMA result, which compiles to a compare chain
-                    const float e0 = pa[2 * jp], e1 = pa[2 * jp + 1];
-                    const float s0 = swap_pair(e0), s1 = swap_pair(e1);
-                    const float lo = odd ? s1 : e0, hi = odd ? e1 : s0;
-                    const uint32_t off = spos[jp] >= 0
-                                             ? (uint32_t)((spos[jp] * D + 32 * dt + (l32 & ~1)) * 4)
-                                             : kSdPadOffset;
-                    __builtin_amdgcn_raw_buffer_store_b64(
-                        u32x2{__float_as_uint(lo * sdI[jp]), __float_as_uint(hi * sdI[jp])}, rparts, off, 0, 0);
+                for (int dt = 0; dt < NDT; ++dt) {
+                    const f32x16 pa = tile(dt);
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const uint32_t off = ok ? (uint32_t)((p * D + 32 * dt + 8 * g + 4 * half) * 4) : kSdPadOffset;
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            u32x4{__float_as_uint(pa[4 * g]), __float_as_uint(pa[4 * g + 1]),
+                                  __float_as_uint(pa[4 * g + 2]), __float_as_uint(pa[4 * g + 3])},
+                            rparts, off, 0, 0);
+                    }
+                }
+                continue;
+            }
+            // the row's largest |R|
+            float m = 0.f;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const f32x16 pa = tile(dt);
+#pragma unroll
+                for (int j = 0; j < 16; ++j) m = fmaxf(m, fabsf(pa[j]));
+            }
+            {
+                const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+                m = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+            }
+            // operands the compiler cannot see through, so that the second round of tiles
+            // is formed again instead of kept from the first
+#pragma unroll
+            for (int kh = 0; kh < NKH; ++kh) asm volatile("" : "+v"(ah[kh]), "+v"(al[kh]));
+            // exponent: m 2^e in [2^14, 32767.5), so that every element rounds into the
+            // 16-bit range; the rounding error is then at most 2^-15 of m
+            int ex = 0;
+            frexpf(m, &ex);
+            int e = m > 0.f ? 15 - ex : 0;
+            e = e > 126 ? 126 : e;
+            if (ldexpf(m, e) >= 32767.5f) --e;
+            const float sc = ldexpf(1.f, e);
+            // the multiplier that turns the stored integers back into the part,
+            // dI 2^-(eq + ew) 2^-e, written over the record's dI
+            if (ok && half == 0) pb.srec_dI[ubase + p] = ldexpf(dIv * part_mul, -e);
+            // round R 2^e to integers (|R 2^e| < 32767.5): adding 1.5 2^23 leaves the
+            // integer, rounded to nearest even, in the low 16 bits of the sum
+            constexpr float kMagic = 12582912.f;
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) {
+                const f32x16 pa = tile(dt);
+                uint32_t wd[8];          // word 2 g + c: d = 32 dt + 8 g + 4 half + 2 c + {0, 1}
+#pragma unroll
+                for (int k2 = 0; k2 < 8; ++k2) {
+                    const float lo = fmaf(pa[2 * k2], sc, kMagic);
+                    const float hi = fmaf(pa[2 * k2 + 1], sc, kMagic);
+                    wd[k2] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x05040100u);
+                }
+                // exchange with the other half (lane l ^ 32) so that a lane holds 8
+                // consecutive d: half 0 keeps group 2 g2 and takes half 1's, half 1 takes
+                // group 2 g2 + 1 of half 0 and keeps its own
+                uint32_t o[8];
+#pragma unroll
+                for (int g2 = 0; g2 < 2; ++g2)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        const uint32_t ev = wd[4 * g2 + c], od = wd[4 * g2 + 2 + c];
+                        const uint32_t t = (uint32_t)__shfl_xor((int)(half ? ev : od), 32);
+                        o[4 * g2 + c] = half ? t : ev;
+                        o[4 * g2 + 2 + c] = half ? od : t;
+                    }
+                // chunk g2: d = 32 dt + 16 g2 + 8 half .. + 7
+#pragma unroll
+                for (int g2 = 0; g2 < 2; ++g2) {
+                    const uint32_t off = ok ? (uint32_t)((p * D + 32 * dt + 16 * g2 + 8 * half) * 2) : kSdPadOffset;
+                    __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[4 * g2], o[4 * g2 + 1], o[4 * g2 + 2], o[4 * g2 + 3]},
+                                                           rparts, off, 0, 0);
                 }
             }
         }
@@ -241,16 +303,10 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
 }
 
 // The body under the register budget of four workgroups per compute unit (32-head
-// groups with D = 32), three (32-head groups, D = 64 or 128), two (64-head groups) or
-// one (128-head groups, which need the whole register file): the most that run without
-// spills.
+// groups), two (64-head groups) or one (128-head groups, which need the whole register
+// file): the most that run without spills.
 template <int HP, int D, bool F16>
 __global__ __launch_bounds__(kSdBlock, 4) void scatter_dk_kernel4(Problem pb) {
-    scatter_dk_body<HP, D, F16>(pb);
-}
-
-template <int HP, int D, bool F16>
-__global__ __launch_bounds__(kSdBlock, 3) void scatter_dk_kernel3(Problem pb) {
     scatter_dk_body<HP, D, F16>(pb);
 }
 
@@ -270,9 +326,8 @@ static hipError_t launch_sd(const Problem &pb, hipStream_t stream) {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return hipErrorInvalidDevice;
-    auto kern = HP > 64   ? scatter_dk_kernel1<HP, D, F16>
-                : HP > 32 ? scatter_dk_kernel2<HP, D, F16>
-                : D <= 32 ? scatter_dk_kernel4<HP, D, F16> : scatter_dk_kernel3<HP, D, F16>;
+    auto kern = HP > 64 ? scatter_dk_kernel1<HP, D, F16> : HP > 32 ? scatter_dk_kernel2<HP, D, F16>
+                                                           : scatter_dk_kernel4<HP, D, F16>;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, kSdBlock, 0) != hipSuccess || per <= 0) per = 1;
     const int64_t U = pb.t1 * pb.n2;
     int64_t grid = (int64_t)cus * per;

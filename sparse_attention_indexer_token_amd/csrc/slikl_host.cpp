@@ -115,7 +115,8 @@ int dk_strategy(const slikl_desc *d) {
 }
 
 // The key-sorted variant of the scatter strategy: every valid slot's part written once
-// as an fp32 row of a buffer, then summed per key through a key-sorted record list.
+// as a row of a buffer (16-bit integers with a per-slot multiplier, or fp32 when a key
+// takes many parts), then summed per key through a key-sorted record list.
 // Asked for explicitly (SORTED), or taken by AUTO where the dense strategy is not and
 // there are at least 2048 units (below that its extra launches cost more than the
 // atomics they save) and the parts buffer fits in 8 GiB.  Measured on long_context
@@ -442,7 +443,8 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
         pb.sort_tmp = (int32_t *)(ws + wp.tmp_off);
         pb.sort_list = (int32_t *)(ws + wp.list_off);
         pb.bin_start = (int32_t *)(ws + wp.bin_off);
-        pb.dk_parts = (float *)(ws + wp.parts_off);
+        pb.dk_parts = ws + wp.parts_off;
+        pb.sort_maxref = (int32_t *)(ws + wp.scale_off) + 8;      // in the zeroed scale block
         pb.sort_shift = g.shift;
         pb.sort_nbuckets = g.nbuckets;
         pb.sort_tile = g.tile;

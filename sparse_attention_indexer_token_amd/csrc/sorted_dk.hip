@@ -4,9 +4,10 @@
 // Follows the formula section of the operator page "aclnnSparseLightningIndexerKLLossGrad":
 // dK is the scatter-add of every valid slot's part dS^T q into the key row that
 // sparseIndices names.  Instead of adding the parts with atomics, the scatter dK kernel
-// writes part o (o = unit * topk + position of a valid slot record) as fp32 row o of a
-// parts buffer, and the rows are summed per bin = key row * N2 + key head through a list
-// of the records sorted by bin:
+// writes part o (o = unit * topk + position of a valid slot record) as row o of a parts
+// buffer (16-bit integers, or fp32 when some bin holds more than kPartsI16MaxRefs
+// records, with a per-record fp32 multiplier), and the rows are summed per bin = key
+// row * N2 + key head through a list of the records sorted by bin:
 //   bucket count    records cut into tiles; per tile a histogram over key buckets
 //                   (bin >> shift) in LDS, written as column `tile` of [bucket][tile];
 //   scan            exclusive prefix of that matrix in bucket-major order (so each
@@ -14,7 +15,8 @@
 //   bucket scatter  per tile, each record takes a place in its bucket's range by an LDS
 //                   atomic; (bin, record) pairs -> tmp;
 //   bucket sort     one workgroup per bucket: an LDS histogram over its bins, its prefix
-//                   -> start[bin], then each record placed by an LDS atomic -> list.
+//                   -> start[bin] (and the most records of one bin -> sort_maxref),
+//                   then each record placed by an LDS atomic -> list.
 //   reduce          the sorted list split evenly over the waves; each wave gathers its
 //                   rows and sums them bin by bin in fp32 (int64 fixed point when
 //                   deterministic: exact, so the sum does not depend on the order of a
@@ -168,8 +170,19 @@ __global__ __launch_bounds__(kSortThreads) void bucket_sort_kernel(Problem pb, i
     // exclusive prefix of the bin counts: thread t owns bins [t * run, (t + 1) * run)
     const int run = (per + kSortThreads - 1) / kSortThreads;
     const int b0 = threadIdx.x * run;
-    int s = 0;
-    for (int i = 0; i < run; ++i) s += b0 + i < per ? h[b0 + i] : 0;
+    int s = 0, mx = 0;
+    for (int i = 0; i < run; ++i) {
+        const int c = b0 + i < per ? h[b0 + i] : 0;
+        s += c;
+        mx = c > mx ? c : mx;
+    }
+    // the most records of one bin, for the parts' storage format
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const int v = __shfl_xor(mx, o);
+        mx = v > mx ? v : mx;
+    }
+    if ((threadIdx.x & 63) == 0 && mx > 0) atomicMax(pb.sort_maxref, mx);
     int total = 0;
     int acc = block_excl_scan<kSortThreads / 64>(s, tmp, &total);
     __syncthreads();                      // every count read before the prefix overwrites it
@@ -194,9 +207,10 @@ constexpr int kRedWaves = 4;
 constexpr int kRedUnroll = 16;
 
 // One wave per contiguous run of the sorted list; lane l holds d = 2l, 2l + 1 of the
-// rows it names (lanes past D/2 idle).
-template <int D, bool DET>
-__global__ __launch_bounds__(64 * kRedWaves) void sorted_reduce_kernel(Problem pb, int nbins) {
+// rows it names (lanes past D/2 idle).  A row's part is its values (16-bit integers or
+// fp32) times the record's multiplier (stored over its dI by the parts kernel).
+template <int D, bool DET, bool I16>
+__device__ __forceinline__ void sorted_reduce_body(const Problem &pb, int nbins) {
     const int lane = threadIdx.x & 63;
     const int gw = blockIdx.x * kRedWaves + (threadIdx.x >> 6);
     const int W = gridDim.x * kRedWaves;
@@ -255,7 +269,9 @@ __global__ __launch_bounds__(64 * kRedWaves) void sorted_reduce_kernel(Problem p
         }
     };
 
-    const float2 *rows = (const float2 *)pb.dk_parts;
+    const uint32_t *rows16 = (const uint32_t *)pb.dk_parts;
+    const float2 *rows32 = (const float2 *)pb.dk_parts;
+    const float *mult = pb.srec_dI;
     const int32_t *list = pb.sort_list;
     // list entries (wave-uniform) of the next batch are loaded while this batch's rows
     // are in flight
@@ -264,9 +280,18 @@ __global__ __launch_bounds__(64 * kRedWaves) void sorted_reduce_kernel(Problem p
     for (int i = 0; i < kRedUnroll; ++i) on[i] = r0 + i < r1 ? list[r0 + i] : 0;
     for (int r = r0; r < r1; r += kRedUnroll) {
         float2 v[kRedUnroll];
+        float mu[kRedUnroll];
 #pragma unroll
-        for (int i = 0; i < kRedUnroll; ++i)
-            v[i] = act && r + i < r1 ? rows[(size_t)on[i] * (D / 2) + lane] : make_float2(0.f, 0.f);
+        for (int i = 0; i < kRedUnroll; ++i) {
+            const bool ld = act && r + i < r1;
+            if constexpr (I16) {
+                const uint32_t x = ld ? rows16[(size_t)on[i] * (D / 2) + lane] : 0u;
+                v[i] = make_float2((float)(int16_t)(x & 0xffffu), (float)(int16_t)(x >> 16));
+            } else {
+                v[i] = ld ? rows32[(size_t)on[i] * (D / 2) + lane] : make_float2(0.f, 0.f);
+            }
+            mu[i] = mult[on[i]];
+        }
 #pragma unroll
         for (int i = 0; i < kRedUnroll; ++i) {
             const int rn = r + kRedUnroll + i;
@@ -286,16 +311,24 @@ __global__ __launch_bounds__(64 * kRedWaves) void sorted_reduce_kernel(Problem p
                     be = start[b + 1];
                 } while (be <= rr);
             }
+            const float x0 = v[i].x * mu[i];
+            const float x1 = v[i].y * mu[i];
             if constexpr (DET) {
-                i0 += __float2ll_rn(v[i].x * det_mul);
-                i1 += __float2ll_rn(v[i].y * det_mul);
+                i0 += __float2ll_rn(x0 * det_mul);
+                i1 += __float2ll_rn(x1 * det_mul);
             } else {
-                a0 += v[i].x;
-                a1 += v[i].y;
+                a0 += x0;
+                a1 += x1;
             }
         }
     }
     flush();
+}
+
+template <int D, bool DET>
+__global__ __launch_bounds__(64 * kRedWaves) void sorted_reduce_kernel(Problem pb, int nbins) {
+    if (*pb.sort_maxref <= kPartsI16MaxRefs) sorted_reduce_body<D, DET, true>(pb, nbins);
+    else sorted_reduce_body<D, DET, false>(pb, nbins);
 }
 
 int device_cus() {
