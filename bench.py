@@ -176,15 +176,21 @@ def parse():
     return ap.parse_args()
 
 
-def cpu_baseline(x, n_rows):
-    import numpy as np
-    from oracle import slikl_grad_ref
+def host_threads():
+    """(cores this process may run on, BLAS threads of the NumPy oracle)."""
     cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
         blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:       # threadpoolctl missing: the BLAS count is unknown
         blas = None
+    return cores, blas
+
+
+def cpu_baseline(x, n_rows):
+    import numpy as np
+    from oracle import slikl_grad_ref
+    cores, blas = host_threads()
     stride = max(1, x.t1 // max(1, n_rows))
     rows = np.arange(0, x.t1, stride)[:n_rows]
     t0 = time.perf_counter()
@@ -293,14 +299,18 @@ def run_attn_p(args, wl_name):
     }
     if not args.no_cpu_baseline:
         from oracle import attn_softmax_l1norm_ref
-        rows = np.arange(0, x.t1, max(1, x.t1 // 64))[:64]
+        # about 10 s of oracle work: each row is Nm x Dm x topk fp64 products
+        n = max(1, min(x.t1, args.cpu_rows // 2))
+        rows = np.arange(0, x.t1, max(1, x.t1 // n))[:n]
+        cores, blas = host_threads()
         t0 = time.perf_counter()
         attn_softmax_l1norm_ref(x.qm, x.km, x.idx, scale=wl.scale, layout_q=x.layout_q, layout_k=x.layout_k,
                                 cu_seqlens_q=x.cu_q, cu_seqlens_k=x.cu_k, rows=rows)
         dt = time.perf_counter() - t0
-        res["cpu_baseline"] = {"value": len(rows) / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
-                               "kind": "oracle", "sample": f"{len(rows)} query rows (evenly spaced), fp64 NumPy "
-                                                           f"oracle of p, {dt:.1f} s wall"}
+        res["cpu_baseline"] = {"value": len(rows) / dt, "unit": "tokens/s", "cores": int(blas or cores),
+                               "kind": "oracle", "affinity_cores": cores, "blas_threads": blas,
+                               "sample": f"{len(rows)} query rows (evenly spaced) of the same workload, fp64 "
+                                         f"NumPy oracle of p, {dt:.1f} s wall"}
     print(json.dumps(res), flush=True)
     return 0
 
@@ -393,14 +403,17 @@ def run_dense(args, wl_name):
     }
     if not args.no_cpu_baseline:
         from oracle import dense_grad_ref
-        rows = np.arange(0, x.t1, max(1, x.t1 // 256))[:256]
+        n = max(1, min(x.t1, args.cpu_rows))
+        rows = np.arange(0, x.t1, max(1, x.t1 // n))[:n]
+        cores, blas = host_threads()
         t0 = time.perf_counter()
         dense_grad_ref(x.q, x.k, x.w, x.p, mask_mode=mask, layout_q=x.layout_q, layout_k=x.layout_k,
                        cu_seqlens_q=x.cu_q, cu_seqlens_k=x.cu_k, rows=rows)
         dt = time.perf_counter() - t0
-        res["cpu_baseline"] = {"value": len(rows) / dt, "unit": "tokens/s", "cores": len(os.sched_getaffinity(0)),
-                               "kind": "oracle", "sample": f"{len(rows)} query rows (evenly spaced), fp64 NumPy "
-                                                           f"oracle of the dense operator, {dt:.1f} s wall"}
+        res["cpu_baseline"] = {"value": len(rows) / dt, "unit": "tokens/s", "cores": int(blas or cores),
+                               "kind": "oracle", "affinity_cores": cores, "blas_threads": blas,
+                               "sample": f"{len(rows)} query rows (evenly spaced) of the same workload, fp64 "
+                                         f"NumPy oracle of the dense operator, {dt:.1f} s wall"}
     print(json.dumps(res), flush=True)
     return 0
 
