@@ -27,10 +27,15 @@ int64_t len_q(const slikl_desc *d) { return d->layout_q == SLIKL_LAYOUT_BSND ? d
 int64_t len_k(const slikl_desc *d) { return d->layout_k == SLIKL_LAYOUT_BSND ? d->s2 : d->max_seqlen_k; }
 bool any_tnd(const slikl_desc *d) { return d->layout_q == SLIKL_LAYOUT_TND || d->layout_k == SLIKL_LAYOUT_TND; }
 // 32-key tiles per wave of the dense dK kernel: the kernel fetches a query row's q once
-// per key block that its named keys meet; when q is too large to stay in the on-die
-// caches (more than 128 MiB) blocks of twice the keys halve those fetches from HBM
+// per key block that its named keys meet.  Blocks of twice the keys halve those fetches
+// where they dominate: when q is too large to stay in the on-die caches (more than 128
+// MiB), or when rows name few keys of the blocks they meet (top-k lists of at most an
+// eighth of the longest key sequence: measured on the contention workload, dK 3.5 ->
+// 2.1 ms, where the dense dsv32 lists run better with 128-key blocks).
 int dense_kt(const slikl_desc *d) {
-    return (double)rows_q(d) * d->n1 * d->d * 2.0 > 128.0 * (1 << 20) ? 2 : 1;
+    const bool big_q = (double)rows_q(d) * d->n1 * d->d * 2.0 > 128.0 * (1 << 20);
+    const bool sparse_rows = len_k(d) >= 8 * d->topk;
+    return big_q || sparse_rows ? 2 : 1;
 }
 
 // Field checks of the operator page's constraints section (dtypes, layouts,
