@@ -197,6 +197,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_p_kernel(AttnPProblem pb) {
         }
         float mxv[1] = {0.f}, smv[1] = {0.f};
         int nvalid;
+        static_assert(kSPT < 16, "block_scan_reduce counts below 16");
         int pos = block_scan_reduce<1, 1, kWaves>(cnt, mxv, smv, s_red, &nvalid);
         int mypos[kSPT];
 #pragma unroll

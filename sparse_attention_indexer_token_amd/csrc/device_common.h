@@ -150,6 +150,21 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
+// Exclusive prefix of v (0 <= v < 16) over the wave and the wave's total, from four lane
+// masks (one per bit of v) and their population counts below each lane: no data moves
+// between lanes.
+__device__ __forceinline__ int wave_excl_scan16(int v, int *wave_total) {
+    int pre = 0, tot = 0;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        const uint64_t m = __builtin_amdgcn_ballot_w64(((v >> b) & 1) != 0);
+        pre += (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
+        tot += __popcll(m) << b;
+    }
+    *wave_total = tot;
+    return pre;
+}
+
 // Block-wide reductions for a block of NW wavefronts; `red` holds >= NW floats.
 template <int NW = 4>
 __device__ __forceinline__ float block_max(float v, float *red) {
@@ -215,25 +230,21 @@ __device__ __forceinline__ void block_reduce_multi(float (&mx)[NM], float (&sm)[
         sm[i] = (red[NM + i] + red[(NM + NS) + NM + i]) + (red[2 * (NM + NS) + NM + i] + red[3 * (NM + NS) + NM + i]);
 }
 
-// Exclusive prefix sum of v over the block (returned; the total in *total)
-// together with block maxima of mx[] and sums of sm[], with one barrier pair.
+// Exclusive prefix sum of v (0 <= v < 16) over the block (returned; the total in
+// *total) together with block maxima of mx[] and sums of sm[], with one barrier pair.
 // `red` holds at least NW * (1 + NM + NS) floats.
 template <int NM, int NS, int NW = 4>
 __device__ __forceinline__ int block_scan_reduce(int v, float (&mx)[NM], float (&sm)[NS], float *red, int *total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     constexpr int W = 1 + NM + NS;
-    int x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        int y = __shfl_up(x, o);
-        if (lane >= o) x += y;
-    }
+    int wtot;
+    const int x = wave_excl_scan16(v, &wtot) + v;          // inclusive within the wave
 #pragma unroll
     for (int i = 0; i < NM; ++i) mx[i] = wave_max(mx[i]);
 #pragma unroll
     for (int i = 0; i < NS; ++i) sm[i] = wave_sum(sm[i]);
     lds_barrier();
-    if (lane == 63) red[wave * W] = __int_as_float(x);
+    if (lane == 0) red[wave * W] = __int_as_float(wtot);
     if (lane == 0) {
 #pragma unroll
         for (int i = 0; i < NM; ++i) red[wave * W + 1 + i] = mx[i];

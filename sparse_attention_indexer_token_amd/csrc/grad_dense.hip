@@ -263,6 +263,7 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
         float mxv[3] = {pmx, kmx, kmn_neg};
         float smv[1] = {pabs};
         int nvalid;
+        static_assert(SPT_MAX < 16, "block_scan_reduce counts below 16");
         int pos = block_scan_reduce<3, 1>(cnt, mxv, smv, s_red, &nvalid);
         const float pmax = mxv[0], psum = smv[0];
         const int kmax_i = (int)mxv[1];
