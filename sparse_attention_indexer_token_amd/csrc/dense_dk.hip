@@ -46,15 +46,20 @@ typedef __attribute__((address_space(3))) void lds_void_t2;
 constexpr int kDkWaves = 4;
 constexpr int kDkBlock = 64 * kDkWaves;
 
-template <int HP, int D, int KT_ = 1>
+// HP: the head padding of the records (head words and w records are laid out for HP
+// heads); HK: the heads the MFMAs cover, a multiple of 16 no smaller than the group
+// (16 for groups of up to 16 heads padded to 32: the k-step over heads 16..31 would
+// only multiply zeros, and the q tile is half the size).
+template <int HP, int D, int KT_ = 1, int HK = HP>
 struct DenseCfg {
+    static_assert(HK % 16 == 0 && HK <= HP, "computed heads");
     static constexpr int NH = HP / 32;          // head words per key
-    static constexpr int NKH = HP / 16;         // k-steps over heads
+    static constexpr int NKH = HK / 16;         // k-steps over heads
     static constexpr int NDT = D / 32;          // d tiles
     static constexpr int DCH = D / 8;           // 16-byte chunks per q row
     static constexpr int KT = KT_;              // 32-key tiles per wave
     static constexpr int KB = 32 * KT * kDkWaves;  // keys per workgroup
-    static constexpr int QBYTES = HP * D * 2;   // q tile
+    static constexpr int QBYTES = HK * D * 2;   // q tile
     static constexpr int NQC = QBYTES / 1024;   // its 1 KiB copies
     static constexpr int MBYTES = KB * NH * 4;  // head words of the block's keys
     static constexpr int NMC = (MBYTES + 1023) / 1024;
@@ -120,9 +125,9 @@ __device__ __forceinline__ int2 dense_rows(const Problem &pb, int b) {
     return int2{pb.cu_q[b], pb.cu_q[b + 1]};
 }
 
-template <int HP, int D, bool F16, int KT>
+template <int HP, int D, bool F16, int KT, int HK>
 __device__ __forceinline__ void dense_dk_body(const Problem &pb) {
-    using C = DenseCfg<HP, D, KT>;
+    using C = DenseCfg<HP, D, KT, HK>;
     constexpr int NH = C::NH, NKH = C::NKH, NDT = C::NDT, DCH = C::DCH, KB = C::KB, NS = C::NS;
     constexpr int CPW = C::CPW;
     constexpr uint32_t kPad = 0x80000000u;      // past the end of every view
@@ -341,14 +346,14 @@ __device__ __forceinline__ void dense_dk_body(const Problem &pb) {
 }
 
 // The body under the register budget of two workgroups per compute unit, or of one.
-template <int HP, int D, bool F16, int KT>
+template <int HP, int D, bool F16, int KT, int HK>
 __global__ __launch_bounds__(kDkBlock, 2) void dense_dk_kernel2(Problem pb) {
-    dense_dk_body<HP, D, F16, KT>(pb);
+    dense_dk_body<HP, D, F16, KT, HK>(pb);
 }
 
-template <int HP, int D, bool F16, int KT>
+template <int HP, int D, bool F16, int KT, int HK>
 __global__ __launch_bounds__(kDkBlock, 1) void dense_dk_kernel1(Problem pb) {
-    dense_dk_body<HP, D, F16, KT>(pb);
+    dense_dk_body<HP, D, F16, KT, HK>(pb);
 }
 
 // Task table (one workgroup): active rows per (key block, row chunk) from the
@@ -657,13 +662,23 @@ __global__ void dense_dk_reduce_kernel(Problem pb) {
     }
 }
 
+template <int HP, int D, bool F16, int KT, int HK>
+static hipError_t launch_dense_hk(const Problem &pb, hipStream_t stream) {
+    static_assert(DenseCfg<HP, D, KT, HK>::WGPC == DenseCfg<HP, D, KT>::WGPC, "grid sized for HP");
+    if constexpr (DenseCfg<HP, D, KT, HK>::WGPC == 2)
+        hipLaunchKernelGGL((dense_dk_kernel2<HP, D, F16, KT, HK>), dim3(pb.dk_slots), dim3(kDkBlock), 0, stream, pb);
+    else
+        hipLaunchKernelGGL((dense_dk_kernel1<HP, D, F16, KT, HK>), dim3(pb.dk_slots), dim3(kDkBlock), 0, stream, pb);
+    return hipGetLastError();
+}
+
+// groups of up to 16 heads (padded to 32 in the records) multiply 16 heads only
 template <int HP, int D, bool F16, int KT>
 static hipError_t launch_dense(const Problem &pb, hipStream_t stream) {
-    if constexpr (DenseCfg<HP, D, KT>::WGPC == 2)
-        hipLaunchKernelGGL((dense_dk_kernel2<HP, D, F16, KT>), dim3(pb.dk_slots), dim3(kDkBlock), 0, stream, pb);
-    else
-        hipLaunchKernelGGL((dense_dk_kernel1<HP, D, F16, KT>), dim3(pb.dk_slots), dim3(kDkBlock), 0, stream, pb);
-    return hipGetLastError();
+    if constexpr (HP == 32) {
+        if (pb.group <= 16) return launch_dense_hk<HP, D, F16, KT, 16>(pb, stream);
+    }
+    return launch_dense_hk<HP, D, F16, KT, HP>(pb, stream);
 }
 
 int dense_dk_keys_per_block(int kt) { return kt == 2 ? DenseCfg<32, 32, 2>::KB : DenseCfg<32, 32, 1>::KB; }
