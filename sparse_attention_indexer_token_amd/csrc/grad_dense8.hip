@@ -56,7 +56,6 @@ constexpr int TOPK_PER_THREAD = 2048 / kBlock8;  // slots of one row per thread 
 template <int HP, int D>
 struct DenseFwdCfg {
     static constexpr int NH = HP / 32;          // 32-head tiles (pass 2, head words)
-    static constexpr int NQT = HP / 16;         // 16-head tiles (pass 1)
     static constexpr int NDT = D / 32;          // 32-wide d tiles of U
     static constexpr int NKS = D / 32;          // k-steps of S over d (16x16x32)
     static constexpr int DCH = D / 8;           // 16-byte chunks per key row
@@ -145,10 +144,15 @@ struct UnitInputs {
 
 // SREC: instead of the dense records, per-slot records for the key-sorted dK strategy
 // (srec_key / srec_dI / srec_mask at [unit, position], srec_cnt[unit]).
-template <int HP, int D, bool F16, bool SREC>
+// HK: the heads pass 1 multiplies, a multiple of 16 no smaller than the group (16 for
+// groups of up to 16 heads padded to HP = 32: the tile of heads 16..31 holds only zero
+// scores, whose ReLU and S > 0 bits are zero).
+template <int HP, int D, bool F16, bool SREC, int HK = HP>
 __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
     using C = DenseFwdCfg<HP, D>;
-    constexpr int NH = C::NH, NQT = C::NQT, NDT = C::NDT, NKS = C::NKS, DCH = C::DCH, NL = C::NL;
+    constexpr int NH = C::NH, NDT = C::NDT, NKS = C::NKS, DCH = C::DCH, NL = C::NL;
+    static_assert(HK % 16 == 0 && HK <= HP, "computed heads");
+    constexpr int NQT = HK / 16;                  // 16-head tiles of pass 1
     constexpr int NST = C::NST;
     constexpr int TOPK_MAX = C::TOPK_MAX;
     constexpr int SPT_MAX = TOPK_PER_THREAD;
@@ -489,11 +493,15 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
 #pragma unroll
                 for (int a = 1; a >= 0; --a) {
                     const int hq = 2 * t + a;
-                    f32x4 c = {0.f, 0.f, 0.f, 0.f};
+                    if (hq < NQT) {
+                        f32x4 c = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int ks = 0; ks < NKS; ++ks) c = mfma16<F16>(qa[hq][ks], bk[ks], c);
+                        for (int ks = 0; ks < NKS; ++ks) c = mfma16<F16>(qa[hq][ks], bk[ks], c);
 #pragma unroll
-                    for (int i = 3; i >= 0; --i) ipp[i] = fmaf(relu_push_bit(c[i], mbits), wr[hq][i], ipp[i]);
+                        for (int i = 3; i >= 0; --i) ipp[i] = fmaf(relu_push_bit(c[i], mbits), wr[hq][i], ipp[i]);
+                    } else {
+                        mbits <<= 4;              // heads past the group: no S > 0 bits
+                    }
                     if (a == 1) mbits <<= 4;
                 }
                 word[t] = mbits << pbase;
@@ -762,13 +770,22 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
     }
 }
 
+template <int HP, int D, bool F16, int HK>
+static hipError_t launch_gd8_hk(const Problem &pb, int grid, bool srec, hipStream_t stream) {
+    if (srec)
+        hipLaunchKernelGGL((grad_dense8_kernel<HP, D, F16, true, HK>), dim3(grid), dim3(kBlock8), 0, stream, pb);
+    else
+        hipLaunchKernelGGL((grad_dense8_kernel<HP, D, F16, false, HK>), dim3(grid), dim3(kBlock8), 0, stream, pb);
+    return hipGetLastError();
+}
+
+// groups of up to 16 heads (padded to 32) multiply 16 heads in pass 1
 template <int HP, int D, bool F16>
 static hipError_t launch_gd8(const Problem &pb, int grid, bool srec, hipStream_t stream) {
-    if (srec)
-        hipLaunchKernelGGL((grad_dense8_kernel<HP, D, F16, true>), dim3(grid), dim3(kBlock8), 0, stream, pb);
-    else
-        hipLaunchKernelGGL((grad_dense8_kernel<HP, D, F16, false>), dim3(grid), dim3(kBlock8), 0, stream, pb);
-    return hipGetLastError();
+    if constexpr (HP == 32) {
+        if (pb.group <= 16) return launch_gd8_hk<HP, D, F16, 16>(pb, grid, srec, stream);
+    }
+    return launch_gd8_hk<HP, D, F16, HP>(pb, grid, srec, stream);
 }
 
 template <int HP, int D, bool F16>
