@@ -66,6 +66,16 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
     // the unit's slot records (head words, dI), staged once per unit
     __shared__ uint32_t s_mw[kSdTopkMax * NH];
     __shared__ float s_dI[kSdTopkMax];
+    // 16-bit rows of a wave's 32 slots, TPG d tiles (64 bytes each) at a time, padded so
+    // that the lanes writing one column of consecutive rows spread over the banks: the
+    // rows leave as whole runs of RB bytes (full cache lines for D >= 64) instead of
+    // 32-byte pieces
+    constexpr int TPG = NDT < 2 ? NDT : 2;          // d tiles per group
+    constexpr int RB = 64 * TPG;                    // bytes of a row's group
+    constexpr int RSTR = RB + 16;                   // LDS row stride
+    constexpr int LPR = RB / 16;                    // lanes per row when stored
+    constexpr int RPI = 64 / LPR;                   // rows per store instruction
+    __shared__ __attribute__((aligned(16))) char s_stage[kSdWaves * 32 * RSTR];
 
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int l32 = lane & 31, half = lane >> 5;
@@ -181,6 +191,7 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
             i16 ? __builtin_amdgcn_make_buffer_rsrc((void *)(parts16 + ubase * D), (short)0, topk * D * 2, 0x00020000)
                 : __builtin_amdgcn_make_buffer_rsrc((void *)(parts32 + ubase * D), (short)0, topk * D * 4, 0x00020000);
 
+        char *const stg = s_stage + wave * (32 * RSTR);
         // ---- slot chunks: 32 per wave, records from LDS ------------------------------------
         for (int c0 = wave * 32; c0 < cnt; c0 += 32 * kSdWaves) {
             uint32_t mw[NH];
@@ -276,25 +287,22 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
                     const float hi = fmaf(pa[2 * k2 + 1], sc, kMagic);
                     wd[k2] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x05040100u);
                 }
-                // exchange with the other half (lane l ^ 32) so that a lane holds 8
-                // consecutive d: half 0 keeps group 2 g2 and takes half 1's, half 1 takes
-                // group 2 g2 + 1 of half 0 and keeps its own
-                uint32_t o[8];
+                // into the wave's stage: row = slot l32, d = 32 (dt % TPG) + 8 g + 4 half + 0..3
+                char *const row = stg + l32 * RSTR + (dt % TPG) * 64 + 8 * half;
 #pragma unroll
-                for (int g2 = 0; g2 < 2; ++g2)
+                for (int g = 0; g < 4; ++g) *(u32x2 *)(row + 16 * g) = u32x2{wd[2 * g], wd[2 * g + 1]};
+                if (dt % TPG == TPG - 1) {
+                    // the group's 32 row runs back in row order, LPR lanes a row, to the
+                    // parts rows (runs of slots past the valid count land past the view)
+                    const int grp0 = dt / TPG;
 #pragma unroll
-                    for (int c = 0; c < 2; ++c) {
-                        const uint32_t ev = wd[4 * g2 + c], od = wd[4 * g2 + 2 + c];
-                        const uint32_t t = (uint32_t)__shfl_xor((int)(half ? ev : od), 32);
-                        o[4 * g2 + c] = half ? t : ev;
-                        o[4 * g2 + 2 + c] = half ? od : t;
+                    for (int i = 0; i < 32 / RPI; ++i) {
+                        const int rr = RPI * i + lane / LPR, cc = lane % LPR;
+                        const u32x4 v = *(const u32x4 *)(stg + rr * RSTR + 16 * cc);
+                        const uint32_t off = c0 + rr < cnt ? (uint32_t)((c0 + rr) * D * 2 + grp0 * RB + 16 * cc)
+                                                           : kSdPadOffset;
+                        __builtin_amdgcn_raw_buffer_store_b128(v, rparts, off, 0, 0);
                     }
-                // chunk g2: d = 32 dt + 16 g2 + 8 half .. + 7
-#pragma unroll
-                for (int g2 = 0; g2 < 2; ++g2) {
-                    const uint32_t off = ok ? (uint32_t)((p * D + 32 * dt + 16 * g2 + 8 * half) * 2) : kSdPadOffset;
-                    __builtin_amdgcn_raw_buffer_store_b128(u32x4{o[4 * g2], o[4 * g2 + 1], o[4 * g2 + 2], o[4 * g2 + 3]},
-                                                           rparts, off, 0, 0);
                 }
             }
         }
@@ -302,11 +310,11 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
     }
 }
 
-// The body under the register budget of four workgroups per compute unit (32-head
-// groups), two (64-head groups) or one (128-head groups, which need the whole register
-// file): the most that run without spills.
+// The body under the register budget of three workgroups per compute unit (32-head
+// groups; three also fill the LDS), two (64-head groups) or one (128-head groups, which
+// need the whole register file): the most that run without spills.
 template <int HP, int D, bool F16>
-__global__ __launch_bounds__(kSdBlock, 4) void scatter_dk_kernel4(Problem pb) {
+__global__ __launch_bounds__(kSdBlock, 3) void scatter_dk_kernel3(Problem pb) {
     scatter_dk_body<HP, D, F16>(pb);
 }
 
@@ -326,8 +334,11 @@ static hipError_t launch_sd(const Problem &pb, hipStream_t stream) {
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
         return hipErrorInvalidDevice;
-    auto kern = HP > 64 ? scatter_dk_kernel1<HP, D, F16> : HP > 32 ? scatter_dk_kernel2<HP, D, F16>
-                                                           : scatter_dk_kernel4<HP, D, F16>;
+    auto kern = [] {            // only the variant this head group runs is instantiated
+        if constexpr (HP > 64) return scatter_dk_kernel1<HP, D, F16>;
+        else if constexpr (HP > 32) return scatter_dk_kernel2<HP, D, F16>;
+        else return scatter_dk_kernel3<HP, D, F16>;
+    }();
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kern, kSdBlock, 0) != hipSuccess || per <= 0) per = 1;
     const int64_t U = pb.t1 * pb.n2;
     int64_t grid = (int64_t)cus * per;
