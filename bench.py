@@ -52,7 +52,7 @@ CSRC = os.path.join(ROOT, "sparse_attention_indexer_token_amd", "csrc")
 _COMMON = ("device_common.h", "slikl_internal.h")
 KERNEL_SOURCES = {
     kern: [os.path.join(CSRC, f) for f in (src,) + _COMMON]
-    for kern, src in (("grad_dense8_kernel", "grad_dense8.hip"), ("grad_dense_kernel", "grad_dense.hip"),
+    for kern, src in (("grad_dense64_kernel", "grad_dense64.hip"), ("grad_dense_kernel", "grad_dense.hip"),
                       ("grad_fused_kernel", "grad_fused.hip"), ("dense_dk_kernel", "dense_dk.hip"),
                       ("scatter_dk_kernel", "scatter_dk.hip"), ("sorted_reduce_kernel", "sorted_dk.hip"))
 }
@@ -71,12 +71,12 @@ def traffic_file(kernel, workload):
 
 def fused_kernel(strategy, group):
     """The fused kernel a call runs: with the dense and sorted dK strategies the
-    eight-wave kernel for head groups padded to at most 64 heads, the four-wave one
+    64-head kernel for head groups padded to at most 64 heads, the 128-head one
     above; with the scatter strategy its own four-wave kernel (which also forms and
     adds the dK parts)."""
     if strategy == "scatter":
         return "grad_fused_kernel"
-    return "grad_dense8_kernel" if group <= 64 else "grad_dense_kernel"
+    return "grad_dense64_kernel" if group <= 64 else "grad_dense_kernel"
 
 
 # the library's parts format: 16-bit rows when no key row takes more than this many

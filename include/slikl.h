@@ -162,7 +162,7 @@ slikl_status slikl_grad_parts(const slikl_desc *desc, int32_t *parts);
 
 /* Per-unit overhead (valid-slot equivalents) the WEIGHTED split uses for
  * `desc`: SLIKL_UNIT_OVERHEAD_DENSE when the resolved dK strategy is DENSE or
- * SORTED (which runs the dense strategy's eight-wave fused kernel), else
+ * SORTED (which runs the dense strategy's 64-head fused kernel), else
  * SLIKL_UNIT_OVERHEAD.  Host only.  PARAM_INVALID / UNSUPPORTED as
  * slikl_grad_workspace_size; NULLPTR for a null argument. */
 slikl_status slikl_grad_unit_overhead(const slikl_desc *desc, int32_t *overhead);

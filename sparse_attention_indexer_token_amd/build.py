@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libslikl.so")
 OBJDIR = os.path.join(PKG, "_build")
 
-SOURCES = ["grad_fused.hip", "grad_dense.hip", "grad_dense8.hip", "dense_dk.hip", "scatter_dk.hip", "sorted_dk.hip",
+SOURCES = ["grad_fused.hip", "grad_dense.hip", "grad_dense64.hip", "dense_dk.hip", "scatter_dk.hip", "sorted_dk.hip",
            "aux_kernels.hip", "attn_p.hip", "slikl_host.cpp"]
 ARCH = "gfx950"
 

@@ -8,7 +8,7 @@
 // as the chain rule through I = W ReLU(S): dS[h,s] = w[h] dI[s] 1[S[h,s] > 0].
 //
 // Serves head groups of more than 64 (head groups of up to 64 go to the
-// eight-wave variant, whose launcher the dispatch below calls).
+// 64-head variant, whose launcher the dispatch below calls).
 //
 // One workgroup (4 wavefronts, one per SIMD) per compute unit walks the
 // (query row, key head) units of its metadata parts.  Per unit the valid slots
@@ -721,13 +721,13 @@ static int blocks_gd() {
 
 hipError_t launch_grad_dense(const Problem &pb, int hp, bool f16, int grid, bool srec, hipStream_t stream) {
     const int d = pb.d;
-    if (hp <= 64) return launch_grad_dense8(pb, hp, f16, grid, srec, stream);
+    if (hp <= 64) return launch_grad_dense64(pb, hp, f16, grid, srec, stream);
     SLIKL_GD_CASES(launch_gd, pb, grid, srec, stream);
     return hipErrorInvalidValue;
 }
 
 int grad_dense_blocks_per_cu(int hp, int d, bool f16) {
-    if (hp <= 64) return grad_dense8_blocks_per_cu(hp, d, f16);
+    if (hp <= 64) return grad_dense64_blocks_per_cu(hp, d, f16);
     SLIKL_GD_CASES(blocks_gd);
     return 1;
 }

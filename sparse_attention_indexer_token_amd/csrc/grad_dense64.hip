@@ -7,21 +7,24 @@
 // y = Softmax(I), dI = y - p, dW = dI ReLU(S)^T, dq = dS K_topk, with dS read
 // as the chain rule through I = W ReLU(S): dS[h,s] = w[h] dI[s] 1[S[h,s] > 0].
 //
-// One workgroup of 8 wavefronts (two per SIMD, so that one wave's waits are
-// covered by the other's work) per compute unit walks the (query row, key
-// head) units of its metadata parts.  Per unit the valid slots are compacted
-// into positions; a step covers 128 positions, 16 per wave, and every wave
-// runs its own barrier-free pipeline over its positions:
+// Two workgroups of 4 wavefronts share a compute unit (two waves per SIMD, one
+// of each workgroup), each walking the (query row, key head) units of its own
+// metadata parts, so that the fixed per-unit work of one (slot compaction,
+// softmax, the reduction of the partial U) runs beside the MFMA passes of the
+// other.  The kernel is written for NW waves: NW = 8 (one workgroup per compute
+// unit) is the other form, slower on every measured workload.  Per unit the
+// valid slots are compacted into positions; a step covers 16 NW positions, 16
+// per wave, and every wave runs its own barrier-free pipeline over its positions:
 //   pass 1  S for all heads of its 16 keys (16x16x32 MFMA, rows = heads), then
 //           per key I = sum_h w_h ReLU(S) and the S > 0 head bits (one 32-bit
 //           word per 32-head tile, bit 16*(h/4 % 2) + 4*(h/8) + h%4 for head h:
-//           the format the dK kernel and the four-wave variant use).
+//           the format the dK kernel and the 128-head variant use).
 //   softmax (block-wide) m, Z, y -> softmax_out, dI = y - p; dI as fp16 after
 //           a per-unit power-of-two scale for pass 2.
 //   pass 2  U^T += K16^T dS16^T over its keys (32x32x16 MFMA; A = fp16 keys via
 //           transposing LDS reads, B = fp16 dI on the S > 0 bits built in
 //           registers), a partial U of every head.
-//   end     the eight partial U are added in a fixed order through LDS;
+//   end     the NW partial U are added in a fixed order through LDS;
 //           dq = w U, and dW = <q, U> per head (U q = sum_s dI ReLU(S)).
 // The keys of both passes form one stream of 16-row copies per wave into a
 // ring of NST stages in LDS (range-checked buffer loads straight to LDS,
@@ -39,21 +42,24 @@
 //   wrec[u]        fp16 hi and lo parts of w 2^ew (w carried to about 22 bits),
 //                  then eq + ew and ed
 // Two waves per SIMD need the U accumulators within 128 registers, so this
-// variant serves head groups of up to 64; larger groups use the four-wave one.
+// variant serves head groups of up to 64; larger groups use the 128-head one.
 #include "device_common.h"
 #include "slikl_internal.h"
 
 namespace slikl {
-namespace dense8 {
+namespace dense64 {
 
 typedef __attribute__((address_space(3))) void lds_void_gd;
 typedef __attribute__((address_space(1))) void glb_void_gd;
 
-constexpr int kWaves8 = 8;
-constexpr int kBlock8 = 64 * kWaves8;
-constexpr int TOPK_PER_THREAD = 2048 / kBlock8;  // slots of one row per thread (topk <= 2048)
+// waves per workgroup: 4 (two workgroups per compute unit, each on its own unit,
+// so that one unit's fixed work runs beside the other's MFMA passes) or 8 (one)
+#ifndef SLIKL_GD64_WAVES
+#define SLIKL_GD64_WAVES 4
+#endif
+constexpr int kWaves64 = SLIKL_GD64_WAVES;
 
-template <int HP, int D>
+template <int HP, int D, int NW>
 struct DenseFwdCfg {
     static constexpr int NH = HP / 32;          // 32-head tiles (pass 2, head words)
     static constexpr int NDT = D / 32;          // 32-wide d tiles of U
@@ -61,16 +67,25 @@ struct DenseFwdCfg {
     static constexpr int DCH = D / 8;           // 16-byte chunks per key row
     static constexpr int NL = D / 32;           // 1 KiB copies per wave step (16 rows)
     static constexpr int RPB = 1024 / (2 * D);  // key rows per copy
-    static constexpr int NST = D == 128 ? (HP == 128 ? 2 : 3) : 4;
+    static constexpr int NT = 64 * NW;          // threads of a workgroup
+    static constexpr int STEP = 16 * NW;        // positions of one step
+    static constexpr int SPT = 2048 / NT;       // slots of one row per thread (topk <= 2048)
+    static constexpr int PPT = 2048 / NT;       // softmax positions per thread
+    static constexpr int NST = NW == 8 ? (D == 128 ? (HP == 128 ? 2 : 3) : 4) : (D == 128 ? 2 : 4);
     static constexpr int STAGE = 16 * D * 2;    // bytes of one wave stage
-    static constexpr int RING = kWaves8 * NST * STAGE;
+    static constexpr int RING = NW * NST * STAGE;
     static constexpr int TOPK_MAX = 2048;
-    // U reductions run in NDH rounds of DH columns (so that 8 partial tiles fit
+    // U reductions run in NDH rounds of DH columns (so that the NW partial tiles fit
     // the ring); fp32 row stride of a round's tile
-    static constexpr int NDH = D == 128 ? 2 : 1;
-    static constexpr int DH = D / NDH;
-    static constexpr int RS = kWaves8 * 32 * (DH + 4) * 4 <= RING ? DH + 4 : DH;
-    static_assert(RING >= kWaves8 * 32 * RS * 4, "U reduction tile fits the ring");
+    static constexpr int DH = NW == 8 ? (D == 128 ? 64 : D) : 32 < D ? 32 : D;
+    static constexpr int NDH = D / DH;
+    static constexpr int RS = NW * 32 * (DH + 4) * 4 <= RING ? DH + 4 : DH;
+    static_assert(RING >= NW * 32 * RS * 4, "U reduction tile fits the ring");
+    static constexpr int EPT = 32 * DH / NT;    // epilogue elements per thread
+    static constexpr int TPH = DH / EPT;        // epilogue threads per head
+    // with four waves fp16 dI goes into the p array (p is read into registers first),
+    // so that the LDS of two workgroups fits a compute unit
+    static constexpr bool D16_IN_P = NW < 8;
 };
 
 // Swizzle of row `row` of a [16 rows][CH 16-byte chunks] stage tile: logical
@@ -135,11 +150,12 @@ __device__ __forceinline__ void wait_for_step(int ahead) {
 // Slot lists and w of one unit, loaded one unit ahead (during the previous
 // unit's epilogue; q itself is loaded at the start of its unit, where its
 // latency overlaps the compaction, so that it is not live beside U).
+template <int SPT>
 struct UnitInputs {
     i32x4 ri;                        // row info (TND: batch, key base, key length, row in batch)
     float wt;                        // w of head `tid` (tid < G)
-    int iv[TOPK_PER_THREAD];         // this thread's run of slots: key index, p
-    float pv[TOPK_PER_THREAD];
+    int iv[SPT];                     // this thread's run of slots: key index, p
+    float pv[SPT];
 };
 
 // SREC: instead of the dense records, per-slot records for the key-sorted dK strategy
@@ -148,15 +164,17 @@ struct UnitInputs {
 // groups of up to 16 heads padded to HP = 32: the tile of heads 16..31 holds only zero
 // scores, whose ReLU and S > 0 bits are zero).
 template <int HP, int D, bool F16, bool SREC, int HK = HP>
-__global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
-    using C = DenseFwdCfg<HP, D>;
+__global__ __launch_bounds__(64 * kWaves64, 8 / kWaves64) void grad_dense64_kernel(Problem pb) {
+    using C = DenseFwdCfg<HP, D, kWaves64>;
+    constexpr int kBlock8 = C::NT;
+    constexpr int STEP = C::STEP;
     constexpr int NH = C::NH, NDT = C::NDT, NKS = C::NKS, DCH = C::DCH, NL = C::NL;
     static_assert(HK % 16 == 0 && HK <= HP, "computed heads");
     constexpr int NQT = HK / 16;                  // 16-head tiles of pass 1
     constexpr int NST = C::NST;
     constexpr int TOPK_MAX = C::TOPK_MAX;
-    constexpr int SPT_MAX = TOPK_PER_THREAD;
-    constexpr int NW = kWaves8;
+    constexpr int SPT_MAX = C::SPT;
+    constexpr int NW = kWaves64;
 
     __shared__ __attribute__((aligned(1024))) char s_ring[C::RING];
     __shared__ __attribute__((aligned(16))) uint32_t s_mask[NH * TOPK_MAX];   // [word][position]
@@ -164,7 +182,8 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
     __shared__ __attribute__((aligned(16))) float s_p[TOPK_MAX];
     __shared__ __attribute__((aligned(16))) int32_t s_key[TOPK_MAX];
     __shared__ __attribute__((aligned(16))) uint16_t s_slot[TOPK_MAX];
-    __shared__ __attribute__((aligned(16))) uint16_t s_d16[TOPK_MAX];          // fp16 dI 2^eds
+    __shared__ __attribute__((aligned(16))) uint16_t s_d16a[C::D16_IN_P ? 8 : TOPK_MAX];   // fp16 dI 2^eds
+    uint16_t *const s_d16 = C::D16_IN_P ? (uint16_t *)s_p : s_d16a;
     __shared__ __attribute__((aligned(16))) float s_w[HP];
     __shared__ float s_red[NW * 6];
 
@@ -204,7 +223,7 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
         }
         return true;
     };
-    UnitInputs in;
+    UnitInputs<SPT_MAX> in;
     auto load_inputs = [&](int uu) {
         const int rr = uu / pb.n2, gg = uu - rr * pb.n2;
         // every load is issued (clamped to an element that exists, then selected
@@ -322,8 +341,8 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
                 ++pos;
             }
         }
-        const int nsteps = (nvalid + 127) >> 7;
-        for (int j = nvalid + tid; j < nsteps * 128; j += kBlock8) s_key[j] = nkrows;   // reads zeros
+        const int nsteps = (nvalid + STEP - 1) / STEP;
+        for (int j = nvalid + tid; j < nsteps * STEP; j += kBlock8) s_key[j] = nkrows;   // reads zeros
 
         // max |w| of the unit from s_w (published by the scan's barriers)
         float wabs = fabsf(s_w[lane < HP ? lane : 0]);
@@ -376,7 +395,7 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
             char *dst = ring + (sigma % NST) * C::STAGE;
             int32_t key[NL];
 #pragma unroll
-            for (int i = 0; i < NL; ++i) key[i] = keys_l[st * 128 + i * C::RPB];   // all reads first
+            for (int i = 0; i < NL; ++i) key[i] = keys_l[st * STEP + i * C::RPB];   // all reads first
 #pragma unroll
             for (int i = 0; i < NL; ++i)
                 __builtin_amdgcn_struct_ptr_buffer_load_lds(second ? rk16 : rk, (lds_void_gd *)(dst + i * 1024), 16,
@@ -509,7 +528,7 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
             const float ip = group_sum((ipp[0] + ipp[1]) + (ipp[2] + ipp[3]));
 #pragma unroll
             for (int t = 0; t < NH; ++t) word[t] = group_or(word[t]);
-            const int pos1 = s * 128 + wave * 16 + l16;
+            const int pos1 = s * STEP + wave * 16 + l16;
             const bool valid = pos1 < nvalid;
             if (valid) mloc = fmaxf(mloc, ip);
             // lane group 0 writes I, group 1 + t head word t (all groups hold both)
@@ -525,24 +544,30 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
 
         // ---- softmax over the valid positions: m, Z, y -> softmax_out, dI ------------
         const float m = block_max<NW>(mloc, s_red);     // (its barriers publish s_I, s_mask)
-        constexpr int PPT = TOPK_MAX / kBlock8;        // positions per thread
+        constexpr int PPT = C::PPT;                    // positions per thread
         const int p0 = tid * PPT;
         float e[PPT];
         float zl = 0.f;
-        const float4 a0 = *(const float4 *)(s_I + p0);
-        const float iv4[4] = {a0.x, a0.y, a0.z, a0.w};
+        float iv4[PPT], pp4[PPT];
+#pragma unroll
+        for (int i = 0; i < PPT; i += 4) {
+            const float4 a0 = *(const float4 *)(s_I + p0 + i);
+            const float4 b0 = *(const float4 *)(s_p + p0 + i);
+            iv4[i] = a0.x; iv4[i + 1] = a0.y; iv4[i + 2] = a0.z; iv4[i + 3] = a0.w;
+            pp4[i] = b0.x; pp4[i + 1] = b0.y; pp4[i + 2] = b0.z; pp4[i + 3] = b0.w;
+        }
 #pragma unroll
         for (int i = 0; i < PPT; ++i) {
             e[i] = p0 + i < nvalid ? expf(iv4[i] - m) : 0.f;
             zl += e[i];
         }
+        // (its barriers also order every read of p above before the fp16 dI stores
+        // below when those share the p array)
         const float Z = block_sum<NW>(zl, s_red + 2 * NW);
         const float invZ = 1.f / Z;
         if (pb.kl) {
             // the unit's KL(p || y): p (log p - (I - m - log Z)) over positions with p > 0
             const float lz = logf(Z);
-            const float4 b0 = *(const float4 *)(s_p + p0);
-            const float pp4[4] = {b0.x, b0.y, b0.z, b0.w};
             float kl = 0.f;
 #pragma unroll
             for (int i = 0; i < PPT; ++i)
@@ -555,8 +580,6 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
         const int eds = pow2_exponent_below_2p15(fmaxf(invZ, pmax));
         const float dsc = ldexpf(1.f, eds);
         {
-            const float4 b0 = *(const float4 *)(s_p + p0);
-            const float pp4[4] = {b0.x, b0.y, b0.z, b0.w};
             uint32_t d16w[PPT / 2];
 #pragma unroll
             for (int i = 0; i < PPT; i += 2) {
@@ -574,7 +597,10 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
                 }
                 d16w[i / 2] = pack2<true>(dd[0] * dsc, dd[1] * dsc);
             }
-            if (p0 < nsteps * 128) *(u32x2 *)(s_d16 + p0) = u32x2{d16w[0], d16w[1]};
+            if (p0 < nsteps * STEP) {
+#pragma unroll
+                for (int i = 0; i < PPT / 2; i += 2) *(u32x2 *)(s_d16 + p0 + 2 * i) = u32x2{d16w[i], d16w[i + 1]};
+            }
         }
 #pragma unroll
         for (int i = 0; i < SPT_MAX; ++i)
@@ -609,7 +635,7 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
                 // Scattered writes; spread over pass 2 they hide behind the other
                 // wave's MFMA work.  Issued before the next copies, so that the copies
                 // after an awaited one stay the last NL memory operations.
-                const int pr = (s + (lane >> 4)) * 128 + wave * 16 + (lane & 15);
+                const int pr = (s + (lane >> 4)) * STEP + wave * 16 + (lane & 15);
                 if (SREC && pr < nvalid) {
                     // per-slot records: key row, dI, head words
                     const size_t o = (size_t)u * topk + pr;
@@ -636,7 +662,7 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
             if (sigma + NST - 1 < T) issue(sigma + NST - 1);
             const char *kb = ring + (sigma % NST) * C::STAGE;
             // B operand: head l32 of each 32-head tile, positions pk .. pk+7 as k
-            const int pk = s * 128 + wave * 16 + 8 * half;
+            const int pk = s * STEP + wave * 16 + 8 * half;
             const u32x4 d16 = *(const u32x4 *)(s_d16 + pk);
             u32x4 bb[NH];
 #pragma unroll
@@ -661,11 +687,12 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
             }
         }
 
-        // ---- U = sum of the eight wave partials (fixed order), NDH rounds over d;
+        // ---- U = sum of the NW wave partials (fixed order), NDH rounds over d;
         //      dq = w U and dW = <q, U> ---------------------------------------------------
         const float uscale = ldexpf(1.f, -eds) * kinv;
         float *red = (float *)s_ring;
-        constexpr int EPT = C::DH / 16;          // elements per thread: 32 heads x DH / 512
+        constexpr int EPT = C::EPT;              // elements per thread: 32 heads x DH / threads
+        constexpr int TPH = C::TPH;              // threads per head
         static_assert(EPT == 2 || EPT == 4, "epilogue store width");
         // range-checked views of this unit's dq rows and dW entries: heads past G
         // (and lanes that do not write) store at an offset past the end, which the
@@ -675,8 +702,8 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
         const __amdgpu_buffer_rsrc_t rdw = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(pb.dw + r * pb.n1 + g * G), (short)0, G * 4, 0x00020000);
         const int et = opaque(tid);
-        const int hh = et >> 4;                  // head of this thread within the tile
-        const int c0 = (et & 15) * EPT;          // its columns within a round
+        const int hh = et / TPH;                 // head of this thread within the tile
+        const int c0 = (et % TPH) * EPT;         // its columns within a round
         // q elements of the dW dot products, loaded ahead of the next unit's inputs
         // (rows past G read head 0: their dq and dW stores are dropped)
         uint32_t qe[NH][C::NDH][EPT / 2];
@@ -759,11 +786,9 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
                     else __builtin_amdgcn_raw_buffer_store_b32(o[0], rdq, dqo, 0, 0);
                 }
             }
-            dot += __shfl_xor(dot, 1);
-            dot += __shfl_xor(dot, 2);
-            dot += __shfl_xor(dot, 4);
-            dot += __shfl_xor(dot, 8);
-            const uint32_t dwo = (h < G && (et & 15) == 0) ? (uint32_t)(h * 4) : kPadOffset;
+#pragma unroll
+            for (int o = 1; o < TPH; o <<= 1) dot += __shfl_xor(dot, o);
+            const uint32_t dwo = (h < G && et % TPH == 0) ? (uint32_t)(h * 4) : kPadOffset;
             __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(dot), rdw, dwo, 0, 0);
         }
         lds_barrier();          // ring, s_w and the position lists are reused by the next unit
@@ -771,34 +796,35 @@ __global__ __launch_bounds__(kBlock8, 1) void grad_dense8_kernel(Problem pb) {
 }
 
 template <int HP, int D, bool F16, int HK>
-static hipError_t launch_gd8_hk(const Problem &pb, int grid, bool srec, hipStream_t stream) {
+static hipError_t launch_gd64_hk(const Problem &pb, int grid, bool srec, hipStream_t stream) {
     if (srec)
-        hipLaunchKernelGGL((grad_dense8_kernel<HP, D, F16, true, HK>), dim3(grid), dim3(kBlock8), 0, stream, pb);
+        hipLaunchKernelGGL((grad_dense64_kernel<HP, D, F16, true, HK>), dim3(grid), dim3(64 * kWaves64), 0, stream, pb);
     else
-        hipLaunchKernelGGL((grad_dense8_kernel<HP, D, F16, false, HK>), dim3(grid), dim3(kBlock8), 0, stream, pb);
+        hipLaunchKernelGGL((grad_dense64_kernel<HP, D, F16, false, HK>), dim3(grid), dim3(64 * kWaves64), 0, stream, pb);
     return hipGetLastError();
 }
 
 // groups of up to 16 heads (padded to 32) multiply 16 heads in pass 1
 template <int HP, int D, bool F16>
-static hipError_t launch_gd8(const Problem &pb, int grid, bool srec, hipStream_t stream) {
+static hipError_t launch_gd64(const Problem &pb, int grid, bool srec, hipStream_t stream) {
     if constexpr (HP == 32) {
-        if (pb.group <= 16) return launch_gd8_hk<HP, D, F16, 16>(pb, grid, srec, stream);
+        if (pb.group <= 16) return launch_gd64_hk<HP, D, F16, 16>(pb, grid, srec, stream);
     }
-    return launch_gd8_hk<HP, D, F16, HP>(pb, grid, srec, stream);
+    return launch_gd64_hk<HP, D, F16, HP>(pb, grid, srec, stream);
 }
 
 template <int HP, int D, bool F16>
-static int blocks_gd8() {
+static int blocks_gd64() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grad_dense8_kernel<HP, D, F16, false>, kBlock8, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grad_dense64_kernel<HP, D, F16, false>, 64 * kWaves64, 0) !=
+        hipSuccess)
         return 0;
     return n;
 }
 
-}  // namespace dense8
+}  // namespace dense64
 
-#define SLIKL_GD8_CASES(FN, ...)                                                                                  \
+#define SLIKL_GD64_CASES(FN, ...)                                                                                  \
     do {                                                                                                          \
         if (hp == 32 && d == 32) return f16 ? FN<32, 32, true>(__VA_ARGS__) : FN<32, 32, false>(__VA_ARGS__);     \
         if (hp == 32 && d == 64) return f16 ? FN<32, 64, true>(__VA_ARGS__) : FN<32, 64, false>(__VA_ARGS__);     \
@@ -808,14 +834,14 @@ static int blocks_gd8() {
         if (hp == 64 && d == 128) return f16 ? FN<64, 128, true>(__VA_ARGS__) : FN<64, 128, false>(__VA_ARGS__);  \
     } while (0)
 
-hipError_t launch_grad_dense8(const Problem &pb, int hp, bool f16, int grid, bool srec, hipStream_t stream) {
+hipError_t launch_grad_dense64(const Problem &pb, int hp, bool f16, int grid, bool srec, hipStream_t stream) {
     const int d = pb.d;
-    SLIKL_GD8_CASES(dense8::launch_gd8, pb, grid, srec, stream);
+    SLIKL_GD64_CASES(dense64::launch_gd64, pb, grid, srec, stream);
     return hipErrorInvalidValue;
 }
 
-int grad_dense8_blocks_per_cu(int hp, int d, bool f16) {
-    SLIKL_GD8_CASES(dense8::blocks_gd8);
+int grad_dense64_blocks_per_cu(int hp, int d, bool f16) {
+    SLIKL_GD64_CASES(dense64::blocks_gd64);
     return 0;
 }
 

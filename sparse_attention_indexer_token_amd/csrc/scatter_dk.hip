@@ -1,4 +1,4 @@
-// dK parts of the key-sorted scatter strategy for gfx950, from the eight-wave fused
+// dK parts of the key-sorted scatter strategy for gfx950, from the 64-head fused
 // kernel's per-slot records.
 //
 // Follows the formula section of the operator page

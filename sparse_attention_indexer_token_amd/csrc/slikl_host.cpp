@@ -45,17 +45,17 @@ int dense_kt(const slikl_desc *d) {
 // side known (BSND, or TND with its maximum given), keys addressed with 32-bit byte
 // offsets (< 2^31 bytes) and key rows below 2^24 (24-bit multiplies; exact in fp32).
 bool dense_fits(const slikl_desc *d) {
-    // the eight-wave fused kernel (head groups up to 64) addresses key rows as
+    // the 64-head fused kernel (head groups up to 64) addresses key rows as
     // buffer records, whose stride field holds 14 bits
     const bool rows_ok = head_tile(d->n2 > 0 ? d->n1 / d->n2 : 1) > 64 || (int64_t)d->n2 * d->d * 2 < 16384;
     return len_q(d) > 0 && len_k(d) > 0 && rows_ok &&
            (double)rows_k(d) * d->n2 * d->d * 2.0 < 2147483648.0 && (double)rows_k(d) < 16777216.0;
 }
 
-// The key-sorted dK runs through the eight-wave kernel's slot records (head groups up to
+// The key-sorted dK runs through the 64-head kernel's slot records (head groups up to
 // 64, key rows within its 14-bit record stride); its bin prefix is one two-level scan.
 bool sorted_fits(const slikl_desc *d) {
-    // the eight-wave kernel (head groups up to 64) addresses key rows as buffer records,
+    // the 64-head kernel (head groups up to 64) addresses key rows as buffer records,
     // whose stride field holds 14 bits
     if (head_tile(d->n2 > 0 ? d->n1 / d->n2 : 1) <= 64 && (int64_t)d->n2 * d->d * 2 >= 16384) return false;
     // record indices are 32-bit; the sort loops step past the last record by up to 4096
@@ -436,7 +436,7 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
     pb.k16 = f16 ? pb.k : (const uint16_t *)(ws + wp.k16_off);
     pb.zero16 = (const uint16_t *)(ws + wp.zero_off);
     const int mode = wp.mode;
-    const bool s8 = wp.sorted;          // eight-wave kernel writing slot records
+    const bool s8 = wp.sorted;          // 64-head kernel writing slot records
     if (s8) {
         pb.srec_key = (int32_t *)(ws + wp.srec_key_off);
         pb.srec_dI = (float *)(ws + wp.srec_dI_off);

@@ -53,7 +53,7 @@ struct Problem {
     // dense strategy with a TND side: per query row {batch, key base, key length
     // (at most s2max), row within its batch}; null for BSND (computed in place)
     const i32x4 *rowinfo;
-    // key-sorted strategy (eight-wave kernel): per (unit, valid position) the key row, dI
+    // key-sorted strategy (64-head kernel): per (unit, valid position) the key row, dI
     // and the S > 0 head words ([U, topk], [U, topk], [U, topk, HP/32]) and per unit the
     // valid count; the parts kernel overwrites each dI with its row's multiplier
     int32_t *srec_key;
@@ -140,14 +140,14 @@ hipError_t launch_grad_fused(const Problem &pb, int hp, bool f16, int mode, int 
                              hipStream_t stream);
 int grad_fused_blocks_per_cu(int hp, int d, bool f16, int mode);
 // fused kernel of the dense dK strategy: writes the dense records above, or with srec
-// the per-slot records of the key-sorted strategy (eight waves up to 64 heads, four
+// the per-slot records of the key-sorted strategy (the 64-head kernel up to 64 heads, the 128-head one
 // above)
 hipError_t launch_grad_dense(const Problem &pb, int hp, bool f16, int grid, bool srec, hipStream_t stream);
 int grad_dense_blocks_per_cu(int hp, int d, bool f16);
-// eight-wave variant for head groups of up to 64 (called by the two above)
-hipError_t launch_grad_dense8(const Problem &pb, int hp, bool f16, int grid, bool srec, hipStream_t stream);
-// scatter dK from the eight-wave kernel's per-slot records (head groups up to 64)
-// dK parts of the key-sorted strategy from the eight-wave kernel's slot records
+// 64-head variant for head groups of up to 64 (called by the two above)
+hipError_t launch_grad_dense64(const Problem &pb, int hp, bool f16, int grid, bool srec, hipStream_t stream);
+// scatter dK from the 64-head kernel's per-slot records (head groups up to 64)
+// dK parts of the key-sorted strategy from the 64-head kernel's slot records
 // (head groups up to 64), stored into dk_parts
 hipError_t launch_scatter_dk(const Problem &pb, int hp, bool f16, hipStream_t stream);
 // key-sorted dK: the bucket sort of the records by bin (list and bin starts), and the
@@ -163,7 +163,7 @@ struct SortGeometry {
 SortGeometry sorted_geometry(int64_t nslot, int64_t nbins);
 hipError_t launch_sorted_prepare(const Problem &pb, hipStream_t stream);
 hipError_t launch_sorted_reduce(const Problem &pb, bool det, hipStream_t stream);
-int grad_dense8_blocks_per_cu(int hp, int d, bool f16);
+int grad_dense64_blocks_per_cu(int hp, int d, bool f16);
 // Up to 8 byte ranges (16-byte aligned starts, sizes multiples of 4) zeroed by one launch.
 // Parts are stored as 16-bit integers with a per-record multiplier when no key row
 // takes more than this many parts; their rounding error (at most 2^-15 of the part's

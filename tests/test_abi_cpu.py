@@ -197,7 +197,7 @@ def test_dk_strategy_query_resolves_auto(lib):
     assert strat(good_desc(dk_mode=3, deterministic=1)) == (0, 3)
     assert strat(good_desc(dk_mode=3, n1=128)) == (0, 3)
     assert strat(good_desc(dk_mode=3, n1=128, n2=2)) == (0, 3)
-    # head groups up to 64 run the eight-wave kernel: N2 * D * 2 below 16384 bytes
+    # head groups up to 64 run the 64-head kernel: N2 * D * 2 below 16384 bytes
     assert strat(good_desc(dk_mode=3, n1=64, n2=64, d=128, s2=512))[0] == 3
     assert strat(good_desc(dk_mode=3, n1=64, n2=32, d=128, s2=512)) == (0, 3)
     # 32-bit record indices: T1 * N2 * topk below 2^31 - 65536
