@@ -719,15 +719,15 @@ static int blocks_gd() {
         if (hp == 128 && d == 128) return f16 ? FN<128, 128, true>(__VA_ARGS__) : FN<128, 128, false>(__VA_ARGS__); \
     } while (0)
 
-hipError_t launch_grad_dense(const Problem &pb, int hp, bool f16, int grid, bool srec, hipStream_t stream) {
+hipError_t launch_grad_dense(const Problem &pb, int hp, bool f16, int cap, int grid, bool srec, hipStream_t stream) {
     const int d = pb.d;
-    if (hp <= 64) return launch_grad_dense64(pb, hp, f16, grid, srec, stream);
+    if (hp <= 64) return launch_grad_dense64(pb, hp, f16, cap, grid, srec, stream);
     SLIKL_GD_CASES(launch_gd, pb, grid, srec, stream);
     return hipErrorInvalidValue;
 }
 
-int grad_dense_blocks_per_cu(int hp, int d, bool f16) {
-    if (hp <= 64) return grad_dense64_blocks_per_cu(hp, d, f16);
+int grad_dense_blocks_per_cu(int hp, int d, bool f16, int cap) {
+    if (hp <= 64) return grad_dense64_blocks_per_cu(hp, d, f16, cap);
     SLIKL_GD_CASES(blocks_gd);
     return 1;
 }

@@ -59,7 +59,10 @@ typedef __attribute__((address_space(1))) void glb_void_gd;
 #endif
 constexpr int kWaves64 = SLIKL_GD64_WAVES;
 
-template <int HP, int D, int NW>
+// Capacity forms: CAP 0 serves top-k lists of at most 512 slots (the per-position
+// arrays are a quarter of the size, so that three workgroups share a compute unit for
+// groups of up to 32 heads), CAP 1 lists of at most 2048 slots.
+template <int HP, int D, int NW, int CAP>
 struct DenseFwdCfg {
     static constexpr int NH = HP / 32;          // 32-head tiles (pass 2, head words)
     static constexpr int NDT = D / 32;          // 32-wide d tiles of U
@@ -69,12 +72,14 @@ struct DenseFwdCfg {
     static constexpr int RPB = 1024 / (2 * D);  // key rows per copy
     static constexpr int NT = 64 * NW;          // threads of a workgroup
     static constexpr int STEP = 16 * NW;        // positions of one step
-    static constexpr int SPT = 2048 / NT;       // slots of one row per thread (topk <= 2048)
-    static constexpr int PPT = 2048 / NT;       // softmax positions per thread
-    static constexpr int NST = NW == 8 ? (D == 128 ? (HP == 128 ? 2 : 3) : 4) : (D == 128 ? 2 : 4);
+    static constexpr int TOPK_MAX = CAP == 0 ? 512 : 2048;
+    static constexpr int SPT = TOPK_MAX / NT;   // slots of one row per thread (topk <= TOPK_MAX)
+    static constexpr int WGPC = NW == 8 ? 1 : (CAP == 0 && HP == 32 ? 3 : 2);   // workgroups per CU
+    // ring stages: with two or three workgroups per compute unit a second stage is
+    // enough (a third measured no faster at D = 128)
+    static constexpr int NST = D < 128 ? 4 : NW == 8 ? 3 : 2;
     static constexpr int STAGE = 16 * D * 2;    // bytes of one wave stage
     static constexpr int RING = NW * NST * STAGE;
-    static constexpr int TOPK_MAX = 2048;
     // U reductions run in NDH rounds of DH columns (so that the NW partial tiles fit
     // the ring); fp32 row stride of a round's tile
     static constexpr int DH = NW == 8 ? (D == 128 ? 64 : D) : 32 < D ? 32 : D;
@@ -83,9 +88,10 @@ struct DenseFwdCfg {
     static_assert(RING >= NW * 32 * RS * 4, "U reduction tile fits the ring");
     static constexpr int EPT = 32 * DH / NT;    // epilogue elements per thread
     static constexpr int TPH = DH / EPT;        // epilogue threads per head
-    // with four waves fp16 dI goes into the p array (p is read into registers first),
-    // so that the LDS of two workgroups fits a compute unit
-    static constexpr bool D16_IN_P = NW < 8;
+    // q is staged in the head-word array when it fits there (free until pass 1), else
+    // in the ring (free until the first key copies)
+    static constexpr int QCOPY_BYTES = NW * ((HP * D * 2 / 1024 + NW - 1) / NW) * 1024;   // dummies included
+    static constexpr bool Q_IN_MASK = QCOPY_BYTES <= NH * TOPK_MAX * 4;
 };
 
 // Swizzle of row `row` of a [16 rows][CH 16-byte chunks] stage tile: logical
@@ -163,9 +169,10 @@ struct UnitInputs {
 // HK: the heads pass 1 multiplies, a multiple of 16 no smaller than the group (16 for
 // groups of up to 16 heads padded to HP = 32: the tile of heads 16..31 holds only zero
 // scores, whose ReLU and S > 0 bits are zero).
-template <int HP, int D, bool F16, bool SREC, int HK = HP>
-__global__ __launch_bounds__(64 * kWaves64, 8 / kWaves64) void grad_dense64_kernel(Problem pb) {
-    using C = DenseFwdCfg<HP, D, kWaves64>;
+template <int HP, int D, bool F16, bool SREC, int HK, int CAP>
+__global__ __launch_bounds__(64 * kWaves64, (DenseFwdCfg<HP, D, kWaves64, CAP>::WGPC)) void grad_dense64_kernel(
+    Problem pb) {
+    using C = DenseFwdCfg<HP, D, kWaves64, CAP>;
     constexpr int kBlock8 = C::NT;
     constexpr int STEP = C::STEP;
     constexpr int NH = C::NH, NDT = C::NDT, NKS = C::NKS, DCH = C::DCH, NL = C::NL;
@@ -179,11 +186,8 @@ __global__ __launch_bounds__(64 * kWaves64, 8 / kWaves64) void grad_dense64_kern
     __shared__ __attribute__((aligned(1024))) char s_ring[C::RING];
     __shared__ __attribute__((aligned(16))) uint32_t s_mask[NH * TOPK_MAX];   // [word][position]
     __shared__ __attribute__((aligned(16))) float s_I[TOPK_MAX];              // I, then dI
-    __shared__ __attribute__((aligned(16))) float s_p[TOPK_MAX];
-    __shared__ __attribute__((aligned(16))) int32_t s_key[TOPK_MAX];
-    __shared__ __attribute__((aligned(16))) uint16_t s_slot[TOPK_MAX];
-    __shared__ __attribute__((aligned(16))) uint16_t s_d16a[C::D16_IN_P ? 8 : TOPK_MAX];   // fp16 dI 2^eds
-    uint16_t *const s_d16 = C::D16_IN_P ? (uint16_t *)s_p : s_d16a;
+    __shared__ __attribute__((aligned(16))) int32_t s_key[TOPK_MAX];          // key row
+    __shared__ __attribute__((aligned(16))) uint16_t s_d16[TOPK_MAX];         // fp16 dI 2^eds
     __shared__ __attribute__((aligned(16))) float s_w[HP];
     __shared__ float s_red[NW * 6];
 
@@ -277,15 +281,15 @@ __global__ __launch_bounds__(64 * kWaves64, 8 / kWaves64) void grad_dense64_kern
         const int s0 = tu * spt;
         if (tu < HP) s_w[tu] = in.wt;
         // ---- q of the unit into LDS once, [HP rows][D] with the key tiles' swizzle, in
-        //      the head-mask array (free until pass 1): 1 KiB direct-to-LDS copies shared
-        //      out over the waves, the same number per wave (copies past the block's
-        //      end fill unused head-mask space); rows past G read past the end of the
-        //      range-checked view and arrive as zeros
-        char *const s_q = (char *)s_mask;
+        //      the head-word array or the ring: 1 KiB direct-to-LDS copies shared out
+        //      over the waves, the same number per wave (copies past the block's end fill
+        //      unused space); rows past G read past the end of the range-checked view and
+        //      arrive as zeros
+        char *const s_q = C::Q_IN_MASK ? (char *)s_mask : s_ring;
         {
             constexpr int NQC = HP * D * 2 / 1024;
             constexpr int CPW = (NQC + NW - 1) / NW;
-            static_assert(NW * CPW * 1024 <= NH * TOPK_MAX * 4, "q copies fit the head-mask array");
+            static_assert(NW * CPW * 1024 <= (C::Q_IN_MASK ? NH * TOPK_MAX * 4 : C::RING), "q copies fit");
             const __amdgpu_buffer_rsrc_t rq =
                 __builtin_amdgcn_make_buffer_rsrc((void *)qrow, (short)0, G * D * 2, 0x00020000);
             const int ln = tu & 63;
@@ -300,17 +304,18 @@ __global__ __launch_bounds__(64 * kWaves64, 8 / kWaves64) void grad_dense64_kern
             }
         }
 
-        // ---- compact the valid slots: key row, slot id, p ------------------------------
+        // ---- compact the valid slots into positions (key rows); the softmax later walks
+        //      this thread's slots again, from the valid-slot bits, the first position
+        //      and p kept in registers
         int cnt = 0;
-        uint32_t zslots = 0;              // in-range slots that are -1 / out of range
+        uint32_t vbits = 0;               // valid slots of this thread
         float kmx = -1.f, kmn_neg = -3.0e38f, pabs = 0.f, pmx = 0.f;
 #pragma unroll
         for (int i = 0; i < SPT_MAX; ++i) {
             const int v = in.iv[i];
-            const bool inr = i < spt && s0 + i < topk;
             const bool ok = v >= 0 && v < klen;
             cnt += ok ? 1 : 0;
-            zslots |= (inr && !ok) ? (1u << i) : 0u;
+            vbits |= ok ? (1u << i) : 0u;
             if (ok) {
                 pabs += fabsf(in.pv[i]);
                 pmx = fmaxf(pmx, fabsf(in.pv[i]));
@@ -320,25 +325,23 @@ __global__ __launch_bounds__(64 * kWaves64, 8 / kWaves64) void grad_dense64_kern
         }
         // kept as one register (recomputing it from the slot lists at its late use
         // would keep those live through pass 1)
-        zslots = (uint32_t)opaque((int)zslots);
+        vbits = (uint32_t)opaque((int)vbits);
         // one barrier pair: positions of the valid slots, maxima {|p|, key, -key},
         // sum of |p| (its barriers also publish s_w)
         float mxv[3] = {pmx, kmx, kmn_neg};
         float smv[1] = {pabs};
         int nvalid;
         static_assert(SPT_MAX < 16, "block_scan_reduce counts below 16");
-        int pos = block_scan_reduce<3, 1, NW>(cnt, mxv, smv, s_red, &nvalid);
+        const int pstart = block_scan_reduce<3, 1, NW>(cnt, mxv, smv, s_red, &nvalid);
         const float pmax = mxv[0], psum = smv[0];
         const int kmax_i = (int)mxv[1];
         const int kmin_i = nvalid > 0 ? (int)(-mxv[2]) : 0x7fffffff;
+        {
+            int pos = pstart;
 #pragma unroll
-        for (int i = 0; i < SPT_MAX; ++i) {
-            const int v = in.iv[i];
-            if (v >= 0 && v < klen) {
-                s_key[pos] = kbase + v;
-                s_slot[pos] = (uint16_t)(s0 + i);
-                s_p[pos] = in.pv[i];
-                ++pos;
+            for (int i = 0; i < SPT_MAX; ++i) {
+                const int v = in.iv[i];
+                if (v >= 0 && v < klen) s_key[pos++] = kbase + v;
             }
         }
         const int nsteps = (nvalid + STEP - 1) / STEP;
@@ -378,6 +381,8 @@ __global__ __launch_bounds__(64 * kWaves64, 8 / kWaves64) void grad_dense64_kern
             qm = wave_max(__uint_as_float(m1 << 16));
         }
         const float qmax = qm;
+        // q staged in the ring: every wave has it in registers before the key copies
+        if constexpr (!C::Q_IN_MASK) lds_barrier();
 
         // ---- key stream: steps [0, nsteps) pass 1 (k), [nsteps, 2 nsteps) pass 2 ------
         // copy i of a wave step: lane l writes physical chunk l % DCH of stage row
@@ -482,9 +487,10 @@ __global__ __launch_bounds__(64 * kWaves64, 8 / kWaves64) void grad_dense64_kern
             wr[hq][0] = w4.x; wr[hq][1] = w4.y; wr[hq][2] = w4.z; wr[hq][3] = w4.w;
         }
         // the zero stores (and the first copies, issued just before them) complete
-        // before the integer adds of pass 2 in any wave
+        // before the integer adds of pass 2 in any wave (and every wave has q in
+        // registers: pass 1 may overwrite the head-word array)
         wait_vmcnt<0>();
-        lds_barrier();            // every wave has q in registers: pass 1 may overwrite s_mask
+        lds_barrier();
 
         // ---- pass 1: S tiles (16 heads x 16 keys) on MFMA; ReLU, w, head bits ----------
         // tile element i of lane l: head 16 hq + 4 grp + i, key l16 of the wave's 16.
@@ -543,35 +549,35 @@ __global__ __launch_bounds__(64 * kWaves64, 8 / kWaves64) void grad_dense64_kern
         }
 
         // ---- softmax over the valid positions: m, Z, y -> softmax_out, dI ------------
+        // Every thread walks its own slots again: the valid ones hold consecutive
+        // positions from pstart; y goes to the slot (0 at in-range slots that are not
+        // valid).
         const float m = block_max<NW>(mloc, s_red);     // (its barriers publish s_I, s_mask)
-        constexpr int PPT = C::PPT;                    // positions per thread
-        const int p0 = tid * PPT;
-        float e[PPT];
+        float e[SPT_MAX], iv[SPT_MAX];
         float zl = 0.f;
-        float iv4[PPT], pp4[PPT];
+        {
+            int pp = pstart;
 #pragma unroll
-        for (int i = 0; i < PPT; i += 4) {
-            const float4 a0 = *(const float4 *)(s_I + p0 + i);
-            const float4 b0 = *(const float4 *)(s_p + p0 + i);
-            iv4[i] = a0.x; iv4[i + 1] = a0.y; iv4[i + 2] = a0.z; iv4[i + 3] = a0.w;
-            pp4[i] = b0.x; pp4[i + 1] = b0.y; pp4[i + 2] = b0.z; pp4[i + 3] = b0.w;
+            for (int i = 0; i < SPT_MAX; ++i) {
+                iv[i] = 0.f;
+                e[i] = 0.f;
+                if ((vbits >> i) & 1u) {
+                    iv[i] = s_I[pp++];
+                    e[i] = expf(iv[i] - m);
+                }
+                zl += e[i];
+            }
         }
-#pragma unroll
-        for (int i = 0; i < PPT; ++i) {
-            e[i] = p0 + i < nvalid ? expf(iv4[i] - m) : 0.f;
-            zl += e[i];
-        }
-        // (its barriers also order every read of p above before the fp16 dI stores
-        // below when those share the p array)
+        // (its barriers also order every read of I above before the dI stores below)
         const float Z = block_sum<NW>(zl, s_red + 2 * NW);
         const float invZ = 1.f / Z;
         if (pb.kl) {
-            // the unit's KL(p || y): p (log p - (I - m - log Z)) over positions with p > 0
+            // the unit's KL(p || y): p (log p - (I - m - log Z)) over slots with p > 0
             const float lz = logf(Z);
             float kl = 0.f;
 #pragma unroll
-            for (int i = 0; i < PPT; ++i)
-                if (p0 + i < nvalid && pp4[i] > 0.f) kl += pp4[i] * (logf(pp4[i]) - (iv4[i] - m) + lz);
+            for (int i = 0; i < SPT_MAX; ++i)
+                if (((vbits >> i) & 1u) && in.pv[i] > 0.f) kl += in.pv[i] * (logf(in.pv[i]) - (iv[i] - m) + lz);
             kl = block_sum<NW>(kl, s_red + 2 * NW);
             if (tid == 0) pb.kl[u] = kl;
         }
@@ -580,31 +586,30 @@ __global__ __launch_bounds__(64 * kWaves64, 8 / kWaves64) void grad_dense64_kern
         const int eds = pow2_exponent_below_2p15(fmaxf(invZ, pmax));
         const float dsc = ldexpf(1.f, eds);
         {
-            uint32_t d16w[PPT / 2];
+            float yv[SPT_MAX];
+            int pp = pstart;
 #pragma unroll
-            for (int i = 0; i < PPT; i += 2) {
-                float dd[2];
-#pragma unroll
-                for (int k2 = 0; k2 < 2; ++k2) {
-                    const int pp = p0 + i + k2;
-                    dd[k2] = 0.f;
-                    if (pp < nvalid) {
-                        const float y = e[i + k2] * invZ;
-                        dd[k2] = y - pp4[i + k2];
-                        yrow[s_slot[pp]] = y;
-                        s_I[pp] = dd[k2];
-                    }
+            for (int i = 0; i < SPT_MAX; ++i) {
+                yv[i] = 0.f;                           // (a unit with no valid slot has Z = 0)
+                if ((vbits >> i) & 1u) {
+                    yv[i] = e[i] * invZ;
+                    const float dd = yv[i] - in.pv[i];
+                    s_I[pp] = dd;
+                    s_d16[pp] = to16<true>(dd * dsc);
+                    ++pp;
                 }
-                d16w[i / 2] = pack2<true>(dd[0] * dsc, dd[1] * dsc);
             }
-            if (p0 < nsteps * STEP) {
+            float *const ys = yrow + s0;
+            if (spt == SPT_MAX && s0 + SPT_MAX <= topk && (((uintptr_t)ys) & 15) == 0 && SPT_MAX % 4 == 0) {
 #pragma unroll
-                for (int i = 0; i < PPT / 2; i += 2) *(u32x2 *)(s_d16 + p0 + 2 * i) = u32x2{d16w[i], d16w[i + 1]};
+                for (int i = 0; i < SPT_MAX; i += 4)
+                    *(float4 *)(ys + i) = float4{yv[i], yv[i + 1], yv[i + 2], yv[i + 3]};
+            } else {
+#pragma unroll
+                for (int i = 0; i < SPT_MAX; ++i)
+                    if (i < spt && s0 + i < topk) ys[i] = yv[i];
             }
         }
-#pragma unroll
-        for (int i = 0; i < SPT_MAX; ++i)
-            if (zslots & (1u << i)) yrow[s0 + i] = 0.f;
         lds_barrier();
 
         // ---- pass 2: U^T += K16^T dS16^T over this wave's positions ----------------------
@@ -795,31 +800,44 @@ __global__ __launch_bounds__(64 * kWaves64, 8 / kWaves64) void grad_dense64_kern
     }
 }
 
-template <int HP, int D, bool F16, int HK>
+template <int HP, int D, bool F16, int HK, int CAP>
 static hipError_t launch_gd64_hk(const Problem &pb, int grid, bool srec, hipStream_t stream) {
     if (srec)
-        hipLaunchKernelGGL((grad_dense64_kernel<HP, D, F16, true, HK>), dim3(grid), dim3(64 * kWaves64), 0, stream, pb);
+        hipLaunchKernelGGL((grad_dense64_kernel<HP, D, F16, true, HK, CAP>), dim3(grid), dim3(64 * kWaves64), 0, stream,
+                           pb);
     else
-        hipLaunchKernelGGL((grad_dense64_kernel<HP, D, F16, false, HK>), dim3(grid), dim3(64 * kWaves64), 0, stream, pb);
+        hipLaunchKernelGGL((grad_dense64_kernel<HP, D, F16, false, HK, CAP>), dim3(grid), dim3(64 * kWaves64), 0,
+                           stream, pb);
     return hipGetLastError();
 }
 
 // groups of up to 16 heads (padded to 32) multiply 16 heads in pass 1
-template <int HP, int D, bool F16>
-static hipError_t launch_gd64(const Problem &pb, int grid, bool srec, hipStream_t stream) {
+template <int HP, int D, bool F16, int CAP>
+static hipError_t launch_gd64_cap(const Problem &pb, int grid, bool srec, hipStream_t stream) {
     if constexpr (HP == 32) {
-        if (pb.group <= 16) return launch_gd64_hk<HP, D, F16, 16>(pb, grid, srec, stream);
+        if (pb.group <= 16) return launch_gd64_hk<HP, D, F16, 16, CAP>(pb, grid, srec, stream);
     }
-    return launch_gd64_hk<HP, D, F16, HP>(pb, grid, srec, stream);
+    return launch_gd64_hk<HP, D, F16, HP, CAP>(pb, grid, srec, stream);
 }
 
 template <int HP, int D, bool F16>
-static int blocks_gd64() {
+static hipError_t launch_gd64(const Problem &pb, int cap, int grid, bool srec, hipStream_t stream) {
+    if (cap == 0) return launch_gd64_cap<HP, D, F16, 0>(pb, grid, srec, stream);
+    return launch_gd64_cap<HP, D, F16, 1>(pb, grid, srec, stream);
+}
+
+template <int HP, int D, bool F16, int CAP>
+static int blocks_gd64_cap() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grad_dense64_kernel<HP, D, F16, false>, 64 * kWaves64, 0) !=
-        hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grad_dense64_kernel<HP, D, F16, false, HP, CAP>,
+                                                     64 * kWaves64, 0) != hipSuccess)
         return 0;
     return n;
+}
+
+template <int HP, int D, bool F16>
+static int blocks_gd64(int cap) {
+    return cap == 0 ? blocks_gd64_cap<HP, D, F16, 0>() : blocks_gd64_cap<HP, D, F16, 1>();
 }
 
 }  // namespace dense64
@@ -834,14 +852,14 @@ static int blocks_gd64() {
         if (hp == 64 && d == 128) return f16 ? FN<64, 128, true>(__VA_ARGS__) : FN<64, 128, false>(__VA_ARGS__);  \
     } while (0)
 
-hipError_t launch_grad_dense64(const Problem &pb, int hp, bool f16, int grid, bool srec, hipStream_t stream) {
+hipError_t launch_grad_dense64(const Problem &pb, int hp, bool f16, int cap, int grid, bool srec, hipStream_t stream) {
     const int d = pb.d;
-    SLIKL_GD64_CASES(dense64::launch_gd64, pb, grid, srec, stream);
+    SLIKL_GD64_CASES(dense64::launch_gd64, pb, cap, grid, srec, stream);
     return hipErrorInvalidValue;
 }
 
-int grad_dense64_blocks_per_cu(int hp, int d, bool f16) {
-    SLIKL_GD64_CASES(dense64::blocks_gd64);
+int grad_dense64_blocks_per_cu(int hp, int d, bool f16, int cap) {
+    SLIKL_GD64_CASES(dense64::blocks_gd64, cap);
     return 0;
 }
 

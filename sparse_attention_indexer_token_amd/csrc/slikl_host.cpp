@@ -274,8 +274,9 @@ slikl_status resolve_parts(const slikl_desc *d, int32_t *parts) {
     const int mode = dk_strategy(d);
     const int hp = head_tile(d->n1 / d->n2);
     const bool f16 = d->dtype == SLIKL_DTYPE_F16;
-    int per_cu = mode == 2 || sorted_dk(d) ? slikl::grad_dense_blocks_per_cu(hp, (int)d->d, f16)
-                                          : slikl::grad_fused_blocks_per_cu(hp, (int)d->d, f16, mode);
+    int per_cu = mode == 2 || sorted_dk(d)
+                     ? slikl::grad_dense_blocks_per_cu(hp, (int)d->d, f16, slikl::dense64_cap(d->topk))
+                     : slikl::grad_fused_blocks_per_cu(hp, (int)d->d, f16, mode);
     int64_t p = (int64_t)cus * per_cu;
     if (p > SLIKL_MAX_PARTS) p = SLIKL_MAX_PARTS;
     if (p < 1) p = 1;
@@ -525,7 +526,8 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
     }
     if (t1 > 0) {
         pe.begin(SLIKL_PHASE_FUSED);
-        e = mode == 2 || s8 ? slikl::launch_grad_dense(pb, head_tile(pb.group), f16, parts, s8, s)
+        e = mode == 2 || s8 ? slikl::launch_grad_dense(pb, head_tile(pb.group), f16, slikl::dense64_cap(desc->topk),
+                                                       parts, s8, s)
                             : slikl::launch_grad_fused(pb, head_tile(pb.group), f16, mode, parts, s);
         pe.end(SLIKL_PHASE_FUSED);
         if (e != hipSuccess) return SLIKL_ERR_LAUNCH;

@@ -142,10 +142,12 @@ int grad_fused_blocks_per_cu(int hp, int d, bool f16, int mode);
 // fused kernel of the dense dK strategy: writes the dense records above, or with srec
 // the per-slot records of the key-sorted strategy (the 64-head kernel up to 64 heads, the 128-head one
 // above)
-hipError_t launch_grad_dense(const Problem &pb, int hp, bool f16, int grid, bool srec, hipStream_t stream);
-int grad_dense_blocks_per_cu(int hp, int d, bool f16);
+hipError_t launch_grad_dense(const Problem &pb, int hp, bool f16, int cap, int grid, bool srec, hipStream_t stream);
+int grad_dense_blocks_per_cu(int hp, int d, bool f16, int cap);
+// capacity form of the 64-head kernel: 0 for top-k lists of at most 512 slots, else 1
+inline int dense64_cap(int64_t topk) { return topk <= 512 ? 0 : 1; }
 // 64-head variant for head groups of up to 64 (called by the two above)
-hipError_t launch_grad_dense64(const Problem &pb, int hp, bool f16, int grid, bool srec, hipStream_t stream);
+hipError_t launch_grad_dense64(const Problem &pb, int hp, bool f16, int cap, int grid, bool srec, hipStream_t stream);
 // scatter dK from the 64-head kernel's per-slot records (head groups up to 64)
 // dK parts of the key-sorted strategy from the 64-head kernel's slot records
 // (head groups up to 64), stored into dk_parts
@@ -163,7 +165,7 @@ struct SortGeometry {
 SortGeometry sorted_geometry(int64_t nslot, int64_t nbins);
 hipError_t launch_sorted_prepare(const Problem &pb, hipStream_t stream);
 hipError_t launch_sorted_reduce(const Problem &pb, bool det, hipStream_t stream);
-int grad_dense64_blocks_per_cu(int hp, int d, bool f16);
+int grad_dense64_blocks_per_cu(int hp, int d, bool f16, int cap);
 // Up to 8 byte ranges (16-byte aligned starts, sizes multiples of 4) zeroed by one launch.
 // Parts are stored as 16-bit integers with a per-record multiplier when no key row
 // takes more than this many parts; their rounding error (at most 2^-15 of the part's
