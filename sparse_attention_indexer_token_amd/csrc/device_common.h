@@ -204,6 +204,39 @@ __device__ __forceinline__ int block_max_int(int v, int *red) {
     return a > b ? a : b;
 }
 
+// Block maxima of mx[] and sums of sm[] over NW wavefronts with one barrier pair (sums
+// in wave order); `red` holds at least NW * (NM + NS) floats.
+template <int NW, int NM, int NS>
+__device__ __forceinline__ void block_max_sum(float (&mx)[NM], float (&sm)[NS], float *red) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < NM; ++i) mx[i] = wave_max(mx[i]);
+#pragma unroll
+    for (int i = 0; i < NS; ++i) sm[i] = wave_sum(sm[i]);
+    lds_barrier();
+    if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < NM; ++i) red[wave * (NM + NS) + i] = mx[i];
+#pragma unroll
+        for (int i = 0; i < NS; ++i) red[wave * (NM + NS) + NM + i] = sm[i];
+    }
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < NM; ++i) {
+        float r = red[i];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) r = fmaxf(r, red[w * (NM + NS) + i]);
+        mx[i] = r;
+    }
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+        float r = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) r += red[w * (NM + NS) + NM + i];
+        sm[i] = r;
+    }
+}
+
 // Several block-wide reductions with one barrier pair: on return mx[i] holds
 // the block maximum of mx[i] and sm[i] the block sum of sm[i].  `red` holds
 // at least 4 * (NM + NS) floats.

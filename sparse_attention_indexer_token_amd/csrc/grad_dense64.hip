@@ -73,6 +73,11 @@ struct DenseFwdCfg {
     static constexpr int NT = 64 * NW;          // threads of a workgroup
     static constexpr int STEP = 16 * NW;        // positions of one step
     static constexpr int TOPK_MAX = CAP == 0 ? 512 : 2048;
+    // keys covered by the bitmap that finds a unit's repeated keys (longer key ranges
+    // count as repeating).  None for lists of at most 512 slots: there the check's LDS
+    // atomics, which serialize on keys named many times (attention sinks), cost more
+    // than the record atomics it saves (contention workload 1.01 -> 1.05 ms).
+    static constexpr int KBITS = CAP == 0 ? 0 : 65536;
     static constexpr int SPT = TOPK_MAX / NT;   // slots of one row per thread (topk <= TOPK_MAX)
     static constexpr int WGPC = NW == 8 ? 1 : (CAP == 0 && HP == 32 ? 3 : 2);   // workgroups per CU
     // ring stages: with two or three workgroups per compute unit a second stage is
@@ -190,6 +195,9 @@ __global__ __launch_bounds__(64 * kWaves64, (DenseFwdCfg<HP, D, kWaves64, CAP>::
     __shared__ __attribute__((aligned(16))) uint16_t s_d16[TOPK_MAX];         // fp16 dI 2^eds
     __shared__ __attribute__((aligned(16))) float s_w[HP];
     __shared__ float s_red[NW * 6];
+    // one bit per key of the unit's batch: set by the unit's valid slots, so that a key
+    // named twice shows (dense records only)
+    __shared__ uint32_t s_kbits[SREC || C::KBITS == 0 ? 1 : C::KBITS / 32];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -253,6 +261,10 @@ __global__ __launch_bounds__(64 * kWaves64, (DenseFwdCfg<HP, D, kWaves64, CAP>::
             in.pv[i] = ok ? c : 0.f;
         }
     };
+    if constexpr (!SREC && C::KBITS > 0) {
+        for (int i = threadIdx.x; i < C::KBITS / 32; i += C::NT) s_kbits[i] = 0u;
+        __syncthreads();
+    }
     bool have = next_unit();
     if (have) load_inputs(cu);
 
@@ -310,6 +322,7 @@ __global__ __launch_bounds__(64 * kWaves64, (DenseFwdCfg<HP, D, kWaves64, CAP>::
         int cnt = 0;
         uint32_t vbits = 0;               // valid slots of this thread
         float kmx = -1.f, kmn_neg = -3.0e38f, pabs = 0.f, pmx = 0.f;
+        const bool kbits_ok = !SREC && C::KBITS > 0 && klen <= C::KBITS;
 #pragma unroll
         for (int i = 0; i < SPT_MAX; ++i) {
             const int v = in.iv[i];
@@ -321,6 +334,7 @@ __global__ __launch_bounds__(64 * kWaves64, (DenseFwdCfg<HP, D, kWaves64, CAP>::
                 pmx = fmaxf(pmx, fabsf(in.pv[i]));
                 kmx = fmaxf(kmx, (float)v);
                 kmn_neg = fmaxf(kmn_neg, -(float)v);
+                if (kbits_ok) atomicOr(&s_kbits[v >> 5], 1u << (v & 31));
             }
         }
         // kept as one register (recomputing it from the slot lists at its late use
@@ -548,11 +562,29 @@ __global__ __launch_bounds__(64 * kWaves64, (DenseFwdCfg<HP, D, kWaves64, CAP>::
             }
         }
 
+        // ---- the running max of I and the keys named: with as many bits set as valid
+        //      slots, no key is named twice and every dK record (u, j) has one writer (a
+        //      plain store; else integer atomics).  The bits are cleared as counted. ----
+        float m;
+        bool unit_dup = true;
+        {
+            int pc = 0;
+            if (kbits_ok) {
+                for (int i = tid; i < (klen + 31) / 32; i += kBlock8) {
+                    pc += __popc(s_kbits[i]);
+                    s_kbits[i] = 0u;
+                }
+            }
+            float mx[1] = {mloc};
+            float sm[1] = {(float)pc};
+            block_max_sum<NW>(mx, sm, s_red);            // (its barriers publish s_I, s_mask)
+            m = mx[0];
+            unit_dup = !kbits_ok || (int)sm[0] != nvalid;
+        }
         // ---- softmax over the valid positions: m, Z, y -> softmax_out, dI ------------
         // Every thread walks its own slots again: the valid ones hold consecutive
         // positions from pstart; y goes to the slot (0 at in-range slots that are not
         // valid).
-        const float m = block_max<NW>(mloc, s_red);     // (its barriers publish s_I, s_mask)
         float e[SPT_MAX], iv[SPT_MAX];
         float zl = 0.f;
         {
@@ -653,7 +685,9 @@ __global__ __launch_bounds__(64 * kWaves64, (DenseFwdCfg<HP, D, kWaves64, CAP>::
                     }
                 } else if (!SREC && pr < nvalid) {
                     const int jrel = s_key[pr] - kbase;
-                    atomicAdd(dimap + jrel, (int32_t)__float2int_rn(s_I[pr] * dfix));
+                    const int32_t dv = (int32_t)__float2int_rn(s_I[pr] * dfix);
+                    if (unit_dup) atomicAdd(dimap + jrel, dv);
+                    else dimap[jrel] = dv;
                     if constexpr (NH == 1) {
                         mmap[jrel] = s_mask[pr];
                     } else if constexpr (NH == 2) {
