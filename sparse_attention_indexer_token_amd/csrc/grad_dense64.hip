@@ -146,6 +146,28 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// as wait_for_step, with R more memory operations (dK records) issued after the awaited
+// copies when `rec` is set
+template <int NST, int NL, int R>
+__device__ __forceinline__ void wait_for_step_rec(int ahead, bool rec) {
+    if constexpr (NST >= 4) {
+        if (ahead >= 2) {
+            if (rec) wait_vmcnt<2 * NL + R>();
+            else wait_vmcnt<2 * NL>();
+            return;
+        }
+    }
+    if constexpr (NST >= 3) {
+        if (ahead >= 1) {
+            if (rec) wait_vmcnt<NL + R>();
+            else wait_vmcnt<NL>();
+            return;
+        }
+    }
+    if (rec) wait_vmcnt<R>();
+    else wait_vmcnt<0>();
+}
+
 template <int NST, int NL>
 __device__ __forceinline__ void wait_for_step(int ahead) {
     // `ahead` later steps have their copies in flight behind this one
@@ -663,42 +685,66 @@ __global__ __launch_bounds__(64 * kWaves64, (DenseFwdCfg<HP, D, kWaves64, CAP>::
         for (int ht = 0; ht < NH; ++ht)
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) uacc[ht][dt] = f32x16{};
+        // dK records go out after a step's copies, as a fixed number of memory operations
+        // per wave (range-checked stores and atomics: those of lanes past the valid
+        // positions land past their view and are dropped), so that the copy waits count
+        // past them instead of waiting for their writes
+        constexpr int NREC = SREC ? 3 : 2;
+        const __amdgpu_buffer_rsrc_t rrec0 =
+            SREC ? __builtin_amdgcn_make_buffer_rsrc((void *)(pb.srec_key + (size_t)u * topk), (short)0, topk * 4,
+                                                     0x00020000)
+                 : __builtin_amdgcn_make_buffer_rsrc((void *)dimap, (short)0, (int)pb.s2max * 4, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rrec1 =
+            SREC ? __builtin_amdgcn_make_buffer_rsrc((void *)(pb.srec_mask + (size_t)u * topk * NH), (short)0,
+                                                     topk * NH * 4, 0x00020000)
+                 : __builtin_amdgcn_make_buffer_rsrc((void *)mmap, (short)0, (int)pb.s2max * NH * 4, 0x00020000);
+        const __amdgpu_buffer_rsrc_t rrec2 =
+            __builtin_amdgcn_make_buffer_rsrc((void *)(SREC ? pb.srec_dI + (size_t)u * topk : nullptr), (short)0,
+                                              SREC ? topk * 4 : 0, 0x00020000);
         for (int s = 0; s < nsteps; ++s) {
             const int sigma = nsteps + s;
-            wait_for_step<NST, NL>(T - 1 - sigma);
+            // records went out at pass-2 steps j with j % 4 == 0, after the copies of that
+            // step: those in the last NST - 1 steps are younger than this step's copies
+            bool rec = false;
+#pragma unroll
+            for (int j = 1; j < NST; ++j) rec |= s - j >= 0 && ((s - j) & 3) == 0;
+            wait_for_step_rec<NST, NL, NREC>(T - 1 - sigma, rec);
+            if (sigma + NST - 1 < T) issue(sigma + NST - 1);
             if ((s & 3) == 0) {
                 // dK records of this wave's positions of steps s .. s+3, one per lane:
-                // dI summed per key (fixed point, integer adds) and the head words.
-                // Scattered writes; spread over pass 2 they hide behind the other
-                // wave's MFMA work.  Issued before the next copies, so that the copies
-                // after an awaited one stay the last NL memory operations.
+                // dI summed per key (fixed point; integer adds when a key may be named
+                // twice) and the head words.  Scattered writes; spread over pass 2 they
+                // hide behind the other wave's MFMA work.
                 const int pr = (s + (lane >> 4)) * STEP + wave * 16 + (lane & 15);
-                if (SREC && pr < nvalid) {
+                const bool okr = pr < nvalid;
+                const int prc = okr ? pr : 0;
+                const uint32_t w0 = s_mask[prc];
+                const uint32_t w1 = NH > 1 ? s_mask[TOPK_MAX + prc] : 0u;
+                if constexpr (SREC) {
                     // per-slot records: key row, dI, head words
-                    const size_t o = (size_t)u * topk + pr;
-                    pb.srec_key[o] = s_key[pr];
-                    pb.srec_dI[o] = s_I[pr];
+                    const uint32_t o4 = okr ? (uint32_t)pr * 4u : kPadOffset;
+                    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)s_key[prc], rrec0, o4, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s_I[prc]), rrec2, o4, 0, 0);
                     if constexpr (NH == 1) {
-                        pb.srec_mask[o] = s_mask[pr];
+                        __builtin_amdgcn_raw_buffer_store_b32(w0, rrec1, o4, 0, 0);
                     } else {
-                        *(u32x2 *)(pb.srec_mask + o * 2) = u32x2{s_mask[pr], s_mask[TOPK_MAX + pr]};
+                        __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, rrec1,
+                                                              okr ? (uint32_t)pr * 8u : kPadOffset, 0, 0);
                     }
-                } else if (!SREC && pr < nvalid) {
-                    const int jrel = s_key[pr] - kbase;
-                    const int32_t dv = (int32_t)__float2int_rn(s_I[pr] * dfix);
-                    if (unit_dup) atomicAdd(dimap + jrel, dv);
-                    else dimap[jrel] = dv;
+                } else {
+                    const int jrel = s_key[prc] - kbase;
+                    const uint32_t o4 = okr ? (uint32_t)jrel * 4u : kPadOffset;
+                    const int32_t dv = (int32_t)__float2int_rn(s_I[prc] * dfix);
+                    if (unit_dup) (void)__builtin_amdgcn_raw_ptr_buffer_atomic_add_i32(dv, rrec0, (int)o4, 0, 0);
+                    else __builtin_amdgcn_raw_buffer_store_b32((uint32_t)dv, rrec0, o4, 0, 0);
                     if constexpr (NH == 1) {
-                        mmap[jrel] = s_mask[pr];
-                    } else if constexpr (NH == 2) {
-                        *(u32x2 *)(mmap + jrel * 2) = u32x2{s_mask[pr], s_mask[TOPK_MAX + pr]};
+                        __builtin_amdgcn_raw_buffer_store_b32(w0, rrec1, o4, 0, 0);
                     } else {
-                        *(u32x4 *)(mmap + jrel * 4) = u32x4{s_mask[pr], s_mask[TOPK_MAX + pr],
-                                                            s_mask[2 * TOPK_MAX + pr], s_mask[3 * TOPK_MAX + pr]};
+                        __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, rrec1,
+                                                              okr ? (uint32_t)jrel * 8u : kPadOffset, 0, 0);
                     }
                 }
             }
-            if (sigma + NST - 1 < T) issue(sigma + NST - 1);
             const char *kb = ring + (sigma % NST) * C::STAGE;
             // B operand: head l32 of each 32-head tile, positions pk .. pk+7 as k
             const int pk = s * STEP + wave * 16 + 8 * half;
