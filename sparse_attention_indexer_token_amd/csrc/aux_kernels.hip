@@ -2,6 +2,7 @@
 // fixed-point scale, and the load-balancing metadata pre-pass.
 #include "device_common.h"
 #include "slikl_internal.h"
+#include "scale_block.h"
 
 namespace slikl {
 
@@ -219,7 +220,10 @@ hipError_t launch_det_scale(const Problem &pb, bool f16, float *scale_block, hip
 // two 2^eK (from max|k|) maps the keys into fp16's range:  max|k| 2^eK < 2^15.
 // bf16 values carry 8 significant bits, fp16 11, so every key whose scaled
 // magnitude is >= 2^-14 converts exactly; smaller ones keep an absolute error
-// below 2^-25 * 2^-eK.  scale block: [5] max|k| bits, [6] 2^-eK, [7] 2^eK.
+// below 2^-25 * 2^-eK.  scale block: [6] 2^-eK, [7] 2^eK; the maximum is taken
+// in kKmaxSlots words, one per 128-byte line from int kKmaxBase on (block b adds
+// its maximum to word b % kKmaxSlots: atomics on one address serialise at its
+// L2 channel, about 12 ns each, so 2048 blocks on one word cost ~25 us).
 // ---------------------------------------------------------------------------
 // max |k| over bf16 keys, 16 bytes per load; for bf16 bits b, |x| orders as the
 // integer b & 0x7fff, so the maximum is taken on packed bit patterns
@@ -243,12 +247,18 @@ __global__ __launch_bounds__(256) void kmax_kernel(const uint16_t *k, size_t n8,
     if (threadIdx.x == 0) {
         uint32_t r = s_m[0];
         for (int w = 1; w < 4; ++w) r = s_m[w] > r ? s_m[w] : r;
-        atomicMax(blk + 5, __float_as_uint(__uint_as_float(r << 16)));
+        atomicMax(blk + kKmaxBase + 32 * (blockIdx.x % kKmaxSlots), __float_as_uint(__uint_as_float(r << 16)));
     }
 }
 
 __device__ __forceinline__ int k_exponent(const uint32_t *blk) {
-    float m = __uint_as_float(blk[5]);
+    uint32_t mb = 0;
+#pragma unroll
+    for (int j = 0; j < kKmaxSlots; ++j) {
+        const uint32_t x = blk[kKmaxBase + 32 * j];
+        mb = x > mb ? x : mb;
+    }
+    float m = __uint_as_float(mb);
     if (!(m > 0.f) || !(m < INFINITY)) return 0;
     int ex;
     frexpf(m, &ex);
@@ -386,6 +396,8 @@ __device__ __forceinline__ int check_cu(const int32_t *cu, int batch, int64_t to
     return (bad ? 1 : 0) | (lng ? 2 : 0);
 }
 
+constexpr int kSplitIlp = 16;
+
 __global__ __launch_bounds__(1024) void meta_split_kernel(Problem pb, int parts, int mode, int overhead,
                                                           int64_t *prefix, const int32_t *cflags,
                                                           int ncflags, int32_t *md) {
@@ -437,7 +449,21 @@ __global__ __launch_bounds__(1024) void meta_split_kernel(Problem pb, int parts,
         const int64_t a = (int64_t)tid * seg, e = a + seg < U ? a + seg : U;
         const bool inlds = U <= kSplitLds && pb.topk + overhead < 65536;
         if (inlds) {
-            for (int64_t i = tid; i < U; i += nt) s_cost[i] = (uint16_t)prefix[i + 1];
+            // batches of kSplitIlp loads in flight per thread (one dependent round trip per
+            // load would cost ~1 us each at 64 K units)
+            for (int64_t i0 = tid; i0 < U; i0 += (int64_t)nt * kSplitIlp) {
+                int64_t v[kSplitIlp];
+#pragma unroll
+                for (int j = 0; j < kSplitIlp; ++j) {
+                    const int64_t i = i0 + (int64_t)nt * j;
+                    v[j] = prefix[(i < U ? i : 0) + 1];
+                }
+#pragma unroll
+                for (int j = 0; j < kSplitIlp; ++j) {
+                    const int64_t i = i0 + (int64_t)nt * j;
+                    if (i < U) s_cost[i] = (uint16_t)v[j];
+                }
+            }
             __syncthreads();
         }
         auto cost = [&](int64_t i) -> int64_t { return inlds ? (int64_t)s_cost[i] : prefix[i + 1]; };
@@ -508,7 +534,16 @@ __global__ __launch_bounds__(1024) void meta_split_kernel(Problem pb, int parts,
     if ((tid & 63) == 0) s_used[tid >> 6] = used;
     // the counting blocks' error words
     int cf = 0;
-    for (int i = tid; i < ncflags; i += nt) cf |= cflags[i];
+    for (int i0 = tid; i0 < ncflags; i0 += nt * kSplitIlp) {
+        int v[kSplitIlp];
+#pragma unroll
+        for (int j = 0; j < kSplitIlp; ++j) {
+            const int i = i0 + nt * j;
+            v[j] = cflags[i < ncflags ? i : 0];
+        }
+#pragma unroll
+        for (int j = 0; j < kSplitIlp; ++j) cf |= i0 + nt * j < ncflags ? v[j] : 0;
+    }
     cf = __syncthreads_or(cf);
     if (tid == 0) {
         int tot = 0;

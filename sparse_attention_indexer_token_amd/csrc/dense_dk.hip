@@ -656,8 +656,20 @@ __global__ void dense_dk_reduce_kernel(Problem pb) {
         }
         const int kbt = (b * pb.n2 + g) * pb.dk_nkb + j / KB;
         const int t0 = pb.kb_tasks[4 * kbt], nt = pb.kb_tasks[4 * kbt + 1];
+        // partials added in task order; loads issued eight at a time (a dependent round
+        // trip per task would bound the kernel by latency)
+        const float *src = pb.dk_part + (size_t)(j % KB) * D + d;
+        const size_t step = (size_t)KB * D;
         float s = 0.f;
-        for (int t = t0; t < t0 + nt; ++t) s += pb.dk_part[((size_t)t * KB + j % KB) * D + d];
+        int t = t0;
+        for (; t + 8 <= t0 + nt; t += 8) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(t + u) * step];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s += v[u];
+        }
+        for (; t < t0 + nt; ++t) s += src[(size_t)t * step];
         pb.dk[i] = to16<F16>(s);
     }
 }

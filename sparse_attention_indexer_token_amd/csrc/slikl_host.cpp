@@ -11,6 +11,7 @@
 
 #include "slikl.h"
 #include "slikl_internal.h"
+#include "scale_block.h"
 
 namespace {
 
@@ -170,7 +171,7 @@ slikl::WorkspacePlan plan(const slikl_desc *d) {
     p.flags_off = off;
     off = align_up(off + (size_t)slikl::kMetaCountBlocksMax * 4);
     p.scale_off = off;
-    off = align_up(off + 64);
+    off = align_up(off + slikl::kScaleBlockBytes);
     p.zero_off = off;
     off = align_up(off + 256);
     p.k16_off = off;
@@ -503,7 +504,7 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
         // its unit's named keys meet
         slikl::ZeroRanges zr{};
         zr.add(pb.dk_acc, wp.acc_bytes);
-        zr.add(ws + wp.scale_off, 64);
+        zr.add(ws + wp.scale_off, slikl::kScaleBlockBytes);
         zr.add(ws + wp.zero_off, 256);
         if (mode == 2) zr.add(pb.kb_diff, wp.kbdiff_bytes);
         e = slikl::launch_zero_ranges(zr, s);
