@@ -17,19 +17,19 @@
 //   slots   chunks of 32 per wave (32x32x16 MFMA, k = 16 heads): A = q (rows = d), B =
 //           the head-masked w parts (columns = slots), two MFMAs per head step and d
 //           tile give R = sum_h 1[S > 0] w[h] q[h, :] 2^(eq + ew) per slot, each lane
-//           holding half of one slot's row.  The row is stored as 16-bit integers
-//           R 2^e with a per-slot exponent e from its largest element m (m 2^e in
-//           [2^14, 2^15), so the rounding error is at most 2^-15 m), as row o = unit *
-//           topk + position of the parts buffer (the slots of a chunk are consecutive
-//           rows), and the record's dI is overwritten by the multiplier
-//           dI 2^-(eq + ew + e) that turns the integers back into the part P[s, :].
+//           holding half of one slot's row.  The part P = dI R 2^-(eq + ew) is stored
+//           as 16-bit integers n = P 2^E with a per-slot exponent E from its largest
+//           element m (m 2^E in [2^14, 2^15), so the rounding error is at most
+//           2^-15 m), as row o = unit * topk + position of the parts buffer (the
+//           slots of a chunk are consecutive rows).  E travels in the row: the lowest
+//           bits of elements 0..7, which are rounded to even integers to hold them.
 //           Half the bytes of fp32 rows, with 15 to 16 significant bits where the part
-//           is largest: the parts buffer is written once and read once, and its
-//           traffic bounds the strategy.  When the key sort finds a key taking more
-//           than kPartsI16MaxRefs parts (an attention sink), the rounding errors of
-//           its many parts could add up past the dk tolerance, and the rows are stored
-//           in fp32 instead (same multiplier, without 2^-e).  A reduction sums the
-//           rows of each key through the key-sorted record list.
+//           is largest, and no per-record side data: the parts buffer is written once
+//           and read once, and its traffic bounds the strategy.  When the key sort
+//           finds a key taking more than kPartsI16MaxRefs parts (an attention sink),
+//           the rounding errors of its many parts could add up past the dk tolerance,
+//           and the rows hold the fp32 parts instead.  A reduction sums the rows of
+//           each key through the key-sorted record list.
 //   records the unit's head words and dI are staged in LDS at the unit's start, every
 //           load issued before the first wait (one memory latency per unit, not one
 //           per chunk).
@@ -230,9 +230,9 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
                 return pa;
             };
             if (!i16) {
-                // fp32 rows: R as formed, the multiplier dI 2^-(eq + ew).  Element group
-                // g of a lane is d = 32 dt + 8 g + 4 half + 0..3 of its slot
-                if (ok && half == 0) pb.srec_dI[ubase + p] = dIv * part_mul;
+                // fp32 rows: the part itself, R dI 2^-(eq + ew).  Element group g of a lane
+                // is d = 32 dt + 8 g + 4 half + 0..3 of its slot
+                const float pm = dIv * part_mul;
 #pragma unroll
                 for (int dt = 0; dt < NDT; ++dt) {
                     const f32x16 pa = tile(dt);
@@ -240,8 +240,8 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
                     for (int g = 0; g < 4; ++g) {
                         const uint32_t off = ok ? (uint32_t)((p * D + 32 * dt + 8 * g + 4 * half) * 4) : kSdPadOffset;
                         __builtin_amdgcn_raw_buffer_store_b128(
-                            u32x4{__float_as_uint(pa[4 * g]), __float_as_uint(pa[4 * g + 1]),
-                                  __float_as_uint(pa[4 * g + 2]), __float_as_uint(pa[4 * g + 3])},
+                            u32x4{__float_as_uint(pa[4 * g] * pm), __float_as_uint(pa[4 * g + 1] * pm),
+                                  __float_as_uint(pa[4 * g + 2] * pm), __float_as_uint(pa[4 * g + 3] * pm)},
                             rparts, off, 0, 0);
                     }
                 }
@@ -263,19 +263,24 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
             // is formed again instead of kept from the first
 #pragma unroll
             for (int kh = 0; kh < NKH; ++kh) asm volatile("" : "+v"(ah[kh]), "+v"(al[kh]));
-            // exponent: m 2^e in [2^14, 32767.5), so that every element rounds into the
-            // 16-bit range; the rounding error is then at most 2^-15 of m
+            // the part is dI R 2^-(eq + ew); its largest |element| is |dI| m.  Exponent E:
+            // |dI| m 2^(E - eq - ew) in [2^14, 32766), so every element rounds into the
+            // 16-bit range with an error of at most 2^-15 of the largest; the row stores
+            // the integers n with part = n 2^-E.  E (in [-126, 126], so that 2^-E is a
+            // normal float) travels in the row itself: the low bits of its elements
+            // d = 0..7, which are rounded to even integers for it (an error of at most
+            // 2^-14 of the largest there).  Element d = 2 l + b carries bit l + 4 b of
+            // E + 128, the bit layout the reduction reads back.
+            const float mp = fabsf(dIv) * m;
             int ex = 0;
-            frexpf(m, &ex);
-            int e = m > 0.f ? 15 - ex : 0;
-            e = e > 126 ? 126 : e;
-            if (ldexpf(m, e) >= 32767.5f) --e;
-            const float sc = ldexpf(1.f, e);
-            // the multiplier that turns the stored integers back into the part,
-            // dI 2^-(eq + ew) 2^-e, written over the record's dI
-            if (ok && half == 0) pb.srec_dI[ubase + p] = ldexpf(dIv * part_mul, -e);
-            // round R 2^e to integers (|R 2^e| < 32767.5): adding 1.5 2^23 leaves the
-            // integer, rounded to nearest even, in the low 16 bits of the sum
+            frexpf(mp, &ex);
+            int E = mp > 0.f ? 15 - ex + eq + ew : 0;
+            E = E > 126 ? 126 : (E < -126 ? -126 : E);
+            if (ldexpf(mp, E - eq - ew) >= 32766.f && E > -126) --E;
+            const float sc = ldexpf(dIv, E - eq - ew);     // dI 2^(E - eq - ew)
+            const uint32_t ebits = (uint32_t)(E + 128);
+            // round R dI 2^(E - eq - ew) to integers (magnitude < 32766): adding 1.5 2^23
+            // leaves the integer, rounded to nearest even, in the low 16 bits of the sum
             constexpr float kMagic = 12582912.f;
 #pragma unroll
             for (int dt = 0; dt < NDT; ++dt) {
@@ -283,6 +288,16 @@ __device__ __forceinline__ void scatter_dk_body(const Problem &pb) {
                 uint32_t wd[8];          // word 2 g + c: d = 32 dt + 8 g + 4 half + 2 c + {0, 1}
 #pragma unroll
                 for (int k2 = 0; k2 < 8; ++k2) {
+                    if (dt == 0 && k2 < 2) {
+                        // d = 4 half + 2 k2 + b: an even integer (2 round(x / 2)) with bit
+                        // 2 half + k2 + 4 b of E + 128 in its lowest bit
+                        const int l = 2 * half + k2;
+                        const uint32_t lo = __float_as_uint(fmaf(pa[2 * k2], 0.5f * sc, kMagic));
+                        const uint32_t hi = __float_as_uint(fmaf(pa[2 * k2 + 1], 0.5f * sc, kMagic));
+                        wd[k2] = ((lo << 1) & 0xfffeu) | ((ebits >> l) & 1u) |
+                                 (((hi << 1) & 0xfffeu) << 16) | (((ebits >> (l + 4)) & 1u) << 16);
+                        continue;
+                    }
                     const float lo = fmaf(pa[2 * k2], sc, kMagic);
                     const float hi = fmaf(pa[2 * k2 + 1], sc, kMagic);
                     wd[k2] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x05040100u);

@@ -55,7 +55,7 @@ struct Problem {
     const i32x4 *rowinfo;
     // key-sorted strategy (64-head kernel): per (unit, valid position) the key row, dI
     // and the S > 0 head words ([U, topk], [U, topk], [U, topk, HP/32]) and per unit the
-    // valid count; the parts kernel overwrites each dI with its row's multiplier
+    // valid count
     int32_t *srec_key;
     float *srec_dI;
     uint32_t *srec_mask;
@@ -67,10 +67,10 @@ struct Problem {
     int32_t *sort_tmp;       // [valid records, 2] (bin, record) pairs grouped by bucket
     int32_t *sort_list;      // [valid records] the records sorted by bin
     int32_t *bin_start;      // [T2 * N2 + 1] first list entry of each bin; [T2 * N2] = total
-    void *dk_parts;          // [U * topk, D] dK part of record o before its multiplier
-                             // srec_dI[o]: 16-bit integers when no bin holds more than
-                             // kPartsI16MaxRefs records (*sort_maxref), else fp32 (valid
-                             // records only)
+    void *dk_parts;          // [U * topk, D] dK part of record o: 16-bit integers n with
+                             // part = n 2^-E, E + 128 in the low bits of elements 0..7,
+                             // when no bin holds more than kPartsI16MaxRefs records
+                             // (*sort_maxref), else fp32 (valid records only)
     int32_t *sort_maxref;    // most records of one bin (zeroed per call; set by the sort)
     int32_t sort_shift, sort_nbuckets, sort_tile, sort_nblk;
     const int32_t *cu_q;     // [batch + 1] or null (BSND)
@@ -167,7 +167,7 @@ hipError_t launch_sorted_prepare(const Problem &pb, hipStream_t stream);
 hipError_t launch_sorted_reduce(const Problem &pb, bool det, hipStream_t stream);
 int grad_dense64_blocks_per_cu(int hp, int d, bool f16, int cap);
 // Up to 8 byte ranges (16-byte aligned starts, sizes multiples of 4) zeroed by one launch.
-// Parts are stored as 16-bit integers with a per-record multiplier when no key row
+// Parts are stored as 16-bit integers with a per-record exponent when no key row
 // takes more than this many parts; their rounding error (at most 2^-15 of the part's
 // largest element) then stays far inside the dk tolerance even when the parts of a key
 // are correlated (repeated slots of one row share one rounded row).  Hotter keys, such

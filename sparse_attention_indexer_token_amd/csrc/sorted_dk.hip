@@ -5,9 +5,9 @@
 // dK is the scatter-add of every valid slot's part dS^T q into the key row that
 // sparseIndices names.  Instead of adding the parts with atomics, the scatter dK kernel
 // writes part o (o = unit * topk + position of a valid slot record) as row o of a parts
-// buffer (16-bit integers, or fp32 when some bin holds more than kPartsI16MaxRefs
-// records, with a per-record fp32 multiplier), and the rows are summed per bin = key
-// row * N2 + key head through a list of the records sorted by bin:
+// buffer (16-bit integers with the row's power-of-two exponent in their lowest bits, or
+// fp32 when some bin holds more than kPartsI16MaxRefs records), and the rows are summed
+// per bin = key row * N2 + key head through a list of the records sorted by bin:
 //   bucket count    records cut into tiles; per tile a histogram over key buckets
 //                   (bin >> shift) in LDS, written as column `tile` of [bucket][tile];
 //   scan            exclusive prefix of that matrix in bucket-major order (so each
@@ -207,8 +207,9 @@ constexpr int kRedWaves = 4;
 constexpr int kRedUnroll = 16;
 
 // One wave per contiguous run of the sorted list; lane l holds d = 2l, 2l + 1 of the
-// rows it names (lanes past D/2 idle).  A row's part is its values (16-bit integers or
-// fp32) times the record's multiplier (stored over its dI by the parts kernel).
+// rows it names (lanes past D/2 idle).  A row is the part itself in fp32, or 16-bit
+// integers n with part = n 2^-E, E + 128 in the lowest bits of elements 0..7 (element
+// 2 l + b, l < 4, holds bit l + 4 b), whose values are then the even integers left.
 template <int D, bool DET, bool I16>
 __device__ __forceinline__ void sorted_reduce_body(const Problem &pb, int nbins) {
     const int lane = threadIdx.x & 63;
@@ -271,8 +272,8 @@ __device__ __forceinline__ void sorted_reduce_body(const Problem &pb, int nbins)
 
     const uint32_t *rows16 = (const uint32_t *)pb.dk_parts;
     const float2 *rows32 = (const float2 *)pb.dk_parts;
-    const float *mult = pb.srec_dI;
     const int32_t *list = pb.sort_list;
+    const uint32_t vmask = lane < 4 ? 0xfffefffeu : 0xffffffffu;    // exponent bits off
     // list entries (wave-uniform) of the next batch are loaded while this batch's rows
     // are in flight
     int on[kRedUnroll];
@@ -280,17 +281,15 @@ __device__ __forceinline__ void sorted_reduce_body(const Problem &pb, int nbins)
     for (int i = 0; i < kRedUnroll; ++i) on[i] = r0 + i < r1 ? list[r0 + i] : 0;
     for (int r = r0; r < r1; r += kRedUnroll) {
         float2 v[kRedUnroll];
-        float mu[kRedUnroll];
+        uint32_t xr[kRedUnroll];
 #pragma unroll
         for (int i = 0; i < kRedUnroll; ++i) {
             const bool ld = act && r + i < r1;
             if constexpr (I16) {
-                const uint32_t x = ld ? rows16[(size_t)on[i] * (D / 2) + lane] : 0u;
-                v[i] = make_float2((float)(int16_t)(x & 0xffffu), (float)(int16_t)(x >> 16));
+                xr[i] = ld ? rows16[(size_t)on[i] * (D / 2) + lane] : 0u;
             } else {
                 v[i] = ld ? rows32[(size_t)on[i] * (D / 2) + lane] : make_float2(0.f, 0.f);
             }
-            mu[i] = mult[on[i]];
         }
 #pragma unroll
         for (int i = 0; i < kRedUnroll; ++i) {
@@ -311,8 +310,19 @@ __device__ __forceinline__ void sorted_reduce_body(const Problem &pb, int nbins)
                     be = start[b + 1];
                 } while (be <= rr);
             }
-            const float x0 = v[i].x * mu[i];
-            const float x1 = v[i].y * mu[i];
+            float x0, x1;
+            if constexpr (I16) {
+                // E + 128 from the low bits of lanes 0..3 (wave-uniform), 2^-E built as a float
+                const uint64_t b0 = __ballot((xr[i] & 1u) != 0u), b1 = __ballot((xr[i] & 0x10000u) != 0u);
+                const uint32_t eb = (uint32_t)(b0 & 15u) | ((uint32_t)(b1 & 15u) << 4);
+                const float sc = __uint_as_float((255u - eb) << 23);
+                const uint32_t x = xr[i] & vmask;
+                x0 = (float)(int16_t)(x & 0xffffu) * sc;
+                x1 = (float)(int16_t)(x >> 16) * sc;
+            } else {
+                x0 = v[i].x;
+                x1 = v[i].y;
+            }
             if constexpr (DET) {
                 i0 += __float2ll_rn(x0 * det_mul);
                 i1 += __float2ll_rn(x1 * det_mul);
