@@ -132,23 +132,88 @@ __global__ __launch_bounds__(kSortThreads) void bucket_count_kernel(Problem pb) 
     for (int i = threadIdx.x; i < nbk; i += kSortThreads) pb.sort_hist[(size_t)i * nblk + blockIdx.x] = h[i];
 }
 
+// Records of one bucket-scatter chunk, staged in LDS sorted by bucket before they are
+// written, so that each bucket's run of the chunk leaves as contiguous stores (written
+// straight from the records, 64 lanes hit up to 64 buckets' lines per store and the
+// lines leave the L2 partly written, several times over).
+constexpr int kScatterChunk = 8192;
+constexpr int kScatterPer = kScatterChunk / kSortThreads;        // records per thread
+constexpr int kBucketsPerThread = kSortBucketsMax / kSortThreads;
+
 __global__ __launch_bounds__(kSortThreads) void bucket_scatter_kernel(Problem pb) {
-    __shared__ int c[kSortBucketsMax];
+    __shared__ int c[kSortBucketsMax];          // next global place of each bucket in this tile
+    __shared__ int lb[kSortBucketsMax];         // chunk counts, then their exclusive prefix
+    __shared__ u32x2 stage[kScatterChunk];
+    __shared__ int s_tmp[kSortThreads / 64];
     const int nbk = pb.sort_nbuckets, tile = pb.sort_tile, nblk = pb.sort_nblk, sh = pb.sort_shift;
-    for (int i = threadIdx.x; i < nbk; i += kSortThreads) c[i] = pb.sort_hist[(size_t)i * nblk + blockIdx.x];
-    __syncthreads();
+    const int tid = threadIdx.x;
+    for (int i = tid; i < nbk; i += kSortThreads) c[i] = pb.sort_hist[(size_t)i * nblk + blockIdx.x];
     const int nslot = (int)(pb.t1 * pb.n2 * pb.topk);
     const int o0 = blockIdx.x * tile;
     const int o1 = o0 + tile < nslot ? o0 + tile : nslot;
     u32x2 *tmp = (u32x2 *)pb.sort_tmp;
-    for (int o = o0 + threadIdx.x; o < o1; o += kSortThreads * kSortIlp) {
-        int bin[kSortIlp], at[kSortIlp];
-        record_bins(pb, o, o1, bin);
+    for (int a = o0; a < o1; a += kScatterChunk) {
+        const int a1 = a + kScatterChunk < o1 ? a + kScatterChunk : o1;
+        for (int i = tid; i < nbk; i += kSortThreads) lb[i] = 0;
+        lds_barrier();
+        // bins and ranks within the chunk's buckets
+        // (record a + tid + kSortThreads i for i < kScatterPer; loads at clamped indices)
+        int bin[kScatterPer], rk[kScatterPer];
+        {
+            int key[kScatterPer], cn[kScatterPer], u[kScatterPer];
 #pragma unroll
-        for (int i = 0; i < kSortIlp; ++i) at[i] = bin[i] >= 0 ? atomicAdd(&c[bin[i] >> sh], 1) : 0;
+            for (int i = 0; i < kScatterPer; ++i) {
+                const int oi = a + tid + kSortThreads * i;
+                const int oc = oi < a1 ? oi : a;
+                u[i] = (int)((unsigned)oc / (unsigned)pb.topk);
+                key[i] = pb.srec_key[oc];
+                cn[i] = pb.srec_cnt[u[i]];
+            }
 #pragma unroll
-        for (int i = 0; i < kSortIlp; ++i)
-            if (bin[i] >= 0) tmp[at[i]] = u32x2{(uint32_t)bin[i], (uint32_t)(o + kSortThreads * i)};
+            for (int i = 0; i < kScatterPer; ++i) {
+                const int oi = a + tid + kSortThreads * i;
+                bin[i] = oi < a1 && oi - u[i] * pb.topk < cn[i] ? key[i] * pb.n2 + u[i] % pb.n2 : -1;
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < kScatterPer; ++i) rk[i] = bin[i] >= 0 ? atomicAdd(&lb[bin[i] >> sh], 1) : 0;
+        lds_barrier();
+        // exclusive prefix of the chunk's bucket counts (thread t: buckets t * kBPT ..)
+        int cnt[kBucketsPerThread], sum = 0;
+#pragma unroll
+        for (int j = 0; j < kBucketsPerThread; ++j) {
+            const int bk = tid * kBucketsPerThread + j;
+            cnt[j] = bk < nbk ? lb[bk] : 0;
+            sum += cnt[j];
+        }
+        int total = 0;
+        int run = block_excl_scan<kSortThreads / 64>(sum, s_tmp, &total);
+#pragma unroll
+        for (int j = 0; j < kBucketsPerThread; ++j) {
+            const int bk = tid * kBucketsPerThread + j;
+            if (bk < nbk) lb[bk] = run;
+            run += cnt[j];
+        }
+        lds_barrier();
+        // records into the stage in bucket order
+#pragma unroll
+        for (int i = 0; i < kScatterPer; ++i) {
+            const int o = a + tid + kSortThreads * i;
+            if (bin[i] >= 0) stage[lb[bin[i] >> sh] + rk[i]] = u32x2{(uint32_t)bin[i], (uint32_t)o};
+        }
+        lds_barrier();
+        // out in stage order: a bucket's run goes to consecutive places
+        for (int j = tid; j < total; j += kSortThreads) {
+            const u32x2 e = stage[j];
+            const int bk = (int)e.x >> sh;
+            tmp[c[bk] + (j - lb[bk])] = e;
+        }
+        lds_barrier();
+#pragma unroll
+        for (int j = 0; j < kBucketsPerThread; ++j) {
+            const int bk = tid * kBucketsPerThread + j;
+            if (bk < nbk) c[bk] += cnt[j];
+        }
     }
 }
 
