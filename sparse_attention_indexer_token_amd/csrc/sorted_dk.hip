@@ -456,7 +456,10 @@ hipError_t launch_sorted_reduce(const Problem &pb, bool det, hipStream_t stream)
     if (cus <= 0) return hipErrorInvalidDevice;
     const int64_t nbins = pb.t2 * pb.n2;
     if (pb.t1 * pb.n2 * pb.topk <= 0 || nbins <= 0) return hipSuccess;
-    const dim3 grid((unsigned)cus * 8), block(64 * kRedWaves);
+    // many short runs (a 4-wave block per 1/64 of a compute unit's share): the row gathers
+    // of more waves are in flight at once (16 blocks per CU 1078 us, 32: 1010, 64: 996 on
+    // long_context's 16.8 M records)
+    const dim3 grid((unsigned)cus * 64), block(64 * kRedWaves);
 #define SLIKL_SR_CASE(DV)                                                                                 \
     if (pb.d == DV) {                                                                                     \
         if (det) hipLaunchKernelGGL((sorted_reduce_kernel<DV, true>), grid, block, 0, stream, pb, (int)nbins); \
