@@ -128,13 +128,12 @@ def phase_work(strategy, wl, x, det):
         # the method's dK contraction dS^T q: one G x D contraction per valid slot
         work["dk"] = ("dense_dk_kernel", "mfma", 2.0 * G * D * V, "FLOP")
     if strategy == "sorted":
-        # each valid slot's part written once (16-bit or fp32 elements, and its
-        # multiplier), with its record (key, dI, head words) read; q read once
+        # each valid slot's part written once (16-bit elements carrying their exponent,
+        # or fp32), with its record (key, dI, head words) read; q read once
         eb = 2.0 if max_key_refs(x) <= PARTS_I16_MAX_REFS else 4.0
-        work["dk"] = ("scatter_dk_kernel", "hbm", V * (eb * D + 12 + 4 * nh) + x.t1 * wl.n1 * D * 2.0, "B")
-        # the parts, their multipliers and the sorted list read once, the fp32
-        # accumulator written once
-        work["dk_reduce"] = ("sorted_reduce_kernel", "hbm", V * (eb * D + 8) + x.t2 * wl.n2 * D * 4.0, "B")
+        work["dk"] = ("scatter_dk_kernel", "hbm", V * (eb * D + 8 + 4 * nh) + x.t1 * wl.n1 * D * 2.0, "B")
+        # the parts and the sorted list read once, the fp32 accumulator written once
+        work["dk_reduce"] = ("sorted_reduce_kernel", "hbm", V * (eb * D + 4) + x.t2 * wl.n2 * D * 4.0, "B")
         work["dk_final"] = ("finalize_kernel", "hbm", x.t2 * wl.n2 * D * (acc_elem + 2.0), "B")
     return work
 
