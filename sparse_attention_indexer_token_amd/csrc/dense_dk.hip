@@ -76,6 +76,11 @@ struct DenseCfg {
     static constexpr int NS_FIT = (160 * 1024 / WGPC - 3 * 1024) / STAGE;
     static constexpr int NS = NS_FIT > 6 ? 6 : NS_FIT;
     static_assert(NS >= 3, "at least three stages");
+    // the row's masked-w table when there are at least two 16-head k-steps (with one,
+    // the selects cost less than the table and its barrier)
+    static constexpr bool LUT = NKH >= 2;
+    static constexpr int LUTB = LUT ? HK * 16 : 16;
+    static_assert(NS * STAGE + 2 * 1024 + LUTB + 64 <= 160 * 1024 / WGPC, "LDS per workgroup");
     static_assert(KB * 4 <= 1024, "one dI copy");
     static_assert(wrec_bytes(HP) <= 1024, "one w record copy");
 };
@@ -136,6 +141,9 @@ __device__ __forceinline__ void dense_dk_body(const Problem &pb) {
     __shared__ __attribute__((aligned(1024))) char s_spare[1024];   // destination of dummy copies
     __shared__ int s_rows[kDkBlock];
     __shared__ int s_cnt[kDkWaves];
+    // the row's head-masked w: entry (pair p, pattern m) = fp16 hi and lo parts of heads
+    // 2p, 2p + 1 with head 2p + i kept when bit i of m is set (8 bytes each)
+    __shared__ __attribute__((aligned(16))) char s_lut[C::LUTB];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -274,6 +282,16 @@ __device__ __forceinline__ void dense_dk_body(const Problem &pb) {
             }
         }
         const char *stg = s_stage + st_use * C::STAGE;
+        if constexpr (C::LUT) {
+            if (tid < 2 * HK) {
+                const int gp = tid >> 2, m = tid & 3;
+                const uint32_t hi = ((const uint32_t *)(stg + C::OFF_MISC))[gp];
+                const uint32_t lo = ((const uint32_t *)(stg + C::OFF_MISC + HP * 2))[gp];
+                const uint32_t msk = (m & 1 ? 0xffffu : 0u) | (m & 2 ? 0xffff0000u : 0u);
+                *(u32x2 *)(s_lut + tid * 8) = u32x2{hi & msk, lo & msk};
+            }
+            lds_barrier();          // the table is complete
+        }
         const int *rec = (const int *)(stg + C::OFF_MISC + HP * 4);
         const float rowscale = ldexpf(1.f, -(rec[0] + rec[1]));
 #pragma unroll
@@ -291,13 +309,25 @@ __device__ __forceinline__ void dense_dk_body(const Problem &pb) {
             for (int kh = 0; kh < NKH; ++kh) {
                 // B operand (head-masked w): column = this lane's key, k element e <->
                 // head 16 kh + 8 (e/4) + 4 half + e%4, whose head bit is 16 half + 8 (kh%2) + e
+                u32x4 bh, bl;
+                if constexpr (C::LUT) {
+                    // elements 2 pr, 2 pr + 1: heads 2p, 2p + 1 of pair p = 8 kh + 4 (pr/2) +
+                    // 2 half + pr%2, read from the table at the pattern of their two bits
+                    const uint32_t word = mw[kh >> 1];
+#pragma unroll
+                    for (int pr = 0; pr < 4; ++pr) {
+                        const uint32_t m = __builtin_amdgcn_ubfe(word, 16 * half + 8 * (kh & 1) + 2 * pr, 2);
+                        const u32x2 e = *(const u32x2 *)(s_lut + 64 * half + 32 * (8 * kh + 4 * (pr >> 1) + (pr & 1)) + 8 * m);
+                        bh[pr] = e.x;
+                        bl[pr] = e.y;
+                    }
+                } else {
                 const uint32_t byte = (mw[kh >> 1] >> (16 * half + 8 * (kh & 1))) & 0xffu;
                 const u32x2 h0 = *(const u32x2 *)(whi + 16 * kh + 4 * half);
                 const u32x2 h1 = *(const u32x2 *)(whi + 16 * kh + 8 + 4 * half);
                 const u32x2 o0 = *(const u32x2 *)(wlo + 16 * kh + 4 * half);
                 const u32x2 o1 = *(const u32x2 *)(wlo + 16 * kh + 8 + 4 * half);
                 const uint32_t wh[4] = {h0.x, h0.y, h1.x, h1.y}, wl[4] = {o0.x, o0.y, o1.x, o1.y};
-                u32x4 bh, bl;
 #pragma unroll
                 for (int pr = 0; pr < 4; ++pr) {
                     const uint32_t lo = (uint32_t)__builtin_amdgcn_sbfe((int)byte, 2 * pr, 1);
@@ -305,6 +335,7 @@ __device__ __forceinline__ void dense_dk_body(const Problem &pb) {
                     const uint32_t msk = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
                     bh[pr] = wh[pr] & msk;
                     bl[pr] = wl[pr] & msk;
+                }
                 }
 #pragma unroll
                 for (int db = 0; db < NDT; ++db) {
