@@ -278,10 +278,12 @@ constexpr int kRedUnroll = 16;
 template <int D, bool DET, bool I16>
 __device__ __forceinline__ void sorted_reduce_body(const Problem &pb, int nbins) {
     const int lane = threadIdx.x & 63;
-    const int gw = blockIdx.x * kRedWaves + (threadIdx.x >> 6);
+    // wave-uniform values are kept in scalar registers (readfirstlane), so that the
+    // per-record control flow is scalar
+    const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * kRedWaves + (threadIdx.x >> 6));
     const int W = gridDim.x * kRedWaves;
     const int32_t *start = pb.bin_start;
-    const int N = start[nbins];
+    const int N = __builtin_amdgcn_readfirstlane(start[nbins]);
     const int per = (N + W - 1) / W;
     const int r0 = gw * per;
     const int r1 = r0 + per < N ? r0 + per : N;
@@ -307,7 +309,7 @@ __device__ __forceinline__ void sorted_reduce_body(const Problem &pb, int nbins)
         lo = nlo;
     }
     int b = lo;
-    int bs = start[b], be = start[b + 1];
+    int bs = __builtin_amdgcn_readfirstlane(start[b]), be = __builtin_amdgcn_readfirstlane(start[b + 1]);
 
     float a0 = 0.f, a1 = 0.f;
     long long i0 = 0, i1 = 0;
@@ -339,32 +341,33 @@ __device__ __forceinline__ void sorted_reduce_body(const Problem &pb, int nbins)
     const float2 *rows32 = (const float2 *)pb.dk_parts;
     const int32_t *list = pb.sort_list;
     const uint32_t vmask = lane < 4 ? 0xfffefffeu : 0xffffffffu;    // exponent bits off
-    // list entries (wave-uniform) of the next batch are loaded while this batch's rows
-    // are in flight
-    int on[kRedUnroll];
-#pragma unroll
-    for (int i = 0; i < kRedUnroll; ++i) on[i] = r0 + i < r1 ? list[r0 + i] : 0;
+    const int col = act ? lane : 0;            // lanes past D/2 read column 0, unused
+    // the list entries of a batch: lane i < kRedUnroll holds entry rb + i (clamped into
+    // the run), one vector load; each record's row address is then formed from its
+    // entry in scalar registers (readlane), so no per-record vector address arithmetic
+    auto load_list = [&](int rb) {
+        const int idx = rb + (lane & (kRedUnroll - 1));
+        return list[idx < r1 ? idx : r1 - 1];
+    };
+    int lst = load_list(r0);
     for (int r = r0; r < r1; r += kRedUnroll) {
+        const int nrec = r1 - r < kRedUnroll ? r1 - r : kRedUnroll;     // uniform
         float2 v[kRedUnroll];
         uint32_t xr[kRedUnroll];
 #pragma unroll
         for (int i = 0; i < kRedUnroll; ++i) {
-            const bool ld = act && r + i < r1;
+            const int o = __builtin_amdgcn_readlane(lst, i);
             if constexpr (I16) {
-                xr[i] = ld ? rows16[(size_t)on[i] * (D / 2) + lane] : 0u;
+                xr[i] = (rows16 + (size_t)o * (D / 2))[col];
             } else {
-                v[i] = ld ? rows32[(size_t)on[i] * (D / 2) + lane] : make_float2(0.f, 0.f);
+                v[i] = (rows32 + (size_t)o * (D / 2))[col];
             }
         }
+        lst = load_list(r + kRedUnroll);        // next batch, while these rows are in flight
 #pragma unroll
         for (int i = 0; i < kRedUnroll; ++i) {
-            const int rn = r + kRedUnroll + i;
-            on[i] = rn < r1 ? list[rn] : 0;
-        }
-#pragma unroll
-        for (int i = 0; i < kRedUnroll; ++i) {
+            if (i >= nrec) continue;           // uniform; the loop stays unrolled
             const int rr = r + i;
-            if (rr >= r1) break;
             if (rr >= be) {                    // the bin ends: write it, step to the next
                 flush();                       // non-empty one
                 a0 = a1 = 0.f;
@@ -372,7 +375,7 @@ __device__ __forceinline__ void sorted_reduce_body(const Problem &pb, int nbins)
                 do {
                     ++b;
                     bs = be;
-                    be = start[b + 1];
+                    be = __builtin_amdgcn_readfirstlane(start[b + 1]);
                 } while (be <= rr);
             }
             float x0, x1;
