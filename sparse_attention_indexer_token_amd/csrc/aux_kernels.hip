@@ -398,6 +398,16 @@ __device__ __forceinline__ int check_cu(const int32_t *cu, int batch, int64_t to
 
 constexpr int kSplitIlp = 16;
 
+// floor(a / b) for 0 <= a < 2^53, 0 < b < 2^53 and a quotient below 2^52: the double
+// quotient (off by at most one) corrected with exact products (a 64-bit integer
+// division is a long software sequence on this target)
+__device__ __forceinline__ int64_t floordiv_nn(int64_t a, int64_t b) {
+    int64_t q = (int64_t)((double)a / (double)b);
+    if (q * b > a) --q;
+    else if ((q + 1) * b <= a) ++q;
+    return q;
+}
+
 __global__ __launch_bounds__(1024) void meta_split_kernel(Problem pb, int parts, int mode, int overhead,
                                                           int64_t *prefix, const int32_t *cflags,
                                                           int ncflags, int32_t *md) {
@@ -497,14 +507,19 @@ __global__ __launch_bounds__(1024) void meta_split_kernel(Problem pb, int parts,
             for (int i = tid; i <= parts; i += nt) bnd[i] = 0;
         } else {
             if (tid == 0) bnd[0] = 0;
+            // u takes the i with E(u-1) parts < i W <= E(u) parts, i.e. E(u) >= thr(i) =
+            // ceil(i W / parts) > E(u-1): walk the units with the next boundary and its
+            // threshold (one division per boundary, not two 64-bit divisions per unit)
             int64_t prev = incl - loc;                         // E(a)
+            int64_t i = floordiv_nn(prev * parts, W) + 1;      // first boundary past E(a)
+            int64_t thr = floordiv_nn(i * W + parts - 1, parts);
             for (int64_t u = a + 1; u <= e; ++u) {
                 const int64_t cur = prev + cost(u - 1);        // E(u)
-                // i with prev parts < i W <= cur parts: i in [floor(prev parts / W) + 1, floor(cur parts / W)]
-                int64_t i0 = prev * parts / W + 1;
-                int64_t i1 = cur * parts / W;
-                if (i1 > parts) i1 = parts;
-                for (int64_t i = i0; i <= i1; ++i) bnd[i] = (int32_t)u;
+                while (i <= parts && cur >= thr) {
+                    bnd[i] = (int32_t)u;
+                    ++i;
+                    thr = floordiv_nn(i * W + parts - 1, parts);
+                }
                 prev = cur;
             }
         }
