@@ -105,7 +105,7 @@ hipError_t launch_zero_ranges(const ZeroRanges &zr, hipStream_t stream) {
     for (int r = 0; r < zr.n; ++r) most = zr.bytes[r] / 16 > most ? zr.bytes[r] / 16 : most;
     if (zr.n == 0) return hipSuccess;
     size_t blocks = (most + 255) / 256;
-    if (blocks > 2048) blocks = 2048;
+    if (blocks > 16384) blocks = 16384;
     if (blocks == 0) blocks = 1;
     hipLaunchKernelGGL(zero_ranges_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, zr);
     return hipGetLastError();
@@ -116,24 +116,41 @@ hipError_t launch_zero_ranges(const ZeroRanges &zr, hipStream_t stream) {
 // point with scale 2^F, read back as acc * 2^-F.
 // ---------------------------------------------------------------------------
 template <bool F16, bool DET>
+__device__ __forceinline__ float acc_value(const void *acc, size_t i, float inv) {
+    if constexpr (DET) return (float)((double)((const long long *)acc)[i] * (double)inv);
+    else return ((const float *)acc)[i];
+}
+
+// Eight elements per thread and step with one 16-byte store when dk is 16-byte
+// aligned (n is a multiple of 32: D is); else one element at a time.
+template <bool F16, bool DET>
 __global__ void finalize_kernel(const void *acc, uint16_t *dk, size_t n, const float *scale) {
     size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     size_t stride = (size_t)gridDim.x * blockDim.x;
     float inv = 1.f;
     if constexpr (DET) inv = scale[1];
-    for (; i < n; i += stride) {
-        float v;
-        if constexpr (DET) v = (float)((double)((const long long *)acc)[i] * (double)inv);
-        else v = ((const float *)acc)[i];
-        dk[i] = to16<F16>(v);
+    if ((((uintptr_t)dk) & 15) == 0) {
+        for (; i < n / 8; i += stride) {
+            float v[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) v[c] = acc_value<F16, DET>(acc, 8 * i + c, inv);
+            u32x4 o;
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                o[c] = (uint32_t)to16<F16>(v[2 * c]) | ((uint32_t)to16<F16>(v[2 * c + 1]) << 16);
+            ((u32x4 *)dk)[i] = o;
+        }
+        return;
     }
+    for (; i < n; i += stride) dk[i] = to16<F16>(acc_value<F16, DET>(acc, i, inv));
 }
 
 hipError_t launch_finalize_dk(const Problem &pb, bool f16, bool det, hipStream_t stream) {
     size_t n = (size_t)pb.t2 * pb.n2 * pb.d;
     if (n == 0) return hipSuccess;
-    size_t blocks = (n + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
+    size_t blocks = (n / 8 + 255) / 256;
+    if (blocks > 16384) blocks = 16384;
+    if (blocks == 0) blocks = 1;
     dim3 gr((unsigned)blocks), bl(256);
     if (f16) {
         if (det) hipLaunchKernelGGL((finalize_kernel<true, true>), gr, bl, 0, stream, pb.dk_acc, pb.dk, n, pb.det_scale);

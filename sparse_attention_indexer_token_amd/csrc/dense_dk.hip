@@ -760,7 +760,7 @@ hipError_t launch_dense_dk(const Problem &pb, int hp, bool f16, hipStream_t stre
 hipError_t launch_dense_dk_reduce(const Problem &pb, bool f16, hipStream_t stream) {
     const size_t n = (size_t)pb.t2 * pb.n2 * pb.d;
     size_t blocks = (n + 255) / 256;
-    if (blocks > 4096) blocks = 4096;
+    if (blocks > 65536) blocks = 65536;
     if (blocks == 0) return hipSuccess;
     if (f16)
         hipLaunchKernelGGL(dense_dk_reduce_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, pb);
