@@ -726,8 +726,8 @@ hipError_t launch_grad_dense(const Problem &pb, int hp, bool f16, int cap, int g
     return hipErrorInvalidValue;
 }
 
-int grad_dense_blocks_per_cu(int hp, int d, bool f16, int cap) {
-    if (hp <= 64) return grad_dense64_blocks_per_cu(hp, d, f16, cap);
+int grad_dense_blocks_per_cu(int hp, int d, bool f16, int cap, int group) {
+    if (hp <= 64) return grad_dense64_blocks_per_cu(hp, d, f16, cap, group);
     SLIKL_GD_CASES(blocks_gd);
     return 1;
 }

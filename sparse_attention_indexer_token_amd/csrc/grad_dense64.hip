@@ -59,6 +59,15 @@ typedef __attribute__((address_space(1))) void glb_void_gd;
 #endif
 constexpr int kWaves64 = SLIKL_GD64_WAVES;
 
+// Workgroups per compute unit: one of 8 waves, else two of 4; three for lists of at
+// most 512 slots and groups of up to 32 heads, four when pass 1 multiplies 16 heads
+// (the register budget of 128 then spills 14 registers, yet the fixed per-unit work
+// of more units overlaps: contention workload 983 -> 928 us against three).
+template <int HP, int CAP, int HK>
+constexpr int gd64_wgpc() {
+    return kWaves64 == 8 ? 1 : (CAP == 0 && HP == 32 ? (HK <= 16 ? 4 : 3) : 2);
+}
+
 // Capacity forms: CAP 0 serves top-k lists of at most 512 slots (the per-position
 // arrays are a quarter of the size, so that three workgroups share a compute unit for
 // groups of up to 32 heads), CAP 1 lists of at most 2048 slots.
@@ -79,7 +88,6 @@ struct DenseFwdCfg {
     // than the record atomics it saves (contention workload 1.01 -> 1.05 ms).
     static constexpr int KBITS = CAP == 0 ? 0 : 65536;
     static constexpr int SPT = TOPK_MAX / NT;   // slots of one row per thread (topk <= TOPK_MAX)
-    static constexpr int WGPC = NW == 8 ? 1 : (CAP == 0 && HP == 32 ? 3 : 2);   // workgroups per CU
     // ring stages: with two or three workgroups per compute unit a second stage is
     // enough (a third measured no faster at D = 128)
     static constexpr int NST = D < 128 ? 4 : NW == 8 ? 3 : 2;
@@ -197,7 +205,7 @@ struct UnitInputs {
 // groups of up to 16 heads padded to HP = 32: the tile of heads 16..31 holds only zero
 // scores, whose ReLU and S > 0 bits are zero).
 template <int HP, int D, bool F16, bool SREC, int HK, int CAP>
-__global__ __launch_bounds__(64 * kWaves64, (DenseFwdCfg<HP, D, kWaves64, CAP>::WGPC)) void grad_dense64_kernel(
+__global__ __launch_bounds__(64 * kWaves64, (gd64_wgpc<HP, CAP, HK>())) void grad_dense64_kernel(
     Problem pb) {
     using C = DenseFwdCfg<HP, D, kWaves64, CAP>;
     constexpr int kBlock8 = C::NT;
@@ -906,18 +914,27 @@ static hipError_t launch_gd64(const Problem &pb, int cap, int grid, bool srec, h
     return launch_gd64_cap<HP, D, F16, 1>(pb, grid, srec, stream);
 }
 
-template <int HP, int D, bool F16, int CAP>
-static int blocks_gd64_cap() {
+template <int HP, int D, bool F16, int HK, int CAP>
+static int blocks_gd64_hk() {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grad_dense64_kernel<HP, D, F16, false, HP, CAP>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, grad_dense64_kernel<HP, D, F16, false, HK, CAP>,
                                                      64 * kWaves64, 0) != hipSuccess)
         return 0;
     return n;
 }
 
+// (the variant the call runs: groups of up to 16 heads padded to 32 multiply 16)
+template <int HP, int D, bool F16, int CAP>
+static int blocks_gd64_cap(int group) {
+    if constexpr (HP == 32) {
+        if (group <= 16) return blocks_gd64_hk<HP, D, F16, 16, CAP>();
+    }
+    return blocks_gd64_hk<HP, D, F16, HP, CAP>();
+}
+
 template <int HP, int D, bool F16>
-static int blocks_gd64(int cap) {
-    return cap == 0 ? blocks_gd64_cap<HP, D, F16, 0>() : blocks_gd64_cap<HP, D, F16, 1>();
+static int blocks_gd64(int cap, int group) {
+    return cap == 0 ? blocks_gd64_cap<HP, D, F16, 0>(group) : blocks_gd64_cap<HP, D, F16, 1>(group);
 }
 
 }  // namespace dense64
@@ -938,8 +955,8 @@ hipError_t launch_grad_dense64(const Problem &pb, int hp, bool f16, int cap, int
     return hipErrorInvalidValue;
 }
 
-int grad_dense64_blocks_per_cu(int hp, int d, bool f16, int cap) {
-    SLIKL_GD64_CASES(dense64::blocks_gd64, cap);
+int grad_dense64_blocks_per_cu(int hp, int d, bool f16, int cap, int group) {
+    SLIKL_GD64_CASES(dense64::blocks_gd64, cap, group);
     return 0;
 }
 

@@ -276,7 +276,8 @@ slikl_status resolve_parts(const slikl_desc *d, int32_t *parts) {
     const int hp = head_tile(d->n1 / d->n2);
     const bool f16 = d->dtype == SLIKL_DTYPE_F16;
     int per_cu = mode == 2 || sorted_dk(d)
-                     ? slikl::grad_dense_blocks_per_cu(hp, (int)d->d, f16, slikl::dense64_cap(d->topk))
+                     ? slikl::grad_dense_blocks_per_cu(hp, (int)d->d, f16, slikl::dense64_cap(d->topk),
+                                                       (int)(d->n1 / d->n2))
                      : slikl::grad_fused_blocks_per_cu(hp, (int)d->d, f16, mode);
     int64_t p = (int64_t)cus * per_cu;
     if (p > SLIKL_MAX_PARTS) p = SLIKL_MAX_PARTS;

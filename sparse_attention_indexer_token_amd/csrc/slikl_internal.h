@@ -143,7 +143,7 @@ int grad_fused_blocks_per_cu(int hp, int d, bool f16, int mode);
 // the per-slot records of the key-sorted strategy (the 64-head kernel up to 64 heads, the 128-head one
 // above)
 hipError_t launch_grad_dense(const Problem &pb, int hp, bool f16, int cap, int grid, bool srec, hipStream_t stream);
-int grad_dense_blocks_per_cu(int hp, int d, bool f16, int cap);
+int grad_dense_blocks_per_cu(int hp, int d, bool f16, int cap, int group);
 // capacity form of the 64-head kernel: 0 for top-k lists of at most 512 slots, else 1
 inline int dense64_cap(int64_t topk) { return topk <= 512 ? 0 : 1; }
 // 64-head variant for head groups of up to 64 (called by the two above)
@@ -165,7 +165,7 @@ struct SortGeometry {
 SortGeometry sorted_geometry(int64_t nslot, int64_t nbins);
 hipError_t launch_sorted_prepare(const Problem &pb, hipStream_t stream);
 hipError_t launch_sorted_reduce(const Problem &pb, bool det, hipStream_t stream);
-int grad_dense64_blocks_per_cu(int hp, int d, bool f16, int cap);
+int grad_dense64_blocks_per_cu(int hp, int d, bool f16, int cap, int group);
 // Up to 8 byte ranges (16-byte aligned starts, sizes multiples of 4) zeroed by one launch.
 // Parts are stored as 16-bit integers with a per-record exponent when no key row
 // takes more than this many parts; their rounding error (at most 2^-15 of the part's
