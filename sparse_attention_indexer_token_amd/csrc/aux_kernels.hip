@@ -66,36 +66,48 @@ hipError_t launch_rowinfo(const Problem &pb, i32x4 *info, hipStream_t stream) {
 // with S1_b rows and S2_b keys sees keys j <= t + S2_b - S1_b.  Key positions at or
 // past L (the dense axis, the longest key sequence given) are not listed.
 // ---------------------------------------------------------------------------
-__global__ void dense_index_kernel(Problem pb, int32_t *idx, int mask_mode, int L) {
-    const int64_t n = pb.t1 * pb.n2 * (int64_t)L;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += stride) {
-        const int j = (int)(e % L);
-        const int64_t r = e / L / pb.n2;
-        int t, s1b, s2b;
-        if (pb.layout_q == 0) {
-            const int b = (int)(r / pb.s1);
-            t = (int)(r - (int64_t)b * pb.s1);
-            s1b = (int)pb.s1;
-            s2b = pb.layout_k == 0 ? (int)pb.s2 : pb.cu_k[b + 1] - pb.cu_k[b];
-        } else {
-            const int b = batch_of_row(pb.cu_q, pb.batch, r);
-            t = (int)(r - pb.cu_q[b]);
-            s1b = pb.cu_q[b + 1] - pb.cu_q[b];
-            s2b = pb.layout_k == 0 ? (int)pb.s2 : pb.cu_k[b + 1] - pb.cu_k[b];
-        }
-        int vis = s2b;
-        if (mask_mode == 3) vis = t + s2b - s1b + 1;
-        vis = vis < 0 ? 0 : (vis > s2b ? s2b : vis);
-        idx[e] = j < vis ? j : -1;
+// A workgroup per (unit, span of 1024 positions): the unit's batch and visible length
+// are found once per workgroup (no 64-bit division or batch search per element), and
+// each thread writes four consecutive positions, as one 16-byte store when aligned.
+constexpr int kIdxSpan = 1024;
+
+__global__ __launch_bounds__(256) void dense_index_kernel(Problem pb, int32_t *idx, int mask_mode, int L) {
+    const int nspan = (L + kIdxSpan - 1) / kIdxSpan;
+    const int64_t blk = blockIdx.x;
+    const int64_t u = blk / nspan;                          // unit: row r = u / N2
+    const int j0 = (int)(blk - u * nspan) * kIdxSpan + 4 * (int)threadIdx.x;
+    const int64_t r = u / pb.n2;
+    int t, s1b, s2b;
+    if (pb.layout_q == 0) {
+        const int b = (int)(r / pb.s1);
+        t = (int)(r - (int64_t)b * pb.s1);
+        s1b = (int)pb.s1;
+        s2b = pb.layout_k == 0 ? (int)pb.s2 : pb.cu_k[b + 1] - pb.cu_k[b];
+    } else {
+        const int b = batch_of_row(pb.cu_q, pb.batch, r);
+        t = (int)(r - pb.cu_q[b]);
+        s1b = pb.cu_q[b + 1] - pb.cu_q[b];
+        s2b = pb.layout_k == 0 ? (int)pb.s2 : pb.cu_k[b + 1] - pb.cu_k[b];
+    }
+    int vis = s2b;
+    if (mask_mode == 3) vis = t + s2b - s1b + 1;
+    vis = vis < 0 ? 0 : (vis > s2b ? s2b : vis);
+    int32_t *row = idx + u * (int64_t)L;
+    if (j0 + 4 <= L && (((uintptr_t)(row + j0)) & 15) == 0) {
+        *(int4 *)(row + j0) = int4{j0 < vis ? j0 : -1, j0 + 1 < vis ? j0 + 1 : -1, j0 + 2 < vis ? j0 + 2 : -1,
+                                   j0 + 3 < vis ? j0 + 3 : -1};
+    } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            if (j0 + c < L) row[j0 + c] = j0 + c < vis ? j0 + c : -1;
     }
 }
 
 hipError_t launch_dense_index(const Problem &pb, int32_t *idx, int mask_mode, int L, hipStream_t stream) {
-    const int64_t n = pb.t1 * pb.n2 * (int64_t)L;
-    if (n <= 0) return hipSuccess;
-    int64_t blocks = (n + 255) / 256;
-    if (blocks > 8192) blocks = 8192;
+    const int64_t units = pb.t1 * pb.n2;
+    if (units <= 0 || L <= 0) return hipSuccess;
+    const int64_t blocks = units * ((L + kIdxSpan - 1) / kIdxSpan);
+    if (blocks > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(dense_index_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pb, idx, mask_mode, L);
     return hipGetLastError();
 }
