@@ -663,45 +663,72 @@ __global__ __launch_bounds__(1024) void dense_dk_tasks_kernel(Problem pb) {
     }
 }
 
-// dk = round16(sum of the key block's task partials, in task order)
+// dk = round16(sum of the key block's task partials, in task order).  A thread takes
+// four consecutive d of one (key row, key head): 16-byte partial loads, one key-row
+// decomposition per four elements (shifts for d, 32-bit divisions for the rest).
 template <bool F16>
 __global__ void dense_dk_reduce_kernel(Problem pb) {
-    const int D = pb.d, KB = pb.dk_kb;
-    const size_t n = (size_t)pb.t2 * pb.n2 * D;
-    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int D = pb.d, KB = pb.dk_kb, n2 = (int)pb.n2;
+    const int ld4 = D == 128 ? 5 : (D == 64 ? 4 : 3);            // log2(D / 4)
+    const size_t n4 = (size_t)pb.t2 * n2 * (D / 4);
+    const bool st8 = (((uintptr_t)pb.dk) & 7) == 0;
+    size_t i4 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
     const size_t stride = (size_t)gridDim.x * blockDim.x;
-    for (; i < n; i += stride) {
-        const size_t kr = i / ((size_t)pb.n2 * D);        // key row (key base of b + j)
-        const int g = (int)((i / D) % pb.n2), d = (int)(i % D);
+    for (; i4 < n4; i4 += stride) {
+        const int d = (int)(i4 & ((D >> 2) - 1)) * 4;
+        const size_t q = i4 >> ld4;                           // key row * N2 + key head
+        const uint32_t kr = n2 == 1 ? (uint32_t)q : (uint32_t)(q / (size_t)n2);   // key rows < 2^24
+        const int g = (int)(q - (size_t)kr * n2);
+        uint16_t *out = pb.dk + q * D + d;
         int b, j;
         if (pb.layout_k == 0) {
-            b = (int)(kr / pb.s2);
-            j = (int)(kr % pb.s2);
+            b = (int)(kr / (uint32_t)pb.s2);
+            j = (int)(kr - (uint32_t)b * (uint32_t)pb.s2);
         } else {
             b = batch_of_row(pb.cu_k, pb.batch, (int64_t)kr);
-            j = (int)(kr - pb.cu_k[b]);
+            j = (int)kr - pb.cu_k[b];
             if (j < 0 || j >= (int)pb.s2max) {          // past the given maximum: no records
-                pb.dk[i] = 0;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) out[c] = 0;
                 continue;
             }
         }
-        const int kbt = (b * pb.n2 + g) * pb.dk_nkb + j / KB;
+        const int kbt = (b * n2 + g) * pb.dk_nkb + j / KB;
         const int t0 = pb.kb_tasks[4 * kbt], nt = pb.kb_tasks[4 * kbt + 1];
         // partials added in task order; loads issued eight at a time (a dependent round
         // trip per task would bound the kernel by latency)
-        const float *src = pb.dk_part + (size_t)(j % KB) * D + d;
-        const size_t step = (size_t)KB * D;
-        float s = 0.f;
+        const float4 *src = (const float4 *)(pb.dk_part + (size_t)(j % KB) * D + d);
+        const size_t step = (size_t)KB * D / 4;
+        float4 s = {0.f, 0.f, 0.f, 0.f};
         int t = t0;
         for (; t + 8 <= t0 + nt; t += 8) {
-            float v[8];
+            float4 v[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) v[u] = src[(size_t)(t + u) * step];
 #pragma unroll
-            for (int u = 0; u < 8; ++u) s += v[u];
+            for (int u = 0; u < 8; ++u) {
+                s.x += v[u].x;
+                s.y += v[u].y;
+                s.z += v[u].z;
+                s.w += v[u].w;
+            }
         }
-        for (; t < t0 + nt; ++t) s += src[(size_t)t * step];
-        pb.dk[i] = to16<F16>(s);
+        for (; t < t0 + nt; ++t) {
+            const float4 v = src[(size_t)t * step];
+            s.x += v.x;
+            s.y += v.y;
+            s.z += v.z;
+            s.w += v.w;
+        }
+        const uint16_t o0 = to16<F16>(s.x), o1 = to16<F16>(s.y), o2 = to16<F16>(s.z), o3 = to16<F16>(s.w);
+        if (st8) {
+            *(u32x2 *)out = u32x2{(uint32_t)o0 | ((uint32_t)o1 << 16), (uint32_t)o2 | ((uint32_t)o3 << 16)};
+        } else {
+            out[0] = o0;
+            out[1] = o1;
+            out[2] = o2;
+            out[3] = o3;
+        }
     }
 }
 
@@ -758,8 +785,8 @@ hipError_t launch_dense_dk(const Problem &pb, int hp, bool f16, hipStream_t stre
 }
 
 hipError_t launch_dense_dk_reduce(const Problem &pb, bool f16, hipStream_t stream) {
-    const size_t n = (size_t)pb.t2 * pb.n2 * pb.d;
-    size_t blocks = (n + 255) / 256;
+    const size_t n4 = (size_t)pb.t2 * pb.n2 * pb.d / 4;
+    size_t blocks = (n4 + 255) / 256;
     if (blocks > 65536) blocks = 65536;
     if (blocks == 0) return hipSuccess;
     if (f16)
