@@ -93,15 +93,28 @@ __global__ __launch_bounds__(kScanThreads) void scan_apply_kernel(int32_t *cnt, 
 // before its first use.
 constexpr int kSortIlp = 4;
 
+// Unit and key head of record o (o < 2^31): a shift when topk and N2 are powers of two
+// (a uniform branch), else 32-bit divisions.
+__device__ __forceinline__ void record_unit(const Problem &pb, int o, int &u, int &g) {
+    const unsigned tk = (unsigned)pb.topk, n2 = (unsigned)pb.n2;
+    if ((tk & (tk - 1)) == 0 && (n2 & (n2 - 1)) == 0) {
+        u = (int)((unsigned)o >> (__builtin_ctz(tk)));
+        g = (int)((unsigned)u & (n2 - 1));
+    } else {
+        u = (int)((unsigned)o / tk);
+        g = (int)((unsigned)u % n2);
+    }
+}
+
 // The bins of records o, o + kSortThreads, ... (kSortIlp of them), -1 past the tile end or
 // past a unit's valid count.  Record indices fit in 32 bits (U * topk < 2^31).
 __device__ __forceinline__ void record_bins(const Problem &pb, int o, int o1, int (&bin)[kSortIlp]) {
-    int key[kSortIlp], cnt[kSortIlp], u[kSortIlp];
+    int key[kSortIlp], cnt[kSortIlp], u[kSortIlp], g[kSortIlp];
 #pragma unroll
     for (int i = 0; i < kSortIlp; ++i) {
         const int oi = o + kSortThreads * i;
         const int oc = oi < o1 ? oi : o;                        // clamped: loads stay in range
-        u[i] = (int)((unsigned)oc / (unsigned)pb.topk);
+        record_unit(pb, oc, u[i], g[i]);
         key[i] = pb.srec_key[oc];
         cnt[i] = pb.srec_cnt[u[i]];
     }
@@ -109,7 +122,7 @@ __device__ __forceinline__ void record_bins(const Problem &pb, int o, int o1, in
     for (int i = 0; i < kSortIlp; ++i) {
         const int oi = o + kSortThreads * i;
         const int p = oi - u[i] * pb.topk;
-        bin[i] = oi < o1 && p < cnt[i] ? key[i] * pb.n2 + u[i] % pb.n2 : -1;
+        bin[i] = oi < o1 && p < cnt[i] ? key[i] * pb.n2 + g[i] : -1;
     }
 }
 
@@ -160,19 +173,19 @@ __global__ __launch_bounds__(kSortThreads) void bucket_scatter_kernel(Problem pb
         // (record a + tid + kSortThreads i for i < kScatterPer; loads at clamped indices)
         int bin[kScatterPer], rk[kScatterPer];
         {
-            int key[kScatterPer], cn[kScatterPer], u[kScatterPer];
+            int key[kScatterPer], cn[kScatterPer], u[kScatterPer], g[kScatterPer];
 #pragma unroll
             for (int i = 0; i < kScatterPer; ++i) {
                 const int oi = a + tid + kSortThreads * i;
                 const int oc = oi < a1 ? oi : a;
-                u[i] = (int)((unsigned)oc / (unsigned)pb.topk);
+                record_unit(pb, oc, u[i], g[i]);
                 key[i] = pb.srec_key[oc];
                 cn[i] = pb.srec_cnt[u[i]];
             }
 #pragma unroll
             for (int i = 0; i < kScatterPer; ++i) {
                 const int oi = a + tid + kSortThreads * i;
-                bin[i] = oi < a1 && oi - u[i] * pb.topk < cn[i] ? key[i] * pb.n2 + u[i] % pb.n2 : -1;
+                bin[i] = oi < a1 && oi - u[i] * pb.topk < cn[i] ? key[i] * pb.n2 + g[i] : -1;
             }
         }
 #pragma unroll
