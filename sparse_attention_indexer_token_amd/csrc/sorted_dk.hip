@@ -12,8 +12,10 @@
 //                   (bin >> shift) in LDS, written as column `tile` of [bucket][tile];
 //   scan            exclusive prefix of that matrix in bucket-major order (so each
 //                   bucket's records are contiguous, each tile's inside its bucket);
-//   bucket scatter  per tile, each record takes a place in its bucket's range by an LDS
-//                   atomic; (bin, record) pairs -> tmp;
+//   bucket scatter  per tile, 8192 records at a time: each record's rank in its bucket
+//                   by an LDS atomic, the records staged in LDS in bucket order, then
+//                   written as contiguous runs into the buckets' ranges; (bin, record)
+//                   pairs -> tmp;
 //   bucket sort     one workgroup per bucket: an LDS histogram over its bins, its prefix
 //                   -> start[bin] (and the most records of one bin -> sort_maxref),
 //                   then each record placed by an LDS atomic -> list.
@@ -191,7 +193,8 @@ __global__ __launch_bounds__(kSortThreads) void bucket_scatter_kernel(Problem pb
 #pragma unroll
         for (int i = 0; i < kScatterPer; ++i) rk[i] = bin[i] >= 0 ? atomicAdd(&lb[bin[i] >> sh], 1) : 0;
         lds_barrier();
-        // exclusive prefix of the chunk's bucket counts (thread t: buckets t * kBPT ..)
+        // exclusive prefix of the chunk's bucket counts (thread t: buckets
+        // t * kBucketsPerThread ..)
         int cnt[kBucketsPerThread], sum = 0;
 #pragma unroll
         for (int j = 0; j < kBucketsPerThread; ++j) {
