@@ -252,17 +252,66 @@ __global__ __launch_bounds__(64 * kWaves64, (gd64_wgpc<HP, CAP, HK>())) void gra
         __builtin_amdgcn_make_buffer_rsrc((void *)pb.k16, (short)krow_bytes, nkrows, 0x00020000);
     constexpr uint32_t kPadOffset = 0x80000000u;      // past the end of every raw view below
 
-    // ---- walk the units of this workgroup's parts, inputs one unit ahead ------------
-    int cpart = (int)blockIdx.x - (int)gridDim.x, cu = 0, cue = 0;
+    // ---- walk the units of the parts this workgroup takes, inputs one unit ahead -----
+    // With at most two parts per workgroup, workgroup b walks parts b, b + grid.  With
+    // more (the host gives TND problems four per workgroup), the parts are handed out by
+    // a counter, last part first (the causal rows at the end of a sequence cost the most,
+    // so the last parts taken are cheap ones and the workgroups finish close together;
+    // whole-part splits of sequences of different lengths are uneven).  Thread 0 takes them; a ring of three LDS entries passes
+    // them on: the entry read at one switch is refilled by thread 0 at the next switch,
+    // for the switch two after that.  Between two switches lies at least one unit with
+    // its barriers, so a refill follows every read of the old value and precedes every
+    // read of the new one.
+    __shared__ int s_pq[3];
+    // part of order number k (k-th from the last); -1 past the last order number, -2 when
+    // the part holds no unit
+    auto part_at = [&](int k) -> int {
+        if (k >= parts) return -1;
+        const int p = parts - 1 - k;
+        const int a = pb.metadata[16 + p], e = pb.metadata[17 + p];
+        return (a < 0 ? 0 : a) < (e > U ? U : e) ? p : -2;
+    };
+    // the first two parts of every workgroup are fixed (order numbers b and grid + b: no
+    // burst of atomics on one word at the start); later ones come from the counter
+    const bool dyn = parts > 2 * (int)gridDim.x;
+    auto grab = [&]() -> int {      // thread 0: the next non-empty part, -1 when none is left
+        for (;;) {
+            const int p = part_at(2 * (int)gridDim.x + atomicAdd(pb.part_ctr, 1));
+            if (p != -2) return p;
+        }
+    };
+    if (dyn) {
+        if (tid == 0) {
+            int p0 = part_at((int)blockIdx.x), p1 = part_at((int)gridDim.x + (int)blockIdx.x);
+            if (p0 < 0) p0 = grab();
+            if (p1 < 0) p1 = p0 < 0 ? -1 : grab();
+            s_pq[0] = p0;
+            s_pq[1] = p1;
+        }
+        lds_barrier();
+    }
+    int cpart = (int)blockIdx.x - (int)gridDim.x;
+    int pseq = 0, cu = 0, cue = 0;
     auto next_unit = [&]() -> bool {
         ++cu;
-        while (cu >= cue) {
-            cpart += gridDim.x;
-            if (cpart >= parts) return false;
-            int a = pb.metadata[16 + cpart], e = pb.metadata[17 + cpart];
-            cu = a < 0 ? 0 : a;
-            cue = e > U ? U : e;
+        if (!dyn) {
+            while (cu >= cue) {
+                cpart += gridDim.x;
+                if (cpart >= parts) return false;
+                const int a = pb.metadata[16 + cpart], e = pb.metadata[17 + cpart];
+                cu = a < 0 ? 0 : a;
+                cue = e > U ? U : e;
+            }
+            return true;
         }
+        if (cu < cue) return true;
+        const int p = s_pq[pseq % 3];
+        if (tid == 0) s_pq[(pseq + 2) % 3] = grab();
+        ++pseq;
+        if (p < 0) return false;
+        const int a = pb.metadata[16 + p], e = pb.metadata[17 + p];
+        cu = a < 0 ? 0 : a;
+        cue = e > U ? U : e;
         return true;
     };
     UnitInputs<SPT_MAX> in;

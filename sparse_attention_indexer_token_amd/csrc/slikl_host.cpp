@@ -280,6 +280,12 @@ slikl_status resolve_parts(const slikl_desc *d, int32_t *parts) {
                                                        (int)(d->n1 / d->n2))
                      : slikl::grad_fused_blocks_per_cu(hp, (int)d->d, f16, mode);
     int64_t p = (int64_t)cus * per_cu;
+    // with TND queries the 64-head fused kernel takes its parts from a counter, four per
+    // workgroup on average: sequences of different lengths leave whole-part splits
+    // uneven (varlen workload: fused kernel 4.49 -> 4.06 ms); BSND rows keep one part
+    // per workgroup, where the counter's traffic cost more than it balanced (dsv32:
+    // 408 -> 465 us)
+    if ((mode == 2 || sorted_dk(d)) && hp <= 64 && d->layout_q == SLIKL_LAYOUT_TND) p *= 4;
     if (p > SLIKL_MAX_PARTS) p = SLIKL_MAX_PARTS;
     if (p < 1) p = 1;
     *parts = (int32_t)p;
@@ -499,6 +505,7 @@ slikl_status grad_impl(const slikl_desc *desc, const void *q, const void *k, con
         metadata = md;
     }
     pb.metadata = metadata;
+    pb.part_ctr = (int32_t *)(ws + wp.scale_off) + 12;        // in the zeroed scale block
     pe.begin(SLIKL_PHASE_FILL);
     {
         // the dense dI rows are zeroed by the fused kernel, each over the key blocks

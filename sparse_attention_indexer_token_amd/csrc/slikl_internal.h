@@ -72,6 +72,7 @@ struct Problem {
                              // when no bin holds more than kPartsI16MaxRefs records
                              // (*sort_maxref), else fp32 (valid records only)
     int32_t *sort_maxref;    // most records of one bin (zeroed per call; set by the sort)
+    int32_t *part_ctr;       // parts handed out so far by the 64-head fused kernel (zeroed per call)
     int32_t sort_shift, sort_nbuckets, sort_tile, sort_nblk;
     const int32_t *cu_q;     // [batch + 1] or null (BSND)
     const int32_t *cu_k;     // [batch + 1] or null (BSND)
