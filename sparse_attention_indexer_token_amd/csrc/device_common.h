@@ -333,6 +333,20 @@ __device__ __forceinline__ int block_excl_scan(int v, int *tmp, int *total) {
     return off + x - v;
 }
 
+// One slot's terms of the loss and its gradient, from the formula section of the
+// operator page "aclnnSparseLightningIndexerKLLossGrad" (the loss of a query row is
+// the KL divergence of Softmax(I) from p, the gradient of I is y - p).  With m the
+// unit's largest I and log_z = log sum exp(I - m), y = exp(I - m) / Z:
+//   kl_term: p (log p - log y) = p (log p - (I - m) + log Z), 0 where p = 0;
+//   dI:      y - p.
+// The fused kernels each hold the slots in their own layout (LDS list, registers
+// per position); these are the one definition of what each slot contributes.
+__device__ __forceinline__ float kl_term(float p, float i_minus_m, float log_z) {
+    return p > 0.f ? p * (logf(p) - i_minus_m + log_z) : 0.f;
+}
+
+__device__ __forceinline__ float softmax_grad(float y, float p) { return y - p; }
+
 // e such that amax * 2^e < 2^15 (0 for zero or non-finite amax), clamped
 __device__ __forceinline__ int pow2_exponent_below_2p15(float amax) {
     if (!(amax > 0.f) || !(amax < INFINITY)) return 0;

@@ -493,7 +493,7 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
             float kl = 0.f;
 #pragma unroll
             for (int i = 0; i < PPT; ++i)
-                if (p0 + i < nvalid && pp8[i] > 0.f) kl += pp8[i] * (logf(pp8[i]) - (iv8[i] - m) + lz);
+                if (p0 + i < nvalid) kl += kl_term(pp8[i], iv8[i] - m, lz);
             kl = block_sum(kl, s_red + 8);
             if (tid == 0) pb.kl[u] = kl;
         }
@@ -514,7 +514,7 @@ __global__ __launch_bounds__(kBlock, 1) void grad_dense_kernel(Problem pb) {
                     dd[k2] = 0.f;
                     if (pp < nvalid) {
                         const float y = e[i + k2] * invZ;
-                        dd[k2] = y - pp8[i + k2];
+                        dd[k2] = softmax_grad(y, pp8[i + k2]);
                         yrow[s_slot[pp]] = y;
                         s_I[pp] = dd[k2];
                     }

@@ -688,7 +688,7 @@ __global__ __launch_bounds__(64 * kWaves64, (gd64_wgpc<HP, CAP, HK>())) void gra
             float kl = 0.f;
 #pragma unroll
             for (int i = 0; i < SPT_MAX; ++i)
-                if (((vbits >> i) & 1u) && in.pv[i] > 0.f) kl += in.pv[i] * (logf(in.pv[i]) - (iv[i] - m) + lz);
+                if ((vbits >> i) & 1u) kl += kl_term(in.pv[i], iv[i] - m, lz);
             kl = block_sum<NW>(kl, s_red + 2 * NW);
             if (tid == 0) pb.kl[u] = kl;
         }
@@ -704,7 +704,7 @@ __global__ __launch_bounds__(64 * kWaves64, (gd64_wgpc<HP, CAP, HK>())) void gra
                 yv[i] = 0.f;                           // (a unit with no valid slot has Z = 0)
                 if ((vbits >> i) & 1u) {
                     yv[i] = e[i] * invZ;
-                    const float dd = yv[i] - in.pv[i];
+                    const float dd = softmax_grad(yv[i], in.pv[i]);
                     s_I[pp] = dd;
                     s_d16[pp] = to16<true>(dd * dsc);
                     ++pp;

@@ -282,7 +282,7 @@ __global__ __launch_bounds__(kBlock, (HP == 128 ? 1 : 2)) void grad_fused_kernel
                 float kl = 0.f;
                 for (int j = tid; j < nvalid; j += kBlock) {
                     const float pv = prow[s_slot[j]];
-                    if (pv > 0.f) kl += pv * (logf(pv) - (s_I[j] - m) + lz);
+                    kl += kl_term(pv, s_I[j] - m, lz);
                 }
                 kl = block_sum(kl, s_red + 4);
                 if (tid == 0) pb.kl[u] = kl;
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kBlock, (HP == 128 ? 1 : 2)) void grad_fused_kernel
                     const int sl = s_slot[j];
                     const float y = expf(s_I[j] - m) / Z;
                     yrow[sl] = y;
-                    dI = y - prow[sl];
+                    dI = softmax_grad(y, prow[sl]);
                 }
                 s_I[j] = dI;
                 amax = fmaxf(amax, fabsf(dI));
