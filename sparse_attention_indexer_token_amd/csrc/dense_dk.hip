@@ -388,14 +388,39 @@ __global__ __launch_bounds__(kDkBlock, 1) void dense_dk_kernel1(Problem pb) {
 }
 
 // Task table (one workgroup): active rows per (key block, row chunk) from the
-// difference arrays, n_k = 1 + floor(c_k (S - K) / C) tasks for a key block with
-// c_k > 0 active rows (C their sum, K such blocks, S resident workgroups; one task
-// each when K >= S), task s of a block starting at the chunk that holds its
-// active row floor(s c_k / n_k).  Key blocks go through LDS KT at a time: a
+// difference arrays, n_k = ceil(c_k / tau) tasks for a key block with c_k > 0
+// active rows, tau the smallest row cap that keeps the tasks within S resident
+// workgroups (C the rows' sum, K such blocks; one task each when K >= S; past 1024
+// key blocks n_k = 1 + floor(c_k (S - K) / C)), task s of a block starting at the
+// chunk that holds its active row floor(s c_k / n_k).  Key blocks go through LDS KT at a time: a
 // thread per chunk runs the prefix over key blocks, a wave per key block the sums
 // and searches over chunks (at most 256 chunks: four per lane).
 constexpr int kTaskKT = 48;
 constexpr int kTaskNchMax = 256;
+
+// Rows per task: the smallest cap tau with sum over key blocks of ceil(c_k / tau) <= S,
+// so that the largest task (which bounds the dK kernel: one task per workgroup) is as
+// small as S tasks allow.  Needs 0 < K < S.  lo = ceil(C / S) is a lower bound (below
+// it the tasks number more than S); hi = min(ceil(C / (S - K)), max c_k) is feasible
+// (sum ceil(c_k / hi) <= C / hi + K <= S, or K tasks of one each).  `need(cap)` gives
+// the task count for a cap, the same value in every thread that calls it.
+template <class Need>
+__device__ __forceinline__ int task_row_cap(long long C, int K, int S, int cmax, Need need) {
+    long long lo = (C + S - 1) / S, hi = (C + (S - K) - 1) / (S - K);
+    if (hi > cmax) hi = cmax;
+    if (lo < 1) lo = 1;
+    if (lo > hi) lo = hi;
+    while (lo < hi) {
+        const long long mid = (lo + hi) >> 1;
+        if (need((int)mid) <= S) hi = mid;
+        else lo = mid + 1;
+    }
+    return (int)hi;
+}
+
+__device__ __forceinline__ int ceil_div_u32(int c, int cap) {
+    return (int)(((unsigned)c + (unsigned)cap - 1u) / (unsigned)cap);
+}
 
 __global__ __launch_bounds__(1024) void dense_dk_tasks_kernel(Problem pb) {
     const int nbg = pb.batch * pb.n2, nkb = pb.dk_nkb, nch = pb.dk_nch, chunk = pb.dk_chunk;
@@ -489,7 +514,20 @@ __global__ __launch_bounds__(1024) void dense_dk_tasks_kernel(Problem pb) {
                 C += ((long long)hi32 << 32) | (unsigned)lo32;
             }
             const int S = pb.dk_slots;
-            const int n = c == 0 ? 0 : (K < S ? 1 + (int)((long long)c * (S - K) / C) : 1);
+            int n = c == 0 ? 0 : 1;
+            if (K > 0 && K < S) {
+                int cmax = c;
+                for (int o = 32; o > 0; o >>= 1) {
+                    const int y = __shfl_xor(cmax, o);
+                    cmax = y > cmax ? y : cmax;
+                }
+                const int tau = task_row_cap(C, K, S, cmax, [&](int cap) {
+                    int x = c > 0 ? ceil_div_u32(c, cap) : 0;
+                    for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+                    return x;
+                });
+                n = c > 0 ? ceil_div_u32(c, tau) : 0;
+            }
             int first = n;                  // exclusive prefix of the task counts
             for (int o = 1; o < 64; o <<= 1) {
                 const int y = __shfl_up(first, o);
@@ -627,6 +665,28 @@ __global__ __launch_bounds__(1024) void dense_dk_tasks_kernel(Problem pb) {
         K += s_ne[w];
     }
     const int S = pb.dk_slots;
+    // rows per task (up to 1024 key blocks, one per thread); beyond that each block
+    // gets 1 + floor(c (S - K) / C) tasks, at most S in all
+    int tau = 0;
+    if (NT <= 1024 && K > 0 && K < S) {
+        const int c = tid < NT ? pb.kb_tasks[4 * tid + 2] : 0;
+        __shared__ int s_red16[16];
+        auto block_red = [&](int x, bool mx) {
+            for (int o = 32; o > 0; o >>= 1) {
+                const int y = __shfl_xor(x, o);
+                x = mx ? (y > x ? y : x) : x + y;
+            }
+            __syncthreads();        // the previous round's readers are done
+            if (lane == 0) s_red16[wave] = x;
+            __syncthreads();
+            int r = s_red16[0];
+            for (int w = 1; w < 16; ++w) r = mx ? (s_red16[w] > r ? s_red16[w] : r) : r + s_red16[w];
+            return r;
+        };
+        const int cmax = block_red(c, true);
+        tau = task_row_cap(C, K, S, cmax,
+                           [&](int cap) { return block_red(c > 0 ? ceil_div_u32(c, cap) : 0, false); });
+    }
     // pass 2: tasks per key block and their first task (exclusive scan in rounds of 1024)
     int base = 0;
     for (int t0 = 0; t0 < NT; t0 += 1024) {
@@ -634,7 +694,7 @@ __global__ __launch_bounds__(1024) void dense_dk_tasks_kernel(Problem pb) {
         int n = 0;
         if (t < NT) {
             const int c = pb.kb_tasks[4 * t + 2];
-            n = c == 0 ? 0 : (K < S ? 1 + (int)((long long)c * (S - K) / C) : 1);
+            n = c == 0 ? 0 : (tau > 0 ? ceil_div_u32(c, tau) : (K < S ? 1 + (int)((long long)c * (S - K) / C) : 1));
         }
         __syncthreads();
         s_scan[tid] = n;
