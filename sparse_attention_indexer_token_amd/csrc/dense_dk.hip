@@ -390,7 +390,8 @@ __global__ __launch_bounds__(kDkBlock, 1) void dense_dk_kernel1(Problem pb) {
 // Task table (one workgroup): active rows per (key block, row chunk) from the
 // difference arrays, n_k = ceil(c_k / tau) tasks for a key block with c_k > 0
 // active rows, tau the smallest row cap that keeps the tasks within S resident
-// workgroups (C the rows' sum, K such blocks; one task each when K >= S; past 1024
+// workgroups, or within 2 S when that balances the workgroups' rows better (C the
+// rows' sum, K such blocks; one task each when K >= S; past 1024
 // key blocks n_k = 1 + floor(c_k (S - K) / C)), task s of a block starting at the
 // chunk that holds its active row floor(s c_k / n_k).  Key blocks go through LDS KT at a time: a
 // thread per chunk runs the prefix over key blocks, a wave per key block the sums
@@ -420,6 +421,25 @@ __device__ __forceinline__ int task_row_cap(long long C, int K, int S, int cmax,
 
 __device__ __forceinline__ int ceil_div_u32(int c, int cap) {
     return (int)(((unsigned)c + (unsigned)cap - 1u) / (unsigned)cap);
+}
+
+// The cap for S tasks, or, for TND queries, for up to 2 S (the dK kernel's workgroups
+// stride over the tasks, so workgroup b takes tasks b and b + S) when twice that cap is
+// below the first by more than 1/32.  The rounding of ceil(c_k / tau) wastes up to one
+// task per key block; two tasks per workgroup halve that.  Sequences of mixed lengths
+// leave the dK kernel waiting on its longest workgroup, and there it pays (varlen_tnd
+// dK 3.61 -> 3.37 ms); equal BSND batches are bound by the kernel's throughput, and
+// the second task's fixed work and partials cost more than the balance gains
+// (contention_det dK 1.30 -> 1.33 ms).
+template <class Need>
+__device__ __forceinline__ int task_row_cap2(const Problem &pb, long long C, int K, int S, int cmax, Need need) {
+    int tau = task_row_cap(C, K, S, cmax, need);
+    const int S2 = 2 * S < pb.dk_max_tasks ? 2 * S : pb.dk_max_tasks;
+    if (pb.layout_q == 1 && S2 > S) {
+        const int tau2 = task_row_cap(C, K, S2, cmax, need);
+        if (64LL * tau2 < 31LL * tau) tau = tau2;
+    }
+    return tau;
 }
 
 __global__ __launch_bounds__(1024) void dense_dk_tasks_kernel(Problem pb) {
@@ -521,7 +541,7 @@ __global__ __launch_bounds__(1024) void dense_dk_tasks_kernel(Problem pb) {
                     const int y = __shfl_xor(cmax, o);
                     cmax = y > cmax ? y : cmax;
                 }
-                const int tau = task_row_cap(C, K, S, cmax, [&](int cap) {
+                const int tau = task_row_cap2(pb, C, K, S, cmax, [&](int cap) {
                     int x = c > 0 ? ceil_div_u32(c, cap) : 0;
                     for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
                     return x;
@@ -684,8 +704,8 @@ __global__ __launch_bounds__(1024) void dense_dk_tasks_kernel(Problem pb) {
             return r;
         };
         const int cmax = block_red(c, true);
-        tau = task_row_cap(C, K, S, cmax,
-                           [&](int cap) { return block_red(c > 0 ? ceil_div_u32(c, cap) : 0, false); });
+        tau = task_row_cap2(pb, C, K, S, cmax,
+                            [&](int cap) { return block_red(c > 0 ? ceil_div_u32(c, cap) : 0, false); });
     }
     // pass 2: tasks per key block and their first task (exclusive scan in rounds of 1024)
     int base = 0;
