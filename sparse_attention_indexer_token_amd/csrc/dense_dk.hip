@@ -427,10 +427,11 @@ __device__ __forceinline__ int ceil_div_u32(int c, int cap) {
 // stride over the tasks, so workgroup b takes tasks b and b + S) when twice that cap is
 // below the first by more than 1/32.  The rounding of ceil(c_k / tau) wastes up to one
 // task per key block; two tasks per workgroup halve that.  Sequences of mixed lengths
-// leave the dK kernel waiting on its longest workgroup, and there it pays (varlen_tnd
-// dK 3.61 -> 3.37 ms); equal BSND batches are bound by the kernel's throughput, and
-// the second task's fixed work and partials cost more than the balance gains
-// (contention_det dK 1.30 -> 1.33 ms).
+// leave the dK kernel waiting on its longest workgroup, and there it pays (8 sequences
+// of 512..8192 rows, 64 heads, top-k 2048: dK 3.61 -> 3.37 ms); equal BSND batches are
+// bound by the kernel's throughput, and the second task's fixed work and partials cost
+// more than the balance gains (4 batches of 8192 rows, 16 heads, top-k 512: dK 1.30 ->
+// 1.33 ms).
 template <class Need>
 __device__ __forceinline__ int task_row_cap2(const Problem &pb, long long C, int K, int S, int cmax, Need need) {
     int tau = task_row_cap(C, K, S, cmax, need);

@@ -31,8 +31,8 @@ bool any_tnd(const slikl_desc *d) { return d->layout_q == SLIKL_LAYOUT_TND || d-
 // per key block that its named keys meet.  Blocks of twice the keys halve those fetches
 // where they dominate: when q is too large to stay in the on-die caches (more than 128
 // MiB), or when rows name few keys of the blocks they meet (top-k lists of at most an
-// eighth of the longest key sequence: measured on the contention workload, dK 3.5 ->
-// 2.1 ms, where the dense dsv32 lists run better with 128-key blocks).
+// eighth of the longest key sequence: 4 batches of 8192 rows, top-k 512, dK 3.5 ->
+// 2.1 ms; one 4096-row sequence with top-k 2048 runs better with 128-key blocks).
 int dense_kt(const slikl_desc *d) {
     const bool big_q = (double)rows_q(d) * d->n1 * d->d * 2.0 > 128.0 * (1 << 20);
     const bool sparse_rows = len_k(d) >= 8 * d->topk;
@@ -125,9 +125,9 @@ int dk_strategy(const slikl_desc *d) {
 // takes many parts), then summed per key through a key-sorted record list.
 // Asked for explicitly (SORTED), or taken by AUTO where the dense strategy is not and
 // there are at least 2048 units (below that its extra launches cost more than the
-// atomics they save) and the parts buffer fits in 8 GiB.  Measured on long_context
-// (S2 = 64 topk): 5.0 ms against 6.9 ms with fp32 atomics, 5.4 against 12.1 ms when
-// deterministic.
+// atomics they save) and the parts buffer fits in 8 GiB.  Measured on 8192 query rows
+// over 131072 keys (S2 = 64 topk, 32 heads): 5.0 ms against 6.9 ms with fp32 atomics,
+// 5.4 against 12.1 ms when deterministic.
 bool sorted_dk(const slikl_desc *d) {
     if (d->dk_mode == SLIKL_DK_SORTED) return true;      // validate checked sorted_fits
     if (d->dk_mode != SLIKL_DK_AUTO || dk_strategy(d) == 2 || !sorted_fits(d)) return false;
@@ -282,9 +282,9 @@ slikl_status resolve_parts(const slikl_desc *d, int32_t *parts) {
     int64_t p = (int64_t)cus * per_cu;
     // with TND queries the 64-head fused kernel takes its parts from a counter, four per
     // workgroup on average: sequences of different lengths leave whole-part splits
-    // uneven (varlen workload: fused kernel 4.49 -> 4.06 ms); BSND rows keep one part
-    // per workgroup, where the counter's traffic cost more than it balanced (dsv32:
-    // 408 -> 465 us)
+    // uneven (8 sequences of 512..8192 rows, 64 heads: fused kernel 4.49 -> 4.06 ms);
+    // BSND rows keep one part per workgroup, where the counter's traffic cost more than
+    // it balanced (one 4096-row sequence, 64 heads, top-k 2048: 408 -> 465 us)
     if ((mode == 2 || sorted_dk(d)) && hp <= 64 && d->layout_q == SLIKL_LAYOUT_TND) p *= 4;
     if (p > SLIKL_MAX_PARTS) p = SLIKL_MAX_PARTS;
     if (p < 1) p = 1;
